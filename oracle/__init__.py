@@ -1,0 +1,307 @@
+"""Scalar CPU oracle for block-scaled quantization -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The GPU engine never does, and the two
+share no code: this wrapper loads ``liborc.so``, built by gcc from
+``oracle.c`` alone.
+
+Inputs are numpy arrays shaped ``[rows, cols]`` or ``[batch, rows, cols]``:
+float32 values, or bf16 given as their raw ``uint16`` bit patterns (pass
+``bf16=True``).  Torch CPU tensors are accepted too and converted losslessly.
+Outputs follow the layouts documented in ``oracle.h``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.environ.get("PQB_ORACLE_LIB") or os.path.join(_HERE, "liborc.so")
+
+F32, BF16 = 0, 1
+TENSOR, ROW, BLK_1x128, BLK_128x128 = 0, 1, 2, 3
+GRANS = {"tensor": TENSOR, "row": ROW, "1x128": BLK_1x128, "128x128": BLK_128x128}
+
+_lib = None
+
+
+def build(verbose: bool = False) -> str:
+    """Compile oracle.c with gcc (IEEE binary32, no contraction, no fast-math)."""
+    cmd = ["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+           "-Wall", "-Wextra", "-o", _LIB_PATH, _SRC, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    return _LIB_PATH
+
+
+def lib():
+    """Load liborc.so, building it first if it is missing or older than its source."""
+    global _lib
+    if _lib is None:
+        if (not os.path.exists(_LIB_PATH)
+                or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
+            build()
+        L = ctypes.CDLL(_LIB_PATH)
+        P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.orc_e4m3_decode.argtypes, L.orc_e4m3_decode.restype = [ctypes.c_uint8], ctypes.c_float
+        L.orc_e4m3_encode.argtypes, L.orc_e4m3_encode.restype = [ctypes.c_float], ctypes.c_uint8
+        L.orc_e2m1_decode.argtypes, L.orc_e2m1_decode.restype = [ctypes.c_uint8], ctypes.c_float
+        L.orc_e2m1_encode.argtypes, L.orc_e2m1_encode.restype = [ctypes.c_float], ctypes.c_uint8
+        L.orc_bf16_round.argtypes, L.orc_bf16_round.restype = [ctypes.c_float], ctypes.c_uint16
+        L.orc_bf16_to_f32.argtypes, L.orc_bf16_to_f32.restype = [ctypes.c_uint16], ctypes.c_float
+        L.orc_uniform_code.argtypes = [ctypes.c_float] * 3
+        L.orc_uniform_code.restype = ctypes.c_float
+        for name in ("orc_fp8_quantize", "orc_fp8_dequantize", "orc_mxfp4_quantize",
+                     "orc_mxfp4_dequantize", "orc_nvfp4_quantize", "orc_nvfp4_dequantize",
+                     "orc_int4_quantize", "orc_int4_dequantize", "orc_kv_write_fp8"):
+            getattr(L, name).restype = I
+        for name in ("orc_e4m3_encode_n", "orc_e2m1_encode_n", "orc_bf16_round_n"):
+            getattr(L, name).argtypes = [P, I64, P]
+            getattr(L, name).restype = None
+        L.orc_fp8_quantize.argtypes = [P, I, I64, I64, I64, I, P, P]
+        L.orc_fp8_dequantize.argtypes = [P, P, I64, I64, I64, I, I, P]
+        L.orc_mxfp4_quantize.argtypes = [P, I, I64, I64, I64, P, P]
+        L.orc_mxfp4_dequantize.argtypes = [P, P, I64, I64, I64, I, P]
+        L.orc_nvfp4_quantize.argtypes = [P, I, I64, I64, I64, P, P, P]
+        L.orc_nvfp4_dequantize.argtypes = [P, P, P, I64, I64, I64, I, P]
+        L.orc_int4_quantize.argtypes = [P, I, I64, I64, I64, P, P, P]
+        L.orc_int4_dequantize.argtypes = [P, P, P, I64, I64, I64, I, P]
+        L.orc_kv_write_fp8.argtypes = [P, P, I, I64, I64, P, P, P, P]
+        _lib = L
+    return _lib
+
+
+# --------------------------------------------------------------------------
+# marshalling helpers
+# --------------------------------------------------------------------------
+
+def _as_input(x, bf16: bool | None):
+    """Return (contiguous numpy array, dtype code, batch, rows, cols)."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().cpu().contiguous()
+            if x.dtype == torch.bfloat16:
+                x, bf16 = x.view(torch.int16).numpy().view(np.uint16), True
+            else:
+                x, bf16 = x.to(torch.float32).numpy(), False
+    except ImportError:  # pragma: no cover
+        pass
+    x = np.ascontiguousarray(x)
+    if bf16 is None:
+        bf16 = x.dtype == np.uint16
+    if bf16:
+        if x.dtype != np.uint16:
+            raise TypeError("bf16 input must be given as uint16 bit patterns")
+    elif x.dtype != np.float32:
+        raise TypeError("input must be float32 or bf16 bits")
+    if x.ndim == 2:
+        batch, rows, cols = 1, x.shape[0], x.shape[1]
+    elif x.ndim == 3:
+        batch, rows, cols = x.shape
+    else:
+        raise ValueError("input must be [rows, cols] or [batch, rows, cols]")
+    return x, (BF16 if bf16 else F32), batch, rows, cols
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise ValueError(f"oracle {what}: shape rejected (status {rc})")
+
+
+def _out(shape, out_bf16: bool):
+    return np.empty(shape, dtype=np.uint16 if out_bf16 else np.float32)
+
+
+# --------------------------------------------------------------------------
+# scalar codecs
+# --------------------------------------------------------------------------
+
+def e4m3_decode(code: int) -> float:
+    return lib().orc_e4m3_decode(code)
+
+
+def e4m3_encode(y: float) -> int:
+    return lib().orc_e4m3_encode(y)
+
+
+def e2m1_decode(nibble: int) -> float:
+    return lib().orc_e2m1_decode(nibble)
+
+
+def e2m1_encode(y: float) -> int:
+    return lib().orc_e2m1_encode(y)
+
+
+def bf16_round(v: float) -> int:
+    return lib().orc_bf16_round(v)
+
+
+def uniform_code(x: float, s: float, z: float) -> float:
+    return lib().orc_uniform_code(x, s, z)
+
+
+def e4m3_encode_array(y) -> np.ndarray:
+    y = np.ascontiguousarray(y, np.float32)
+    out = np.empty(y.shape, np.uint8)
+    lib().orc_e4m3_encode_n(_p(y), y.size, _p(out))
+    return out
+
+
+def e2m1_encode_array(y) -> np.ndarray:
+    y = np.ascontiguousarray(y, np.float32)
+    out = np.empty(y.shape, np.uint8)
+    lib().orc_e2m1_encode_n(_p(y), y.size, _p(out))
+    return out
+
+
+def bf16_round_array(v) -> np.ndarray:
+    v = np.ascontiguousarray(v, np.float32)
+    out = np.empty(v.shape, np.uint16)
+    lib().orc_bf16_round_n(_p(v), v.size, _p(out))
+    return out
+
+
+# --------------------------------------------------------------------------
+# quantizers
+# --------------------------------------------------------------------------
+
+def _fp8_nscales(gran, batch, rows, cols):
+    if gran == TENSOR:
+        return (batch,)
+    if gran == ROW:
+        return (batch, rows)
+    if gran == BLK_1x128:
+        return (batch, rows, cols // 128)
+    br = min(128, rows)
+    return (batch, rows // br if br else 0, cols // 128)
+
+
+def fp8_quantize(x, gran, bf16=None):
+    """-> (codes u8 [batch, rows, cols], scales f32 in the scope layout)."""
+    gran = GRANS.get(gran, gran)
+    x, dt, b, r, c = _as_input(x, bf16)
+    codes = np.empty((b, r, c), np.uint8)
+    br = min(128, r)
+    if gran == BLK_128x128 and (c % 128 or (br and r % br)):
+        _check(-4, "fp8_quantize")
+    if gran == BLK_1x128 and c % 128:
+        _check(-4, "fp8_quantize")
+    scales = np.empty(_fp8_nscales(gran, b, r, c), np.float32)
+    _check(lib().orc_fp8_quantize(_p(x), dt, b, r, c, gran, _p(codes), _p(scales)), "fp8_quantize")
+    return codes, scales
+
+
+def fp8_dequantize(codes, scales, gran, out_bf16=False):
+    gran = GRANS.get(gran, gran)
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.float32)
+    b, r, c = codes.shape
+    out = _out((b, r, c), out_bf16)
+    _check(lib().orc_fp8_dequantize(_p(codes), _p(scales), b, r, c, gran, int(out_bf16), _p(out)),
+           "fp8_dequantize")
+    return out
+
+
+def mxfp4_quantize(x, bf16=None):
+    """-> (codes u8 [batch, rows, cols/2], scales u8 E8M0 [batch, rows, cols/32])."""
+    x, dt, b, r, c = _as_input(x, bf16)
+    if c % 32:
+        _check(-4, "mxfp4_quantize")
+    codes = np.zeros((b, r, c // 2), np.uint8)
+    scales = np.empty((b, r, c // 32), np.uint8)
+    _check(lib().orc_mxfp4_quantize(_p(x), dt, b, r, c, _p(codes), _p(scales)), "mxfp4_quantize")
+    return codes, scales
+
+
+def mxfp4_dequantize(codes, scales, out_bf16=False):
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    b, r, c2 = codes.shape
+    out = _out((b, r, 2 * c2), out_bf16)
+    _check(lib().orc_mxfp4_dequantize(_p(codes), _p(scales), b, r, 2 * c2, int(out_bf16), _p(out)),
+           "mxfp4_dequantize")
+    return out
+
+
+def nvfp4_quantize(x, bf16=None):
+    """-> (codes u8 [b, r, c/2], block scales u8 E4M3 [b, r, c/16], tensor scale f32 [b])."""
+    x, dt, b, r, c = _as_input(x, bf16)
+    if c % 16:
+        _check(-4, "nvfp4_quantize")
+    codes = np.zeros((b, r, c // 2), np.uint8)
+    scales = np.empty((b, r, c // 16), np.uint8)
+    gs = np.empty((b,), np.float32)
+    _check(lib().orc_nvfp4_quantize(_p(x), dt, b, r, c, _p(codes), _p(scales), _p(gs)),
+           "nvfp4_quantize")
+    return codes, scales, gs
+
+
+def nvfp4_dequantize(codes, scales, gs, out_bf16=False):
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    gs = np.ascontiguousarray(gs, np.float32)
+    b, r, c2 = codes.shape
+    out = _out((b, r, 2 * c2), out_bf16)
+    _check(lib().orc_nvfp4_dequantize(_p(codes), _p(scales), _p(gs), b, r, 2 * c2, int(out_bf16),
+                                      _p(out)), "nvfp4_dequantize")
+    return out
+
+
+def int4_zero_bytes_per_row(cols: int) -> int:
+    return (cols // 128 + 1) // 2
+
+
+def int4_quantize(x, bf16=None):
+    """-> (codes u8 [b, r, c/2], scales bf16-bits u16 [b, r, c/128], zeros u8 [b, r, ceil(G/2)])."""
+    x, dt, b, r, c = _as_input(x, bf16)
+    if c % 128:
+        _check(-4, "int4_quantize")
+    codes = np.zeros((b, r, c // 2), np.uint8)
+    scales = np.empty((b, r, c // 128), np.uint16)
+    zeros = np.zeros((b, r, int4_zero_bytes_per_row(c)), np.uint8)
+    _check(lib().orc_int4_quantize(_p(x), dt, b, r, c, _p(codes), _p(scales), _p(zeros)),
+           "int4_quantize")
+    return codes, scales, zeros
+
+
+def int4_dequantize(codes, scales, zeros, out_bf16=False):
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint16)
+    zeros = np.ascontiguousarray(zeros, np.uint8)
+    b, r, c2 = codes.shape
+    out = _out((b, r, 2 * c2), out_bf16)
+    _check(lib().orc_int4_dequantize(_p(codes), _p(scales), _p(zeros), b, r, 2 * c2,
+                                     int(out_bf16), _p(out)), "int4_dequantize")
+    return out
+
+
+def kv_write_fp8(k, v, bf16=None):
+    """K, V shaped [layers, ...]; one scale per layer for each.
+    -> (k_codes, v_codes, k_scales [layers], v_scales [layers])."""
+    k2, dtk, *_ = _as_input(k.reshape(k.shape[0], -1), bf16)
+    v2, dtv, *_ = _as_input(v.reshape(v.shape[0], -1), bf16)
+    if dtk != dtv or k2.shape != v2.shape:
+        raise ValueError("K and V must share dtype and shape")
+    layers, per = k2.shape
+    kc = np.empty((layers, per), np.uint8)
+    vc = np.empty((layers, per), np.uint8)
+    ks = np.empty((layers,), np.float32)
+    vs = np.empty((layers,), np.float32)
+    _check(lib().orc_kv_write_fp8(_p(k2), _p(v2), dtk, layers, per, _p(kc), _p(vc), _p(ks),
+                                  _p(vs)), "kv_write_fp8")
+    return kc, vc, ks, vs
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to float32 (exact)."""
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)

@@ -1,0 +1,425 @@
+/*
+ * Scalar CPU oracle for block-scaled quantization.  TEST INFRASTRUCTURE ONLY:
+ * the test suite, the smoke check and the benchmark's CPU-baseline leg are its
+ * only users.  It is deliberately slow and literal, and it shares no code with
+ * the HIP engine.
+ *
+ * Sources (page title, section):
+ *   [DEPLOY]   "量化部署实战" (quantization deployment in practice):
+ *              sections 格式速查 (format table) and 伪量化实现 (the fake-quant
+ *              module that quantizes and immediately dequantizes in float32).
+ *   [BYTES]    "14. 量化：让每一步搬更少的字节": sections 量化在做什么
+ *              (uniform quantizer and its worked example) and the table of new
+ *              low-bit formats (FP8 / FP4 / micro-scaling).
+ *   [NOTES]    "LLM 推理优化 · 量化（Quantization）系统学习笔记": §4.2 (bit
+ *              layouts) and §5.1 (symmetric and asymmetric formulas).
+ *
+ * All arithmetic is IEEE binary32, round-to-nearest-even, with subnormals,
+ * exactly as [DEPLOY] computes on float32 tensors.  Every division is a true
+ * IEEE division.  Build with -O2 -ffp-contract=off, no fast-math.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* Number formats                                                            */
+/* ------------------------------------------------------------------------ */
+
+/* E4M3 [DEPLOY 格式速查; NOTES §4.2]: 1 sign, 4 exponent, 3 mantissa bits, no
+ * infinities and a single NaN pattern per sign (exponent and mantissa all
+ * ones), largest finite value 448.  448 = 1.75 * 2^8 fixes the exponent bias at
+ * 7; exponent field 0 holds the subnormals m * 2^-9. */
+float orc_e4m3_decode(uint8_t code) {
+  int sign = code >> 7, e = (code >> 3) & 15, m = code & 7;
+  float mag;
+  if (e == 15 && m == 7) return sign ? -NAN : NAN;
+  if (e == 0)
+    mag = ldexpf((float)m, -9);
+  else
+    mag = ldexpf((float)(8 + m), e - 10);
+  return sign ? -mag : mag;
+}
+
+/* E4M3 rounding: the nearest finite E4M3 value, ties to the code with an even
+ * mantissa (round-to-nearest-even), sign bit copied from y.  This is the
+ * float32 -> float8_e4m3fn cast that [DEPLOY 伪量化实现] applies after clamping
+ * to +-448.  The search runs over every non-negative finite code.  Distances
+ * are taken in double: for the two codes that bracket |y| the difference is
+ * exact, which is all the decision needs. */
+uint8_t orc_e4m3_encode(float y) {
+  double a = fabs((double)y);
+  int best = 0;
+  double bestd = a; /* distance to code 0 (value 0) */
+  for (int c = 1; c <= 0x7E; ++c) {
+    double d = fabs(a - (double)orc_e4m3_decode((uint8_t)c));
+    if (d < bestd || (d == bestd && (c & 1) == 0)) {
+      best = c;
+      bestd = d;
+    }
+  }
+  return (uint8_t)((signbit(y) ? 0x80 : 0x00) | best);
+}
+
+/* E2M1 [DEPLOY 格式速查, 伪量化实现; BYTES 新格式]: the non-negative values are
+ * 0, 0.5, 1, 1.5, 2, 3, 4, 6.  The nibble holds the sign in bit 3 and the index
+ * into this list in bits 0..2 (with exponent bias 1 the index is exactly the
+ * 3-bit exponent:mantissa field). */
+static const float E2M1_VALUES[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+
+float orc_e2m1_decode(uint8_t nibble) {
+  float v = E2M1_VALUES[nibble & 7];
+  return (nibble & 8) ? -v : v;
+}
+
+/* E2M1 rounding as [DEPLOY 伪量化实现] defines it: the float32 distance from |y|
+ * to each of the eight values, the first index of the smallest distance wins
+ * (so ties go to the smaller magnitude), and the sign is that of y with
+ * sign(0) = 0, so -0.0 gives +0 and a small negative y gives -0. */
+uint8_t orc_e2m1_encode(float y) {
+  float a = fabsf(y);
+  int best = 0;
+  float bestd = fabsf(a - E2M1_VALUES[0]);
+  for (int i = 1; i < 8; ++i) {
+    float d = fabsf(a - E2M1_VALUES[i]);
+    if (d < bestd) {
+      best = i;
+      bestd = d;
+    }
+  }
+  return (uint8_t)(((y < 0.0f) ? 8 : 0) | best);
+}
+
+/* bf16 [NOTES §4.2]: the upper 16 bits of a binary32.  Rounding: of the two
+ * bf16 values that bracket v (the truncation and its successor in magnitude)
+ * take the nearer, on a tie the one with an even last bit. */
+uint16_t orc_bf16_round(float v) {
+  uint32_t b;
+  memcpy(&b, &v, 4);
+  uint32_t lo = b & 0xFFFF0000u, rem = b & 0x0000FFFFu;
+  if (rem > 0x8000u || (rem == 0x8000u && (lo & 0x00010000u))) lo += 0x00010000u;
+  return (uint16_t)(lo >> 16);
+}
+
+float orc_bf16_to_f32(uint16_t h) {
+  uint32_t b = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &b, 4);
+  return f;
+}
+
+/* Uniform quantizer [BYTES 量化在做什么; NOTES §5.1]: the stored integer is the
+ * rounded quotient x/s, shifted by the zero-point z in the asymmetric form.
+ * Rounding is IEEE round-to-nearest-even on the float32 quotient. */
+float orc_uniform_code(float x, float s, float z) { return rintf(x / s) + z; }
+
+/* ------------------------------------------------------------------------ */
+/* Helpers                                                                   */
+/* ------------------------------------------------------------------------ */
+
+static float ld(const void* x, int dtype, int64_t i) {
+  if (dtype == ORC_BF16) return orc_bf16_to_f32(((const uint16_t*)x)[i]);
+  return ((const float*)x)[i];
+}
+
+static void st(void* out, int dtype, int64_t i, float v) {
+  if (dtype == ORC_BF16)
+    ((uint16_t*)out)[i] = orc_bf16_round(v);
+  else
+    ((float*)out)[i] = v;
+}
+
+static float clampf(float v, float lo, float hi) { return fminf(fmaxf(v, lo), hi); }
+
+static void put_nibble(uint8_t* buf, int64_t i, uint8_t v) {
+  uint8_t* p = buf + (i >> 1);
+  if (i & 1)
+    *p = (uint8_t)((*p & 0x0F) | ((v & 0x0F) << 4));
+  else
+    *p = (uint8_t)((*p & 0xF0) | (v & 0x0F));
+}
+
+static uint8_t get_nibble(const uint8_t* buf, int64_t i) {
+  uint8_t b = buf[i >> 1];
+  return (i & 1) ? (uint8_t)(b >> 4) : (uint8_t)(b & 0x0F);
+}
+
+static int bad_dims(int64_t batch, int64_t rows, int64_t cols) {
+  return batch < 0 || rows < 0 || cols < 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* FP8 E4M3 [DEPLOY 伪量化实现]                                              */
+/* ------------------------------------------------------------------------ */
+
+/* One scope: its scale is max(amax, 1e-12) / 448, each element becomes the
+ * E4M3 code of clamp(x / scale, -448, 448). */
+static float fp8_scale(float amax) { return fmaxf(amax, 1e-12f) / 448.0f; }
+
+static uint8_t fp8_code(float x, float s) { return orc_e4m3_encode(clampf(x / s, -448.0f, 448.0f)); }
+
+/* Index of the scale that element (b, r, c) uses; -1 for a rejected shape. */
+static int64_t fp8_scale_index(int gran, int64_t rows, int64_t cols, int64_t b, int64_t r,
+                               int64_t c) {
+  switch (gran) {
+    case ORC_TENSOR:
+      return b;
+    case ORC_ROW:
+      return b * rows + r;
+    case ORC_BLK_1x128:
+      return (b * rows + r) * (cols / 128) + c / 128;
+    case ORC_BLK_128x128: {
+      int64_t br = rows < 128 ? rows : 128;
+      return (b * (rows / br) + r / br) * (cols / 128) + c / 128;
+    }
+  }
+  return -1;
+}
+
+static int fp8_shape_ok(int gran, int64_t rows, int64_t cols) {
+  switch (gran) {
+    case ORC_TENSOR:
+    case ORC_ROW:
+      return 1;
+    case ORC_BLK_1x128:
+      return cols % 128 == 0;
+    case ORC_BLK_128x128: {
+      int64_t br = rows < 128 ? rows : 128;
+      return cols % 128 == 0 && (rows == 0 || rows % br == 0);
+    }
+  }
+  return 0;
+}
+
+static int64_t fp8_num_scales(int gran, int64_t batch, int64_t rows, int64_t cols) {
+  switch (gran) {
+    case ORC_TENSOR:
+      return batch;
+    case ORC_ROW:
+      return batch * rows;
+    case ORC_BLK_1x128:
+      return batch * rows * (cols / 128);
+    case ORC_BLK_128x128: {
+      int64_t br = rows < 128 ? rows : 128;
+      return rows == 0 ? 0 : batch * (rows / br) * (cols / 128);
+    }
+  }
+  return 0;
+}
+
+int orc_fp8_quantize(const void* x, int dtype, int64_t batch, int64_t rows, int64_t cols,
+                     int gran, uint8_t* codes, float* scales) {
+  if (bad_dims(batch, rows, cols) || gran < ORC_TENSOR || gran > ORC_BLK_128x128) return -4;
+  if (!fp8_shape_ok(gran, rows, cols)) return -4;
+  int64_t ns = fp8_num_scales(gran, batch, rows, cols);
+  /* pass 1: amax of every scope (|x| >= 0, so 0 is the neutral element) */
+  for (int64_t i = 0; i < ns; ++i) scales[i] = 0.0f;
+  for (int64_t b = 0; b < batch; ++b)
+    for (int64_t r = 0; r < rows; ++r)
+      for (int64_t c = 0; c < cols; ++c) {
+        int64_t si = fp8_scale_index(gran, rows, cols, b, r, c);
+        scales[si] = fmaxf(scales[si], fabsf(ld(x, dtype, (b * rows + r) * cols + c)));
+      }
+  for (int64_t i = 0; i < ns; ++i) scales[i] = fp8_scale(scales[i]);
+  /* pass 2: codes */
+  for (int64_t b = 0; b < batch; ++b)
+    for (int64_t r = 0; r < rows; ++r)
+      for (int64_t c = 0; c < cols; ++c) {
+        int64_t i = (b * rows + r) * cols + c;
+        codes[i] = fp8_code(ld(x, dtype, i), scales[fp8_scale_index(gran, rows, cols, b, r, c)]);
+      }
+  return 0;
+}
+
+/* Dequantization is the decoded E4M3 value times its scope's scale. */
+int orc_fp8_dequantize(const uint8_t* codes, const float* scales, int64_t batch, int64_t rows,
+                       int64_t cols, int gran, int out_dtype, void* out) {
+  if (bad_dims(batch, rows, cols) || gran < ORC_TENSOR || gran > ORC_BLK_128x128) return -4;
+  if (!fp8_shape_ok(gran, rows, cols)) return -4;
+  for (int64_t b = 0; b < batch; ++b)
+    for (int64_t r = 0; r < rows; ++r)
+      for (int64_t c = 0; c < cols; ++c) {
+        int64_t i = (b * rows + r) * cols + c;
+        float s = scales[fp8_scale_index(gran, rows, cols, b, r, c)];
+        st(out, out_dtype, i, orc_e4m3_decode(codes[i]) * s);
+      }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* MXFP4 [DEPLOY 伪量化实现; BYTES 新格式]                                   */
+/* ------------------------------------------------------------------------ */
+
+/* Each run of 32 elements along the last dimension shares the scale
+ * 2^(floor(log2(max(amax, 1e-12))) - 2): E2M1's largest exponent is 2, so the
+ * block maximum lands in [4, 8) before the clamp to 6.  floor(log2 a) is read
+ * exactly from the binary exponent (frexp gives a = f * 2^e, f in [0.5, 1)).
+ * The E8M0 byte stores the exponent with bias 127. */
+int orc_mxfp4_quantize(const void* x, int dtype, int64_t batch, int64_t rows, int64_t cols,
+                       uint8_t* codes, uint8_t* scales) {
+  if (bad_dims(batch, rows, cols) || cols % 32 != 0) return -4;
+  int64_t nblk = batch * rows * (cols / 32);
+  for (int64_t k = 0; k < nblk; ++k) {
+    float amax = 0.0f;
+    for (int64_t j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(ld(x, dtype, k * 32 + j)));
+    int e;
+    frexpf(fmaxf(amax, 1e-12f), &e);
+    int X = (e - 1) - 2;
+    float scale = ldexpf(1.0f, X);
+    scales[k] = (uint8_t)(X + 127);
+    for (int64_t j = 0; j < 32; ++j) {
+      float y = clampf(ld(x, dtype, k * 32 + j) / scale, -6.0f, 6.0f);
+      put_nibble(codes, k * 32 + j, orc_e2m1_encode(y));
+    }
+  }
+  return 0;
+}
+
+int orc_mxfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t batch,
+                         int64_t rows, int64_t cols, int out_dtype, void* out) {
+  if (bad_dims(batch, rows, cols) || cols % 32 != 0) return -4;
+  int64_t n = batch * rows * cols;
+  for (int64_t i = 0; i < n; ++i) {
+    float scale = ldexpf(1.0f, (int)scales[i / 32] - 127);
+    st(out, out_dtype, i, orc_e2m1_decode(get_nibble(codes, i)) * scale);
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* NVFP4 [DEPLOY 伪量化实现; BYTES 新格式]                                   */
+/* ------------------------------------------------------------------------ */
+
+/* Two levels.  The tensor scale is max(amax_tensor, 1e-12) / (448 * 6).  Each
+ * run of 16 elements stores the E4M3 code of (amax_block / 6) / tensor_scale
+ * (two divisions, in that order).  The elements are rounded to E2M1 against
+ * max(decoded block scale, 1e-12) * tensor_scale. */
+static float nv_effective_scale(uint8_t code, float gs) {
+  return fmaxf(orc_e4m3_decode(code), 1e-12f) * gs;
+}
+
+int orc_nvfp4_quantize(const void* x, int dtype, int64_t batch, int64_t rows, int64_t cols,
+                       uint8_t* codes, uint8_t* scales, float* tensor_scale) {
+  if (bad_dims(batch, rows, cols) || cols % 16 != 0) return -4;
+  int64_t per = rows * cols;
+  for (int64_t b = 0; b < batch; ++b) {
+    const int64_t base = b * per;
+    float amax_t = 0.0f;
+    for (int64_t i = 0; i < per; ++i) amax_t = fmaxf(amax_t, fabsf(ld(x, dtype, base + i)));
+    float gs = fmaxf(amax_t, 1e-12f) / (448.0f * 6.0f);
+    tensor_scale[b] = gs;
+    for (int64_t k = 0; k < per / 16; ++k) {
+      const int64_t e0 = base + k * 16;
+      float amax_b = 0.0f;
+      for (int64_t j = 0; j < 16; ++j) amax_b = fmaxf(amax_b, fabsf(ld(x, dtype, e0 + j)));
+      uint8_t bs = orc_e4m3_encode(amax_b / 6.0f / gs);
+      scales[e0 / 16] = bs;
+      float s = nv_effective_scale(bs, gs);
+      for (int64_t j = 0; j < 16; ++j) {
+        float y = clampf(ld(x, dtype, e0 + j) / s, -6.0f, 6.0f);
+        put_nibble(codes, e0 + j, orc_e2m1_encode(y));
+      }
+    }
+  }
+  return 0;
+}
+
+int orc_nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
+                         int64_t batch, int64_t rows, int64_t cols, int out_dtype, void* out) {
+  if (bad_dims(batch, rows, cols) || cols % 16 != 0) return -4;
+  int64_t per = rows * cols;
+  for (int64_t b = 0; b < batch; ++b)
+    for (int64_t i = 0; i < per; ++i) {
+      int64_t g = b * per + i;
+      float s = nv_effective_scale(scales[g / 16], tensor_scale[b]);
+      st(out, out_dtype, g, orc_e2m1_decode(get_nibble(codes, g)) * s);
+    }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* INT4 group-128 asymmetric [DEPLOY 格式速查; BYTES 量化在做什么; NOTES §5.1] */
+/* ------------------------------------------------------------------------ */
+
+/* Integers -8..7, one 2-byte (bf16) scale and one zero-point per run of 128
+ * elements.  The range [lo, hi] of a group is widened to contain 0; its 15
+ * steps give s = bf16(max(hi - lo, 1e-12) / 15), and the rounded s is the one
+ * used.  The zero-point maps lo to -8: z = -8 - round(lo / s).  An element
+ * becomes clamp(round(x / s) + z, -8, 7) and reads back as (q - z) * s. */
+static int64_t int4_zero_bytes_per_row(int64_t cols) { return (cols / 128 + 1) / 2; }
+
+int orc_int4_quantize(const void* x, int dtype, int64_t batch, int64_t rows, int64_t cols,
+                      uint8_t* codes, uint16_t* scales, uint8_t* zeros) {
+  if (bad_dims(batch, rows, cols) || cols % 128 != 0) return -4;
+  const int64_t G = cols / 128, zb = int4_zero_bytes_per_row(cols);
+  for (int64_t row = 0; row < batch * rows; ++row) {
+    for (int64_t i = 0; i < zb; ++i) zeros[row * zb + i] = 0;
+    for (int64_t g = 0; g < G; ++g) {
+      const int64_t e0 = row * cols + g * 128;
+      float lo = 0.0f, hi = 0.0f;
+      for (int64_t j = 0; j < 128; ++j) {
+        float v = ld(x, dtype, e0 + j);
+        lo = fminf(lo, v);
+        hi = fmaxf(hi, v);
+      }
+      uint16_t sb = orc_bf16_round(fmaxf(hi - lo, 1e-12f) / 15.0f);
+      float s = orc_bf16_to_f32(sb);
+      float z = clampf(-8.0f - rintf(lo / s), -8.0f, 7.0f);
+      scales[row * G + g] = sb;
+      put_nibble(zeros + row * zb, g, (uint8_t)((int)z & 0x0F));
+      for (int64_t j = 0; j < 128; ++j) {
+        float q = clampf(orc_uniform_code(ld(x, dtype, e0 + j), s, z), -8.0f, 7.0f);
+        put_nibble(codes, e0 + j, (uint8_t)((int)q & 0x0F));
+      }
+    }
+  }
+  return 0;
+}
+
+static int sext4(uint8_t v) { return (v & 8) ? (int)v - 16 : (int)v; }
+
+int orc_int4_dequantize(const uint8_t* codes, const uint16_t* scales, const uint8_t* zeros,
+                        int64_t batch, int64_t rows, int64_t cols, int out_dtype, void* out) {
+  if (bad_dims(batch, rows, cols) || cols % 128 != 0) return -4;
+  const int64_t G = cols / 128, zb = int4_zero_bytes_per_row(cols);
+  for (int64_t row = 0; row < batch * rows; ++row)
+    for (int64_t c = 0; c < cols; ++c) {
+      int64_t i = row * cols + c, g = c / 128;
+      int q = sext4(get_nibble(codes, i));
+      int z = sext4(get_nibble(zeros + row * zb, g));
+      float s = orc_bf16_to_f32(scales[row * G + g]);
+      st(out, out_dtype, i, (float)(q - z) * s);
+    }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* FP8 KV-cache write [DEPLOY 伪量化实现, the FP8 KV cache class]             */
+/* ------------------------------------------------------------------------ */
+
+/* Each write quantizes K and V with the per-tensor FP8 rule, so every layer
+ * gets one scale of its own for K and one for V, set by the data written. */
+int orc_kv_write_fp8(const void* k, const void* v, int dtype, int64_t layers,
+                     int64_t elems_per_layer, uint8_t* k_codes, uint8_t* v_codes,
+                     float* k_scales, float* v_scales) {
+  int rc = orc_fp8_quantize(k, dtype, layers, 1, elems_per_layer, ORC_TENSOR, k_codes, k_scales);
+  if (rc) return rc;
+  return orc_fp8_quantize(v, dtype, layers, 1, elems_per_layer, ORC_TENSOR, v_codes, v_scales);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Array forms of the codecs (for exhaustive tests)                          */
+/* ------------------------------------------------------------------------ */
+
+void orc_e4m3_encode_n(const float* y, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_encode(y[i]);
+}
+
+void orc_e2m1_encode_n(const float* y, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_e2m1_encode(y[i]);
+}
+
+void orc_bf16_round_n(const float* v, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16_round(v[i]);
+}
