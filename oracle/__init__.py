@@ -257,18 +257,15 @@ def nvfp4_dequantize(codes, scales, gs, out_bf16=False):
     return out
 
 
-def int4_zero_bytes_per_row(cols: int) -> int:
-    return (cols // 128 + 1) // 2
-
-
 def int4_quantize(x, bf16=None):
-    """-> (codes u8 [b, r, c/2], scales bf16-bits u16 [b, r, c/128], zeros u8 [b, r, ceil(G/2)])."""
+    """-> (codes u8 [b, r, c/2], scales bf16-bits u16 [b, r, c/128],
+    zeros u8 [ceil(b*r*c/128 / 2)]: two signed nibbles per byte over the flat group index)."""
     x, dt, b, r, c = _as_input(x, bf16)
     if c % 128:
         _check(-4, "int4_quantize")
     codes = np.zeros((b, r, c // 2), np.uint8)
     scales = np.empty((b, r, c // 128), np.uint16)
-    zeros = np.zeros((b, r, int4_zero_bytes_per_row(c)), np.uint8)
+    zeros = np.zeros(((b * r * (c // 128) + 1) // 2,), np.uint8)
     _check(lib().orc_int4_quantize(_p(x), dt, b, r, c, _p(codes), _p(scales), _p(zeros)),
            "int4_quantize")
     return codes, scales, zeros

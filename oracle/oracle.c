@@ -73,12 +73,13 @@ float orc_e2m1_decode(uint8_t nibble) {
   return (nibble & 8) ? -v : v;
 }
 
-/* E2M1 rounding as [DEPLOY 伪量化实现] defines it: the float32 distance from |y|
- * to each of the eight values, the first index of the smallest distance wins
- * (so ties go to the smaller magnitude), and the sign is that of y with
- * sign(0) = 0, so -0.0 gives +0 and a small negative y gives -0. */
+/* E2M1 rounding as [DEPLOY 伪量化实现] defines it: y is clamped to [-6, 6],
+ * then the float32 distance from |y| to each of the eight values is taken and
+ * the first index of the smallest distance wins (so ties go to the smaller
+ * magnitude); the sign is that of y with sign(0) = 0, so -0.0 gives +0 and a
+ * small negative y gives -0. */
 uint8_t orc_e2m1_encode(float y) {
-  float a = fabsf(y);
+  float a = fabsf(fminf(fmaxf(y, -6.0f), 6.0f));
   int best = 0;
   float bestd = fabsf(a - E2M1_VALUES[0]);
   for (int i = 1; i < 8; ++i) {
@@ -347,16 +348,14 @@ int orc_nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const floa
  * steps give s = bf16(max(hi - lo, 1e-12) / 15), and the rounded s is the one
  * used.  The zero-point maps lo to -8: z = -8 - round(lo / s).  An element
  * becomes clamp(round(x / s) + z, -8, 7) and reads back as (q - z) * s. */
-static int64_t int4_zero_bytes_per_row(int64_t cols) { return (cols / 128 + 1) / 2; }
-
 int orc_int4_quantize(const void* x, int dtype, int64_t batch, int64_t rows, int64_t cols,
                       uint8_t* codes, uint16_t* scales, uint8_t* zeros) {
   if (bad_dims(batch, rows, cols) || cols % 128 != 0) return -4;
-  const int64_t G = cols / 128, zb = int4_zero_bytes_per_row(cols);
+  const int64_t G = cols / 128, ngroups = batch * rows * G;
+  for (int64_t i = 0; i < (ngroups + 1) / 2; ++i) zeros[i] = 0;
   for (int64_t row = 0; row < batch * rows; ++row) {
-    for (int64_t i = 0; i < zb; ++i) zeros[row * zb + i] = 0;
     for (int64_t g = 0; g < G; ++g) {
-      const int64_t e0 = row * cols + g * 128;
+      const int64_t gi = row * G + g, e0 = gi * 128;
       float lo = 0.0f, hi = 0.0f;
       for (int64_t j = 0; j < 128; ++j) {
         float v = ld(x, dtype, e0 + j);
@@ -366,8 +365,8 @@ int orc_int4_quantize(const void* x, int dtype, int64_t batch, int64_t rows, int
       uint16_t sb = orc_bf16_round(fmaxf(hi - lo, 1e-12f) / 15.0f);
       float s = orc_bf16_to_f32(sb);
       float z = clampf(-8.0f - rintf(lo / s), -8.0f, 7.0f);
-      scales[row * G + g] = sb;
-      put_nibble(zeros + row * zb, g, (uint8_t)((int)z & 0x0F));
+      scales[gi] = sb;
+      put_nibble(zeros, gi, (uint8_t)((int)z & 0x0F));
       for (int64_t j = 0; j < 128; ++j) {
         float q = clampf(orc_uniform_code(ld(x, dtype, e0 + j), s, z), -8.0f, 7.0f);
         put_nibble(codes, e0 + j, (uint8_t)((int)q & 0x0F));
@@ -382,15 +381,14 @@ static int sext4(uint8_t v) { return (v & 8) ? (int)v - 16 : (int)v; }
 int orc_int4_dequantize(const uint8_t* codes, const uint16_t* scales, const uint8_t* zeros,
                         int64_t batch, int64_t rows, int64_t cols, int out_dtype, void* out) {
   if (bad_dims(batch, rows, cols) || cols % 128 != 0) return -4;
-  const int64_t G = cols / 128, zb = int4_zero_bytes_per_row(cols);
-  for (int64_t row = 0; row < batch * rows; ++row)
-    for (int64_t c = 0; c < cols; ++c) {
-      int64_t i = row * cols + c, g = c / 128;
-      int q = sext4(get_nibble(codes, i));
-      int z = sext4(get_nibble(zeros + row * zb, g));
-      float s = orc_bf16_to_f32(scales[row * G + g]);
-      st(out, out_dtype, i, (float)(q - z) * s);
-    }
+  const int64_t n = batch * rows * cols;
+  for (int64_t i = 0; i < n; ++i) {
+    const int64_t gi = i / 128;
+    int q = sext4(get_nibble(codes, i));
+    int z = sext4(get_nibble(zeros, gi));
+    float s = orc_bf16_to_f32(scales[gi]);
+    st(out, out_dtype, i, (float)(q - z) * s);
+  }
   return 0;
 }
 

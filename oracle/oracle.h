@@ -19,7 +19,8 @@
  *   MXFP4 scales   u8 E8M0 [batch, rows, cols/32]
  *   NVFP4 scales   u8 E4M3 [batch, rows, cols/16] plus f32 tensor scale [batch]
  *   INT4 scales    bf16 bits [batch, rows, cols/128]; zero-points as signed
- *                  nibbles [batch, rows, ceil((cols/128)/2)]
+ *                  nibbles, two per byte over the flat group index
+ *                  (ceil(batch*rows*cols/128 / 2) bytes)
  *
  * Return value of the quantizers: 0 on success, -4 for a shape that the
  * pages' reshape would reject.

@@ -162,6 +162,8 @@ def test_e2m1_sign_rule(orc):
     assert orc.e2m1_encode(-0.1) == 8        # negative, rounds to zero -> -0
     assert orc.e2m1_encode(-1e-40) == 8
     assert orc.e2m1_encode(6.0) == 7 and orc.e2m1_encode(-6.0) == 15
+    # the clamp to +-6 comes first: huge values saturate
+    assert orc.e2m1_encode(1e30) == 7 and orc.e2m1_encode(-1e30) == 15
 
 
 def test_e2m1_brute_force_exact_rationals(orc):

@@ -348,7 +348,7 @@ def test_int4_groups(orc, dtype):
     x, isb = make(shape, seed=12, scale=0.02, dtype=dtype)
     xv = values(x, isb).reshape(shape)
     codes, scales, zeros = orc.int4_quantize(x.reshape(shape), bf16=isb)
-    assert codes.shape == (2, 8, 192) and scales.shape == (2, 8, 3) and zeros.shape == (2, 8, 2)
+    assert codes.shape == (2, 8, 192) and scales.shape == (2, 8, 3) and zeros.shape == (24,)
     deq = orc.int4_dequantize(codes, scales, zeros)
     G = 3
     for row in range(16):
@@ -359,7 +359,8 @@ def test_int4_groups(orc, dtype):
             s_bits = torch_bf16_bits(np.array([np.maximum(hi - lo, f32(1e-12)) / f32(15)]))[0]
             assert scales.reshape(16, G)[row, g] == s_bits
             s = widen(np.array([s_bits]))[0]
-            z_nib = int(zeros.reshape(16, 2)[row, g // 2] >> (4 * (g % 2))) & 15
+            gi = row * G + g                       # flat group index
+            z_nib = int(zeros[gi // 2] >> (4 * (gi % 2))) & 15
             z = z_nib - 16 if z_nib & 8 else z_nib
             assert z == -8 - int(np.rint(lo / s))
             q = []
@@ -383,7 +384,7 @@ def test_int4_special_groups(orc):
     codes, scales, zeros = orc.int4_quantize(x)
     deq = orc.int4_dequantize(codes, scales, zeros)
     assert np.all(deq[0, 0] == 0)
-    z = [(zeros[0, r, 0] & 15) for r in range(3)]
+    z = [(int(zeros[r // 2]) >> (4 * (r % 2))) & 15 for r in range(3)]
     assert z[0] == 8 and z[1] == 8                   # z = -8 (nibble 0x8)
     assert nib(codes, 128 + 127) == 7                # hi -> 7
     assert nib(codes, 256) == 8                      # lo -> -8
@@ -402,8 +403,8 @@ def test_int4_range_always_contains_zero(orc):
     s = widen(scales)[0]
     want = torch_bf16_bits(np.array([f32(1.5) / f32(15)]))[0]
     assert scales[0, 0, 0] == want and scales[0, 1, 0] == want
-    assert zeros[0, 0, 0] & 15 == 8                                      # lo = 0: z = -8
-    assert zeros[0, 1, 0] & 15 == (-8 - int(np.rint(f32(-1.5) / s[1, 0]))) & 15   # = 7
+    assert zeros[0] & 15 == 8                                            # lo = 0: z = -8
+    assert zeros[0] >> 4 == (-8 - int(np.rint(f32(-1.5) / s[1, 0]))) & 15  # = 7
     q0 = nib(codes, 0)                                                   # 0.5 / 0.1 = 5 -> -3
     assert (q0 - 16 if q0 & 8 else q0) == int(np.rint(f32(0.5) / s[0, 0])) - 8
     assert nib(codes, 128) == 8                                          # -1.5 -> -8
