@@ -1,0 +1,155 @@
+/*
+ * pqb -- block-scaled quantize-pack / dequantize engine for MI355X (gfx950).
+ *
+ * C ABI.  Every pointer named x, codes, scales, aux, out, k, v, workspace is a
+ * device pointer owned by the caller; the library never allocates, frees or
+ * synchronizes.  Every call enqueues its kernels on `stream` (a hipStream_t,
+ * NULL for the default stream) and returns at once; results are ready when
+ * the stream reaches that point.  Calls are thread-safe: the library keeps no
+ * mutable global state.
+ *
+ * Formats and the passages that define them (page title, section):
+ *   "量化部署实战" (quantization deployment in practice), section 伪量化实现
+ *   (fake-quant implementation): FP8 E4M3 with per-tensor, per-row and
+ *   block (128x128 or 1x128) scales, each scale max(amax, 1e-12)/448;
+ *   MXFP4 (32-element blocks, scale 2^(floor(log2 max(amax,1e-12)) - 2));
+ *   NVFP4 (16-element blocks, E4M3 block scale of (amax_block/6)/gs with tensor
+ *   scale gs = max(amax_tensor, 1e-12)/(448*6)); the FP8 KV cache that
+ *   quantizes K and V per tensor on every write.  Same page, 格式速查 (format
+ *   table): INT4 integers -8..7 with one scale (+ zero-point) per 128.
+ *   "14. 量化：让每一步搬更少的字节", section 量化在做什么: the uniform
+ *   quantizer q = round(x/s) and its 2-byte scale per 128 weights.
+ *   "LLM 推理优化 · 量化（Quantization）系统学习笔记" §5.1: asymmetric
+ *   q = clamp(round(x/s) + z, qmin, qmax).
+ *
+ * Arithmetic: IEEE binary32 with round-to-nearest-even and subnormals; bf16
+ * inputs are widened exactly.  Every quotient x/s is the correctly rounded
+ * one.  Element rounding: E4M3 round-to-nearest-even after the clamp to +-448;
+ * E2M1 to the nearest of {0, .5, 1, 1.5, 2, 3, 4, 6} with ties to the smaller
+ * magnitude, sign bit set for negative values (so -0.0 gives +0); INT4
+ * q = clamp(rint(x/s) + z, -8, 7).  Inputs must be finite.
+ *
+ * Shapes.  A tensor is [batch, rows, cols], contiguous and row-major.
+ * "Per tensor" (FP8 TENSOR, the NVFP4 tensor scale) means per batch slice.
+ *
+ * Valid (format, granularity) pairs and the layouts they produce:
+ *   FP8_E4M3 x TENSOR     codes u8 [b, r, c]      scales f32 [b]
+ *   FP8_E4M3 x ROW        codes u8 [b, r, c]      scales f32 [b, r]
+ *   FP8_E4M3 x BLK_1x128  codes u8 [b, r, c]      scales f32 [b, r, c/128]
+ *   FP8_E4M3 x BLK_128x128 codes u8 [b, r, c]     scales f32 [b, r/br, c/128],
+ *                                                 br = min(128, r)
+ *   MXFP4 x BLK_32        codes u8 [b, r, c/2]    scales u8 E8M0 [b, r, c/32]
+ *                                                 (exponent + 127)
+ *   NVFP4 x BLK_16        codes u8 [b, r, c/2]    scales u8 E4M3 [b, r, c/16]
+ *                                                 aux f32 tensor scale [b]
+ *   INT4_ASYM x GRP_128   codes u8 [b, r, c/2]    scales bf16 [b, r, c/128]
+ *                                                 aux u8 zero-points, two per
+ *                                                 byte over the flat group
+ *                                                 index (ceil(b*r*c/256) bytes)
+ * 4-bit codes: element 2i in the low nibble of byte i.  INT4 codes and
+ * zero-points are two's-complement nibbles; dequant is (q - z) * s.
+ *
+ * Shape rules: 1x128 and GRP_128 need c % 128 == 0; 128x128 needs c % 128 == 0
+ * and r <= 128 or r % 128 == 0; BLK_32 needs c % 32 == 0; BLK_16 needs
+ * c % 16 == 0.  An empty tensor (b*r*c == 0) is accepted and launches nothing.
+ *
+ * Alignment: x, codes and out must be 16-byte aligned; scales and aux 4-byte
+ * aligned (2-byte for INT4 scales, 1 for byte scales and zero-points);
+ * workspace 16-byte aligned.
+ *
+ * Errors: host-detectable problems return a negative status before anything
+ * is enqueued.  A failed launch returns PQB_ERR_HIP.  Faults inside a kernel
+ * surface at the caller's next synchronization.
+ */
+#ifndef PQB_H
+#define PQB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PQB_ABI_VERSION 1
+
+typedef enum pqb_status {
+  PQB_OK = 0,
+  PQB_ERR_NULL = -1,      /* a required pointer is NULL */
+  PQB_ERR_ENUM = -2,      /* unknown dtype, format or granularity */
+  PQB_ERR_COMBO = -3,     /* format and granularity do not go together */
+  PQB_ERR_SHAPE = -4,     /* negative size, or a shape the block rules reject */
+  PQB_ERR_ALIGN = -5,     /* a pointer breaks the alignment rules */
+  PQB_ERR_WORKSPACE = -6, /* workspace smaller than pqb_query_sizes asks */
+  PQB_ERR_HIP = -7        /* the HIP runtime refused a launch */
+} pqb_status;
+
+typedef enum pqb_dtype { PQB_F32 = 0, PQB_BF16 = 1 } pqb_dtype;
+
+typedef enum pqb_format {
+  PQB_FP8_E4M3 = 0,
+  PQB_MXFP4 = 1,
+  PQB_NVFP4 = 2,
+  PQB_INT4_ASYM = 3
+} pqb_format;
+
+typedef enum pqb_gran {
+  PQB_TENSOR = 0,
+  PQB_ROW = 1,
+  PQB_BLK_1x128 = 2,
+  PQB_BLK_128x128 = 3,
+  PQB_BLK_32 = 4,
+  PQB_BLK_16 = 5,
+  PQB_GRP_128 = 6
+} pqb_gran;
+
+/* Byte sizes of the buffers a (format, granularity, shape) needs.  `aux` is 0
+ * when unused; `workspace` is the scratch that pqb_quantize needs (0 for the
+ * one-pass formats).  Sizes do not depend on the input dtype. */
+typedef struct pqb_sizes {
+  size_t codes, scales, aux, workspace;
+} pqb_sizes;
+
+pqb_status pqb_query_sizes(pqb_format fmt, pqb_gran gran, int64_t batch, int64_t rows,
+                           int64_t cols, pqb_sizes* out);
+
+/* Quantize x ([batch, rows, cols] of `dtype`) into codes, scales and aux with
+ * the layouts above.  The two-pass formats (FP8 TENSOR, NVFP4) first reduce the
+ * per-tensor amax into `workspace` (at least pqb_query_sizes().workspace
+ * bytes; its contents on entry do not matter and are overwritten). */
+pqb_status pqb_quantize(const void* x, pqb_dtype dtype, int64_t batch, int64_t rows, int64_t cols,
+                        pqb_format fmt, pqb_gran gran, void* codes, void* scales, void* aux,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Inverse of pqb_quantize: out[b, r, c] = decoded code times its scale(s),
+ * as float32 or rounded to bf16 (round-to-nearest-even) by `out_dtype`.
+ * FP8: dec(code) * s.  MXFP4: +-V * 2^(e8m0 - 127) (exact).  NVFP4:
+ * +-V * (max(dec(block scale), 1e-12) * gs).  INT4: (q - z) * s (exact). */
+pqb_status pqb_dequantize(const void* codes, const void* scales, const void* aux, pqb_format fmt,
+                          pqb_gran gran, int64_t batch, int64_t rows, int64_t cols,
+                          pqb_dtype out_dtype, void* out, void* stream);
+
+/* FP8 KV-cache write: K and V are [layers, elems_per_layer] of `dtype`.  Each
+ * (layer, K) and (layer, V) slice gets its own per-tensor FP8 scale (written
+ * to k_scales[layer], v_scales[layer]) and its E4M3 codes (k_codes, v_codes,
+ * same layout as the input).  Workspace: pqb_kv_workspace_bytes(). */
+size_t pqb_kv_workspace_bytes(int64_t layers, int64_t elems_per_layer);
+pqb_status pqb_kv_write_fp8(const void* k, const void* v, pqb_dtype dtype, int64_t layers,
+                            int64_t elems_per_layer, uint8_t* k_codes, uint8_t* v_codes,
+                            float* k_scales, float* v_scales, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* Element codecs exposed for testing the rounding rules on arrays of float32:
+ * E4M3 of y (round-to-nearest-even; |y| must not exceed 464) into one byte
+ * per element; E2M1 of y (ties to the smaller magnitude, saturating at 6)
+ * into one nibble per byte (low 4 bits). */
+pqb_status pqb_encode_e4m3(const float* y, int64_t n, uint8_t* out, void* stream);
+pqb_status pqb_encode_e2m1(const float* y, int64_t n, uint8_t* out, void* stream);
+
+const char* pqb_status_string(pqb_status s);
+int pqb_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PQB_H */

@@ -1,0 +1,275 @@
+// The C ABI declared in include/pqb.h: argument validation, buffer sizes and
+// dispatch to the kernel launchers.  Nothing here allocates or synchronizes.
+#include <hip/hip_runtime.h>
+
+#include "../../include/pqb.h"
+#include "launch.h"
+
+namespace {
+
+using namespace pqb;
+
+bool valid_dtype(int d) { return d == PQB_F32 || d == PQB_BF16; }
+
+bool valid_pair(int fmt, int gran) {
+  switch (fmt) {
+    case PQB_FP8_E4M3:
+      return gran == PQB_TENSOR || gran == PQB_ROW || gran == PQB_BLK_1x128 ||
+             gran == PQB_BLK_128x128;
+    case PQB_MXFP4:
+      return gran == PQB_BLK_32;
+    case PQB_NVFP4:
+      return gran == PQB_BLK_16;
+    case PQB_INT4_ASYM:
+      return gran == PQB_GRP_128;
+  }
+  return false;
+}
+
+bool known_format(int f) { return f >= PQB_FP8_E4M3 && f <= PQB_INT4_ASYM; }
+bool known_gran(int g) { return g >= PQB_TENSOR && g <= PQB_GRP_128; }
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+constexpr int64_t kMaxGridY = 65535;
+
+// Shape rules of one (format, granularity) pair; also bounds the grid sizes
+// the launchers will form.
+pqb_status check_shape(int fmt, int gran, int64_t b, int64_t r, int64_t c) {
+  if (b < 0 || r < 0 || c < 0) return PQB_ERR_SHAPE;
+  if (r > 0 && c > INT64_MAX / r) return PQB_ERR_SHAPE;
+  if (b > 0 && r * c > INT64_MAX / 4 / b) return PQB_ERR_SHAPE;
+  switch (gran) {
+    case PQB_TENSOR:
+      if (b > kMaxGridY) return PQB_ERR_SHAPE;
+      break;
+    case PQB_ROW:
+      break;
+    case PQB_BLK_1x128:
+    case PQB_GRP_128:
+      if (c % 128) return PQB_ERR_SHAPE;
+      break;
+    case PQB_BLK_128x128: {
+      if (c % 128) return PQB_ERR_SHAPE;
+      if (r > 128 && r % 128) return PQB_ERR_SHAPE;
+      const int64_t br = r < 128 ? r : 128;
+      if (br > 0 && b * (r / br) * (c / 128) > 0xFFFFFFFFll) return PQB_ERR_SHAPE;
+      break;
+    }
+    case PQB_BLK_32:
+      if (c % 32) return PQB_ERR_SHAPE;
+      break;
+    case PQB_BLK_16:
+      if (c % 16 || b > kMaxGridY) return PQB_ERR_SHAPE;
+      break;
+  }
+  (void)fmt;
+  return PQB_OK;
+}
+
+int64_t fp8_num_scales(int gran, int64_t b, int64_t r, int64_t c) {
+  switch (gran) {
+    case PQB_TENSOR: return b;
+    case PQB_ROW: return b * r;
+    case PQB_BLK_1x128: return b * r * (c / 128);
+    default: {
+      const int64_t br = r < 128 ? r : 128;
+      return br == 0 ? 0 : b * (r / br) * (c / 128);
+    }
+  }
+}
+
+pqb_sizes sizes_of(int fmt, int gran, int64_t b, int64_t r, int64_t c) {
+  pqb_sizes s{0, 0, 0, 0};
+  const int64_t n = b * r * c;
+  switch (fmt) {
+    case PQB_FP8_E4M3:
+      s.codes = (size_t)n;
+      s.scales = 4 * (size_t)fp8_num_scales(gran, b, r, c);
+      if (gran == PQB_TENSOR && n > 0)
+        s.workspace = 4 * (size_t)b * (size_t)amax_partials_per_slice(b, r * c, 1);
+      break;
+    case PQB_MXFP4:
+      s.codes = (size_t)n / 2;
+      s.scales = (size_t)n / 32;
+      break;
+    case PQB_NVFP4:
+      s.codes = (size_t)n / 2;
+      s.scales = (size_t)n / 16;
+      s.aux = 4 * (size_t)b;
+      if (n > 0) s.workspace = 4 * (size_t)b * (size_t)amax_partials_per_slice(b, r * c, 1);
+      break;
+    case PQB_INT4_ASYM:
+      s.codes = (size_t)n / 2;
+      s.scales = 2 * (size_t)(n / 128);
+      s.aux = (size_t)(n / 128 + 1) / 2;
+      break;
+  }
+  return s;
+}
+
+pqb_status hip_status(hipError_t e) { return e == hipSuccess ? PQB_OK : PQB_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int pqb_abi_version(void) { return PQB_ABI_VERSION; }
+
+const char* pqb_status_string(pqb_status s) {
+  switch (s) {
+    case PQB_OK: return "ok";
+    case PQB_ERR_NULL: return "a required pointer is NULL";
+    case PQB_ERR_ENUM: return "unknown dtype, format or granularity";
+    case PQB_ERR_COMBO: return "format and granularity do not go together";
+    case PQB_ERR_SHAPE: return "shape rejected by the block rules";
+    case PQB_ERR_ALIGN: return "pointer alignment rule broken";
+    case PQB_ERR_WORKSPACE: return "workspace too small";
+    case PQB_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+pqb_status pqb_query_sizes(pqb_format fmt, pqb_gran gran, int64_t batch, int64_t rows,
+                           int64_t cols, pqb_sizes* out) {
+  if (!out) return PQB_ERR_NULL;
+  if (!known_format(fmt) || !known_gran(gran)) return PQB_ERR_ENUM;
+  if (!valid_pair(fmt, gran)) return PQB_ERR_COMBO;
+  const pqb_status st = check_shape(fmt, gran, batch, rows, cols);
+  if (st != PQB_OK) return st;
+  *out = sizes_of(fmt, gran, batch, rows, cols);
+  return PQB_OK;
+}
+
+pqb_status pqb_quantize(const void* x, pqb_dtype dtype, int64_t batch, int64_t rows, int64_t cols,
+                        pqb_format fmt, pqb_gran gran, void* codes, void* scales, void* aux,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(dtype) || !known_format(fmt) || !known_gran(gran)) return PQB_ERR_ENUM;
+  if (!valid_pair(fmt, gran)) return PQB_ERR_COMBO;
+  pqb_status st = check_shape(fmt, gran, batch, rows, cols);
+  if (st != PQB_OK) return st;
+  const int64_t n = batch * rows * cols;
+  if (n == 0) return PQB_OK;
+  const pqb_sizes need = sizes_of(fmt, gran, batch, rows, cols);
+  if (!x || !codes || !scales) return PQB_ERR_NULL;
+  if (need.aux && !aux) return PQB_ERR_NULL;
+  if (need.workspace && !workspace) return PQB_ERR_NULL;
+  if (workspace_bytes < need.workspace) return PQB_ERR_WORKSPACE;
+  if (!aligned(x, 16) || !aligned(codes, 16) || (need.workspace && !aligned(workspace, 16)))
+    return PQB_ERR_ALIGN;
+  if (fmt == PQB_FP8_E4M3 && !aligned(scales, 4)) return PQB_ERR_ALIGN;
+  if (fmt == PQB_INT4_ASYM && !aligned(scales, 2)) return PQB_ERR_ALIGN;
+  if (fmt == PQB_NVFP4 && !aligned(aux, 4)) return PQB_ERR_ALIGN;
+  const bool bf16 = dtype == PQB_BF16;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* c8 = (uint8_t*)codes;
+  switch (fmt) {
+    case PQB_FP8_E4M3: {
+      float* sc = (float*)scales;
+      switch (gran) {
+        case PQB_TENSOR: {
+          const void* xs[1] = {x};
+          uint8_t* cs[1] = {c8};
+          float* ss[1] = {sc};
+          return hip_status(launch_fp8_tensor(xs, bf16, 1, batch, rows * cols, cs, ss,
+                                              (float*)workspace, s));
+        }
+        case PQB_ROW:
+          return hip_status(launch_fp8_row(x, bf16, batch * rows, cols, c8, sc, s));
+        case PQB_BLK_1x128:
+          return hip_status(launch_fp8_1x128(x, bf16, n, c8, sc, s));
+        default:
+          return hip_status(launch_fp8_128x128(x, bf16, batch, rows, cols, c8, sc, s));
+      }
+    }
+    case PQB_MXFP4:
+      return hip_status(launch_mxfp4(x, bf16, n, c8, (uint8_t*)scales, s));
+    case PQB_NVFP4:
+      return hip_status(launch_nvfp4(x, bf16, batch, rows * cols, c8, (uint8_t*)scales,
+                                     (float*)aux, (float*)workspace, s));
+    case PQB_INT4_ASYM:
+      return hip_status(
+          launch_int4(x, bf16, n, c8, (uint16_t*)scales, (uint8_t*)aux, s));
+  }
+  return PQB_ERR_ENUM;
+}
+
+pqb_status pqb_dequantize(const void* codes, const void* scales, const void* aux, pqb_format fmt,
+                          pqb_gran gran, int64_t batch, int64_t rows, int64_t cols,
+                          pqb_dtype out_dtype, void* out, void* stream) {
+  if (!valid_dtype(out_dtype) || !known_format(fmt) || !known_gran(gran)) return PQB_ERR_ENUM;
+  if (!valid_pair(fmt, gran)) return PQB_ERR_COMBO;
+  pqb_status st = check_shape(fmt, gran, batch, rows, cols);
+  if (st != PQB_OK) return st;
+  const int64_t n = batch * rows * cols;
+  if (n == 0) return PQB_OK;
+  const pqb_sizes need = sizes_of(fmt, gran, batch, rows, cols);
+  if (!codes || !scales || !out || (need.aux && !aux)) return PQB_ERR_NULL;
+  if (!aligned(codes, 16) || !aligned(out, 16)) return PQB_ERR_ALIGN;
+  if (fmt == PQB_FP8_E4M3 && !aligned(scales, 4)) return PQB_ERR_ALIGN;
+  if (fmt == PQB_INT4_ASYM && !aligned(scales, 2)) return PQB_ERR_ALIGN;
+  if (fmt == PQB_NVFP4 && !aligned(aux, 4)) return PQB_ERR_ALIGN;
+  if (fmt == PQB_FP8_E4M3 && batch * rows > 0 && (cols > 0x7FFFFFFF)) return PQB_ERR_SHAPE;
+  const bool bf16 = out_dtype == PQB_BF16;
+  hipStream_t s = (hipStream_t)stream;
+  switch (fmt) {
+    case PQB_FP8_E4M3:
+      return hip_status(launch_fp8_dequant((const uint8_t*)codes, (const float*)scales, gran,
+                                           batch, rows, cols, bf16, out, s));
+    case PQB_MXFP4:
+      return hip_status(launch_mxfp4_dequant((const uint8_t*)codes, (const uint8_t*)scales, n,
+                                             bf16, out, s));
+    case PQB_NVFP4:
+      return hip_status(launch_nvfp4_dequant((const uint8_t*)codes, (const uint8_t*)scales,
+                                             (const float*)aux, batch, rows * cols, bf16, out,
+                                             s));
+    case PQB_INT4_ASYM:
+      return hip_status(launch_int4_dequant((const uint8_t*)codes, (const uint16_t*)scales,
+                                            (const uint8_t*)aux, n, bf16, out, s));
+  }
+  return PQB_ERR_ENUM;
+}
+
+size_t pqb_kv_workspace_bytes(int64_t layers, int64_t elems_per_layer) {
+  if (layers <= 0 || elems_per_layer <= 0) return 0;
+  return 4 * 2 * (size_t)layers * (size_t)amax_partials_per_slice(layers, elems_per_layer, 2);
+}
+
+pqb_status pqb_kv_write_fp8(const void* k, const void* v, pqb_dtype dtype, int64_t layers,
+                            int64_t elems_per_layer, uint8_t* k_codes, uint8_t* v_codes,
+                            float* k_scales, float* v_scales, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(dtype)) return PQB_ERR_ENUM;
+  if (layers < 0 || elems_per_layer < 0 || layers > kMaxGridY) return PQB_ERR_SHAPE;
+  if (elems_per_layer > 0 && layers > INT64_MAX / 4 / elems_per_layer) return PQB_ERR_SHAPE;
+  if (layers == 0 || elems_per_layer == 0) return PQB_OK;
+  if (!k || !v || !k_codes || !v_codes || !k_scales || !v_scales || !workspace)
+    return PQB_ERR_NULL;
+  if (workspace_bytes < pqb_kv_workspace_bytes(layers, elems_per_layer)) return PQB_ERR_WORKSPACE;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) ||
+      !aligned(k_scales, 4) || !aligned(v_scales, 4) || !aligned(workspace, 16))
+    return PQB_ERR_ALIGN;
+  const void* xs[2] = {k, v};
+  uint8_t* cs[2] = {k_codes, v_codes};
+  float* ss[2] = {k_scales, v_scales};
+  return hip_status(launch_fp8_tensor(xs, dtype == PQB_BF16, 2, layers, elems_per_layer, cs, ss,
+                                      (float*)workspace, (hipStream_t)stream));
+}
+
+pqb_status pqb_encode_e4m3(const float* y, int64_t n, uint8_t* out, void* stream) {
+  if (n < 0) return PQB_ERR_SHAPE;
+  if (n == 0) return PQB_OK;
+  if (!y || !out) return PQB_ERR_NULL;
+  if (!aligned(y, 4)) return PQB_ERR_ALIGN;
+  return hip_status(launch_encode_e4m3(y, n, out, (hipStream_t)stream));
+}
+
+pqb_status pqb_encode_e2m1(const float* y, int64_t n, uint8_t* out, void* stream) {
+  if (n < 0) return PQB_ERR_SHAPE;
+  if (n == 0) return PQB_OK;
+  if (!y || !out) return PQB_ERR_NULL;
+  if (!aligned(y, 4)) return PQB_ERR_ALIGN;
+  return hip_status(launch_encode_e2m1(y, n, out, (hipStream_t)stream));
+}
+
+}  // extern "C"

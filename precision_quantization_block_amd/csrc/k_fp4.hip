@@ -1,0 +1,284 @@
+// MXFP4 and NVFP4 quantize / dequantize kernels (E2M1 elements).
+//
+// MXFP4 (page "量化部署实战", section 伪量化实现): a 32-element block shares
+// 2^X with X = floor(log2 max(amax, 1e-12)) - 2, stored as the E8M0 byte X+127.
+// floor(log2 a) of a normal float is its unbiased exponent field.
+// NVFP4 (same section): gs = max(amax_tensor, 1e-12) / (448*6); each 16-element
+// block stores bs = E4M3(RN(RN(amax_block / 6) / gs)); elements are rounded
+// against s = RN(max(dec(bs), 1e-12) * gs).
+#include "device.h"
+#include "launch.h"
+
+namespace pqb {
+namespace {
+
+constexpr float kInv6 = 1.0f / 6.0f;
+
+
+// ---------------------------------------------------------------------------
+// MXFP4: 4 lanes x 8 elements per block.  y = x * 2^-X is exactly RN(x / 2^X)
+// (a product with a power of two), so the E2M1 table sees the page's quotient,
+// signed zeros included (a -0.0 quotient maps to nibble 0).
+// ---------------------------------------------------------------------------
+template <typename T, int kUnr>
+__global__ __launch_bounds__(kBlockThreads) void k_mxfp4(const T* __restrict__ x, int64_t nunits,
+                                                          uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales) {
+  __shared__ uint8_t lut[kE2M1LutSize];
+  e2m1_lut_fill(lut, 0);
+  __syncthreads();
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wave = ((int64_t)blockIdx.x * kBlockThreads + threadIdx.x) / kWave;
+  const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
+  const int64_t ntiles = (nunits + kWave - 1) / kWave;
+  for (int64_t t0 = wave * kUnr; t0 < ntiles; t0 += nwaves * kUnr) {
+    Raw8 raw[kUnr];
+#pragma unroll
+    for (int k = 0; k < kUnr; ++k) {
+      const int64_t u = (t0 + k) * kWave + lane;
+      raw[k] = u < nunits ? load_raw8(x + u * 8) : Raw8{};
+    }
+#pragma unroll
+    for (int k = 0; k < kUnr; ++k) {
+      const int64_t u = (t0 + k) * kWave + lane;
+      float v[8];
+      widen8(raw[k], x, v);
+      const float a = fmaxf(group_max<4>(absmax8(v)), 1e-12f);
+      const uint32_t ef = as_u(a) >> 23;          // biased exponent of a normal a
+      const float mul = as_f((256u - ef) << 23);  // 2^-X with X = ef - 129
+      uint32_t w = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w |= (uint32_t)lut[e2m1_key(v[i] * mul)] << (4 * i);
+      if (u < nunits) {
+        st_nt4(codes + u * 4, w);
+        if ((lane & 3) == 0) scales[u >> 2] = (uint8_t)(ef - 2u);
+      }
+    }
+  }
+}
+
+// Signed E2M1 values, nibble -> float.
+__device__ __forceinline__ float e2m1_value(uint32_t nib) {
+  const uint32_t m = nib & 7u;
+  // m >= 2: 2^(m/2 - 1) * (1 + (m & 1) / 2); m == 1: 0.5; m == 0: 0
+  uint32_t b = m >= 2u ? ((((m >> 1) + 126u) << 23) | ((m & 1u) << 22)) : (m ? 0x3F000000u : 0u);
+  return as_f(b | ((nib & 8u) << 28));
+}
+
+
+template <bool kBf16Out>
+__global__ __launch_bounds__(kBlockThreads) void k_mxfp4_dequant(const uint8_t* __restrict__ codes,
+                                                                  const uint8_t* __restrict__ scales,
+                                                                  int64_t nunits,
+                                                                  void* __restrict__ out) {
+  for (int64_t u = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x; u < nunits;
+       u += (int64_t)gridDim.x * kBlockThreads) {
+    const uint32_t w = reinterpret_cast<const uint32_t*>(codes)[u];
+    const float sc = as_f((uint32_t)scales[u >> 2] << 23);  // 2^(e - 127), e in [85, 252]
+    float o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = e2m1_value(w >> (4 * i)) * sc;
+    store_out8<kBf16Out>(out, u, o);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4 pass 2 (pass 1 is the shared amax-partials kernel): 2 lanes x 8
+// elements per block.  Each workgroup rebuilds gs, the E2M1 table and, for all
+// 127 finite block-scale codes, the element scale s and RN(1/s) in LDS.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float block_max4(float m, float* red) {
+  m = wave_max(m);
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  return m;
+}
+
+template <typename T, int kUnr>
+__global__ __launch_bounds__(kBlockThreads) void k_nvfp4_quant(const T* __restrict__ x,
+                                                                int64_t per_slice,
+                                                                uint8_t* __restrict__ codes,
+                                                                uint8_t* __restrict__ scales,
+                                                                float* __restrict__ gs_out,
+                                                                const float* __restrict__ partials,
+                                                                int P) {
+  __shared__ uint8_t lut[kE2M1LutSize];
+  __shared__ float se[128], ye[128];
+  __shared__ float red[kBlockThreads / kWave];
+  const int64_t b = blockIdx.y;
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < P; i += kBlockThreads) m = fmaxf(m, partials[b * P + i]);
+  const float amax_t = block_max4(m, red);
+  const float gs = fmaxf(amax_t, 1e-12f) / 2688.0f;  // 448 * 6
+  const float ygs = 1.0f / gs;
+  e2m1_lut_fill(lut, 8);
+  for (int c = threadIdx.x; c < 127; c += kBlockThreads) {
+    const float sc = fmaxf(e4m3_decode((uint32_t)c), 1e-12f) * gs;
+    se[c] = sc;
+    ye[c] = 1.0f / sc;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0 && threadIdx.x == 0) gs_out[b] = gs;
+
+  const T* xs = x + b * per_slice;
+  uint8_t* cs = codes + b * (per_slice / 2);
+  uint8_t* ss = scales + b * (per_slice / 16);
+  const int64_t nunits = per_slice / 8;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wave = ((int64_t)blockIdx.x * kBlockThreads + threadIdx.x) / kWave;
+  const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
+  const int64_t ntiles = (nunits + kWave - 1) / kWave;
+  for (int64_t t0 = wave * kUnr; t0 < ntiles; t0 += nwaves * kUnr) {
+    Raw8 raw[kUnr];
+#pragma unroll
+    for (int k = 0; k < kUnr; ++k) {
+      const int64_t u = (t0 + k) * kWave + lane;
+      raw[k] = u < nunits ? load_raw8(xs + u * 8) : Raw8{};
+    }
+#pragma unroll
+    for (int k = 0; k < kUnr; ++k) {
+      const int64_t u = (t0 + k) * kWave + lane;
+      float v[8];
+      widen8(raw[k], xs, v);
+      const float ab = group_max<2>(absmax8(v));
+      const float bq = div_mag(div_const(ab, 6.0f, kInv6), gs, ygs);  // <= 448 (1 + 2^-22)
+      const uint32_t bs = cvt_e4m3x2<false>(bq, 0.0f, 0u) & 0x7Fu;  // bq >= 0
+      const float s = se[bs], ys = ye[bs];
+      uint32_t w = 0;
+      if (s < 2.0f && s >= 0x1p-60f) {
+        // Every nonzero x has a nonzero RN(x / s) here (|x / s| > 2^-150), so
+        // the nibble's sign is that of x (with -0.0 first mapped to +0).
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float xi = v[i] + 0.0f;
+          const float q = with_sign_of(div_mag(fabsf(xi), s, ys), xi);
+          w |= (uint32_t)lut[e2m1_key(q)] << (4 * i);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w |= (uint32_t)lut[e2m1_key(v[i] / s + 0.0f)] << (4 * i);
+      }
+      if (u < nunits) {
+        st_nt4(cs + u * 4, w);
+        if ((lane & 1) == 0) ss[u >> 1] = (uint8_t)bs;
+      }
+    }
+  }
+}
+
+template <bool kBf16Out>
+__global__ __launch_bounds__(kBlockThreads) void k_nvfp4_dequant(const uint8_t* __restrict__ codes,
+                                                                  const uint8_t* __restrict__ scales,
+                                                                  const float* __restrict__ gs,
+                                                                  int64_t per_slice,
+                                                                  void* __restrict__ out) {
+  const int64_t b = blockIdx.y;
+  const float g = gs[b];
+  const int64_t nunits = per_slice / 8, u0 = b * nunits;
+  for (int64_t u = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x; u < nunits;
+       u += (int64_t)gridDim.x * kBlockThreads) {
+    const uint32_t w = reinterpret_cast<const uint32_t*>(codes)[u0 + u];
+    const float s = fmaxf(e4m3_decode(scales[(u0 + u) >> 1]), 1e-12f) * g;
+    float o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = e2m1_value(w >> (4 * i)) * s;
+    store_out8<kBf16Out>(out, u0 + u, o);
+  }
+}
+
+// E2M1 nibble of each float (one byte per element).
+__global__ __launch_bounds__(kBlockThreads) void k_encode_e2m1(const float* __restrict__ y,
+                                                               int64_t n,
+                                                               uint8_t* __restrict__ out) {
+  __shared__ uint8_t lut[kE2M1LutSize];
+  e2m1_lut_fill(lut, 0);
+  __syncthreads();
+  for (int64_t i = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * kBlockThreads)
+    out[i] = lut[e2m1_key(y[i])];
+}
+
+inline int grid_cap(int64_t work, int64_t per_block, int64_t cap) {
+  int64_t g = (work + per_block - 1) / per_block;
+  return (int)(g < 1 ? 1 : (g > cap ? cap : g));
+}
+
+// Workgroups for the table-building kernels: enough to fill the chip, few
+// enough that each one amortizes its table over many tiles.
+constexpr int64_t kTableKernelCap = 256 * 8;
+
+}  // namespace
+
+hipError_t launch_mxfp4(const void* x, bool bf16, int64_t n, uint8_t* codes, uint8_t* scales,
+                        hipStream_t st) {
+  constexpr int kUnr = 4;
+  const int64_t nunits = n / 8, ntiles = (nunits + kWave - 1) / kWave;
+  const int grid = grid_cap(ntiles, (int64_t)kUnr * (kBlockThreads / kWave), kTableKernelCap);
+  if (bf16)
+    hipLaunchKernelGGL((k_mxfp4<uint16_t, kUnr>), dim3(grid), dim3(kBlockThreads), 0, st,
+                       (const uint16_t*)x, nunits, codes, scales);
+  else
+    hipLaunchKernelGGL((k_mxfp4<float, kUnr>), dim3(grid), dim3(kBlockThreads), 0, st,
+                       (const float*)x, nunits, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, int64_t n,
+                                bool out_bf16, void* out, hipStream_t st) {
+  const int64_t nunits = n / 8;
+  const int grid = grid_cap(nunits, kBlockThreads, 1 << 20);
+  if (out_bf16)
+    hipLaunchKernelGGL(k_mxfp4_dequant<true>, dim3(grid), dim3(kBlockThreads), 0, st, codes,
+                       scales, nunits, out);
+  else
+    hipLaunchKernelGGL(k_mxfp4_dequant<false>, dim3(grid), dim3(kBlockThreads), 0, st, codes,
+                       scales, nunits, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_nvfp4(const void* x, bool bf16, int64_t batch, int64_t per_slice,
+                        uint8_t* codes, uint8_t* scales, float* gs, float* partials,
+                        hipStream_t st) {
+  constexpr int kUnr = 2;
+  const int P = amax_partials_per_slice(batch, per_slice, 1);
+  const void* xs[1] = {x};
+  hipError_t e = launch_amax_partials(xs, bf16, 1, batch, per_slice, partials, P, st);
+  if (e != hipSuccess) return e;
+  const int64_t nunits = per_slice / 8, ntiles = (nunits + kWave - 1) / kWave;
+  int64_t cap = kTableKernelCap / (batch > 0 ? batch : 1);
+  if (cap < 1) cap = 1;
+  const int gx = grid_cap(ntiles, (int64_t)kUnr * (kBlockThreads / kWave), cap);
+  const dim3 grid(gx, (unsigned)batch);
+  if (bf16)
+    hipLaunchKernelGGL((k_nvfp4_quant<uint16_t, kUnr>), grid, dim3(kBlockThreads), 0, st,
+                       (const uint16_t*)x, per_slice, codes, scales, gs, partials, P);
+  else
+    hipLaunchKernelGGL((k_nvfp4_quant<float, kUnr>), grid, dim3(kBlockThreads), 0, st,
+                       (const float*)x, per_slice, codes, scales, gs, partials, P);
+  return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const float* gs,
+                                int64_t batch, int64_t per_slice, bool out_bf16, void* out,
+                                hipStream_t st) {
+  const int64_t nunits = per_slice / 8;
+  const dim3 grid(grid_cap(nunits, kBlockThreads, 8192), (unsigned)batch);
+  if (out_bf16)
+    hipLaunchKernelGGL(k_nvfp4_dequant<true>, grid, dim3(kBlockThreads), 0, st, codes, scales, gs,
+                       per_slice, out);
+  else
+    hipLaunchKernelGGL(k_nvfp4_dequant<false>, grid, dim3(kBlockThreads), 0, st, codes, scales,
+                       gs, per_slice, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_encode_e2m1(const float* y, int64_t n, uint8_t* out, hipStream_t st) {
+  hipLaunchKernelGGL(k_encode_e2m1, dim3(grid_cap(n, kBlockThreads, 4096)), dim3(kBlockThreads),
+                     0, st, y, n, out);
+  return hipGetLastError();
+}
+
+}  // namespace pqb

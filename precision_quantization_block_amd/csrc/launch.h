@@ -1,0 +1,57 @@
+// Internal launch interface between the C ABI (abi.hip) and the kernel files.
+// Every launcher enqueues on `stream` and returns the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pqb {
+
+// Partial-maximum workspace for the two-pass (per-tensor) formats: P floats per
+// (tensor, batch slice).  P depends only on the shape, so the size query and
+// the launch agree.
+int amax_partials_per_slice(int64_t batch, int64_t per_slice, int ntensors);
+
+// Pass 1 of the two-pass formats: partials[(t * batch + b) * P + i] = amax of
+// share i of slice b of tensor t.
+hipError_t launch_amax_partials(const void* const* x, bool bf16, int ntensors, int64_t batch,
+                                int64_t per_slice, float* partials, int P, hipStream_t st);
+
+// ---- FP8 E4M3 -------------------------------------------------------------
+hipError_t launch_fp8_1x128(const void* x, bool bf16, int64_t n, uint8_t* codes, float* scales,
+                            hipStream_t st);
+hipError_t launch_fp8_128x128(const void* x, bool bf16, int64_t batch, int64_t rows,
+                              int64_t cols, uint8_t* codes, float* scales, hipStream_t st);
+hipError_t launch_fp8_row(const void* x, bool bf16, int64_t nrows, int64_t cols, uint8_t* codes,
+                          float* scales, hipStream_t st);
+// Per-tensor over `ntensors` tensors (1, or 2 for K and V) of `batch` slices.
+hipError_t launch_fp8_tensor(const void* const* x, bool bf16, int ntensors, int64_t batch,
+                             int64_t per_slice, uint8_t* const* codes, float* const* scales,
+                             float* partials, hipStream_t st);
+hipError_t launch_fp8_dequant(const uint8_t* codes, const float* scales, int gran, int64_t batch,
+                              int64_t rows, int64_t cols, bool out_bf16, void* out,
+                              hipStream_t st);
+
+// ---- MXFP4 / NVFP4 ----------------------------------------------------------
+hipError_t launch_mxfp4(const void* x, bool bf16, int64_t n, uint8_t* codes, uint8_t* scales,
+                        hipStream_t st);
+hipError_t launch_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, int64_t n,
+                                bool out_bf16, void* out, hipStream_t st);
+hipError_t launch_nvfp4(const void* x, bool bf16, int64_t batch, int64_t per_slice,
+                        uint8_t* codes, uint8_t* scales, float* gs, float* partials,
+                        hipStream_t st);
+hipError_t launch_nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const float* gs,
+                                int64_t batch, int64_t per_slice, bool out_bf16, void* out,
+                                hipStream_t st);
+
+// ---- INT4 group-128 asymmetric --------------------------------------------
+hipError_t launch_int4(const void* x, bool bf16, int64_t n, uint8_t* codes, uint16_t* scales,
+                       uint8_t* zeros, hipStream_t st);
+hipError_t launch_int4_dequant(const uint8_t* codes, const uint16_t* scales, const uint8_t* zeros,
+                               int64_t n, bool out_bf16, void* out, hipStream_t st);
+
+// ---- element codecs ---------------------------------------------------------
+hipError_t launch_encode_e4m3(const float* y, int64_t n, uint8_t* out, hipStream_t st);
+hipError_t launch_encode_e2m1(const float* y, int64_t n, uint8_t* out, hipStream_t st);
+
+}  // namespace pqb

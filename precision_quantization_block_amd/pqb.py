@@ -1,0 +1,261 @@
+"""Thin Python binding over libpqb.so (argument marshalling only).
+
+Every step of quantization runs in the HIP kernels behind the C ABI of
+include/pqb.h.  Torch supplies device memory and the current stream; there is
+no CPU fallback: if libpqb.so is missing or a tensor is not on the GPU, the
+call raises.
+
+Page-named fake-quant helpers (fp8_per_tensor, fp8_per_row, fp8_blockwise,
+mxfp4, nvfp4, fp8_kv_write) mirror the fake-quant module on the page "量化部署
+实战" (section 伪量化实现): quantize, then dequantize, returning float32 of the
+input's shape.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpqb.so")
+
+F32, BF16 = 0, 1
+FORMATS = {"fp8_e4m3": 0, "mxfp4": 1, "nvfp4": 2, "int4_asym": 3}
+GRANS = {"tensor": 0, "row": 1, "1x128": 2, "128x128": 3, "blk32": 4, "blk16": 5, "grp128": 6}
+DEFAULT_GRAN = {"mxfp4": "blk32", "nvfp4": "blk16", "int4_asym": "grp128"}
+
+_lib = None
+
+
+class PqbError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+class _Sizes(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_size_t), ("scales", ctypes.c_size_t),
+                ("aux", ctypes.c_size_t), ("workspace", ctypes.c_size_t)]
+
+
+def lib():
+    """Load libpqb.so (built by __graft_entry__.build() or _build.py)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+        L.pqb_abi_version.restype = I
+        L.pqb_status_string.argtypes, L.pqb_status_string.restype = [I], ctypes.c_char_p
+        L.pqb_query_sizes.argtypes = [I, I, I64, I64, I64, ctypes.POINTER(_Sizes)]
+        L.pqb_quantize.argtypes = [P, I, I64, I64, I64, I, I, P, P, P, P, SZ, P]
+        L.pqb_dequantize.argtypes = [P, P, P, I, I, I64, I64, I64, I, P, P]
+        L.pqb_kv_workspace_bytes.argtypes, L.pqb_kv_workspace_bytes.restype = [I64, I64], SZ
+        L.pqb_kv_write_fp8.argtypes = [P, P, I, I64, I64, P, P, P, P, P, SZ, P]
+        L.pqb_encode_e4m3.argtypes = [P, I64, P, P]
+        L.pqb_encode_e2m1.argtypes = [P, I64, P, P]
+        for f in ("pqb_query_sizes", "pqb_quantize", "pqb_dequantize", "pqb_kv_write_fp8",
+                  "pqb_encode_e4m3", "pqb_encode_e2m1"):
+            getattr(L, f).restype = I
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().pqb_status_string(status).decode()
+
+
+def abi_version() -> int:
+    return lib().pqb_abi_version()
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise PqbError(status, what)
+
+
+def _fmt(fmt) -> int:
+    return FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+
+
+def _gran(gran) -> int:
+    return GRANS[gran] if isinstance(gran, str) else int(gran)
+
+
+def _ptr(t: torch.Tensor | None):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev_tensor(x: torch.Tensor, name: str, dtypes=(torch.float32, torch.bfloat16)):
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if x.dtype not in dtypes:
+        raise ValueError(f"{name} must have dtype in {dtypes}, got {x.dtype}")
+    return x.contiguous()
+
+
+def query_sizes(fmt, gran, batch: int, rows: int, cols: int) -> dict:
+    s = _Sizes()
+    _check(lib().pqb_query_sizes(_fmt(fmt), _gran(gran), batch, rows, cols, ctypes.byref(s)),
+           "query_sizes")
+    return {"codes": s.codes, "scales": s.scales, "aux": s.aux, "workspace": s.workspace}
+
+
+@dataclass
+class Quantized:
+    """Packed codes, encoded scales and the format's auxiliary buffer."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    aux: torch.Tensor | None
+    fmt: str
+    gran: str
+    shape: tuple   # (batch, rows, cols)
+
+
+def _scale_dtype(fmt: str):
+    return {"fp8_e4m3": torch.float32, "mxfp4": torch.uint8, "nvfp4": torch.uint8,
+            "int4_asym": torch.bfloat16}[fmt]
+
+
+def _bytes(n: int, dtype, device):
+    esize = torch.empty((), dtype=dtype).element_size()
+    return torch.empty((n // esize,), dtype=dtype, device=device)
+
+
+def quantize(x: torch.Tensor, fmt: str, gran: str | None = None, *, shape=None,
+             workspace: torch.Tensor | None = None) -> Quantized:
+    """Quantize x viewed as [batch, rows, cols] (default: leading dims are the
+    batch, the last two are rows and cols)."""
+    gran = gran or DEFAULT_GRAN[fmt]
+    x = _dev_tensor(x, "x")
+    b, r, c = shape if shape is not None else _bcr(x.shape)
+    if b * r * c != x.numel():
+        raise ValueError("shape does not match the tensor")
+    sz = query_sizes(fmt, gran, b, r, c)
+    dev = x.device
+    codes = torch.empty((sz["codes"],), dtype=torch.uint8, device=dev)
+    scales = _bytes(sz["scales"], _scale_dtype(fmt), dev)
+    aux = None
+    if sz["aux"]:
+        aux = (torch.empty((b,), dtype=torch.float32, device=dev) if fmt == "nvfp4"
+               else torch.empty((sz["aux"],), dtype=torch.uint8, device=dev))
+    if sz["workspace"] and (workspace is None or workspace.numel() * workspace.element_size()
+                            < sz["workspace"]):
+        workspace = torch.empty((sz["workspace"] // 4,), dtype=torch.float32, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().pqb_quantize(_ptr(x), BF16 if x.dtype == torch.bfloat16 else F32, b, r, c,
+                              _fmt(fmt), _gran(gran), _ptr(codes), _ptr(scales), _ptr(aux),
+                              _ptr(workspace), ws_bytes, _stream(dev)), "quantize")
+    return Quantized(codes, scales, aux, fmt, gran, (b, r, c))
+
+
+def dequantize(q: Quantized, out_dtype=torch.float32) -> torch.Tensor:
+    b, r, c = q.shape
+    out = torch.empty((b, r, c), dtype=out_dtype, device=q.codes.device)
+    _check(lib().pqb_dequantize(_ptr(q.codes), _ptr(q.scales), _ptr(q.aux), _fmt(q.fmt),
+                                _gran(q.gran), b, r, c,
+                                BF16 if out_dtype == torch.bfloat16 else F32, _ptr(out),
+                                _stream(out.device)), "dequantize")
+    return out
+
+
+def kv_write_fp8(k: torch.Tensor, v: torch.Tensor, workspace: torch.Tensor | None = None):
+    """K and V shaped [layers, ...]; one FP8 scale per layer for each.
+    Returns (k_codes, v_codes, k_scales, v_scales) with codes shaped like the input."""
+    k = _dev_tensor(k, "k")
+    v = _dev_tensor(v, "v")
+    if k.shape != v.shape or k.dtype != v.dtype:
+        raise ValueError("K and V must share shape and dtype")
+    layers = k.shape[0]
+    per = k.numel() // layers if layers else 0
+    dev = k.device
+    kc = torch.empty(k.shape, dtype=torch.uint8, device=dev)
+    vc = torch.empty(v.shape, dtype=torch.uint8, device=dev)
+    ks = torch.empty((layers,), dtype=torch.float32, device=dev)
+    vs = torch.empty((layers,), dtype=torch.float32, device=dev)
+    need = lib().pqb_kv_workspace_bytes(layers, per)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty((max(need, 4) // 4,), dtype=torch.float32, device=dev)
+    _check(lib().pqb_kv_write_fp8(_ptr(k), _ptr(v), BF16 if k.dtype == torch.bfloat16 else F32,
+                                  layers, per, _ptr(kc), _ptr(vc), _ptr(ks), _ptr(vs),
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _stream(dev)), "kv_write_fp8")
+    return kc, vc, ks, vs
+
+
+def encode_e4m3(y: torch.Tensor) -> torch.Tensor:
+    y = _dev_tensor(y, "y", (torch.float32,))
+    out = torch.empty(y.shape, dtype=torch.uint8, device=y.device)
+    _check(lib().pqb_encode_e4m3(_ptr(y), y.numel(), _ptr(out), _stream(y.device)), "encode_e4m3")
+    return out
+
+
+def encode_e2m1(y: torch.Tensor) -> torch.Tensor:
+    y = _dev_tensor(y, "y", (torch.float32,))
+    out = torch.empty(y.shape, dtype=torch.uint8, device=y.device)
+    _check(lib().pqb_encode_e2m1(_ptr(y), y.numel(), _ptr(out), _stream(y.device)), "encode_e2m1")
+    return out
+
+
+# --------------------------------------------------------------------------
+# page-named fake-quant helpers: quantize then dequantize, float32 out
+# --------------------------------------------------------------------------
+
+def _bcr(shape):
+    if len(shape) == 0:
+        return 1, 1, 1
+    if len(shape) == 1:
+        return 1, 1, shape[0]
+    return math.prod(shape[:-2]), shape[-2], shape[-1]
+
+
+def _fake(x, fmt, gran, shape):
+    return dequantize(quantize(x, fmt, gran, shape=shape)).reshape(x.shape)
+
+
+def fp8_per_tensor(x):
+    return _fake(x, "fp8_e4m3", "tensor", (1, math.prod(x.shape[:-1]), x.shape[-1]))
+
+
+def fp8_per_row(x):
+    return _fake(x, "fp8_e4m3", "row", (1, math.prod(x.shape[:-1]), x.shape[-1]))
+
+
+def fp8_blockwise(x, block=(128, 128)):
+    if tuple(block) == (128, 128):
+        return _fake(x, "fp8_e4m3", "128x128", _bcr(x.shape))
+    if tuple(block) == (1, 128):
+        return _fake(x, "fp8_e4m3", "1x128", (1, math.prod(x.shape[:-1]), x.shape[-1]))
+    raise ValueError("block must be (128, 128) or (1, 128)")
+
+
+def mxfp4(w, block=32):
+    if block != 32:
+        raise ValueError("MXFP4 blocks are 32 elements")
+    return _fake(w, "mxfp4", "blk32", (1, math.prod(w.shape[:-1]), w.shape[-1]))
+
+
+def nvfp4(w, block=16):
+    if block != 16:
+        raise ValueError("NVFP4 blocks are 16 elements")
+    return _fake(w, "nvfp4", "blk16", (1, math.prod(w.shape[:-1]), w.shape[-1]))
+
+
+def fp8_kv_write(k, v):
+    """FP8 KV-cache write with one scale per layer: returns dequantized (k, v)."""
+    kc, vc, ks, vs = kv_write_fp8(k, v)
+    layers = k.shape[0]
+    outs = []
+    for codes, sc in ((kc, ks), (vc, vs)):
+        q = Quantized(codes.reshape(-1), sc, None, "fp8_e4m3", "tensor",
+                      (layers, 1, codes.numel() // max(layers, 1)))
+        outs.append(dequantize(q).reshape(k.shape))
+    return tuple(outs)

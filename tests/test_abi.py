@@ -1,0 +1,148 @@
+"""The C ABI on the CPU: the library loads, exports what include/pqb.h
+declares, sizes its buffers as the pages' storage arithmetic says, and turns
+bad arguments into status codes before anything reaches the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT, golden
+
+HEADER = os.path.join(ROOT, "include", "pqb.h")
+
+import precision_quantization_block_amd as pqb  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def L():
+    return pqb.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pqb_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert "pqb_quantize" in names and "pqb_dequantize" in names and "pqb_kv_write_fp8" in names
+    for n in names:
+        assert hasattr(L, n), n
+    assert pqb.abi_version() == 1
+
+
+def test_status_strings(L):
+    for code in range(0, -8, -1):
+        assert pqb.status_string(code) not in ("", "unknown status")
+    assert pqb.status_string(5) == "unknown status"
+
+
+def test_sizes_match_storage_arithmetic():
+    n = 28672 * 8192
+    mx = pqb.query_sizes("mxfp4", "blk32", 1, 28672, 8192)
+    assert (mx["codes"] + mx["scales"]) * 8 / n == golden("mxfp4_bits_per_element")
+    nv = pqb.query_sizes("nvfp4", "blk16", 1, 28672, 8192)
+    assert (nv["codes"] + nv["scales"]) * 8 / n == golden("nvfp4_bits_per_element")
+    assert nv["aux"] == 4 and nv["workspace"] > 0
+    i4 = pqb.query_sizes("int4_asym", "grp128", 1, 4096, 4096)
+    per = (i4["codes"] + i4["scales"]) / (4096 * 4096)
+    assert per == 0.515625 and round(per, 3) == golden("int4_g128_bytes_per_weight")
+    assert i4["aux"] == 4096 * 4096 // 256
+    f8 = pqb.query_sizes("fp8_e4m3", "1x128", 1, 8192, 7168)
+    assert f8 == {"codes": 58720256, "scales": 1835008, "aux": 0, "workspace": 0}
+    f8w = pqb.query_sizes("fp8_e4m3", "128x128", 1, 7168, 2048)
+    assert f8w["scales"] == 4 * 56 * 16
+    f8s = pqb.query_sizes("fp8_e4m3", "128x128", 1, 64, 256)
+    assert f8s["scales"] == 4 * 1 * 2
+
+
+def test_llama8b_int4_total_is_about_3_6_gb():
+    """32 decoder layers of the Llama-3.1-8B linear shapes at INT4 g128:
+    packed codes plus 2-byte scales come to about 3.6 GB."""
+    shapes = [(4096, 4096), (1024, 4096), (1024, 4096), (4096, 4096),
+              (14336, 4096), (14336, 4096), (4096, 14336)]
+    total = params = 0
+    for r, c in shapes:
+        s = pqb.query_sizes("int4_asym", "grp128", 1, r, c)
+        total += s["codes"] + s["scales"]
+        params += r * c
+    total *= 32
+    params *= 32
+    assert total == 3_598_712_832
+    assert round(total / 1e9, 1) == golden("llama8b_int4_gb")
+    assert round(params / 1e9, 1) == 7.0
+
+
+def test_kv_workspace_and_bytes():
+    assert pqb.lib().pqb_kv_workspace_bytes(28, 32768 * 8 * 128) > 0
+    assert pqb.lib().pqb_kv_workspace_bytes(0, 10) == 0
+
+
+@pytest.mark.parametrize("fmt,gran,shape,status", [
+    ("fp8_e4m3", "blk32", (1, 8, 32), -3),
+    ("mxfp4", "1x128", (1, 8, 128), -3),
+    ("fp8_e4m3", "1x128", (1, 8, 100), -4),
+    ("fp8_e4m3", "128x128", (1, 200, 128), -4),
+    ("fp8_e4m3", "128x128", (1, 128, 130), -4),
+    ("mxfp4", "blk32", (1, 8, 48), -4),
+    ("nvfp4", "blk16", (1, 8, 24), -4),
+    ("int4_asym", "grp128", (1, 8, 64), -4),
+    ("fp8_e4m3", "row", (-1, 8, 64), -4),
+])
+def test_query_sizes_rejects(fmt, gran, shape, status):
+    with pytest.raises(pqb.PqbError) as e:
+        pqb.query_sizes(fmt, gran, *shape)
+    assert e.value.status == status
+
+
+def test_quantize_argument_errors_before_launch(L):
+    """Every case below must fail validation, so no kernel is ever enqueued."""
+    P = ctypes.c_void_p
+    fake = P(0x10000)          # aligned, never dereferenced
+    odd = P(0x10001)
+    q = L.pqb_quantize
+    # unknown enums
+    assert q(fake, 7, 1, 8, 128, 0, 2, fake, fake, None, None, 0, None) == -2
+    assert q(fake, 1, 1, 8, 128, 9, 2, fake, fake, None, None, 0, None) == -2
+    assert q(fake, 1, 1, 8, 128, 0, 9, fake, fake, None, None, 0, None) == -2
+    # bad pairing and shapes
+    assert q(fake, 1, 1, 8, 128, 0, 4, fake, fake, None, None, 0, None) == -3
+    assert q(fake, 1, 1, 8, 100, 0, 2, fake, fake, None, None, 0, None) == -4
+    # null pointers
+    assert q(None, 1, 1, 8, 128, 0, 2, fake, fake, None, None, 0, None) == -1
+    assert q(fake, 1, 1, 8, 128, 0, 2, None, fake, None, None, 0, None) == -1
+    assert q(fake, 1, 1, 8, 128, 2, 5, fake, fake, None, fake, 1 << 20, None) == -1   # NV aux
+    assert q(fake, 1, 1, 8, 128, 3, 6, fake, fake, None, None, 0, None) == -1        # INT4 aux
+    assert q(fake, 1, 1, 8, 128, 0, 0, fake, fake, None, None, 0, None) == -1        # workspace
+    # workspace too small
+    assert q(fake, 1, 1, 8, 128, 0, 0, fake, fake, None, fake, 0, None) == -6
+    # alignment
+    assert q(odd, 1, 1, 8, 128, 0, 2, fake, fake, None, None, 0, None) == -5
+    assert q(fake, 1, 1, 8, 128, 0, 2, odd, fake, None, None, 0, None) == -5
+    # empty tensors succeed without touching anything
+    assert q(None, 1, 0, 8, 128, 0, 2, None, None, None, None, 0, None) == 0
+
+
+def test_dequantize_and_kv_errors(L):
+    P = ctypes.c_void_p
+    fake, odd = P(0x10000), P(0x10002)
+    d = L.pqb_dequantize
+    assert d(fake, fake, None, 0, 2, 1, 8, 128, 5, fake, None) == -2
+    assert d(None, fake, None, 0, 2, 1, 8, 128, 0, fake, None) == -1
+    assert d(fake, fake, None, 2, 5, 1, 8, 128, 0, fake, None) == -1       # NV needs gs
+    assert d(fake, fake, None, 0, 2, 1, 8, 128, 0, odd, None) == -5
+    kv = L.pqb_kv_write_fp8
+    assert kv(fake, fake, 1, 2, 1024, fake, fake, fake, fake, fake, 0, None) == -6
+    assert kv(None, fake, 1, 2, 1024, fake, fake, fake, fake, fake, 1 << 20, None) == -1
+    assert kv(fake, fake, 4, 2, 1024, fake, fake, fake, fake, fake, 1 << 20, None) == -2
+    assert kv(fake, fake, 1, 0, 1024, None, None, None, None, None, 0, None) == 0
+    assert L.pqb_encode_e4m3(None, 4, fake, None) == -1
+    assert L.pqb_encode_e2m1(fake, -1, fake, None) == -4
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        pqb.quantize(torch.zeros(4, 128), "fp8_e4m3", "1x128")
