@@ -1,0 +1,371 @@
+"""Throughput of the quantize-pack path on one MI355X.
+
+Headline workload: the FP8 E4M3 W8A8 set, one step =
+  quantize a bf16 weight [7168, 2048] with 128x128 block scales
+  + quantize bf16 activations [8192, 7168] with 1x128 block scales.
+value = (bytes read + bytes written) per step / time, in GB/s; inputs sit in HBM
+before timing starts, and several buffer sets rotate so the 256 MB Infinity
+Cache cannot serve repeated reads.
+
+Also reported (under "formats"): MXFP4 / NVFP4 on the float32 [3072, 1024] MLP
+weight and on the bf16 [28672, 8192] heavy-tailed weight, INT4 group-128 over
+all 224 Llama-3.1-8B-shaped decoder weights, the FP8 KV write of
+[28 x 32768 x 8 x 128] K and V, and every format on a 1 GiB bf16 tensor.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras]
+       [--no-cpu] [--copy-probe]
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "quantize-pack GB/s (bytes in+out) and % of HBM peak, per format"
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "fp8_1x128_act_8192x7168_counters.json")
+KERNEL_SOURCES = ["precision_quantization_block_amd/csrc/k_fp8.hip",
+                  "precision_quantization_block_amd/csrc/device.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class Engine:
+    """Direct C-ABI calls on preallocated buffers (no allocation while timing)."""
+
+    def __init__(self, torch, pqb):
+        self.torch, self.pqb, self.L = torch, pqb, pqb.lib()
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def alloc(self, fmt, gran, shape, device):
+        t = self.torch
+        s = self.pqb.query_sizes(fmt, gran, *shape)
+        buf = {k: (t.empty((max(v, 16),), dtype=t.uint8, device=device) if v else None)
+               for k, v in s.items()}
+        buf["sizes"] = s
+        return buf
+
+    def quantize(self, x, fmt, gran, shape, buf):
+        P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None  # noqa: E731
+        s = buf["sizes"]
+        rc = self.L.pqb_quantize(P(x), 1 if x.dtype == self.torch.bfloat16 else 0, *shape,
+                                 self.pqb.FORMATS[fmt], self.pqb.GRANS[gran], P(buf["codes"]),
+                                 P(buf["scales"]), P(buf["aux"]), P(buf["workspace"]),
+                                 s["workspace"], self.stream)
+        if rc != 0:
+            raise RuntimeError(f"pqb_quantize {fmt}/{gran}: status {rc}")
+
+    def dequantize(self, buf, fmt, gran, shape, out):
+        P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None  # noqa: E731
+        rc = self.L.pqb_dequantize(P(buf["codes"]), P(buf["scales"]), P(buf["aux"]),
+                                   self.pqb.FORMATS[fmt], self.pqb.GRANS[gran], *shape,
+                                   1 if out.dtype == self.torch.bfloat16 else 0, P(out),
+                                   self.stream)
+        if rc != 0:
+            raise RuntimeError(f"pqb_dequantize {fmt}/{gran}: status {rc}")
+
+    def kv(self, k, v, kc, vc, ks, vs, ws):
+        P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+        layers = k.shape[0]
+        rc = self.L.pqb_kv_write_fp8(P(k), P(v), 1, layers, k.numel() // layers, P(kc), P(vc),
+                                     P(ks), P(vs), P(ws), ws.numel(), self.stream)
+        if rc != 0:
+            raise RuntimeError(f"pqb_kv_write_fp8: status {rc}")
+
+
+def out_bytes(sizes):
+    return sizes["codes"] + sizes["scales"] + sizes["aux"]
+
+
+def time_loop(torch, fn, reps, warmup):
+    """Average time (ms) per call over `reps` back-to-back calls on the current
+    stream, bracketed by two events."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(reps):
+        fn(i)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def rec(bytes_moved, ms, **kw):
+    gbs = bytes_moved / (ms * 1e-3) / 1e9
+    d = {"bytes": int(bytes_moved), "ms": round(ms, 5), "gbs": round(gbs, 1),
+         "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    d.update(kw)
+    return d
+
+
+# ----------------------------------------------------------------------------
+# headline: FP8 W8A8 set
+# ----------------------------------------------------------------------------
+
+def bench_main(torch, eng, synth, steps, warmup, nsets):
+    dev = torch.device("cuda:0")
+    wshape, ashape = (1, 7168, 2048), (1, 8192, 7168)
+    sets = []
+    for i in range(nsets):
+        w = synth.fp8_weight(seed=1 + 1000 * i, device=dev)
+        a = synth.fp8_activation(seed=2 + 1000 * i, device=dev)
+        sets.append((w, a, eng.alloc("fp8_e4m3", "128x128", wshape, dev),
+                     eng.alloc("fp8_e4m3", "1x128", ashape, dev)))
+    w_bytes = 7168 * 2048 * 2 + out_bytes(sets[0][2]["sizes"])
+    a_bytes = 8192 * 7168 * 2 + out_bytes(sets[0][3]["sizes"])
+    step_bytes = w_bytes + a_bytes
+
+    def step(i):
+        w, a, wb, ab = sets[i % nsets]
+        eng.quantize(a, "fp8_e4m3", "1x128", ashape, ab)
+        eng.quantize(w, "fp8_e4m3", "128x128", wshape, wb)
+
+    def act_only(i):
+        _, a, _, ab = sets[i % nsets]
+        eng.quantize(a, "fp8_e4m3", "1x128", ashape, ab)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    # timed region 1: the whole step (both kernels), events only at the ends
+    wall0 = time.perf_counter()
+    ev[0].record()
+    for k in range(steps):
+        step(k)
+    ev[1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = ev[0].elapsed_time(ev[1])
+    # timed region 2: the dominant kernel alone, back to back on the same stream
+    ev[2].record()
+    for k in range(steps):
+        act_only(k)
+    ev[3].record()
+    torch.cuda.synchronize()
+    a_avg = ev[2].elapsed_time(ev[3]) / steps
+    log(f"main: {steps} steps {ms_total:.3f} ms (wall {wall * 1e3:.3f} ms), "
+        f"act kernel avg {a_avg * 1e3:.1f} us")
+    return {"ms_per_step": ms_total / steps, "step_bytes": step_bytes, "act_bytes": a_bytes,
+            "w_bytes": w_bytes, "act_kernel_ms_avg": a_avg, "wall_s": wall}
+
+
+# ----------------------------------------------------------------------------
+# other workloads
+# ----------------------------------------------------------------------------
+
+def bench_extras(torch, eng, synth, reps):
+    dev = torch.device("cuda:0")
+    out = {}
+
+    def one(name, x, fmt, gran, shape, nsets=1, dq_dtype=None):
+        xs = [x] + [x.clone() for _ in range(nsets - 1)]
+        bufs = [eng.alloc(fmt, gran, shape, dev) for _ in range(nsets)]
+        nb = x.numel() * x.element_size() + out_bytes(bufs[0]["sizes"])
+        ms = time_loop(torch, lambda i: eng.quantize(xs[i % nsets], fmt, gran, shape,
+                                                     bufs[i % nsets]), reps, 3)
+        out[name] = rec(nb, ms, op=f"quantize {fmt}/{gran}", shape=list(shape),
+                        dtype=str(x.dtype).replace("torch.", ""))
+        if dq_dtype is not None:
+            o = torch.empty(shape, dtype=dq_dtype, device=dev)
+            nbd = out_bytes(bufs[0]["sizes"]) + o.numel() * o.element_size()
+            ms = time_loop(torch, lambda i: eng.dequantize(bufs[i % nsets], fmt, gran, shape, o),
+                           reps, 3)
+            out[name + "_dequant"] = rec(nbd, ms, op=f"dequantize {fmt} -> "
+                                         f"{str(dq_dtype).replace('torch.', '')}",
+                                         shape=list(shape))
+        log(f"{name}: {out[name]['gbs']} GB/s")
+
+    # float32 MLP weight, MXFP4 and NVFP4 (cache-resident unless rotated: 16 sets)
+    w = synth.mlp_weight_fp32(device=dev)
+    one("mlp3072x1024_f32_mxfp4", w, "mxfp4", "blk32", (1, 3072, 1024), 16, torch.float32)
+    one("mlp3072x1024_f32_nvfp4", w, "nvfp4", "blk16", (1, 3072, 1024), 16, torch.float32)
+    del w
+    # heavy-tailed [28672, 8192] bf16 weight
+    w = synth.heavy_tail_weight(device=dev)
+    one("w28672x8192_bf16_mxfp4", w, "mxfp4", "blk32", (1, 28672, 8192), 2, torch.bfloat16)
+    one("w28672x8192_bf16_nvfp4", w, "nvfp4", "blk16", (1, 28672, 8192), 2, torch.bfloat16)
+    del w
+    # FP8 weight alone (128x128 tiles)
+    w = synth.fp8_weight(device=dev)
+    one("w7168x2048_bf16_fp8_128x128", w, "fp8_e4m3", "128x128", (1, 7168, 2048), 8)
+    del w
+    # 1 GiB bf16 tensor, every format
+    g = synth.gaussian(device=dev)
+    shp = (1, 65536, 8192)
+    for fmt, gran, dq in (("fp8_e4m3", "1x128", torch.bfloat16), ("fp8_e4m3", "128x128", None),
+                          ("fp8_e4m3", "row", None), ("fp8_e4m3", "tensor", None),
+                          ("mxfp4", "blk32", torch.bfloat16), ("nvfp4", "blk16", None),
+                          ("int4_asym", "grp128", torch.bfloat16)):
+        one(f"sweep1GiB_bf16_{fmt}_{gran}", g, fmt, gran, shp, 1, dq)
+    del g
+    torch.cuda.empty_cache()
+    # FP8 KV write
+    k, v = synth.kv_cache(device=dev)
+    kc = torch.empty(k.shape, dtype=torch.uint8, device=dev)
+    vc = torch.empty_like(kc)
+    ks = torch.empty((28,), dtype=torch.float32, device=dev)
+    vs = torch.empty_like(ks)
+    ws = torch.empty((eng.L.pqb_kv_workspace_bytes(28, 32768 * 1024),), dtype=torch.uint8,
+                     device=dev)
+    nb = 2 * k.numel() * 2 + 2 * k.numel() + 2 * 28 * 4
+    ms = time_loop(torch, lambda i: eng.kv(k, v, kc, vc, ks, vs, ws), max(3, reps // 4), 2)
+    out["kv28x32768x8x128_bf16_fp8"] = rec(nb, ms, op="FP8 KV write (per-layer scales)",
+                                           shape=[28, 32768, 8, 128],
+                                           bytes_with_pass1_read=int(nb + 2 * k.numel() * 2))
+    log(f"kv: {out['kv28x32768x8x128_bf16_fp8']['gbs']} GB/s")
+    del k, v, kc, vc
+    torch.cuda.empty_cache()
+    # INT4 over the 224 Llama-3.1-8B-shaped decoder weights (one call per tensor)
+    ws_ = []
+    bufs = []
+    from precision_quantization_block_amd.synth import LLAMA_LAYERS, LLAMA_PROJ
+    nb = 0
+    for layer in range(LLAMA_LAYERS):
+        for p, (_, r, c) in enumerate(LLAMA_PROJ):
+            x = synth.llama_weight(layer, p, device=dev)
+            b = eng.alloc("int4_asym", "grp128", (1, r, c), dev)
+            ws_.append((x, (1, r, c)))
+            bufs.append(b)
+            nb += x.numel() * 2 + out_bytes(b["sizes"])
+
+    def all_int4(i):
+        for (x, shp), b in zip(ws_, bufs):
+            eng.quantize(x, "int4_asym", "grp128", shp, b)
+
+    ms = time_loop(torch, all_int4, 3, 1)
+    out["llama8b_224w_bf16_int4_g128"] = rec(nb, ms, op="INT4 g128 asym, 224 tensors",
+                                             launches=len(bufs))
+    log(f"int4 llama: {out['llama8b_224w_bf16_int4_g128']['gbs']} GB/s")
+    return out
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the headline workload
+# ----------------------------------------------------------------------------
+
+def cpu_baseline(torch, synth, act_rows=1536, w_rows=128):
+    import oracle
+    a = synth.fp8_activation(device="cpu")[:act_rows].contiguous()
+    w = synth.fp8_weight(device="cpu")[:w_rows].contiguous()
+    oracle.lib()
+    t0 = time.perf_counter()
+    ac, as_ = oracle.fp8_quantize(a, "1x128")
+    wc, ws = oracle.fp8_quantize(w, "128x128")
+    dt = time.perf_counter() - t0
+    nbytes = a.numel() * 2 + ac.nbytes + as_.nbytes + w.numel() * 2 + wc.nbytes + ws.nbytes
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {act_rows} of 8192 activation rows (1x128) and first {w_rows} of "
+                      f"7168 weight rows (128x128), single-threaded scalar oracle, "
+                      f"{dt:.1f} s for {nbytes / 1e6:.1f} MB",
+            "host_cpu": _cpu_model(), "host_cores_available": os.cpu_count()}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def copy_probe(torch, reps=3):
+    """A plain elementwise kernel of known traffic (1 GiB read + 1 GiB written),
+    for scaling rocprof's FETCH_SIZE / WRITE_SIZE."""
+    x = torch.ones((1 << 28,), dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    for _ in range(reps):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    log(f"copy probe: {reps} x torch.neg on {x.numel() * 4} bytes")
+
+
+# ----------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--sets", type=int, default=6, help="rotated buffer sets (> 1 GiB total)")
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--reps", type=int, default=20)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the quantizers shard without communication; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import precision_quantization_block_amd as pqb
+    from precision_quantization_block_amd import synth
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    eng = Engine(torch, pqb)
+
+    if args.copy_probe:
+        copy_probe(torch)
+
+    m = bench_main(torch, eng, synth, args.steps, args.warmup, args.sets)
+    value = m["step_bytes"] / (m["ms_per_step"] * 1e-3) / 1e9
+    achieved = m["act_bytes"] / (m["act_kernel_ms_avg"] * 1e-3) / 1e9
+    traffic = None
+    try:
+        with open(COUNTERS_FILE) as f:
+            c = json.load(f)
+        if c.get("kernel_hash") == kernel_hash():
+            traffic = c.get("traffic_bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(m["ms_per_step"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16->e4m3",
+        "data": "synthetic (seeded; see precision_quantization_block_amd/synth.py)",
+        "config": {"workload": "FP8 E4M3 W8A8 set: bf16 weight [7168x2048] 128x128 blocks + "
+                               "bf16 activations [8192x7168] 1x128 blocks",
+                   "step_bytes": m["step_bytes"], "rotated_buffer_sets": args.sets,
+                   "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
+        "roofline": {"bound": "hbm", "kernel": "k_fp8_1x128 (activations [8192x7168] bf16)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": m["act_bytes"],
+                     "avg_launch_ms": round(m["act_kernel_ms_avg"], 5)},
+    }
+    if not args.no_extras:
+        line["formats"] = bench_extras(torch, eng, synth, args.reps)
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(torch, synth)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
