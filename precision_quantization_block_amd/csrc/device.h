@@ -59,26 +59,6 @@ __device__ __forceinline__ Raw8 load_raw8(const float* p) {
   return r;
 }
 
-// Eight float32 results stored as float32 (32 bytes) or RNE bf16 (16 bytes) at
-// unit u of `out` (element 8u).
-__device__ __forceinline__ uint32_t bf16_rne_bits(float v);
-template <bool kBf16Out>
-__device__ __forceinline__ void store_out8(void* out, int64_t u, const float o[8]) {
-  if constexpr (kBf16Out) {
-    st_nt16(reinterpret_cast<uint16_t*>(out) + 8 * u,
-            bf16_rne_bits(o[0]) | (bf16_rne_bits(o[1]) << 16),
-            bf16_rne_bits(o[2]) | (bf16_rne_bits(o[3]) << 16),
-            bf16_rne_bits(o[4]) | (bf16_rne_bits(o[5]) << 16),
-            bf16_rne_bits(o[6]) | (bf16_rne_bits(o[7]) << 16));
-  } else {
-    float* p = reinterpret_cast<float*>(out) + 8 * u;
-    st_nt16(p, __float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
-            __float_as_uint(o[3]));
-    st_nt16(p + 4, __float_as_uint(o[4]), __float_as_uint(o[5]), __float_as_uint(o[6]),
-            __float_as_uint(o[7]));
-  }
-}
-
 // bf16 -> f32 is a 16-bit shift of the bit pattern (exact).
 __device__ __forceinline__ void widen8(const Raw8& r, const uint16_t*, float v[8]) {
   v[0] = as_f(r.a.x << 16); v[1] = as_f(r.a.x & 0xFFFF0000u);
@@ -92,11 +72,19 @@ __device__ __forceinline__ void widen8(const Raw8& r, const float*, float v[8]) 
   v[4] = as_f(r.b.x); v[5] = as_f(r.b.y); v[6] = as_f(r.b.z); v[7] = as_f(r.b.w);
 }
 
-// Largest |v| of eight values (|v| >= 0, inputs finite).
+// Largest |v| of eight values (|v| >= 0, inputs finite): four 3-input maxes
+// (the third input of the last one is 0, which changes nothing for |v| >= 0).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
+}
+__device__ __forceinline__ float min3f(float a, float b, float c) {
+  return __builtin_fminf(__builtin_fminf(a, b), c);
+}
 __device__ __forceinline__ float absmax8(const float v[8]) {
-  float m0 = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fabsf(v[2]));
-  float m1 = fmaxf(fmaxf(fabsf(v[3]), fabsf(v[4])), fabsf(v[5]));
-  return fmaxf(fmaxf(m0, m1), fmaxf(fabsf(v[6]), fabsf(v[7])));
+  const float m1 = max3f(fabsf(v[0]), fabsf(v[1]), fabsf(v[2]));
+  const float m2 = max3f(fabsf(v[3]), fabsf(v[4]), fabsf(v[5]));
+  const float m3 = max3f(fabsf(v[6]), fabsf(v[7]), 0.0f);
+  return max3f(m1, m2, m3);
 }
 
 // ---------------------------------------------------------------------------
@@ -104,80 +92,70 @@ __device__ __forceinline__ float absmax8(const float v[8]) {
 // ---------------------------------------------------------------------------
 
 template <int kCtrl>
-__device__ __forceinline__ float dpp(float v) {
-  return as_f(__builtin_amdgcn_update_dpp(0, (int)as_u(v), kCtrl, 0xF, 0xF, false));
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, 0xF, 0xF, false);
 }
 constexpr int kDppXor1 = 0xB1;       // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;       // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;
 constexpr int kDppMirror = 0x140;
 
-// Max (or min) over aligned groups of kLanes lanes (2, 4, 8 or 16); every
-// lane of the group receives the result.
+// Max over aligned groups of kLanes lanes (2, 4, 8 or 16) of non-negative
+// floats given as bit patterns (for those the unsigned order is the float
+// order, and no NaN handling is needed); every lane of the group receives it.
 template <int kLanes>
-__device__ __forceinline__ float group_max(float v) {
-  if constexpr (kLanes >= 2) v = fmaxf(v, dpp<kDppXor1>(v));
-  if constexpr (kLanes >= 4) v = fmaxf(v, dpp<kDppXor2>(v));
-  if constexpr (kLanes >= 8) v = fmaxf(v, dpp<kDppHalfMirror>(v));
-  if constexpr (kLanes >= 16) v = fmaxf(v, dpp<kDppMirror>(v));
+__device__ __forceinline__ uint32_t group_umax(uint32_t v) {
+  if constexpr (kLanes >= 2) v = max(v, dpp<kDppXor1>(v));
+  if constexpr (kLanes >= 4) v = max(v, dpp<kDppXor2>(v));
+  if constexpr (kLanes >= 8) v = max(v, dpp<kDppHalfMirror>(v));
+  if constexpr (kLanes >= 16) v = max(v, dpp<kDppMirror>(v));
   return v;
 }
 
-template <int kLanes>
-__device__ __forceinline__ float group_min(float v) {
-  if constexpr (kLanes >= 2) v = fminf(v, dpp<kDppXor1>(v));
-  if constexpr (kLanes >= 4) v = fminf(v, dpp<kDppXor2>(v));
-  if constexpr (kLanes >= 8) v = fminf(v, dpp<kDppHalfMirror>(v));
-  if constexpr (kLanes >= 16) v = fminf(v, dpp<kDppMirror>(v));
+// Max of non-negative float bit patterns over the whole wave.
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+  v = group_umax<16>(v);
+  v = max(v, (uint32_t)__shfl_xor((int)v, 16));
+  v = max(v, (uint32_t)__shfl_xor((int)v, 32));
   return v;
 }
 
-// Max over the whole wave (every lane receives it).
-__device__ __forceinline__ float wave_max(float v) {
-  v = group_max<16>(v);
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
-}
+__device__ __forceinline__ float wave_max(float v) { return as_f(wave_umax(as_u(v))); }
 
 // ---------------------------------------------------------------------------
 // Correctly rounded division.
 // ---------------------------------------------------------------------------
 
-// RN(a / s) for a >= 0 from y = RN(1/s).  Markstein's correction (P.
-// Markstein, IBM J. Res. Dev. 34(1), 1990; Muller et al., Handbook of
-// Floating-Point Arithmetic, division with an FMA): when y is within half an
-// ulp of 1/s and q is within one ulp of a/s, the residual r = a - s*q is exact
-// and RN(q + r*y) = RN(a/s).  q0 = RN(a*y) can be up to 1.5 ulp off, so a first
-// correction brings it within one ulp and the second one is exact.  (The
-// residual is carried negated, s*q - a, which changes no value or rounding.)
-// Exactness needs normal residuals: with s >= 2^-60 (every caller guarantees
-// it or takes a true division instead) every quotient at or above 2^-20 is
-// exact.  Smaller quotients come out within a few ulps and non-negative; every
-// code this library derives from such a quotient is the code of zero.
-__device__ __forceinline__ float div_mag(float a, float s, float y) {
-  float q = a * y;
-  float r = __builtin_fmaf(q, s, -a);
-  q = __builtin_fmaf(-r, y, q);
-  r = __builtin_fmaf(q, s, -a);
+// RN(1/s) for every float s in [2^-64, 2^126): the hardware reciprocal and one
+// Newton step, e = 1 - s*r and y = r + e*r, each rounded once.  This equals IEEE
+// division for every float in that range (checked exhaustively on gfx950, all
+// 1.6e9 values); every scale this library forms lies inside it.
+__device__ __forceinline__ float recip_rn(float s) {
+  const float r = __builtin_amdgcn_rcpf(s);
+  return __builtin_fmaf(__builtin_fmaf(-s, r, 1.0f), r, r);
+}
+
+// RN(x / s) from y = RN(1/s): q = RN(x*y), then one Markstein correction with
+// the residual r = s*q - x (P. Markstein, IBM J. Res. Dev. 34(1), 1990; Muller
+// et al., Handbook of Floating-Point Arithmetic, division with an FMA).  For
+// x, s with significands in [1, 2) the result equals IEEE division for all
+// 2^46 pairs (checked exhaustively on gfx950); scaling by powers of two carries
+// this to every x, s whose quotient and residual are normal.  Every step
+// commutes with negating x, and the signed zeros come out as IEEE division
+// gives them (x = -0 gives -0; a negative x never gives +0).  Where the
+// quotient is below about 2^-100 it is only close to RN(x/s); every code this
+// library derives from such a quotient is a code of zero.
+__device__ __forceinline__ float div_rn(float x, float s, float y) {
+  const float q = x * y;
+  const float r = __builtin_fmaf(q, s, -x);
   return __builtin_fmaf(-r, y, q);
 }
 
-// |q| with the sign bit of x: RN(x / s) from the magnitude quotient (IEEE
-// division gives its result the sign of x, zero included, since s > 0).
-__device__ __forceinline__ float with_sign_of(float mag, float x) {
-  return as_f((as_u(mag) & 0x7FFFFFFFu) | (as_u(x) & 0x80000000u));
-}
-
-// RN(a / d) for a constant d with c = RN(1/d): one Markstein correction.  For
-// d in {3, 7, 15, 448, 6, 2688} this was checked against IEEE division for
-// every significand in three consecutive binades (so for every normal a whose
+// RN(a / d) for a constant d with c = RN(1/d): the same correction.  For d in
+// {6, 15, 448, 2688} this was checked against IEEE division for every
+// significand in three consecutive binades (so for every normal a whose
 // quotient is normal).
-__device__ __forceinline__ float div_const(float a, float d, float c) {
-  float q = a * c;
-  float r = __builtin_fmaf(q, d, -a);
-  return __builtin_fmaf(-r, c, q);
-}
+__device__ __forceinline__ float div_const(float a, float d, float c) { return div_rn(a, d, c); }
 
 // ---------------------------------------------------------------------------
 // Rounding to the target grids.
@@ -190,8 +168,10 @@ __device__ __forceinline__ uint32_t cvt_e4m3x2(float a, float b, uint32_t old) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, kHi);
 }
 
+// Four values -> four E4M3 bytes.  The first conversion's untouched high half
+// is overwritten by the second, so its starting value does not matter.
 __device__ __forceinline__ uint32_t e4m3_bytes4(float a, float b, float c, float d) {
-  uint32_t w = cvt_e4m3x2<false>(a, b, 0u);
+  uint32_t w = cvt_e4m3x2<false>(a, b, as_u(a));
   return cvt_e4m3x2<true>(c, d, w);
 }
 
@@ -220,21 +200,55 @@ __device__ __forceinline__ void e2m1_lut_fill(uint8_t* lut, int neg_zero_nibble)
   }
 }
 
-// Round-to-nearest-even of a float32 to bf16 bits.
+// Round-to-nearest-even of a float32 to bf16 bits (integer form).
 __device__ __forceinline__ uint32_t bf16_rne_bits(float v) {
   uint32_t b = as_u(v);
   return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
 }
 
+// Two float32 -> two bf16 (round-to-nearest-even) packed in one dword, low
+// half first; the hardware conversion.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
 // ---------------------------------------------------------------------------
-// E4M3 decode (for dequantization): code -> float (NaN codes never occur).
+// E4M3 decode (for dequantization).  Every E4M3 value is a float32, so the
+// hardware conversion is exact; NaN codes never occur in quantizer output.
 // ---------------------------------------------------------------------------
+template <bool kHi>
+__device__ __forceinline__ f32x2 e4m3x2_decode(uint32_t w) {
+  const auto v = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, kHi);
+  return f32x2{v[0], v[1]};
+}
+
 __device__ __forceinline__ float e4m3_decode(uint32_t c) {
-  uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  // normal: 2^(e-7) * (1 + m/8); subnormal: m * 2^-9
-  uint32_t nb = ((e + 120u) << 23) | (m << 20);
-  float v = e ? as_f(nb) : (float)m * 0x1p-9f;
-  return (c & 0x80u) ? -v : v;
+  return __builtin_amdgcn_cvt_pk_f32_fp8((int)(c & 0xFFu), false)[0];
+}
+
+// Eight float32 results stored as float32 or as RNE bf16 at unit u (element 8u).
+template <bool kBf16Out>
+__device__ __forceinline__ void store_out8(void* out, int64_t u, const float o[8]) {
+  if constexpr (kBf16Out) {
+    st_nt16(reinterpret_cast<uint16_t*>(out) + 8 * u, bf16x2_rne(o[0], o[1]),
+            bf16x2_rne(o[2], o[3]), bf16x2_rne(o[4], o[5]), bf16x2_rne(o[6], o[7]));
+  } else {
+    float* p = reinterpret_cast<float*>(out) + 8 * u;
+    st_nt16(p, as_u(o[0]), as_u(o[1]), as_u(o[2]), as_u(o[3]));
+    st_nt16(p + 4, as_u(o[4]), as_u(o[5]), as_u(o[6]), as_u(o[7]));
+  }
+}
+
+// Bit pattern of max(amax, 1e-12f), the floor every scale formula applies.
+constexpr uint32_t kAmaxFloorBits = __builtin_bit_cast(uint32_t, 1e-12f);
+
+// Wave index that the compiler knows to be uniform across the wave.
+__device__ __forceinline__ int wave_index() {
+  return __builtin_amdgcn_readfirstlane((int)(blockIdx.x * (kBlockThreads / kWave) +
+                                              threadIdx.x / kWave));
 }
 
 }  // namespace pqb

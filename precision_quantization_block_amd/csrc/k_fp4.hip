@@ -14,12 +14,40 @@ namespace {
 
 constexpr float kInv6 = 1.0f / 6.0f;
 
-
 // ---------------------------------------------------------------------------
 // MXFP4: 4 lanes x 8 elements per block.  y = x * 2^-X is exactly RN(x / 2^X)
 // (a product with a power of two), so the E2M1 table sees the page's quotient,
 // signed zeros included (a -0.0 quotient maps to nibble 0).
 // ---------------------------------------------------------------------------
+template <typename T, int kUnr, bool kGuard>
+__device__ __forceinline__ void mx_chunk(const T* __restrict__ x, int64_t u0, int64_t nunits,
+                                         uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                         const uint8_t* lut) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const T* xb = x + u0 * 8;
+  Raw8 raw[kUnr];
+#pragma unroll
+  for (int k = 0; k < kUnr; ++k)
+    raw[k] = (!kGuard || u0 + k * kWave + lane < nunits) ? load_raw8(xb + (k * kWave + lane) * 8)
+                                                           : Raw8{};
+#pragma unroll
+  for (int k = 0; k < kUnr; ++k) {
+    float v[8];
+    widen8(raw[k], x, v);
+    const uint32_t a = max(group_umax<4>(as_u(absmax8(v))), kAmaxFloorBits);
+    const uint32_t ef = a >> 23;                // biased exponent of a normal a
+    const float mul = as_f((256u - ef) << 23);  // 2^-X with X = ef - 129
+    uint32_t w = lut[e2m1_key(v[0] * mul)];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) w |= (uint32_t)lut[e2m1_key(v[i] * mul)] << (4 * i);
+    const int64_t u = u0 + k * kWave + lane;
+    if (!kGuard || u < nunits) {
+      st_nt4(codes + u * 4, w);
+      if ((lane & 3) == 0) scales[u >> 2] = (uint8_t)(ef - 2u);
+    }
+  }
+}
+
 template <typename T, int kUnr>
 __global__ __launch_bounds__(kBlockThreads) void k_mxfp4(const T* __restrict__ x, int64_t nunits,
                                                           uint8_t* __restrict__ codes,
@@ -27,33 +55,13 @@ __global__ __launch_bounds__(kBlockThreads) void k_mxfp4(const T* __restrict__ x
   __shared__ uint8_t lut[kE2M1LutSize];
   e2m1_lut_fill(lut, 0);
   __syncthreads();
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t wave = ((int64_t)blockIdx.x * kBlockThreads + threadIdx.x) / kWave;
   const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
-  const int64_t ntiles = (nunits + kWave - 1) / kWave;
-  for (int64_t t0 = wave * kUnr; t0 < ntiles; t0 += nwaves * kUnr) {
-    Raw8 raw[kUnr];
-#pragma unroll
-    for (int k = 0; k < kUnr; ++k) {
-      const int64_t u = (t0 + k) * kWave + lane;
-      raw[k] = u < nunits ? load_raw8(x + u * 8) : Raw8{};
-    }
-#pragma unroll
-    for (int k = 0; k < kUnr; ++k) {
-      const int64_t u = (t0 + k) * kWave + lane;
-      float v[8];
-      widen8(raw[k], x, v);
-      const float a = fmaxf(group_max<4>(absmax8(v)), 1e-12f);
-      const uint32_t ef = as_u(a) >> 23;          // biased exponent of a normal a
-      const float mul = as_f((256u - ef) << 23);  // 2^-X with X = ef - 129
-      uint32_t w = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) w |= (uint32_t)lut[e2m1_key(v[i] * mul)] << (4 * i);
-      if (u < nunits) {
-        st_nt4(codes + u * 4, w);
-        if ((lane & 3) == 0) scales[u >> 2] = (uint8_t)(ef - 2u);
-      }
-    }
+  for (int64_t t0 = (int64_t)wave_index() * kUnr; t0 * kWave < nunits; t0 += nwaves * kUnr) {
+    const int64_t u0 = t0 * kWave;
+    if (u0 + kUnr * kWave <= nunits)
+      mx_chunk<T, kUnr, false>(x, u0, nunits, codes, scales, lut);
+    else
+      mx_chunk<T, kUnr, true>(x, u0, nunits, codes, scales, lut);
   }
 }
 
@@ -64,7 +72,6 @@ __device__ __forceinline__ float e2m1_value(uint32_t nib) {
   uint32_t b = m >= 2u ? ((((m >> 1) + 126u) << 23) | ((m & 1u) << 22)) : (m ? 0x3F000000u : 0u);
   return as_f(b | ((nib & 8u) << 28));
 }
-
 
 template <bool kBf16Out>
 __global__ __launch_bounds__(kBlockThreads) void k_mxfp4_dequant(const uint8_t* __restrict__ codes,
@@ -87,14 +94,51 @@ __global__ __launch_bounds__(kBlockThreads) void k_mxfp4_dequant(const uint8_t* 
 // elements per block.  Each workgroup rebuilds gs, the E2M1 table and, for all
 // 127 finite block-scale codes, the element scale s and RN(1/s) in LDS.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float block_max4(float m, float* red) {
-  m = wave_max(m);
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  if (lane == 0) red[wave] = m;
-  __syncthreads();
-  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  return m;
+struct NvTables {
+  uint8_t lut[kE2M1LutSize];
+  float se[128], ye[128];
+  uint32_t red[kBlockThreads / kWave];
+};
+
+template <typename T, int kUnr, bool kGuard>
+__device__ __forceinline__ void nv_chunk(const T* __restrict__ xs, int64_t u0, int64_t nunits,
+                                         uint8_t* __restrict__ cs, uint8_t* __restrict__ ss,
+                                         float gs, float ygs, const NvTables& tb) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const T* xb = xs + u0 * 8;
+  Raw8 raw[kUnr];
+#pragma unroll
+  for (int k = 0; k < kUnr; ++k)
+    raw[k] = (!kGuard || u0 + k * kWave + lane < nunits) ? load_raw8(xb + (k * kWave + lane) * 8)
+                                                           : Raw8{};
+#pragma unroll
+  for (int k = 0; k < kUnr; ++k) {
+    float v[8];
+    widen8(raw[k], xs, v);
+    const float ab = as_f(group_umax<2>(as_u(absmax8(v))));
+    const float bq = div_rn(div_const(ab, 6.0f, kInv6), gs, ygs);  // <= 448 (1 + 2^-22)
+    const uint32_t bs = cvt_e4m3x2<false>(bq, 0.0f, 0u) & 0x7Fu;     // bq >= 0
+    const float s = tb.se[bs], ys = tb.ye[bs];
+    uint32_t w = 0;
+    if (s < 2.0f && s >= 0x1p-60f) {
+      // Here every nonzero x has a nonzero RN(x / s) (|x / s| > 2^-150), so its
+      // nibble carries the sign of x even when the magnitude is 0: with -0.0
+      // mapped to +0 first, a quotient of -0 stands for "negative, rounds to
+      // zero" and the table's key 1024 holds nibble 8.
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        w |= (uint32_t)tb.lut[e2m1_key(div_rn(v[i] + 0.0f, s, ys))] << (4 * i);
+    } else {
+      // IEEE division; a -0 quotient has sign(y) = 0, so it becomes +0 first.
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w |= (uint32_t)tb.lut[e2m1_key(v[i] / s + 0.0f)] << (4 * i);
+    }
+    const int64_t u = u0 + k * kWave + lane;
+    if (!kGuard || u < nunits) {
+      st_nt4(cs + u * 4, w);
+      if ((lane & 1) == 0) ss[u >> 1] = (uint8_t)bs;
+    }
+  }
 }
 
 template <typename T, int kUnr>
@@ -105,20 +149,21 @@ __global__ __launch_bounds__(kBlockThreads) void k_nvfp4_quant(const T* __restri
                                                                 float* __restrict__ gs_out,
                                                                 const float* __restrict__ partials,
                                                                 int P) {
-  __shared__ uint8_t lut[kE2M1LutSize];
-  __shared__ float se[128], ye[128];
-  __shared__ float red[kBlockThreads / kWave];
+  __shared__ NvTables tb;
   const int64_t b = blockIdx.y;
-  float m = 0.0f;
-  for (int i = threadIdx.x; i < P; i += kBlockThreads) m = fmaxf(m, partials[b * P + i]);
-  const float amax_t = block_max4(m, red);
-  const float gs = fmaxf(amax_t, 1e-12f) / 2688.0f;  // 448 * 6
-  const float ygs = 1.0f / gs;
-  e2m1_lut_fill(lut, 8);
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < P; i += kBlockThreads) m = max(m, as_u(partials[b * P + i]));
+  m = wave_umax(m);
+  if ((threadIdx.x & (kWave - 1)) == 0) tb.red[threadIdx.x / kWave] = m;
+  e2m1_lut_fill(tb.lut, 8);
+  __syncthreads();
+  m = max(max(tb.red[0], tb.red[1]), max(tb.red[2], tb.red[3]));
+  const float gs = as_f(max(m, kAmaxFloorBits)) / 2688.0f;  // 448 * 6
+  const float ygs = recip_rn(gs);
   for (int c = threadIdx.x; c < 127; c += kBlockThreads) {
     const float sc = fmaxf(e4m3_decode((uint32_t)c), 1e-12f) * gs;
-    se[c] = sc;
-    ye[c] = 1.0f / sc;
+    tb.se[c] = sc;
+    tb.ye[c] = 1.0f / sc;
   }
   __syncthreads();
   if (blockIdx.x == 0 && threadIdx.x == 0) gs_out[b] = gs;
@@ -127,45 +172,13 @@ __global__ __launch_bounds__(kBlockThreads) void k_nvfp4_quant(const T* __restri
   uint8_t* cs = codes + b * (per_slice / 2);
   uint8_t* ss = scales + b * (per_slice / 16);
   const int64_t nunits = per_slice / 8;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t wave = ((int64_t)blockIdx.x * kBlockThreads + threadIdx.x) / kWave;
   const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
-  const int64_t ntiles = (nunits + kWave - 1) / kWave;
-  for (int64_t t0 = wave * kUnr; t0 < ntiles; t0 += nwaves * kUnr) {
-    Raw8 raw[kUnr];
-#pragma unroll
-    for (int k = 0; k < kUnr; ++k) {
-      const int64_t u = (t0 + k) * kWave + lane;
-      raw[k] = u < nunits ? load_raw8(xs + u * 8) : Raw8{};
-    }
-#pragma unroll
-    for (int k = 0; k < kUnr; ++k) {
-      const int64_t u = (t0 + k) * kWave + lane;
-      float v[8];
-      widen8(raw[k], xs, v);
-      const float ab = group_max<2>(absmax8(v));
-      const float bq = div_mag(div_const(ab, 6.0f, kInv6), gs, ygs);  // <= 448 (1 + 2^-22)
-      const uint32_t bs = cvt_e4m3x2<false>(bq, 0.0f, 0u) & 0x7Fu;  // bq >= 0
-      const float s = se[bs], ys = ye[bs];
-      uint32_t w = 0;
-      if (s < 2.0f && s >= 0x1p-60f) {
-        // Every nonzero x has a nonzero RN(x / s) here (|x / s| > 2^-150), so
-        // the nibble's sign is that of x (with -0.0 first mapped to +0).
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float xi = v[i] + 0.0f;
-          const float q = with_sign_of(div_mag(fabsf(xi), s, ys), xi);
-          w |= (uint32_t)lut[e2m1_key(q)] << (4 * i);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) w |= (uint32_t)lut[e2m1_key(v[i] / s + 0.0f)] << (4 * i);
-      }
-      if (u < nunits) {
-        st_nt4(cs + u * 4, w);
-        if ((lane & 1) == 0) ss[u >> 1] = (uint8_t)bs;
-      }
-    }
+  for (int64_t t0 = (int64_t)wave_index() * kUnr; t0 * kWave < nunits; t0 += nwaves * kUnr) {
+    const int64_t u0 = t0 * kWave;
+    if (u0 + kUnr * kWave <= nunits)
+      nv_chunk<T, kUnr, false>(xs, u0, nunits, cs, ss, gs, ygs, tb);
+    else
+      nv_chunk<T, kUnr, true>(xs, u0, nunits, cs, ss, gs, ygs, tb);
   }
 }
 
@@ -229,7 +242,7 @@ hipError_t launch_mxfp4(const void* x, bool bf16, int64_t n, uint8_t* codes, uin
 hipError_t launch_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, int64_t n,
                                 bool out_bf16, void* out, hipStream_t st) {
   const int64_t nunits = n / 8;
-  const int grid = grid_cap(nunits, kBlockThreads, 1 << 20);
+  const int grid = grid_cap(nunits, (int64_t)kBlockThreads * 4, 1 << 20);
   if (out_bf16)
     hipLaunchKernelGGL(k_mxfp4_dequant<true>, dim3(grid), dim3(kBlockThreads), 0, st, codes,
                        scales, nunits, out);
@@ -265,7 +278,7 @@ hipError_t launch_nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, con
                                 int64_t batch, int64_t per_slice, bool out_bf16, void* out,
                                 hipStream_t st) {
   const int64_t nunits = per_slice / 8;
-  const dim3 grid(grid_cap(nunits, kBlockThreads, 8192), (unsigned)batch);
+  const dim3 grid(grid_cap(nunits, (int64_t)kBlockThreads * 4, 8192), (unsigned)batch);
   if (out_bf16)
     hipLaunchKernelGGL(k_nvfp4_dequant<true>, grid, dim3(kBlockThreads), 0, st, codes, scales, gs,
                        per_slice, out);

@@ -1,9 +1,10 @@
-// FP8 E4M3 quantize kernels: 1x128 blocks, 128x128 tiles, rows, per tensor.
+// FP8 E4M3 quantize / dequantize kernels: 1x128 blocks, 128x128 tiles, rows,
+// per tensor.
 //
 // Scale of a scope: s = RN(max(amax, 1e-12) / 448); codes are E4M3(RN(x / s))
-// (the page "量化部署实战", section 伪量化实现).  The clamp to +-448 that the
-// page applies before the cast never binds: |x| <= amax gives |x/s| <= 448 up
-// to one rounding, which still rounds to 448.
+// (page "量化部署实战", section 伪量化实现).  The clamp to +-448 that the page
+// applies before the cast never binds here: |x| <= amax gives |x/s| <= 448 up to
+// one rounding, which still rounds to 448.
 #include "device.h"
 #include "launch.h"
 
@@ -12,59 +13,80 @@ namespace {
 
 constexpr float kInv448 = 1.0f / 448.0f;  // RN(1/448), folded at compile time
 
-__device__ __forceinline__ float fp8_scale(float amax) {
-  return div_const(fmaxf(amax, 1e-12f), 448.0f, kInv448);
+// s from the bit pattern of a scope's amax (a non-negative float).
+__device__ __forceinline__ float fp8_scale_bits(uint32_t amax_bits) {
+  return div_const(as_f(max(amax_bits, kAmaxFloorBits)), 448.0f, kInv448);
 }
 
-// RN(x / s) with the sign of x (E4M3 keeps the sign of every quotient).
-__device__ __forceinline__ float fp8_quot(float x, float s, float y) {
-  return with_sign_of(div_mag(fabsf(x), s, y), x);
-}
-
-// Quantize eight values with scale s (and y = RN(1/s)); two code dwords.
+// Eight values -> eight E4M3 codes (two dwords) with scale s and y = RN(1/s).
 __device__ __forceinline__ uint2 fp8_pack8(const float v[8], float s, float y) {
-  uint32_t w0 = e4m3_bytes4(fp8_quot(v[0], s, y), fp8_quot(v[1], s, y), fp8_quot(v[2], s, y),
-                            fp8_quot(v[3], s, y));
-  uint32_t w1 = e4m3_bytes4(fp8_quot(v[4], s, y), fp8_quot(v[5], s, y), fp8_quot(v[6], s, y),
-                            fp8_quot(v[7], s, y));
+  const uint32_t w0 = e4m3_bytes4(div_rn(v[0], s, y), div_rn(v[1], s, y), div_rn(v[2], s, y),
+                                  div_rn(v[3], s, y));
+  const uint32_t w1 = e4m3_bytes4(div_rn(v[4], s, y), div_rn(v[5], s, y), div_rn(v[6], s, y),
+                                  div_rn(v[7], s, y));
   return make_uint2(w0, w1);
 }
 
 __device__ __forceinline__ void store_codes8(uint8_t* p, uint2 w) { st_nt8(p, w.x, w.y); }
 
+template <typename T>
+__device__ __forceinline__ float ld1(const T* p);
+template <>
+__device__ __forceinline__ float ld1<uint16_t>(const uint16_t* p) {
+  return as_f((uint32_t)*p << 16);
+}
+template <>
+__device__ __forceinline__ float ld1<float>(const float* p) {
+  return *p;
+}
+
+__device__ __forceinline__ uint8_t e4m3_byte(float q) {
+  return (uint8_t)(cvt_e4m3x2<false>(q, 0.0f, 0u) & 0xFFu);
+}
+
 // ---------------------------------------------------------------------------
 // 1x128: a 128-element block is 16 lanes x 8 elements, one DPP row.  Each wave
-// walks kUnr consecutive tiles of 64 units (8 elements each) per iteration.
+// streams kUnr consecutive tiles of 64 units (8 elements each) per iteration;
+// only the last, partial chunk of the tensor checks bounds.
 // ---------------------------------------------------------------------------
+template <typename T, int kUnr, bool kGuard>
+__device__ __forceinline__ void fp8_1x128_chunk(const T* __restrict__ x, int64_t u0, int64_t nunits,
+                                                uint8_t* __restrict__ codes,
+                                                float* __restrict__ scales) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const T* xb = x + u0 * 8;
+  Raw8 raw[kUnr];
+#pragma unroll
+  for (int k = 0; k < kUnr; ++k)
+    raw[k] = (!kGuard || u0 + k * kWave + lane < nunits) ? load_raw8(xb + (k * kWave + lane) * 8)
+                                                           : Raw8{};
+#pragma unroll
+  for (int k = 0; k < kUnr; ++k) {
+    float v[8];
+    widen8(raw[k], x, v);
+    const float s = fp8_scale_bits(group_umax<16>(as_u(absmax8(v))));
+    const float y = recip_rn(s);
+    const uint2 w = fp8_pack8(v, s, y);
+    const int64_t u = u0 + k * kWave + lane;
+    if (!kGuard || u < nunits) {
+      store_codes8(codes + u * 8, w);
+      if ((lane & 15) == 0) scales[u >> 4] = s;
+    }
+  }
+}
+
 template <typename T, int kUnr>
 __global__ __launch_bounds__(kBlockThreads) void k_fp8_1x128(const T* __restrict__ x,
                                                               int64_t nunits,
                                                               uint8_t* __restrict__ codes,
                                                               float* __restrict__ scales) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t wave = ((int64_t)blockIdx.x * kBlockThreads + threadIdx.x) / kWave;
   const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
-  const int64_t ntiles = (nunits + kWave - 1) / kWave;
-  for (int64_t t0 = wave * kUnr; t0 < ntiles; t0 += nwaves * kUnr) {
-    Raw8 raw[kUnr];
-#pragma unroll
-    for (int k = 0; k < kUnr; ++k) {
-      const int64_t u = (t0 + k) * kWave + lane;
-      raw[k] = u < nunits ? load_raw8(x + u * 8) : Raw8{};
-    }
-#pragma unroll
-    for (int k = 0; k < kUnr; ++k) {
-      const int64_t u = (t0 + k) * kWave + lane;
-      float v[8];
-      widen8(raw[k], x, v);
-      const float s = fp8_scale(group_max<16>(absmax8(v)));
-      const float y = 1.0f / s;
-      const uint2 w = fp8_pack8(v, s, y);
-      if (u < nunits) {
-        store_codes8(codes + u * 8, w);
-        if ((lane & 15) == 0) scales[u >> 4] = s;
-      }
-    }
+  for (int64_t t0 = (int64_t)wave_index() * kUnr; t0 * kWave < nunits; t0 += nwaves * kUnr) {
+    const int64_t u0 = t0 * kWave;
+    if (u0 + kUnr * kWave <= nunits)
+      fp8_1x128_chunk<T, kUnr, false>(x, u0, nunits, codes, scales);
+    else
+      fp8_1x128_chunk<T, kUnr, true>(x, u0, nunits, codes, scales);
   }
 }
 
@@ -79,14 +101,14 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_128x128(const T* __restri
                                                                 int br,
                                                                 uint8_t* __restrict__ codes,
                                                                 float* __restrict__ scales) {
-  __shared__ float red[kBlockThreads / kWave];
-  const int64_t tiles_c = cols / 128, tiles_r = rows / br;
+  __shared__ uint32_t red[kBlockThreads / kWave];
+  const int64_t tiles_c = cols / 128;
   const int64_t t = blockIdx.x;
-  const int64_t tc = t % tiles_c, trb = t / tiles_c;  // trb = b * tiles_r + tr
+  const int64_t tc = t % tiles_c, trb = t / tiles_c;  // trb = b * (rows / br) + tile row
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int r0 = wave * 4 + (lane >> 4);
-  const int64_t base = trb * br * cols + tc * 128 + (lane & 15) * 8;  // rows of a slice are
-                                                                      // contiguous across b
+  // rows of consecutive batch slices are contiguous, so tile row trb starts at row trb*br
+  const int64_t base = trb * br * cols + tc * 128 + (lane & 15) * 8;
   Raw8 raw[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
@@ -94,18 +116,18 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_128x128(const T* __restri
     raw[k] = r < br ? load_raw8(x + base + (int64_t)r * cols) : Raw8{};
   }
   float v[8][8];
-  float m = 0.0f;
+  uint32_t m = 0;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     widen8(raw[k], x, v[k]);
-    m = fmaxf(m, absmax8(v[k]));
+    m = max(m, as_u(absmax8(v[k])));
   }
-  m = wave_max(m);
+  m = wave_umax(m);
   if (lane == 0) red[wave] = m;
   __syncthreads();
-  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float s = fp8_scale(m);
-  const float y = 1.0f / s;
+  m = max(max(red[0], red[1]), max(red[2], red[3]));
+  const float s = fp8_scale_bits(m);
+  const float y = recip_rn(s);
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int r = r0 + 16 * k;
@@ -125,8 +147,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_row_vec(const T* __restri
                                                                 uint8_t* __restrict__ codes,
                                                                 float* __restrict__ scales) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t row = (int64_t)blockIdx.x * (kBlockThreads / kWave) + threadIdx.x / kWave;
-  if (row >= nrows) return;  // whole wave leaves together
+  const int64_t row = wave_index();
+  if (row >= nrows) return;  // the whole wave leaves together
   const int64_t upr = cols / 8;
   const T* xr = x + row * cols;
   Raw8 raw[kMaxU];
@@ -135,16 +157,15 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_row_vec(const T* __restri
     const int64_t u = (int64_t)k * kWave + lane;
     raw[k] = u < upr ? load_raw8(xr + u * 8) : Raw8{};
   }
-  float m = 0.0f;
+  uint32_t m = 0;
 #pragma unroll
   for (int k = 0; k < kMaxU; ++k) {
     float v[8];
     widen8(raw[k], x, v);
-    m = fmaxf(m, absmax8(v));
+    m = max(m, as_u(absmax8(v)));
   }
-  m = wave_max(m);
-  const float s = fp8_scale(m);
-  const float y = 1.0f / s;
+  const float s = fp8_scale_bits(wave_umax(m));
+  const float y = recip_rn(s);
 #pragma unroll
   for (int k = 0; k < kMaxU; ++k) {
     const int64_t u = (int64_t)k * kWave + lane;
@@ -159,35 +180,19 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_row_vec(const T* __restri
 // Per row, any width: one wave per row, element-wise, reading the row twice
 // (the second read is served by the caches).
 template <typename T>
-__device__ __forceinline__ float ld1(const T* p);
-template <>
-__device__ __forceinline__ float ld1<uint16_t>(const uint16_t* p) {
-  return as_f((uint32_t)*p << 16);
-}
-template <>
-__device__ __forceinline__ float ld1<float>(const float* p) {
-  return *p;
-}
-
-__device__ __forceinline__ uint8_t e4m3_byte(float q) {
-  return (uint8_t)(cvt_e4m3x2<false>(q, 0.0f, 0u) & 0xFFu);
-}
-
-template <typename T>
 __global__ __launch_bounds__(kBlockThreads) void k_fp8_row_any(const T* __restrict__ x,
                                                                 int64_t nrows, int64_t cols,
                                                                 uint8_t* __restrict__ codes,
                                                                 float* __restrict__ scales) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t row = (int64_t)blockIdx.x * (kBlockThreads / kWave) + threadIdx.x / kWave;
+  const int64_t row = wave_index();
   if (row >= nrows) return;
   const T* xr = x + row * cols;
-  float m = 0.0f;
-  for (int64_t c = lane; c < cols; c += kWave) m = fmaxf(m, fabsf(ld1(xr + c)));
-  m = wave_max(m);
-  const float s = fp8_scale(m);
-  const float y = 1.0f / s;
-  for (int64_t c = lane; c < cols; c += kWave) codes[row * cols + c] = e4m3_byte(fp8_quot(ld1(xr + c), s, y));
+  uint32_t m = 0;
+  for (int64_t c = lane; c < cols; c += kWave) m = max(m, as_u(fabsf(ld1(xr + c))));
+  const float s = fp8_scale_bits(wave_umax(m));
+  const float y = recip_rn(s);
+  for (int64_t c = lane; c < cols; c += kWave) codes[row * cols + c] = e4m3_byte(div_rn(ld1(xr + c), s, y));
   if (lane == 0) scales[row] = s;
 }
 
@@ -203,12 +208,13 @@ struct TensorArgs {
   float* scales[2];
 };
 
-__device__ __forceinline__ float block_max(float m, float* red) {
-  m = wave_max(m);
+// Max of non-negative float bit patterns over the workgroup (all threads get it).
+__device__ __forceinline__ uint32_t block_umax(uint32_t m, uint32_t* red) {
+  m = wave_umax(m);
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   if (lane == 0) red[wave] = m;
   __syncthreads();
-  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  m = max(max(red[0], red[1]), max(red[2], red[3]));
   __syncthreads();
   return m;
 }
@@ -216,42 +222,44 @@ __device__ __forceinline__ float block_max(float m, float* red) {
 template <typename T, bool kVec>
 __global__ __launch_bounds__(kBlockThreads) void k_amax_partial(TensorArgs a, int64_t per_slice,
                                                                  float* __restrict__ partials) {
-  __shared__ float red[kBlockThreads / kWave];
+  __shared__ uint32_t red[kBlockThreads / kWave];
   const int64_t b = blockIdx.y, P = gridDim.x;
   const T* xs = reinterpret_cast<const T*>(a.x[blockIdx.z]) + b * per_slice;
-  float m = 0.0f;
+  uint32_t m = 0;
   if constexpr (kVec) {
     const int64_t nunits = per_slice / 8;
     const int64_t stride = P * kBlockThreads;
     int64_t u = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
     for (; u + 3 * stride < nunits; u += 4 * stride) {
-      Raw8 r0 = load_raw8(xs + u * 8), r1 = load_raw8(xs + (u + stride) * 8);
-      Raw8 r2 = load_raw8(xs + (u + 2 * stride) * 8), r3 = load_raw8(xs + (u + 3 * stride) * 8);
+      const Raw8 r0 = load_raw8(xs + u * 8), r1 = load_raw8(xs + (u + stride) * 8);
+      const Raw8 r2 = load_raw8(xs + (u + 2 * stride) * 8);
+      const Raw8 r3 = load_raw8(xs + (u + 3 * stride) * 8);
       float v[8];
-      widen8(r0, xs, v); m = fmaxf(m, absmax8(v));
-      widen8(r1, xs, v); m = fmaxf(m, absmax8(v));
-      widen8(r2, xs, v); m = fmaxf(m, absmax8(v));
-      widen8(r3, xs, v); m = fmaxf(m, absmax8(v));
+      widen8(r0, xs, v); m = max(m, as_u(absmax8(v)));
+      widen8(r1, xs, v); m = max(m, as_u(absmax8(v)));
+      widen8(r2, xs, v); m = max(m, as_u(absmax8(v)));
+      widen8(r3, xs, v); m = max(m, as_u(absmax8(v)));
     }
     for (; u < nunits; u += stride) {
       float v[8];
       widen8(load_raw8(xs + u * 8), xs, v);
-      m = fmaxf(m, absmax8(v));
+      m = max(m, as_u(absmax8(v)));
     }
   } else {
     for (int64_t i = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x; i < per_slice;
          i += P * kBlockThreads)
-      m = fmaxf(m, fabsf(ld1(xs + i)));
+      m = max(m, as_u(fabsf(ld1(xs + i))));
   }
-  m = block_max(m, red);
-  if (threadIdx.x == 0) partials[((int64_t)blockIdx.z * gridDim.y + b) * P + blockIdx.x] = m;
+  m = block_umax(m, red);
+  if (threadIdx.x == 0) partials[((int64_t)blockIdx.z * gridDim.y + b) * P + blockIdx.x] = as_f(m);
 }
 
 // Reduce the P partials of one slice (all threads receive the maximum).
-__device__ __forceinline__ float reduce_partials(const float* __restrict__ p, int P, float* red) {
-  float m = 0.0f;
-  for (int i = threadIdx.x; i < P; i += kBlockThreads) m = fmaxf(m, p[i]);
-  return block_max(m, red);
+__device__ __forceinline__ uint32_t reduce_partials(const float* __restrict__ p, int P,
+                                                    uint32_t* red) {
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < P; i += kBlockThreads) m = max(m, as_u(p[i]));
+  return block_umax(m, red);
 }
 
 template <typename T, bool kVec>
@@ -259,12 +267,11 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_tensor_quant(TensorArgs a
                                                                      int64_t per_slice,
                                                                      const float* __restrict__ partials,
                                                                      int P) {
-  __shared__ float red[kBlockThreads / kWave];
+  __shared__ uint32_t red[kBlockThreads / kWave];
   const int64_t b = blockIdx.y;
   const int tz = blockIdx.z;
-  const float m = reduce_partials(partials + ((int64_t)tz * gridDim.y + b) * P, P, red);
-  const float s = fp8_scale(m);
-  const float y = 1.0f / s;
+  const float s = fp8_scale_bits(reduce_partials(partials + ((int64_t)tz * gridDim.y + b) * P, P, red));
+  const float y = recip_rn(s);
   const T* xs = reinterpret_cast<const T*>(a.x[tz]) + b * per_slice;
   uint8_t* cs = a.codes[tz] + b * per_slice;
   const int64_t stride = (int64_t)gridDim.x * kBlockThreads;
@@ -272,7 +279,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_tensor_quant(TensorArgs a
     const int64_t nunits = per_slice / 8;
     int64_t u = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
     for (; u + stride < nunits; u += 2 * stride) {
-      Raw8 r0 = load_raw8(xs + u * 8), r1 = load_raw8(xs + (u + stride) * 8);
+      const Raw8 r0 = load_raw8(xs + u * 8), r1 = load_raw8(xs + (u + stride) * 8);
       float v[8];
       widen8(r0, xs, v);
       store_codes8(cs + u * 8, fp8_pack8(v, s, y));
@@ -286,44 +293,82 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_tensor_quant(TensorArgs a
     }
   } else {
     for (int64_t i = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x; i < per_slice; i += stride)
-      cs[i] = e4m3_byte(fp8_quot(ld1(xs + i), s, y));
+      cs[i] = e4m3_byte(div_rn(ld1(xs + i), s, y));
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) a.scales[tz][b] = s;
 }
 
 // ---------------------------------------------------------------------------
-// Dequantization: out = dec(code) * s, float32 or RNE to bf16.  One workgroup
-// row-chunk at a time: blockIdx.y strides over the rows of all slices.
+// Dequantization: out = dec(code) * s, float32 or RNE bf16.
 // ---------------------------------------------------------------------------
-template <bool kBf16Out>
-__device__ __forceinline__ void store_out(void* out, int64_t i, float v) {
-  if constexpr (kBf16Out)
-    reinterpret_cast<uint16_t*>(out)[i] = (uint16_t)bf16_rne_bits(v);
-  else
-    reinterpret_cast<float*>(out)[i] = v;
+__device__ __forceinline__ void fp8_decode8(uint2 w, float s, float o[8]) {
+  const f32x2 a = e4m3x2_decode<false>(w.x), b = e4m3x2_decode<true>(w.x);
+  const f32x2 c = e4m3x2_decode<false>(w.y), d = e4m3x2_decode<true>(w.y);
+  o[0] = a.x * s; o[1] = a.y * s; o[2] = b.x * s; o[3] = b.y * s;
+  o[4] = c.x * s; o[5] = c.y * s; o[6] = d.x * s; o[7] = d.y * s;
 }
 
+__device__ __forceinline__ uint2 ld_codes8(const uint8_t* p) {
+  return *reinterpret_cast<const uint2*>(p);
+}
+
+// 1x128: the scale of unit u (8 elements) is scales[u / 16].
 template <bool kBf16Out>
-__global__ __launch_bounds__(kBlockThreads) void k_fp8_dequant(const uint8_t* __restrict__ codes,
-                                                                const float* __restrict__ scales,
-                                                                int gran, int64_t nrows_total,
-                                                                int64_t rows, int64_t cols, int br,
-                                                                void* __restrict__ out) {
-  for (int64_t gr = blockIdx.y; gr < nrows_total; gr += gridDim.y) {
+__global__ __launch_bounds__(kBlockThreads) void k_fp8_dequant_1x128(const uint8_t* __restrict__ codes,
+                                                                      const float* __restrict__ scales,
+                                                                      int64_t nunits,
+                                                                      void* __restrict__ out) {
+  for (int64_t u = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x; u < nunits;
+       u += (int64_t)gridDim.x * kBlockThreads) {
+    float o[8];
+    fp8_decode8(ld_codes8(codes + u * 8), scales[u >> 4], o);
+    store_out8<kBf16Out>(out, u, o);
+  }
+}
+
+// Other scopes, one wave per row (rows of all slices in sequence): the row's
+// scale index is formed once per row; only the 128-column block varies.
+template <bool kBf16Out, bool kVec>
+__global__ __launch_bounds__(kBlockThreads) void k_fp8_dequant_rows(const uint8_t* __restrict__ codes,
+                                                                     const float* __restrict__ scales,
+                                                                     int gran, int64_t nrows_total,
+                                                                     int64_t rows, int64_t cols,
+                                                                     int br,
+                                                                     void* __restrict__ out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t nw = (int64_t)gridDim.x * (kBlockThreads / kWave);
+  for (int64_t gr = wave_index(); gr < nrows_total; gr += nw) {
     const int64_t b = gr / rows, r = gr - b * rows;
-    for (int64_t c = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x; c < cols;
-         c += (int64_t)gridDim.x * kBlockThreads) {
-      int64_t si;
-      switch (gran) {
-        case 0: si = b; break;
-        case 1: si = gr; break;
-        case 2: si = gr * (cols / 128) + c / 128; break;
-        default: si = (b * (rows / br) + r / br) * (cols / 128) + c / 128; break;
+    int64_t si0 = 0, tile_stride = 0;  // scale index of column c: si0 + (c / 128) * tile_stride
+    switch (gran) {
+      case 0: si0 = b; break;
+      case 1: si0 = gr; break;
+      default: si0 = (b * (rows / br) + r / br) * (cols / 128); tile_stride = 1; break;
+    }
+    if constexpr (kVec) {
+      for (int64_t u = lane; u < cols / 8; u += kWave) {
+        float o[8];
+        fp8_decode8(ld_codes8(codes + gr * cols + u * 8), scales[si0 + (u >> 4) * tile_stride], o);
+        store_out8<kBf16Out>(out, gr * (cols / 8) + u, o);
       }
-      const int64_t i = gr * cols + c;
-      store_out<kBf16Out>(out, i, e4m3_decode(codes[i]) * scales[si]);
+    } else {
+      for (int64_t c = lane; c < cols; c += kWave) {
+        const float v = e4m3_decode(codes[gr * cols + c]) * scales[si0 + (c >> 7) * tile_stride];
+        if constexpr (kBf16Out)
+          reinterpret_cast<uint16_t*>(out)[gr * cols + c] = (uint16_t)bf16x2_rne(v, 0.0f);
+        else
+          reinterpret_cast<float*>(out)[gr * cols + c] = v;
+      }
     }
   }
+}
+
+__global__ __launch_bounds__(kBlockThreads) void k_encode_e4m3(const float* __restrict__ y,
+                                                               int64_t n,
+                                                               uint8_t* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * kBlockThreads)
+    out[i] = e4m3_byte(y[i]);
 }
 
 inline int blocks_for(int64_t work, int64_t per_block, int64_t cap) {
@@ -351,7 +396,7 @@ hipError_t launch_fp8_1x128(const void* x, bool bf16, int64_t n, uint8_t* codes,
   constexpr int kUnr = 4;
   const int64_t nunits = n / 8;
   const int64_t ntiles = (nunits + kWave - 1) / kWave;
-  const int grid = blocks_for(ntiles, (int64_t)kUnr * (kBlockThreads / kWave), 1 << 30);
+  const int grid = blocks_for(ntiles, (int64_t)kUnr * (kBlockThreads / kWave), 1 << 29);
   if (bf16)
     hipLaunchKernelGGL((k_fp8_1x128<uint16_t, kUnr>), dim3(grid), dim3(kBlockThreads), 0, st,
                        (const uint16_t*)x, nunits, codes, scales);
@@ -458,27 +503,33 @@ hipError_t launch_fp8_tensor(const void* const* x, bool bf16, int ntensors, int6
 hipError_t launch_fp8_dequant(const uint8_t* codes, const float* scales, int gran, int64_t batch,
                               int64_t rows, int64_t cols, bool out_bf16, void* out,
                               hipStream_t st) {
+  const int64_t n = batch * rows * cols;
+  if (gran == 2) {  // 1x128: cols % 128 == 0, flat
+    const int64_t nunits = n / 8;
+    const int grid = blocks_for(nunits, (int64_t)kBlockThreads * 4, 1 << 20);
+    if (out_bf16)
+      hipLaunchKernelGGL(k_fp8_dequant_1x128<true>, dim3(grid), dim3(kBlockThreads), 0, st, codes,
+                         scales, nunits, out);
+    else
+      hipLaunchKernelGGL(k_fp8_dequant_1x128<false>, dim3(grid), dim3(kBlockThreads), 0, st,
+                         codes, scales, nunits, out);
+    return hipGetLastError();
+  }
   const int br = (int)(rows < 128 ? rows : 128);
   const int64_t nrows = batch * rows;
-  const dim3 grid(blocks_for(cols, kBlockThreads, 64), (unsigned)(nrows < 65535 ? nrows : 65535));
-  if (out_bf16)
-    hipLaunchKernelGGL(k_fp8_dequant<true>, grid, dim3(kBlockThreads), 0, st, codes, scales, gran,
-                       nrows, rows, cols, br, out);
-  else
-    hipLaunchKernelGGL(k_fp8_dequant<false>, grid, dim3(kBlockThreads), 0, st, codes, scales,
-                       gran, nrows, rows, cols, br, out);
+  const int grid = blocks_for(nrows, kBlockThreads / kWave, 1 << 16);
+  const bool vec = cols % 8 == 0;
+#define PQB_DQ(B, V)                                                                           \
+  hipLaunchKernelGGL((k_fp8_dequant_rows<B, V>), dim3(grid), dim3(kBlockThreads), 0, st, codes, \
+                     scales, gran, nrows, rows, cols, br, out)
+  if (out_bf16) {
+    if (vec) PQB_DQ(true, true); else PQB_DQ(true, false);
+  } else {
+    if (vec) PQB_DQ(false, true); else PQB_DQ(false, false);
+  }
+#undef PQB_DQ
   return hipGetLastError();
 }
-
-namespace {
-__global__ __launch_bounds__(kBlockThreads) void k_encode_e4m3(const float* __restrict__ y,
-                                                               int64_t n,
-                                                               uint8_t* __restrict__ out) {
-  for (int64_t i = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * kBlockThreads)
-    out[i] = e4m3_byte(y[i]);
-}
-}  // namespace
 
 hipError_t launch_encode_e4m3(const float* y, int64_t n, uint8_t* out, hipStream_t st) {
   hipLaunchKernelGGL(k_encode_e4m3, dim3(blocks_for(n, kBlockThreads, 4096)), dim3(kBlockThreads),
