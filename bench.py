@@ -2,7 +2,8 @@
 
 Headline workload: the FP8 E4M3 W8A8 set, one step =
   quantize a bf16 weight [7168, 2048] with 128x128 block scales
-  + quantize bf16 activations [8192, 7168] with 1x128 block scales.
+  + quantize bf16 activations [8192, 7168] with 1x128 block scales,
+issued as one pqb_quantize_batch call (a single fused launch).
 value = (bytes read + bytes written) per step / time, in GB/s; inputs sit in HBM
 before timing starts, and several buffer sets rotate so the 256 MB Infinity
 Cache cannot serve repeated reads.
@@ -29,8 +30,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "quantize-pack GB/s (bytes in+out) and % of HBM peak, per format"
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "fp8_1x128_act_8192x7168_counters.json")
-KERNEL_SOURCES = ["precision_quantization_block_amd/csrc/k_fp8.hip",
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "k_multi_fp8_w8a8_7168x2048_8192x7168_counters.json")
+KERNEL_SOURCES = ["precision_quantization_block_amd/csrc/k_multi.hip",
+                  "precision_quantization_block_amd/csrc/quant.h",
                   "precision_quantization_block_amd/csrc/device.h"]
 
 
@@ -70,6 +72,24 @@ class Engine:
                                  s["workspace"], self.stream)
         if rc != 0:
             raise RuntimeError(f"pqb_quantize {fmt}/{gran}: status {rc}")
+
+    def jobs(self, items):
+        """A prebuilt pqb_job array for `items` = [(x, fmt, gran, shape, buf)]."""
+        J = self.pqb.pqb._Job
+        arr = (J * len(items))()
+        for j, (x, fmt, gran, shape, buf) in zip(arr, items):
+            j.x, j.codes, j.scales = x.data_ptr(), buf["codes"].data_ptr(), \
+                buf["scales"].data_ptr()
+            j.aux = buf["aux"].data_ptr() if buf["aux"] is not None else None
+            j.batch, j.rows, j.cols = shape
+            j.dtype = 1 if x.dtype == self.torch.bfloat16 else 0
+            j.fmt, j.gran = self.pqb.FORMATS[fmt], self.pqb.GRANS[gran]
+        return arr, len(items)
+
+    def batch(self, jobs):
+        rc = self.L.pqb_quantize_batch(jobs[0], jobs[1], self.stream)
+        if rc != 0:
+            raise RuntimeError(f"pqb_quantize_batch: status {rc}")
 
     def dequantize(self, buf, fmt, gran, shape, out):
         P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None  # noqa: E731
@@ -132,8 +152,13 @@ def bench_main(torch, eng, synth, steps, warmup, nsets):
     w_bytes = 7168 * 2048 * 2 + out_bytes(sets[0][2]["sizes"])
     a_bytes = 8192 * 7168 * 2 + out_bytes(sets[0][3]["sizes"])
     step_bytes = w_bytes + a_bytes
+    jobs = [eng.jobs([(a, "fp8_e4m3", "1x128", ashape, ab), (w, "fp8_e4m3", "128x128", wshape, wb)])
+            for w, a, wb, ab in sets]
 
     def step(i):
+        eng.batch(jobs[i % nsets])
+
+    def two_launches(i):
         w, a, wb, ab = sets[i % nsets]
         eng.quantize(a, "fp8_e4m3", "1x128", ashape, ab)
         eng.quantize(w, "fp8_e4m3", "128x128", wshape, wb)
@@ -144,9 +169,11 @@ def bench_main(torch, eng, synth, steps, warmup, nsets):
 
     for i in range(warmup):
         step(i)
+        two_launches(i)
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    # timed region 1: the whole step (both kernels), events only at the ends
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    # timed region: K steps back to back, events only at the ends.  A step is
+    # one launch, so this is also the fused kernel's average launch duration.
     wall0 = time.perf_counter()
     ev[0].record()
     for k in range(steps):
@@ -155,17 +182,15 @@ def bench_main(torch, eng, synth, steps, warmup, nsets):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_total = ev[0].elapsed_time(ev[1])
-    # timed region 2: the dominant kernel alone, back to back on the same stream
-    ev[2].record()
-    for k in range(steps):
-        act_only(k)
-    ev[3].record()
-    torch.cuda.synchronize()
-    a_avg = ev[2].elapsed_time(ev[3]) / steps
-    log(f"main: {steps} steps {ms_total:.3f} ms (wall {wall * 1e3:.3f} ms), "
-        f"act kernel avg {a_avg * 1e3:.1f} us")
+    # for comparison: the same step as two single-tensor launches, and the
+    # activation kernel alone
+    ms_two = time_loop(torch, two_launches, steps, 0)
+    a_avg = time_loop(torch, act_only, steps, 0)
+    log(f"main: {steps} fused steps {ms_total:.3f} ms (wall {wall * 1e3:.3f} ms); "
+        f"two launches {ms_two * 1e3:.1f} us/step; activation kernel {a_avg * 1e3:.1f} us")
     return {"ms_per_step": ms_total / steps, "step_bytes": step_bytes, "act_bytes": a_bytes,
-            "w_bytes": w_bytes, "act_kernel_ms_avg": a_avg, "wall_s": wall}
+            "w_bytes": w_bytes, "ms_two_launches": ms_two, "act_kernel_ms_avg": a_avg,
+            "wall_s": wall}
 
 
 # ----------------------------------------------------------------------------
@@ -247,14 +272,23 @@ def bench_extras(torch, eng, synth, reps):
             bufs.append(b)
             nb += x.numel() * 2 + out_bytes(b["sizes"])
 
+    jobs = eng.jobs([(x, "int4_asym", "grp128", shp, b) for (x, shp), b in zip(ws_, bufs)])
+
     def all_int4(i):
+        eng.batch(jobs)
+
+    def one_by_one(i):
         for (x, shp), b in zip(ws_, bufs):
             eng.quantize(x, "int4_asym", "grp128", shp, b)
 
     ms = time_loop(torch, all_int4, 3, 1)
-    out["llama8b_224w_bf16_int4_g128"] = rec(nb, ms, op="INT4 g128 asym, 224 tensors",
-                                             launches=len(bufs))
-    log(f"int4 llama: {out['llama8b_224w_bf16_int4_g128']['gbs']} GB/s")
+    out["llama8b_224w_bf16_int4_g128"] = rec(nb, ms, op="INT4 g128 asym, 224 tensors, one "
+                                             "pqb_quantize_batch call", launches=-(-224 // 24))
+    ms = time_loop(torch, one_by_one, 3, 1)
+    out["llama8b_224w_bf16_int4_g128_per_tensor"] = rec(nb, ms, op="same, one pqb_quantize "
+                                                        "call per tensor", launches=224)
+    log(f"int4 llama: {out['llama8b_224w_bf16_int4_g128']['gbs']} GB/s batched, "
+        f"{out['llama8b_224w_bf16_int4_g128_per_tensor']['gbs']} GB/s per tensor")
     return out
 
 
@@ -262,7 +296,7 @@ def bench_extras(torch, eng, synth, reps):
 # CPU baseline: the oracle on a bounded sample of the headline workload
 # ----------------------------------------------------------------------------
 
-def cpu_baseline(torch, synth, act_rows=1536, w_rows=128):
+def cpu_baseline(torch, synth, act_rows=4608, w_rows=384):
     import oracle
     a = synth.fp8_activation(device="cpu")[:act_rows].contiguous()
     w = synth.fp8_weight(device="cpu")[:w_rows].contiguous()
@@ -334,7 +368,7 @@ def main():
 
     m = bench_main(torch, eng, synth, args.steps, args.warmup, args.sets)
     value = m["step_bytes"] / (m["ms_per_step"] * 1e-3) / 1e9
-    achieved = m["act_bytes"] / (m["act_kernel_ms_avg"] * 1e-3) / 1e9
+    achieved = value   # one fused launch per step
     traffic = None
     try:
         with open(COUNTERS_FILE) as f:
@@ -352,11 +386,17 @@ def main():
                                "bf16 activations [8192x7168] 1x128 blocks",
                    "step_bytes": m["step_bytes"], "rotated_buffer_sets": args.sets,
                    "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
-        "roofline": {"bound": "hbm", "kernel": "k_fp8_1x128 (activations [8192x7168] bf16)",
+        "roofline": {"bound": "hbm", "kernel": "k_multi (fused W 128x128 + A 1x128 launch)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": m["act_bytes"],
-                     "avg_launch_ms": round(m["act_kernel_ms_avg"], 5)},
+                     "algorithmic_bytes_per_launch": m["step_bytes"],
+                     "avg_launch_ms": round(m["ms_per_step"], 5)},
+        "unfused": {"two_launch_step_ms": round(m["ms_two_launches"], 5),
+                    "two_launch_gbs": round(m["step_bytes"] / (m["ms_two_launches"] * 1e-3) / 1e9,
+                                            1),
+                    "act_kernel_k_fp8_1x128_ms": round(m["act_kernel_ms_avg"], 5),
+                    "act_kernel_gbs": round(m["act_bytes"] / (m["act_kernel_ms_avg"] * 1e-3) / 1e9,
+                                            1)},
     }
     if not args.no_extras:
         line["formats"] = bench_extras(torch, eng, synth, args.reps)

@@ -121,6 +121,30 @@ pqb_status pqb_quantize(const void* x, pqb_dtype dtype, int64_t batch, int64_t r
                         pqb_format fmt, pqb_gran gran, void* codes, void* scales, void* aux,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* One tensor of a fused batch: the arguments of one pqb_quantize call. */
+typedef struct pqb_job {
+  const void* x;    /* input [batch, rows, cols] of `dtype` */
+  void* codes;      /* outputs, laid out as for pqb_quantize */
+  void* scales;
+  void* aux;        /* INT4 zero-points; NULL for the other formats */
+  int64_t batch, rows, cols;
+  int32_t dtype;    /* pqb_dtype */
+  int32_t fmt;      /* pqb_format */
+  int32_t gran;     /* pqb_gran */
+  int32_t reserved; /* must be 0 (else PQB_ERR_ENUM) */
+} pqb_job;
+
+/* Quantize several tensors with as few launches as possible: the 128x128,
+ * 1x128, MXFP4 and INT4 jobs share fused launches of up to 24 jobs, per-row
+ * FP8 jobs get a launch each.  Each job's outputs are exactly those of
+ * pqb_quantize on the same arguments.  Only the one-pass formats qualify (FP8
+ * ROW / BLK_1x128 / BLK_128x128, MXFP4, INT4); a per-tensor FP8 or NVFP4 job
+ * returns PQB_ERR_COMBO.  Every job is validated (same rules and codes as
+ * pqb_quantize) before anything is enqueued.  Outputs of different jobs must
+ * not overlap each other or any input.  `jobs` is a host array and may be
+ * reused once the call returns. */
+pqb_status pqb_quantize_batch(const pqb_job* jobs, int64_t njobs, void* stream);
+
 /* Inverse of pqb_quantize: out[b, r, c] = decoded code times its scale(s),
  * as float32 or rounded to bf16 (round-to-nearest-even) by `out_dtype`.
  * FP8: dec(code) * s.  MXFP4: +-V * 2^(e8m0 - 127) (exact).  NVFP4:

@@ -6,7 +6,7 @@ include/pqb.h.  The binding is loaded on first use so that the input
 generators in `synth` import without the engine.
 """
 _EXPORTS = {
-    "quantize", "dequantize", "query_sizes", "kv_write_fp8", "encode_e4m3", "encode_e2m1",
+    "quantize", "quantize_batch", "dequantize", "query_sizes", "kv_write_fp8", "encode_e4m3", "encode_e2m1",
     "fp8_per_tensor", "fp8_per_row", "fp8_blockwise", "mxfp4", "nvfp4", "fp8_kv_write",
     "Quantized", "PqbError", "abi_version", "status_string", "lib", "FORMATS", "GRANS",
     "LIB_PATH",

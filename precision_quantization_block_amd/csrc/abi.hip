@@ -2,6 +2,8 @@
 // dispatch to the kernel launchers.  Nothing here allocates or synchronizes.
 #include <hip/hip_runtime.h>
 
+#include <vector>
+
 #include "../../include/pqb.h"
 #include "launch.h"
 
@@ -141,25 +143,38 @@ pqb_status pqb_query_sizes(pqb_format fmt, pqb_gran gran, int64_t batch, int64_t
   return PQB_OK;
 }
 
-pqb_status pqb_quantize(const void* x, pqb_dtype dtype, int64_t batch, int64_t rows, int64_t cols,
-                        pqb_format fmt, pqb_gran gran, void* codes, void* scales, void* aux,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+// Validation shared by pqb_quantize and pqb_quantize_batch; fills `need`.
+static pqb_status check_quantize(const void* x, int dtype, int64_t batch, int64_t rows,
+                                 int64_t cols, int fmt, int gran, const void* codes,
+                                 const void* scales, const void* aux, const void* workspace,
+                                 size_t workspace_bytes, pqb_sizes* need) {
   if (!valid_dtype(dtype) || !known_format(fmt) || !known_gran(gran)) return PQB_ERR_ENUM;
   if (!valid_pair(fmt, gran)) return PQB_ERR_COMBO;
   pqb_status st = check_shape(fmt, gran, batch, rows, cols);
   if (st != PQB_OK) return st;
-  const int64_t n = batch * rows * cols;
-  if (n == 0) return PQB_OK;
-  const pqb_sizes need = sizes_of(fmt, gran, batch, rows, cols);
+  *need = sizes_of(fmt, gran, batch, rows, cols);
+  if (batch * rows * cols == 0) return PQB_OK;
   if (!x || !codes || !scales) return PQB_ERR_NULL;
-  if (need.aux && !aux) return PQB_ERR_NULL;
-  if (need.workspace && !workspace) return PQB_ERR_NULL;
-  if (workspace_bytes < need.workspace) return PQB_ERR_WORKSPACE;
-  if (!aligned(x, 16) || !aligned(codes, 16) || (need.workspace && !aligned(workspace, 16)))
+  if (need->aux && !aux) return PQB_ERR_NULL;
+  if (need->workspace && !workspace) return PQB_ERR_NULL;
+  if (workspace_bytes < need->workspace) return PQB_ERR_WORKSPACE;
+  if (!aligned(x, 16) || !aligned(codes, 16) || (need->workspace && !aligned(workspace, 16)))
     return PQB_ERR_ALIGN;
   if (fmt == PQB_FP8_E4M3 && !aligned(scales, 4)) return PQB_ERR_ALIGN;
   if (fmt == PQB_INT4_ASYM && !aligned(scales, 2)) return PQB_ERR_ALIGN;
   if (fmt == PQB_NVFP4 && !aligned(aux, 4)) return PQB_ERR_ALIGN;
+  return PQB_OK;
+}
+
+pqb_status pqb_quantize(const void* x, pqb_dtype dtype, int64_t batch, int64_t rows, int64_t cols,
+                        pqb_format fmt, pqb_gran gran, void* codes, void* scales, void* aux,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  pqb_sizes need;
+  const pqb_status st = check_quantize(x, dtype, batch, rows, cols, fmt, gran, codes, scales, aux,
+                                       workspace, workspace_bytes, &need);
+  if (st != PQB_OK) return st;
+  const int64_t n = batch * rows * cols;
+  if (n == 0) return PQB_OK;
   const bool bf16 = dtype == PQB_BF16;
   hipStream_t s = (hipStream_t)stream;
   uint8_t* c8 = (uint8_t*)codes;
@@ -192,6 +207,51 @@ pqb_status pqb_quantize(const void* x, pqb_dtype dtype, int64_t batch, int64_t r
           launch_int4(x, bf16, n, c8, (uint16_t*)scales, (uint8_t*)aux, s));
   }
   return PQB_ERR_ENUM;
+}
+
+pqb_status pqb_quantize_batch(const pqb_job* jobs, int64_t njobs, void* stream) {
+  if (njobs < 0) return PQB_ERR_SHAPE;
+  if (njobs == 0) return PQB_OK;
+  if (!jobs) return PQB_ERR_NULL;
+  for (int64_t i = 0; i < njobs; ++i) {
+    const pqb_job& j = jobs[i];
+    if (j.reserved != 0) return PQB_ERR_ENUM;
+    pqb_sizes need;
+    const pqb_status st = check_quantize(j.x, j.dtype, j.batch, j.rows, j.cols, j.fmt, j.gran,
+                                         j.codes, j.scales, j.aux, nullptr, 0, &need);
+    if (st == PQB_ERR_NULL && need.workspace) return PQB_ERR_COMBO;  // two-pass format
+    if (st != PQB_OK) return st;
+    if (need.workspace) return PQB_ERR_COMBO;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  std::vector<MultiJob> fused;
+  fused.reserve((size_t)njobs);
+  for (int64_t i = 0; i < njobs; ++i) {
+    const pqb_job& j = jobs[i];
+    if (j.batch * j.rows * j.cols == 0) continue;
+    MultiJob m{j.x, (uint8_t*)j.codes, j.scales, (uint8_t*)j.aux, j.batch, j.rows, j.cols, 0,
+               j.dtype == PQB_BF16};
+    if (j.fmt == PQB_FP8_E4M3 && j.gran == PQB_ROW) continue;  // launched below
+    if (j.fmt == PQB_FP8_E4M3)
+      m.kind = j.gran == PQB_BLK_1x128 ? kMultiFp8Blk : kMultiFp8Tile;
+    else if (j.fmt == PQB_MXFP4)
+      m.kind = kMultiMx;
+    else
+      m.kind = kMultiInt4;
+    fused.push_back(m);
+  }
+  if (!fused.empty()) {
+    const hipError_t e = launch_multi(fused.data(), (int)fused.size(), s);
+    if (e != hipSuccess) return PQB_ERR_HIP;
+  }
+  for (int64_t i = 0; i < njobs; ++i) {
+    const pqb_job& j = jobs[i];
+    if (j.fmt != PQB_FP8_E4M3 || j.gran != PQB_ROW || j.batch * j.rows * j.cols == 0) continue;
+    const hipError_t e = launch_fp8_row(j.x, j.dtype == PQB_BF16, j.batch * j.rows, j.cols,
+                                        (uint8_t*)j.codes, (float*)j.scales, s);
+    if (e != hipSuccess) return PQB_ERR_HIP;
+  }
+  return PQB_OK;
 }
 
 pqb_status pqb_dequantize(const void* codes, const void* scales, const void* aux, pqb_format fmt,

@@ -189,14 +189,34 @@ constexpr int kE2M1LutSize = 2048;
 __device__ __forceinline__ uint32_t e2m1_key(float y) { return (as_u(y) + 0x1FFFFFu) >> 21; }
 
 // Fill the table (call with all threads of the block, then __syncthreads()).
-__device__ __forceinline__ void e2m1_lut_fill(uint8_t* lut, int neg_zero_nibble) {
+// Keys below 501 have magnitude 0 and keys above 517 magnitude 7, so most
+// 4-key dwords are constants; only the few around the decision points are
+// computed key by key.
+__device__ __forceinline__ uint32_t e2m1_entry(int k, int neg_zero_nibble) {
   constexpr int kT[7] = {500, 506, 509, 511, 513, 515, 517};  // bits(t) >> 21
-  for (int k = threadIdx.x; k < kE2M1LutSize; k += blockDim.x) {
-    int mag = k & 1023, neg = k >> 10;
-    int m = 0;
+  const int mag = k & 1023, neg = k >> 10;
+  int m = 0;
 #pragma unroll
-    for (int j = 0; j < 7; ++j) m += mag > kT[j];
-    lut[k] = (uint8_t)(neg ? (mag > 0 ? 8 | m : neg_zero_nibble) : m);
+  for (int j = 0; j < 7; ++j) m += mag > kT[j];
+  return (uint32_t)(neg ? (mag > 0 ? 8 | m : neg_zero_nibble) : m);
+}
+
+__device__ __forceinline__ void e2m1_lut_fill(uint8_t* lut, int neg_zero_nibble) {
+  uint32_t* w = reinterpret_cast<uint32_t*>(lut);
+  for (int d = threadIdx.x; d < kE2M1LutSize / 4; d += blockDim.x) {
+    const int k0 = 4 * d, mag0 = k0 & 1023;
+    const uint32_t sign = (k0 >> 10) ? 0x08080808u : 0u;
+    uint32_t word;
+    if (mag0 >= 4 && mag0 + 3 <= 500) {
+      word = sign;                 // magnitude 0
+    } else if (mag0 >= 518) {
+      word = sign | 0x07070707u;   // magnitude 7 (saturated at 6)
+    } else {
+      word = e2m1_entry(k0, neg_zero_nibble) | (e2m1_entry(k0 + 1, neg_zero_nibble) << 8) |
+             (e2m1_entry(k0 + 2, neg_zero_nibble) << 16) |
+             (e2m1_entry(k0 + 3, neg_zero_nibble) << 24);
+    }
+    w[d] = word;
   }
 }
 

@@ -6,53 +6,17 @@
 // NVFP4 (same section): gs = max(amax_tensor, 1e-12) / (448*6); each 16-element
 // block stores bs = E4M3(RN(RN(amax_block / 6) / gs)); elements are rounded
 // against s = RN(max(dec(bs), 1e-12) * gs).
-#include "device.h"
 #include "launch.h"
+#include "quant.h"
 
 namespace pqb {
 namespace {
-
-constexpr float kInv6 = 1.0f / 6.0f;
-
-// ---------------------------------------------------------------------------
-// MXFP4: 4 lanes x 8 elements per block.  y = x * 2^-X is exactly RN(x / 2^X)
-// (a product with a power of two), so the E2M1 table sees the page's quotient,
-// signed zeros included (a -0.0 quotient maps to nibble 0).
-// ---------------------------------------------------------------------------
-template <typename T, int kUnr, bool kGuard>
-__device__ __forceinline__ void mx_chunk(const T* __restrict__ x, int64_t u0, int64_t nunits,
-                                         uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                         const uint8_t* lut) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const T* xb = x + u0 * 8;
-  Raw8 raw[kUnr];
-#pragma unroll
-  for (int k = 0; k < kUnr; ++k)
-    raw[k] = (!kGuard || u0 + k * kWave + lane < nunits) ? load_raw8(xb + (k * kWave + lane) * 8)
-                                                           : Raw8{};
-#pragma unroll
-  for (int k = 0; k < kUnr; ++k) {
-    float v[8];
-    widen8(raw[k], x, v);
-    const uint32_t a = max(group_umax<4>(as_u(absmax8(v))), kAmaxFloorBits);
-    const uint32_t ef = a >> 23;                // biased exponent of a normal a
-    const float mul = as_f((256u - ef) << 23);  // 2^-X with X = ef - 129
-    uint32_t w = lut[e2m1_key(v[0] * mul)];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) w |= (uint32_t)lut[e2m1_key(v[i] * mul)] << (4 * i);
-    const int64_t u = u0 + k * kWave + lane;
-    if (!kGuard || u < nunits) {
-      st_nt4(codes + u * 4, w);
-      if ((lane & 3) == 0) scales[u >> 2] = (uint8_t)(ef - 2u);
-    }
-  }
-}
 
 template <typename T, int kUnr>
 __global__ __launch_bounds__(kBlockThreads) void k_mxfp4(const T* __restrict__ x, int64_t nunits,
                                                           uint8_t* __restrict__ codes,
                                                           uint8_t* __restrict__ scales) {
-  __shared__ uint8_t lut[kE2M1LutSize];
+  __shared__ __align__(16) uint8_t lut[kE2M1LutSize];
   e2m1_lut_fill(lut, 0);
   __syncthreads();
   const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
@@ -94,7 +58,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_mxfp4_dequant(const uint8_t* 
 // elements per block.  Each workgroup rebuilds gs, the E2M1 table and, for all
 // 127 finite block-scale codes, the element scale s and RN(1/s) in LDS.
 // ---------------------------------------------------------------------------
-struct NvTables {
+struct __align__(16) NvTables {
   uint8_t lut[kE2M1LutSize];
   float se[128], ye[128];
   uint32_t red[kBlockThreads / kWave];
@@ -206,7 +170,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_nvfp4_dequant(const uint8_t* 
 __global__ __launch_bounds__(kBlockThreads) void k_encode_e2m1(const float* __restrict__ y,
                                                                int64_t n,
                                                                uint8_t* __restrict__ out) {
-  __shared__ uint8_t lut[kE2M1LutSize];
+  __shared__ __align__(16) uint8_t lut[kE2M1LutSize];
   e2m1_lut_fill(lut, 0);
   __syncthreads();
   for (int64_t i = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x; i < n;

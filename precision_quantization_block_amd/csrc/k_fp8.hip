@@ -1,79 +1,15 @@
 // FP8 E4M3 quantize / dequantize kernels: 1x128 blocks, 128x128 tiles, rows,
-// per tensor.
+// per tensor (the per-chunk bodies are in quant.h).
 //
 // Scale of a scope: s = RN(max(amax, 1e-12) / 448); codes are E4M3(RN(x / s))
 // (page "量化部署实战", section 伪量化实现).  The clamp to +-448 that the page
 // applies before the cast never binds here: |x| <= amax gives |x/s| <= 448 up to
 // one rounding, which still rounds to 448.
-#include "device.h"
 #include "launch.h"
+#include "quant.h"
 
 namespace pqb {
 namespace {
-
-constexpr float kInv448 = 1.0f / 448.0f;  // RN(1/448), folded at compile time
-
-// s from the bit pattern of a scope's amax (a non-negative float).
-__device__ __forceinline__ float fp8_scale_bits(uint32_t amax_bits) {
-  return div_const(as_f(max(amax_bits, kAmaxFloorBits)), 448.0f, kInv448);
-}
-
-// Eight values -> eight E4M3 codes (two dwords) with scale s and y = RN(1/s).
-__device__ __forceinline__ uint2 fp8_pack8(const float v[8], float s, float y) {
-  const uint32_t w0 = e4m3_bytes4(div_rn(v[0], s, y), div_rn(v[1], s, y), div_rn(v[2], s, y),
-                                  div_rn(v[3], s, y));
-  const uint32_t w1 = e4m3_bytes4(div_rn(v[4], s, y), div_rn(v[5], s, y), div_rn(v[6], s, y),
-                                  div_rn(v[7], s, y));
-  return make_uint2(w0, w1);
-}
-
-__device__ __forceinline__ void store_codes8(uint8_t* p, uint2 w) { st_nt8(p, w.x, w.y); }
-
-template <typename T>
-__device__ __forceinline__ float ld1(const T* p);
-template <>
-__device__ __forceinline__ float ld1<uint16_t>(const uint16_t* p) {
-  return as_f((uint32_t)*p << 16);
-}
-template <>
-__device__ __forceinline__ float ld1<float>(const float* p) {
-  return *p;
-}
-
-__device__ __forceinline__ uint8_t e4m3_byte(float q) {
-  return (uint8_t)(cvt_e4m3x2<false>(q, 0.0f, 0u) & 0xFFu);
-}
-
-// ---------------------------------------------------------------------------
-// 1x128: a 128-element block is 16 lanes x 8 elements, one DPP row.  Each wave
-// streams kUnr consecutive tiles of 64 units (8 elements each) per iteration;
-// only the last, partial chunk of the tensor checks bounds.
-// ---------------------------------------------------------------------------
-template <typename T, int kUnr, bool kGuard>
-__device__ __forceinline__ void fp8_1x128_chunk(const T* __restrict__ x, int64_t u0, int64_t nunits,
-                                                uint8_t* __restrict__ codes,
-                                                float* __restrict__ scales) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const T* xb = x + u0 * 8;
-  Raw8 raw[kUnr];
-#pragma unroll
-  for (int k = 0; k < kUnr; ++k)
-    raw[k] = (!kGuard || u0 + k * kWave + lane < nunits) ? load_raw8(xb + (k * kWave + lane) * 8)
-                                                           : Raw8{};
-#pragma unroll
-  for (int k = 0; k < kUnr; ++k) {
-    float v[8];
-    widen8(raw[k], x, v);
-    const float s = fp8_scale_bits(group_umax<16>(as_u(absmax8(v))));
-    const float y = recip_rn(s);
-    const uint2 w = fp8_pack8(v, s, y);
-    const int64_t u = u0 + k * kWave + lane;
-    if (!kGuard || u < nunits) {
-      store_codes8(codes + u * 8, w);
-      if ((lane & 15) == 0) scales[u >> 4] = s;
-    }
-  }
-}
 
 template <typename T, int kUnr>
 __global__ __launch_bounds__(kBlockThreads) void k_fp8_1x128(const T* __restrict__ x,
@@ -90,110 +26,34 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_1x128(const T* __restrict
   }
 }
 
-// ---------------------------------------------------------------------------
-// 128x128 (br x 128 with br = min(128, rows)): one workgroup per tile.  Lane l
-// of wave w covers unit (l % 16) of tile rows w*4 + l/16 + 16k, k < 8; the
-// tile's amax is reduced through DPP, a cross-row shuffle and LDS.
-// ---------------------------------------------------------------------------
+constexpr int kTileWaves = 8;  // 512 threads per 128x128 tile: 4 rows of it per lane
+
 template <typename T>
-__global__ __launch_bounds__(kBlockThreads) void k_fp8_128x128(const T* __restrict__ x,
-                                                                int64_t rows, int64_t cols,
-                                                                int br,
-                                                                uint8_t* __restrict__ codes,
-                                                                float* __restrict__ scales) {
-  __shared__ uint32_t red[kBlockThreads / kWave];
-  const int64_t tiles_c = cols / 128;
-  const int64_t t = blockIdx.x;
-  const int64_t tc = t % tiles_c, trb = t / tiles_c;  // trb = b * (rows / br) + tile row
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int r0 = wave * 4 + (lane >> 4);
-  // rows of consecutive batch slices are contiguous, so tile row trb starts at row trb*br
-  const int64_t base = trb * br * cols + tc * 128 + (lane & 15) * 8;
-  Raw8 raw[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int r = r0 + 16 * k;
-    raw[k] = r < br ? load_raw8(x + base + (int64_t)r * cols) : Raw8{};
-  }
-  float v[8][8];
-  uint32_t m = 0;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    widen8(raw[k], x, v[k]);
-    m = max(m, as_u(absmax8(v[k])));
-  }
-  m = wave_umax(m);
-  if (lane == 0) red[wave] = m;
-  __syncthreads();
-  m = max(max(red[0], red[1]), max(red[2], red[3]));
-  const float s = fp8_scale_bits(m);
-  const float y = recip_rn(s);
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int r = r0 + 16 * k;
-    const uint2 w = fp8_pack8(v[k], s, y);
-    if (r < br) store_codes8(codes + base + (int64_t)r * cols, w);
-  }
-  if (threadIdx.x == 0) scales[t] = s;
+__global__ __launch_bounds__(kTileWaves * kWave) void k_fp8_128x128(const T* __restrict__ x,
+                                                                     int64_t rows, int64_t cols,
+                                                                     int br,
+                                                                     uint8_t* __restrict__ codes,
+                                                                     float* __restrict__ scales) {
+  __shared__ uint32_t red[kTileWaves];
+  fp8_tile_128x128<T, kTileWaves>(x, rows, cols, br, blockIdx.x, codes, scales, red);
 }
 
-// ---------------------------------------------------------------------------
-// Per row, vector path (cols % 8 == 0, cols <= 512 * kMaxU): one wave per row,
-// the row stays in registers between the reduction and the quantization.
-// ---------------------------------------------------------------------------
 template <typename T, int kMaxU>
 __global__ __launch_bounds__(kBlockThreads) void k_fp8_row_vec(const T* __restrict__ x,
                                                                 int64_t nrows, int64_t cols,
                                                                 uint8_t* __restrict__ codes,
                                                                 float* __restrict__ scales) {
-  const int lane = threadIdx.x & (kWave - 1);
   const int64_t row = wave_index();
-  if (row >= nrows) return;  // the whole wave leaves together
-  const int64_t upr = cols / 8;
-  const T* xr = x + row * cols;
-  Raw8 raw[kMaxU];
-#pragma unroll
-  for (int k = 0; k < kMaxU; ++k) {
-    const int64_t u = (int64_t)k * kWave + lane;
-    raw[k] = u < upr ? load_raw8(xr + u * 8) : Raw8{};
-  }
-  uint32_t m = 0;
-#pragma unroll
-  for (int k = 0; k < kMaxU; ++k) {
-    float v[8];
-    widen8(raw[k], x, v);
-    m = max(m, as_u(absmax8(v)));
-  }
-  const float s = fp8_scale_bits(wave_umax(m));
-  const float y = recip_rn(s);
-#pragma unroll
-  for (int k = 0; k < kMaxU; ++k) {
-    const int64_t u = (int64_t)k * kWave + lane;
-    float v[8];
-    widen8(raw[k], x, v);
-    const uint2 w = fp8_pack8(v, s, y);
-    if (u < upr) store_codes8(codes + row * cols + u * 8, w);
-  }
-  if (lane == 0) scales[row] = s;
+  if (row < nrows) fp8_row_vec<T, kMaxU>(x, row, cols, codes, scales);  // whole waves
 }
 
-// Per row, any width: one wave per row, element-wise, reading the row twice
-// (the second read is served by the caches).
 template <typename T>
 __global__ __launch_bounds__(kBlockThreads) void k_fp8_row_any(const T* __restrict__ x,
                                                                 int64_t nrows, int64_t cols,
                                                                 uint8_t* __restrict__ codes,
                                                                 float* __restrict__ scales) {
-  const int lane = threadIdx.x & (kWave - 1);
   const int64_t row = wave_index();
-  if (row >= nrows) return;
-  const T* xr = x + row * cols;
-  uint32_t m = 0;
-  for (int64_t c = lane; c < cols; c += kWave) m = max(m, as_u(fabsf(ld1(xr + c))));
-  const float s = fp8_scale_bits(wave_umax(m));
-  const float y = recip_rn(s);
-  for (int64_t c = lane; c < cols; c += kWave) codes[row * cols + c] = e4m3_byte(div_rn(ld1(xr + c), s, y));
-  if (lane == 0) scales[row] = s;
+  if (row < nrows) fp8_row_any<T>(x, row, cols, codes, scales);
 }
 
 // ---------------------------------------------------------------------------
@@ -411,11 +271,11 @@ hipError_t launch_fp8_128x128(const void* x, bool bf16, int64_t batch, int64_t r
   const int br = (int)(rows < 128 ? rows : 128);
   const int64_t tiles = batch * (rows / br) * (cols / 128);
   if (bf16)
-    hipLaunchKernelGGL(k_fp8_128x128<uint16_t>, dim3((unsigned)tiles), dim3(kBlockThreads), 0, st,
-                       (const uint16_t*)x, rows, cols, br, codes, scales);
+    hipLaunchKernelGGL(k_fp8_128x128<uint16_t>, dim3((unsigned)tiles), dim3(kTileWaves * kWave),
+                       0, st, (const uint16_t*)x, rows, cols, br, codes, scales);
   else
-    hipLaunchKernelGGL(k_fp8_128x128<float>, dim3((unsigned)tiles), dim3(kBlockThreads), 0, st,
-                       (const float*)x, rows, cols, br, codes, scales);
+    hipLaunchKernelGGL(k_fp8_128x128<float>, dim3((unsigned)tiles), dim3(kTileWaves * kWave), 0,
+                       st, (const float*)x, rows, cols, br, codes, scales);
   return hipGetLastError();
 }
 

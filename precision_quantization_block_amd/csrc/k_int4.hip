@@ -6,68 +6,11 @@
 // 更少的字节", 量化在做什么).  The group range [lo, hi] is widened to hold 0, its
 // 15 steps give s = bf16(max(hi - lo, 1e-12) / 15) (the rounded s is the one
 // used), and z = -8 - rint(lo / s) puts lo on -8.
-#include "device.h"
 #include "launch.h"
+#include "quant.h"
 
 namespace pqb {
 namespace {
-
-constexpr float kInv15 = 1.0f / 15.0f;
-constexpr float kRound = 12582912.0f;  // 1.5 * 2^23: adding it rounds |q| < 2^22 to an
-                                       // integer, ties to even (the constant is even)
-
-// A group of 128 is 16 lanes x 8 elements (one DPP row).  Zero-points are two
-// per byte over the flat group index; group 2j (lanes 0-15 of a 32-lane half)
-// and group 2j+1 (lanes 16-31) share byte j.
-template <typename T, int kUnr, bool kGuard>
-__device__ __forceinline__ void int4_chunk(const T* __restrict__ x, int64_t u0, int64_t nunits,
-                                           uint8_t* __restrict__ codes,
-                                           uint16_t* __restrict__ scales,
-                                           uint8_t* __restrict__ zeros) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const T* xb = x + u0 * 8;
-  Raw8 raw[kUnr];
-#pragma unroll
-  for (int k = 0; k < kUnr; ++k)
-    raw[k] = (!kGuard || u0 + k * kWave + lane < nunits) ? load_raw8(xb + (k * kWave + lane) * 8)
-                                                           : Raw8{};
-#pragma unroll
-  for (int k = 0; k < kUnr; ++k) {
-    float v[8];
-    widen8(raw[k], x, v);
-    // hi = max(0, max x) >= 0 and -lo = -min(0, min x) >= 0, reduced as bit
-    // patterns.  A lane whose values are all on one side yields a zero that may
-    // be -0.0; taking |.| first keeps its pattern 0 so it cannot win the max.
-    const float h = max3f(max3f(v[0], v[1], v[2]), max3f(v[3], v[4], v[5]), max3f(v[6], v[7], 0.0f));
-    const float l = min3f(min3f(v[0], v[1], v[2]), min3f(v[3], v[4], v[5]), min3f(v[6], v[7], 0.0f));
-    const float hi = as_f(group_umax<16>(as_u(fabsf(h))));
-    const float lo = -as_f(group_umax<16>(as_u(fabsf(l))));
-    const float t = div_const(as_f(max(as_u(hi - lo), kAmaxFloorBits)), 15.0f, kInv15);
-    const uint32_t sb = bf16_rne_bits(t);
-    const float s = as_f(sb << 16);
-    const float y = recip_rn(s);
-    // div_rn commutes with negation, so it also gives RN(lo / s) for lo <= 0
-    const float z = fminf(fmaxf(-8.0f - rintf(div_rn(lo, s, y)), -8.0f), 7.0f);
-    // q + 8 = rint(x / s) + z + 8, clamped to [0, 15]: the integer sits in the low
-    // bits of x/s + 1.5 * 2^23
-    const int zofs = (int)z + 8 - (int)0x4B400000;
-    uint32_t w = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int q = (int)as_u(div_rn(v[i], s, y) + kRound) + zofs;
-      w |= (uint32_t)min(max(q, 0), 15) << (4 * i);
-    }
-    w ^= 0x88888888u;  // offset binary -> two's-complement nibbles
-    const int zn = ((int)z) & 15;
-    const int zn_odd = __shfl_down(zn, 16);
-    const int64_t u = u0 + k * kWave + lane;
-    if (!kGuard || u < nunits) {
-      st_nt4(reinterpret_cast<uint32_t*>(codes) + u, w);
-      if ((lane & 15) == 0) scales[u >> 4] = (uint16_t)sb;
-      if ((lane & 31) == 0) zeros[u >> 5] = (uint8_t)(zn | ((u + 16 < nunits ? zn_odd : 0) << 4));
-    }
-  }
-}
 
 template <typename T, int kUnr>
 __global__ __launch_bounds__(kBlockThreads) void k_int4(const T* __restrict__ x, int64_t nunits,

@@ -50,6 +50,21 @@ hipError_t launch_int4(const void* x, bool bf16, int64_t n, uint8_t* codes, uint
 hipError_t launch_int4_dequant(const uint8_t* codes, const uint16_t* scales, const uint8_t* zeros,
                                int64_t n, bool out_bf16, void* out, hipStream_t st);
 
+// ---- fused multi-tensor launch ----------------------------------------------
+// Jobs of the one-pass formats, fused into launches of up to kMaxBatchJobs.
+constexpr int kMaxBatchJobs = 24;
+enum MultiKind { kMultiFp8Blk = 0, kMultiFp8Tile = 1, kMultiMx = 2, kMultiInt4 = 3 };
+struct MultiJob {
+  const void* x;
+  uint8_t* codes;
+  void* scales;
+  uint8_t* aux;
+  int64_t batch, rows, cols;
+  int kind;
+  bool bf16;
+};
+hipError_t launch_multi(const MultiJob* jobs, int njobs, hipStream_t st);
+
 // ---- element codecs ---------------------------------------------------------
 hipError_t launch_encode_e4m3(const float* y, int64_t n, uint8_t* out, hipStream_t st);
 hipError_t launch_encode_e2m1(const float* y, int64_t n, uint8_t* out, hipStream_t st);

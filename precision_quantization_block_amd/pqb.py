@@ -36,6 +36,13 @@ class PqbError(RuntimeError):
         self.status = status
 
 
+class _Job(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("aux", ctypes.c_void_p), ("batch", ctypes.c_int64), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64), ("dtype", ctypes.c_int32), ("fmt", ctypes.c_int32),
+                ("gran", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
 class _Sizes(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_size_t), ("scales", ctypes.c_size_t),
                 ("aux", ctypes.c_size_t), ("workspace", ctypes.c_size_t)]
@@ -54,11 +61,13 @@ def lib():
         L.pqb_query_sizes.argtypes = [I, I, I64, I64, I64, ctypes.POINTER(_Sizes)]
         L.pqb_quantize.argtypes = [P, I, I64, I64, I64, I, I, P, P, P, P, SZ, P]
         L.pqb_dequantize.argtypes = [P, P, P, I, I, I64, I64, I64, I, P, P]
+        L.pqb_quantize_batch.argtypes = [ctypes.POINTER(_Job), I64, P]
         L.pqb_kv_workspace_bytes.argtypes, L.pqb_kv_workspace_bytes.restype = [I64, I64], SZ
         L.pqb_kv_write_fp8.argtypes = [P, P, I, I64, I64, P, P, P, P, P, SZ, P]
         L.pqb_encode_e4m3.argtypes = [P, I64, P, P]
         L.pqb_encode_e2m1.argtypes = [P, I64, P, P]
-        for f in ("pqb_query_sizes", "pqb_quantize", "pqb_dequantize", "pqb_kv_write_fp8",
+        for f in ("pqb_query_sizes", "pqb_quantize", "pqb_quantize_batch", "pqb_dequantize",
+                  "pqb_kv_write_fp8",
                   "pqb_encode_e4m3", "pqb_encode_e2m1"):
             getattr(L, f).restype = I
         _lib = L
@@ -139,14 +148,8 @@ def quantize(x: torch.Tensor, fmt: str, gran: str | None = None, *, shape=None,
     b, r, c = shape if shape is not None else _bcr(x.shape)
     if b * r * c != x.numel():
         raise ValueError("shape does not match the tensor")
-    sz = query_sizes(fmt, gran, b, r, c)
     dev = x.device
-    codes = torch.empty((sz["codes"],), dtype=torch.uint8, device=dev)
-    scales = _bytes(sz["scales"], _scale_dtype(fmt), dev)
-    aux = None
-    if sz["aux"]:
-        aux = (torch.empty((b,), dtype=torch.float32, device=dev) if fmt == "nvfp4"
-               else torch.empty((sz["aux"],), dtype=torch.uint8, device=dev))
+    sz, codes, scales, aux = _alloc_outputs(fmt, gran, b, r, c, dev)
     if sz["workspace"] and (workspace is None or workspace.numel() * workspace.element_size()
                             < sz["workspace"]):
         workspace = torch.empty((sz["workspace"] // 4,), dtype=torch.float32, device=dev)
@@ -155,6 +158,42 @@ def quantize(x: torch.Tensor, fmt: str, gran: str | None = None, *, shape=None,
                               _fmt(fmt), _gran(gran), _ptr(codes), _ptr(scales), _ptr(aux),
                               _ptr(workspace), ws_bytes, _stream(dev)), "quantize")
     return Quantized(codes, scales, aux, fmt, gran, (b, r, c))
+
+
+def _alloc_outputs(fmt, gran, b, r, c, dev):
+    sz = query_sizes(fmt, gran, b, r, c)
+    codes = torch.empty((sz["codes"],), dtype=torch.uint8, device=dev)
+    scales = _bytes(sz["scales"], _scale_dtype(fmt), dev)
+    aux = None
+    if sz["aux"]:
+        aux = (torch.empty((b,), dtype=torch.float32, device=dev) if fmt == "nvfp4"
+               else torch.empty((sz["aux"],), dtype=torch.uint8, device=dev))
+    return sz, codes, scales, aux
+
+
+def quantize_batch(items) -> list:
+    """Quantize several tensors with fused launches (one-pass formats only).
+    `items`: sequence of (x, fmt, gran) or (x, fmt, gran, shape) tuples.
+    Returns one Quantized per item, identical to quantize() on each."""
+    outs, jobs = [], []
+    dev = None
+    for it in items:
+        x, fmt, gran = it[0], it[1], it[2] or DEFAULT_GRAN[it[1]]
+        x = _dev_tensor(x, "x")
+        dev = x.device if dev is None else dev
+        b, r, c = it[3] if len(it) > 3 and it[3] is not None else _bcr(x.shape)
+        if b * r * c != x.numel():
+            raise ValueError("shape does not match the tensor")
+        _, codes, scales, aux = _alloc_outputs(fmt, gran, b, r, c, x.device)
+        outs.append((x, Quantized(codes, scales, aux, fmt, gran, (b, r, c))))
+        jobs.append(_Job(x.data_ptr(), codes.data_ptr(), scales.data_ptr(),
+                         aux.data_ptr() if aux is not None else None, b, r, c,
+                         BF16 if x.dtype == torch.bfloat16 else F32, _fmt(fmt), _gran(gran), 0))
+    if not jobs:
+        return []
+    arr = (_Job * len(jobs))(*jobs)
+    _check(lib().pqb_quantize_batch(arr, len(jobs), _stream(dev)), "quantize_batch")
+    return [q for _, q in outs]
 
 
 def dequantize(q: Quantized, out_dtype=torch.float32) -> torch.Tensor:

@@ -146,3 +146,34 @@ def test_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(ValueError):
         pqb.quantize(torch.zeros(4, 128), "fp8_e4m3", "1x128")
+
+
+def test_quantize_batch_errors_before_launch(L):
+    J = pqb.pqb._Job
+    fake = 0x10000
+
+    def job(**kw):
+        d = dict(x=fake, codes=fake, scales=fake, aux=None, batch=1, rows=128, cols=256,
+                 dtype=1, fmt=0, gran=2, reserved=0)
+        d.update(kw)
+        return J(**d)
+
+    def run(*jobs):
+        return L.pqb_quantize_batch((J * len(jobs))(*jobs), len(jobs), None)
+
+    # a bad job anywhere fails the whole call before anything is enqueued
+    assert run(job(), job(gran=0)) == -3                 # per-tensor FP8 needs two passes
+    assert run(job(fmt=2, gran=5), job()) == -3          # so does NVFP4
+    assert run(job(), job(reserved=1)) == -2
+    assert run(job(), job(fmt=7)) == -2
+    assert run(job(), job(dtype=3)) == -2
+    assert run(job(), job(x=None)) == -1
+    assert run(job(fmt=3, gran=6)) == -1                 # INT4 needs its zero-point buffer
+    assert run(job(), job(cols=100)) == -4
+    assert run(job(), job(rows=-1)) == -4
+    assert run(job(), job(codes=fake + 2)) == -5
+    assert L.pqb_quantize_batch(None, -1, None) == -4
+    assert L.pqb_quantize_batch(None, 1, None) == -1
+    assert L.pqb_quantize_batch(None, 0, None) == 0
+    # empty jobs are accepted and launch nothing (no device is touched)
+    assert run(job(rows=0), job(batch=0, fmt=3, gran=6, aux=fake)) == 0
