@@ -14,7 +14,7 @@ all 224 Llama-3.1-8B-shaped decoder weights, the FP8 KV write of
 [28 x 32768 x 8 x 128] K and V, and every format on a 1 GiB bf16 tensor.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras]
-       [--no-cpu] [--copy-probe]
+       [--no-cpu] [--copy-probe] [--reps R] [--only NAME]
 """
 import argparse
 import ctypes
@@ -128,10 +128,41 @@ def time_loop(torch, fn, reps, warmup):
     return a.elapsed_time(b) / reps
 
 
-def rec(bytes_moved, ms, **kw):
-    gbs = bytes_moved / (ms * 1e-3) / 1e9
-    d = {"bytes": int(bytes_moved), "ms": round(ms, 5), "gbs": round(gbs, 1),
+def time_reps(torch, fn, reps, warmup):
+    """(loop mean, median, min) in ms.  The mean comes from `reps` back-to-back
+    calls bracketed by two events; median and min from a second run of `reps`
+    calls with an event between consecutive calls (each such event adds a small
+    gap, so per-repeat times run slightly above the back-to-back mean)."""
+    mean = time_loop(torch, fn, reps, warmup)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
+        fn(i)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    t = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))
+    mid = reps // 2
+    med = t[mid] if reps % 2 else 0.5 * (t[mid - 1] + t[mid])
+    return mean, med, t[0]
+
+
+def rec(bytes_moved, times, two_pass_read=0, **kw):
+    """One result record; `times` = (mean, median, min) in ms.  GB/s (Form 1)
+    counts the input once plus every output; for two-pass formats
+    `two_pass_read` is the second input read, added in the *_incl_pass1
+    figures."""
+    mean, med, mn = times
+    gbs = bytes_moved / (mean * 1e-3) / 1e9
+    d = {"bytes": int(bytes_moved), "ms": round(mean, 5), "ms_median": round(med, 5),
+         "ms_min": round(mn, 5), "gbs": round(gbs, 1),
+         "gbs_median": round(bytes_moved / (med * 1e-3) / 1e9, 1),
+         "gbs_at_min": round(bytes_moved / (mn * 1e-3) / 1e9, 1),
          "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    if two_pass_read:
+        tb = bytes_moved + two_pass_read
+        d["bytes_incl_pass1"] = int(tb)
+        d["gbs_incl_pass1"] = round(tb / (mean * 1e-3) / 1e9, 1)
+        d["frac_hbm_peak_incl_pass1"] = round(tb / (mean * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
     d.update(kw)
     return d
 
@@ -197,53 +228,78 @@ def bench_main(torch, eng, synth, steps, warmup, nsets):
 # other workloads
 # ----------------------------------------------------------------------------
 
-def bench_extras(torch, eng, synth, reps):
+def bench_extras(torch, eng, synth, reps, only=None):
+    """Every other workload; `only` keeps the ones whose name contains it."""
     dev = torch.device("cuda:0")
     out = {}
 
+    def want(*names):
+        return only is None or any(only in n for n in names)
+
     def one(name, x, fmt, gran, shape, nsets=1, dq_dtype=None):
+        if not want(name):
+            return
         xs = [x] + [x.clone() for _ in range(nsets - 1)]
         bufs = [eng.alloc(fmt, gran, shape, dev) for _ in range(nsets)]
-        nb = x.numel() * x.element_size() + out_bytes(bufs[0]["sizes"])
-        ms = time_loop(torch, lambda i: eng.quantize(xs[i % nsets], fmt, gran, shape,
-                                                     bufs[i % nsets]), reps, 3)
-        out[name] = rec(nb, ms, op=f"quantize {fmt}/{gran}", shape=list(shape),
-                        dtype=str(x.dtype).replace("torch.", ""))
+        in_bytes = x.numel() * x.element_size()
+        nb = in_bytes + out_bytes(bufs[0]["sizes"])
+        two_pass = fmt == "nvfp4" or gran == "tensor"
+        t = time_reps(torch, lambda i: eng.quantize(xs[i % nsets], fmt, gran, shape,
+                                                    bufs[i % nsets]), reps, 3)
+        out[name] = rec(nb, t, in_bytes if two_pass else 0, op=f"quantize {fmt}/{gran}",
+                        shape=list(shape), dtype=str(x.dtype).replace("torch.", ""),
+                        rotated_sets=nsets)
         if dq_dtype is not None:
-            o = torch.empty(shape, dtype=dq_dtype, device=dev)
-            nbd = out_bytes(bufs[0]["sizes"]) + o.numel() * o.element_size()
-            ms = time_loop(torch, lambda i: eng.dequantize(bufs[i % nsets], fmt, gran, shape, o),
-                           reps, 3)
-            out[name + "_dequant"] = rec(nbd, ms, op=f"dequantize {fmt} -> "
+            o = [torch.empty(shape, dtype=dq_dtype, device=dev) for _ in range(min(nsets, 2))]
+            nbd = out_bytes(bufs[0]["sizes"]) + o[0].numel() * o[0].element_size()
+            t = time_reps(torch, lambda i: eng.dequantize(bufs[i % nsets], fmt, gran, shape,
+                                                          o[i % len(o)]), reps, 3)
+            out[name + "_dequant"] = rec(nbd, t, op=f"dequantize {fmt} -> "
                                          f"{str(dq_dtype).replace('torch.', '')}",
-                                         shape=list(shape))
+                                         shape=list(shape), rotated_sets=nsets)
         log(f"{name}: {out[name]['gbs']} GB/s")
 
-    # float32 MLP weight, MXFP4 and NVFP4 (cache-resident unless rotated: 16 sets)
-    w = synth.mlp_weight_fp32(device=dev)
-    one("mlp3072x1024_f32_mxfp4", w, "mxfp4", "blk32", (1, 3072, 1024), 16, torch.float32)
-    one("mlp3072x1024_f32_nvfp4", w, "nvfp4", "blk16", (1, 3072, 1024), 16, torch.float32)
-    del w
+    # float32 MLP weight, MXFP4 and NVFP4: 32 rotated copies (403 MB) so that the
+    # 256 MB Infinity Cache cannot hold them all
+    if want("mlp3072x1024"):
+        w = synth.mlp_weight_fp32(device=dev)
+        one("mlp3072x1024_f32_mxfp4", w, "mxfp4", "blk32", (1, 3072, 1024), 32, torch.float32)
+        one("mlp3072x1024_f32_nvfp4", w, "nvfp4", "blk16", (1, 3072, 1024), 32, torch.float32)
+        del w
     # heavy-tailed [28672, 8192] bf16 weight
-    w = synth.heavy_tail_weight(device=dev)
-    one("w28672x8192_bf16_mxfp4", w, "mxfp4", "blk32", (1, 28672, 8192), 2, torch.bfloat16)
-    one("w28672x8192_bf16_nvfp4", w, "nvfp4", "blk16", (1, 28672, 8192), 2, torch.bfloat16)
-    del w
+    if want("w28672x8192"):
+        w = synth.heavy_tail_weight(device=dev)
+        one("w28672x8192_bf16_mxfp4", w, "mxfp4", "blk32", (1, 28672, 8192), 2, torch.bfloat16)
+        one("w28672x8192_bf16_nvfp4", w, "nvfp4", "blk16", (1, 28672, 8192), 2, torch.bfloat16)
+        del w
     # FP8 weight alone (128x128 tiles)
-    w = synth.fp8_weight(device=dev)
-    one("w7168x2048_bf16_fp8_128x128", w, "fp8_e4m3", "128x128", (1, 7168, 2048), 8)
-    del w
+    if want("w7168x2048"):
+        w = synth.fp8_weight(device=dev)
+        one("w7168x2048_bf16_fp8_128x128", w, "fp8_e4m3", "128x128", (1, 7168, 2048), 8)
+        del w
     # 1 GiB bf16 tensor, every format
-    g = synth.gaussian(device=dev)
-    shp = (1, 65536, 8192)
-    for fmt, gran, dq in (("fp8_e4m3", "1x128", torch.bfloat16), ("fp8_e4m3", "128x128", None),
-                          ("fp8_e4m3", "row", None), ("fp8_e4m3", "tensor", None),
-                          ("mxfp4", "blk32", torch.bfloat16), ("nvfp4", "blk16", None),
-                          ("int4_asym", "grp128", torch.bfloat16)):
-        one(f"sweep1GiB_bf16_{fmt}_{gran}", g, fmt, gran, shp, 1, dq)
-    del g
+    sweep = (("fp8_e4m3", "1x128", torch.bfloat16), ("fp8_e4m3", "128x128", None),
+             ("fp8_e4m3", "row", None), ("fp8_e4m3", "tensor", None),
+             ("mxfp4", "blk32", torch.bfloat16), ("nvfp4", "blk16", None),
+             ("int4_asym", "grp128", torch.bfloat16))
+    names = [f"sweep1GiB_bf16_{f}_{g}" for f, g, _ in sweep]
+    if want(*names):
+        g = synth.gaussian(device=dev)
+        for name, (fmt, gran, dq) in zip(names, sweep):
+            one(name, g, fmt, gran, (1, 65536, 8192), 1, dq)
+        del g
     torch.cuda.empty_cache()
-    # FP8 KV write
+    if want("kv28x32768x8x128_bf16_fp8"):
+        out.update(bench_kv(torch, eng, synth, reps))
+    if want("llama8b_224w_bf16_int4_g128"):
+        out.update(bench_llama_int4(torch, eng, synth))
+    return out
+
+
+def bench_kv(torch, eng, synth, reps):
+    """FP8 KV write of K and V [28, 32768, 8, 128] bf16, one scale per slice."""
+    dev = torch.device("cuda:0")
+    out = {}
     k, v = synth.kv_cache(device=dev)
     kc = torch.empty(k.shape, dtype=torch.uint8, device=dev)
     vc = torch.empty_like(kc)
@@ -252,14 +308,20 @@ def bench_extras(torch, eng, synth, reps):
     ws = torch.empty((eng.L.pqb_kv_workspace_bytes(28, 32768 * 1024),), dtype=torch.uint8,
                      device=dev)
     nb = 2 * k.numel() * 2 + 2 * k.numel() + 2 * 28 * 4
-    ms = time_loop(torch, lambda i: eng.kv(k, v, kc, vc, ks, vs, ws), max(3, reps // 4), 2)
-    out["kv28x32768x8x128_bf16_fp8"] = rec(nb, ms, op="FP8 KV write (per-layer scales)",
-                                           shape=[28, 32768, 8, 128],
-                                           bytes_with_pass1_read=int(nb + 2 * k.numel() * 2))
+    t = time_reps(torch, lambda i: eng.kv(k, v, kc, vc, ks, vs, ws), max(5, reps // 2), 2)
+    out["kv28x32768x8x128_bf16_fp8"] = rec(nb, t, 2 * k.numel() * 2,
+                                           op="FP8 KV write (per-layer scales)",
+                                           shape=[28, 32768, 8, 128])
     log(f"kv: {out['kv28x32768x8x128_bf16_fp8']['gbs']} GB/s")
     del k, v, kc, vc
     torch.cuda.empty_cache()
-    # INT4 over the 224 Llama-3.1-8B-shaped decoder weights (one call per tensor)
+    return out
+
+
+def bench_llama_int4(torch, eng, synth):
+    """INT4 g128 over the 224 Llama-3.1-8B-shaped decoder weights."""
+    dev = torch.device("cuda:0")
+    out = {}
     ws_ = []
     bufs = []
     from precision_quantization_block_amd.synth import LLAMA_LAYERS, LLAMA_PROJ
@@ -281,14 +343,28 @@ def bench_extras(torch, eng, synth, reps):
         for (x, shp), b in zip(ws_, bufs):
             eng.quantize(x, "int4_asym", "grp128", shp, b)
 
-    ms = time_loop(torch, all_int4, 3, 1)
-    out["llama8b_224w_bf16_int4_g128"] = rec(nb, ms, op="INT4 g128 asym, 224 tensors, one "
+    t = time_reps(torch, all_int4, 5, 1)
+    out["llama8b_224w_bf16_int4_g128"] = rec(nb, t, op="INT4 g128 asym, 224 tensors, one "
                                              "pqb_quantize_batch call", launches=-(-224 // 24))
-    ms = time_loop(torch, one_by_one, 3, 1)
-    out["llama8b_224w_bf16_int4_g128_per_tensor"] = rec(nb, ms, op="same, one pqb_quantize "
+    t = time_reps(torch, one_by_one, 5, 1)
+    out["llama8b_224w_bf16_int4_g128_per_tensor"] = rec(nb, t, op="same, one pqb_quantize "
                                                         "call per tensor", launches=224)
     log(f"int4 llama: {out['llama8b_224w_bf16_int4_g128']['gbs']} GB/s batched, "
         f"{out['llama8b_224w_bf16_int4_g128_per_tensor']['gbs']} GB/s per tensor")
+    # dequantize all 224 back to bf16 (one call per tensor)
+    outs = [torch.empty(shp, dtype=torch.bfloat16, device=dev) for _, shp in ws_]
+    nbd = sum(out_bytes(b["sizes"]) + o.numel() * 2 for b, o in zip(bufs, outs))
+
+    def dq_all(i):
+        for (_, shp), b, o in zip(ws_, bufs, outs):
+            eng.dequantize(b, "int4_asym", "grp128", shp, o)
+
+    t = time_reps(torch, dq_all, 5, 1)
+    out["llama8b_224w_bf16_int4_g128_dequant"] = rec(nbd, t, op="dequantize INT4 -> bf16, "
+                                                     "224 tensors", launches=224)
+    log(f"int4 llama dequant: {out['llama8b_224w_bf16_int4_g128_dequant']['gbs']} GB/s")
+    del ws_, bufs, outs
+    torch.cuda.empty_cache()
     return out
 
 
@@ -296,20 +372,42 @@ def bench_extras(torch, eng, synth, reps):
 # CPU baseline: the oracle on a bounded sample of the headline workload
 # ----------------------------------------------------------------------------
 
-def cpu_baseline(torch, synth, act_rows=4608, w_rows=384):
+def cpu_baseline(torch, synth, act_rows=2304, w_rows=256, threads=None):
+    """The oracle on the host cores: single-threaded on the first rows of the
+    step's tensors, then one thread per core over row chunks of the whole step
+    (ctypes releases the GIL inside the C oracle)."""
     import oracle
-    a = synth.fp8_activation(device="cpu")[:act_rows].contiguous()
-    w = synth.fp8_weight(device="cpu")[:w_rows].contiguous()
+    from concurrent.futures import ThreadPoolExecutor
+    threads = threads or min(16, os.cpu_count() or 1)
+    A = synth.fp8_activation(device="cpu")
+    W = synth.fp8_weight(device="cpu")
     oracle.lib()
+
+    def step_bytes(a_rows, w_rows_):
+        return a_rows * 7168 * 3 + a_rows * 56 * 4 + w_rows_ * 2048 * 3 + (w_rows_ // 128) * 16 * 4
+
+    a, w = A[:act_rows].contiguous(), W[:w_rows].contiguous()
     t0 = time.perf_counter()
-    ac, as_ = oracle.fp8_quantize(a, "1x128")
-    wc, ws = oracle.fp8_quantize(w, "128x128")
-    dt = time.perf_counter() - t0
-    nbytes = a.numel() * 2 + ac.nbytes + as_.nbytes + w.numel() * 2 + wc.nbytes + ws.nbytes
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {act_rows} of 8192 activation rows (1x128) and first {w_rows} of "
-                      f"7168 weight rows (128x128), single-threaded scalar oracle, "
-                      f"{dt:.1f} s for {nbytes / 1e6:.1f} MB",
+    oracle.fp8_quantize(a, "1x128")
+    oracle.fp8_quantize(w, "128x128")
+    dt1 = time.perf_counter() - t0
+    nb1 = step_bytes(act_rows, w_rows)
+    # whole step, row chunks (multiples of 128 rows for the 128x128 weight)
+    a_chunks = [A[i:i + 256] for i in range(0, 8192, 256)]
+    w_chunks = [W[i:i + 256] for i in range(0, 7168, 256)]
+    jobs = [(c, "128x128") for c in w_chunks] + [(c, "1x128") for c in a_chunks]
+    with ThreadPoolExecutor(threads) as ex:
+        t0 = time.perf_counter()
+        list(ex.map(lambda j: oracle.fp8_quantize(j[0], j[1]), jobs))
+        dtn = time.perf_counter() - t0
+    nbn = step_bytes(8192, 7168)
+    return {"value": round(nbn / dtn / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole W8A8 step (activations [8192x7168] 1x128 + weight [7168x2048] "
+                      f"128x128), {threads} threads over 256-row chunks: {dtn:.2f} s wall for "
+                      f"{nbn / 1e6:.1f} MB",
+            "single_thread": {"value": round(nb1 / dt1 / 1e9, 4), "cores": 1,
+                              "sample": f"first {act_rows} activation rows and first {w_rows} "
+                                        f"weight rows: {dt1:.1f} s for {nb1 / 1e6:.1f} MB"},
             "host_cpu": _cpu_model(), "host_cores_available": os.cpu_count()}
 
 
@@ -322,6 +420,28 @@ def _cpu_model():
     except OSError:
         pass
     return None
+
+
+def hbm_reference(torch, reps=10):
+    """Bandwidth of plain torch elementwise kernels over bf16 buffers, by
+    read:write ratio (neg 1:1, add 2:1, addcmul 3:1; 1 GiB written by neg,
+    512 MiB by the others), as context for the 8 TB/s published peak."""
+    n = 1 << 29  # bf16 elements = 1 GiB
+    a = torch.ones((n,), dtype=torch.bfloat16, device="cuda:0")
+    b = torch.ones((n,), dtype=torch.bfloat16, device="cuda:0")
+    c = torch.empty((n,), dtype=torch.bfloat16, device="cuda:0")
+    h = n // 2
+    res = {}
+    t = time_loop(torch, lambda i: torch.neg(a, out=c), reps, 2)
+    res["neg_1r1w_gbs"] = round(2 * n * 2 / (t * 1e-3) / 1e9, 1)
+    t = time_loop(torch, lambda i: torch.add(a[:h], b[:h], out=c[:h]), reps, 2)
+    res["add_2r1w_gbs"] = round(3 * h * 2 / (t * 1e-3) / 1e9, 1)
+    t = time_loop(torch, lambda i: torch.addcmul(a[:h], b[:h], a[h:], out=c[:h]), reps, 2)
+    res["addcmul_3r1w_gbs"] = round(4 * h * 2 / (t * 1e-3) / 1e9, 1)
+    del a, b, c
+    torch.cuda.empty_cache()
+    log(f"hbm reference: {res}")
+    return res
 
 
 def copy_probe(torch, reps=3):
@@ -347,6 +467,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--reps", type=int, default=20)
+    ap.add_argument("--only", default=None,
+                    help="run only the format workloads whose name contains this string "
+                         "(no headline line; prints the records as JSON)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -365,6 +488,9 @@ def main():
 
     if args.copy_probe:
         copy_probe(torch)
+    if args.only is not None:
+        print(json.dumps(bench_extras(torch, eng, synth, args.reps, args.only)), flush=True)
+        return
 
     m = bench_main(torch, eng, synth, args.steps, args.warmup, args.sets)
     value = m["step_bytes"] / (m["ms_per_step"] * 1e-3) / 1e9
@@ -400,6 +526,7 @@ def main():
     }
     if not args.no_extras:
         line["formats"] = bench_extras(torch, eng, synth, args.reps)
+        line["hbm_reference"] = hbm_reference(torch)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(torch, synth)
     else:

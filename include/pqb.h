@@ -134,9 +134,9 @@ typedef struct pqb_job {
   int32_t reserved; /* must be 0 (else PQB_ERR_ENUM) */
 } pqb_job;
 
-/* Quantize several tensors with as few launches as possible: the 128x128,
- * 1x128, MXFP4 and INT4 jobs share fused launches of up to 24 jobs, per-row
- * FP8 jobs get a launch each.  Each job's outputs are exactly those of
+/* Quantize several tensors with as few launches as possible: jobs of one
+ * family share fused launches of up to 24 jobs (FP8 1x128 and 128x128
+ * together; MXFP4; INT4), per-row FP8 jobs get a launch each.  Each job's outputs are exactly those of
  * pqb_quantize on the same arguments.  Only the one-pass formats qualify (FP8
  * ROW / BLK_1x128 / BLK_128x128, MXFP4, INT4); a per-tensor FP8 or NVFP4 job
  * returns PQB_ERR_COMBO.  Every job is validated (same rules and codes as

@@ -183,23 +183,25 @@ inline int grid_cap(int64_t work, int64_t per_block, int64_t cap) {
   return (int)(g < 1 ? 1 : (g > cap ? cap : g));
 }
 
-// Workgroups for the table-building kernels: enough to fill the chip, few
-// enough that each one amortizes its table over many tiles.
+// Workgroups for the NVFP4 pass-2 kernel, which rebuilds gs, the E2M1 table
+// and the 127-entry scale tables per workgroup: enough to fill the chip, few
+// enough that each one amortizes its tables over many tiles.
 constexpr int64_t kTableKernelCap = 256 * 8;
 
 }  // namespace
 
 hipError_t launch_mxfp4(const void* x, bool bf16, int64_t n, uint8_t* codes, uint8_t* scales,
                         hipStream_t st) {
-  constexpr int kUnr = 4;
+  // one chunk per wave (8 KiB of input: 8 tiles of bf16 or 4 of float32); the
+  // table fill costs each workgroup two dword stores per thread and one barrier
   const int64_t nunits = n / 8, ntiles = (nunits + kWave - 1) / kWave;
-  const int grid = grid_cap(ntiles, (int64_t)kUnr * (kBlockThreads / kWave), kTableKernelCap);
+  const int64_t waves = kBlockThreads / kWave;
   if (bf16)
-    hipLaunchKernelGGL((k_mxfp4<uint16_t, kUnr>), dim3(grid), dim3(kBlockThreads), 0, st,
-                       (const uint16_t*)x, nunits, codes, scales);
+    hipLaunchKernelGGL((k_mxfp4<uint16_t, 8>), dim3(grid_cap(ntiles, 8 * waves, 1 << 30)),
+                       dim3(kBlockThreads), 0, st, (const uint16_t*)x, nunits, codes, scales);
   else
-    hipLaunchKernelGGL((k_mxfp4<float, kUnr>), dim3(grid), dim3(kBlockThreads), 0, st,
-                       (const float*)x, nunits, codes, scales);
+    hipLaunchKernelGGL((k_mxfp4<float, 4>), dim3(grid_cap(ntiles, 4 * waves, 1 << 30)),
+                       dim3(kBlockThreads), 0, st, (const float*)x, nunits, codes, scales);
   return hipGetLastError();
 }
 

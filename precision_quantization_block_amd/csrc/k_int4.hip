@@ -59,15 +59,15 @@ inline int grid_for(int64_t work, int64_t per_block, int64_t cap) {
 
 hipError_t launch_int4(const void* x, bool bf16, int64_t n, uint8_t* codes, uint16_t* scales,
                        uint8_t* zeros, hipStream_t st) {
-  constexpr int kUnr = 4;
+  // one chunk per wave: 8 tiles of bf16 or 4 of float32 (8 KiB of input)
   const int64_t nunits = n / 8, ntiles = (nunits + kWave - 1) / kWave;
-  const int grid = grid_for(ntiles, (int64_t)kUnr * (kBlockThreads / kWave), 1 << 30);
+  const int64_t waves = kBlockThreads / kWave;
   if (bf16)
-    hipLaunchKernelGGL((k_int4<uint16_t, kUnr>), dim3(grid), dim3(kBlockThreads), 0, st,
-                       (const uint16_t*)x, nunits, codes, scales, zeros);
+    hipLaunchKernelGGL((k_int4<uint16_t, 8>), dim3(grid_for(ntiles, 8 * waves, 1 << 30)),
+                       dim3(kBlockThreads), 0, st, (const uint16_t*)x, nunits, codes, scales, zeros);
   else
-    hipLaunchKernelGGL((k_int4<float, kUnr>), dim3(grid), dim3(kBlockThreads), 0, st,
-                       (const float*)x, nunits, codes, scales, zeros);
+    hipLaunchKernelGGL((k_int4<float, 4>), dim3(grid_for(ntiles, 4 * waves, 1 << 30)),
+                       dim3(kBlockThreads), 0, st, (const float*)x, nunits, codes, scales, zeros);
   return hipGetLastError();
 }
 
