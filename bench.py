@@ -219,9 +219,12 @@ def bench_main(torch, eng, synth, steps, warmup, nsets):
     a_avg = time_loop(torch, act_only, steps, 0)
     log(f"main: {steps} fused steps {ms_total:.3f} ms (wall {wall * 1e3:.3f} ms); "
         f"two launches {ms_two * 1e3:.1f} us/step; activation kernel {a_avg * 1e3:.1f} us")
+    # leave set 0's outputs from the fused kernel in place for the parity check
+    step(0)
+    torch.cuda.synchronize()
     return {"ms_per_step": ms_total / steps, "step_bytes": step_bytes, "act_bytes": a_bytes,
             "w_bytes": w_bytes, "ms_two_launches": ms_two, "act_kernel_ms_avg": a_avg,
-            "wall_s": wall}
+            "wall_s": wall, "set0": sets[0]}
 
 
 # ----------------------------------------------------------------------------
@@ -372,34 +375,37 @@ def bench_llama_int4(torch, eng, synth):
 # CPU baseline: the oracle on a bounded sample of the headline workload
 # ----------------------------------------------------------------------------
 
-def cpu_baseline(torch, synth, act_rows=2304, w_rows=256, threads=None):
-    """The oracle on the host cores: single-threaded on the first rows of the
-    step's tensors, then one thread per core over row chunks of the whole step
-    (ctypes releases the GIL inside the C oracle)."""
+def cpu_baseline(torch, a_host, w_host, act_rows=2304, w_rows=256, threads=None):
+    """The oracle on the host cores, on the same inputs as the GPU's set 0:
+    single-threaded on the first rows of the step's tensors, then one thread per
+    core over row chunks of the whole step (ctypes releases the GIL inside the
+    C oracle).  Returns the record and the oracle's outputs for the whole step."""
+    import numpy as np
     import oracle
     from concurrent.futures import ThreadPoolExecutor
     threads = threads or min(16, os.cpu_count() or 1)
-    A = synth.fp8_activation(device="cpu")
-    W = synth.fp8_weight(device="cpu")
     oracle.lib()
 
     def step_bytes(a_rows, w_rows_):
         return a_rows * 7168 * 3 + a_rows * 56 * 4 + w_rows_ * 2048 * 3 + (w_rows_ // 128) * 16 * 4
 
-    a, w = A[:act_rows].contiguous(), W[:w_rows].contiguous()
     t0 = time.perf_counter()
-    oracle.fp8_quantize(a, "1x128")
-    oracle.fp8_quantize(w, "128x128")
+    oracle.fp8_quantize(a_host[:act_rows].contiguous(), "1x128")
+    oracle.fp8_quantize(w_host[:w_rows].contiguous(), "128x128")
     dt1 = time.perf_counter() - t0
     nb1 = step_bytes(act_rows, w_rows)
     # whole step, row chunks (multiples of 128 rows for the 128x128 weight)
-    a_chunks = [A[i:i + 256] for i in range(0, 8192, 256)]
-    w_chunks = [W[i:i + 256] for i in range(0, 7168, 256)]
-    jobs = [(c, "128x128") for c in w_chunks] + [(c, "1x128") for c in a_chunks]
+    jobs = [(w_host[i:i + 256], "128x128") for i in range(0, 7168, 256)] + \
+           [(a_host[i:i + 256], "1x128") for i in range(0, 8192, 256)]
     with ThreadPoolExecutor(threads) as ex:
         t0 = time.perf_counter()
-        list(ex.map(lambda j: oracle.fp8_quantize(j[0], j[1]), jobs))
+        res = list(ex.map(lambda j: oracle.fp8_quantize(j[0].contiguous(), j[1]), jobs))
         dtn = time.perf_counter() - t0
+    nw = 7168 // 256
+    outs = {"w_codes": np.concatenate([r[0].reshape(-1) for r in res[:nw]]),
+            "w_scales": np.concatenate([r[1].reshape(-1) for r in res[:nw]]),
+            "a_codes": np.concatenate([r[0].reshape(-1) for r in res[nw:]]),
+            "a_scales": np.concatenate([r[1].reshape(-1) for r in res[nw:]])}
     nbn = step_bytes(8192, 7168)
     return {"value": round(nbn / dtn / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"the whole W8A8 step (activations [8192x7168] 1x128 + weight [7168x2048] "
@@ -408,7 +414,26 @@ def cpu_baseline(torch, synth, act_rows=2304, w_rows=256, threads=None):
             "single_thread": {"value": round(nb1 / dt1 / 1e9, 4), "cores": 1,
                               "sample": f"first {act_rows} activation rows and first {w_rows} "
                                         f"weight rows: {dt1:.1f} s for {nb1 / 1e6:.1f} MB"},
-            "host_cpu": _cpu_model(), "host_cores_available": os.cpu_count()}
+            "host_cpu": _cpu_model(), "host_cores_available": os.cpu_count()}, outs
+
+
+def parity_of_step(torch, set0, outs):
+    """Byte-compare the GPU's codes and scales for one W8A8 step with the oracle's."""
+    import numpy as np
+    _, _, wb, ab = set0
+    mism, total = 0, 0
+    for key, buf, name in (("w_codes", wb, "codes"), ("w_scales", wb, "scales"),
+                           ("a_codes", ab, "codes"), ("a_scales", ab, "scales")):
+        ref = outs[key].view(np.uint8)
+        got = buf[name][: buf["sizes"][name]].cpu().numpy()
+        if got.shape != ref.shape:
+            mism += max(got.size, ref.size)
+        else:
+            mism += int(np.count_nonzero(got != ref))
+        total += ref.size
+    return {"checked": "every code and scale byte of one fused W8A8 step (buffer set 0) "
+                       "against the oracle on the same inputs",
+            "bytes_compared": total, "mismatches": mism}
 
 
 def _cpu_model():
@@ -527,11 +552,17 @@ def main():
     if not args.no_extras:
         line["formats"] = bench_extras(torch, eng, synth, args.reps)
         line["hbm_reference"] = hbm_reference(torch)
+    line["parity"] = None
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(torch, synth)
+        w0, a0 = m["set0"][0], m["set0"][1]
+        line["cpu_baseline"], outs = cpu_baseline(torch, a0.cpu(), w0.cpu())
+        line["parity"] = parity_of_step(torch, m["set0"], outs)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)
+    if line["parity"] is not None and line["parity"]["mismatches"]:
+        log(f"PARITY FAILURE: {line['parity']['mismatches']} bytes differ from the oracle")
+        sys.exit(3)
 
 
 if __name__ == "__main__":
