@@ -58,7 +58,8 @@ def lib():
         L.orc_uniform_code.restype = ctypes.c_float
         for name in ("orc_fp8_quantize", "orc_fp8_dequantize", "orc_mxfp4_quantize",
                      "orc_mxfp4_dequantize", "orc_nvfp4_quantize", "orc_nvfp4_dequantize",
-                     "orc_int4_quantize", "orc_int4_dequantize", "orc_kv_write_fp8"):
+                     "orc_int4_quantize", "orc_int4_dequantize", "orc_kv_write_fp8",
+                     "orc_kv_quant_fp8"):
             getattr(L, name).restype = I
         for name in ("orc_e4m3_encode_n", "orc_e2m1_encode_n", "orc_bf16_round_n"):
             getattr(L, name).argtypes = [P, I64, P]
@@ -72,6 +73,7 @@ def lib():
         L.orc_int4_quantize.argtypes = [P, I, I64, I64, I64, P, P, P]
         L.orc_int4_dequantize.argtypes = [P, P, P, I64, I64, I64, I, P]
         L.orc_kv_write_fp8.argtypes = [P, P, I, I64, I64, P, P, P, P]
+        L.orc_kv_quant_fp8.argtypes = [P, I, I64, I64, I64, I64, I, P, P]
         _lib = L
     return _lib
 
@@ -297,6 +299,26 @@ def kv_write_fp8(k, v, bf16=None):
     _check(lib().orc_kv_write_fp8(_p(k2), _p(v2), dtk, layers, per, _p(kc), _p(vc), _p(ks),
                                   _p(vs)), "kv_write_fp8")
     return kc, vc, ks, vs
+
+
+KV_MODES = {"layer": 0, "head": 1, "static": 2}
+
+
+def kv_quant_fp8(x, mode, scales=None, bf16=None):
+    """FP8 KV-cache variant on x [layers, tokens, heads, head_dim].
+    mode "layer" -> scales [layers]; "head" -> [layers, heads]; "static" uses
+    the given float32 scales [layers].  -> (codes u8 of x's shape, scales)."""
+    mode = KV_MODES.get(mode, mode)
+    L, T, H, D = x.shape
+    x2, dt, *_ = _as_input(x.reshape(L, -1), bf16)
+    codes = np.empty((L, T, H, D), np.uint8)
+    if mode == 2:
+        sc = np.ascontiguousarray(np.asarray(scales, np.float32).reshape(L))
+    else:
+        sc = np.empty((L, H) if mode == 1 else (L,), np.float32)
+    _check(lib().orc_kv_quant_fp8(_p(x2), dt, L, T, H, D, mode, _p(codes), _p(sc)),
+           "kv_quant_fp8")
+    return codes, sc
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:

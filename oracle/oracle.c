@@ -407,6 +407,52 @@ int orc_kv_write_fp8(const void* k, const void* v, int dtype, int64_t layers,
 }
 
 /* ------------------------------------------------------------------------ */
+/* FP8 KV-cache variants [DEPLOY KV Cache 量化：误差要和信号比]               */
+/* ------------------------------------------------------------------------ */
+
+/* The page quantizes K and V with quantizers chosen independently: per tensor
+ * (one scale for the layer's whole cache), or per head (its per_head function:
+ * the amax over the token and head_dim axes, so every (layer, head) gets
+ * max(amax, 1e-12) / 448).  For deployment it recommends scales computed
+ * offline from calibration data; with such a static scale s the write is
+ * E4M3(clamp(x / s, -448, 448)) and the clamp can bind.
+ * Layout: x is [layers, tokens, heads, head_dim], row-major (token-major, as a
+ * paged cache stores it); the per-head scope of (l, h) is x[l, :, h, :].
+ * Scales: LAYER [layers]; HEAD [layers, heads]; STATIC [layers], read. */
+static int64_t kv_scope(int mode, int64_t heads, int64_t l, int64_t h) {
+  return mode == ORC_KV_HEAD ? l * heads + h : l;
+}
+
+int orc_kv_quant_fp8(const void* x, int dtype, int64_t layers, int64_t tokens, int64_t heads,
+                     int64_t head_dim, int mode, uint8_t* codes, float* scales) {
+  if (layers < 0 || tokens < 0 || heads < 0 || head_dim < 0) return -4;
+  if (mode < ORC_KV_LAYER || mode > ORC_KV_STATIC) return -2;
+  int64_t nscopes = mode == ORC_KV_HEAD ? layers * heads : layers;
+  if (mode != ORC_KV_STATIC) {
+    /* pass 1: the amax of every scope */
+    for (int64_t i = 0; i < nscopes; ++i) scales[i] = 0.0f;
+    for (int64_t l = 0; l < layers; ++l)
+      for (int64_t t = 0; t < tokens; ++t)
+        for (int64_t h = 0; h < heads; ++h)
+          for (int64_t d = 0; d < head_dim; ++d) {
+            int64_t i = ((l * tokens + t) * heads + h) * head_dim + d;
+            int64_t si = kv_scope(mode, heads, l, h);
+            scales[si] = fmaxf(scales[si], fabsf(ld(x, dtype, i)));
+          }
+    for (int64_t i = 0; i < nscopes; ++i) scales[i] = fp8_scale(scales[i]);
+  }
+  /* pass 2: codes, with the clamp of the page's fp8 helper */
+  for (int64_t l = 0; l < layers; ++l)
+    for (int64_t t = 0; t < tokens; ++t)
+      for (int64_t h = 0; h < heads; ++h)
+        for (int64_t d = 0; d < head_dim; ++d) {
+          int64_t i = ((l * tokens + t) * heads + h) * head_dim + d;
+          codes[i] = fp8_code(ld(x, dtype, i), scales[kv_scope(mode, heads, l, h)]);
+        }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Array forms of the codecs (for exhaustive tests)                          */
 /* ------------------------------------------------------------------------ */
 

@@ -75,6 +75,12 @@ int orc_int4_dequantize(const uint8_t* codes, const uint16_t* scales, const uint
                         int64_t batch, int64_t rows, int64_t cols, int out_dtype, void* out);
 
 /* FP8 KV-cache write: one per-tensor scale per layer, separately for K and V */
+/* FP8 KV-cache variants on [layers, tokens, heads, head_dim]: one scale per
+ * layer (LAYER), per (layer, head) over tokens x head_dim (HEAD), or a given
+ * per-layer scale (STATIC, scales read).  Returns -2 for an unknown mode. */
+enum { ORC_KV_LAYER = 0, ORC_KV_HEAD = 1, ORC_KV_STATIC = 2 };
+int orc_kv_quant_fp8(const void* x, int dtype, int64_t layers, int64_t tokens, int64_t heads,
+                     int64_t head_dim, int mode, uint8_t* codes, float* scales);
 int orc_kv_write_fp8(const void* k, const void* v, int dtype, int64_t layers,
                      int64_t elems_per_layer, uint8_t* k_codes, uint8_t* v_codes,
                      float* k_scales, float* v_scales);
