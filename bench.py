@@ -316,6 +316,30 @@ def bench_kv(torch, eng, synth, reps):
                                            op="FP8 KV write (per-layer scales)",
                                            shape=[28, 32768, 8, 128])
     log(f"kv: {out['kv28x32768x8x128_bf16_fp8']['gbs']} GB/s")
+    # the same cache with a scale per (layer, head), and with static per-layer scales
+    L_, T_, H_, D_ = 28, 32768, 8, 128
+    ksh = torch.empty((L_, H_), dtype=torch.float32, device=dev)
+    vsh = torch.empty_like(ksh)
+    wsx = torch.empty((eng.L.pqb_kv_workspace_bytes_ex(L_, T_, H_, D_),), dtype=torch.uint8,
+                      device=dev)
+    P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None  # noqa: E731
+
+    def kv_ex(km, vm, ks_, vs_):
+        rc = eng.L.pqb_kv_write_fp8_ex(P(k), P(v), 1, L_, T_, H_, D_, km, vm, P(kc), P(vc),
+                                       P(ks_), P(vs_), P(wsx), wsx.numel(), eng.stream)
+        if rc != 0:
+            raise RuntimeError(f"pqb_kv_write_fp8_ex: status {rc}")
+
+    t = time_reps(torch, lambda i: kv_ex(1, 1, ksh, vsh), max(5, reps // 2), 2)
+    out["kv28x32768x8x128_bf16_fp8_per_head"] = rec(nb - 2 * 28 * 4 + 2 * 28 * 8 * 4, t,
+                                                    2 * k.numel() * 2,
+                                                    op="FP8 KV write, scale per (layer, head)",
+                                                    shape=[28, 32768, 8, 128])
+    t = time_reps(torch, lambda i: kv_ex(2, 2, ks, vs), max(5, reps // 2), 2)
+    out["kv28x32768x8x128_bf16_fp8_static"] = rec(nb, t, op="FP8 KV write, static per-layer "
+                                                  "scales (one pass)", shape=[28, 32768, 8, 128])
+    log(f"kv per head: {out['kv28x32768x8x128_bf16_fp8_per_head']['gbs']} GB/s, static: "
+        f"{out['kv28x32768x8x128_bf16_fp8_static']['gbs']} GB/s")
     del k, v, kc, vc
     torch.cuda.empty_cache()
     return out

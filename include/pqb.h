@@ -163,6 +163,39 @@ pqb_status pqb_kv_write_fp8(const void* k, const void* v, pqb_dtype dtype, int64
                             float* k_scales, float* v_scales, void* workspace,
                             size_t workspace_bytes, void* stream);
 
+/* FP8 KV-cache write with a scale mode chosen for K and for V separately
+ * (page "量化部署实战", section KV Cache 量化：误差要和信号比: K and V get
+ * independent quantizers; per_head takes the amax over the token and head_dim
+ * axes; calibrated scales computed offline are recommended for deployment).
+ *
+ * K and V are [layers, tokens, heads, head_dim] of `dtype`, token-major (the
+ * layout of a paged cache); codes have the same layout, one byte each.
+ *   PQB_KV_LAYER   one dynamic scale per layer: scales [layers] (written);
+ *                  identical to pqb_kv_write_fp8.
+ *   PQB_KV_HEAD    one dynamic scale per (layer, head) over tokens x head_dim:
+ *                  scales [layers, heads] (written).
+ *   PQB_KV_STATIC  a given scale per layer (calibrated offline): scales
+ *                  [layers] are READ; codes are E4M3(clamp(x / s, -448, 448)),
+ *                  where the clamp can bind.  Each s must lie in [2^-64, 2^126)
+ *                  (results for other s are unspecified).
+ * Dynamic scales are max(amax, 1e-12) / 448.  Pass k = NULL (or v = NULL) to
+ * write only the other; its codes and scales pointers are then ignored.
+ * Shape rules: head_dim % 8 == 0; for PQB_KV_HEAD also heads <= 256 and
+ * r / gcd(r, 256) <= 64 for the row width r = heads * head_dim / 8 (e.g. 8 x 128,
+ * 32 x 128, 40 x 128, 12 x 64).
+ * Workspace (only when a dynamic mode is used): pqb_kv_workspace_bytes_ex(),
+ * 16-byte aligned.  Alignment: k, v and codes 16 bytes, scales 4 bytes.
+ * Errors: PQB_ERR_ENUM for an unknown dtype or mode, PQB_ERR_SHAPE for shapes
+ * breaking the rules above, PQB_ERR_NULL if both k and v are NULL or a needed
+ * pointer is NULL, PQB_ERR_WORKSPACE, PQB_ERR_ALIGN; all before any launch. */
+typedef enum pqb_kv_mode { PQB_KV_LAYER = 0, PQB_KV_HEAD = 1, PQB_KV_STATIC = 2 } pqb_kv_mode;
+size_t pqb_kv_workspace_bytes_ex(int64_t layers, int64_t tokens, int64_t heads, int64_t head_dim);
+pqb_status pqb_kv_write_fp8_ex(const void* k, const void* v, pqb_dtype dtype, int64_t layers,
+                               int64_t tokens, int64_t heads, int64_t head_dim,
+                               pqb_kv_mode k_mode, pqb_kv_mode v_mode, uint8_t* k_codes,
+                               uint8_t* v_codes, float* k_scales, float* v_scales,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* Element codecs exposed for testing the rounding rules on arrays of float32:
  * E4M3 of y (round-to-nearest-even; |y| must not exceed 464) into one byte
  * per element; E2M1 of y (ties to the smaller magnitude, saturating at 6)

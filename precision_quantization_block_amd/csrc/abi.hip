@@ -316,6 +316,73 @@ pqb_status pqb_kv_write_fp8(const void* k, const void* v, pqb_dtype dtype, int64
                                       (float*)workspace, (hipStream_t)stream));
 }
 
+static bool kv_dims_ok(int64_t layers, int64_t tokens, int64_t heads, int64_t head_dim) {
+  if (layers < 0 || tokens < 0 || heads < 0 || head_dim < 0 || head_dim % 8) return false;
+  if (layers > kMaxGridY) return false;
+  if (heads > 0 && head_dim > INT32_MAX / 8 / heads) return false;  // row width fits int32
+  const int64_t row = heads * head_dim;
+  if (row > 0 && tokens > INT64_MAX / 4 / row) return false;
+  if (row * tokens > 0 && layers > INT64_MAX / 4 / (row * tokens)) return false;
+  return true;
+}
+
+static bool kv_head_ok(int64_t heads, int64_t head_dim) {
+  return heads <= kMaxKvHeads && kv_stride_multiple(heads * head_dim / 8) <= kMaxKvStrideMultiple;
+}
+
+size_t pqb_kv_workspace_bytes_ex(int64_t layers, int64_t tokens, int64_t heads,
+                                 int64_t head_dim) {
+  if (!kv_dims_ok(layers, tokens, heads, head_dim)) return 0;
+  if (layers == 0 || tokens == 0 || heads == 0 || head_dim == 0) return 0;
+  const int64_t per_layer = tokens * heads * head_dim, row_units = heads * head_dim / 8;
+  size_t best = 0;
+  for (int nt = 1; nt <= 2; ++nt)
+    for (int head = 0; head <= (kv_head_ok(heads, head_dim) ? 1 : 0); ++head) {
+      const size_t b = 4 * (size_t)nt * (size_t)layers *
+                       (size_t)kv_partials_per_slice(layers, per_layer, row_units, nt, head) *
+                       (size_t)heads;
+      if (b > best) best = b;
+    }
+  return best;
+}
+
+pqb_status pqb_kv_write_fp8_ex(const void* k, const void* v, pqb_dtype dtype, int64_t layers,
+                               int64_t tokens, int64_t heads, int64_t head_dim,
+                               pqb_kv_mode k_mode, pqb_kv_mode v_mode, uint8_t* k_codes,
+                               uint8_t* v_codes, float* k_scales, float* v_scales,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(dtype)) return PQB_ERR_ENUM;
+  const int modes[2] = {(int)k_mode, (int)v_mode};
+  for (int m : modes)
+    if (m < PQB_KV_LAYER || m > PQB_KV_STATIC) return PQB_ERR_ENUM;
+  if (!kv_dims_ok(layers, tokens, heads, head_dim)) return PQB_ERR_SHAPE;
+  const void* xs[2] = {k, v};
+  uint8_t* cs[2] = {k_codes, v_codes};
+  float* ss[2] = {k_scales, v_scales};
+  KvTensor t[2];
+  int nt = 0;
+  bool dynamic = false;
+  for (int i = 0; i < 2; ++i) {
+    if (!xs[i]) continue;
+    if (modes[i] == PQB_KV_HEAD && !kv_head_ok(heads, head_dim)) return PQB_ERR_SHAPE;
+    t[nt++] = KvTensor{xs[i], cs[i], ss[i], modes[i]};
+    dynamic |= modes[i] != PQB_KV_STATIC;
+  }
+  if (nt == 0) return PQB_ERR_NULL;
+  if (layers == 0 || tokens == 0 || heads == 0 || head_dim == 0) return PQB_OK;
+  for (int i = 0; i < nt; ++i)
+    if (!t[i].codes || !t[i].scales) return PQB_ERR_NULL;
+  if (dynamic && !workspace) return PQB_ERR_NULL;
+  if (dynamic && workspace_bytes < pqb_kv_workspace_bytes_ex(layers, tokens, heads, head_dim))
+    return PQB_ERR_WORKSPACE;
+  for (int i = 0; i < nt; ++i)
+    if (!aligned(t[i].x, 16) || !aligned(t[i].codes, 16) || !aligned(t[i].scales, 4))
+      return PQB_ERR_ALIGN;
+  if (dynamic && !aligned(workspace, 16)) return PQB_ERR_ALIGN;
+  return hip_status(launch_kv_fp8(t, nt, dtype == PQB_BF16, layers, tokens, heads, head_dim,
+                                  (uint32_t*)workspace, (hipStream_t)stream));
+}
+
 pqb_status pqb_encode_e4m3(const float* y, int64_t n, uint8_t* out, void* stream) {
   if (n < 0) return PQB_ERR_SHAPE;
   if (n == 0) return PQB_OK;

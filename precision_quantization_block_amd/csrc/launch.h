@@ -65,6 +65,27 @@ struct MultiJob {
 };
 hipError_t launch_multi(const MultiJob* jobs, int njobs, hipStream_t st);
 
+// ---- FP8 KV-cache write with a scale mode per tensor ------------------------
+// x is [layers, tokens, heads, head_dim]; scales [layers] (LAYER, STATIC: read)
+// or [layers, heads] (HEAD).  Partials: uint32 amax bits, [tensor][layer][P][heads].
+enum KvMode { kKvLayer = 0, kKvHead = 1, kKvStatic = 2 };
+constexpr int kMaxKvHeads = 256;
+struct KvTensor {
+  const void* x;
+  uint8_t* codes;
+  float* scales;
+  int mode;
+};
+// Grid strides of the per-head passes are multiples of row_units; they are
+// rounded to kv_stride_multiple(row_units) workgroups (at most kMaxKvStrideMultiple).
+constexpr int64_t kMaxKvStrideMultiple = 64;
+int64_t kv_stride_multiple(int64_t row_units);
+int kv_partials_per_slice(int64_t layers, int64_t per_layer, int64_t row_units, int ntensors,
+                          bool head);
+hipError_t launch_kv_fp8(const KvTensor* t, int ntensors, bool bf16, int64_t layers,
+                         int64_t tokens, int64_t heads, int64_t head_dim, uint32_t* partials,
+                         hipStream_t st);
+
 // ---- element codecs ---------------------------------------------------------
 hipError_t launch_encode_e4m3(const float* y, int64_t n, uint8_t* out, hipStream_t st);
 hipError_t launch_encode_e2m1(const float* y, int64_t n, uint8_t* out, hipStream_t st);

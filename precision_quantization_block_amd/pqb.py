@@ -64,10 +64,13 @@ def lib():
         L.pqb_quantize_batch.argtypes = [ctypes.POINTER(_Job), I64, P]
         L.pqb_kv_workspace_bytes.argtypes, L.pqb_kv_workspace_bytes.restype = [I64, I64], SZ
         L.pqb_kv_write_fp8.argtypes = [P, P, I, I64, I64, P, P, P, P, P, SZ, P]
+        L.pqb_kv_workspace_bytes_ex.argtypes = [I64, I64, I64, I64]
+        L.pqb_kv_workspace_bytes_ex.restype = SZ
+        L.pqb_kv_write_fp8_ex.argtypes = [P, P, I, I64, I64, I64, I64, I, I, P, P, P, P, P, SZ, P]
         L.pqb_encode_e4m3.argtypes = [P, I64, P, P]
         L.pqb_encode_e2m1.argtypes = [P, I64, P, P]
         for f in ("pqb_query_sizes", "pqb_quantize", "pqb_quantize_batch", "pqb_dequantize",
-                  "pqb_kv_write_fp8",
+                  "pqb_kv_write_fp8", "pqb_kv_write_fp8_ex",
                   "pqb_encode_e4m3", "pqb_encode_e2m1"):
             getattr(L, f).restype = I
         _lib = L
@@ -228,6 +231,54 @@ def kv_write_fp8(k: torch.Tensor, v: torch.Tensor, workspace: torch.Tensor | Non
                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
                                   _stream(dev)), "kv_write_fp8")
     return kc, vc, ks, vs
+
+
+KV_MODES = {"layer": 0, "head": 1, "static": 2}
+
+
+def kv_write_fp8_ex(k: torch.Tensor | None, v: torch.Tensor | None, k_mode="layer",
+                    v_mode="layer", k_scales: torch.Tensor | None = None,
+                    v_scales: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """FP8 KV write with a scale mode per tensor; K and V are [layers, tokens,
+    heads, head_dim] (either may be None).  Modes: "layer" (scales [layers]),
+    "head" (scales [layers, heads]) or "static" (the given float32 scales
+    [layers] are used).  Returns (k_codes, v_codes, k_scales, v_scales); the
+    entries of a tensor passed as None are None."""
+    xs = [k, v]
+    modes = [KV_MODES.get(k_mode, k_mode), KV_MODES.get(v_mode, v_mode)]
+    given = [k_scales, v_scales]
+    ref = next((t for t in xs if t is not None), None)
+    if ref is None:
+        raise ValueError("pass K, V or both")
+    if ref.dim() != 4:
+        raise ValueError("K and V must be [layers, tokens, heads, head_dim]")
+    L, T, H, D = ref.shape
+    dev = ref.device
+    codes, scales = [None, None], [None, None]
+    for i, x in enumerate(xs):
+        if x is None:
+            continue
+        x = _dev_tensor(x, "kv"[i])
+        if x.shape != ref.shape or x.dtype != ref.dtype:
+            raise ValueError("K and V must share shape and dtype")
+        xs[i] = x
+        codes[i] = torch.empty(x.shape, dtype=torch.uint8, device=dev)
+        if modes[i] == 2:
+            if given[i] is None:
+                raise ValueError("a static mode needs its scales")
+            scales[i] = _dev_tensor(given[i], "scales", (torch.float32,)).reshape(L)
+        else:
+            scales[i] = torch.empty((L, H) if modes[i] == 1 else (L,), dtype=torch.float32,
+                                    device=dev)
+    need = lib().pqb_kv_workspace_bytes_ex(L, T, H, D)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty((max(need, 4) // 4,), dtype=torch.float32, device=dev)
+    _check(lib().pqb_kv_write_fp8_ex(
+        _ptr(xs[0]), _ptr(xs[1]), BF16 if ref.dtype == torch.bfloat16 else F32, L, T, H, D,
+        modes[0], modes[1], _ptr(codes[0]), _ptr(codes[1]), _ptr(scales[0]), _ptr(scales[1]),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev)),
+        "kv_write_fp8_ex")
+    return codes[0], codes[1], scales[0], scales[1]
 
 
 def encode_e4m3(y: torch.Tensor) -> torch.Tensor:

@@ -177,3 +177,33 @@ def test_quantize_batch_errors_before_launch(L):
     assert L.pqb_quantize_batch(None, 0, None) == 0
     # empty jobs are accepted and launch nothing (no device is touched)
     assert run(job(rows=0), job(batch=0, fmt=3, gran=6, aux=fake)) == 0
+
+
+def test_kv_write_ex_errors_before_launch(L):
+    P = ctypes.c_void_p
+    fake, odd = P(0x10000), P(0x10002)
+    ws = L.pqb_kv_workspace_bytes_ex
+    f = L.pqb_kv_write_fp8_ex
+    big = 1 << 30
+
+    def kv(k=fake, v=fake, dt=1, shape=(2, 16, 8, 128), km=0, vm=0, kc=fake, vc=fake,
+           ks=fake, vs=fake, w=fake, wb=big):
+        return f(k, v, dt, *shape, km, vm, kc, vc, ks, vs, w, wb, None)
+
+    assert ws(2, 16, 8, 128) > 0
+    assert ws(2, 16, 8, 100) == 0                     # head_dim % 8
+    assert kv(dt=5) == -2
+    assert kv(km=3) == -2 and kv(vm=-1) == -2
+    assert kv(shape=(2, 16, 8, 100)) == -4
+    assert kv(shape=(-1, 16, 8, 128)) == -4
+    assert kv(shape=(2, 16, 300, 128), km=1) == -4    # more heads than the per-head limit
+    assert kv(shape=(2, 16, 7, 1000), km=1) == -4     # row width 875: stride multiple too large
+    assert kv(k=None, v=None) == -1
+    assert kv(kc=None) == -1 and kv(vs=None) == -1
+    assert kv(w=None) == -1
+    assert kv(wb=ws(2, 16, 8, 128) - 1) == -6
+    assert kv(k=odd) == -5 and kv(vc=odd) == -5 and kv(w=odd) == -5
+    # static modes need no workspace; empty shapes launch nothing
+    assert kv(shape=(0, 16, 8, 128)) == 0
+    assert kv(shape=(2, 0, 8, 128), km=1, vm=1, w=None, wb=0) == 0
+    assert kv(k=None, kc=None, ks=None, shape=(2, 0, 8, 128)) == 0
