@@ -181,8 +181,7 @@ pqb_status pqb_kv_write_fp8(const void* k, const void* v, pqb_dtype dtype, int64
  * Dynamic scales are max(amax, 1e-12) / 448.  Pass k = NULL (or v = NULL) to
  * write only the other; its codes and scales pointers are then ignored.
  * Shape rules: head_dim % 8 == 0; for PQB_KV_HEAD also heads <= 256 and
- * r / gcd(r, 256) <= 64 for the row width r = heads * head_dim / 8 (e.g. 8 x 128,
- * 32 x 128, 40 x 128, 12 x 64).
+ * heads * (head_dim / 8)^2 < 2^32 (any head_dim up to 32760 with 256 heads).
  * Workspace (only when a dynamic mode is used): pqb_kv_workspace_bytes_ex(),
  * 16-byte aligned.  Alignment: k, v and codes 16 bytes, scales 4 bytes.
  * Errors: PQB_ERR_ENUM for an unknown dtype or mode, PQB_ERR_SHAPE for shapes

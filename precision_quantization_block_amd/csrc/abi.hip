@@ -81,6 +81,13 @@ int64_t fp8_num_scales(int gran, int64_t b, int64_t r, int64_t c) {
   }
 }
 
+// Workspace of the per-tensor FP8 passes over `nt` tensors of `slices` slices.
+size_t tensor_workspace(int nt, int64_t slices, int64_t per_slice) {
+  if (slices <= 0 || per_slice <= 0) return 0;
+  if (per_slice % 8 == 0) return twopass_workspace_bytes(nt, slices, per_slice, 1, false);
+  return 4 * (size_t)nt * (size_t)slices * (size_t)amax_partials_per_slice(slices, per_slice, nt);
+}
+
 pqb_sizes sizes_of(int fmt, int gran, int64_t b, int64_t r, int64_t c) {
   pqb_sizes s{0, 0, 0, 0};
   const int64_t n = b * r * c;
@@ -88,8 +95,7 @@ pqb_sizes sizes_of(int fmt, int gran, int64_t b, int64_t r, int64_t c) {
     case PQB_FP8_E4M3:
       s.codes = (size_t)n;
       s.scales = 4 * (size_t)fp8_num_scales(gran, b, r, c);
-      if (gran == PQB_TENSOR && n > 0)
-        s.workspace = 4 * (size_t)b * (size_t)amax_partials_per_slice(b, r * c, 1);
+      if (gran == PQB_TENSOR && n > 0) s.workspace = tensor_workspace(1, b, r * c);
       break;
     case PQB_MXFP4:
       s.codes = (size_t)n / 2;
@@ -99,7 +105,7 @@ pqb_sizes sizes_of(int fmt, int gran, int64_t b, int64_t r, int64_t c) {
       s.codes = (size_t)n / 2;
       s.scales = (size_t)n / 16;
       s.aux = 4 * (size_t)b;
-      if (n > 0) s.workspace = 4 * (size_t)b * (size_t)amax_partials_per_slice(b, r * c, 1);
+      if (n > 0) s.workspace = twopass_workspace_bytes(1, b, r * c, 1, true);
       break;
     case PQB_INT4_ASYM:
       s.codes = (size_t)n / 2;
@@ -292,7 +298,7 @@ pqb_status pqb_dequantize(const void* codes, const void* scales, const void* aux
 
 size_t pqb_kv_workspace_bytes(int64_t layers, int64_t elems_per_layer) {
   if (layers <= 0 || elems_per_layer <= 0) return 0;
-  return 4 * 2 * (size_t)layers * (size_t)amax_partials_per_slice(layers, elems_per_layer, 2);
+  return tensor_workspace(2, layers, elems_per_layer);
 }
 
 pqb_status pqb_kv_write_fp8(const void* k, const void* v, pqb_dtype dtype, int64_t layers,
@@ -326,24 +332,19 @@ static bool kv_dims_ok(int64_t layers, int64_t tokens, int64_t heads, int64_t he
   return true;
 }
 
+// Per head: the LDS tables hold kMaxKvHeads entries, and the head of a column
+// c < heads * hu (hu = head_dim / 8) is the multiply-high of c by
+// ceil(2^32 / hu), exact while heads * hu * hu < 2^32.
 static bool kv_head_ok(int64_t heads, int64_t head_dim) {
-  return heads <= kMaxKvHeads && kv_stride_multiple(heads * head_dim / 8) <= kMaxKvStrideMultiple;
+  const int64_t hu = head_dim / 8;
+  return heads <= kMaxKvHeads && hu < (int64_t)1 << 16 && heads * hu * hu < (int64_t)1 << 32;
 }
 
 size_t pqb_kv_workspace_bytes_ex(int64_t layers, int64_t tokens, int64_t heads,
                                  int64_t head_dim) {
   if (!kv_dims_ok(layers, tokens, heads, head_dim)) return 0;
   if (layers == 0 || tokens == 0 || heads == 0 || head_dim == 0) return 0;
-  const int64_t per_layer = tokens * heads * head_dim, row_units = heads * head_dim / 8;
-  size_t best = 0;
-  for (int nt = 1; nt <= 2; ++nt)
-    for (int head = 0; head <= (kv_head_ok(heads, head_dim) ? 1 : 0); ++head) {
-      const size_t b = 4 * (size_t)nt * (size_t)layers *
-                       (size_t)kv_partials_per_slice(layers, per_layer, row_units, nt, head) *
-                       (size_t)heads;
-      if (b > best) best = b;
-    }
-  return best;
+  return kv_workspace_bytes(layers, tokens, heads, head_dim);
 }
 
 pqb_status pqb_kv_write_fp8_ex(const void* k, const void* v, pqb_dtype dtype, int64_t layers,
@@ -380,7 +381,7 @@ pqb_status pqb_kv_write_fp8_ex(const void* k, const void* v, pqb_dtype dtype, in
       return PQB_ERR_ALIGN;
   if (dynamic && !aligned(workspace, 16)) return PQB_ERR_ALIGN;
   return hip_status(launch_kv_fp8(t, nt, dtype == PQB_BF16, layers, tokens, heads, head_dim,
-                                  (uint32_t*)workspace, (hipStream_t)stream));
+                                  (float*)workspace, (hipStream_t)stream));
 }
 
 pqb_status pqb_encode_e4m3(const float* y, int64_t n, uint8_t* out, void* stream) {

@@ -136,21 +136,12 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_tensor_quant(TensorArgs a
   uint8_t* cs = a.codes[tz] + b * per_slice;
   const int64_t stride = (int64_t)gridDim.x * kBlockThreads;
   if constexpr (kVec) {
-    const int64_t nunits = per_slice / 8;
-    int64_t u = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
-    for (; u + stride < nunits; u += 2 * stride) {
-      const Raw8 r0 = load_raw8(xs + u * 8), r1 = load_raw8(xs + (u + stride) * 8);
-      float v[8];
-      widen8(r0, xs, v);
-      store_codes8(cs + u * 8, fp8_pack8(v, s, y));
-      widen8(r1, xs, v);
-      store_codes8(cs + (u + stride) * 8, fp8_pack8(v, s, y));
-    }
-    for (; u < nunits; u += stride) {
-      float v[8];
-      widen8(load_raw8(xs + u * 8), xs, v);
-      store_codes8(cs + u * 8, fp8_pack8(v, s, y));
-    }
+    stream_units<T, kStreamLoads>(xs, (int64_t)blockIdx.x * kBlockThreads + threadIdx.x,
+                                  per_slice / 8, stride, [&](const Raw8& r, int64_t u) {
+                                    float v[8];
+                                    widen8(r, xs, v);
+                                    store_codes8(cs + u * 8, fp8_pack8(v, s, y));
+                                  });
   } else {
     for (int64_t i = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x; i < per_slice; i += stride)
       cs[i] = e4m3_byte(div_rn(ld1(xs + i), s, y));
@@ -329,6 +320,9 @@ hipError_t launch_amax_partials(const void* const* x, bool bf16, int ntensors, i
 hipError_t launch_fp8_tensor(const void* const* x, bool bf16, int ntensors, int64_t batch,
                              int64_t per_slice, uint8_t* const* codes, float* const* scales,
                              float* partials, hipStream_t st) {
+  if (per_slice % 8 == 0)
+    return launch_tensor_fp8(x, bf16, ntensors, batch, per_slice, codes, scales, partials, st);
+  // slices whose length is not a multiple of 8: element-wise grid-stride passes
   TensorArgs a{};
   for (int i = 0; i < ntensors; ++i) {
     a.x[i] = x[i];

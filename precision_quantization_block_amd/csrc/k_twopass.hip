@@ -1,0 +1,423 @@
+// Formats whose scale depends on a whole tensor: FP8 per tensor, the FP8 KV
+// write (per layer, per head or static; page "量化部署实战", sections 伪量化实现
+// and KV Cache 量化：误差要和信号比) and NVFP4's tensor scale (same page).
+//
+// Three launches, each streaming one 8 KiB chunk of input per wave (8 bf16 or
+// 4 float32 tiles), the access pattern that sustains the highest bandwidth:
+//   pass 1    every workgroup writes the amax of its share, per group (the
+//             slice, or each head), into group-major partials;
+//   finalize  one workgroup per slice reduces them, writes the output scales
+//             and a small table for pass 2 (s per group; for NVFP4 gs, RN(1/gs)
+//             and s, RN(1/s) of all 127 block-scale codes);
+//   pass 2    quantizes with the finished table.
+// A slice is one batch slice (per-tensor FP8, NVFP4) or one layer of K or V.
+// Per head, a lane follows its unit's column through the chunk: one 64-bit
+// remainder per chunk, then +64 units per tile with one wrap, and the head is
+// a multiply-high by ceil(2^32 / head_units) (exact for the bounded sizes;
+// the column itself when head_units is 1).
+#include "launch.h"
+#include "quant.h"
+
+namespace pqb {
+namespace {
+
+template <typename T>
+constexpr int kChunkUnr = sizeof(T) == 2 ? 8 : 4;
+constexpr int kWgWaves = kBlockThreads / kWave;
+
+struct TpArgs {
+  const void* x[2];
+  uint8_t* codes[2];
+  void* scales[2];  // FP8 / KV: float scales (STATIC: read); NVFP4: u8 block scales
+  float* gs[2];     // NVFP4 tensor scales
+  int32_t mode[2];  // kKvLayer (also per-tensor FP8 and NVFP4), kKvHead, kKvStatic
+};
+
+struct TpGeo {
+  int64_t per_slice;  // elements per slice (multiple of 8)
+  int64_t slices;     // per tensor
+  int32_t W;          // pass-1 workgroups per slice
+  int32_t G;          // group stride of partials and of the FP8 final table (1 or heads)
+  int32_t row_units;  // per head: units per token row (heads * head_dim / 8)
+  uint32_t head_magic;  // per head: ceil(2^32 / (head_dim / 8))
+};
+
+// NVFP4 final table per slice: [0] gs, [1] RN(1/gs), [2 + c] s of block-scale
+// code c, [2 + 128 + c] RN(1/s), c < 127; 258 floats, padded to 264.
+constexpr int kNvSe = 2, kNvYe = 2 + 128, kNvFinal = 264;
+
+__device__ __forceinline__ int groups_of(const TpArgs& a, const TpGeo& g, int tz) {
+  return a.mode[tz] == kKvHead ? g.G : 1;
+}
+
+// Column (unit index within a token row) of this lane's first unit of a chunk,
+// and the per-tile step, for the per-head scope.
+struct ColWalk {
+  uint32_t c, step, R, magic;
+  __device__ __forceinline__ ColWalk(int64_t u0, const TpGeo& g)
+      : c((uint32_t)((u0 + (threadIdx.x & (kWave - 1))) % g.row_units)),
+        step((uint32_t)(kWave % g.row_units)),
+        R((uint32_t)g.row_units),
+        magic(g.head_magic) {}
+  // magic == 0 stands for head_units == 1 (ceil(2^32 / 1) does not fit 32 bits)
+  __device__ __forceinline__ int head() const { return (int)(magic ? __umulhi(c, magic) : c); }
+  __device__ __forceinline__ void next() {
+    c += step;
+    if (c >= R) c -= R;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// pass 1
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kBlockThreads) void k_tp_amax(TpArgs a, TpGeo g,
+                                                           float* __restrict__ partials) {
+  constexpr int U = kChunkUnr<T>;
+  __shared__ uint32_t red[kMaxKvHeads > kWgWaves ? kMaxKvHeads : kWgWaves];
+  const int tz = blockIdx.z;
+  if (a.mode[tz] == kKvStatic) return;  // uniform over the workgroup
+  const int64_t b = blockIdx.y;
+  const int G = groups_of(a, g, tz);
+  const T* xs = reinterpret_cast<const T*>(a.x[tz]) + b * g.per_slice;
+  const int64_t nunits = g.per_slice / 8;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  const int64_t u0 = ((int64_t)blockIdx.x * kWgWaves + wave) * U * kWave;
+  float* out = partials + ((int64_t)tz * g.slices + b) * g.G * g.W + blockIdx.x;
+  Raw8 raw[U];
+  const bool any = u0 < nunits;
+  if (any) {
+    if (u0 + U * kWave <= nunits)
+      load_chunk<T, U, false>(xs, u0, nunits, raw);
+    else
+      load_chunk<T, U, true>(xs, u0, nunits, raw);  // missing units read as zeros
+  }
+  if (G == 1) {
+    uint32_t m = 0;
+    if (any) {
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        float v[8];
+        widen8(raw[k], xs, v);
+        m = max(m, as_u(absmax8(v)));
+      }
+    }
+    m = wave_umax(m);
+    if ((threadIdx.x & (kWave - 1)) == 0) red[wave] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t r = red[0];
+      for (int i = 1; i < kWgWaves; ++i) r = max(r, red[i]);
+      out[0] = as_f(r);
+    }
+    return;
+  }
+  for (int i = threadIdx.x; i < G; i += kBlockThreads) red[i] = 0;
+  __syncthreads();
+  if (any) {
+    ColWalk col(u0, g);
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      float v[8];
+      widen8(raw[k], xs, v);
+      atomicMax(&red[col.head()], as_u(absmax8(v)));  // zeros for missing units
+      col.next();
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < G; i += kBlockThreads) out[(int64_t)i * g.W] = as_f(red[i]);
+}
+
+// ---------------------------------------------------------------------------
+// finalize: grid (slices, tensors)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t reduce_row(const float* __restrict__ p, int W, uint32_t* red) {
+  uint32_t m = 0;
+  int i = threadIdx.x;
+  for (; i + 3 * kBlockThreads < W; i += 4 * kBlockThreads)
+    m = max(max(max(m, as_u(p[i])), as_u(p[i + kBlockThreads])),
+            max(as_u(p[i + 2 * kBlockThreads]), as_u(p[i + 3 * kBlockThreads])));
+  for (; i < W; i += kBlockThreads) m = max(m, as_u(p[i]));
+  m = wave_umax(m);
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = m;
+  __syncthreads();
+  m = red[0];
+  for (int w = 1; w < kWgWaves; ++w) m = max(m, red[w]);
+  __syncthreads();
+  return m;
+}
+
+__global__ __launch_bounds__(kBlockThreads) void k_tp_finalize_fp8(TpArgs a, TpGeo g,
+                                                                   const float* __restrict__ partials,
+                                                                   float* __restrict__ fin) {
+  __shared__ uint32_t red[kWgWaves];
+  const int tz = blockIdx.y;
+  if (a.mode[tz] == kKvStatic) return;
+  const int64_t b = blockIdx.x, slot = (int64_t)tz * g.slices + b;
+  const int G = groups_of(a, g, tz);
+  float* sc = reinterpret_cast<float*>(a.scales[tz]);
+  for (int grp = 0; grp < G; ++grp) {
+    const float s = fp8_scale_bits(reduce_row(partials + (slot * g.G + grp) * g.W, g.W, red));
+    if (threadIdx.x == 0) {
+      fin[slot * g.G + grp] = s;
+      sc[b * G + grp] = s;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kBlockThreads) void k_tp_finalize_nv(TpArgs a, TpGeo g,
+                                                                  const float* __restrict__ partials,
+                                                                  float* __restrict__ fin) {
+  __shared__ uint32_t red[kWgWaves];
+  const int64_t b = blockIdx.x;
+  const uint32_t m = reduce_row(partials + b * g.W, g.W, red);
+  const float gs = as_f(max(m, kAmaxFloorBits)) / 2688.0f;  // 448 * 6, IEEE division
+  float* f = fin + b * kNvFinal;
+  if (threadIdx.x == 0) {
+    f[0] = gs;
+    f[1] = recip_rn(gs);
+    a.gs[0][b] = gs;
+  }
+  // element scale of every finite block-scale code: max(dec(code), 1e-12) * gs
+  for (int c = threadIdx.x; c < 127; c += kBlockThreads) {
+    const float sc = fmaxf(e4m3_decode((uint32_t)c), 1e-12f) * gs;
+    f[kNvSe + c] = sc;
+    f[kNvYe + c] = 1.0f / sc;  // IEEE division
+  }
+}
+
+// ---------------------------------------------------------------------------
+// pass 2
+// ---------------------------------------------------------------------------
+// Eight codes with the static-scale clamp: |x| is first limited to 512 s (so
+// x * RN(1/s) cannot overflow; any |x/s| >= 512 saturates anyway), then the
+// correctly rounded quotient is clamped to +-448.
+__device__ __forceinline__ uint2 fp8_pack8_clamped(const float v[8], float s, float y, float lim) {
+  float q[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    q[i] = __builtin_amdgcn_fmed3f(div_rn(__builtin_amdgcn_fmed3f(v[i], -lim, lim), s, y), -448.0f,
+                                   448.0f);
+  return make_uint2(e4m3_bytes4(q[0], q[1], q[2], q[3]), e4m3_bytes4(q[4], q[5], q[6], q[7]));
+}
+
+template <typename T, int kMode, bool kGuard>
+__device__ __forceinline__ void fp8_tp_chunk(const T* __restrict__ xs, int64_t u0, int64_t nunits,
+                                             uint8_t* __restrict__ cs, float s, float y,
+                                             const float* ss, const float* ys, const TpGeo& g) {
+  constexpr int U = kChunkUnr<T>;
+  const int lane = threadIdx.x & (kWave - 1);
+  Raw8 raw[U];
+  load_chunk<T, U, kGuard>(xs, u0, nunits, raw);
+  [[maybe_unused]] ColWalk col(kMode == kKvHead ? u0 : 0, g);
+  const float lim = s * 512.0f;
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    float v[8];
+    widen8(raw[k], xs, v);
+    uint2 w;
+    if constexpr (kMode == kKvHead) {
+      const int h = col.head();
+      w = fp8_pack8(v, ss[h], ys[h]);
+      col.next();
+    } else if constexpr (kMode == kKvStatic) {
+      w = fp8_pack8_clamped(v, s, y, lim);
+    } else {
+      w = fp8_pack8(v, s, y);
+    }
+    const int64_t u = u0 + k * kWave + lane;
+    if (!kGuard || u < nunits) store_codes8(cs + u * 8, w);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kBlockThreads) void k_tp_fp8(TpArgs a, TpGeo g,
+                                                          const float* __restrict__ fin) {
+  constexpr int U = kChunkUnr<T>;
+  __shared__ float ss[kMaxKvHeads], ys[kMaxKvHeads];
+  const int tz = blockIdx.z, mode = a.mode[tz];
+  const int64_t b = blockIdx.y, slot = (int64_t)tz * g.slices + b;
+  float s = 0.0f, y = 0.0f;
+  if (mode == kKvHead) {
+    for (int i = threadIdx.x; i < g.G; i += kBlockThreads) {
+      const float si = fin[slot * g.G + i];
+      ss[i] = si;
+      ys[i] = recip_rn(si);
+    }
+    __syncthreads();
+  } else {
+    s = mode == kKvStatic ? reinterpret_cast<const float*>(a.scales[tz])[b] : fin[slot * g.G];
+    y = recip_rn(s);
+  }
+  const T* xs = reinterpret_cast<const T*>(a.x[tz]) + b * g.per_slice;
+  uint8_t* cs = a.codes[tz] + b * g.per_slice;
+  const int64_t nunits = g.per_slice / 8;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  const int64_t u0 = ((int64_t)blockIdx.x * kWgWaves + wave) * U * kWave;
+  if (u0 >= nunits) return;
+  const bool full = u0 + U * kWave <= nunits;
+  switch (mode) {
+    case kKvHead:
+      if (full) fp8_tp_chunk<T, kKvHead, false>(xs, u0, nunits, cs, s, y, ss, ys, g);
+      else fp8_tp_chunk<T, kKvHead, true>(xs, u0, nunits, cs, s, y, ss, ys, g);
+      break;
+    case kKvStatic:
+      if (full) fp8_tp_chunk<T, kKvStatic, false>(xs, u0, nunits, cs, s, y, ss, ys, g);
+      else fp8_tp_chunk<T, kKvStatic, true>(xs, u0, nunits, cs, s, y, ss, ys, g);
+      break;
+    default:
+      if (full) fp8_tp_chunk<T, kKvLayer, false>(xs, u0, nunits, cs, s, y, ss, ys, g);
+      else fp8_tp_chunk<T, kKvLayer, true>(xs, u0, nunits, cs, s, y, ss, ys, g);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kBlockThreads) void k_tp_nv(TpArgs a, TpGeo g,
+                                                         const float* __restrict__ fin) {
+  constexpr int U = kChunkUnr<T>;
+  __shared__ NvTables tb;
+  const int64_t b = blockIdx.y;
+  const float* f = fin + b * kNvFinal;
+  e2m1_lut_fill(tb.lut, 8);
+  for (int c = threadIdx.x; c < 127; c += kBlockThreads) {
+    tb.se[c] = f[kNvSe + c];
+    tb.ye[c] = f[kNvYe + c];
+  }
+  const float gs = f[0], ygs = f[1];
+  __syncthreads();
+  const T* xs = reinterpret_cast<const T*>(a.x[0]) + b * g.per_slice;
+  uint8_t* cs = a.codes[0] + b * (g.per_slice / 2);
+  uint8_t* bs = reinterpret_cast<uint8_t*>(a.scales[0]) + b * (g.per_slice / 16);
+  const int64_t nunits = g.per_slice / 8;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  const int64_t u0 = ((int64_t)blockIdx.x * kWgWaves + wave) * U * kWave;
+  if (u0 >= nunits) return;
+  if (u0 + U * kWave <= nunits)
+    nv_chunk<T, U, false>(xs, u0, nunits, cs, bs, gs, ygs, tb);
+  else
+    nv_chunk<T, U, true>(xs, u0, nunits, cs, bs, gs, ygs, tb);
+}
+
+int64_t wgs_per_slice(int64_t per_slice, bool bf16) {
+  const int64_t units_per_wg = (int64_t)(bf16 ? 8 : 4) * kWave * kWgWaves;
+  const int64_t w = (per_slice / 8 + units_per_wg - 1) / units_per_wg;
+  return w < 1 ? 1 : w;
+}
+
+// ceil(2^32 / head_units) for head_units >= 2; 0 (identity) for head_units == 1.
+uint32_t head_magic(int64_t head_units) {
+  return head_units == 1 ? 0u : (uint32_t)((0xFFFFFFFFull / (uint64_t)head_units) + 1);
+}
+
+hipError_t launch_tp(const TpArgs& a, int nt, bool bf16, const TpGeo& g, bool nv, float* ws,
+                     hipStream_t st) {
+  float* partials = ws;
+  float* fin = ws + (int64_t)nt * g.slices * g.G * g.W;
+  bool dynamic = false;
+  for (int i = 0; i < nt; ++i) dynamic |= a.mode[i] != kKvStatic;
+  const dim3 grid((unsigned)g.W, (unsigned)g.slices, (unsigned)nt);
+  if (dynamic) {
+    if (bf16)
+      hipLaunchKernelGGL(k_tp_amax<uint16_t>, grid, dim3(kBlockThreads), 0, st, a, g, partials);
+    else
+      hipLaunchKernelGGL(k_tp_amax<float>, grid, dim3(kBlockThreads), 0, st, a, g, partials);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (nv)
+      hipLaunchKernelGGL(k_tp_finalize_nv, dim3((unsigned)g.slices, 1), dim3(kBlockThreads), 0,
+                         st, a, g, partials, fin);
+    else
+      hipLaunchKernelGGL(k_tp_finalize_fp8, dim3((unsigned)g.slices, (unsigned)nt),
+                         dim3(kBlockThreads), 0, st, a, g, partials, fin);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (nv) {
+    if (bf16)
+      hipLaunchKernelGGL(k_tp_nv<uint16_t>, grid, dim3(kBlockThreads), 0, st, a, g, fin);
+    else
+      hipLaunchKernelGGL(k_tp_nv<float>, grid, dim3(kBlockThreads), 0, st, a, g, fin);
+  } else {
+    if (bf16)
+      hipLaunchKernelGGL(k_tp_fp8<uint16_t>, grid, dim3(kBlockThreads), 0, st, a, g, fin);
+    else
+      hipLaunchKernelGGL(k_tp_fp8<float>, grid, dim3(kBlockThreads), 0, st, a, g, fin);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t twopass_workspace_bytes(int ntensors, int64_t slices, int64_t per_slice, int64_t groups,
+                               bool nv) {
+  if (slices <= 0 || per_slice <= 0) return 0;
+  const int64_t W = wgs_per_slice(per_slice, false);  // float32 needs the most workgroups
+  const int64_t fin = nv ? kNvFinal : groups;
+  return 4 * (size_t)ntensors * (size_t)slices * ((size_t)groups * (size_t)W + (size_t)fin);
+}
+
+hipError_t launch_tensor_fp8(const void* const* x, bool bf16, int ntensors, int64_t slices,
+                             int64_t per_slice, uint8_t* const* codes, float* const* scales,
+                             float* ws, hipStream_t st) {
+  TpArgs a{};
+  for (int i = 0; i < ntensors; ++i) {
+    a.x[i] = x[i];
+    a.codes[i] = codes[i];
+    a.scales[i] = scales[i];
+    a.mode[i] = kKvLayer;
+  }
+  TpGeo g{};
+  g.per_slice = per_slice;
+  g.slices = slices;
+  g.W = (int32_t)wgs_per_slice(per_slice, bf16);
+  g.G = 1;
+  g.row_units = 1;
+  g.head_magic = 0;
+  return launch_tp(a, ntensors, bf16, g, false, ws, st);
+}
+
+hipError_t launch_nvfp4(const void* x, bool bf16, int64_t batch, int64_t per_slice,
+                        uint8_t* codes, uint8_t* scales, float* gs, float* ws, hipStream_t st) {
+  TpArgs a{};
+  a.x[0] = x;
+  a.codes[0] = codes;
+  a.scales[0] = scales;
+  a.gs[0] = gs;
+  a.mode[0] = kKvLayer;
+  TpGeo g{};
+  g.per_slice = per_slice;
+  g.slices = batch;
+  g.W = (int32_t)wgs_per_slice(per_slice, bf16);
+  g.G = 1;
+  g.row_units = 1;
+  return launch_tp(a, 1, bf16, g, true, ws, st);
+}
+
+hipError_t launch_kv_fp8(const KvTensor* t, int ntensors, bool bf16, int64_t layers,
+                         int64_t tokens, int64_t heads, int64_t head_dim, float* ws,
+                         hipStream_t st) {
+  TpArgs a{};
+  bool head = false;
+  for (int i = 0; i < ntensors; ++i) {
+    a.x[i] = t[i].x;
+    a.codes[i] = t[i].codes;
+    a.scales[i] = t[i].scales;
+    a.mode[i] = t[i].mode;
+    head |= t[i].mode == kKvHead;
+  }
+  TpGeo g{};
+  g.per_slice = tokens * heads * head_dim;
+  g.slices = layers;
+  g.W = (int32_t)wgs_per_slice(g.per_slice, bf16);
+  g.G = head ? (int32_t)heads : 1;
+  g.row_units = (int32_t)(heads * head_dim / 8);
+  g.head_magic = head_magic(head_dim / 8);
+  return launch_tp(a, ntensors, bf16, g, false, ws, st);
+}
+
+size_t kv_workspace_bytes(int64_t layers, int64_t tokens, int64_t heads, int64_t head_dim) {
+  // two tensors, per-head groups (the largest any mode combination needs)
+  return twopass_workspace_bytes(2, layers, tokens * heads * head_dim, heads, false);
+}
+
+}  // namespace pqb

@@ -38,8 +38,7 @@ hipError_t launch_mxfp4(const void* x, bool bf16, int64_t n, uint8_t* codes, uin
 hipError_t launch_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, int64_t n,
                                 bool out_bf16, void* out, hipStream_t st);
 hipError_t launch_nvfp4(const void* x, bool bf16, int64_t batch, int64_t per_slice,
-                        uint8_t* codes, uint8_t* scales, float* gs, float* partials,
-                        hipStream_t st);
+                        uint8_t* codes, uint8_t* scales, float* gs, float* ws, hipStream_t st);
 hipError_t launch_nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const float* gs,
                                 int64_t batch, int64_t per_slice, bool out_bf16, void* out,
                                 hipStream_t st);
@@ -65,9 +64,17 @@ struct MultiJob {
 };
 hipError_t launch_multi(const MultiJob* jobs, int njobs, hipStream_t st);
 
-// ---- FP8 KV-cache write with a scale mode per tensor ------------------------
-// x is [layers, tokens, heads, head_dim]; scales [layers] (LAYER, STATIC: read)
-// or [layers, heads] (HEAD).  Partials: uint32 amax bits, [tensor][layer][P][heads].
+// ---- two-pass formats (k_twopass.hip) -------------------------------------
+// Chunked pass 1 -> finalize -> pass 2 for slices whose length is a multiple
+// of 8.  Workspace: twopass_workspace_bytes(); contents on entry do not matter.
+size_t twopass_workspace_bytes(int ntensors, int64_t slices, int64_t per_slice, int64_t groups,
+                               bool nv);
+hipError_t launch_tensor_fp8(const void* const* x, bool bf16, int ntensors, int64_t slices,
+                             int64_t per_slice, uint8_t* const* codes, float* const* scales,
+                             float* ws, hipStream_t st);
+
+// FP8 KV-cache write with a scale mode per tensor: x is [layers, tokens, heads,
+// head_dim]; scales [layers] (LAYER; STATIC: read) or [layers, heads] (HEAD).
 enum KvMode { kKvLayer = 0, kKvHead = 1, kKvStatic = 2 };
 constexpr int kMaxKvHeads = 256;
 struct KvTensor {
@@ -76,14 +83,9 @@ struct KvTensor {
   float* scales;
   int mode;
 };
-// Grid strides of the per-head passes are multiples of row_units; they are
-// rounded to kv_stride_multiple(row_units) workgroups (at most kMaxKvStrideMultiple).
-constexpr int64_t kMaxKvStrideMultiple = 64;
-int64_t kv_stride_multiple(int64_t row_units);
-int kv_partials_per_slice(int64_t layers, int64_t per_layer, int64_t row_units, int ntensors,
-                          bool head);
+size_t kv_workspace_bytes(int64_t layers, int64_t tokens, int64_t heads, int64_t head_dim);
 hipError_t launch_kv_fp8(const KvTensor* t, int ntensors, bool bf16, int64_t layers,
-                         int64_t tokens, int64_t heads, int64_t head_dim, uint32_t* partials,
+                         int64_t tokens, int64_t heads, int64_t head_dim, float* ws,
                          hipStream_t st);
 
 // ---- element codecs ---------------------------------------------------------

@@ -64,6 +64,22 @@ __device__ __forceinline__ void load_chunk(const T* __restrict__ x, int64_t u0, 
                                                            : Raw8{};
 }
 
+// Grid-stride walk over units u, u + stride, ... < nunits with kLoads loads in
+// flight per thread: body(raw, unit) runs once per unit, in order.
+constexpr int kStreamLoads = 2;
+template <typename T, int kLoads, typename Body>
+__device__ __forceinline__ void stream_units(const T* __restrict__ xs, int64_t u, int64_t nunits,
+                                             int64_t stride, Body body) {
+  for (; u + (kLoads - 1) * stride < nunits; u += kLoads * stride) {
+    Raw8 r[kLoads];
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) r[k] = load_raw8(xs + (u + k * stride) * 8);
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) body(r[k], u + k * stride);
+  }
+  for (; u < nunits; u += stride) body(load_raw8(xs + u * 8), u);
+}
+
 // 1x128 blocks: a block is 16 lanes x 8 elements, one DPP row.
 template <typename T, int kUnr, bool kGuard>
 __device__ __forceinline__ void fp8_1x128_chunk(const T* __restrict__ x, int64_t u0, int64_t nunits,
@@ -212,6 +228,58 @@ __device__ __forceinline__ void mx_chunk(const T* __restrict__ x, int64_t u0, in
     if (!kGuard || u < nunits) {
       st_nt4(codes + u * 4, w);
       if ((lane & 3) == 0) scales[u >> 2] = (uint8_t)(ef - 2u);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4 (page "量化部署实战", section 伪量化实现), pass 2: 2 lanes x 8 elements
+// per 16-element block.  The block scale code is E4M3((amax_b / 6) / gs); the
+// element scale of every finite code, s = max(dec(code), 1e-12) * gs, and
+// RN(1/s) come from a table in LDS, as does the E2M1 rule.
+// ---------------------------------------------------------------------------
+struct __align__(16) NvTables {
+  uint8_t lut[kE2M1LutSize];
+  float se[128], ye[128];
+};
+
+template <typename T, int kUnr, bool kGuard>
+__device__ __forceinline__ void nv_chunk(const T* __restrict__ xs, int64_t u0, int64_t nunits,
+                                         uint8_t* __restrict__ cs, uint8_t* __restrict__ ss,
+                                         float gs, float ygs, const NvTables& tb) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const T* xb = xs + u0 * 8;
+  Raw8 raw[kUnr];
+#pragma unroll
+  for (int k = 0; k < kUnr; ++k)
+    raw[k] = (!kGuard || u0 + k * kWave + lane < nunits) ? load_raw8(xb + (k * kWave + lane) * 8)
+                                                           : Raw8{};
+#pragma unroll
+  for (int k = 0; k < kUnr; ++k) {
+    float v[8];
+    widen8(raw[k], xs, v);
+    const float ab = as_f(group_umax<2>(as_u(absmax8(v))));
+    const float bq = div_rn(div_const(ab, 6.0f, kInv6), gs, ygs);  // <= 448 (1 + 2^-22)
+    const uint32_t bs = cvt_e4m3x2<false>(bq, 0.0f, 0u) & 0x7Fu;     // bq >= 0
+    const float s = tb.se[bs], ys = tb.ye[bs];
+    uint32_t w = 0;
+    if (s < 2.0f && s >= 0x1p-60f) {
+      // Here every nonzero x has a nonzero RN(x / s) (|x / s| > 2^-150), so its
+      // nibble carries the sign of x even when the magnitude is 0: with -0.0
+      // mapped to +0 first, a quotient of -0 stands for "negative, rounds to
+      // zero" and the table's key 1024 holds nibble 8.
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        w |= (uint32_t)tb.lut[e2m1_key(div_rn(v[i] + 0.0f, s, ys))] << (4 * i);
+    } else {
+      // IEEE division; a -0 quotient has sign(y) = 0, so it becomes +0 first.
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w |= (uint32_t)tb.lut[e2m1_key(v[i] / s + 0.0f)] << (4 * i);
+    }
+    const int64_t u = u0 + k * kWave + lane;
+    if (!kGuard || u < nunits) {
+      st_nt4(cs + u * 4, w);
+      if ((lane & 1) == 0) ss[u >> 1] = (uint8_t)bs;
     }
   }
 }

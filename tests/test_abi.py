@@ -197,7 +197,7 @@ def test_kv_write_ex_errors_before_launch(L):
     assert kv(shape=(2, 16, 8, 100)) == -4
     assert kv(shape=(-1, 16, 8, 128)) == -4
     assert kv(shape=(2, 16, 300, 128), km=1) == -4    # more heads than the per-head limit
-    assert kv(shape=(2, 16, 7, 1000), km=1) == -4     # row width 875: stride multiple too large
+    assert kv(shape=(2, 16, 256, 8 * 4096), km=1) == -4  # heads * (head_dim/8)^2 = 2^32
     assert kv(k=None, v=None) == -1
     assert kv(kc=None) == -1 and kv(vs=None) == -1
     assert kv(w=None) == -1
@@ -207,3 +207,28 @@ def test_kv_write_ex_errors_before_launch(L):
     assert kv(shape=(0, 16, 8, 128)) == 0
     assert kv(shape=(2, 0, 8, 128), km=1, vm=1, w=None, wb=0) == 0
     assert kv(k=None, kc=None, ks=None, shape=(2, 0, 8, 128)) == 0
+
+
+def test_head_index_by_multiply_high_is_exact():
+    """Per-head kernels find the head of a column c < heads * hu (hu = head_dim
+    / 8 units) as the high 32 bits of c * ceil(2^32 / hu).  The ABI admits
+    heads * hu^2 < 2^32; check every column at the edges of that rule."""
+    import numpy as np
+
+    def heads_of(c, hu):
+        # the kernel's arithmetic: a 32-bit multiplier, 0 meaning "the column itself"
+        magic = 0 if hu == 1 else ((0xFFFFFFFF // hu) + 1)
+        assert magic < 1 << 32
+        if magic == 0:
+            return c.copy()
+        return (c.astype(np.uint64) * np.uint64(magic)) >> np.uint64(32)
+
+    for heads, hu in ((256, 4095), (256, 1), (1, 65535), (255, 4103), (3, 37837), (8, 16),
+                      (40, 16), (12, 8)):
+        assert heads * hu * hu < 1 << 32
+        c = np.arange(heads * hu, dtype=np.uint64)
+        assert np.array_equal(heads_of(c, hu), c // np.uint64(hu)), (heads, hu)
+    # just past the rule the shortcut does fail somewhere, so the bound is needed
+    heads, hu = 65536, 65535
+    c = np.arange(heads * hu - 100000, heads * hu, dtype=np.uint64)
+    assert not np.array_equal(heads_of(c, hu), c // np.uint64(hu))
