@@ -29,6 +29,10 @@ __device__ __forceinline__ uint4 ld_nt16(const void* p) {
   u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+__device__ __forceinline__ uint2 ld_nt8(const void* p) {
+  u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_uint2(v[0], v[1]);
+}
 __device__ __forceinline__ void st_nt4(void* p, uint32_t w) {
   __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(p));
 }

@@ -1,0 +1,232 @@
+// Dequantization of the flat formats (page "量化部署实战", section 伪量化实现:
+// the fake-quant functions return decoded code times scale, as float32).
+//
+// Lane l of a wave expands unit u = u0 + 64 k + l (8 elements) of each of the
+// kDqTiles wave-wide tiles of its chunk: the wave's code loads (4 bytes of
+// nibbles or 8 FP8 bytes per lane) and its 16-byte output stores (bf16; two
+// for float32) each cover one contiguous range, so every store instruction
+// writes whole 1 KiB (2 KiB) spans.  All loads of the chunk are issued before
+// the first store.  Outputs are float32 or RNE bf16.
+#include "launch.h"
+#include "quant.h"
+
+namespace pqb {
+namespace {
+
+constexpr int kDqTiles = 4;
+constexpr int kDqWaves = kBlockThreads / kWave;
+
+// Unit of this lane in tile 0 of its wave's chunk.
+__device__ __forceinline__ int64_t dq_unit0() {
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  return ((int64_t)blockIdx.x * kDqWaves + wave) * kDqTiles * kWave + (threadIdx.x & (kWave - 1));
+}
+
+int dq_grid(int64_t nunits) {
+  const int64_t per_wg = (int64_t)kDqTiles * kWave * kDqWaves;
+  const int64_t g = (nunits + per_wg - 1) / per_wg;
+  return (int)(g < 1 ? 1 : g);
+}
+
+// FP8 1x128: unit u's scale is u / 16.
+template <bool kBf16Out>
+__global__ __launch_bounds__(kBlockThreads) void k_dq_fp8_1x128(const uint8_t* __restrict__ codes,
+                                                                const float* __restrict__ scales,
+                                                                int64_t nunits,
+                                                                void* __restrict__ out) {
+  const int64_t u0 = dq_unit0();
+  uint2 c[kDqTiles];
+  float s[kDqTiles];
+#pragma unroll
+  for (int k = 0; k < kDqTiles; ++k) {
+    const int64_t u = u0 + k * kWave;
+    if (u < nunits) {
+      c[k] = ld_nt8(codes + u * 8);
+      s[k] = scales[u >> 4];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kDqTiles; ++k) {
+    const int64_t u = u0 + k * kWave;
+    if (u < nunits) {
+      float o[8];
+      fp8_decode8(c[k], s[k], o);
+      store_out8<kBf16Out>(out, u, o);
+    }
+  }
+}
+
+// MXFP4 with the gfx950 scaled FP4 conversion, two nibbles per instruction
+// (byte j of w gives elements 2j and 2j + 1, low nibble first).  With a scale
+// 2^k it returns +-V * 2^k exactly, signed zeros included, in float32 or bf16:
+// a GPU check over every code byte, byte position and E8M0 scale found it
+// equal, bit for bit, to the decoded value times the scale.  (It uses only the
+// scale's exponent, so NVFP4's arbitrary scales cannot go through it.)
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+template <bool kBf16Out>
+__device__ __forceinline__ void mx_expand8(uint32_t w, float s, void* out, int64_t u) {
+  if constexpr (kBf16Out) {
+    const uint32_t p0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0));
+    const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1));
+    const uint32_t p2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2));
+    const uint32_t p3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3));
+    st_nt16(reinterpret_cast<uint16_t*>(out) + 8 * u, p0, p1, p2, p3);
+  } else {
+    const f32x2v a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, 0);
+    const f32x2v b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, 1);
+    const f32x2v c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, 2);
+    const f32x2v d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, 3);
+    float* p = reinterpret_cast<float*>(out) + 8 * u;
+    st_nt16(p, as_u(a[0]), as_u(a[1]), as_u(b[0]), as_u(b[1]));
+    st_nt16(p + 4, as_u(c[0]), as_u(c[1]), as_u(d[0]), as_u(d[1]));
+  }
+}
+
+// MXFP4: unit u is a quarter of block u / 4; +-V * 2^(e - 127) is exact.
+template <bool kBf16Out>
+__global__ __launch_bounds__(kBlockThreads) void k_dq_mxfp4(const uint8_t* __restrict__ codes,
+                                                            const uint8_t* __restrict__ scales,
+                                                            int64_t nunits,
+                                                            void* __restrict__ out) {
+  const int64_t u0 = dq_unit0();
+  uint32_t c[kDqTiles], e[kDqTiles];
+#pragma unroll
+  for (int k = 0; k < kDqTiles; ++k) {
+    const int64_t u = u0 + k * kWave;
+    if (u < nunits) {
+      c[k] = reinterpret_cast<const uint32_t*>(codes)[u];
+      e[k] = scales[u >> 2];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kDqTiles; ++k) {
+    const int64_t u = u0 + k * kWave;
+    if (u < nunits) {
+      mx_expand8<kBf16Out>(c[k], as_f(e[k] << 23), out, u);  // 2^(e - 127), e in [85, 252]
+    }
+  }
+}
+
+// NVFP4, slice b = blockIdx.y: unit u is half of block u / 2; element scale
+// max(dec(block scale), 1e-12) * gs.
+template <bool kBf16Out>
+__global__ __launch_bounds__(kBlockThreads) void k_dq_nvfp4(const uint8_t* __restrict__ codes,
+                                                            const uint8_t* __restrict__ scales,
+                                                            const float* __restrict__ gs,
+                                                            int64_t per_slice,
+                                                            void* __restrict__ out) {
+  const int64_t b = blockIdx.y, nunits = per_slice / 8, base = b * nunits;
+  const float g = gs[b];
+  const int64_t u0 = dq_unit0();
+  uint32_t c[kDqTiles], bs[kDqTiles];
+#pragma unroll
+  for (int k = 0; k < kDqTiles; ++k) {
+    const int64_t u = u0 + k * kWave;
+    if (u < nunits) {
+      c[k] = reinterpret_cast<const uint32_t*>(codes)[base + u];
+      bs[k] = scales[(base + u) >> 1];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kDqTiles; ++k) {
+    const int64_t u = u0 + k * kWave;
+    if (u < nunits) {
+      const float s = fmaxf(e4m3_decode(bs[k]), 1e-12f) * g;
+      float o[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = e2m1_value(c[k] >> (4 * i)) * s;
+      store_out8<kBf16Out>(out, base + u, o);
+    }
+  }
+}
+
+// INT4: unit u lies in group u / 16; (q - z) * s is exact in float32
+// (|q - z| <= 15 and s has 8 significant bits).
+template <bool kBf16Out>
+__global__ __launch_bounds__(kBlockThreads) void k_dq_int4(const uint8_t* __restrict__ codes,
+                                                           const uint16_t* __restrict__ scales,
+                                                           const uint8_t* __restrict__ zeros,
+                                                           int64_t nunits,
+                                                           void* __restrict__ out) {
+  const int64_t u0 = dq_unit0();
+  uint32_t c[kDqTiles], sb[kDqTiles], zb[kDqTiles];
+#pragma unroll
+  for (int k = 0; k < kDqTiles; ++k) {
+    const int64_t u = u0 + k * kWave;
+    if (u < nunits) {
+      c[k] = reinterpret_cast<const uint32_t*>(codes)[u];
+      sb[k] = scales[u >> 4];
+      zb[k] = zeros[u >> 5];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kDqTiles; ++k) {
+    const int64_t u = u0 + k * kWave;
+    if (u < nunits) {
+      const float s = as_f(sb[k] << 16);
+      const int z = ((int)(zb[k] >> (4 * ((u >> 4) & 1))) << 28) >> 28;  // sign-extend
+      float o[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int q = ((int)(c[k] >> (4 * i)) << 28) >> 28;
+        o[i] = (float)(q - z) * s;
+      }
+      store_out8<kBf16Out>(out, u, o);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fp8_1x128_dequant(const uint8_t* codes, const float* scales, int64_t n,
+                                    bool out_bf16, void* out, hipStream_t st) {
+  const int64_t nl = n / 8;
+  if (out_bf16)
+    hipLaunchKernelGGL(k_dq_fp8_1x128<true>, dim3(dq_grid(nl)), dim3(kBlockThreads), 0, st, codes,
+                       scales, nl, out);
+  else
+    hipLaunchKernelGGL(k_dq_fp8_1x128<false>, dim3(dq_grid(nl)), dim3(kBlockThreads), 0, st,
+                       codes, scales, nl, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, int64_t n,
+                                bool out_bf16, void* out, hipStream_t st) {
+  const int64_t nl = n / 8;
+  if (out_bf16)
+    hipLaunchKernelGGL(k_dq_mxfp4<true>, dim3(dq_grid(nl)), dim3(kBlockThreads), 0, st, codes,
+                       scales, nl, out);
+  else
+    hipLaunchKernelGGL(k_dq_mxfp4<false>, dim3(dq_grid(nl)), dim3(kBlockThreads), 0, st, codes,
+                       scales, nl, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const float* gs,
+                                int64_t batch, int64_t per_slice, bool out_bf16, void* out,
+                                hipStream_t st) {
+  const dim3 grid(dq_grid(per_slice / 8), (unsigned)batch);
+  if (out_bf16)
+    hipLaunchKernelGGL(k_dq_nvfp4<true>, grid, dim3(kBlockThreads), 0, st, codes, scales, gs,
+                       per_slice, out);
+  else
+    hipLaunchKernelGGL(k_dq_nvfp4<false>, grid, dim3(kBlockThreads), 0, st, codes, scales, gs,
+                       per_slice, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_int4_dequant(const uint8_t* codes, const uint16_t* scales, const uint8_t* zeros,
+                               int64_t n, bool out_bf16, void* out, hipStream_t st) {
+  const int64_t nl = n / 8;
+  if (out_bf16)
+    hipLaunchKernelGGL(k_dq_int4<true>, dim3(dq_grid(nl)), dim3(kBlockThreads), 0, st, codes,
+                       scales, zeros, nl, out);
+  else
+    hipLaunchKernelGGL(k_dq_int4<false>, dim3(dq_grid(nl)), dim3(kBlockThreads), 0, st, codes,
+                       scales, zeros, nl, out);
+  return hipGetLastError();
+}
+
+}  // namespace pqb

@@ -29,49 +29,6 @@ __global__ __launch_bounds__(kBlockThreads) void k_mxfp4(const T* __restrict__ x
   }
 }
 
-// Signed E2M1 values, nibble -> float.
-__device__ __forceinline__ float e2m1_value(uint32_t nib) {
-  const uint32_t m = nib & 7u;
-  // m >= 2: 2^(m/2 - 1) * (1 + (m & 1) / 2); m == 1: 0.5; m == 0: 0
-  uint32_t b = m >= 2u ? ((((m >> 1) + 126u) << 23) | ((m & 1u) << 22)) : (m ? 0x3F000000u : 0u);
-  return as_f(b | ((nib & 8u) << 28));
-}
-
-template <bool kBf16Out>
-__global__ __launch_bounds__(kBlockThreads) void k_mxfp4_dequant(const uint8_t* __restrict__ codes,
-                                                                  const uint8_t* __restrict__ scales,
-                                                                  int64_t nunits,
-                                                                  void* __restrict__ out) {
-  for (int64_t u = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x; u < nunits;
-       u += (int64_t)gridDim.x * kBlockThreads) {
-    const uint32_t w = reinterpret_cast<const uint32_t*>(codes)[u];
-    const float sc = as_f((uint32_t)scales[u >> 2] << 23);  // 2^(e - 127), e in [85, 252]
-    float o[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = e2m1_value(w >> (4 * i)) * sc;
-    store_out8<kBf16Out>(out, u, o);
-  }
-}
-
-template <bool kBf16Out>
-__global__ __launch_bounds__(kBlockThreads) void k_nvfp4_dequant(const uint8_t* __restrict__ codes,
-                                                                  const uint8_t* __restrict__ scales,
-                                                                  const float* __restrict__ gs,
-                                                                  int64_t per_slice,
-                                                                  void* __restrict__ out) {
-  const int64_t b = blockIdx.y;
-  const float g = gs[b];
-  const int64_t nunits = per_slice / 8, u0 = b * nunits;
-  for (int64_t u = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x; u < nunits;
-       u += (int64_t)gridDim.x * kBlockThreads) {
-    const uint32_t w = reinterpret_cast<const uint32_t*>(codes)[u0 + u];
-    const float s = fmaxf(e4m3_decode(scales[(u0 + u) >> 1]), 1e-12f) * g;
-    float o[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = e2m1_value(w >> (4 * i)) * s;
-    store_out8<kBf16Out>(out, u0 + u, o);
-  }
-}
 
 // E2M1 nibble of each float (one byte per element).
 __global__ __launch_bounds__(kBlockThreads) void k_encode_e2m1(const float* __restrict__ y,
@@ -104,33 +61,6 @@ hipError_t launch_mxfp4(const void* x, bool bf16, int64_t n, uint8_t* codes, uin
   else
     hipLaunchKernelGGL((k_mxfp4<float, 4>), dim3(grid_cap(ntiles, 4 * waves, 1 << 30)),
                        dim3(kBlockThreads), 0, st, (const float*)x, nunits, codes, scales);
-  return hipGetLastError();
-}
-
-hipError_t launch_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, int64_t n,
-                                bool out_bf16, void* out, hipStream_t st) {
-  const int64_t nunits = n / 8;
-  const int grid = grid_cap(nunits, (int64_t)kBlockThreads * 4, 1 << 20);
-  if (out_bf16)
-    hipLaunchKernelGGL(k_mxfp4_dequant<true>, dim3(grid), dim3(kBlockThreads), 0, st, codes,
-                       scales, nunits, out);
-  else
-    hipLaunchKernelGGL(k_mxfp4_dequant<false>, dim3(grid), dim3(kBlockThreads), 0, st, codes,
-                       scales, nunits, out);
-  return hipGetLastError();
-}
-
-hipError_t launch_nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const float* gs,
-                                int64_t batch, int64_t per_slice, bool out_bf16, void* out,
-                                hipStream_t st) {
-  const int64_t nunits = per_slice / 8;
-  const dim3 grid(grid_cap(nunits, (int64_t)kBlockThreads * 4, 8192), (unsigned)batch);
-  if (out_bf16)
-    hipLaunchKernelGGL(k_nvfp4_dequant<true>, grid, dim3(kBlockThreads), 0, st, codes, scales, gs,
-                       per_slice, out);
-  else
-    hipLaunchKernelGGL(k_nvfp4_dequant<false>, grid, dim3(kBlockThreads), 0, st, codes, scales,
-                       gs, per_slice, out);
   return hipGetLastError();
 }
 

@@ -152,29 +152,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_tensor_quant(TensorArgs a
 // ---------------------------------------------------------------------------
 // Dequantization: out = dec(code) * s, float32 or RNE bf16.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void fp8_decode8(uint2 w, float s, float o[8]) {
-  const f32x2 a = e4m3x2_decode<false>(w.x), b = e4m3x2_decode<true>(w.x);
-  const f32x2 c = e4m3x2_decode<false>(w.y), d = e4m3x2_decode<true>(w.y);
-  o[0] = a.x * s; o[1] = a.y * s; o[2] = b.x * s; o[3] = b.y * s;
-  o[4] = c.x * s; o[5] = c.y * s; o[6] = d.x * s; o[7] = d.y * s;
-}
 
 __device__ __forceinline__ uint2 ld_codes8(const uint8_t* p) {
   return *reinterpret_cast<const uint2*>(p);
-}
-
-// 1x128: the scale of unit u (8 elements) is scales[u / 16].
-template <bool kBf16Out>
-__global__ __launch_bounds__(kBlockThreads) void k_fp8_dequant_1x128(const uint8_t* __restrict__ codes,
-                                                                      const float* __restrict__ scales,
-                                                                      int64_t nunits,
-                                                                      void* __restrict__ out) {
-  for (int64_t u = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x; u < nunits;
-       u += (int64_t)gridDim.x * kBlockThreads) {
-    float o[8];
-    fp8_decode8(ld_codes8(codes + u * 8), scales[u >> 4], o);
-    store_out8<kBf16Out>(out, u, o);
-  }
 }
 
 // Other scopes, one wave per row (rows of all slices in sequence): the row's
@@ -358,17 +338,8 @@ hipError_t launch_fp8_dequant(const uint8_t* codes, const float* scales, int gra
                               int64_t rows, int64_t cols, bool out_bf16, void* out,
                               hipStream_t st) {
   const int64_t n = batch * rows * cols;
-  if (gran == 2) {  // 1x128: cols % 128 == 0, flat
-    const int64_t nunits = n / 8;
-    const int grid = blocks_for(nunits, (int64_t)kBlockThreads * 4, 1 << 20);
-    if (out_bf16)
-      hipLaunchKernelGGL(k_fp8_dequant_1x128<true>, dim3(grid), dim3(kBlockThreads), 0, st, codes,
-                         scales, nunits, out);
-    else
-      hipLaunchKernelGGL(k_fp8_dequant_1x128<false>, dim3(grid), dim3(kBlockThreads), 0, st,
-                         codes, scales, nunits, out);
-    return hipGetLastError();
-  }
+  if (gran == 2)  // 1x128: cols % 128 == 0, flat
+    return launch_fp8_1x128_dequant(codes, scales, n, out_bf16, out, st);
   const int br = (int)(rows < 128 ? rows : 128);
   const int64_t nrows = batch * rows;
   const int grid = blocks_for(nrows, kBlockThreads / kWave, 1 << 16);

@@ -27,29 +27,6 @@ __global__ __launch_bounds__(kBlockThreads) void k_int4(const T* __restrict__ x,
   }
 }
 
-// (q - z) * s is exact in float32: |q - z| <= 15 and s has 8 significant bits.
-template <bool kBf16Out>
-__global__ __launch_bounds__(kBlockThreads) void k_int4_dequant(const uint8_t* __restrict__ codes,
-                                                                 const uint16_t* __restrict__ scales,
-                                                                 const uint8_t* __restrict__ zeros,
-                                                                 int64_t nunits,
-                                                                 void* __restrict__ out) {
-  for (int64_t u = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x; u < nunits;
-       u += (int64_t)gridDim.x * kBlockThreads) {
-    const uint32_t w = reinterpret_cast<const uint32_t*>(codes)[u];
-    const int64_t g = u >> 4;
-    const float s = as_f((uint32_t)scales[g] << 16);
-    const int z = ((int)(zeros[g >> 1] >> (4 * (g & 1))) << 28) >> 28;  // sign-extend
-    float o[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int q = ((int)(w >> (4 * i)) << 28) >> 28;
-      o[i] = (float)(q - z) * s;
-    }
-    store_out8<kBf16Out>(out, u, o);
-  }
-}
-
 inline int grid_for(int64_t work, int64_t per_block, int64_t cap) {
   int64_t g = (work + per_block - 1) / per_block;
   return (int)(g < 1 ? 1 : (g > cap ? cap : g));
@@ -68,19 +45,6 @@ hipError_t launch_int4(const void* x, bool bf16, int64_t n, uint8_t* codes, uint
   else
     hipLaunchKernelGGL((k_int4<float, 4>), dim3(grid_for(ntiles, 4 * waves, 1 << 30)),
                        dim3(kBlockThreads), 0, st, (const float*)x, nunits, codes, scales, zeros);
-  return hipGetLastError();
-}
-
-hipError_t launch_int4_dequant(const uint8_t* codes, const uint16_t* scales, const uint8_t* zeros,
-                               int64_t n, bool out_bf16, void* out, hipStream_t st) {
-  const int64_t nunits = n / 8;
-  const int grid = grid_for(nunits, kBlockThreads, 1 << 20);
-  if (out_bf16)
-    hipLaunchKernelGGL(k_int4_dequant<true>, dim3(grid), dim3(kBlockThreads), 0, st, codes, scales,
-                       zeros, nunits, out);
-  else
-    hipLaunchKernelGGL(k_int4_dequant<false>, dim3(grid), dim3(kBlockThreads), 0, st, codes,
-                       scales, zeros, nunits, out);
   return hipGetLastError();
 }
 

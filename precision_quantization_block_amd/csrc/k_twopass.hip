@@ -131,26 +131,34 @@ __global__ __launch_bounds__(kBlockThreads) void k_tp_amax(TpArgs a, TpGeo g,
 // ---------------------------------------------------------------------------
 // finalize: grid (slices, tensors)
 // ---------------------------------------------------------------------------
+// Finalize workgroups are 1024 threads with 8 loads in flight each: a slice
+// of 1 GiB of bf16 has 32768 partials, and the reduction is latency-bound.
+constexpr int kFinThreads = 1024, kFinWaves = kFinThreads / kWave, kFinLoads = 8;
+
 __device__ __forceinline__ uint32_t reduce_row(const float* __restrict__ p, int W, uint32_t* red) {
   uint32_t m = 0;
   int i = threadIdx.x;
-  for (; i + 3 * kBlockThreads < W; i += 4 * kBlockThreads)
-    m = max(max(max(m, as_u(p[i])), as_u(p[i + kBlockThreads])),
-            max(as_u(p[i + 2 * kBlockThreads]), as_u(p[i + 3 * kBlockThreads])));
-  for (; i < W; i += kBlockThreads) m = max(m, as_u(p[i]));
+  for (; i + (kFinLoads - 1) * kFinThreads < W; i += kFinLoads * kFinThreads) {
+    uint32_t v[kFinLoads];
+#pragma unroll
+    for (int k = 0; k < kFinLoads; ++k) v[k] = as_u(p[i + k * kFinThreads]);
+#pragma unroll
+    for (int k = 0; k < kFinLoads; ++k) m = max(m, v[k]);
+  }
+  for (; i < W; i += kFinThreads) m = max(m, as_u(p[i]));
   m = wave_umax(m);
   if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = m;
   __syncthreads();
   m = red[0];
-  for (int w = 1; w < kWgWaves; ++w) m = max(m, red[w]);
+  for (int w = 1; w < kFinWaves; ++w) m = max(m, red[w]);
   __syncthreads();
   return m;
 }
 
-__global__ __launch_bounds__(kBlockThreads) void k_tp_finalize_fp8(TpArgs a, TpGeo g,
-                                                                   const float* __restrict__ partials,
-                                                                   float* __restrict__ fin) {
-  __shared__ uint32_t red[kWgWaves];
+__global__ __launch_bounds__(kFinThreads) void k_tp_finalize_fp8(TpArgs a, TpGeo g,
+                                                                 const float* __restrict__ partials,
+                                                                 float* __restrict__ fin) {
+  __shared__ uint32_t red[kFinWaves];
   const int tz = blockIdx.y;
   if (a.mode[tz] == kKvStatic) return;
   const int64_t b = blockIdx.x, slot = (int64_t)tz * g.slices + b;
@@ -165,10 +173,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_tp_finalize_fp8(TpArgs a, TpG
   }
 }
 
-__global__ __launch_bounds__(kBlockThreads) void k_tp_finalize_nv(TpArgs a, TpGeo g,
-                                                                  const float* __restrict__ partials,
-                                                                  float* __restrict__ fin) {
-  __shared__ uint32_t red[kWgWaves];
+__global__ __launch_bounds__(kFinThreads) void k_tp_finalize_nv(TpArgs a, TpGeo g,
+                                                                const float* __restrict__ partials,
+                                                                float* __restrict__ fin) {
+  __shared__ uint32_t red[kFinWaves];
   const int64_t b = blockIdx.x;
   const uint32_t m = reduce_row(partials + b * g.W, g.W, red);
   const float gs = as_f(max(m, kAmaxFloorBits)) / 2688.0f;  // 448 * 6, IEEE division
@@ -179,7 +187,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_tp_finalize_nv(TpArgs a, TpGe
     a.gs[0][b] = gs;
   }
   // element scale of every finite block-scale code: max(dec(code), 1e-12) * gs
-  for (int c = threadIdx.x; c < 127; c += kBlockThreads) {
+  for (int c = threadIdx.x; c < 127; c += kFinThreads) {
     const float sc = fmaxf(e4m3_decode((uint32_t)c), 1e-12f) * gs;
     f[kNvSe + c] = sc;
     f[kNvYe + c] = 1.0f / sc;  // IEEE division
@@ -324,11 +332,11 @@ hipError_t launch_tp(const TpArgs& a, int nt, bool bf16, const TpGeo& g, bool nv
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (nv)
-      hipLaunchKernelGGL(k_tp_finalize_nv, dim3((unsigned)g.slices, 1), dim3(kBlockThreads), 0,
+      hipLaunchKernelGGL(k_tp_finalize_nv, dim3((unsigned)g.slices, 1), dim3(kFinThreads), 0,
                          st, a, g, partials, fin);
     else
       hipLaunchKernelGGL(k_tp_finalize_fp8, dim3((unsigned)g.slices, (unsigned)nt),
-                         dim3(kBlockThreads), 0, st, a, g, partials, fin);
+                         dim3(kFinThreads), 0, st, a, g, partials, fin);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

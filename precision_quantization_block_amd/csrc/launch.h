@@ -28,6 +28,8 @@ hipError_t launch_fp8_row(const void* x, bool bf16, int64_t nrows, int64_t cols,
 hipError_t launch_fp8_tensor(const void* const* x, bool bf16, int ntensors, int64_t batch,
                              int64_t per_slice, uint8_t* const* codes, float* const* scales,
                              float* partials, hipStream_t st);
+hipError_t launch_fp8_1x128_dequant(const uint8_t* codes, const float* scales, int64_t n,
+                                    bool out_bf16, void* out, hipStream_t st);
 hipError_t launch_fp8_dequant(const uint8_t* codes, const float* scales, int gran, int64_t batch,
                               int64_t rows, int64_t cols, bool out_bf16, void* out,
                               hipStream_t st);

@@ -285,6 +285,25 @@ __device__ __forceinline__ void nv_chunk(const T* __restrict__ xs, int64_t u0, i
 }
 
 // ---------------------------------------------------------------------------
+// Decoders shared by the dequantization kernels.
+// ---------------------------------------------------------------------------
+// Eight E4M3 codes (two dwords) -> eight values times s.
+__device__ __forceinline__ void fp8_decode8(uint2 w, float s, float o[8]) {
+  const f32x2 a = e4m3x2_decode<false>(w.x), b = e4m3x2_decode<true>(w.x);
+  const f32x2 c = e4m3x2_decode<false>(w.y), d = e4m3x2_decode<true>(w.y);
+  o[0] = a.x * s; o[1] = a.y * s; o[2] = b.x * s; o[3] = b.y * s;
+  o[4] = c.x * s; o[5] = c.y * s; o[6] = d.x * s; o[7] = d.y * s;
+}
+
+// Signed E2M1 values, nibble -> float.
+__device__ __forceinline__ float e2m1_value(uint32_t nib) {
+  const uint32_t m = nib & 7u;
+  // m >= 2: 2^(m/2 - 1) * (1 + (m & 1) / 2); m == 1: 0.5; m == 0: 0
+  uint32_t b = m >= 2u ? ((((m >> 1) + 126u) << 23) | ((m & 1u) << 22)) : (m ? 0x3F000000u : 0u);
+  return as_f(b | ((nib & 8u) << 28));
+}
+
+// ---------------------------------------------------------------------------
 // INT4 group-128 asymmetric: integers -8..7 with one scale and zero-point per
 // 128 elements (page "量化部署实战", 格式速查); q = clamp(round(x / s) + z, qmin,
 // qmax) ("LLM 推理优化 · 量化 学习笔记" §5.1); 2-byte scale per 128 ("14. 量化：
