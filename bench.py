@@ -239,12 +239,19 @@ def bench_extras(torch, eng, synth, reps, only=None):
     def want(*names):
         return only is None or any(only in n for n in names)
 
-    def one(name, x, fmt, gran, shape, nsets=1, dq_dtype=None):
+    def one(name, x, fmt, gran, shape, dq_dtype=None):
+        """Quantize (and dequantize) `x`, rotating over enough buffer sets that
+        the Infinity Cache cannot serve repeated reads: at least 4 sets and
+        more than 1 GiB in all for tensors under 1 GiB."""
         if not want(name):
             return
+        in_bytes = x.numel() * x.element_size()
+        set_bytes = in_bytes + out_bytes(eng.pqb.query_sizes(fmt, gran, *shape))
+        if dq_dtype is not None:
+            set_bytes += x.numel() * torch.empty((), dtype=dq_dtype).element_size()
+        nsets = 1 if in_bytes >= 1 << 30 else max(4, -(-(1 << 30) // set_bytes) + 1)
         xs = [x] + [x.clone() for _ in range(nsets - 1)]
         bufs = [eng.alloc(fmt, gran, shape, dev) for _ in range(nsets)]
-        in_bytes = x.numel() * x.element_size()
         nb = in_bytes + out_bytes(bufs[0]["sizes"])
         two_pass = fmt == "nvfp4" or gran == "tensor"
         t = time_reps(torch, lambda i: eng.quantize(xs[i % nsets], fmt, gran, shape,
@@ -253,32 +260,33 @@ def bench_extras(torch, eng, synth, reps, only=None):
                         shape=list(shape), dtype=str(x.dtype).replace("torch.", ""),
                         rotated_sets=nsets)
         if dq_dtype is not None:
-            o = [torch.empty(shape, dtype=dq_dtype, device=dev) for _ in range(min(nsets, 2))]
+            o = [torch.empty(shape, dtype=dq_dtype, device=dev) for _ in range(nsets)]
             nbd = out_bytes(bufs[0]["sizes"]) + o[0].numel() * o[0].element_size()
             t = time_reps(torch, lambda i: eng.dequantize(bufs[i % nsets], fmt, gran, shape,
-                                                          o[i % len(o)]), reps, 3)
+                                                          o[i % nsets]), reps, 3)
             out[name + "_dequant"] = rec(nbd, t, op=f"dequantize {fmt} -> "
                                          f"{str(dq_dtype).replace('torch.', '')}",
                                          shape=list(shape), rotated_sets=nsets)
-        log(f"{name}: {out[name]['gbs']} GB/s")
+        log(f"{name}: {out[name]['gbs']} GB/s over {nsets} buffer sets")
+        del xs, bufs
+        torch.cuda.empty_cache()
 
-    # float32 MLP weight, MXFP4 and NVFP4: 32 rotated copies (403 MB) so that the
-    # 256 MB Infinity Cache cannot hold them all
+    # float32 MLP weight, MXFP4 and NVFP4
     if want("mlp3072x1024"):
         w = synth.mlp_weight_fp32(device=dev)
-        one("mlp3072x1024_f32_mxfp4", w, "mxfp4", "blk32", (1, 3072, 1024), 32, torch.float32)
-        one("mlp3072x1024_f32_nvfp4", w, "nvfp4", "blk16", (1, 3072, 1024), 32, torch.float32)
+        one("mlp3072x1024_f32_mxfp4", w, "mxfp4", "blk32", (1, 3072, 1024), torch.float32)
+        one("mlp3072x1024_f32_nvfp4", w, "nvfp4", "blk16", (1, 3072, 1024), torch.float32)
         del w
     # heavy-tailed [28672, 8192] bf16 weight
     if want("w28672x8192"):
         w = synth.heavy_tail_weight(device=dev)
-        one("w28672x8192_bf16_mxfp4", w, "mxfp4", "blk32", (1, 28672, 8192), 2, torch.bfloat16)
-        one("w28672x8192_bf16_nvfp4", w, "nvfp4", "blk16", (1, 28672, 8192), 2, torch.bfloat16)
+        one("w28672x8192_bf16_mxfp4", w, "mxfp4", "blk32", (1, 28672, 8192), torch.bfloat16)
+        one("w28672x8192_bf16_nvfp4", w, "nvfp4", "blk16", (1, 28672, 8192), torch.bfloat16)
         del w
     # FP8 weight alone (128x128 tiles)
     if want("w7168x2048"):
         w = synth.fp8_weight(device=dev)
-        one("w7168x2048_bf16_fp8_128x128", w, "fp8_e4m3", "128x128", (1, 7168, 2048), 8)
+        one("w7168x2048_bf16_fp8_128x128", w, "fp8_e4m3", "128x128", (1, 7168, 2048))
         del w
     # 1 GiB bf16 tensor, every format
     sweep = (("fp8_e4m3", "1x128", torch.bfloat16), ("fp8_e4m3", "128x128", None),
@@ -289,7 +297,7 @@ def bench_extras(torch, eng, synth, reps, only=None):
     if want(*names):
         g = synth.gaussian(device=dev)
         for name, (fmt, gran, dq) in zip(names, sweep):
-            one(name, g, fmt, gran, (1, 65536, 8192), 1, dq)
+            one(name, g, fmt, gran, (1, 65536, 8192), dq)
         del g
     torch.cuda.empty_cache()
     if want("kv28x32768x8x128_bf16_fp8"):
