@@ -51,6 +51,8 @@ def lib():
         L.orc_e4m3_decode.argtypes, L.orc_e4m3_decode.restype = [ctypes.c_uint8], ctypes.c_float
         L.orc_e4m3_encode.argtypes, L.orc_e4m3_encode.restype = [ctypes.c_float], ctypes.c_uint8
         L.orc_e2m1_decode.argtypes, L.orc_e2m1_decode.restype = [ctypes.c_uint8], ctypes.c_float
+        L.orc_e5m2_decode.argtypes, L.orc_e5m2_decode.restype = [ctypes.c_uint8], ctypes.c_float
+        L.orc_e5m2_encode.argtypes, L.orc_e5m2_encode.restype = [ctypes.c_float], ctypes.c_uint8
         L.orc_e2m1_encode.argtypes, L.orc_e2m1_encode.restype = [ctypes.c_float], ctypes.c_uint8
         L.orc_bf16_round.argtypes, L.orc_bf16_round.restype = [ctypes.c_float], ctypes.c_uint16
         L.orc_bf16_to_f32.argtypes, L.orc_bf16_to_f32.restype = [ctypes.c_uint16], ctypes.c_float
@@ -59,14 +61,23 @@ def lib():
         for name in ("orc_fp8_quantize", "orc_fp8_dequantize", "orc_mxfp4_quantize",
                      "orc_mxfp4_dequantize", "orc_nvfp4_quantize", "orc_nvfp4_dequantize",
                      "orc_int4_quantize", "orc_int4_dequantize", "orc_kv_write_fp8",
-                     "orc_kv_quant_fp8"):
+                     "orc_kv_quant_fp8", "orc_fp8x_quantize", "orc_fp8x_dequantize",
+                     "orc_mxfp8_quantize", "orc_mxfp8_dequantize", "orc_int8_quantize",
+                     "orc_int8_dequantize"):
             getattr(L, name).restype = I
-        for name in ("orc_e4m3_encode_n", "orc_e2m1_encode_n", "orc_bf16_round_n"):
+        for name in ("orc_e4m3_encode_n", "orc_e5m2_encode_n", "orc_e2m1_encode_n",
+                     "orc_bf16_round_n"):
             getattr(L, name).argtypes = [P, I64, P]
             getattr(L, name).restype = None
         L.orc_fp8_quantize.argtypes = [P, I, I64, I64, I64, I, P, P]
         L.orc_fp8_dequantize.argtypes = [P, P, I64, I64, I64, I, I, P]
         L.orc_mxfp4_quantize.argtypes = [P, I, I64, I64, I64, P, P]
+        L.orc_fp8x_quantize.argtypes = [P, I, I64, I64, I64, I, I, P, P]
+        L.orc_fp8x_dequantize.argtypes = [P, P, I64, I64, I64, I, I, I, P]
+        L.orc_mxfp8_quantize.argtypes = [P, I, I64, I64, I64, P, P]
+        L.orc_mxfp8_dequantize.argtypes = [P, P, I64, I64, I64, I, P]
+        L.orc_int8_quantize.argtypes = [P, I, I64, I64, I64, I, P, P]
+        L.orc_int8_dequantize.argtypes = [P, P, I64, I64, I64, I, I, P]
         L.orc_mxfp4_dequantize.argtypes = [P, P, I64, I64, I64, I, P]
         L.orc_nvfp4_quantize.argtypes = [P, I, I64, I64, I64, P, P, P]
         L.orc_nvfp4_dequantize.argtypes = [P, P, P, I64, I64, I64, I, P]
@@ -159,6 +170,13 @@ def e4m3_encode_array(y) -> np.ndarray:
     return out
 
 
+def e5m2_encode_array(y) -> np.ndarray:
+    y = np.ascontiguousarray(y, np.float32)
+    out = np.empty(y.shape, np.uint8)
+    lib().orc_e5m2_encode_n(_p(y), y.size, _p(out))
+    return out
+
+
 def e2m1_encode_array(y) -> np.ndarray:
     y = np.ascontiguousarray(y, np.float32)
     out = np.empty(y.shape, np.uint8)
@@ -188,9 +206,14 @@ def _fp8_nscales(gran, batch, rows, cols):
     return (batch, rows // br if br else 0, cols // 128)
 
 
-def fp8_quantize(x, gran, bf16=None):
-    """-> (codes u8 [batch, rows, cols], scales f32 in the scope layout)."""
+ELEMS = {"e4m3": 0, "e5m2": 1}
+
+
+def fp8_quantize(x, gran, bf16=None, elem="e4m3"):
+    """-> (codes u8 [batch, rows, cols], scales f32 in the scope layout).
+    elem: "e4m3" (scale amax/448) or "e5m2" (scale amax/57344)."""
     gran = GRANS.get(gran, gran)
+    elem = ELEMS.get(elem, elem)
     x, dt, b, r, c = _as_input(x, bf16)
     codes = np.empty((b, r, c), np.uint8)
     br = min(128, r)
@@ -199,18 +222,66 @@ def fp8_quantize(x, gran, bf16=None):
     if gran == BLK_1x128 and c % 128:
         _check(-4, "fp8_quantize")
     scales = np.empty(_fp8_nscales(gran, b, r, c), np.float32)
-    _check(lib().orc_fp8_quantize(_p(x), dt, b, r, c, gran, _p(codes), _p(scales)), "fp8_quantize")
+    _check(lib().orc_fp8x_quantize(_p(x), dt, b, r, c, gran, elem, _p(codes), _p(scales)),
+           "fp8_quantize")
     return codes, scales
 
 
-def fp8_dequantize(codes, scales, gran, out_bf16=False):
+def fp8_dequantize(codes, scales, gran, out_bf16=False, elem="e4m3"):
     gran = GRANS.get(gran, gran)
+    elem = ELEMS.get(elem, elem)
     codes = np.ascontiguousarray(codes, np.uint8)
     scales = np.ascontiguousarray(scales, np.float32)
     b, r, c = codes.shape
     out = _out((b, r, c), out_bf16)
-    _check(lib().orc_fp8_dequantize(_p(codes), _p(scales), b, r, c, gran, int(out_bf16), _p(out)),
-           "fp8_dequantize")
+    _check(lib().orc_fp8x_dequantize(_p(codes), _p(scales), b, r, c, gran, elem, int(out_bf16),
+                                     _p(out)), "fp8_dequantize")
+    return out
+
+
+def mxfp8_quantize(x, bf16=None):
+    """-> (codes u8 E4M3 [batch, rows, cols], scales u8 E8M0 [batch, rows, cols/32])."""
+    x, dt, b, r, c = _as_input(x, bf16)
+    if c % 32:
+        _check(-4, "mxfp8_quantize")
+    codes = np.empty((b, r, c), np.uint8)
+    scales = np.empty((b, r, c // 32), np.uint8)
+    _check(lib().orc_mxfp8_quantize(_p(x), dt, b, r, c, _p(codes), _p(scales)), "mxfp8_quantize")
+    return codes, scales
+
+
+def mxfp8_dequantize(codes, scales, out_bf16=False):
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    b, r, c = codes.shape
+    out = _out((b, r, c), out_bf16)
+    _check(lib().orc_mxfp8_dequantize(_p(codes), _p(scales), b, r, c, int(out_bf16), _p(out)),
+           "mxfp8_dequantize")
+    return out
+
+
+def int8_quantize(x, gran, bf16=None):
+    """Symmetric INT8, gran "tensor" or "row".
+    -> (codes i8 [batch, rows, cols], scales f32 [batch] or [batch, rows])."""
+    gran = GRANS.get(gran, gran)
+    x, dt, b, r, c = _as_input(x, bf16)
+    if gran not in (TENSOR, ROW):
+        _check(-4, "int8_quantize")
+    codes = np.empty((b, r, c), np.int8)
+    scales = np.empty((b,) if gran == TENSOR else (b, r), np.float32)
+    _check(lib().orc_int8_quantize(_p(x), dt, b, r, c, gran, _p(codes), _p(scales)),
+           "int8_quantize")
+    return codes, scales
+
+
+def int8_dequantize(codes, scales, gran, out_bf16=False):
+    gran = GRANS.get(gran, gran)
+    codes = np.ascontiguousarray(codes, np.int8)
+    scales = np.ascontiguousarray(scales, np.float32)
+    b, r, c = codes.shape
+    out = _out((b, r, c), out_bf16)
+    _check(lib().orc_int8_dequantize(_p(codes), _p(scales), b, r, c, gran, int(out_bf16), _p(out)),
+           "int8_dequantize")
     return out
 
 

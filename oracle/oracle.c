@@ -62,6 +62,38 @@ uint8_t orc_e4m3_encode(float y) {
   return (uint8_t)((signbit(y) ? 0x80 : 0x00) | best);
 }
 
+/* E5M2 [BYTES 低位浮点格式 table; NOTES §4.2]: 1 sign, 5 exponent, 2 mantissa
+ * bits, largest finite value 57344 = 1.75 * 2^15, which fixes the bias at 15.
+ * Exponent field 31 holds the infinities (mantissa 0) and NaNs; field 0 holds
+ * the subnormals m * 2^-16. */
+float orc_e5m2_decode(uint8_t code) {
+  int sign = code >> 7, e = (code >> 2) & 31, m = code & 3;
+  float mag;
+  if (e == 31) return m ? (sign ? -NAN : NAN) : (sign ? -INFINITY : INFINITY);
+  if (e == 0)
+    mag = ldexpf((float)m, -16);
+  else
+    mag = ldexpf((float)(4 + m), e - 17);
+  return sign ? -mag : mag;
+}
+
+/* E5M2 rounding: the nearest finite E5M2 value, ties to the code with an even
+ * mantissa (round-to-nearest-even), sign bit copied from y; the search runs
+ * over every non-negative finite code (0x00..0x7B). */
+uint8_t orc_e5m2_encode(float y) {
+  double a = fabs((double)y);
+  int best = 0;
+  double bestd = a;
+  for (int c = 1; c <= 0x7B; ++c) {
+    double d = fabs(a - (double)orc_e5m2_decode((uint8_t)c));
+    if (d < bestd || (d == bestd && (c & 1) == 0)) {
+      best = c;
+      bestd = d;
+    }
+  }
+  return (uint8_t)((signbit(y) ? 0x80 : 0x00) | best);
+}
+
 /* E2M1 [DEPLOY 格式速查, 伪量化实现; BYTES 新格式]: the non-negative values are
  * 0, 0.5, 1, 1.5, 2, 3, 4, 6.  The nibble holds the sign in bit 3 and the index
  * into this list in bits 0..2 (with exponent bias 1 the index is exactly the
@@ -155,10 +187,25 @@ static int bad_dims(int64_t batch, int64_t rows, int64_t cols) {
 /* ------------------------------------------------------------------------ */
 
 /* One scope: its scale is max(amax, 1e-12) / 448, each element becomes the
- * E4M3 code of clamp(x / scale, -448, 448). */
+ * E4M3 code of clamp(x / scale, -448, 448).  With E5M2 elements the same steps
+ * use E5M2's largest value, 57344, in place of 448. */
 static float fp8_scale(float amax) { return fmaxf(amax, 1e-12f) / 448.0f; }
 
 static uint8_t fp8_code(float x, float s) { return orc_e4m3_encode(clampf(x / s, -448.0f, 448.0f)); }
+
+static float fp8x_max(int elem) { return elem == ORC_E5M2 ? 57344.0f : 448.0f; }
+
+static float fp8x_scale(float amax, int elem) { return fmaxf(amax, 1e-12f) / fp8x_max(elem); }
+
+static uint8_t fp8x_code(float x, float s, int elem) {
+  float m = fp8x_max(elem);
+  float y = clampf(x / s, -m, m);
+  return elem == ORC_E5M2 ? orc_e5m2_encode(y) : orc_e4m3_encode(y);
+}
+
+static float fp8x_decode(uint8_t code, int elem) {
+  return elem == ORC_E5M2 ? orc_e5m2_decode(code) : orc_e4m3_decode(code);
+}
 
 /* Index of the scale that element (b, r, c) uses; -1 for a rejected shape. */
 static int64_t fp8_scale_index(int gran, int64_t rows, int64_t cols, int64_t b, int64_t r,
@@ -211,6 +258,17 @@ static int64_t fp8_num_scales(int gran, int64_t batch, int64_t rows, int64_t col
 
 int orc_fp8_quantize(const void* x, int dtype, int64_t batch, int64_t rows, int64_t cols,
                      int gran, uint8_t* codes, float* scales) {
+  return orc_fp8x_quantize(x, dtype, batch, rows, cols, gran, ORC_E4M3, codes, scales);
+}
+
+int orc_fp8_dequantize(const uint8_t* codes, const float* scales, int64_t batch, int64_t rows,
+                       int64_t cols, int gran, int out_dtype, void* out) {
+  return orc_fp8x_dequantize(codes, scales, batch, rows, cols, gran, ORC_E4M3, out_dtype, out);
+}
+
+int orc_fp8x_quantize(const void* x, int dtype, int64_t batch, int64_t rows, int64_t cols,
+                      int gran, int elem, uint8_t* codes, float* scales) {
+  if (elem != ORC_E4M3 && elem != ORC_E5M2) return -2;
   if (bad_dims(batch, rows, cols) || gran < ORC_TENSOR || gran > ORC_BLK_128x128) return -4;
   if (!fp8_shape_ok(gran, rows, cols)) return -4;
   int64_t ns = fp8_num_scales(gran, batch, rows, cols);
@@ -222,20 +280,22 @@ int orc_fp8_quantize(const void* x, int dtype, int64_t batch, int64_t rows, int6
         int64_t si = fp8_scale_index(gran, rows, cols, b, r, c);
         scales[si] = fmaxf(scales[si], fabsf(ld(x, dtype, (b * rows + r) * cols + c)));
       }
-  for (int64_t i = 0; i < ns; ++i) scales[i] = fp8_scale(scales[i]);
+  for (int64_t i = 0; i < ns; ++i) scales[i] = fp8x_scale(scales[i], elem);
   /* pass 2: codes */
   for (int64_t b = 0; b < batch; ++b)
     for (int64_t r = 0; r < rows; ++r)
       for (int64_t c = 0; c < cols; ++c) {
         int64_t i = (b * rows + r) * cols + c;
-        codes[i] = fp8_code(ld(x, dtype, i), scales[fp8_scale_index(gran, rows, cols, b, r, c)]);
+        codes[i] = fp8x_code(ld(x, dtype, i), scales[fp8_scale_index(gran, rows, cols, b, r, c)],
+                             elem);
       }
   return 0;
 }
 
-/* Dequantization is the decoded E4M3 value times its scope's scale. */
-int orc_fp8_dequantize(const uint8_t* codes, const float* scales, int64_t batch, int64_t rows,
-                       int64_t cols, int gran, int out_dtype, void* out) {
+/* Dequantization is the decoded E4M3 (E5M2) value times its scope's scale. */
+int orc_fp8x_dequantize(const uint8_t* codes, const float* scales, int64_t batch, int64_t rows,
+                        int64_t cols, int gran, int elem, int out_dtype, void* out) {
+  if (elem != ORC_E4M3 && elem != ORC_E5M2) return -2;
   if (bad_dims(batch, rows, cols) || gran < ORC_TENSOR || gran > ORC_BLK_128x128) return -4;
   if (!fp8_shape_ok(gran, rows, cols)) return -4;
   for (int64_t b = 0; b < batch; ++b)
@@ -243,7 +303,7 @@ int orc_fp8_dequantize(const uint8_t* codes, const float* scales, int64_t batch,
       for (int64_t c = 0; c < cols; ++c) {
         int64_t i = (b * rows + r) * cols + c;
         float s = scales[fp8_scale_index(gran, rows, cols, b, r, c)];
-        st(out, out_dtype, i, orc_e4m3_decode(codes[i]) * s);
+        st(out, out_dtype, i, fp8x_decode(codes[i], elem) * s);
       }
   return 0;
 }
@@ -407,6 +467,77 @@ int orc_kv_write_fp8(const void* k, const void* v, int dtype, int64_t layers,
 }
 
 /* ------------------------------------------------------------------------ */
+/* MXFP8 [NOTES §4.1, §4.2, §4.5; BYTES 低位浮点格式]                         */
+/* ------------------------------------------------------------------------ */
+
+/* Blocks of 32 share an E8M0 power-of-two scale; the elements are E4M3.  By
+ * the same rule as MXFP4 (whose scale exponent is floor(log2 amax) minus
+ * E2M1's largest exponent, 2), the scale is 2^X with X = floor(log2(max(amax,
+ * 1e-12))) - 8, 8 being E4M3's largest exponent.  Each element is the E4M3
+ * code of clamp(x / 2^X, -448, 448); the block maximum lands in [256, 512), so
+ * the clamp binds for blocks whose maximum has a significand of 1.75 or more.
+ * The stored byte is X + 127. */
+int orc_mxfp8_quantize(const void* x, int dtype, int64_t batch, int64_t rows, int64_t cols,
+                       uint8_t* codes, uint8_t* scales) {
+  if (bad_dims(batch, rows, cols) || cols % 32) return -4;
+  int64_t nblk = batch * rows * cols / 32;
+  for (int64_t k = 0; k < nblk; ++k) {
+    float amax = 0.0f;
+    for (int64_t j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(ld(x, dtype, k * 32 + j)));
+    int e;
+    frexpf(fmaxf(amax, 1e-12f), &e); /* max(amax, 1e-12) = f * 2^e, f in [0.5, 1) */
+    int X = (e - 1) - 8;
+    scales[k] = (uint8_t)(X + 127);
+    for (int64_t j = 0; j < 32; ++j) {
+      float y = clampf(ldexpf(ld(x, dtype, k * 32 + j), -X), -448.0f, 448.0f);
+      codes[k * 32 + j] = orc_e4m3_encode(y);
+    }
+  }
+  return 0;
+}
+
+int orc_mxfp8_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t batch,
+                         int64_t rows, int64_t cols, int out_dtype, void* out) {
+  if (bad_dims(batch, rows, cols) || cols % 32) return -4;
+  int64_t n = batch * rows * cols;
+  for (int64_t i = 0; i < n; ++i)
+    st(out, out_dtype, i, ldexpf(orc_e4m3_decode(codes[i]), (int)scales[i / 32] - 127));
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Symmetric INT8 [DEPLOY 格式速查; BYTES 量化在做什么; NOTES §5.1]          */
+/* ------------------------------------------------------------------------ */
+
+/* W8A8 INT8 is per channel (a weight row) and per token (an activation row);
+ * per tensor is also offered.  The scale is max(amax, 1e-12) / 127 (the INT8
+ * form of the symmetric scale) and q = clamp(rint(x / s), -128, 127). */
+int orc_int8_quantize(const void* x, int dtype, int64_t batch, int64_t rows, int64_t cols,
+                      int gran, int8_t* codes, float* scales) {
+  if (bad_dims(batch, rows, cols) || (gran != ORC_TENSOR && gran != ORC_ROW)) return -4;
+  int64_t ns = gran == ORC_TENSOR ? batch : batch * rows;
+  int64_t per = gran == ORC_TENSOR ? rows * cols : cols;
+  for (int64_t k = 0; k < ns; ++k) {
+    float amax = 0.0f;
+    for (int64_t j = 0; j < per; ++j) amax = fmaxf(amax, fabsf(ld(x, dtype, k * per + j)));
+    float s = fmaxf(amax, 1e-12f) / 127.0f;
+    scales[k] = s;
+    for (int64_t j = 0; j < per; ++j)
+      codes[k * per + j] = (int8_t)clampf(rintf(ld(x, dtype, k * per + j) / s), -128.0f, 127.0f);
+  }
+  return 0;
+}
+
+int orc_int8_dequantize(const int8_t* codes, const float* scales, int64_t batch, int64_t rows,
+                        int64_t cols, int gran, int out_dtype, void* out) {
+  if (bad_dims(batch, rows, cols) || (gran != ORC_TENSOR && gran != ORC_ROW)) return -4;
+  int64_t per = gran == ORC_TENSOR ? rows * cols : cols;
+  int64_t n = batch * rows * cols;
+  for (int64_t i = 0; i < n; ++i) st(out, out_dtype, i, (float)codes[i] * scales[i / per]);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* FP8 KV-cache variants [DEPLOY KV Cache 量化：误差要和信号比]               */
 /* ------------------------------------------------------------------------ */
 
@@ -458,6 +589,10 @@ int orc_kv_quant_fp8(const void* x, int dtype, int64_t layers, int64_t tokens, i
 
 void orc_e4m3_encode_n(const float* y, int64_t n, uint8_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_encode(y[i]);
+}
+
+void orc_e5m2_encode_n(const float* y, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_e5m2_encode(y[i]);
 }
 
 void orc_e2m1_encode_n(const float* y, int64_t n, uint8_t* out) {

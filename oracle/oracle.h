@@ -35,15 +35,19 @@ extern "C" {
 
 enum { ORC_F32 = 0, ORC_BF16 = 1 };
 enum { ORC_TENSOR = 0, ORC_ROW = 1, ORC_BLK_1x128 = 2, ORC_BLK_128x128 = 3 };
+enum { ORC_E4M3 = 0, ORC_E5M2 = 1 };
 
 /* number formats */
 float    orc_e4m3_decode(uint8_t code);
 uint8_t  orc_e4m3_encode(float y);
+float    orc_e5m2_decode(uint8_t code);
+uint8_t  orc_e5m2_encode(float y);
 float    orc_e2m1_decode(uint8_t nibble);
 uint8_t  orc_e2m1_encode(float y);
 uint16_t orc_bf16_round(float v);
 float    orc_bf16_to_f32(uint16_t h);
 void     orc_e4m3_encode_n(const float* y, int64_t n, uint8_t* out);
+void     orc_e5m2_encode_n(const float* y, int64_t n, uint8_t* out);
 void     orc_e2m1_encode_n(const float* y, int64_t n, uint8_t* out);
 void     orc_bf16_round_n(const float* v, int64_t n, uint16_t* out);
 
@@ -57,6 +61,22 @@ int orc_fp8_dequantize(const uint8_t* codes, const float* scales, int64_t batch,
                        int64_t cols, int gran, int out_dtype, void* out);
 
 /* MXFP4: E2M1 in 32-element blocks, E8M0 power-of-two scale */
+/* FP8 scopes with E4M3 (max 448) or E5M2 (max 57344) elements; returns -2
+ * for an unknown element format. */
+int orc_fp8x_quantize(const void* x, int dtype, int64_t batch, int64_t rows, int64_t cols,
+                      int gran, int elem, uint8_t* codes, float* scales);
+int orc_fp8x_dequantize(const uint8_t* codes, const float* scales, int64_t batch, int64_t rows,
+                        int64_t cols, int gran, int elem, int out_dtype, void* out);
+/* MXFP8: E4M3 codes u8 [batch, rows, cols], E8M0 scales u8 [batch, rows, cols/32]. */
+int orc_mxfp8_quantize(const void* x, int dtype, int64_t batch, int64_t rows, int64_t cols,
+                       uint8_t* codes, uint8_t* scales);
+int orc_mxfp8_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t batch,
+                         int64_t rows, int64_t cols, int out_dtype, void* out);
+/* Symmetric INT8, TENSOR or ROW: codes i8 [batch, rows, cols], scales f32. */
+int orc_int8_quantize(const void* x, int dtype, int64_t batch, int64_t rows, int64_t cols,
+                      int gran, int8_t* codes, float* scales);
+int orc_int8_dequantize(const int8_t* codes, const float* scales, int64_t batch, int64_t rows,
+                        int64_t cols, int gran, int out_dtype, void* out);
 int orc_mxfp4_quantize(const void* x, int dtype, int64_t batch, int64_t rows, int64_t cols,
                        uint8_t* codes, uint8_t* scales);
 int orc_mxfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t batch,
