@@ -292,7 +292,8 @@ def bench_extras(torch, eng, synth, reps, only=None):
     sweep = (("fp8_e4m3", "1x128", torch.bfloat16), ("fp8_e4m3", "128x128", None),
              ("fp8_e4m3", "row", None), ("fp8_e4m3", "tensor", None),
              ("mxfp4", "blk32", torch.bfloat16), ("nvfp4", "blk16", None),
-             ("int4_asym", "grp128", torch.bfloat16))
+             ("int4_asym", "grp128", torch.bfloat16), ("fp8_e5m2", "1x128", torch.bfloat16),
+             ("int8_sym", "row", torch.bfloat16), ("mxfp8", "blk32", torch.bfloat16))
     names = [f"sweep1GiB_bf16_{f}_{g}" for f, g, _ in sweep]
     if want(*names):
         g = synth.gaussian(device=dev)

@@ -20,14 +20,18 @@
  *   "14. 量化：让每一步搬更少的字节", section 量化在做什么: the uniform
  *   quantizer q = round(x/s) and its 2-byte scale per 128 weights.
  *   "LLM 推理优化 · 量化（Quantization）系统学习笔记" §5.1: asymmetric
- *   q = clamp(round(x/s) + z, qmin, qmax).
+ *   q = clamp(round(x/s) + z, qmin, qmax); §4.2 and §4.5: FP8 E5M2 (max 57344)
+ *   and MXFP8 (32-element blocks, E8M0 scale, E4M3 elements).  "14. 量化：让
+ *   每一步搬更少的字节", 量化在做什么 and the low-precision float table:
+ *   symmetric INT8 with s = max|x| / 127, and E5M2's largest value 57344.
  *
  * Arithmetic: IEEE binary32 with round-to-nearest-even and subnormals; bf16
  * inputs are widened exactly.  Every quotient x/s is the correctly rounded
  * one.  Element rounding: E4M3 round-to-nearest-even after the clamp to +-448;
- * E2M1 to the nearest of {0, .5, 1, 1.5, 2, 3, 4, 6} with ties to the smaller
- * magnitude, sign bit set for negative values (so -0.0 gives +0); INT4
- * q = clamp(rint(x/s) + z, -8, 7).  Inputs must be finite.
+ * E5M2 round-to-nearest-even (max 57344); E2M1 to the nearest of {0, .5, 1,
+ * 1.5, 2, 3, 4, 6} with ties to the smaller magnitude, sign bit set for negative
+ * values (so -0.0 gives +0); INT4 q = clamp(rint(x/s) + z, -8, 7); INT8
+ * q = clamp(rint(x/s), -128, 127).  Inputs must be finite.
  *
  * Shapes.  A tensor is [batch, rows, cols], contiguous and row-major.
  * "Per tensor" (FP8 TENSOR, the NVFP4 tensor scale) means per batch slice.
@@ -38,6 +42,13 @@
  *   FP8_E4M3 x BLK_1x128  codes u8 [b, r, c]      scales f32 [b, r, c/128]
  *   FP8_E4M3 x BLK_128x128 codes u8 [b, r, c]     scales f32 [b, r/br, c/128],
  *                                                 br = min(128, r)
+ *   FP8_E5M2 x the same four scopes, same layouts; s = max(amax, 1e-12)/57344
+ *   INT8_SYM x TENSOR / ROW: codes i8 [b, r, c], scales f32 [b] / [b, r];
+ *                                                 s = max(amax, 1e-12)/127
+ *   MXFP8 x BLK_32        codes u8 E4M3 [b, r, c] scales u8 E8M0 [b, r, c/32]
+ *                                                 (X + 127, X = floor(log2
+ *                                                 max(amax,1e-12)) - 8; codes
+ *                                                 E4M3(clamp(x/2^X, +-448)))
  *   MXFP4 x BLK_32        codes u8 [b, r, c/2]    scales u8 E8M0 [b, r, c/32]
  *                                                 (exponent + 127)
  *   NVFP4 x BLK_16        codes u8 [b, r, c/2]    scales u8 E4M3 [b, r, c/16]
@@ -90,7 +101,10 @@ typedef enum pqb_format {
   PQB_FP8_E4M3 = 0,
   PQB_MXFP4 = 1,
   PQB_NVFP4 = 2,
-  PQB_INT4_ASYM = 3
+  PQB_INT4_ASYM = 3,
+  PQB_FP8_E5M2 = 4,
+  PQB_MXFP8 = 5,
+  PQB_INT8_SYM = 6
 } pqb_format;
 
 typedef enum pqb_gran {
@@ -135,11 +149,11 @@ typedef struct pqb_job {
 } pqb_job;
 
 /* Quantize several tensors with as few launches as possible: jobs of one
- * family share fused launches of up to 24 jobs (FP8 1x128 and 128x128
- * together; MXFP4; INT4), per-row FP8 jobs get a launch each.  Each job's outputs are exactly those of
- * pqb_quantize on the same arguments.  Only the one-pass formats qualify (FP8
- * ROW / BLK_1x128 / BLK_128x128, MXFP4, INT4); a per-tensor FP8 or NVFP4 job
- * returns PQB_ERR_COMBO.  Every job is validated (same rules and codes as
+ * family share fused launches of up to 24 jobs (FP8 E4M3/E5M2 1x128 and
+ * 128x128 together; MXFP4 with MXFP8; INT4), per-row jobs (FP8, INT8) get a
+ * launch each.  Each job's outputs are exactly those of pqb_quantize on the
+ * same arguments.  Only the one-pass pairs qualify; a per-tensor job (FP8,
+ * INT8) or an NVFP4 job returns PQB_ERR_COMBO.  Every job is validated (same rules and codes as
  * pqb_quantize) before anything is enqueued.  Outputs of different jobs must
  * not overlap each other or any input.  `jobs` is a host array and may be
  * reused once the call returns. */
@@ -147,7 +161,8 @@ pqb_status pqb_quantize_batch(const pqb_job* jobs, int64_t njobs, void* stream);
 
 /* Inverse of pqb_quantize: out[b, r, c] = decoded code times its scale(s),
  * as float32 or rounded to bf16 (round-to-nearest-even) by `out_dtype`.
- * FP8: dec(code) * s.  MXFP4: +-V * 2^(e8m0 - 127) (exact).  NVFP4:
+ * FP8 (E4M3, E5M2): dec(code) * s.  INT8: q * s.  MXFP4: +-V * 2^(e8m0 - 127)
+ * and MXFP8: dec(code) * 2^(e8m0 - 127) (both exact).  NVFP4:
  * +-V * (max(dec(block scale), 1e-12) * gs).  INT4: (q - z) * s (exact). */
 pqb_status pqb_dequantize(const void* codes, const void* scales, const void* aux, pqb_format fmt,
                           pqb_gran gran, int64_t batch, int64_t rows, int64_t cols,
@@ -200,6 +215,9 @@ pqb_status pqb_kv_write_fp8_ex(const void* k, const void* v, pqb_dtype dtype, in
  * per element; E2M1 of y (ties to the smaller magnitude, saturating at 6)
  * into one nibble per byte (low 4 bits). */
 pqb_status pqb_encode_e4m3(const float* y, int64_t n, uint8_t* out, void* stream);
+/* E5M2 of y (round-to-nearest-even; |y| must not exceed 57344) into one byte
+ * per element. */
+pqb_status pqb_encode_e5m2(const float* y, int64_t n, uint8_t* out, void* stream);
 pqb_status pqb_encode_e2m1(const float* y, int64_t n, uint8_t* out, void* stream);
 
 const char* pqb_status_string(pqb_status s);

@@ -16,9 +16,13 @@ bool valid_dtype(int d) { return d == PQB_F32 || d == PQB_BF16; }
 bool valid_pair(int fmt, int gran) {
   switch (fmt) {
     case PQB_FP8_E4M3:
+    case PQB_FP8_E5M2:
       return gran == PQB_TENSOR || gran == PQB_ROW || gran == PQB_BLK_1x128 ||
              gran == PQB_BLK_128x128;
+    case PQB_INT8_SYM:
+      return gran == PQB_TENSOR || gran == PQB_ROW;
     case PQB_MXFP4:
+    case PQB_MXFP8:
       return gran == PQB_BLK_32;
     case PQB_NVFP4:
       return gran == PQB_BLK_16;
@@ -28,7 +32,12 @@ bool valid_pair(int fmt, int gran) {
   return false;
 }
 
-bool known_format(int f) { return f >= PQB_FP8_E4M3 && f <= PQB_INT4_ASYM; }
+bool known_format(int f) { return f >= PQB_FP8_E4M3 && f <= PQB_INT8_SYM; }
+
+// Formats with one byte per element and float32 scales over the FP8 scopes,
+// and their element kind for the launchers (0 E4M3, 1 E5M2, 2 INT8).
+bool one_byte(int f) { return f == PQB_FP8_E4M3 || f == PQB_FP8_E5M2 || f == PQB_INT8_SYM; }
+int elem_of(int f) { return f == PQB_FP8_E5M2 ? 1 : f == PQB_INT8_SYM ? 2 : 0; }
 bool known_gran(int g) { return g >= PQB_TENSOR && g <= PQB_GRP_128; }
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -93,9 +102,15 @@ pqb_sizes sizes_of(int fmt, int gran, int64_t b, int64_t r, int64_t c) {
   const int64_t n = b * r * c;
   switch (fmt) {
     case PQB_FP8_E4M3:
+    case PQB_FP8_E5M2:
+    case PQB_INT8_SYM:
       s.codes = (size_t)n;
       s.scales = 4 * (size_t)fp8_num_scales(gran, b, r, c);
       if (gran == PQB_TENSOR && n > 0) s.workspace = tensor_workspace(1, b, r * c);
+      break;
+    case PQB_MXFP8:
+      s.codes = (size_t)n;
+      s.scales = (size_t)n / 32;
       break;
     case PQB_MXFP4:
       s.codes = (size_t)n / 2;
@@ -166,7 +181,7 @@ static pqb_status check_quantize(const void* x, int dtype, int64_t batch, int64_
   if (workspace_bytes < need->workspace) return PQB_ERR_WORKSPACE;
   if (!aligned(x, 16) || !aligned(codes, 16) || (need->workspace && !aligned(workspace, 16)))
     return PQB_ERR_ALIGN;
-  if (fmt == PQB_FP8_E4M3 && !aligned(scales, 4)) return PQB_ERR_ALIGN;
+  if (one_byte(fmt) && !aligned(scales, 4)) return PQB_ERR_ALIGN;
   if (fmt == PQB_INT4_ASYM && !aligned(scales, 2)) return PQB_ERR_ALIGN;
   if (fmt == PQB_NVFP4 && !aligned(aux, 4)) return PQB_ERR_ALIGN;
   return PQB_OK;
@@ -185,24 +200,29 @@ pqb_status pqb_quantize(const void* x, pqb_dtype dtype, int64_t batch, int64_t r
   hipStream_t s = (hipStream_t)stream;
   uint8_t* c8 = (uint8_t*)codes;
   switch (fmt) {
-    case PQB_FP8_E4M3: {
+    case PQB_FP8_E4M3:
+    case PQB_FP8_E5M2:
+    case PQB_INT8_SYM: {
       float* sc = (float*)scales;
+      const int el = elem_of(fmt);
       switch (gran) {
         case PQB_TENSOR: {
           const void* xs[1] = {x};
           uint8_t* cs[1] = {c8};
           float* ss[1] = {sc};
           return hip_status(launch_fp8_tensor(xs, bf16, 1, batch, rows * cols, cs, ss,
-                                              (float*)workspace, s));
+                                              (float*)workspace, s, el));
         }
         case PQB_ROW:
-          return hip_status(launch_fp8_row(x, bf16, batch * rows, cols, c8, sc, s));
+          return hip_status(launch_fp8_row(x, bf16, batch * rows, cols, c8, sc, s, el));
         case PQB_BLK_1x128:
-          return hip_status(launch_fp8_1x128(x, bf16, n, c8, sc, s));
+          return hip_status(launch_fp8_1x128(x, bf16, n, c8, sc, s, el));
         default:
-          return hip_status(launch_fp8_128x128(x, bf16, batch, rows, cols, c8, sc, s));
+          return hip_status(launch_fp8_128x128(x, bf16, batch, rows, cols, c8, sc, s, el));
       }
     }
+    case PQB_MXFP8:
+      return hip_status(launch_mxfp8(x, bf16, n, c8, (uint8_t*)scales, s));
     case PQB_MXFP4:
       return hip_status(launch_mxfp4(x, bf16, n, c8, (uint8_t*)scales, s));
     case PQB_NVFP4:
@@ -236,12 +256,14 @@ pqb_status pqb_quantize_batch(const pqb_job* jobs, int64_t njobs, void* stream) 
     const pqb_job& j = jobs[i];
     if (j.batch * j.rows * j.cols == 0) continue;
     MultiJob m{j.x, (uint8_t*)j.codes, j.scales, (uint8_t*)j.aux, j.batch, j.rows, j.cols, 0,
-               j.dtype == PQB_BF16};
-    if (j.fmt == PQB_FP8_E4M3 && j.gran == PQB_ROW) continue;  // launched below
-    if (j.fmt == PQB_FP8_E4M3)
+               j.dtype == PQB_BF16, elem_of(j.fmt)};
+    if (one_byte(j.fmt) && j.gran == PQB_ROW) continue;  // launched below
+    if (one_byte(j.fmt))  // E4M3 or E5M2 (INT8 has only ROW here)
       m.kind = j.gran == PQB_BLK_1x128 ? kMultiFp8Blk : kMultiFp8Tile;
     else if (j.fmt == PQB_MXFP4)
       m.kind = kMultiMx;
+    else if (j.fmt == PQB_MXFP8)
+      m.kind = kMultiMx8;
     else
       m.kind = kMultiInt4;
     fused.push_back(m);
@@ -252,9 +274,9 @@ pqb_status pqb_quantize_batch(const pqb_job* jobs, int64_t njobs, void* stream) 
   }
   for (int64_t i = 0; i < njobs; ++i) {
     const pqb_job& j = jobs[i];
-    if (j.fmt != PQB_FP8_E4M3 || j.gran != PQB_ROW || j.batch * j.rows * j.cols == 0) continue;
+    if (!one_byte(j.fmt) || j.gran != PQB_ROW || j.batch * j.rows * j.cols == 0) continue;
     const hipError_t e = launch_fp8_row(j.x, j.dtype == PQB_BF16, j.batch * j.rows, j.cols,
-                                        (uint8_t*)j.codes, (float*)j.scales, s);
+                                        (uint8_t*)j.codes, (float*)j.scales, s, elem_of(j.fmt));
     if (e != hipSuccess) return PQB_ERR_HIP;
   }
   return PQB_OK;
@@ -272,16 +294,21 @@ pqb_status pqb_dequantize(const void* codes, const void* scales, const void* aux
   const pqb_sizes need = sizes_of(fmt, gran, batch, rows, cols);
   if (!codes || !scales || !out || (need.aux && !aux)) return PQB_ERR_NULL;
   if (!aligned(codes, 16) || !aligned(out, 16)) return PQB_ERR_ALIGN;
-  if (fmt == PQB_FP8_E4M3 && !aligned(scales, 4)) return PQB_ERR_ALIGN;
+  if (one_byte(fmt) && !aligned(scales, 4)) return PQB_ERR_ALIGN;
   if (fmt == PQB_INT4_ASYM && !aligned(scales, 2)) return PQB_ERR_ALIGN;
   if (fmt == PQB_NVFP4 && !aligned(aux, 4)) return PQB_ERR_ALIGN;
-  if (fmt == PQB_FP8_E4M3 && batch * rows > 0 && (cols > 0x7FFFFFFF)) return PQB_ERR_SHAPE;
+  if (one_byte(fmt) && batch * rows > 0 && (cols > 0x7FFFFFFF)) return PQB_ERR_SHAPE;
   const bool bf16 = out_dtype == PQB_BF16;
   hipStream_t s = (hipStream_t)stream;
   switch (fmt) {
     case PQB_FP8_E4M3:
+    case PQB_FP8_E5M2:
+    case PQB_INT8_SYM:
       return hip_status(launch_fp8_dequant((const uint8_t*)codes, (const float*)scales, gran,
-                                           batch, rows, cols, bf16, out, s));
+                                           batch, rows, cols, bf16, out, s, elem_of(fmt)));
+    case PQB_MXFP8:
+      return hip_status(launch_mxfp8_dequant((const uint8_t*)codes, (const uint8_t*)scales, n,
+                                             bf16, out, s));
     case PQB_MXFP4:
       return hip_status(launch_mxfp4_dequant((const uint8_t*)codes, (const uint8_t*)scales, n,
                                              bf16, out, s));
@@ -389,7 +416,15 @@ pqb_status pqb_encode_e4m3(const float* y, int64_t n, uint8_t* out, void* stream
   if (n == 0) return PQB_OK;
   if (!y || !out) return PQB_ERR_NULL;
   if (!aligned(y, 4)) return PQB_ERR_ALIGN;
-  return hip_status(launch_encode_e4m3(y, n, out, (hipStream_t)stream));
+  return hip_status(launch_encode_elem(y, n, out, (hipStream_t)stream, 0));
+}
+
+pqb_status pqb_encode_e5m2(const float* y, int64_t n, uint8_t* out, void* stream) {
+  if (n < 0) return PQB_ERR_SHAPE;
+  if (n == 0) return PQB_OK;
+  if (!y || !out) return PQB_ERR_NULL;
+  if (!aligned(y, 4)) return PQB_ERR_ALIGN;
+  return hip_status(launch_encode_elem(y, n, out, (hipStream_t)stream, 1));
 }
 
 pqb_status pqb_encode_e2m1(const float* y, int64_t n, uint8_t* out, void* stream) {

@@ -179,6 +179,28 @@ __device__ __forceinline__ uint32_t e4m3_bytes4(float a, float b, float c, float
   return cvt_e4m3x2<true>(c, d, w);
 }
 
+// Two values -> two E5M2 bytes (round-to-nearest-even, subnormals kept, sign
+// kept), written into the low (kHi = false) or high 16 bits of `old`.
+template <bool kHi>
+__device__ __forceinline__ uint32_t cvt_e5m2x2(float a, float b, uint32_t old) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, (int)old, kHi);
+}
+
+__device__ __forceinline__ uint32_t e5m2_bytes4(float a, float b, float c, float d) {
+  uint32_t w = cvt_e5m2x2<false>(a, b, as_u(a));
+  return cvt_e5m2x2<true>(c, d, w);
+}
+
+// Four integer-valued floats in [-128, 127] -> four two's-complement bytes:
+// adding 1.5 * 2^23 rounds to an integer (ties to even) and leaves it in the
+// low bits of the sum's pattern.
+constexpr float kRoundInt = 12582912.0f;
+__device__ __forceinline__ uint32_t int8_bytes4(float a, float b, float c, float d) {
+  const uint32_t qa = as_u(a + kRoundInt), qb = as_u(b + kRoundInt);
+  const uint32_t qc = as_u(c + kRoundInt), qd = as_u(d + kRoundInt);
+  return (qa & 0xFFu) | ((qb & 0xFFu) << 8) | ((qc & 0xFFu) << 16) | (qd << 24);
+}
+
 // E2M1 nibble of y (nearest value, ties to the smaller magnitude, sign bit for
 // y < 0, saturating at 6) by table lookup.  The seven decision points 0.25,
 // 0.75, 1.25, 1.75, 2.5, 3.5 and 5 are float32 values whose bit patterns are
@@ -251,6 +273,18 @@ __device__ __forceinline__ f32x2 e4m3x2_decode(uint32_t w) {
 
 __device__ __forceinline__ float e4m3_decode(uint32_t c) {
   return __builtin_amdgcn_cvt_pk_f32_fp8((int)(c & 0xFFu), false)[0];
+}
+
+template <bool kHi>
+__device__ __forceinline__ f32x2 e5m2x2_decode(uint32_t w) {
+  const auto v = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, kHi);
+  return f32x2{v[0], v[1]};
+}
+
+template <bool kHi>
+__device__ __forceinline__ f32x2 int8x2_decode(uint32_t w) {
+  const int sh = kHi ? 16 : 0;
+  return f32x2{(float)((int)(w << (24 - sh)) >> 24), (float)((int)(w << (16 - sh)) >> 24)};
 }
 
 // Eight float32 results stored as float32 or as RNE bf16 at unit u (element 8u).

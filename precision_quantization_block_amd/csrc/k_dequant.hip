@@ -29,7 +29,7 @@ int dq_grid(int64_t nunits) {
 }
 
 // FP8 1x128: unit u's scale is u / 16.
-template <bool kBf16Out>
+template <bool kBf16Out, int kElem>
 __global__ __launch_bounds__(kBlockThreads) void k_dq_fp8_1x128(const uint8_t* __restrict__ codes,
                                                                 const float* __restrict__ scales,
                                                                 int64_t nunits,
@@ -50,7 +50,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_dq_fp8_1x128(const uint8_t* _
     const int64_t u = u0 + k * kWave;
     if (u < nunits) {
       float o[8];
-      fp8_decode8(c[k], s[k], o);
+      fp8_decode8<kElem>(c[k], s[k], o);
       store_out8<kBf16Out>(out, u, o);
     }
   }
@@ -105,6 +105,34 @@ __global__ __launch_bounds__(kBlockThreads) void k_dq_mxfp4(const uint8_t* __res
     const int64_t u = u0 + k * kWave;
     if (u < nunits) {
       mx_expand8<kBf16Out>(c[k], as_f(e[k] << 23), out, u);  // 2^(e - 127), e in [85, 252]
+    }
+  }
+}
+
+// MXFP8: unit u is a quarter of block u / 4; dec(code) * 2^(e - 127) is exact.
+template <bool kBf16Out>
+__global__ __launch_bounds__(kBlockThreads) void k_dq_mxfp8(const uint8_t* __restrict__ codes,
+                                                            const uint8_t* __restrict__ scales,
+                                                            int64_t nunits,
+                                                            void* __restrict__ out) {
+  const int64_t u0 = dq_unit0();
+  uint2 c[kDqTiles];
+  uint32_t e[kDqTiles];
+#pragma unroll
+  for (int k = 0; k < kDqTiles; ++k) {
+    const int64_t u = u0 + k * kWave;
+    if (u < nunits) {
+      c[k] = ld_nt8(codes + u * 8);
+      e[k] = scales[u >> 2];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kDqTiles; ++k) {
+    const int64_t u = u0 + k * kWave;
+    if (u < nunits) {
+      float o[8];
+      fp8_decode8<kE4M3>(c[k], as_f(e[k] << 23), o);  // 2^(e - 127), e in [79, 246]
+      store_out8<kBf16Out>(out, u, o);
     }
   }
 }
@@ -181,15 +209,17 @@ __global__ __launch_bounds__(kBlockThreads) void k_dq_int4(const uint8_t* __rest
 }  // namespace
 
 hipError_t launch_fp8_1x128_dequant(const uint8_t* codes, const float* scales, int64_t n,
-                                    bool out_bf16, void* out, hipStream_t st) {
+                                    bool out_bf16, void* out, hipStream_t st, int elem) {
   const int64_t nl = n / 8;
-  if (out_bf16)
-    hipLaunchKernelGGL(k_dq_fp8_1x128<true>, dim3(dq_grid(nl)), dim3(kBlockThreads), 0, st, codes,
-                       scales, nl, out);
-  else
-    hipLaunchKernelGGL(k_dq_fp8_1x128<false>, dim3(dq_grid(nl)), dim3(kBlockThreads), 0, st,
-                       codes, scales, nl, out);
-  return hipGetLastError();
+  return with_elem(elem, [&](auto e) {
+    constexpr int E = decltype(e)::value;
+    if (out_bf16)
+      hipLaunchKernelGGL((k_dq_fp8_1x128<true, E>), dim3(dq_grid(nl)), dim3(kBlockThreads), 0, st,
+                         codes, scales, nl, out);
+    else
+      hipLaunchKernelGGL((k_dq_fp8_1x128<false, E>), dim3(dq_grid(nl)), dim3(kBlockThreads), 0,
+                         st, codes, scales, nl, out);
+  });
 }
 
 hipError_t launch_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, int64_t n,
@@ -200,6 +230,18 @@ hipError_t launch_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, int
                        scales, nl, out);
   else
     hipLaunchKernelGGL(k_dq_mxfp4<false>, dim3(dq_grid(nl)), dim3(kBlockThreads), 0, st, codes,
+                       scales, nl, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_mxfp8_dequant(const uint8_t* codes, const uint8_t* scales, int64_t n,
+                                bool out_bf16, void* out, hipStream_t st) {
+  const int64_t nl = n / 8;
+  if (out_bf16)
+    hipLaunchKernelGGL(k_dq_mxfp8<true>, dim3(dq_grid(nl)), dim3(kBlockThreads), 0, st, codes,
+                       scales, nl, out);
+  else
+    hipLaunchKernelGGL(k_dq_mxfp8<false>, dim3(dq_grid(nl)), dim3(kBlockThreads), 0, st, codes,
                        scales, nl, out);
   return hipGetLastError();
 }

@@ -47,6 +47,20 @@ inline int grid_cap(int64_t work, int64_t per_block, int64_t cap) {
   return (int)(g < 1 ? 1 : (g > cap ? cap : g));
 }
 
+// MXFP8: one chunk of 8 bf16 (4 float32) tiles per wave.
+template <typename T, int kUnr>
+__global__ __launch_bounds__(kBlockThreads) void k_mxfp8(const T* __restrict__ x, int64_t nunits,
+                                                          uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales) {
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  const int64_t u0 = ((int64_t)blockIdx.x * (kBlockThreads / kWave) + wave) * kUnr * kWave;
+  if (u0 >= nunits) return;
+  if (u0 + kUnr * kWave <= nunits)
+    mx8_chunk<T, kUnr, false>(x, u0, nunits, codes, scales);
+  else
+    mx8_chunk<T, kUnr, true>(x, u0, nunits, codes, scales);
+}
+
 }  // namespace
 
 hipError_t launch_mxfp4(const void* x, bool bf16, int64_t n, uint8_t* codes, uint8_t* scales,
@@ -60,6 +74,19 @@ hipError_t launch_mxfp4(const void* x, bool bf16, int64_t n, uint8_t* codes, uin
                        dim3(kBlockThreads), 0, st, (const uint16_t*)x, nunits, codes, scales);
   else
     hipLaunchKernelGGL((k_mxfp4<float, 4>), dim3(grid_cap(ntiles, 4 * waves, 1 << 30)),
+                       dim3(kBlockThreads), 0, st, (const float*)x, nunits, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_mxfp8(const void* x, bool bf16, int64_t n, uint8_t* codes, uint8_t* scales,
+                        hipStream_t st) {
+  const int64_t nunits = n / 8, ntiles = (nunits + kWave - 1) / kWave;
+  const int64_t waves = kBlockThreads / kWave;
+  if (bf16)
+    hipLaunchKernelGGL((k_mxfp8<uint16_t, 8>), dim3(grid_cap(ntiles, 8 * waves, 1 << 30)),
+                       dim3(kBlockThreads), 0, st, (const uint16_t*)x, nunits, codes, scales);
+  else
+    hipLaunchKernelGGL((k_mxfp8<float, 4>), dim3(grid_cap(ntiles, 4 * waves, 1 << 30)),
                        dim3(kBlockThreads), 0, st, (const float*)x, nunits, codes, scales);
   return hipGetLastError();
 }

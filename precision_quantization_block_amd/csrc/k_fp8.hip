@@ -1,17 +1,21 @@
-// FP8 E4M3 quantize / dequantize kernels: 1x128 blocks, 128x128 tiles, rows,
-// per tensor (the per-chunk bodies are in quant.h).
+// Scaled one-byte codes: FP8 E4M3, FP8 E5M2 and symmetric INT8 with 1x128
+// blocks, 128x128 tiles, rows and (for slices whose length is not a multiple
+// of 8) per tensor; the per-chunk bodies are in quant.h, the chunked per-tensor
+// path in k_twopass.hip.
 //
-// Scale of a scope: s = RN(max(amax, 1e-12) / 448); codes are E4M3(RN(x / s))
-// (page "量化部署实战", section 伪量化实现).  The clamp to +-448 that the page
-// applies before the cast never binds here: |x| <= amax gives |x/s| <= 448 up to
-// one rounding, which still rounds to 448.
+// Scale of a scope: s = RN(max(amax, 1e-12) / M) with M = 448 (E4M3), 57344
+// (E5M2) or 127 (INT8); codes are the element code of RN(x / s) (page "量化部署
+// 实战", section 伪量化实现; the E5M2 row of the low-precision float table and
+// the symmetric INT8 scale on "14. 量化：让每一步搬更少的字节").  The page's
+// clamp to +-M never binds: |x| <= amax gives |x/s| <= M up to one rounding,
+// which still rounds to M.
 #include "launch.h"
 #include "quant.h"
 
 namespace pqb {
 namespace {
 
-template <typename T, int kUnr>
+template <typename T, int kUnr, int kElem>
 __global__ __launch_bounds__(kBlockThreads) void k_fp8_1x128(const T* __restrict__ x,
                                                               int64_t nunits,
                                                               uint8_t* __restrict__ codes,
@@ -20,47 +24,48 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_1x128(const T* __restrict
   for (int64_t t0 = (int64_t)wave_index() * kUnr; t0 * kWave < nunits; t0 += nwaves * kUnr) {
     const int64_t u0 = t0 * kWave;
     if (u0 + kUnr * kWave <= nunits)
-      fp8_1x128_chunk<T, kUnr, false>(x, u0, nunits, codes, scales);
+      fp8_1x128_chunk<T, kUnr, false, kElem>(x, u0, nunits, codes, scales);
     else
-      fp8_1x128_chunk<T, kUnr, true>(x, u0, nunits, codes, scales);
+      fp8_1x128_chunk<T, kUnr, true, kElem>(x, u0, nunits, codes, scales);
   }
 }
 
 constexpr int kTileWaves = 8;  // 512 threads per 128x128 tile: 4 rows of it per lane
 
-template <typename T>
+template <typename T, int kElem>
 __global__ __launch_bounds__(kTileWaves * kWave) void k_fp8_128x128(const T* __restrict__ x,
                                                                      int64_t rows, int64_t cols,
                                                                      int br,
                                                                      uint8_t* __restrict__ codes,
                                                                      float* __restrict__ scales) {
   __shared__ uint32_t red[kTileWaves];
-  fp8_tile_128x128<T, kTileWaves>(x, rows, cols, br, blockIdx.x, codes, scales, red);
+  fp8_tile_128x128<T, kTileWaves, kElem>(x, rows, cols, br, blockIdx.x, codes, scales, red);
 }
 
-template <typename T, int kMaxU>
+template <typename T, int kMaxU, int kElem>
 __global__ __launch_bounds__(kBlockThreads) void k_fp8_row_vec(const T* __restrict__ x,
                                                                 int64_t nrows, int64_t cols,
                                                                 uint8_t* __restrict__ codes,
                                                                 float* __restrict__ scales) {
   const int64_t row = wave_index();
-  if (row < nrows) fp8_row_vec<T, kMaxU>(x, row, cols, codes, scales);  // whole waves
+  if (row < nrows) fp8_row_vec<T, kMaxU, kElem>(x, row, cols, codes, scales);  // whole waves
 }
 
-template <typename T>
+template <typename T, int kElem>
 __global__ __launch_bounds__(kBlockThreads) void k_fp8_row_any(const T* __restrict__ x,
                                                                 int64_t nrows, int64_t cols,
                                                                 uint8_t* __restrict__ codes,
                                                                 float* __restrict__ scales) {
   const int64_t row = wave_index();
-  if (row < nrows) fp8_row_any<T>(x, row, cols, codes, scales);
+  if (row < nrows) fp8_row_any<T, kElem>(x, row, cols, codes, scales);
 }
 
 // ---------------------------------------------------------------------------
-// Per tensor (per batch slice), two passes.  Pass 1: each workgroup writes the
-// amax of its share of a slice to partials[(tensor * batch + b) * P + blockIdx.x].
-// Pass 2: each workgroup reduces the slice's P partials, forms s and quantizes
-// its share.  blockIdx.y = slice, blockIdx.z = tensor (K or V for the KV write).
+// Per tensor for slices whose length is not a multiple of 8 (element-wise).
+// Pass 1: each workgroup writes the amax of its share of a slice to
+// partials[(tensor * batch + b) * P + blockIdx.x].  Pass 2: each workgroup
+// reduces the slice's P partials, forms s and quantizes its share.
+// blockIdx.y = slice, blockIdx.z = tensor (K or V for the KV write).
 // ---------------------------------------------------------------------------
 struct TensorArgs {
   const void* x[2];
@@ -79,37 +84,16 @@ __device__ __forceinline__ uint32_t block_umax(uint32_t m, uint32_t* red) {
   return m;
 }
 
-template <typename T, bool kVec>
+template <typename T>
 __global__ __launch_bounds__(kBlockThreads) void k_amax_partial(TensorArgs a, int64_t per_slice,
                                                                  float* __restrict__ partials) {
   __shared__ uint32_t red[kBlockThreads / kWave];
   const int64_t b = blockIdx.y, P = gridDim.x;
   const T* xs = reinterpret_cast<const T*>(a.x[blockIdx.z]) + b * per_slice;
   uint32_t m = 0;
-  if constexpr (kVec) {
-    const int64_t nunits = per_slice / 8;
-    const int64_t stride = P * kBlockThreads;
-    int64_t u = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
-    for (; u + 3 * stride < nunits; u += 4 * stride) {
-      const Raw8 r0 = load_raw8(xs + u * 8), r1 = load_raw8(xs + (u + stride) * 8);
-      const Raw8 r2 = load_raw8(xs + (u + 2 * stride) * 8);
-      const Raw8 r3 = load_raw8(xs + (u + 3 * stride) * 8);
-      float v[8];
-      widen8(r0, xs, v); m = max(m, as_u(absmax8(v)));
-      widen8(r1, xs, v); m = max(m, as_u(absmax8(v)));
-      widen8(r2, xs, v); m = max(m, as_u(absmax8(v)));
-      widen8(r3, xs, v); m = max(m, as_u(absmax8(v)));
-    }
-    for (; u < nunits; u += stride) {
-      float v[8];
-      widen8(load_raw8(xs + u * 8), xs, v);
-      m = max(m, as_u(absmax8(v)));
-    }
-  } else {
-    for (int64_t i = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x; i < per_slice;
-         i += P * kBlockThreads)
-      m = max(m, as_u(fabsf(ld1(xs + i))));
-  }
+  for (int64_t i = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x; i < per_slice;
+       i += P * kBlockThreads)
+    m = max(m, as_u(fabsf(ld1(xs + i))));
   m = block_umax(m, red);
   if (threadIdx.x == 0) partials[((int64_t)blockIdx.z * gridDim.y + b) * P + blockIdx.x] = as_f(m);
 }
@@ -122,7 +106,7 @@ __device__ __forceinline__ uint32_t reduce_partials(const float* __restrict__ p,
   return block_umax(m, red);
 }
 
-template <typename T, bool kVec>
+template <typename T, int kElem>
 __global__ __launch_bounds__(kBlockThreads) void k_fp8_tensor_quant(TensorArgs a,
                                                                      int64_t per_slice,
                                                                      const float* __restrict__ partials,
@@ -130,36 +114,28 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_tensor_quant(TensorArgs a
   __shared__ uint32_t red[kBlockThreads / kWave];
   const int64_t b = blockIdx.y;
   const int tz = blockIdx.z;
-  const float s = fp8_scale_bits(reduce_partials(partials + ((int64_t)tz * gridDim.y + b) * P, P, red));
+  const float s =
+      fp8_scale_bits<kElem>(reduce_partials(partials + ((int64_t)tz * gridDim.y + b) * P, P, red));
   const float y = recip_rn(s);
   const T* xs = reinterpret_cast<const T*>(a.x[tz]) + b * per_slice;
   uint8_t* cs = a.codes[tz] + b * per_slice;
   const int64_t stride = (int64_t)gridDim.x * kBlockThreads;
-  if constexpr (kVec) {
-    stream_units<T, kStreamLoads>(xs, (int64_t)blockIdx.x * kBlockThreads + threadIdx.x,
-                                  per_slice / 8, stride, [&](const Raw8& r, int64_t u) {
-                                    float v[8];
-                                    widen8(r, xs, v);
-                                    store_codes8(cs + u * 8, fp8_pack8(v, s, y));
-                                  });
-  } else {
-    for (int64_t i = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x; i < per_slice; i += stride)
-      cs[i] = e4m3_byte(div_rn(ld1(xs + i), s, y));
-  }
+  for (int64_t i = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x; i < per_slice; i += stride)
+    cs[i] = elem_byte<kElem>(div_rn(ld1(xs + i), s, y));
   if (blockIdx.x == 0 && threadIdx.x == 0) a.scales[tz][b] = s;
 }
 
 // ---------------------------------------------------------------------------
-// Dequantization: out = dec(code) * s, float32 or RNE bf16.
+// Dequantization of the per-tensor, per-row and 128x128 scopes: out =
+// dec(code) * s, float32 or RNE bf16, one wave per row (rows of all slices in
+// sequence): the row's scale index is formed once per row; only the
+// 128-column block varies.
 // ---------------------------------------------------------------------------
-
 __device__ __forceinline__ uint2 ld_codes8(const uint8_t* p) {
   return *reinterpret_cast<const uint2*>(p);
 }
 
-// Other scopes, one wave per row (rows of all slices in sequence): the row's
-// scale index is formed once per row; only the 128-column block varies.
-template <bool kBf16Out, bool kVec>
+template <bool kBf16Out, bool kVec, int kElem>
 __global__ __launch_bounds__(kBlockThreads) void k_fp8_dequant_rows(const uint8_t* __restrict__ codes,
                                                                      const float* __restrict__ scales,
                                                                      int gran, int64_t nrows_total,
@@ -179,12 +155,14 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_dequant_rows(const uint8_
     if constexpr (kVec) {
       for (int64_t u = lane; u < cols / 8; u += kWave) {
         float o[8];
-        fp8_decode8(ld_codes8(codes + gr * cols + u * 8), scales[si0 + (u >> 4) * tile_stride], o);
+        fp8_decode8<kElem>(ld_codes8(codes + gr * cols + u * 8),
+                           scales[si0 + (u >> 4) * tile_stride], o);
         store_out8<kBf16Out>(out, gr * (cols / 8) + u, o);
       }
     } else {
       for (int64_t c = lane; c < cols; c += kWave) {
-        const float v = e4m3_decode(codes[gr * cols + c]) * scales[si0 + (c >> 7) * tile_stride];
+        const float v = elem_decode2<kElem, false>(codes[gr * cols + c]).x *
+                        scales[si0 + (c >> 7) * tile_stride];
         if constexpr (kBf16Out)
           reinterpret_cast<uint16_t*>(out)[gr * cols + c] = (uint16_t)bf16x2_rne(v, 0.0f);
         else
@@ -194,12 +172,13 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_dequant_rows(const uint8_
   }
 }
 
-__global__ __launch_bounds__(kBlockThreads) void k_encode_e4m3(const float* __restrict__ y,
+template <int kElem>
+__global__ __launch_bounds__(kBlockThreads) void k_encode_elem(const float* __restrict__ y,
                                                                int64_t n,
                                                                uint8_t* __restrict__ out) {
   for (int64_t i = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * kBlockThreads)
-    out[i] = e4m3_byte(y[i]);
+    out[i] = elem_byte<kElem>(y[i]);
 }
 
 inline int blocks_for(int64_t work, int64_t per_block, int64_t cap) {
@@ -223,85 +202,71 @@ int amax_partials_per_slice(int64_t batch, int64_t per_slice, int ntensors) {
 }
 
 hipError_t launch_fp8_1x128(const void* x, bool bf16, int64_t n, uint8_t* codes, float* scales,
-                            hipStream_t st) {
+                            hipStream_t st, int elem) {
   constexpr int kUnr = 4;
   const int64_t nunits = n / 8;
   const int64_t ntiles = (nunits + kWave - 1) / kWave;
   const int grid = blocks_for(ntiles, (int64_t)kUnr * (kBlockThreads / kWave), 1 << 29);
-  if (bf16)
-    hipLaunchKernelGGL((k_fp8_1x128<uint16_t, kUnr>), dim3(grid), dim3(kBlockThreads), 0, st,
-                       (const uint16_t*)x, nunits, codes, scales);
-  else
-    hipLaunchKernelGGL((k_fp8_1x128<float, kUnr>), dim3(grid), dim3(kBlockThreads), 0, st,
-                       (const float*)x, nunits, codes, scales);
-  return hipGetLastError();
+  return with_elem(elem, [&](auto e) {
+    constexpr int E = decltype(e)::value;
+    if (bf16)
+      hipLaunchKernelGGL((k_fp8_1x128<uint16_t, kUnr, E>), dim3(grid), dim3(kBlockThreads), 0, st,
+                         (const uint16_t*)x, nunits, codes, scales);
+    else
+      hipLaunchKernelGGL((k_fp8_1x128<float, kUnr, E>), dim3(grid), dim3(kBlockThreads), 0, st,
+                         (const float*)x, nunits, codes, scales);
+  });
 }
 
 hipError_t launch_fp8_128x128(const void* x, bool bf16, int64_t batch, int64_t rows,
-                              int64_t cols, uint8_t* codes, float* scales, hipStream_t st) {
+                              int64_t cols, uint8_t* codes, float* scales, hipStream_t st,
+                              int elem) {
   const int br = (int)(rows < 128 ? rows : 128);
   const int64_t tiles = batch * (rows / br) * (cols / 128);
-  if (bf16)
-    hipLaunchKernelGGL(k_fp8_128x128<uint16_t>, dim3((unsigned)tiles), dim3(kTileWaves * kWave),
-                       0, st, (const uint16_t*)x, rows, cols, br, codes, scales);
-  else
-    hipLaunchKernelGGL(k_fp8_128x128<float>, dim3((unsigned)tiles), dim3(kTileWaves * kWave), 0,
-                       st, (const float*)x, rows, cols, br, codes, scales);
-  return hipGetLastError();
+  return with_elem(elem, [&](auto e) {
+    constexpr int E = decltype(e)::value;
+    if (bf16)
+      hipLaunchKernelGGL((k_fp8_128x128<uint16_t, E>), dim3((unsigned)tiles),
+                         dim3(kTileWaves * kWave), 0, st, (const uint16_t*)x, rows, cols, br, codes,
+                         scales);
+    else
+      hipLaunchKernelGGL((k_fp8_128x128<float, E>), dim3((unsigned)tiles),
+                         dim3(kTileWaves * kWave), 0, st, (const float*)x, rows, cols, br, codes,
+                         scales);
+  });
 }
 
 hipError_t launch_fp8_row(const void* x, bool bf16, int64_t nrows, int64_t cols, uint8_t* codes,
-                          float* scales, hipStream_t st) {
+                          float* scales, hipStream_t st, int elem) {
   constexpr int kMaxU = 16;  // up to 8192 columns in registers
   const int grid = (int)((nrows + 3) / 4);
   const bool vec = cols % 8 == 0 && cols <= (int64_t)kWave * 8 * kMaxU;
-  if (bf16) {
-    if (vec)
-      hipLaunchKernelGGL((k_fp8_row_vec<uint16_t, kMaxU>), dim3(grid), dim3(kBlockThreads), 0, st,
-                         (const uint16_t*)x, nrows, cols, codes, scales);
-    else
-      hipLaunchKernelGGL(k_fp8_row_any<uint16_t>, dim3(grid), dim3(kBlockThreads), 0, st,
-                         (const uint16_t*)x, nrows, cols, codes, scales);
-  } else {
-    if (vec)
-      hipLaunchKernelGGL((k_fp8_row_vec<float, kMaxU>), dim3(grid), dim3(kBlockThreads), 0, st,
-                         (const float*)x, nrows, cols, codes, scales);
-    else
-      hipLaunchKernelGGL(k_fp8_row_any<float>, dim3(grid), dim3(kBlockThreads), 0, st,
-                         (const float*)x, nrows, cols, codes, scales);
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_amax_partials(const void* const* x, bool bf16, int ntensors, int64_t batch,
-                                int64_t per_slice, float* partials, int P, hipStream_t st) {
-  TensorArgs a{};
-  for (int i = 0; i < ntensors; ++i) a.x[i] = x[i];
-  const dim3 g1(P, (unsigned)batch, ntensors);
-  const bool vec = per_slice % 8 == 0;
-  if (bf16) {
-    if (vec)
-      hipLaunchKernelGGL((k_amax_partial<uint16_t, true>), g1, dim3(kBlockThreads), 0, st, a,
-                         per_slice, partials);
-    else
-      hipLaunchKernelGGL((k_amax_partial<uint16_t, false>), g1, dim3(kBlockThreads), 0, st, a,
-                         per_slice, partials);
-  } else {
-    if (vec)
-      hipLaunchKernelGGL((k_amax_partial<float, true>), g1, dim3(kBlockThreads), 0, st, a,
-                         per_slice, partials);
-    else
-      hipLaunchKernelGGL((k_amax_partial<float, false>), g1, dim3(kBlockThreads), 0, st, a,
-                         per_slice, partials);
-  }
-  return hipGetLastError();
+  return with_elem(elem, [&](auto e) {
+    constexpr int E = decltype(e)::value;
+    if (bf16) {
+      if (vec)
+        hipLaunchKernelGGL((k_fp8_row_vec<uint16_t, kMaxU, E>), dim3(grid), dim3(kBlockThreads), 0,
+                           st, (const uint16_t*)x, nrows, cols, codes, scales);
+      else
+        hipLaunchKernelGGL((k_fp8_row_any<uint16_t, E>), dim3(grid), dim3(kBlockThreads), 0, st,
+                           (const uint16_t*)x, nrows, cols, codes, scales);
+    } else {
+      if (vec)
+        hipLaunchKernelGGL((k_fp8_row_vec<float, kMaxU, E>), dim3(grid), dim3(kBlockThreads), 0,
+                           st, (const float*)x, nrows, cols, codes, scales);
+      else
+        hipLaunchKernelGGL((k_fp8_row_any<float, E>), dim3(grid), dim3(kBlockThreads), 0, st,
+                           (const float*)x, nrows, cols, codes, scales);
+    }
+  });
 }
 
 hipError_t launch_fp8_tensor(const void* const* x, bool bf16, int ntensors, int64_t batch,
                              int64_t per_slice, uint8_t* const* codes, float* const* scales,
-                             float* partials, hipStream_t st) {
+                             float* partials, hipStream_t st, int elem) {
   if (per_slice % 8 == 0)
-    return launch_tensor_fp8(x, bf16, ntensors, batch, per_slice, codes, scales, partials, st);
+    return launch_tensor_fp8(x, bf16, ntensors, batch, per_slice, codes, scales, partials, st,
+                             elem);
   // slices whose length is not a multiple of 8: element-wise grid-stride passes
   TensorArgs a{};
   for (int i = 0; i < ntensors; ++i) {
@@ -310,56 +275,59 @@ hipError_t launch_fp8_tensor(const void* const* x, bool bf16, int ntensors, int6
     a.scales[i] = scales[i];
   }
   const int P = amax_partials_per_slice(batch, per_slice, ntensors);
-  hipError_t e = launch_amax_partials(x, bf16, ntensors, batch, per_slice, partials, P, st);
-  if (e != hipSuccess) return e;
-  const bool vec = per_slice % 8 == 0;
-  // pass 2: about 8 units per thread, at most 1024 workgroups per slice
-  const int q = blocks_for(per_slice / 8, (int64_t)kBlockThreads * 8, 1024);
+  const dim3 g1(P, (unsigned)batch, ntensors);
+  if (bf16)
+    hipLaunchKernelGGL(k_amax_partial<uint16_t>, g1, dim3(kBlockThreads), 0, st, a, per_slice,
+                       partials);
+  else
+    hipLaunchKernelGGL(k_amax_partial<float>, g1, dim3(kBlockThreads), 0, st, a, per_slice,
+                       partials);
+  const hipError_t e1 = hipGetLastError();
+  if (e1 != hipSuccess) return e1;
+  // pass 2: about 8 elements per thread, at most 1024 workgroups per slice
+  const int q = blocks_for(per_slice, (int64_t)kBlockThreads * 8, 1024);
   const dim3 g2(q, (unsigned)batch, ntensors);
-  if (bf16) {
-    if (vec)
-      hipLaunchKernelGGL((k_fp8_tensor_quant<uint16_t, true>), g2, dim3(kBlockThreads), 0, st, a,
+  return with_elem(elem, [&](auto e) {
+    constexpr int E = decltype(e)::value;
+    if (bf16)
+      hipLaunchKernelGGL((k_fp8_tensor_quant<uint16_t, E>), g2, dim3(kBlockThreads), 0, st, a,
                          per_slice, partials, P);
     else
-      hipLaunchKernelGGL((k_fp8_tensor_quant<uint16_t, false>), g2, dim3(kBlockThreads), 0, st,
-                         a, per_slice, partials, P);
-  } else {
-    if (vec)
-      hipLaunchKernelGGL((k_fp8_tensor_quant<float, true>), g2, dim3(kBlockThreads), 0, st, a,
+      hipLaunchKernelGGL((k_fp8_tensor_quant<float, E>), g2, dim3(kBlockThreads), 0, st, a,
                          per_slice, partials, P);
-    else
-      hipLaunchKernelGGL((k_fp8_tensor_quant<float, false>), g2, dim3(kBlockThreads), 0, st, a,
-                         per_slice, partials, P);
-  }
-  return hipGetLastError();
+  });
 }
 
 hipError_t launch_fp8_dequant(const uint8_t* codes, const float* scales, int gran, int64_t batch,
                               int64_t rows, int64_t cols, bool out_bf16, void* out,
-                              hipStream_t st) {
+                              hipStream_t st, int elem) {
   const int64_t n = batch * rows * cols;
   if (gran == 2)  // 1x128: cols % 128 == 0, flat
-    return launch_fp8_1x128_dequant(codes, scales, n, out_bf16, out, st);
+    return launch_fp8_1x128_dequant(codes, scales, n, out_bf16, out, st, elem);
   const int br = (int)(rows < 128 ? rows : 128);
   const int64_t nrows = batch * rows;
   const int grid = blocks_for(nrows, kBlockThreads / kWave, 1 << 16);
   const bool vec = cols % 8 == 0;
-#define PQB_DQ(B, V)                                                                           \
-  hipLaunchKernelGGL((k_fp8_dequant_rows<B, V>), dim3(grid), dim3(kBlockThreads), 0, st, codes, \
-                     scales, gran, nrows, rows, cols, br, out)
-  if (out_bf16) {
-    if (vec) PQB_DQ(true, true); else PQB_DQ(true, false);
-  } else {
-    if (vec) PQB_DQ(false, true); else PQB_DQ(false, false);
-  }
+  return with_elem(elem, [&](auto e) {
+    constexpr int E = decltype(e)::value;
+#define PQB_DQ(B, V)                                                                          \
+  hipLaunchKernelGGL((k_fp8_dequant_rows<B, V, E>), dim3(grid), dim3(kBlockThreads), 0, st,    \
+                     codes, scales, gran, nrows, rows, cols, br, out)
+    if (out_bf16) {
+      if (vec) PQB_DQ(true, true); else PQB_DQ(true, false);
+    } else {
+      if (vec) PQB_DQ(false, true); else PQB_DQ(false, false);
+    }
 #undef PQB_DQ
-  return hipGetLastError();
+  });
 }
 
-hipError_t launch_encode_e4m3(const float* y, int64_t n, uint8_t* out, hipStream_t st) {
-  hipLaunchKernelGGL(k_encode_e4m3, dim3(blocks_for(n, kBlockThreads, 4096)), dim3(kBlockThreads),
-                     0, st, y, n, out);
-  return hipGetLastError();
+hipError_t launch_encode_elem(const float* y, int64_t n, uint8_t* out, hipStream_t st, int elem) {
+  return with_elem(elem, [&](auto e) {
+    constexpr int E = decltype(e)::value;
+    hipLaunchKernelGGL(k_encode_elem<E>, dim3(blocks_for(n, kBlockThreads, 4096)),
+                       dim3(kBlockThreads), 0, st, y, n, out);
+  });
 }
 
 }  // namespace pqb

@@ -1,8 +1,9 @@
 // Fused quantization of several tensors per launch (pqb_quantize_batch).
 //
-// Jobs are grouped by family, one kernel per family: FP8 (1x128 blocks and
-// 128x128 tiles together, 512-thread workgroups because a tile is 8 waves),
-// MXFP4 and INT4 (256-thread workgroups, longer chunks per wave).  Within a
+// Jobs are grouped by family, one kernel per family: FP8 E4M3 / E5M2 (1x128
+// blocks and 128x128 tiles together, 512-thread workgroups because a tile is
+// 8 waves), MXFP4 with MXFP8, and INT4 (256-thread workgroups, longer chunks
+// per wave).  Within a
 // launch every job gets a contiguous range of workgroups; a workgroup finds its
 // job by scanning the prefix table in the kernel arguments (uniform, scalar)
 // and runs that job's body from quant.h with its local workgroup index.  One
@@ -18,7 +19,7 @@
 namespace pqb {
 namespace {
 
-enum : int32_t { kJobFp8Blk = 0, kJobFp8Tile = 1, kJobMx = 2, kJobInt4 = 3 };
+enum : int32_t { kJobFp8Blk = 0, kJobFp8Tile = 1, kJobMx = 2, kJobInt4 = 3, kJobMx8 = 4 };
 enum Family : int { kFamFp8 = 0, kFamMx = 1, kFamInt4 = 2 };
 
 constexpr int kFp8Waves = 8;  // 512 threads: a 128x128 tile holds 4 rows per lane
@@ -42,7 +43,7 @@ struct Job {
   int32_t kind;
   int32_t bf16;
   int32_t br;      // tiles: min(128, rows)
-  int32_t pad;
+  int32_t elem;    // FP8 kinds: kE4M3 or kE5M2
 };
 
 struct MultiArgs {
@@ -64,24 +65,39 @@ __device__ __forceinline__ void flat_job(int64_t local, int64_t nunits, Body bod
     body(u0, std::integral_constant<bool, true>{});
 }
 
+template <typename T, int kElem>
+__device__ __forceinline__ void fp8_job(const Job& jb, const T* x, int64_t local, uint32_t* red) {
+  if (jb.kind == kJobFp8Blk) {
+    flat_job<kFp8Waves, kFp8Unr>(local, jb.nunits, [&](int64_t u0, auto g) {
+      fp8_1x128_chunk<T, kFp8Unr, decltype(g)::value, kElem>(x, u0, jb.nunits, jb.codes,
+                                                              reinterpret_cast<float*>(jb.scales));
+    });
+  } else {
+    fp8_tile_128x128<T, kFp8Waves, kElem>(x, jb.rows, jb.cols, jb.br, local, jb.codes,
+                                          reinterpret_cast<float*>(jb.scales), red);
+  }
+}
+
 template <int kFam, typename T>
 __device__ __forceinline__ void run_job(const Job& jb, int64_t local, uint8_t* lut, uint32_t* red) {
   const T* x = reinterpret_cast<const T*>(jb.x);
   if constexpr (kFam == kFamFp8) {
-    if (jb.kind == kJobFp8Blk) {
-      flat_job<kFp8Waves, kFp8Unr>(local, jb.nunits, [&](int64_t u0, auto g) {
-        fp8_1x128_chunk<T, kFp8Unr, decltype(g)::value>(x, u0, jb.nunits, jb.codes,
-                                                         reinterpret_cast<float*>(jb.scales));
+    if (jb.elem == kE5M2)
+      fp8_job<T, kE5M2>(jb, x, local, red);
+    else
+      fp8_job<T, kE4M3>(jb, x, local, red);
+  } else if constexpr (kFam == kFamMx) {
+    if (jb.kind == kJobMx8) {
+      flat_job<kFp4Waves, kFp4Unr<T>>(local, jb.nunits, [&](int64_t u0, auto g) {
+        mx8_chunk<T, kFp4Unr<T>, decltype(g)::value>(x, u0, jb.nunits, jb.codes,
+                                                      reinterpret_cast<uint8_t*>(jb.scales));
       });
     } else {
-      fp8_tile_128x128<T, kFp8Waves>(x, jb.rows, jb.cols, jb.br, local, jb.codes,
-                                     reinterpret_cast<float*>(jb.scales), red);
+      flat_job<kFp4Waves, kFp4Unr<T>>(local, jb.nunits, [&](int64_t u0, auto g) {
+        mx_chunk<T, kFp4Unr<T>, decltype(g)::value>(x, u0, jb.nunits, jb.codes,
+                                                     reinterpret_cast<uint8_t*>(jb.scales), lut);
+      });
     }
-  } else if constexpr (kFam == kFamMx) {
-    flat_job<kFp4Waves, kFp4Unr<T>>(local, jb.nunits, [&](int64_t u0, auto g) {
-      mx_chunk<T, kFp4Unr<T>, decltype(g)::value>(x, u0, jb.nunits, jb.codes,
-                                                   reinterpret_cast<uint8_t*>(jb.scales), lut);
-    });
   } else {
     flat_job<kFp4Waves, kFp4Unr<T>>(local, jb.nunits, [&](int64_t u0, auto g) {
       int4_chunk<T, kFp4Unr<T>, decltype(g)::value>(x, u0, jb.nunits, jb.codes,
@@ -111,7 +127,7 @@ __global__ __launch_bounds__(kThreads<kFam>) void k_multi(MultiArgs a) {
 }
 
 int family_of(int kind) {
-  return kind == kMultiMx ? kFamMx : kind == kMultiInt4 ? kFamInt4 : kFamFp8;
+  return (kind == kMultiMx || kind == kMultiMx8) ? kFamMx : kind == kMultiInt4 ? kFamInt4 : kFamFp8;
 }
 
 // Workgroups one job needs in its family's kernel; fills the kernel-side job.
@@ -122,6 +138,7 @@ int64_t describe(const MultiJob& m, Job& jb) {
   jb.scales = m.scales;
   jb.aux = m.aux;
   jb.bf16 = m.bf16;
+  jb.elem = m.elem;
   jb.cols = m.cols;
   jb.nunits = m.batch * m.rows * m.cols / 8;
   auto flat_wgs = [&](int waves, int unr) {
@@ -140,6 +157,9 @@ int64_t describe(const MultiJob& m, Job& jb) {
       return m.batch * (m.rows / jb.br) * (m.cols / 128);
     case kMultiMx:
       jb.kind = kJobMx;
+      return flat_wgs(kFp4Waves, fp4_unr);
+    case kMultiMx8:
+      jb.kind = kJobMx8;
       return flat_wgs(kFp4Waves, fp4_unr);
     default:
       jb.kind = kJobInt4;

@@ -155,6 +155,7 @@ __device__ __forceinline__ uint32_t reduce_row(const float* __restrict__ p, int 
   return m;
 }
 
+template <int kElem>
 __global__ __launch_bounds__(kFinThreads) void k_tp_finalize_fp8(TpArgs a, TpGeo g,
                                                                  const float* __restrict__ partials,
                                                                  float* __restrict__ fin) {
@@ -165,7 +166,8 @@ __global__ __launch_bounds__(kFinThreads) void k_tp_finalize_fp8(TpArgs a, TpGeo
   const int G = groups_of(a, g, tz);
   float* sc = reinterpret_cast<float*>(a.scales[tz]);
   for (int grp = 0; grp < G; ++grp) {
-    const float s = fp8_scale_bits(reduce_row(partials + (slot * g.G + grp) * g.W, g.W, red));
+    const float s =
+        fp8_scale_bits<kElem>(reduce_row(partials + (slot * g.G + grp) * g.W, g.W, red));
     if (threadIdx.x == 0) {
       fin[slot * g.G + grp] = s;
       sc[b * G + grp] = s;
@@ -209,7 +211,7 @@ __device__ __forceinline__ uint2 fp8_pack8_clamped(const float v[8], float s, fl
   return make_uint2(e4m3_bytes4(q[0], q[1], q[2], q[3]), e4m3_bytes4(q[4], q[5], q[6], q[7]));
 }
 
-template <typename T, int kMode, bool kGuard>
+template <typename T, int kMode, bool kGuard, int kElem>
 __device__ __forceinline__ void fp8_tp_chunk(const T* __restrict__ xs, int64_t u0, int64_t nunits,
                                              uint8_t* __restrict__ cs, float s, float y,
                                              const float* ss, const float* ys, const TpGeo& g) {
@@ -226,19 +228,19 @@ __device__ __forceinline__ void fp8_tp_chunk(const T* __restrict__ xs, int64_t u
     uint2 w;
     if constexpr (kMode == kKvHead) {
       const int h = col.head();
-      w = fp8_pack8(v, ss[h], ys[h]);
+      w = fp8_pack8<kElem>(v, ss[h], ys[h]);
       col.next();
     } else if constexpr (kMode == kKvStatic) {
       w = fp8_pack8_clamped(v, s, y, lim);
     } else {
-      w = fp8_pack8(v, s, y);
+      w = fp8_pack8<kElem>(v, s, y);
     }
     const int64_t u = u0 + k * kWave + lane;
     if (!kGuard || u < nunits) store_codes8(cs + u * 8, w);
   }
 }
 
-template <typename T>
+template <typename T, int kElem>
 __global__ __launch_bounds__(kBlockThreads) void k_tp_fp8(TpArgs a, TpGeo g,
                                                           const float* __restrict__ fin) {
   constexpr int U = kChunkUnr<T>;
@@ -266,16 +268,16 @@ __global__ __launch_bounds__(kBlockThreads) void k_tp_fp8(TpArgs a, TpGeo g,
   const bool full = u0 + U * kWave <= nunits;
   switch (mode) {
     case kKvHead:
-      if (full) fp8_tp_chunk<T, kKvHead, false>(xs, u0, nunits, cs, s, y, ss, ys, g);
-      else fp8_tp_chunk<T, kKvHead, true>(xs, u0, nunits, cs, s, y, ss, ys, g);
+      if (full) fp8_tp_chunk<T, kKvHead, false, kElem>(xs, u0, nunits, cs, s, y, ss, ys, g);
+      else fp8_tp_chunk<T, kKvHead, true, kElem>(xs, u0, nunits, cs, s, y, ss, ys, g);
       break;
     case kKvStatic:
-      if (full) fp8_tp_chunk<T, kKvStatic, false>(xs, u0, nunits, cs, s, y, ss, ys, g);
-      else fp8_tp_chunk<T, kKvStatic, true>(xs, u0, nunits, cs, s, y, ss, ys, g);
+      if (full) fp8_tp_chunk<T, kKvStatic, false, kElem>(xs, u0, nunits, cs, s, y, ss, ys, g);
+      else fp8_tp_chunk<T, kKvStatic, true, kElem>(xs, u0, nunits, cs, s, y, ss, ys, g);
       break;
     default:
-      if (full) fp8_tp_chunk<T, kKvLayer, false>(xs, u0, nunits, cs, s, y, ss, ys, g);
-      else fp8_tp_chunk<T, kKvLayer, true>(xs, u0, nunits, cs, s, y, ss, ys, g);
+      if (full) fp8_tp_chunk<T, kKvLayer, false, kElem>(xs, u0, nunits, cs, s, y, ss, ys, g);
+      else fp8_tp_chunk<T, kKvLayer, true, kElem>(xs, u0, nunits, cs, s, y, ss, ys, g);
   }
 }
 
@@ -318,7 +320,7 @@ uint32_t head_magic(int64_t head_units) {
 }
 
 hipError_t launch_tp(const TpArgs& a, int nt, bool bf16, const TpGeo& g, bool nv, float* ws,
-                     hipStream_t st) {
+                     hipStream_t st, int elem = kE4M3) {
   float* partials = ws;
   float* fin = ws + (int64_t)nt * g.slices * g.G * g.W;
   bool dynamic = false;
@@ -335,9 +337,12 @@ hipError_t launch_tp(const TpArgs& a, int nt, bool bf16, const TpGeo& g, bool nv
       hipLaunchKernelGGL(k_tp_finalize_nv, dim3((unsigned)g.slices, 1), dim3(kFinThreads), 0,
                          st, a, g, partials, fin);
     else
-      hipLaunchKernelGGL(k_tp_finalize_fp8, dim3((unsigned)g.slices, (unsigned)nt),
-                         dim3(kFinThreads), 0, st, a, g, partials, fin);
-    e = hipGetLastError();
+      e = with_elem(elem, [&](auto el) {
+        hipLaunchKernelGGL(k_tp_finalize_fp8<decltype(el)::value>,
+                           dim3((unsigned)g.slices, (unsigned)nt), dim3(kFinThreads), 0, st, a, g,
+                           partials, fin);
+      });
+    if (e == hipSuccess) e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (nv) {
@@ -346,10 +351,13 @@ hipError_t launch_tp(const TpArgs& a, int nt, bool bf16, const TpGeo& g, bool nv
     else
       hipLaunchKernelGGL(k_tp_nv<float>, grid, dim3(kBlockThreads), 0, st, a, g, fin);
   } else {
-    if (bf16)
-      hipLaunchKernelGGL(k_tp_fp8<uint16_t>, grid, dim3(kBlockThreads), 0, st, a, g, fin);
-    else
-      hipLaunchKernelGGL(k_tp_fp8<float>, grid, dim3(kBlockThreads), 0, st, a, g, fin);
+    return with_elem(elem, [&](auto el) {
+      constexpr int E = decltype(el)::value;
+      if (bf16)
+        hipLaunchKernelGGL((k_tp_fp8<uint16_t, E>), grid, dim3(kBlockThreads), 0, st, a, g, fin);
+      else
+        hipLaunchKernelGGL((k_tp_fp8<float, E>), grid, dim3(kBlockThreads), 0, st, a, g, fin);
+    });
   }
   return hipGetLastError();
 }
@@ -366,7 +374,7 @@ size_t twopass_workspace_bytes(int ntensors, int64_t slices, int64_t per_slice, 
 
 hipError_t launch_tensor_fp8(const void* const* x, bool bf16, int ntensors, int64_t slices,
                              int64_t per_slice, uint8_t* const* codes, float* const* scales,
-                             float* ws, hipStream_t st) {
+                             float* ws, hipStream_t st, int elem) {
   TpArgs a{};
   for (int i = 0; i < ntensors; ++i) {
     a.x[i] = x[i];
@@ -381,7 +389,7 @@ hipError_t launch_tensor_fp8(const void* const* x, bool bf16, int ntensors, int6
   g.G = 1;
   g.row_units = 1;
   g.head_magic = 0;
-  return launch_tp(a, ntensors, bf16, g, false, ws, st);
+  return launch_tp(a, ntensors, bf16, g, false, ws, st, elem);
 }
 
 hipError_t launch_nvfp4(const void* x, bool bf16, int64_t batch, int64_t per_slice,

@@ -18,25 +18,31 @@ hipError_t launch_amax_partials(const void* const* x, bool bf16, int ntensors, i
                                 int64_t per_slice, float* partials, int P, hipStream_t st);
 
 // ---- FP8 E4M3 -------------------------------------------------------------
+// `elem`: 0 E4M3, 1 E5M2, 2 INT8 (the Elem kinds of quant.h).
 hipError_t launch_fp8_1x128(const void* x, bool bf16, int64_t n, uint8_t* codes, float* scales,
-                            hipStream_t st);
+                            hipStream_t st, int elem = 0);
 hipError_t launch_fp8_128x128(const void* x, bool bf16, int64_t batch, int64_t rows,
-                              int64_t cols, uint8_t* codes, float* scales, hipStream_t st);
+                              int64_t cols, uint8_t* codes, float* scales, hipStream_t st,
+                              int elem = 0);
 hipError_t launch_fp8_row(const void* x, bool bf16, int64_t nrows, int64_t cols, uint8_t* codes,
-                          float* scales, hipStream_t st);
+                          float* scales, hipStream_t st, int elem = 0);
 // Per-tensor over `ntensors` tensors (1, or 2 for K and V) of `batch` slices.
 hipError_t launch_fp8_tensor(const void* const* x, bool bf16, int ntensors, int64_t batch,
                              int64_t per_slice, uint8_t* const* codes, float* const* scales,
-                             float* partials, hipStream_t st);
+                             float* partials, hipStream_t st, int elem = 0);
 hipError_t launch_fp8_1x128_dequant(const uint8_t* codes, const float* scales, int64_t n,
-                                    bool out_bf16, void* out, hipStream_t st);
+                                    bool out_bf16, void* out, hipStream_t st, int elem = 0);
 hipError_t launch_fp8_dequant(const uint8_t* codes, const float* scales, int gran, int64_t batch,
                               int64_t rows, int64_t cols, bool out_bf16, void* out,
-                              hipStream_t st);
+                              hipStream_t st, int elem = 0);
 
 // ---- MXFP4 / NVFP4 ----------------------------------------------------------
 hipError_t launch_mxfp4(const void* x, bool bf16, int64_t n, uint8_t* codes, uint8_t* scales,
                         hipStream_t st);
+hipError_t launch_mxfp8(const void* x, bool bf16, int64_t n, uint8_t* codes, uint8_t* scales,
+                        hipStream_t st);
+hipError_t launch_mxfp8_dequant(const uint8_t* codes, const uint8_t* scales, int64_t n,
+                                bool out_bf16, void* out, hipStream_t st);
 hipError_t launch_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, int64_t n,
                                 bool out_bf16, void* out, hipStream_t st);
 hipError_t launch_nvfp4(const void* x, bool bf16, int64_t batch, int64_t per_slice,
@@ -54,7 +60,7 @@ hipError_t launch_int4_dequant(const uint8_t* codes, const uint16_t* scales, con
 // ---- fused multi-tensor launch ----------------------------------------------
 // Jobs of the one-pass formats, fused into launches of up to kMaxBatchJobs.
 constexpr int kMaxBatchJobs = 24;
-enum MultiKind { kMultiFp8Blk = 0, kMultiFp8Tile = 1, kMultiMx = 2, kMultiInt4 = 3 };
+enum MultiKind { kMultiFp8Blk = 0, kMultiFp8Tile = 1, kMultiMx = 2, kMultiInt4 = 3, kMultiMx8 = 4 };
 struct MultiJob {
   const void* x;
   uint8_t* codes;
@@ -63,6 +69,7 @@ struct MultiJob {
   int64_t batch, rows, cols;
   int kind;
   bool bf16;
+  int elem;  // FP8 kinds: kE4M3 or kE5M2
 };
 hipError_t launch_multi(const MultiJob* jobs, int njobs, hipStream_t st);
 
@@ -73,7 +80,7 @@ size_t twopass_workspace_bytes(int ntensors, int64_t slices, int64_t per_slice, 
                                bool nv);
 hipError_t launch_tensor_fp8(const void* const* x, bool bf16, int ntensors, int64_t slices,
                              int64_t per_slice, uint8_t* const* codes, float* const* scales,
-                             float* ws, hipStream_t st);
+                             float* ws, hipStream_t st, int elem = 0);
 
 // FP8 KV-cache write with a scale mode per tensor: x is [layers, tokens, heads,
 // head_dim]; scales [layers] (LAYER; STATIC: read) or [layers, heads] (HEAD).
@@ -91,7 +98,7 @@ hipError_t launch_kv_fp8(const KvTensor* t, int ntensors, bool bf16, int64_t lay
                          hipStream_t st);
 
 // ---- element codecs ---------------------------------------------------------
-hipError_t launch_encode_e4m3(const float* y, int64_t n, uint8_t* out, hipStream_t st);
+hipError_t launch_encode_elem(const float* y, int64_t n, uint8_t* out, hipStream_t st, int elem);
 hipError_t launch_encode_e2m1(const float* y, int64_t n, uint8_t* out, hipStream_t st);
 
 }  // namespace pqb

@@ -22,17 +22,72 @@ constexpr float kRound = 12582912.0f;  // 1.5 * 2^23: adding it rounds |q| < 2^2
 // amax gives |x/s| <= 448 up to one rounding, which still rounds to 448.
 // ---------------------------------------------------------------------------
 
-// s from the bit pattern of a scope's amax (a non-negative float).
-__device__ __forceinline__ float fp8_scale_bits(uint32_t amax_bits) {
-  return div_const(as_f(max(amax_bits, kAmaxFloorBits)), 448.0f, kInv448);
+// ---------------------------------------------------------------------------
+// Element formats of the scaled one-byte codes.  All share the scopes (per
+// tensor, row, 1x128, 128x128 tile) and s = RN(max(amax, 1e-12) / M):
+//   kE4M3  M = 448    code E4M3(RN(x / s))               (page "量化部署实战")
+//   kE5M2  M = 57344  code E5M2(RN(x / s))               (E5M2 row of the
+//          low-precision float table, "14. 量化：让每一步搬更少的字节")
+//   kI8    M = 127    code rint(RN(x / s)) as int8       (symmetric INT8,
+//          "14. 量化：让每一步搬更少的字节", 量化在做什么)
+// |x| <= amax keeps |x / s| <= M up to one rounding, which still rounds to M,
+// so no clamp is needed.  RN(a / M) uses one correction with RN(1/M); a CPU
+// check found it equal to IEEE division for every significand in three
+// binades for each M.
+// ---------------------------------------------------------------------------
+enum Elem : int { kE4M3 = 0, kE5M2 = 1, kI8 = 2 };
+
+template <int kElem>
+struct ElemMax;
+template <>
+struct ElemMax<kE4M3> {
+  static constexpr float m = 448.0f, inv = 1.0f / 448.0f;
+};
+template <>
+struct ElemMax<kE5M2> {
+  static constexpr float m = 57344.0f, inv = 1.0f / 57344.0f;
+};
+template <>
+struct ElemMax<kI8> {
+  static constexpr float m = 127.0f, inv = 1.0f / 127.0f;
+};
+
+// Host side: calls f(std::integral_constant<int, kElem>) for a runtime element
+// kind and returns the launch status.
+template <typename F>
+inline hipError_t with_elem(int elem, F f) {
+  switch (elem) {
+    case kE4M3: f(std::integral_constant<int, kE4M3>{}); break;
+    case kE5M2: f(std::integral_constant<int, kE5M2>{}); break;
+    case kI8: f(std::integral_constant<int, kI8>{}); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
-// Eight values -> eight E4M3 codes (two dwords) with scale s and y = RN(1/s).
+template <int kElem>
+__device__ __forceinline__ uint32_t elem_bytes4(float a, float b, float c, float d) {
+  if constexpr (kElem == kE5M2)
+    return e5m2_bytes4(a, b, c, d);
+  else if constexpr (kElem == kI8)
+    return int8_bytes4(a, b, c, d);
+  else
+    return e4m3_bytes4(a, b, c, d);
+}
+
+// s from the bit pattern of a scope's amax (a non-negative float).
+template <int kElem = kE4M3>
+__device__ __forceinline__ float fp8_scale_bits(uint32_t amax_bits) {
+  return div_const(as_f(max(amax_bits, kAmaxFloorBits)), ElemMax<kElem>::m, ElemMax<kElem>::inv);
+}
+
+// Eight values -> eight codes (two dwords) with scale s and y = RN(1/s).
+template <int kElem = kE4M3>
 __device__ __forceinline__ uint2 fp8_pack8(const float v[8], float s, float y) {
-  const uint32_t w0 = e4m3_bytes4(div_rn(v[0], s, y), div_rn(v[1], s, y), div_rn(v[2], s, y),
-                                  div_rn(v[3], s, y));
-  const uint32_t w1 = e4m3_bytes4(div_rn(v[4], s, y), div_rn(v[5], s, y), div_rn(v[6], s, y),
-                                  div_rn(v[7], s, y));
+  const uint32_t w0 = elem_bytes4<kElem>(div_rn(v[0], s, y), div_rn(v[1], s, y),
+                                         div_rn(v[2], s, y), div_rn(v[3], s, y));
+  const uint32_t w1 = elem_bytes4<kElem>(div_rn(v[4], s, y), div_rn(v[5], s, y),
+                                         div_rn(v[6], s, y), div_rn(v[7], s, y));
   return make_uint2(w0, w1);
 }
 
@@ -49,8 +104,9 @@ __device__ __forceinline__ float ld1<float>(const float* p) {
   return *p;
 }
 
-__device__ __forceinline__ uint8_t e4m3_byte(float q) {
-  return (uint8_t)(cvt_e4m3x2<false>(q, 0.0f, 0u) & 0xFFu);
+template <int kElem = kE4M3>
+__device__ __forceinline__ uint8_t elem_byte(float q) {
+  return (uint8_t)(elem_bytes4<kElem>(q, 0.0f, 0.0f, 0.0f) & 0xFFu);
 }
 
 template <typename T, int kUnr, bool kGuard>
@@ -81,7 +137,7 @@ __device__ __forceinline__ void stream_units(const T* __restrict__ xs, int64_t u
 }
 
 // 1x128 blocks: a block is 16 lanes x 8 elements, one DPP row.
-template <typename T, int kUnr, bool kGuard>
+template <typename T, int kUnr, bool kGuard, int kElem = kE4M3>
 __device__ __forceinline__ void fp8_1x128_chunk(const T* __restrict__ x, int64_t u0, int64_t nunits,
                                                 uint8_t* __restrict__ codes,
                                                 float* __restrict__ scales) {
@@ -92,9 +148,9 @@ __device__ __forceinline__ void fp8_1x128_chunk(const T* __restrict__ x, int64_t
   for (int k = 0; k < kUnr; ++k) {
     float v[8];
     widen8(raw[k], x, v);
-    const float s = fp8_scale_bits(group_umax<16>(as_u(absmax8(v))));
+    const float s = fp8_scale_bits<kElem>(group_umax<16>(as_u(absmax8(v))));
     const float y = recip_rn(s);
-    const uint2 w = fp8_pack8(v, s, y);
+    const uint2 w = fp8_pack8<kElem>(v, s, y);
     const int64_t u = u0 + k * kWave + lane;
     if (!kGuard || u < nunits) {
       store_codes8(codes + u * 8, w);
@@ -107,7 +163,7 @@ __device__ __forceinline__ void fp8_1x128_chunk(const T* __restrict__ x, int64_t
 // 8).  Lane l of wave w covers unit (l % 16) of tile rows w*4 + l/16 + 4*kWaves*k,
 // k < 32 / kWaves; the tile's amax is reduced through DPP, a cross-row shuffle
 // and LDS (`red`, kWaves words).  All threads of the workgroup must call it.
-template <typename T, int kWaves>
+template <typename T, int kWaves, int kElem = kE4M3>
 __device__ __forceinline__ void fp8_tile_128x128(const T* __restrict__ x, int64_t rows,
                                                  int64_t cols, int br, int64_t t,
                                                  uint8_t* __restrict__ codes,
@@ -137,21 +193,21 @@ __device__ __forceinline__ void fp8_tile_128x128(const T* __restrict__ x, int64_
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < kWaves; ++i) m = max(m, red[i]);
-  const float s = fp8_scale_bits(m);
+  const float s = fp8_scale_bits<kElem>(m);
   const float y = recip_rn(s);
 #pragma unroll
   for (int k = 0; k < kRowsPerLane; ++k) {
     const int r = r0 + kRowStep * k;
     float v[8];
     widen8(raw[k], x, v);
-    const uint2 w = fp8_pack8(v, s, y);
+    const uint2 w = fp8_pack8<kElem>(v, s, y);
     if (r < br) store_codes8(codes + base + (int64_t)r * cols, w);
   }
   if (threadIdx.x == 0) scales[t] = s;
 }
 
 // One row per wave, held in registers (cols % 8 == 0, cols <= 512 * kMaxU).
-template <typename T, int kMaxU>
+template <typename T, int kMaxU, int kElem = kE4M3>
 __device__ __forceinline__ void fp8_row_vec(const T* __restrict__ x, int64_t row, int64_t cols,
                                             uint8_t* __restrict__ codes,
                                             float* __restrict__ scales) {
@@ -171,21 +227,21 @@ __device__ __forceinline__ void fp8_row_vec(const T* __restrict__ x, int64_t row
     widen8(raw[k], x, v);
     m = max(m, as_u(absmax8(v)));
   }
-  const float s = fp8_scale_bits(wave_umax(m));
+  const float s = fp8_scale_bits<kElem>(wave_umax(m));
   const float y = recip_rn(s);
 #pragma unroll
   for (int k = 0; k < kMaxU; ++k) {
     const int64_t u = (int64_t)k * kWave + lane;
     float v[8];
     widen8(raw[k], x, v);
-    const uint2 w = fp8_pack8(v, s, y);
+    const uint2 w = fp8_pack8<kElem>(v, s, y);
     if (u < upr) store_codes8(codes + row * cols + u * 8, w);
   }
   if (lane == 0) scales[row] = s;
 }
 
 // One row per wave, any width, element-wise (the second read hits the caches).
-template <typename T>
+template <typename T, int kElem = kE4M3>
 __device__ __forceinline__ void fp8_row_any(const T* __restrict__ x, int64_t row, int64_t cols,
                                             uint8_t* __restrict__ codes,
                                             float* __restrict__ scales) {
@@ -193,10 +249,10 @@ __device__ __forceinline__ void fp8_row_any(const T* __restrict__ x, int64_t row
   const T* xr = x + row * cols;
   uint32_t m = 0;
   for (int64_t c = lane; c < cols; c += kWave) m = max(m, as_u(fabsf(ld1(xr + c))));
-  const float s = fp8_scale_bits(wave_umax(m));
+  const float s = fp8_scale_bits<kElem>(wave_umax(m));
   const float y = recip_rn(s);
   for (int64_t c = lane; c < cols; c += kWave)
-    codes[row * cols + c] = e4m3_byte(div_rn(ld1(xr + c), s, y));
+    codes[row * cols + c] = elem_byte<kElem>(div_rn(ld1(xr + c), s, y));
   if (lane == 0) scales[row] = s;
 }
 
@@ -287,10 +343,21 @@ __device__ __forceinline__ void nv_chunk(const T* __restrict__ xs, int64_t u0, i
 // ---------------------------------------------------------------------------
 // Decoders shared by the dequantization kernels.
 // ---------------------------------------------------------------------------
-// Eight E4M3 codes (two dwords) -> eight values times s.
+// Eight codes (two dwords) -> eight values times s.
+template <int kElem, bool kHi>
+__device__ __forceinline__ f32x2 elem_decode2(uint32_t w) {
+  if constexpr (kElem == kE5M2)
+    return e5m2x2_decode<kHi>(w);
+  else if constexpr (kElem == kI8)
+    return int8x2_decode<kHi>(w);
+  else
+    return e4m3x2_decode<kHi>(w);
+}
+
+template <int kElem = kE4M3>
 __device__ __forceinline__ void fp8_decode8(uint2 w, float s, float o[8]) {
-  const f32x2 a = e4m3x2_decode<false>(w.x), b = e4m3x2_decode<true>(w.x);
-  const f32x2 c = e4m3x2_decode<false>(w.y), d = e4m3x2_decode<true>(w.y);
+  const f32x2 a = elem_decode2<kElem, false>(w.x), b = elem_decode2<kElem, true>(w.x);
+  const f32x2 c = elem_decode2<kElem, false>(w.y), d = elem_decode2<kElem, true>(w.y);
   o[0] = a.x * s; o[1] = a.y * s; o[2] = b.x * s; o[3] = b.y * s;
   o[4] = c.x * s; o[5] = c.y * s; o[6] = d.x * s; o[7] = d.y * s;
 }
@@ -301,6 +368,41 @@ __device__ __forceinline__ float e2m1_value(uint32_t nib) {
   // m >= 2: 2^(m/2 - 1) * (1 + (m & 1) / 2); m == 1: 0.5; m == 0: 0
   uint32_t b = m >= 2u ? ((((m >> 1) + 126u) << 23) | ((m & 1u) << 22)) : (m ? 0x3F000000u : 0u);
   return as_f(b | ((nib & 8u) << 28));
+}
+
+// ---------------------------------------------------------------------------
+// MXFP8 (32-element blocks, E8M0 scale, E4M3 elements; pages "LLM 推理优化 ·
+// 量化学习笔记" §4.2 / §4.5): 2^X with X = floor(log2 max(amax, 1e-12)) - 8
+// (E4M3's largest exponent is 8, as 2 is E2M1's for MXFP4); codes
+// E4M3(clamp(x * 2^-X, +-448)), where x * 2^-X is exact and the block maximum
+// lands in [256, 512), so the clamp binds for large significands.  A block is 4
+// lanes x 8 elements; the scale byte is X + 127.
+// ---------------------------------------------------------------------------
+template <typename T, int kUnr, bool kGuard>
+__device__ __forceinline__ void mx8_chunk(const T* __restrict__ x, int64_t u0, int64_t nunits,
+                                          uint8_t* __restrict__ codes,
+                                          uint8_t* __restrict__ scales) {
+  const int lane = threadIdx.x & (kWave - 1);
+  Raw8 raw[kUnr];
+  load_chunk<T, kUnr, kGuard>(x, u0, nunits, raw);
+#pragma unroll
+  for (int k = 0; k < kUnr; ++k) {
+    float v[8];
+    widen8(raw[k], x, v);
+    const uint32_t a = max(group_umax<4>(as_u(absmax8(v))), kAmaxFloorBits);
+    const uint32_t ef = a >> 23;                // biased exponent of a normal a
+    const float mul = as_f((262u - ef) << 23);  // 2^-X with X = ef - 135
+    float q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = __builtin_amdgcn_fmed3f(v[i] * mul, -448.0f, 448.0f);
+    const uint2 w = make_uint2(e4m3_bytes4(q[0], q[1], q[2], q[3]),
+                               e4m3_bytes4(q[4], q[5], q[6], q[7]));
+    const int64_t u = u0 + k * kWave + lane;
+    if (!kGuard || u < nunits) {
+      store_codes8(codes + u * 8, w);
+      if ((lane & 3) == 0) scales[u >> 2] = (uint8_t)(ef - 8u);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -23,9 +23,11 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libpqb.so")
 
 F32, BF16 = 0, 1
-FORMATS = {"fp8_e4m3": 0, "mxfp4": 1, "nvfp4": 2, "int4_asym": 3}
+FORMATS = {"fp8_e4m3": 0, "mxfp4": 1, "nvfp4": 2, "int4_asym": 3, "fp8_e5m2": 4, "mxfp8": 5,
+           "int8_sym": 6}
 GRANS = {"tensor": 0, "row": 1, "1x128": 2, "128x128": 3, "blk32": 4, "blk16": 5, "grp128": 6}
-DEFAULT_GRAN = {"mxfp4": "blk32", "nvfp4": "blk16", "int4_asym": "grp128"}
+DEFAULT_GRAN = {"mxfp4": "blk32", "nvfp4": "blk16", "int4_asym": "grp128", "mxfp8": "blk32",
+                "int8_sym": "row"}
 
 _lib = None
 
@@ -68,10 +70,11 @@ def lib():
         L.pqb_kv_workspace_bytes_ex.restype = SZ
         L.pqb_kv_write_fp8_ex.argtypes = [P, P, I, I64, I64, I64, I64, I, I, P, P, P, P, P, SZ, P]
         L.pqb_encode_e4m3.argtypes = [P, I64, P, P]
+        L.pqb_encode_e5m2.argtypes = [P, I64, P, P]
         L.pqb_encode_e2m1.argtypes = [P, I64, P, P]
         for f in ("pqb_query_sizes", "pqb_quantize", "pqb_quantize_batch", "pqb_dequantize",
                   "pqb_kv_write_fp8", "pqb_kv_write_fp8_ex",
-                  "pqb_encode_e4m3", "pqb_encode_e2m1"):
+                  "pqb_encode_e4m3", "pqb_encode_e5m2", "pqb_encode_e2m1"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -133,7 +136,8 @@ class Quantized:
 
 
 def _scale_dtype(fmt: str):
-    return {"fp8_e4m3": torch.float32, "mxfp4": torch.uint8, "nvfp4": torch.uint8,
+    return {"fp8_e4m3": torch.float32, "fp8_e5m2": torch.float32, "int8_sym": torch.float32,
+            "mxfp4": torch.uint8, "mxfp8": torch.uint8, "nvfp4": torch.uint8,
             "int4_asym": torch.bfloat16}[fmt]
 
 
@@ -279,6 +283,13 @@ def kv_write_fp8_ex(k: torch.Tensor | None, v: torch.Tensor | None, k_mode="laye
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev)),
         "kv_write_fp8_ex")
     return codes[0], codes[1], scales[0], scales[1]
+
+
+def encode_e5m2(y: torch.Tensor) -> torch.Tensor:
+    y = _dev_tensor(y, "y", (torch.float32,))
+    out = torch.empty(y.shape, dtype=torch.uint8, device=y.device)
+    _check(lib().pqb_encode_e5m2(_ptr(y), y.numel(), _ptr(out), _stream(y.device)), "encode_e5m2")
+    return out
 
 
 def encode_e4m3(y: torch.Tensor) -> torch.Tensor:

@@ -232,3 +232,28 @@ def test_head_index_by_multiply_high_is_exact():
     heads, hu = 65536, 65535
     c = np.arange(heads * hu - 100000, heads * hu, dtype=np.uint64)
     assert not np.array_equal(heads_of(c, hu), c // np.uint64(hu))
+
+
+def test_variant_sizes_and_pairs(L):
+    # E5M2 sizes equal E4M3's; INT8 has per-tensor and per-row scopes only;
+    # MXFP8 stores one byte per element and one E8M0 byte per 32
+    for gran in ("tensor", "row", "1x128", "128x128"):
+        assert pqb.query_sizes("fp8_e5m2", gran, 2, 256, 384) == \
+            pqb.query_sizes("fp8_e4m3", gran, 2, 256, 384)
+    assert pqb.query_sizes("int8_sym", "row", 2, 3, 40) == \
+        {"codes": 240, "scales": 24, "aux": 0, "workspace": 0}
+    assert pqb.query_sizes("mxfp8", "blk32", 1, 4, 64) == \
+        {"codes": 256, "scales": 8, "aux": 0, "workspace": 0}
+    S = pqb.pqb._Sizes()
+    assert L.pqb_query_sizes(6, 2, 1, 8, 128, ctypes.byref(S)) == -3   # INT8 x 1x128
+    assert L.pqb_query_sizes(5, 5, 1, 8, 128, ctypes.byref(S)) == -3   # MXFP8 x blk16
+    assert L.pqb_query_sizes(5, 4, 1, 8, 48, ctypes.byref(S)) == -4    # MXFP8 needs c % 32
+    assert L.pqb_query_sizes(7, 0, 1, 8, 128, ctypes.byref(S)) == -2   # unknown format
+    # per-tensor INT8 and E5M2 need workspace, so the batch call refuses them
+    J = pqb.pqb._Job
+    fake = 0x10000
+    jobs = (J * 1)(J(fake, fake, fake, None, 1, 8, 128, 1, 6, 0, 0))
+    assert L.pqb_quantize_batch(jobs, 1, None) == -3
+    jobs = (J * 1)(J(fake, fake, fake, None, 1, 8, 128, 1, 4, 0, 0))
+    assert L.pqb_quantize_batch(jobs, 1, None) == -3
+    assert L.pqb_encode_e5m2(None, 4, fake, None) == -1
