@@ -63,7 +63,7 @@ def lib():
                      "orc_int4_quantize", "orc_int4_dequantize", "orc_kv_write_fp8",
                      "orc_kv_quant_fp8", "orc_fp8x_quantize", "orc_fp8x_dequantize",
                      "orc_mxfp8_quantize", "orc_mxfp8_dequantize", "orc_int8_quantize",
-                     "orc_int8_dequantize"):
+                     "orc_int8_dequantize", "orc_kivi_quant", "orc_kivi_dequant"):
             getattr(L, name).restype = I
         for name in ("orc_e4m3_encode_n", "orc_e5m2_encode_n", "orc_e2m1_encode_n",
                      "orc_bf16_round_n"):
@@ -85,6 +85,8 @@ def lib():
         L.orc_int4_dequantize.argtypes = [P, P, P, I64, I64, I64, I, P]
         L.orc_kv_write_fp8.argtypes = [P, P, I, I64, I64, P, P, P, P]
         L.orc_kv_quant_fp8.argtypes = [P, I, I64, I64, I64, I64, I, P, P]
+        L.orc_kivi_quant.argtypes = [P, I, I64, I64, I64, I64, I, I, P, P, P]
+        L.orc_kivi_dequant.argtypes = [P, P, P, I64, I64, I64, I64, I, I, I, P]
         _lib = L
     return _lib
 
@@ -390,6 +392,33 @@ def kv_quant_fp8(x, mode, scales=None, bf16=None):
     _check(lib().orc_kv_quant_fp8(_p(x2), dt, L, T, H, D, mode, _p(codes), _p(sc)),
            "kv_quant_fp8")
     return codes, sc
+
+
+def kivi_quant(x, bits, is_k, bf16=None):
+    """KIVI-style KV quantization of x [layers, tokens, heads, head_dim].
+    -> (codes u8 [L, T, H, D * bits / 8], scales f32, mins f32) with groups
+    [L, T/32, H, D] for K and [L, T, H, D/32] for V."""
+    L_, T, H, D = x.shape
+    x2, dt, *_ = _as_input(x.reshape(L_, -1), bf16)
+    gshape = (L_, T // 32, H, D) if is_k else (L_, T, H, D // 32)
+    codes = np.zeros((L_, T, H, D * bits // 8), np.uint8)
+    scales = np.empty(gshape, np.float32)
+    mins = np.empty(gshape, np.float32)
+    _check(lib().orc_kivi_quant(_p(x2), dt, L_, T, H, D, bits, int(is_k), _p(codes), _p(scales),
+                                _p(mins)), "kivi_quant")
+    return codes, scales, mins
+
+
+def kivi_dequant(codes, scales, mins, bits, is_k, out_bf16=False):
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.float32)
+    mins = np.ascontiguousarray(mins, np.float32)
+    L_, T, H, Db = codes.shape
+    D = Db * 8 // bits
+    out = _out((L_, T, H * D), out_bf16).reshape(L_, T, H, D)
+    _check(lib().orc_kivi_dequant(_p(codes), _p(scales), _p(mins), L_, T, H, D, bits, int(is_k),
+                                  int(out_bf16), _p(out)), "kivi_dequant")
+    return out
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:

@@ -21,6 +21,7 @@
 #include "oracle.h"
 
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 /* ------------------------------------------------------------------------ */
@@ -579,6 +580,98 @@ int orc_kv_quant_fp8(const void* x, int dtype, int64_t layers, int64_t tokens, i
         for (int64_t d = 0; d < head_dim; ++d) {
           int64_t i = ((l * tokens + t) * heads + h) * head_dim + d;
           codes[i] = fp8_code(ld(x, dtype, i), scales[kv_scope(mode, heads, l, h)]);
+        }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* KIVI-style KV quantization [DEPLOY KV Cache 量化：误差要和信号比; BYTES   */
+/* 路线三; NOTES §5.1, §7.4]                                                 */
+/* ------------------------------------------------------------------------ */
+
+/* K per channel, grouped over tokens; V per token, grouped over channels;
+ * b = 2 or 4 bits, asymmetric.  The zero-point absorbs a channel's constant
+ * bias: for a group with minimum m and maximum M,
+ *   s = max(M - m, 1e-12) / (2^b - 1),  q = clamp(rint((x - m) / s), 0, 2^b - 1),
+ *   dequant x = q * s + m,
+ * the form the KIVI method uses (the zero-point kept as the real minimum, not
+ * an integer, which could not hold a large bias in b bits).  Groups are 32
+ * tokens (K) or 32 channels (V).  Layout [layers, tokens, heads, head_dim];
+ * codes packed along the flat index, element i at bits b * (i % (8 / b)) of
+ * byte i * b / 8.  Scales and minimums are float32:
+ *   K [layers, tokens / 32, heads, head_dim]   (tokens % 32 == 0)
+ *   V [layers, tokens, heads, head_dim / 32]   (head_dim % 32 == 0) */
+static int64_t kivi_group(int is_k, int64_t T, int64_t H, int64_t D, int64_t l, int64_t t,
+                          int64_t h, int64_t d) {
+  if (is_k) return ((l * (T / 32) + t / 32) * H + h) * D + d;
+  return ((l * T + t) * H + h) * (D / 32) + d / 32;
+}
+
+static void put_bits(uint8_t* buf, int64_t i, int bits, unsigned v) {
+  int per = 8 / bits;
+  int sh = bits * (int)(i % per);
+  uint8_t mask = (uint8_t)(((1u << bits) - 1) << sh);
+  buf[i / per] = (uint8_t)((buf[i / per] & ~mask) | ((v << sh) & mask));
+}
+
+static unsigned get_bits(const uint8_t* buf, int64_t i, int bits) {
+  int per = 8 / bits;
+  return (buf[i / per] >> (bits * (int)(i % per))) & ((1u << bits) - 1);
+}
+
+int orc_kivi_quant(const void* x, int dtype, int64_t layers, int64_t tokens, int64_t heads,
+                   int64_t head_dim, int bits, int is_k, uint8_t* codes, float* scales,
+                   float* mins) {
+  if (bits != 2 && bits != 4) return -2;
+  if (layers < 0 || tokens < 0 || heads < 0 || head_dim < 0 || head_dim % 32) return -4;
+  if (is_k && tokens % 32) return -4;
+  int64_t ng = is_k ? layers * (tokens / 32) * heads * head_dim
+                    : layers * tokens * heads * (head_dim / 32);
+  float* mx = (float*)malloc((size_t)(ng > 0 ? ng : 1) * sizeof(float));
+  if (!mx) return -1;
+  for (int64_t g = 0; g < ng; ++g) {
+    mins[g] = INFINITY;
+    mx[g] = -INFINITY;
+  }
+  for (int64_t l = 0; l < layers; ++l)
+    for (int64_t t = 0; t < tokens; ++t)
+      for (int64_t h = 0; h < heads; ++h)
+        for (int64_t d = 0; d < head_dim; ++d) {
+          int64_t i = ((l * tokens + t) * heads + h) * head_dim + d;
+          int64_t g = kivi_group(is_k, tokens, heads, head_dim, l, t, h, d);
+          float v = ld(x, dtype, i);
+          mins[g] = fminf(mins[g], v);
+          mx[g] = fmaxf(mx[g], v);
+        }
+  float qmax = (float)((1 << bits) - 1);
+  for (int64_t g = 0; g < ng; ++g) scales[g] = fmaxf(mx[g] - mins[g], 1e-12f) / qmax;
+  free(mx);
+  for (int64_t l = 0; l < layers; ++l)
+    for (int64_t t = 0; t < tokens; ++t)
+      for (int64_t h = 0; h < heads; ++h)
+        for (int64_t d = 0; d < head_dim; ++d) {
+          int64_t i = ((l * tokens + t) * heads + h) * head_dim + d;
+          int64_t g = kivi_group(is_k, tokens, heads, head_dim, l, t, h, d);
+          float q = clampf(rintf((ld(x, dtype, i) - mins[g]) / scales[g]), 0.0f, qmax);
+          put_bits(codes, i, bits, (unsigned)q);
+        }
+  return 0;
+}
+
+int orc_kivi_dequant(const uint8_t* codes, const float* scales, const float* mins, int64_t layers,
+                     int64_t tokens, int64_t heads, int64_t head_dim, int bits, int is_k,
+                     int out_dtype, void* out) {
+  if (bits != 2 && bits != 4) return -2;
+  if (layers < 0 || tokens < 0 || heads < 0 || head_dim < 0 || head_dim % 32) return -4;
+  if (is_k && tokens % 32) return -4;
+  for (int64_t l = 0; l < layers; ++l)
+    for (int64_t t = 0; t < tokens; ++t)
+      for (int64_t h = 0; h < heads; ++h)
+        for (int64_t d = 0; d < head_dim; ++d) {
+          int64_t i = ((l * tokens + t) * heads + h) * head_dim + d;
+          int64_t g = kivi_group(is_k, tokens, heads, head_dim, l, t, h, d);
+          float prod = (float)get_bits(codes, i, bits) * scales[g];
+          st(out, out_dtype, i, prod + mins[g]);
         }
   return 0;
 }

@@ -101,6 +101,15 @@ int orc_int4_dequantize(const uint8_t* codes, const uint16_t* scales, const uint
 enum { ORC_KV_LAYER = 0, ORC_KV_HEAD = 1, ORC_KV_STATIC = 2 };
 int orc_kv_quant_fp8(const void* x, int dtype, int64_t layers, int64_t tokens, int64_t heads,
                      int64_t head_dim, int mode, uint8_t* codes, float* scales);
+/* KIVI-style b-bit (2 or 4) asymmetric KV quantization on [layers, tokens,
+ * heads, head_dim]: K (is_k = 1) per channel over groups of 32 tokens, V per
+ * token over groups of 32 channels; float32 scales and minimums per group. */
+int orc_kivi_quant(const void* x, int dtype, int64_t layers, int64_t tokens, int64_t heads,
+                   int64_t head_dim, int bits, int is_k, uint8_t* codes, float* scales,
+                   float* mins);
+int orc_kivi_dequant(const uint8_t* codes, const float* scales, const float* mins, int64_t layers,
+                     int64_t tokens, int64_t heads, int64_t head_dim, int bits, int is_k,
+                     int out_dtype, void* out);
 int orc_kv_write_fp8(const void* k, const void* v, int dtype, int64_t layers,
                      int64_t elems_per_layer, uint8_t* k_codes, uint8_t* v_codes,
                      float* k_scales, float* v_scales);
