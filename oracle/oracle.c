@@ -594,6 +594,7 @@ int orc_kv_quant_fp8(const void* x, int dtype, int64_t layers, int64_t tokens, i
  * bias: for a group with minimum m and maximum M,
  *   s = max(M - m, 1e-12) / (2^b - 1),  q = clamp(rint((x - m) / s), 0, 2^b - 1),
  *   dequant x = q * s + m,
+ * with a zero minimum taken as +0 (the pages give no sign for min(-0, +0)),
  * the form the KIVI method uses (the zero-point kept as the real minimum, not
  * an integer, which could not hold a large bias in b bits).  Groups are 32
  * tokens (K) or 32 channels (V).  Layout [layers, tokens, heads, head_dim];
@@ -644,7 +645,10 @@ int orc_kivi_quant(const void* x, int dtype, int64_t layers, int64_t tokens, int
           mx[g] = fmaxf(mx[g], v);
         }
   float qmax = (float)((1 << bits) - 1);
-  for (int64_t g = 0; g < ng; ++g) scales[g] = fmaxf(mx[g] - mins[g], 1e-12f) / qmax;
+  for (int64_t g = 0; g < ng; ++g) {
+    mins[g] = mins[g] + 0.0f; /* a zero minimum is +0, whichever zeros the group holds */
+    scales[g] = fmaxf(mx[g] - mins[g], 1e-12f) / qmax;
+  }
   free(mx);
   for (int64_t l = 0; l < layers; ++l)
     for (int64_t t = 0; t < tokens; ++t)

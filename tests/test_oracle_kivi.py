@@ -126,3 +126,15 @@ def test_kivi_argument_errors():
     oracle.kivi_quant(np.zeros((1, 33, 1, 32), np.float32), 2, False)     # V does not
     with pytest.raises(ValueError):
         oracle.kivi_quant(np.zeros((1, 32, 1, 48), np.float32), 2, False)  # D % 32
+
+
+def test_kivi_zero_minimum_is_positive_zero():
+    """A group whose minimum is zero stores +0 whichever signed zeros it holds."""
+    x = np.zeros((1, 32, 1, 32), np.float32)
+    x[0, :, 0, 0] = -0.0
+    x[0, 3, 0, 0] = 1.0
+    x[0, 5, 0, 1:] = -0.0
+    for is_k in (True, False):
+        _, _, m = oracle.kivi_quant(x, 4, is_k)
+        zero = m == 0
+        assert zero.any() and not np.signbit(m[zero]).any()
