@@ -301,7 +301,7 @@ def bench_extras(torch, eng, synth, reps, only=None):
             one(name, g, fmt, gran, (1, 65536, 8192), dq)
         del g
     torch.cuda.empty_cache()
-    if want("kv28x32768x8x128_bf16_fp8"):
+    if want("kv28x32768x8x128_bf16_fp8", "kv28x32768x8x128_bf16_kivi"):
         out.update(bench_kv(torch, eng, synth, reps))
     if want("llama8b_224w_bf16_int4_g128"):
         out.update(bench_llama_int4(torch, eng, synth))
@@ -349,7 +349,46 @@ def bench_kv(torch, eng, synth, reps):
                                                   "scales (one pass)", shape=[28, 32768, 8, 128])
     log(f"kv per head: {out['kv28x32768x8x128_bf16_fp8_per_head']['gbs']} GB/s, static: "
         f"{out['kv28x32768x8x128_bf16_fp8_static']['gbs']} GB/s")
-    del k, v, kc, vc
+    del kc, vc
+    # KIVI-style 2/4-bit cache of the same K and V: K per channel over 32 tokens,
+    # V per token over 32 channels; float32 scale and minimum per group.
+    n = k.numel()
+    for bits in (2, 4):
+        cb = n * bits // 8
+        kcb = torch.empty((cb,), dtype=torch.uint8, device=dev)
+        vcb = torch.empty_like(kcb)
+        kpar = torch.empty((2, L_, T_ // 32, H_, D_), dtype=torch.float32, device=dev)
+        vpar = torch.empty((2, L_, T_, H_, D_ // 32), dtype=torch.float32, device=dev)
+
+        def kivi_w(i, bits=bits, kcb=kcb, vcb=vcb, kpar=kpar, vpar=vpar):
+            rc = eng.L.pqb_kv_write_kivi(P(k), P(v), 1, L_, T_, H_, D_, bits, P(kcb), P(vcb),
+                                         P(kpar[0]), P(kpar[1]), P(vpar[0]), P(vpar[1]),
+                                         eng.stream)
+            if rc != 0:
+                raise RuntimeError(f"pqb_kv_write_kivi: status {rc}")
+
+        t = time_reps(torch, kivi_w, max(5, reps // 2), 2)
+        key = f"kv28x32768x8x128_bf16_kivi{bits}"
+        out[key] = rec(2 * n * 2 + 2 * cb + 2 * (n // 32) * 8, t,
+                       op=f"KIVI {bits}-bit KV write (K per channel, V per token, groups of 32)",
+                       shape=[28, 32768, 8, 128], launches=2)
+        ko = torch.empty_like(k)
+        vo = torch.empty_like(v)
+
+        def kivi_r(i, bits=bits, kcb=kcb, vcb=vcb, kpar=kpar, vpar=vpar):
+            rc = eng.L.pqb_kv_read_kivi(P(kcb), P(vcb), P(kpar[0]), P(kpar[1]), P(vpar[0]),
+                                        P(vpar[1]), L_, T_, H_, D_, bits, 1, P(ko), P(vo),
+                                        eng.stream)
+            if rc != 0:
+                raise RuntimeError(f"pqb_kv_read_kivi: status {rc}")
+
+        t = time_reps(torch, kivi_r, max(5, reps // 2), 2)
+        out[key + "_read"] = rec(2 * n * 2 + 2 * cb + 2 * (n // 32) * 8, t,
+                                 op=f"KIVI {bits}-bit KV read to bf16", shape=[28, 32768, 8, 128],
+                                 launches=2)
+        log(f"kivi{bits}: write {out[key]['gbs']} GB/s, read {out[key + '_read']['gbs']} GB/s")
+        del kcb, vcb, kpar, vpar, ko, vo
+    del k, v
     torch.cuda.empty_cache()
     return out
 

@@ -210,6 +210,46 @@ pqb_status pqb_kv_write_fp8_ex(const void* k, const void* v, pqb_dtype dtype, in
                                uint8_t* v_codes, float* k_scales, float* v_scales,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* KIVI-style 2- or 4-bit KV cache (page "量化部署实战", section KV Cache 量化:
+ * K carries a per-channel bias, so per-channel scales with a zero-point suit
+ * it; page "14. 量化：让每一步搬更少的字节", 路线三: KIVI quantizes K per
+ * channel and V per token, at 2 bits).
+ *
+ * K and V are [layers, tokens, heads, head_dim] of `dtype`, token-major.  The
+ * quantizer is asymmetric over groups of 32: a K group is 32 consecutive
+ * tokens of one (layer, head, channel), a V group 32 consecutive channels of
+ * one (layer, token, head).  For a group with minimum m (a zero minimum is
+ * stored as +0) and maximum M, in float32 with round-to-nearest-even:
+ *   s = max(M - m, 1e-12) / (2^bits - 1),
+ *   q = clamp(rint((x - m) / s), 0, 2^bits - 1)   (the quotient correctly rounded),
+ *   dequantized x = q * s + m                      (product and sum rounded separately;
+ *                                                   then bf16 RNE for a bf16 output).
+ * Layouts: codes u8 [n * bits / 8] over the flat element index
+ * i = ((layer * tokens + token) * heads + head) * head_dim + channel, element i
+ * at bits bits * (i % (8 / bits)) of byte i * bits / 8; K scales and mins f32
+ * [layers, tokens / 32, heads, head_dim]; V scales and mins f32 [layers, tokens,
+ * heads, head_dim / 32].
+ * pqb_kv_write_kivi quantizes k and v; pqb_kv_read_kivi dequantizes codes,
+ * scales and mins back into k_out and v_out (same layout as the input, of
+ * out_dtype).  Pass NULL for k (k_codes for the read) to handle V only, or for
+ * v (v_codes) to handle K only; that tensor's other pointers are then ignored.
+ * Shape rules: bits is 2 or 4; head_dim % 32 == 0; tokens % 32 == 0 when K is
+ * handled; layers * tokens * heads * head_dim < 2^36.  Inputs must be finite
+ * and each group's range M - m below the float32 overflow threshold.
+ * Alignment: k, v, codes, scales, mins and outputs 16 bytes.
+ * Errors, all before any launch: PQB_ERR_ENUM for an unknown dtype or bits,
+ * PQB_ERR_SHAPE for shapes breaking the rules above, PQB_ERR_NULL if both
+ * tensors are NULL or a needed pointer is NULL, PQB_ERR_ALIGN. */
+pqb_status pqb_kv_write_kivi(const void* k, const void* v, pqb_dtype dtype, int64_t layers,
+                             int64_t tokens, int64_t heads, int64_t head_dim, int bits,
+                             uint8_t* k_codes, uint8_t* v_codes, float* k_scales, float* k_mins,
+                             float* v_scales, float* v_mins, void* stream);
+pqb_status pqb_kv_read_kivi(const uint8_t* k_codes, const uint8_t* v_codes,
+                            const float* k_scales, const float* k_mins, const float* v_scales,
+                            const float* v_mins, int64_t layers, int64_t tokens, int64_t heads,
+                            int64_t head_dim, int bits, pqb_dtype out_dtype, void* k_out,
+                            void* v_out, void* stream);
+
 /* Element codecs exposed for testing the rounding rules on arrays of float32:
  * E4M3 of y (round-to-nearest-even; |y| must not exceed 464) into one byte
  * per element; E2M1 of y (ties to the smaller magnitude, saturating at 6)

@@ -43,6 +43,8 @@ bool known_gran(int g) { return g >= PQB_TENSOR && g <= PQB_GRP_128; }
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 constexpr int64_t kMaxGridY = 65535;
+// KIVI kernels use one-dimensional grids of up to n / 32 threads.
+constexpr int64_t kKiviMaxElems = (int64_t)1 << 36;
 
 // Shape rules of one (format, granularity) pair; also bounds the grid sizes
 // the launchers will form.
@@ -409,6 +411,77 @@ pqb_status pqb_kv_write_fp8_ex(const void* k, const void* v, pqb_dtype dtype, in
   if (dynamic && !aligned(workspace, 16)) return PQB_ERR_ALIGN;
   return hip_status(launch_kv_fp8(t, nt, dtype == PQB_BF16, layers, tokens, heads, head_dim,
                                   (float*)workspace, (hipStream_t)stream));
+}
+
+// KIVI shape rules; `with_k` adds the 32-token groups of K.
+static bool kivi_dims_ok(int64_t layers, int64_t tokens, int64_t heads, int64_t head_dim,
+                         bool with_k) {
+  if (layers < 0 || tokens < 0 || heads < 0 || head_dim < 0 || head_dim % 32) return false;
+  if (with_k && tokens % 32) return false;
+  int64_t n = 1;
+  for (int64_t d : {layers, tokens, heads, head_dim}) {
+    if (d == 0) return true;
+    if (d > (kKiviMaxElems - 1) / n) return false;  // n * d < 2^36
+    n *= d;
+  }
+  return true;
+}
+
+pqb_status pqb_kv_write_kivi(const void* k, const void* v, pqb_dtype dtype, int64_t layers,
+                             int64_t tokens, int64_t heads, int64_t head_dim, int bits,
+                             uint8_t* k_codes, uint8_t* v_codes, float* k_scales, float* k_mins,
+                             float* v_scales, float* v_mins, void* stream) {
+  if (!valid_dtype(dtype) || (bits != 2 && bits != 4)) return PQB_ERR_ENUM;
+  if (!k && !v) return PQB_ERR_NULL;
+  if (!kivi_dims_ok(layers, tokens, heads, head_dim, k != nullptr)) return PQB_ERR_SHAPE;
+  const int64_t n = layers * tokens * heads * head_dim;
+  if (n == 0) return PQB_OK;
+  if ((k && (!k_codes || !k_scales || !k_mins)) || (v && (!v_codes || !v_scales || !v_mins)))
+    return PQB_ERR_NULL;
+  if (k && !(aligned(k, 16) && aligned(k_codes, 16) && aligned(k_scales, 16) && aligned(k_mins, 16)))
+    return PQB_ERR_ALIGN;
+  if (v && !(aligned(v, 16) && aligned(v_codes, 16) && aligned(v_scales, 16) && aligned(v_mins, 16)))
+    return PQB_ERR_ALIGN;
+  const bool bf16 = dtype == PQB_BF16;
+  const hipStream_t st = (hipStream_t)stream;
+  if (k) {
+    const hipError_t e = launch_kivi_k(k, bf16, layers, tokens, heads, head_dim, bits, k_codes,
+                                       k_scales, k_mins, st);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  if (v) return hip_status(launch_kivi_v(v, bf16, n, bits, v_codes, v_scales, v_mins, st));
+  return PQB_OK;
+}
+
+pqb_status pqb_kv_read_kivi(const uint8_t* k_codes, const uint8_t* v_codes,
+                            const float* k_scales, const float* k_mins, const float* v_scales,
+                            const float* v_mins, int64_t layers, int64_t tokens, int64_t heads,
+                            int64_t head_dim, int bits, pqb_dtype out_dtype, void* k_out,
+                            void* v_out, void* stream) {
+  if (!valid_dtype(out_dtype) || (bits != 2 && bits != 4)) return PQB_ERR_ENUM;
+  if (!k_codes && !v_codes) return PQB_ERR_NULL;
+  if (!kivi_dims_ok(layers, tokens, heads, head_dim, k_codes != nullptr)) return PQB_ERR_SHAPE;
+  const int64_t n = layers * tokens * heads * head_dim;
+  if (n == 0) return PQB_OK;
+  if ((k_codes && (!k_scales || !k_mins || !k_out)) ||
+      (v_codes && (!v_scales || !v_mins || !v_out)))
+    return PQB_ERR_NULL;
+  if (k_codes && !(aligned(k_codes, 16) && aligned(k_scales, 16) && aligned(k_mins, 16) &&
+                   aligned(k_out, 16)))
+    return PQB_ERR_ALIGN;
+  if (v_codes && !(aligned(v_codes, 16) && aligned(v_scales, 16) && aligned(v_mins, 16) &&
+                   aligned(v_out, 16)))
+    return PQB_ERR_ALIGN;
+  const bool bf16 = out_dtype == PQB_BF16;
+  const hipStream_t st = (hipStream_t)stream;
+  if (k_codes) {
+    const hipError_t e = launch_kivi_k_dequant(k_codes, k_scales, k_mins, layers, tokens, heads,
+                                               head_dim, bits, bf16, k_out, st);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  if (v_codes)
+    return hip_status(launch_kivi_v_dequant(v_codes, v_scales, v_mins, n, bits, bf16, v_out, st));
+  return PQB_OK;
 }
 
 pqb_status pqb_encode_e4m3(const float* y, int64_t n, uint8_t* out, void* stream) {

@@ -97,6 +97,22 @@ hipError_t launch_kv_fp8(const KvTensor* t, int ntensors, bool bf16, int64_t lay
                          int64_t tokens, int64_t heads, int64_t head_dim, float* ws,
                          hipStream_t st);
 
+// KIVI-style 2- or 4-bit KV quantization: x is [layers, tokens, heads,
+// head_dim]; K groups are 32 tokens of one channel (tokens % 32 == 0), V
+// groups 32 channels of one token (head_dim % 32 == 0).  Codes pack element i
+// at bits b * (i % (8 / b)); scales and mins are float32, K [layers, tokens /
+// 32, heads, head_dim], V [n / 32].
+hipError_t launch_kivi_k(const void* x, bool bf16, int64_t layers, int64_t tokens, int64_t heads,
+                         int64_t head_dim, int bits, uint8_t* codes, float* scales, float* mins,
+                         hipStream_t st);
+hipError_t launch_kivi_v(const void* x, bool bf16, int64_t n, int bits, uint8_t* codes,
+                         float* scales, float* mins, hipStream_t st);
+hipError_t launch_kivi_k_dequant(const uint8_t* codes, const float* scales, const float* mins,
+                                 int64_t layers, int64_t tokens, int64_t heads, int64_t head_dim,
+                                 int bits, bool out_bf16, void* out, hipStream_t st);
+hipError_t launch_kivi_v_dequant(const uint8_t* codes, const float* scales, const float* mins,
+                                 int64_t n, int bits, bool out_bf16, void* out, hipStream_t st);
+
 // ---- element codecs ---------------------------------------------------------
 hipError_t launch_encode_elem(const float* y, int64_t n, uint8_t* out, hipStream_t st, int elem);
 hipError_t launch_encode_e2m1(const float* y, int64_t n, uint8_t* out, hipStream_t st);

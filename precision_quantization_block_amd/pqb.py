@@ -69,11 +69,14 @@ def lib():
         L.pqb_kv_workspace_bytes_ex.argtypes = [I64, I64, I64, I64]
         L.pqb_kv_workspace_bytes_ex.restype = SZ
         L.pqb_kv_write_fp8_ex.argtypes = [P, P, I, I64, I64, I64, I64, I, I, P, P, P, P, P, SZ, P]
+        L.pqb_kv_write_kivi.argtypes = [P, P, I, I64, I64, I64, I64, I, P, P, P, P, P, P, P]
+        L.pqb_kv_read_kivi.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I, I, P, P, P]
         L.pqb_encode_e4m3.argtypes = [P, I64, P, P]
         L.pqb_encode_e5m2.argtypes = [P, I64, P, P]
         L.pqb_encode_e2m1.argtypes = [P, I64, P, P]
         for f in ("pqb_query_sizes", "pqb_quantize", "pqb_quantize_batch", "pqb_dequantize",
-                  "pqb_kv_write_fp8", "pqb_kv_write_fp8_ex",
+                  "pqb_kv_write_fp8", "pqb_kv_write_fp8_ex", "pqb_kv_write_kivi",
+                  "pqb_kv_read_kivi",
                   "pqb_encode_e4m3", "pqb_encode_e5m2", "pqb_encode_e2m1"):
             getattr(L, f).restype = I
         _lib = L
@@ -283,6 +286,75 @@ def kv_write_fp8_ex(k: torch.Tensor | None, v: torch.Tensor | None, k_mode="laye
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev)),
         "kv_write_fp8_ex")
     return codes[0], codes[1], scales[0], scales[1]
+
+
+def kivi_layouts(L, T, H, D, bits):
+    """Shapes of (codes, K scales / mins, V scales / mins) for a KIVI cache of
+    [L, T, H, D]: codes pack 8 / bits elements per byte along the flat index."""
+    return (L * T * H * D * bits // 8,), (L, T // 32, H, D), (L, T, H, D // 32)
+
+
+def kv_write_kivi(k: torch.Tensor | None, v: torch.Tensor | None, bits: int = 2):
+    """KIVI-style KV write: K quantized per channel over groups of 32 tokens, V
+    per token over groups of 32 channels, both asymmetric at `bits` (2 or 4).
+    K and V are [layers, tokens, heads, head_dim] (either may be None).  Returns
+    ((k_codes, k_scales, k_mins), (v_codes, v_scales, v_mins)), None for a
+    tensor passed as None."""
+    xs = [k, v]
+    ref = next((t for t in xs if t is not None), None)
+    if ref is None:
+        raise ValueError("pass K, V or both")
+    if ref.dim() != 4:
+        raise ValueError("K and V must be [layers, tokens, heads, head_dim]")
+    L, T, H, D = ref.shape
+    dev = ref.device
+    shapes = kivi_layouts(L, T, H, D, bits)
+    outs = [None, None]
+    for i, x in enumerate(xs):
+        if x is None:
+            continue
+        x = _dev_tensor(x, "kv"[i])
+        if x.shape != ref.shape or x.dtype != ref.dtype:
+            raise ValueError("K and V must share shape and dtype")
+        xs[i] = x
+        sshape = shapes[1 + i]
+        outs[i] = (torch.empty(shapes[0], dtype=torch.uint8, device=dev),
+                   torch.empty(sshape, dtype=torch.float32, device=dev),
+                   torch.empty(sshape, dtype=torch.float32, device=dev))
+    kc, ks, km = outs[0] if outs[0] else (None, None, None)
+    vc, vs, vm = outs[1] if outs[1] else (None, None, None)
+    _check(lib().pqb_kv_write_kivi(
+        _ptr(xs[0]), _ptr(xs[1]), BF16 if ref.dtype == torch.bfloat16 else F32, L, T, H, D, bits,
+        _ptr(kc), _ptr(vc), _ptr(ks), _ptr(km), _ptr(vs), _ptr(vm), _stream(dev)),
+        "kv_write_kivi")
+    return outs[0], outs[1]
+
+
+def kv_read_kivi(k_parts, v_parts, shape, bits: int = 2, out_dtype=torch.bfloat16):
+    """Dequantize a KIVI cache written by kv_write_kivi back to `shape` =
+    (layers, tokens, heads, head_dim) in out_dtype.  k_parts / v_parts are the
+    (codes, scales, mins) triples (either may be None).  Returns (k, v)."""
+    L, T, H, D = shape
+    parts = [k_parts, v_parts]
+    ref = next((p for p in parts if p is not None), None)
+    if ref is None:
+        raise ValueError("pass K, V or both")
+    dev = ref[0].device
+    outs, args = [None, None], [[None] * 3, [None] * 3]
+    for i, p in enumerate(parts):
+        if p is None:
+            continue
+        c, s, m = p
+        args[i] = [_dev_tensor(c, "codes", (torch.uint8,)),
+                   _dev_tensor(s, "scales", (torch.float32,)),
+                   _dev_tensor(m, "mins", (torch.float32,))]
+        outs[i] = torch.empty(tuple(shape), dtype=out_dtype, device=dev)
+    _check(lib().pqb_kv_read_kivi(
+        _ptr(args[0][0]), _ptr(args[1][0]), _ptr(args[0][1]), _ptr(args[0][2]),
+        _ptr(args[1][1]), _ptr(args[1][2]), L, T, H, D, bits,
+        BF16 if out_dtype == torch.bfloat16 else F32, _ptr(outs[0]), _ptr(outs[1]), _stream(dev)),
+        "kv_read_kivi")
+    return outs[0], outs[1]
 
 
 def encode_e5m2(y: torch.Tensor) -> torch.Tensor:

@@ -209,6 +209,40 @@ def test_kv_write_ex_errors_before_launch(L):
     assert kv(k=None, kc=None, ks=None, shape=(2, 0, 8, 128)) == 0
 
 
+def test_kivi_errors_before_launch(L):
+    P = ctypes.c_void_p
+    fake, odd, odd8 = P(0x10000), P(0x10002), P(0x10008)
+    w = L.pqb_kv_write_kivi
+    r = L.pqb_kv_read_kivi
+
+    def wr(k=fake, v=fake, dt=1, shape=(2, 64, 8, 128), bits=2, kc=fake, vc=fake, ks=fake,
+           km=fake, vs=fake, vm=fake):
+        return w(k, v, dt, *shape, bits, kc, vc, ks, km, vs, vm, None)
+
+    def rd(kc=fake, vc=fake, ks=fake, km=fake, vs=fake, vm=fake, shape=(2, 64, 8, 128), bits=4,
+           dt=0, ko=fake, vo=fake):
+        return r(kc, vc, ks, km, vs, vm, *shape, bits, dt, ko, vo, None)
+
+    for f in (wr, rd):
+        assert f(dt=2) == -2
+        assert f(bits=3) == -2 and f(bits=8) == -2 and f(bits=0) == -2
+        assert f(shape=(2, 64, 8, 96 + 8)) == -4           # head_dim % 32
+        assert f(shape=(2, 48, 8, 128)) == -4              # K needs tokens % 32
+        assert f(shape=(-2, 64, 8, 128)) == -4
+        assert f(shape=(1 << 20, 1 << 10, 1 << 4, 128)) == -4   # 2^41 elements
+        assert f(shape=(1 << 30, 1 << 30, 1 << 30, 1 << 30)) == -4  # product overflows int64
+    assert wr(k=None, v=None) == -1 and rd(kc=None, vc=None) == -1
+    assert wr(kc=None) == -1 and wr(km=None) == -1 and wr(vm=None) == -1
+    assert rd(ks=None) == -1 and rd(vo=None) == -1 and rd(ko=None) == -1
+    assert wr(k=odd) == -5 and wr(vc=odd8) == -5 and wr(ks=odd8) == -5 and wr(vm=odd8) == -5
+    assert rd(kc=odd8) == -5 and rd(vs=odd8) == -5 and rd(ko=odd8) == -5
+    # empty shapes launch nothing; V alone does not need tokens % 32
+    assert wr(shape=(0, 64, 8, 128)) == 0 and rd(shape=(2, 64, 0, 128)) == 0
+    assert wr(k=None, kc=None, ks=None, km=None, shape=(2, 0, 8, 128)) == 0
+    assert wr(k=None, shape=(2, 48, 8, 128), v=fake, vc=None) == -1   # V checks still run
+    assert rd(kc=None, shape=(0, 48, 8, 128)) == 0
+
+
 def test_head_index_by_multiply_high_is_exact():
     """Per-head kernels find the head of a column c < heads * hu (hu = head_dim
     / 8 units) as the high 32 bits of c * ceil(2^32 / hu).  The ABI admits
