@@ -33,6 +33,12 @@ __device__ __forceinline__ uint2 ld_nt8(const void* p) {
   u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
   return make_uint2(v[0], v[1]);
 }
+__device__ __forceinline__ void st_nt1(void* p, uint32_t w) {
+  __builtin_nontemporal_store((uint8_t)w, reinterpret_cast<uint8_t*>(p));
+}
+__device__ __forceinline__ void st_nt2(void* p, uint32_t w) {
+  __builtin_nontemporal_store((uint16_t)w, reinterpret_cast<uint16_t*>(p));
+}
 __device__ __forceinline__ void st_nt4(void* p, uint32_t w) {
   __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(p));
 }
