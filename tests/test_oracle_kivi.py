@@ -138,3 +138,20 @@ def test_kivi_zero_minimum_is_positive_zero():
         _, _, m = oracle.kivi_quant(x, 4, is_k)
         zero = m == 0
         assert zero.any() and not np.signbit(m[zero]).any()
+
+
+def test_kivi_rounding_ties_go_to_even():
+    """With m = 0 and M = 3 at 2 bits (or M = 15 at 4 bits) the step is exactly
+    1, so halves are exact ties and rint sends them to the even integer."""
+    x = np.zeros((1, 1, 1, 32), np.float32)
+    x[0, 0, 0, :8] = [0.0, 3.0, 0.5, 1.5, 2.5, 1.0, 2.0, 0.25]
+    c, s, m = oracle.kivi_quant(x, 2, False)
+    assert s[0, 0, 0, 0] == 1.0 and m[0, 0, 0, 0] == 0.0
+    q = [(int(c[0, 0, 0, i // 4]) >> (2 * (i % 4))) & 3 for i in range(8)]
+    assert q == [0, 3, 0, 2, 2, 1, 2, 0]
+    x4 = x * 5
+    x4[0, 0, 0, :8] = [0.0, 15.0, 6.5, 7.5, 13.5, 14.5, 0.5, 2.5]
+    c, s, m = oracle.kivi_quant(x4, 4, False)
+    assert s[0, 0, 0, 0] == 1.0
+    q = [(int(c[0, 0, 0, i // 2]) >> (4 * (i % 2))) & 15 for i in range(8)]
+    assert q == [0, 15, 6, 8, 14, 14, 0, 2]
