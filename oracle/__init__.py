@@ -424,3 +424,53 @@ def kivi_dequant(codes, scales, mins, bits, is_k, out_bf16=False):
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     """Widen bf16 bit patterns to float32 (exact)."""
     return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# --------------------------------------------------------------------------
+# block-scaled FP8 GEMM (a consumer of the 1x128 and 128x128 codes)
+# --------------------------------------------------------------------------
+
+def _e4m3_table() -> np.ndarray:
+    return np.array([e4m3_decode(c) for c in range(256)], np.float64)
+
+
+def fp8_block_gemm(a_codes, a_scales, b_codes, b_scales, abs_sum=False):
+    """Block-scaled FP8 GEMM, page "量化部署实战", exercise section on FP8
+    blockwise scaling: inside each 128-deep block of K the FP8 products are
+    summed, that block sum is multiplied by the block's activation scale and
+    weight scale, and the results are added into the float32 output.
+
+        C[m, n] = sum_kb sA[m, kb] * sB[n // 128, kb] * P[m, n, kb],
+        P[m, n, kb] = sum_{k in kb} dec(a[m, k]) * dec(b[n, k]).
+
+    a_codes u8 E4M3 [M, K] with a_scales f32 [M, K/128] (the 1x128 layout);
+    b_codes u8 E4M3 [N, K] with b_scales f32 [N/128, K/128] (the 128x128
+    layout); K and N multiples of 128.  Written out in float64: every block sum
+    P is exact there (its terms are multiples of 2^-18 below 2^18, fewer than
+    2^8 of them), so the only roundings are the float64 scale products and
+    additions, far below float32 resolution.
+
+    Returns C as float64 [M, N]; with abs_sum, also the same sum taken over
+    absolute values (sum_kb |sA sB| sum_k |dec(a) dec(b)|), which sets the
+    scale of any float32 evaluation's rounding error."""
+    a_codes = np.ascontiguousarray(a_codes, np.uint8)
+    b_codes = np.ascontiguousarray(b_codes, np.uint8)
+    M, K = a_codes.shape
+    N, Kb = b_codes.shape
+    if K != Kb or K % 128 or N % 128:
+        raise ValueError("need a [M, K], b [N, K] with K and N multiples of 128")
+    sa = np.asarray(a_scales, np.float32).astype(np.float64).reshape(M, K // 128)
+    sb = np.asarray(b_scales, np.float32).astype(np.float64).reshape(N // 128, K // 128)
+    dec = _e4m3_table()
+    a = dec[a_codes]
+    b = dec[b_codes]
+    C = np.zeros((M, N), np.float64)
+    S = np.zeros((M, N), np.float64) if abs_sum else None
+    for kb in range(K // 128):
+        ks = slice(128 * kb, 128 * kb + 128)
+        P = a[:, ks] @ b[:, ks].T                                # exact block sums
+        s = sa[:, kb, None] * np.repeat(sb[:, kb], 128)[None, :]
+        C += s * P
+        if abs_sum:
+            S += np.abs(s) * (np.abs(a[:, ks]) @ np.abs(b[:, ks]).T)
+    return (C, S) if abs_sum else C
