@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+FP8_MFMA_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 matrix peak (no sparsity)
 METRIC = "quantize-pack GB/s (bytes in+out) and % of HBM peak, per format"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "k_multi_fp8_w8a8_7168x2048_8192x7168_counters.json")
 KERNEL_SOURCES = ["precision_quantization_block_amd/csrc/k_multi.hip",
@@ -303,6 +304,8 @@ def bench_extras(torch, eng, synth, reps, only=None):
     torch.cuda.empty_cache()
     if want("kv28x32768x8x128_bf16_fp8", "kv28x32768x8x128_bf16_kivi"):
         out.update(bench_kv(torch, eng, synth, reps))
+    if want("gemm_fp8_bs_8192x7168x2048_bf16", "gemm_fp8_bs_8192x2048x7168_bf16"):
+        out.update(bench_gemm(torch, eng, synth, reps))
     if want("llama8b_224w_bf16_int4_g128"):
         out.update(bench_llama_int4(torch, eng, synth))
     return out
@@ -389,6 +392,45 @@ def bench_kv(torch, eng, synth, reps):
         log(f"kivi{bits}: write {out[key]['gbs']} GB/s, read {out[key + '_read']['gbs']} GB/s")
         del kcb, vcb, kpar, vpar, ko, vo
     del k, v
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_gemm(torch, eng, synth, reps):
+    """Block-scaled FP8 GEMM on codes the engine wrote: activations [M, K] with
+    1x128 scales times a weight [N, K] with 128x128 scales, bf16 output."""
+    dev = torch.device("cuda:0")
+    out = {}
+    for (M, N, K) in ((8192, 7168, 2048), (8192, 2048, 7168)):
+        x = synth.fp8_activation(rows=M, cols=K, device=dev)
+        w = synth.fp8_weight(rows=N, cols=K, device=dev)
+        qa = eng.pqb.quantize(x, "fp8_e4m3", "1x128")
+        qw = eng.pqb.quantize(w, "fp8_e4m3", "128x128")
+        a, sa = qa.codes.reshape(M, K), qa.scales.reshape(M, K // 128)
+        b, sb = qw.codes.reshape(N, K), qw.scales.reshape(N // 128, K // 128)
+        c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+
+        def run(i):
+            rc = eng.L.pqb_gemm_fp8_blockscaled(P(a), P(sa), P(b), P(sb), M, N, K, 1, P(c),
+                                                eng.stream)
+            if rc != 0:
+                raise RuntimeError(f"pqb_gemm_fp8_blockscaled: status {rc}")
+
+        mean, med, mn = time_reps(torch, run, max(10, reps), 3)
+        flops = 2 * M * N * K
+        tf = flops / (mean * 1e-3) / 1e12
+        key = f"gemm_fp8_bs_{M}x{N}x{K}_bf16"
+        out[key] = {"flops": flops, "ms": round(mean, 5), "ms_median": round(med, 5),
+                    "ms_min": round(mn, 5), "tflops": round(tf, 1),
+                    "tflops_at_min": round(flops / (mn * 1e-3) / 1e12, 1),
+                    "frac_fp8_mfma_peak": round(tf / FP8_MFMA_PEAK_TFLOPS, 4),
+                    "op": "C = A (1x128 scales) x W^T (128x128 scales), scales promoted per "
+                          "128-deep K block, bf16 out",
+                    "bytes_in_out": M * K + N * K + 4 * (M + N // 128) * (K // 128) + 2 * M * N}
+        log(f"{key}: {out[key]['tflops']} TFLOP/s ({out[key]['frac_fp8_mfma_peak'] * 100:.1f}% "
+            f"of {FP8_MFMA_PEAK_TFLOPS:.0f})")
+        del x, w, qa, qw, a, b, c
     torch.cuda.empty_cache()
     return out
 

@@ -250,6 +250,29 @@ pqb_status pqb_kv_read_kivi(const uint8_t* k_codes, const uint8_t* v_codes,
                             int64_t head_dim, int bits, pqb_dtype out_dtype, void* k_out,
                             void* v_out, void* stream);
 
+/* Block-scaled FP8 GEMM, the consumer of the codes above (page "量化部署实战",
+ * exercise section on FP8 blockwise scaling: within each 128-deep block of K
+ * the FP8 products are summed on the matrix cores, the block sum is multiplied
+ * by that block's activation and weight scales, and the result is accumulated
+ * in float32):
+ *   C[m, n] = sum_kb RN(a_scales[m, kb] * b_scales[n / 128, kb]) * P[m, n, kb],
+ *   P[m, n, kb] = sum over the block of dec(a[m, k]) * dec(b[n, k]),
+ * one fused multiply-add per block into a float32 accumulator (bf16 output is
+ * its RNE rounding).  P is formed by the matrix core in float32; the
+ * evaluation error against exact arithmetic is at most about (130 + K/128)
+ * * 2^-24 * sum_kb |sA sB| sum_k |dec(a) dec(b)|.
+ * a: E4M3 codes [M, K] with a_scales f32 [M, K/128] (the FP8 BLK_1x128 layout
+ * of a [1, M, K] tensor); b: E4M3 codes [N, K] with b_scales f32 [N/128, K/128]
+ * (the BLK_128x128 layout of a [1, N, K] weight); c: [M, N] row-major of
+ * out_dtype.  Shape rules: K % 128 == 0, N % 128 == 0, M, N, K < 2^31 and
+ * ceil(M/128) * (N/128) < 2^31; M = 0 or N = 0 does nothing; K = 0 writes zeros.
+ * Codes must not be NaN (0x7F, 0xFF), as the quantizers never write them.
+ * Alignment: a, b and c 16 bytes, scales 4 bytes.  Errors, before any launch:
+ * PQB_ERR_ENUM (out_dtype), PQB_ERR_SHAPE, PQB_ERR_NULL, PQB_ERR_ALIGN. */
+pqb_status pqb_gemm_fp8_blockscaled(const uint8_t* a, const float* a_scales, const uint8_t* b,
+                                    const float* b_scales, int64_t m, int64_t n, int64_t k,
+                                    pqb_dtype out_dtype, void* c, void* stream);
+
 /* Element codecs exposed for testing the rounding rules on arrays of float32:
  * E4M3 of y (round-to-nearest-even; |y| must not exceed 464) into one byte
  * per element; E2M1 of y (ties to the smaller magnitude, saturating at 6)

@@ -484,6 +484,22 @@ pqb_status pqb_kv_read_kivi(const uint8_t* k_codes, const uint8_t* v_codes,
   return PQB_OK;
 }
 
+pqb_status pqb_gemm_fp8_blockscaled(const uint8_t* a, const float* a_scales, const uint8_t* b,
+                                    const float* b_scales, int64_t m, int64_t n, int64_t k,
+                                    pqb_dtype out_dtype, void* c, void* stream) {
+  if (!valid_dtype(out_dtype)) return PQB_ERR_ENUM;
+  if (m < 0 || n < 0 || k < 0 || k % 128 || n % 128) return PQB_ERR_SHAPE;
+  if (m > INT32_MAX || n > INT32_MAX || k > INT32_MAX) return PQB_ERR_SHAPE;
+  if ((m + 127) / 128 * (n / 128) > INT32_MAX) return PQB_ERR_SHAPE;
+  if (m == 0 || n == 0) return PQB_OK;
+  if (!c || (k > 0 && (!a || !b || !a_scales || !b_scales))) return PQB_ERR_NULL;
+  if (!aligned(c, 16)) return PQB_ERR_ALIGN;
+  if (k > 0 && !(aligned(a, 16) && aligned(b, 16) && aligned(a_scales, 4) && aligned(b_scales, 4)))
+    return PQB_ERR_ALIGN;
+  return hip_status(launch_gemm_fp8_bs(a, a_scales, b, b_scales, m, n, k, out_dtype == PQB_BF16, c,
+                                       (hipStream_t)stream));
+}
+
 pqb_status pqb_encode_e4m3(const float* y, int64_t n, uint8_t* out, void* stream) {
   if (n < 0) return PQB_ERR_SHAPE;
   if (n == 0) return PQB_OK;

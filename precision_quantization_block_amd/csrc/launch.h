@@ -113,6 +113,13 @@ hipError_t launch_kivi_k_dequant(const uint8_t* codes, const float* scales, cons
 hipError_t launch_kivi_v_dequant(const uint8_t* codes, const float* scales, const float* mins,
                                  int64_t n, int bits, bool out_bf16, void* out, hipStream_t st);
 
+// Block-scaled FP8 GEMM: C [M, N] = A [M, K] x B [N, K]^T with 1x128 scales on A
+// and 128x128 scales on B, promoted per 128-deep K block; K % 128 == 0,
+// N % 128 == 0.
+hipError_t launch_gemm_fp8_bs(const uint8_t* a, const float* a_scales, const uint8_t* b,
+                              const float* b_scales, int64_t M, int64_t N, int64_t K,
+                              bool out_bf16, void* c, hipStream_t st);
+
 // ---- element codecs ---------------------------------------------------------
 hipError_t launch_encode_elem(const float* y, int64_t n, uint8_t* out, hipStream_t st, int elem);
 hipError_t launch_encode_e2m1(const float* y, int64_t n, uint8_t* out, hipStream_t st);

@@ -71,12 +71,13 @@ def lib():
         L.pqb_kv_write_fp8_ex.argtypes = [P, P, I, I64, I64, I64, I64, I, I, P, P, P, P, P, SZ, P]
         L.pqb_kv_write_kivi.argtypes = [P, P, I, I64, I64, I64, I64, I, P, P, P, P, P, P, P]
         L.pqb_kv_read_kivi.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I, I, P, P, P]
+        L.pqb_gemm_fp8_blockscaled.argtypes = [P, P, P, P, I64, I64, I64, I, P, P]
         L.pqb_encode_e4m3.argtypes = [P, I64, P, P]
         L.pqb_encode_e5m2.argtypes = [P, I64, P, P]
         L.pqb_encode_e2m1.argtypes = [P, I64, P, P]
         for f in ("pqb_query_sizes", "pqb_quantize", "pqb_quantize_batch", "pqb_dequantize",
                   "pqb_kv_write_fp8", "pqb_kv_write_fp8_ex", "pqb_kv_write_kivi",
-                  "pqb_kv_read_kivi",
+                  "pqb_kv_read_kivi", "pqb_gemm_fp8_blockscaled",
                   "pqb_encode_e4m3", "pqb_encode_e5m2", "pqb_encode_e2m1"):
             getattr(L, f).restype = I
         _lib = L
@@ -355,6 +356,32 @@ def kv_read_kivi(k_parts, v_parts, shape, bits: int = 2, out_dtype=torch.bfloat1
         BF16 if out_dtype == torch.bfloat16 else F32, _ptr(outs[0]), _ptr(outs[1]), _stream(dev)),
         "kv_read_kivi")
     return outs[0], outs[1]
+
+
+def gemm_fp8_blockscaled(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Tensor,
+                         b_scales: torch.Tensor, out_dtype=torch.bfloat16,
+                         out: torch.Tensor | None = None) -> torch.Tensor:
+    """C [M, N] = the block-scaled FP8 product of activation codes [M, K] with
+    1x128 scales [M, K/128] and weight codes [N, K] with 128x128 scales
+    [N/128, K/128] (the layouts quantize() writes for "1x128" and "128x128")."""
+    a = _dev_tensor(a_codes, "a_codes", (torch.uint8,))
+    b = _dev_tensor(b_codes, "b_codes", (torch.uint8,))
+    sa = _dev_tensor(a_scales, "a_scales", (torch.float32,))
+    sb = _dev_tensor(b_scales, "b_scales", (torch.float32,))
+    M, K = a.shape[-2], a.shape[-1]
+    N = b.shape[-2]
+    if b.shape[-1] != K or a.numel() != M * K or b.numel() != N * K:
+        raise ValueError("a must be [M, K] and b [N, K]")
+    if sa.numel() != M * (K // 128) or sb.numel() != (N // 128) * (K // 128):
+        raise ValueError("scales must be [M, K/128] and [N/128, K/128]")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    elif out.shape != (M, N) or out.dtype != out_dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [M, N] tensor of out_dtype")
+    _check(lib().pqb_gemm_fp8_blockscaled(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), M, N, K,
+                                          BF16 if out_dtype == torch.bfloat16 else F32,
+                                          _ptr(out), _stream(a.device)), "gemm_fp8_blockscaled")
+    return out
 
 
 def encode_e5m2(y: torch.Tensor) -> torch.Tensor:

@@ -243,6 +243,23 @@ def test_kivi_errors_before_launch(L):
     assert rd(kc=None, shape=(0, 48, 8, 128)) == 0
 
 
+def test_gemm_errors_before_launch(L):
+    P = ctypes.c_void_p
+    fake, odd = P(0x10000), P(0x10008)
+    g = L.pqb_gemm_fp8_blockscaled
+
+    def gm(a=fake, sa=fake, b=fake, sb=fake, m=256, n=256, k=512, dt=1, c=fake):
+        return g(a, sa, b, sb, m, n, k, dt, c, None)
+
+    assert gm(dt=3) == -2
+    assert gm(k=500) == -4 and gm(n=200) == -4 and gm(m=-1) == -4 and gm(k=-128) == -4
+    assert gm(m=1 << 31) == -4 and gm(k=1 << 31) == -4
+    assert gm(m=(1 << 31) - 1, n=(1 << 30)) == -4          # too many tiles
+    assert gm(a=None) == -1 and gm(sb=None) == -1 and gm(c=None) == -1
+    assert gm(a=odd) == -5 and gm(b=odd) == -5 and gm(c=odd) == -5 and gm(sa=P(0x10002)) == -5
+    assert gm(m=0) == 0 and gm(n=0, c=None) == 0               # nothing to do
+
+
 def test_head_index_by_multiply_high_is_exact():
     """Per-head kernels find the head of a column c < heads * hu (hu = head_dim
     / 8 units) as the high 32 bits of c * ceil(2^32 / hu).  The ABI admits
