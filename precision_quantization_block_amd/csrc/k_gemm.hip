@@ -14,11 +14,17 @@
 // 64 x 64 quarter at (64 wm, 64 wn), as 4 x 4 tiles of 16 x 16.  One
 // v_mfma_f32_16x16x128_f8f6f4 covers a whole 128-deep K block of one 16 x 16
 // tile, so every MFMA result is promoted at once: acc = fma(P, sA sB, acc).
-// The 128 x 128-byte tiles of A and B for one K block are staged through LDS,
-// double buffered, with the next block's global loads in flight during the
-// current block's MFMAs.  LDS rows hold 8 chunks of 16 bytes, chunk c of row r
-// at position c ^ (r & 7), so the 8 lanes that read chunk c of 8 consecutive
-// rows touch 8 distinct 16-byte bank groups.
+// The 128 x 128-byte tiles of A and B for one K block, and its 128 activation
+// scales, go straight from global memory into LDS (global_load_lds_dwordx4:
+// each wave instruction fills 1 KiB of LDS, lane l the 16 bytes at 16 l) in a
+// ring of kGStages slots, so the loads of the next kGStages - 1 blocks are in
+// flight while one block is multiplied.  The loads are issued from inline
+// assembly and waited for with explicit vmcnt counts (every wave issues the
+// same 9 loads per block), since the compiler would otherwise wait for all of
+// them before every LDS read.  LDS rows hold 8 chunks of 16 bytes, chunk c of
+// row r at position c ^ (r & 7) (the lane filling position p loads chunk
+// p ^ (r & 7)), so the 8 lanes that read chunk c of 8 consecutive rows touch
+// 8 distinct 16-byte bank groups.
 //
 // MFMA operand layout: lane l holds row (l & 15) of its 16-row A slice (and
 // column (l & 15) of its B slice) and 32 bytes of K; A and B take the same 32
@@ -36,9 +42,14 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int kGT = 128;                     // tile edge in M, N and K
 constexpr int kGThreads = 256;               // 4 waves, 2 x 2
 constexpr int kGTileBytes = kGT * kGT;       // one FP8 tile of A or B
+constexpr int kGScaleBytes = 4 * 256;        // activation scales of one block (each row twice)
+constexpr int kGSlotBytes = 2 * kGTileBytes + kGScaleBytes;
+constexpr int kGStages = 2;                  // ring slots
+constexpr int kGLoadsPerBlock = 9;           // DMA instructions per wave per block
 constexpr int kGOutStride = 64 + 4;          // floats per row of a wave's staged 64 x 64 result
 constexpr int kGOutBytes = 4 * 64 * kGOutStride * 4;
-constexpr int kGLdsBytes = 4 * kGTileBytes > kGOutBytes ? 4 * kGTileBytes : kGOutBytes;
+constexpr int kGLdsBytes =
+    kGStages * kGSlotBytes > kGOutBytes ? kGStages * kGSlotBytes : kGOutBytes;
 
 // Byte offset of 16-byte chunk c of row r in a staged 128 x 128-byte tile.
 __device__ __forceinline__ int tile_off(int r, int c) { return r * kGT + ((c ^ (r & 7)) << 4); }
@@ -50,6 +61,33 @@ __device__ __forceinline__ v8i frag(const uint8_t* tile, int r, int q) {
   return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p);
+}
+
+// Wave-wide DMA of 16 (4) bytes per lane from g to LDS address lds + 16 l (4 l).
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
+               : "memory");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds)
+               : "memory");
+}
+
+// Wait until at most `blocks` blocks of this wave's DMA are still in flight.
+static_assert(kGLoadsPerBlock == 9, "the vmcnt counts below assume 9 loads per block");
+__device__ __forceinline__ void wait_blocks(int blocks) {
+  if (blocks <= 0)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if (blocks == 1)
+    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+}
+
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 template <bool kBf16Out>
 __global__ __launch_bounds__(kGThreads) void k_gemm_fp8_bs(const uint8_t* __restrict__ A,
                                                            const float* __restrict__ sA,
@@ -57,42 +95,41 @@ __global__ __launch_bounds__(kGThreads) void k_gemm_fp8_bs(const uint8_t* __rest
                                                            const float* __restrict__ sB, int M,
                                                            int N, int K, int tiles_n,
                                                            void* __restrict__ C) {
-  // [A buf 0 | A buf 1 | B buf 0 | B buf 1], reused for the epilogue
+  // kGStages slots of [A tile | B tile | scales], reused for the epilogue
   __shared__ __align__(16) uint8_t lds[kGLdsBytes];
-  __shared__ __align__(16) float lds_s[2][kGT];
-  auto lds_a = [&](int buf) { return lds + buf * kGTileBytes; };
-  auto lds_b = [&](int buf) { return lds + (2 + buf) * kGTileBytes; };
+  auto slot = [&](int s) { return lds + s * kGSlotBytes; };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
+  // Workgroups i, i + 8, ... run on one XCD: each XCD takes a contiguous run of
+  // tiles, walked down bands of up to 8 tile rows, so neighbouring workgroups
+  // on an XCD share A rows and B columns in its L2.
+  const int nwg = gridDim.x, per = nwg / 8;
+  const int t = per * 8 == nwg ? (blockIdx.x & 7) * per + (blockIdx.x >> 3) : blockIdx.x;
+  const int band = t / (8 * tiles_n), rem = t - band * 8 * tiles_n;
+  const int band_rows = min(8, nwg / tiles_n - band * 8);
+  const int tm = band * 8 + rem % band_rows, tn = rem / band_rows;
   const int m0 = tm * kGT, n0 = tn * kGT;
   const int nkb = K / kGT;
 
-  // Staging: thread t moves chunk (t & 7) of rows (t >> 3) + 32 i, i < 4, of
-  // both tiles, and (t < 128) the activation scale of row t.
-  const int srow = tid >> 3, sc = tid & 7;
-  uint4 ra[4], rb[4];
-  float rs = 0.0f;
-  auto load_block = [&](int kb) {
-    const int64_t k0 = (int64_t)kb * kGT + 16 * sc;
+  // DMA of block kb into slot s.  Wave w fills rows 32 w .. 32 w + 31 of both
+  // tiles (4 instructions of 8 rows each) and the scales of those rows (lanes
+  // 32 .. 63 repeat lanes 0 .. 31, at scale slots 64 w .. 64 w + 63).  Rows of
+  // A at or past M read row M - 1 instead; their results are never stored.
+  const int drow = lane >> 3, dpos = lane & 7;
+  auto issue_block = [&](int kb, int s) {
+    const uint32_t base = lds_addr(slot(s));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = srow + 32 * i;
-      ra[i] = m0 + r < M ? *reinterpret_cast<const uint4*>(A + (int64_t)(m0 + r) * K + k0)
-                         : uint4{0, 0, 0, 0};
-      rb[i] = *reinterpret_cast<const uint4*>(B + (int64_t)(n0 + r) * K + k0);
+    for (int j = 0; j < 4; ++j) {
+      const int r = wave * 32 + j * 8 + drow;
+      const int64_t col = (int64_t)kb * kGT + 16 * (dpos ^ (r & 7));
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(base + (wave * 32 + j * 8) * kGT);
+      dma16(A + (int64_t)min(m0 + r, M - 1) * K + col, dst);
+      dma16(B + (int64_t)(n0 + r) * K + col, dst + kGTileBytes);
     }
-    if (tid < kGT) rs = m0 + tid < M ? sA[(int64_t)(m0 + tid) * nkb + kb] : 0.0f;
-  };
-  auto store_block = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = srow + 32 * i;
-      *reinterpret_cast<uint4*>(lds_a(buf) + tile_off(r, sc)) = ra[i];
-      *reinterpret_cast<uint4*>(lds_b(buf) + tile_off(r, sc)) = rb[i];
-    }
-    if (tid < kGT) lds_s[buf][tid] = rs;
+    const int sr = min(m0 + wave * 32 + (lane & 31), M - 1);
+    dma4(sA + (int64_t)sr * nkb + kb,
+         __builtin_amdgcn_readfirstlane(base + 2 * kGTileBytes + wave * 256));
   };
 
   const int wm = wave >> 1, wn = wave & 1;
@@ -103,27 +140,29 @@ __global__ __launch_bounds__(kGThreads) void k_gemm_fp8_bs(const uint8_t* __rest
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  if (nkb > 0) {
-    load_block(0);
-    store_block(0);
-  }
-  __syncthreads();
+  for (int s = 0; s < kGStages - 1 && s < nkb; ++s) issue_block(s, s);
   const float* sB_col = sB + (int64_t)(n0 / kGT) * nkb;
   for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    if (kb + 1 < nkb) load_block(kb + 1);
+    // this block's DMA done (for every wave after the barrier), and every wave
+    // done reading the slot the next issue overwrites
+    wait_blocks(min(kGStages - 2, nkb - 1 - kb));
+    barrier();
+    if (kb + kGStages - 1 < nkb) issue_block(kb + kGStages - 1, (kb + kGStages - 1) % kGStages);
+    const uint8_t* sl = slot(kb % kGStages);
+    const float* ls = reinterpret_cast<const float*>(sl + 2 * kGTileBytes);
     const float sb = sB_col[kb];
     v8i af[4];
     v4f sab[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      af[mt] = frag(lds_a(buf), wm * 64 + mt * 16 + r16, q);
-      const v4f s4 = *reinterpret_cast<const v4f*>(&lds_s[buf][wm * 64 + mt * 16 + 4 * q]);
+      const int r = wm * 64 + mt * 16;               // 16 rows from one wave's scale run
+      af[mt] = frag(sl, r + r16, q);
+      const v4f s4 = *reinterpret_cast<const v4f*>(&ls[(r >> 5) * 64 + (r & 31) + 4 * q]);
       sab[mt] = s4 * sb;
     }
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      const v8i bf = frag(lds_b(buf), wn * 64 + nt * 16 + r16, q);
+      const v8i bf = frag(sl + kGTileBytes, wn * 64 + nt * 16 + r16, q);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
@@ -132,9 +171,8 @@ __global__ __launch_bounds__(kGThreads) void k_gemm_fp8_bs(const uint8_t* __rest
         for (int r = 0; r < 4; ++r) acc[mt][nt][r] = __builtin_fmaf(p[r], sab[mt][r], acc[mt][nt][r]);
       }
     }
-    if (kb + 1 < nkb) store_block(buf ^ 1);
-    __syncthreads();
   }
+  barrier();  // every wave done with the ring before it becomes the output stage
 
   // Epilogue: each wave stages its 64 x 64 floats in LDS (rows padded to 68
   // floats), then writes whole row segments: 256 bytes per row for float32,
