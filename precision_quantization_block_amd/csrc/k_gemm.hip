@@ -20,8 +20,8 @@
 // ring of kGStages slots, so the loads of the next kGStages - 1 blocks are in
 // flight while one block is multiplied.  The loads are issued from inline
 // assembly and waited for with explicit vmcnt counts (every wave issues the
-// same 9 loads per block), since the compiler would otherwise wait for all of
-// them before every LDS read.  LDS rows hold 8 chunks of 16 bytes, chunk c of
+// same number of loads per block), since the compiler would otherwise wait for
+// all of them before every LDS read.  LDS rows hold 8 chunks of 16 bytes, chunk c of
 // row r at position c ^ (r & 7) (the lane filling position p loads chunk
 // p ^ (r & 7)), so the 8 lanes that read chunk c of 8 consecutive rows touch
 // 8 distinct 16-byte bank groups.
@@ -39,15 +39,18 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kGT = 128;                     // tile edge in M, N and K
-constexpr int kGThreads = 256;               // 4 waves, 2 x 2
-constexpr int kGTileBytes = kGT * kGT;       // one FP8 tile of A or B
-constexpr int kGScaleBytes = 4 * 256;        // activation scales of one block (each row twice)
-constexpr int kGSlotBytes = 2 * kGTileBytes + kGScaleBytes;
+constexpr int kGT = 128;                     // K block, B tile rows, B scale block edge
+constexpr int kGTM = 128;                    // A tile rows (128 or 256)
+constexpr int kGWaves = 2 * kGTM / 64;       // waves kGTM / 64 x 2, each 64 x 64 of C
+constexpr int kGThreads = 64 * kGWaves;
+constexpr int kGTileA = kGTM * kGT, kGTileB = kGT * kGT;   // FP8 tile bytes for one K block
+constexpr int kGScaleBytes = 4 * 2 * kGTM;   // activation scales of one block (each row twice)
+constexpr int kGSlotBytes = kGTileA + kGTileB + kGScaleBytes;
 constexpr int kGStages = 2;                  // ring slots
-constexpr int kGLoadsPerBlock = 9;           // DMA instructions per wave per block
+constexpr int kGBInstr = kGT / kGWaves / 8;  // B DMA instructions per wave per block
+constexpr int kGLoadsPerBlock = 4 + kGBInstr + 1;   // DMA instructions per wave per block
 constexpr int kGOutStride = 64 + 4;          // floats per row of a wave's staged 64 x 64 result
-constexpr int kGOutBytes = 4 * 64 * kGOutStride * 4;
+constexpr int kGOutBytes = kGWaves * 64 * kGOutStride * 4;
 constexpr int kGLdsBytes =
     kGStages * kGSlotBytes > kGOutBytes ? kGStages * kGSlotBytes : kGOutBytes;
 
@@ -76,14 +79,17 @@ __device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
 }
 
 // Wait until at most `blocks` blocks of this wave's DMA are still in flight.
-static_assert(kGLoadsPerBlock == 9, "the vmcnt counts below assume 9 loads per block");
+template <int kN>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kN) : "memory");
+}
 __device__ __forceinline__ void wait_blocks(int blocks) {
   if (blocks <= 0)
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_vmcnt<0>();
   else if (blocks == 1)
-    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    wait_vmcnt<kGLoadsPerBlock>();
   else
-    asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+    wait_vmcnt<2 * kGLoadsPerBlock>();
 }
 
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
@@ -96,6 +102,7 @@ __global__ __launch_bounds__(kGThreads) void k_gemm_fp8_bs(const uint8_t* __rest
                                                            int N, int K, int tiles_n,
                                                            void* __restrict__ C) {
   // kGStages slots of [A tile | B tile | scales], reused for the epilogue
+  static_assert(kGStages <= 3, "wait_blocks counts at most 2 later blocks");
   __shared__ __align__(16) uint8_t lds[kGLdsBytes];
   auto slot = [&](int s) { return lds + s * kGSlotBytes; };
 
@@ -109,7 +116,7 @@ __global__ __launch_bounds__(kGThreads) void k_gemm_fp8_bs(const uint8_t* __rest
   const int band = t / (8 * tiles_n), rem = t - band * 8 * tiles_n;
   const int band_rows = min(8, nwg / tiles_n - band * 8);
   const int tm = band * 8 + rem % band_rows, tn = rem / band_rows;
-  const int m0 = tm * kGT, n0 = tn * kGT;
+  const int m0 = tm * kGTM, n0 = tn * kGT;
   const int nkb = K / kGT;
 
   // DMA of block kb into slot s.  Wave w fills rows 32 w .. 32 w + 31 of both
@@ -119,17 +126,22 @@ __global__ __launch_bounds__(kGThreads) void k_gemm_fp8_bs(const uint8_t* __rest
   const int drow = lane >> 3, dpos = lane & 7;
   auto issue_block = [&](int kb, int s) {
     const uint32_t base = lds_addr(slot(s));
+    const int64_t k0 = (int64_t)kb * kGT;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 4; ++j) {                      // A rows 32 w + 8 j + (l >> 3)
       const int r = wave * 32 + j * 8 + drow;
-      const int64_t col = (int64_t)kb * kGT + 16 * (dpos ^ (r & 7));
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(base + (wave * 32 + j * 8) * kGT);
-      dma16(A + (int64_t)min(m0 + r, M - 1) * K + col, dst);
-      dma16(B + (int64_t)(n0 + r) * K + col, dst + kGTileBytes);
+      dma16(A + (int64_t)min(m0 + r, M - 1) * K + k0 + 16 * (dpos ^ (r & 7)),
+            __builtin_amdgcn_readfirstlane(base + (wave * 32 + j * 8) * kGT));
+    }
+#pragma unroll
+    for (int j = 0; j < kGBInstr; ++j) {               // B rows 8 (kGBInstr w + j) + (l >> 3)
+      const int r = (wave * kGBInstr + j) * 8 + drow;
+      dma16(B + (int64_t)(n0 + r) * K + k0 + 16 * (dpos ^ (r & 7)),
+            __builtin_amdgcn_readfirstlane(base + kGTileA + (wave * kGBInstr + j) * 8 * kGT));
     }
     const int sr = min(m0 + wave * 32 + (lane & 31), M - 1);
     dma4(sA + (int64_t)sr * nkb + kb,
-         __builtin_amdgcn_readfirstlane(base + 2 * kGTileBytes + wave * 256));
+         __builtin_amdgcn_readfirstlane(base + kGTileA + kGTileB + wave * 256));
   };
 
   const int wm = wave >> 1, wn = wave & 1;
@@ -149,7 +161,7 @@ __global__ __launch_bounds__(kGThreads) void k_gemm_fp8_bs(const uint8_t* __rest
     barrier();
     if (kb + kGStages - 1 < nkb) issue_block(kb + kGStages - 1, (kb + kGStages - 1) % kGStages);
     const uint8_t* sl = slot(kb % kGStages);
-    const float* ls = reinterpret_cast<const float*>(sl + 2 * kGTileBytes);
+    const float* ls = reinterpret_cast<const float*>(sl + kGTileA + kGTileB);
     const float sb = sB_col[kb];
     v8i af[4];
     v4f sab[4];
@@ -162,7 +174,7 @@ __global__ __launch_bounds__(kGThreads) void k_gemm_fp8_bs(const uint8_t* __rest
     }
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      const v8i bf = frag(sl + kGTileBytes, wn * 64 + nt * 16 + r16, q);
+      const v8i bf = frag(sl + kGTileA, wn * 64 + nt * 16 + r16, q);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
@@ -219,7 +231,7 @@ __global__ __launch_bounds__(kGThreads) void k_gemm_fp8_bs(const uint8_t* __rest
 hipError_t launch_gemm_fp8_bs(const uint8_t* a, const float* a_scales, const uint8_t* b,
                               const float* b_scales, int64_t M, int64_t N, int64_t K,
                               bool out_bf16, void* c, hipStream_t st) {
-  const int tiles_m = (int)((M + kGT - 1) / kGT), tiles_n = (int)(N / kGT);
+  const int tiles_m = (int)((M + kGTM - 1) / kGTM), tiles_n = (int)(N / kGT);
   const dim3 grid((unsigned)tiles_m * (unsigned)tiles_n);
   if (out_bf16)
     hipLaunchKernelGGL((k_gemm_fp8_bs<true>), grid, dim3(kGThreads), 0, st, a, a_scales, b,
