@@ -430,7 +430,33 @@ def bench_gemm(torch, eng, synth, reps):
                     "bytes_in_out": M * K + N * K + 4 * (M + N // 128) * (K // 128) + 2 * M * N}
         log(f"{key}: {out[key]['tflops']} TFLOP/s ({out[key]['frac_fp8_mfma_peak'] * 100:.1f}% "
             f"of {FP8_MFMA_PEAK_TFLOPS:.0f})")
-        del x, w, qa, qw, a, b, c
+        # the next layer's FP8 1x128 activation quantization fused into the
+        # epilogue, against the same GEMM with bf16 output followed by the
+        # 1x128 quantizer on that output
+        cc = torch.empty((M, N), dtype=torch.uint8, device=dev)
+        cs = torch.empty((M, N // 128), dtype=torch.float32, device=dev)
+        qbuf = eng.alloc("fp8_e4m3", "1x128", (1, M, N), dev)
+
+        def fused(i):
+            rc = eng.L.pqb_gemm_fp8_blockscaled_quant(P(a), P(sa), P(b), P(sb), M, N, K, P(cc),
+                                                      P(cs), eng.stream)
+            if rc != 0:
+                raise RuntimeError(f"pqb_gemm_fp8_blockscaled_quant: status {rc}")
+
+        def unfused(i):
+            run(i)
+            eng.quantize(c, "fp8_e4m3", "1x128", (1, M, N), qbuf)
+
+        fm = time_reps(torch, fused, max(10, reps), 3)
+        um = time_reps(torch, unfused, max(10, reps), 3)
+        out[key + "_fused_fp8_1x128"] = {
+            "ms": round(fm[0], 5), "ms_median": round(fm[1], 5),
+            "tflops": round(flops / (fm[0] * 1e-3) / 1e12, 1),
+            "unfused_ms": round(um[0], 5), "unfused_ms_median": round(um[1], 5),
+            "op": "the same GEMM with its float32 result quantized to FP8 E4M3 1x128 in the "
+                  "epilogue; unfused = bf16 GEMM output, then the 1x128 quantizer on it"}
+        log(f"{key} fused fp8 1x128: {fm[0] * 1e3:.1f} us vs unfused {um[0] * 1e3:.1f} us")
+        del x, w, qa, qw, a, b, c, cc, cs, qbuf
     torch.cuda.empty_cache()
     return out
 

@@ -273,6 +273,22 @@ pqb_status pqb_gemm_fp8_blockscaled(const uint8_t* a, const float* a_scales, con
                                     const float* b_scales, int64_t m, int64_t n, int64_t k,
                                     pqb_dtype out_dtype, void* c, void* stream);
 
+/* The same GEMM with the next layer's activation quantization fused into its
+ * epilogue (same page and section: the (1, 128) activation scales should be
+ * computed at the end of the kernel that produces the activations, so that
+ * the activations are not written and read back once more).  The float32
+ * accumulators C[m, n] (as pqb_gemm_fp8_blockscaled computes them) are
+ * quantized like pqb_quantize FP8_E4M3 x BLK_1x128 of a [1, M, N] tensor:
+ * c_scales[m, j] = max(amax over C[m, 128 j .. 128 j + 127], 1e-12) / 448,
+ * c_codes[m, n] = E4M3(clamp(C[m, n] / c_scales[m, n / 128], -448, 448)).
+ * c_codes u8 [M, N] (16-byte aligned), c_scales f32 [M, N/128] (4-byte
+ * aligned).  Shape rules and errors as for pqb_gemm_fp8_blockscaled; a NULL
+ * c_scales is PQB_ERR_NULL. */
+pqb_status pqb_gemm_fp8_blockscaled_quant(const uint8_t* a, const float* a_scales,
+                                          const uint8_t* b, const float* b_scales, int64_t m,
+                                          int64_t n, int64_t k, uint8_t* c_codes,
+                                          float* c_scales, void* stream);
+
 /* Element codecs exposed for testing the rounding rules on arrays of float32:
  * E4M3 of y (round-to-nearest-even; |y| must not exceed 464) into one byte
  * per element; E2M1 of y (ties to the smaller magnitude, saturating at 6)

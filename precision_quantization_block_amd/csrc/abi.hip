@@ -484,10 +484,10 @@ pqb_status pqb_kv_read_kivi(const uint8_t* k_codes, const uint8_t* v_codes,
   return PQB_OK;
 }
 
-pqb_status pqb_gemm_fp8_blockscaled(const uint8_t* a, const float* a_scales, const uint8_t* b,
-                                    const float* b_scales, int64_t m, int64_t n, int64_t k,
-                                    pqb_dtype out_dtype, void* c, void* stream) {
-  if (!valid_dtype(out_dtype)) return PQB_ERR_ENUM;
+// Shape, pointer and alignment rules shared by the GEMM entry points.
+static pqb_status check_gemm(const uint8_t* a, const float* a_scales, const uint8_t* b,
+                             const float* b_scales, int64_t m, int64_t n, int64_t k,
+                             const void* c) {
   if (m < 0 || n < 0 || k < 0 || k % 128 || n % 128) return PQB_ERR_SHAPE;
   if (m > INT32_MAX || n > INT32_MAX || k > INT32_MAX) return PQB_ERR_SHAPE;
   if ((m + 127) / 128 * (n / 128) > INT32_MAX) return PQB_ERR_SHAPE;
@@ -496,7 +496,29 @@ pqb_status pqb_gemm_fp8_blockscaled(const uint8_t* a, const float* a_scales, con
   if (!aligned(c, 16)) return PQB_ERR_ALIGN;
   if (k > 0 && !(aligned(a, 16) && aligned(b, 16) && aligned(a_scales, 4) && aligned(b_scales, 4)))
     return PQB_ERR_ALIGN;
-  return hip_status(launch_gemm_fp8_bs(a, a_scales, b, b_scales, m, n, k, out_dtype == PQB_BF16, c,
+  return PQB_OK;
+}
+
+pqb_status pqb_gemm_fp8_blockscaled(const uint8_t* a, const float* a_scales, const uint8_t* b,
+                                    const float* b_scales, int64_t m, int64_t n, int64_t k,
+                                    pqb_dtype out_dtype, void* c, void* stream) {
+  if (!valid_dtype(out_dtype)) return PQB_ERR_ENUM;
+  const pqb_status e = check_gemm(a, a_scales, b, b_scales, m, n, k, c);
+  if (e != PQB_OK || m == 0 || n == 0) return e;
+  return hip_status(launch_gemm_fp8_bs(a, a_scales, b, b_scales, m, n, k,
+                                       out_dtype == PQB_BF16 ? 1 : 0, c, nullptr,
+                                       (hipStream_t)stream));
+}
+
+pqb_status pqb_gemm_fp8_blockscaled_quant(const uint8_t* a, const float* a_scales,
+                                          const uint8_t* b, const float* b_scales, int64_t m,
+                                          int64_t n, int64_t k, uint8_t* c_codes,
+                                          float* c_scales, void* stream) {
+  const pqb_status e = check_gemm(a, a_scales, b, b_scales, m, n, k, c_codes);
+  if (e != PQB_OK || m == 0 || n == 0) return e;
+  if (!c_scales) return PQB_ERR_NULL;
+  if (!aligned(c_scales, 4)) return PQB_ERR_ALIGN;
+  return hip_status(launch_gemm_fp8_bs(a, a_scales, b, b_scales, m, n, k, 2, c_codes, c_scales,
                                        (hipStream_t)stream));
 }
 

@@ -30,8 +30,8 @@
 // column (l & 15) of its B slice) and 32 bytes of K; A and B take the same 32
 // bytes of the block, so the products pair up whatever order the matrix core
 // sums them in.  Result layout: lane l, register r is C[4 (l >> 4) + r][l & 15].
-#include "device.h"
 #include "launch.h"
+#include "quant.h"
 
 namespace pqb {
 namespace {
@@ -94,13 +94,18 @@ __device__ __forceinline__ void wait_blocks(int blocks) {
 
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-template <bool kBf16Out>
+// Output forms: float32, bf16, or FP8 E4M3 codes with one scale per 128
+// columns of a row (the 1x128 activation layout), quantized in the epilogue.
+enum GemmOut { kOutF32 = 0, kOutBf16 = 1, kOutFp8 = 2 };
+
+template <int kOut>
 __global__ __launch_bounds__(kGThreads) void k_gemm_fp8_bs(const uint8_t* __restrict__ A,
                                                            const float* __restrict__ sA,
                                                            const uint8_t* __restrict__ B,
                                                            const float* __restrict__ sB, int M,
                                                            int N, int K, int tiles_n,
-                                                           void* __restrict__ C) {
+                                                           void* __restrict__ C,
+                                                           float* __restrict__ c_scales) {
   // kGStages slots of [A tile | B tile | scales], reused for the epilogue
   static_assert(kGStages <= 3, "wait_blocks counts at most 2 later blocks");
   __shared__ __align__(16) uint8_t lds[kGLdsBytes];
@@ -198,8 +203,40 @@ __global__ __launch_bounds__(kGThreads) void k_gemm_fp8_bs(const uint8_t* __rest
       for (int r = 0; r < 4; ++r)
         out_lds[(mt * 16 + 4 * q + r) * kGOutStride + nt * 16 + r16] = acc[mt][nt][r];
   __syncthreads();
+  if constexpr (kOut == kOutFp8) {
+    // FP8 1x128 quantization of the tile's rows, each exactly one 128-column
+    // block: thread t takes columns 64 (t & 1) .. + 63 of row t >> 1 (staged by
+    // wave (row / 64, t & 1)); the pair's maxima meet by DPP, then the scale
+    // and codes follow the 1x128 quantizer's arithmetic.
+    static_assert(kGTM == 128 && kGThreads == 256, "two threads per row of a 128-row tile");
+    const int rr = tid >> 1, half = tid & 1;
+    const float* v = reinterpret_cast<const float*>(lds) +
+                     ((rr >> 6) * 2 + half) * 64 * kGOutStride + (rr & 63) * kGOutStride;
+    uint32_t am = 0;
+#pragma unroll
+    for (int i = 0; i < 64; i += 4) {
+      const v4f x = *reinterpret_cast<const v4f*>(v + i);
+      am = max(am, max(max(as_u(fabsf(x[0])), as_u(fabsf(x[1]))),
+                       max(as_u(fabsf(x[2])), as_u(fabsf(x[3])))));
+    }
+    const float s = fp8_scale_bits<kE4M3>(group_umax<2>(am));
+    const float y = recip_rn(s);
+    if (m0 + rr < M) {
+      uint8_t* dst = reinterpret_cast<uint8_t*>(C) + (int64_t)(m0 + rr) * N + n0 + 64 * half;
+#pragma unroll
+      for (int i = 0; i < 64; i += 16) {
+        float w[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) w[j] = v[i + j];
+        const uint2 lo = fp8_pack8<kE4M3>(w, s, y), hi = fp8_pack8<kE4M3>(w + 8, s, y);
+        st_nt16(dst + i, lo.x, lo.y, hi.x, hi.y);
+      }
+      if (half == 0) c_scales[(int64_t)(m0 + rr) * (N / kGT) + n0 / kGT] = s;
+    }
+    return;
+  }
   const int row0 = m0 + wm * 64, col0 = n0 + wn * 64;
-  if constexpr (kBf16Out) {
+  if constexpr (kOut == kOutBf16) {
     // 8 lanes per row, 8 rows per step
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -229,16 +266,20 @@ __global__ __launch_bounds__(kGThreads) void k_gemm_fp8_bs(const uint8_t* __rest
 }  // namespace
 
 hipError_t launch_gemm_fp8_bs(const uint8_t* a, const float* a_scales, const uint8_t* b,
-                              const float* b_scales, int64_t M, int64_t N, int64_t K,
-                              bool out_bf16, void* c, hipStream_t st) {
+                              const float* b_scales, int64_t M, int64_t N, int64_t K, int out,
+                              void* c, float* c_scales, hipStream_t st) {
   const int tiles_m = (int)((M + kGTM - 1) / kGTM), tiles_n = (int)(N / kGT);
   const dim3 grid((unsigned)tiles_m * (unsigned)tiles_n);
-  if (out_bf16)
-    hipLaunchKernelGGL((k_gemm_fp8_bs<true>), grid, dim3(kGThreads), 0, st, a, a_scales, b,
-                       b_scales, (int)M, (int)N, (int)K, tiles_n, c);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(kGThreads), 0, st, a, a_scales, b, b_scales, (int)M,
+                       (int)N, (int)K, tiles_n, c, c_scales);
+  };
+  if (out == kOutBf16)
+    go(k_gemm_fp8_bs<kOutBf16>);
+  else if (out == kOutFp8)
+    go(k_gemm_fp8_bs<kOutFp8>);
   else
-    hipLaunchKernelGGL((k_gemm_fp8_bs<false>), grid, dim3(kGThreads), 0, st, a, a_scales, b,
-                       b_scales, (int)M, (int)N, (int)K, tiles_n, c);
+    go(k_gemm_fp8_bs<kOutF32>);
   return hipGetLastError();
 }
 

@@ -115,10 +115,11 @@ hipError_t launch_kivi_v_dequant(const uint8_t* codes, const float* scales, cons
 
 // Block-scaled FP8 GEMM: C [M, N] = A [M, K] x B [N, K]^T with 1x128 scales on A
 // and 128x128 scales on B, promoted per 128-deep K block; K % 128 == 0,
-// N % 128 == 0.
+// N % 128 == 0.  out: 0 float32, 1 bf16, 2 FP8 E4M3 codes [M, N] with 1x128
+// scales c_scales [M, N / 128] (c_scales unused otherwise).
 hipError_t launch_gemm_fp8_bs(const uint8_t* a, const float* a_scales, const uint8_t* b,
-                              const float* b_scales, int64_t M, int64_t N, int64_t K,
-                              bool out_bf16, void* c, hipStream_t st);
+                              const float* b_scales, int64_t M, int64_t N, int64_t K, int out,
+                              void* c, float* c_scales, hipStream_t st);
 
 // ---- element codecs ---------------------------------------------------------
 hipError_t launch_encode_elem(const float* y, int64_t n, uint8_t* out, hipStream_t st, int elem);

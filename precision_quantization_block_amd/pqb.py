@@ -72,12 +72,14 @@ def lib():
         L.pqb_kv_write_kivi.argtypes = [P, P, I, I64, I64, I64, I64, I, P, P, P, P, P, P, P]
         L.pqb_kv_read_kivi.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I, I, P, P, P]
         L.pqb_gemm_fp8_blockscaled.argtypes = [P, P, P, P, I64, I64, I64, I, P, P]
+        L.pqb_gemm_fp8_blockscaled_quant.argtypes = [P, P, P, P, I64, I64, I64, P, P, P]
         L.pqb_encode_e4m3.argtypes = [P, I64, P, P]
         L.pqb_encode_e5m2.argtypes = [P, I64, P, P]
         L.pqb_encode_e2m1.argtypes = [P, I64, P, P]
         for f in ("pqb_query_sizes", "pqb_quantize", "pqb_quantize_batch", "pqb_dequantize",
                   "pqb_kv_write_fp8", "pqb_kv_write_fp8_ex", "pqb_kv_write_kivi",
                   "pqb_kv_read_kivi", "pqb_gemm_fp8_blockscaled",
+                  "pqb_gemm_fp8_blockscaled_quant",
                   "pqb_encode_e4m3", "pqb_encode_e5m2", "pqb_encode_e2m1"):
             getattr(L, f).restype = I
         _lib = L
@@ -382,6 +384,28 @@ def gemm_fp8_blockscaled(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes:
                                           BF16 if out_dtype == torch.bfloat16 else F32,
                                           _ptr(out), _stream(a.device)), "gemm_fp8_blockscaled")
     return out
+
+
+def gemm_fp8_blockscaled_quant(a_codes: torch.Tensor, a_scales: torch.Tensor,
+                               b_codes: torch.Tensor, b_scales: torch.Tensor):
+    """The block-scaled FP8 GEMM with its float32 result quantized to FP8 E4M3
+    1x128 in the epilogue.  Returns (codes u8 [M, N], scales f32 [M, N/128])."""
+    a = _dev_tensor(a_codes, "a_codes", (torch.uint8,))
+    b = _dev_tensor(b_codes, "b_codes", (torch.uint8,))
+    sa = _dev_tensor(a_scales, "a_scales", (torch.float32,))
+    sb = _dev_tensor(b_scales, "b_scales", (torch.float32,))
+    M, K = a.shape[-2], a.shape[-1]
+    N = b.shape[-2]
+    if b.shape[-1] != K or a.numel() != M * K or b.numel() != N * K:
+        raise ValueError("a must be [M, K] and b [N, K]")
+    if sa.numel() != M * (K // 128) or sb.numel() != (N // 128) * (K // 128):
+        raise ValueError("scales must be [M, K/128] and [N/128, K/128]")
+    codes = torch.empty((M, N), dtype=torch.uint8, device=a.device)
+    scales = torch.empty((M, N // 128), dtype=torch.float32, device=a.device)
+    _check(lib().pqb_gemm_fp8_blockscaled_quant(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), M, N, K,
+                                                _ptr(codes), _ptr(scales), _stream(a.device)),
+           "gemm_fp8_blockscaled_quant")
+    return codes, scales
 
 
 def encode_e5m2(y: torch.Tensor) -> torch.Tensor:

@@ -258,6 +258,15 @@ def test_gemm_errors_before_launch(L):
     assert gm(a=None) == -1 and gm(sb=None) == -1 and gm(c=None) == -1
     assert gm(a=odd) == -5 and gm(b=odd) == -5 and gm(c=odd) == -5 and gm(sa=P(0x10002)) == -5
     assert gm(m=0) == 0 and gm(n=0, c=None) == 0               # nothing to do
+    gq = L.pqb_gemm_fp8_blockscaled_quant
+
+    def gmq(a=fake, sa=fake, b=fake, sb=fake, m=256, n=256, k=512, c=fake, cs=fake):
+        return gq(a, sa, b, sb, m, n, k, c, cs, None)
+
+    assert gmq(k=500) == -4 and gmq(n=200) == -4
+    assert gmq(cs=None) == -1 and gmq(c=None) == -1 and gmq(a=None) == -1
+    assert gmq(cs=P(0x10002)) == -5 and gmq(c=odd) == -5
+    assert gmq(m=0) == 0
 
 
 def test_head_index_by_multiply_high_is_exact():

@@ -173,3 +173,41 @@ def test_gemm_full_size_sampled(pqb):
     tol = tolerance(an[rows], san[rows], bn, sbn, S)
     got = c[torch.from_numpy(rows).to(DEV)].float().cpu().numpy().astype(np.float64)
     assert np.all(np.abs(got - want) <= tol + 2.0 ** -8 * (np.abs(want) + tol))
+
+
+@pytest.mark.parametrize("shape", [(256, 384, 512), (100, 256, 256), (300, 640, 1152), (1, 128, 128)])
+def test_gemm_fused_fp8_quant_matches_oracle_quantizer(pqb, shape):
+    """The fused epilogue: its codes and scales equal the oracle's FP8 1x128
+    quantization of the GEMM's own float32 result (checked against the oracle
+    GEMM above), byte for byte."""
+    M, N, K = shape
+    r = rng(f"fused{shape}")
+    a, b = random_codes(r, (M, K)), random_codes(r, (N, K))
+    sa = (r.uniform(0.5, 2, (M, K // 128)) * 2.0 ** r.integers(-6, 6, (M, 1))).astype(np.float32)
+    sb = (r.uniform(0.5, 2, (N // 128, K // 128)) * 2.0 ** -8).astype(np.float32)
+    ad, sad, bd, sbd = to_dev(a), to_dev(sa), to_dev(b), to_dev(sb)
+    c32 = pqb.gemm_fp8_blockscaled(ad, sad, bd, sbd, out_dtype=torch.float32).cpu().numpy()
+    codes, scales = pqb.gemm_fp8_blockscaled_quant(ad, sad, bd, sbd)
+    oc, os_ = oracle.fp8_quantize(c32[None], "1x128")
+    assert np.array_equal(scales.cpu().numpy().view(np.int32).reshape(-1), os_.view(np.int32).reshape(-1))
+    assert np.array_equal(codes.cpu().numpy().reshape(-1), oc.reshape(-1))
+    if M <= 300:
+        check(pqb, a, sa, b, sb, f"fused {shape} (float32 result)")
+
+
+def test_gemm_fused_quant_full_size_sampled(pqb):
+    """Fused GEMM + 1x128 quantization at the benchmark's shape: sampled rows of
+    the codes and scales against the oracle quantizer on the GEMM's float32 rows."""
+    x = synth.fp8_activation(rows=8192, cols=2048, device=DEV)
+    w = synth.fp8_weight(device=DEV)
+    qa = pqb.quantize(x, "fp8_e4m3", "1x128")
+    qw = pqb.quantize(w, "fp8_e4m3", "128x128")
+    M, N, K = 8192, 7168, 2048
+    args = (qa.codes.reshape(M, K), qa.scales.reshape(M, K // 128), qw.codes.reshape(N, K),
+            qw.scales.reshape(N // 128, K // 128))
+    codes, scales = pqb.gemm_fp8_blockscaled_quant(*args)
+    c32 = pqb.gemm_fp8_blockscaled(*args, out_dtype=torch.float32)
+    rows = torch.from_numpy(np.sort(rng("fq").choice(M, 32, replace=False))).to(DEV)
+    oc, os_ = oracle.fp8_quantize(c32[rows].cpu().numpy()[None], "1x128")
+    assert np.array_equal(codes[rows].cpu().numpy().reshape(-1), oc.reshape(-1))
+    assert np.array_equal(scales[rows].cpu().numpy().reshape(-1).view(np.int32), os_.reshape(-1).view(np.int32))
