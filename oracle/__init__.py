@@ -474,3 +474,33 @@ def fp8_block_gemm(a_codes, a_scales, b_codes, b_scales, abs_sum=False):
         if abs_sum:
             S += np.abs(s) * (np.abs(a[:, ks]) @ np.abs(b[:, ks]).T)
     return (C, S) if abs_sum else C
+
+
+# --------------------------------------------------------------------------
+# W4A16 product (a consumer of the INT4 group-128 codes)
+# --------------------------------------------------------------------------
+
+def w4a16_gemv(x, codes, scales, zeros, abs_sum=False):
+    """y = x @ dequant(W)^T for bf16 activations x [M, K] and an INT4 group-128
+    asymmetric weight W [N, K] in the engine's layout (codes [N, K/2], bf16
+    scales [N, K/128], zero-point nibbles over the flat group index): page "14.
+    量化：让每一步搬更少的字节", 路线一 (W4A16: 4-bit weights read from memory,
+    unpacked and dequantized to 16 bits, then multiplied; the Marlin role).
+
+    The dequantized weights are the oracle's own int4_dequantize values, (q -
+    z) * s, exact in float32; x is widened from bf16 exactly; the product is
+    the float64 matmul (every term is exact in float64, the sums round at
+    2^-53).  Returns y as float64 [M, N]; with abs_sum, also sum_k |x| |w|,
+    which sets the scale of a float32 evaluation's error.  x may be a torch
+    bf16 tensor or raw bf16 bits (uint16)."""
+    if hasattr(x, "dtype") and str(x.dtype) == "torch.bfloat16":
+        xb = x.contiguous().view(__import__("torch").int16).numpy().view(np.uint16)
+    else:
+        xb = np.ascontiguousarray(x, np.uint16)
+    M, K = xb.shape
+    codes = np.ascontiguousarray(codes, np.uint8)
+    N = codes.size * 2 // K
+    w = int4_dequantize(codes.reshape(1, N, K // 2), scales, zeros)[0].astype(np.float64)
+    xf = bf16_bits_to_f32(xb).astype(np.float64)
+    y = xf @ w.T
+    return (y, np.abs(xf) @ np.abs(w).T) if abs_sum else y
