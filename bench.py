@@ -306,6 +306,8 @@ def bench_extras(torch, eng, synth, reps, only=None):
         out.update(bench_kv(torch, eng, synth, reps))
     if want("gemm_fp8_bs_8192x7168x2048_bf16", "gemm_fp8_bs_8192x2048x7168_bf16"):
         out.update(bench_gemm(torch, eng, synth, reps))
+    if want("llama8b_224w_int4_g128_w4a16_decode_m1_one_batch"):
+        out.update(bench_w4a16(torch, eng, synth, reps))
     if want("llama8b_224w_bf16_int4_g128"):
         out.update(bench_llama_int4(torch, eng, synth))
     return out
@@ -457,6 +459,67 @@ def bench_gemm(torch, eng, synth, reps):
                   "epilogue; unfused = bf16 GEMM output, then the 1x128 quantizer on it"}
         log(f"{key} fused fp8 1x128: {fm[0] * 1e3:.1f} us vs unfused {um[0] * 1e3:.1f} us")
         del x, w, qa, qw, a, b, c, cc, cs, qbuf
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_w4a16(torch, eng, synth, reps):
+    """W4A16 decode over the 224 Llama-3.1-8B-shaped weights in INT4 g128: one
+    token (M = 1) and a batch of 4, every weight read once per step."""
+    dev = torch.device("cuda:0")
+    from precision_quantization_block_amd.synth import LLAMA_LAYERS, LLAMA_PROJ
+    ws, wbytes = [], 0
+    for layer in range(LLAMA_LAYERS):
+        for p, (_, r, c) in enumerate(LLAMA_PROJ):
+            w = synth.llama_weight(layer, p, device=dev)
+            b = eng.alloc("int4_asym", "grp128", (1, r, c), dev)
+            eng.quantize(w, "int4_asym", "grp128", (1, r, c), b)
+            ws.append((r, c, b))
+            wbytes += out_bytes(b["sizes"])
+            del w
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    J = eng.pqb.pqb._W4Job
+    out = {}
+    per_layer = len(LLAMA_PROJ)
+    for M in (1, 4):
+        g = torch.Generator(device=dev).manual_seed(77)
+        xs = {K: torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
+              for K in sorted({c for _, c, _ in ws})}
+        ys = [torch.empty((M, r), dtype=torch.bfloat16, device=dev) for r, _, _ in ws]
+        jobs = [J(xs[c].data_ptr(), b["codes"].data_ptr(), b["scales"].data_ptr(),
+                  b["aux"].data_ptr(), y.data_ptr(), r, c) for (r, c, b), y in zip(ws, ys)]
+
+        def batch(js):
+            arr = (J * len(js))(*js)
+            return lambda: eng.L.pqb_gemv_w4a16_batch(arr, len(js), M, 1, eng.stream)
+
+        # one decode step three ways: every weight its own launch; per layer the
+        # projections that share an input together (q k v | o | gate up | down);
+        # all 224 weights in one batch call (7 launches of up to 32)
+        single = [batch([j]) for j in jobs]
+        grouped = []
+        for L0 in range(0, len(jobs), per_layer):
+            lj = jobs[L0:L0 + per_layer]
+            grouped += [batch(lj[0:3]), batch(lj[3:4]), batch(lj[4:6]), batch(lj[6:7])]
+        whole = [batch(jobs)]
+        nb = wbytes + sum(2 * M * c + 2 * M * r for r, c, _ in ws)
+        for name, calls in (("per_weight", single), ("per_layer_groups", grouped),
+                            ("one_batch", whole)):
+            def step(i, calls=calls):
+                for f in calls:
+                    rc = f()
+                    if rc != 0:
+                        raise RuntimeError(f"pqb_gemv_w4a16_batch: status {rc}")
+
+            t = time_reps(torch, step, max(5, reps // 4), 2)
+            key = f"llama8b_224w_int4_g128_w4a16_decode_m{M}_{name}"
+            out[key] = rec(nb, t, op=f"W4A16 product, M = {M}, all 224 weights, {name}",
+                           calls=len(calls))
+            out[key]["ms_per_step"] = round(t[0], 4)
+            log(f"w4a16 decode M={M} {name}: {t[0]:.3f} ms per step, {out[key]['gbs']} GB/s")
+    del ws
     torch.cuda.empty_cache()
     return out
 

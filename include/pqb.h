@@ -289,6 +289,41 @@ pqb_status pqb_gemm_fp8_blockscaled_quant(const uint8_t* a, const float* a_scale
                                           int64_t n, int64_t k, uint8_t* c_codes,
                                           float* c_scales, void* stream);
 
+/* W4A16 product, the consumer of the INT4 group-128 codes (page "14. 量化：让
+ * 每一步搬更少的字节", 路线一: 4-bit weights read from memory, unpacked and
+ * dequantized to 16 bits, then multiplied):
+ *   y[m, n] = sum_k x[m, k] * (q[n, k] - z[n, k/128]) * s[n, k/128].
+ * x: bf16 activations [m, k] (decode batch, 1 <= m <= 8); codes / scales /
+ * zeros: the INT4_ASYM x GRP_128 layout pqb_quantize writes for a [1, n, k]
+ * weight (codes u8 [n, k/2], bf16 scales [n, k/128], zero-point nibbles over
+ * the flat group index); y: [m, n] row-major of out_dtype.  Evaluated in
+ * float32 with FMAs: per 32 weights of one group, s * (sum x (q + 8) - (8 + z)
+ * * sum x), then a sum over the units; the error against exact arithmetic is
+ * at most about (40 + k/2048) * 2^-24 * sum_k |s| |x| (|q + 8| + |8 + z|).
+ * Shape rules: k % 128 == 0, m <= 8, n * (k/128) < 2^31, k < 2^31; m = 0 or
+ * n = 0 does nothing.  Alignment: x and codes 16 bytes, scales 2, y 4.
+ * Errors, before any launch: PQB_ERR_ENUM (out_dtype), PQB_ERR_SHAPE,
+ * PQB_ERR_NULL, PQB_ERR_ALIGN. */
+pqb_status pqb_gemv_w4a16(const void* x, int64_t m, const uint8_t* codes, const void* scales,
+                          const uint8_t* zeros, int64_t n, int64_t k, pqb_dtype out_dtype,
+                          void* y, void* stream);
+
+/* Several W4A16 products in as few launches as possible (up to 32 per
+ * launch), e.g. the projections of a layer that share their input.  Each job
+ * is one pqb_gemv_w4a16 call (same rules); all jobs share m and out_dtype.
+ * Every job is validated before anything is enqueued.  `jobs` is a host array
+ * and may be reused once the call returns; outputs must not overlap. */
+typedef struct pqb_w4a16_job {
+  const void* x;        /* bf16 [m, k] */
+  const uint8_t* codes; /* INT4 group-128 weight [n, k] */
+  const void* scales;
+  const uint8_t* zeros;
+  void* y;              /* [m, n] of out_dtype */
+  int64_t n, k;
+} pqb_w4a16_job;
+pqb_status pqb_gemv_w4a16_batch(const pqb_w4a16_job* jobs, int64_t njobs, int64_t m,
+                                pqb_dtype out_dtype, void* stream);
+
 /* Element codecs exposed for testing the rounding rules on arrays of float32:
  * E4M3 of y (round-to-nearest-even; |y| must not exceed 464) into one byte
  * per element; E2M1 of y (ties to the smaller magnitude, saturating at 6)

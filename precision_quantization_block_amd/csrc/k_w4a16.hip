@@ -1,0 +1,237 @@
+// W4A16 product, the consumer of the INT4 group-128 codes (page "14. 量化：让
+// 每一步搬更少的字节", 路线一: the 4-bit weights are read from memory,
+// unpacked and dequantized to 16 bits, and multiplied, which is what cuts
+// decode time):
+//
+//   y[m, n] = sum_k x[m, k] * (q[n, k] - z[n, g]) * s[n, g],   g = k / 128,
+//
+// for bf16 activations x [M, K], M <= 8 (decode), and a weight in the layout
+// pqb_quantize writes for INT4_ASYM x GRP_128: codes [N, K / 2] (element 2i in
+// the low nibble of byte i, two's complement), bf16 scales [N, K / 128],
+// zero-point nibbles over the flat group index n * K / 128 + g.
+//
+// With q + 8 = (nibble ^ 8) in 0 .. 15 and c = 8 + z, a unit of 32 weights
+// inside one group contributes s * (sum x (q + 8) - c * sum x): the products x
+// (q + 8) are exact in float32, each nibble costs one byte-to-float conversion
+// (v_cvt_f32_ubyte) and one FMA per activation row, and the 4-bit unpacking is
+// two AND / shift / XOR steps per four weights.
+//
+// Lane l of a wave handles code units u = l, l + 64, ... (16 bytes = 32
+// weights each) of kR consecutive rows; every wave load instruction reads 1
+// KiB of one row.  The units are walked as items of kSteps units per lane, and
+// the codes of the next item are loaded before the current one is computed.  The activations are read once per unit and
+// reused for the kR rows.  A wave-wide sum ends each row.
+// One launch serves up to kW4MaxJobs independent products (the projections
+// that share an input, or any batch of weights): workgroup b belongs to the
+// job whose range of workgroups holds b.
+#include "device.h"
+#include "launch.h"
+
+namespace pqb {
+namespace {
+
+constexpr int kWThreads = 256;  // 4 waves
+// Two launch shapes, chosen by the rows one launch covers (measured on the
+// Llama-3.1-8B-shaped weights): 2 rows per wave with 2 units per lane in
+// flight when a launch holds a few projections (more waves), 8 rows with 1
+// unit when it holds hundreds of thousands of rows (the activations then
+// serve 8 rows per load).
+constexpr int kBigLaunchRows = 1 << 16;
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Low and high nibbles of the 4 bytes of w as bytes, each plus 8 (sign flip).
+__device__ __forceinline__ void nibbles_plus8(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  lo = (w & 0x0F0F0F0Fu) ^ 0x08080808u;
+  hi = ((w >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;
+}
+
+__device__ __forceinline__ float byte_f(uint32_t v, int j) {
+  return (float)((v >> (8 * j)) & 0xFFu);  // v_cvt_f32_ubyte<j>
+}
+
+template <int kM, bool kBf16Out, int kR, int kSteps>
+__global__ __launch_bounds__(kWThreads) void k_w4a16(const W4Args a) {
+  constexpr int kBlocks = 1;
+  int jb = 0;
+  while (jb + 1 < a.njobs && a.wg_begin[jb + 1] <= (int)blockIdx.x) ++jb;
+  const uint16_t* __restrict__ x = a.job[jb].x;
+  const uint8_t* __restrict__ codes = a.job[jb].codes;
+  const uint16_t* __restrict__ scales = a.job[jb].scales;
+  const uint8_t* __restrict__ zeros = a.job[jb].zeros;
+  void* __restrict__ y = a.job[jb].y;
+  const int N = a.job[jb].N, K = a.job[jb].K;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  // This wave's rows: kBlocks blocks of kR, walked as items (block, chunk of
+  // kSteps units per lane); the codes of item i + 1 are loaded before item i
+  // is computed.
+  const int nw0 = (((int)blockIdx.x - a.wg_begin[jb]) * (kWThreads / 64) + wave) * kR * kBlocks;
+  if (nw0 >= N) return;
+  const int U = K / 32, G = K / 128;
+  const int chunks = (U + 64 * kSteps - 1) / (64 * kSteps);
+  const int blocks = min(kBlocks, (N - nw0 + kR - 1) / kR);
+  const int items = blocks * chunks;
+
+  auto load_item = [&](int it, uint4 (&c)[kSteps][kR]) {
+    const int b = it / chunks, u0 = (it - b * chunks) * 64 * kSteps;
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      const int u = u0 + 64 * s + lane;
+#pragma unroll
+      for (int r = 0; r < kR; ++r) {
+        const int row = min(nw0 + b * kR + r, N - 1);   // rows past N are never stored
+        c[s][r] = u < U ? ld_nt16(codes + (int64_t)row * (K / 2) + 16 * u) : uint4{0, 0, 0, 0};
+      }
+    }
+  };
+
+  float acc[kM][kR];
+#pragma unroll
+  for (int m = 0; m < kM; ++m)
+#pragma unroll
+    for (int r = 0; r < kR; ++r) acc[m][r] = 0.0f;
+  uint4 cur[kSteps][kR], nxt[kSteps][kR];
+  load_item(0, cur);
+  for (int it = 0; it < items; ++it) {
+    if (it + 1 < items) load_item(it + 1, nxt);
+    const int b = it / chunks, u0 = (it - b * chunks) * 64 * kSteps;
+    const int n0 = nw0 + b * kR;
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      const int u = u0 + 64 * s + lane;
+      if (u >= U) break;
+      // activations of this unit: 16 bf16 pairs per row m
+      uint32_t xd[kM][16];
+      float xs[kM];
+#pragma unroll
+      for (int m = 0; m < kM; ++m) {
+        const uint4* p = reinterpret_cast<const uint4*>(x + (int64_t)m * K + 32 * u);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint4 v = p[i];
+          xd[m][4 * i] = v.x;
+          xd[m][4 * i + 1] = v.y;
+          xd[m][4 * i + 2] = v.z;
+          xd[m][4 * i + 3] = v.w;
+        }
+        float t = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) t += as_f(xd[m][i] << 16) + as_f(xd[m][i] & 0xFFFF0000u);
+        xs[m] = t;
+      }
+      const int g = u >> 2;
+#pragma unroll
+      for (int r = 0; r < kR; ++r) {
+        const int gi = min(n0 + r, N - 1) * G + g;
+        const float sc = as_f((uint32_t)scales[gi] << 16);
+        const int zn = (zeros[gi >> 1] >> (4 * (gi & 1))) & 0xF;
+        const float cz = (float)(8 + (zn >= 8 ? zn - 16 : zn));
+        const uint32_t w4[4] = {cur[s][r].x, cur[s][r].y, cur[s][r].z, cur[s][r].w};
+        float dot[kM];
+#pragma unroll
+        for (int m = 0; m < kM; ++m) dot[m] = 0.0f;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          uint32_t lo, hi;
+          nibbles_plus8(w4[d], lo, hi);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float ql = byte_f(lo, j), qh = byte_f(hi, j);
+#pragma unroll
+            for (int m = 0; m < kM; ++m) {
+              const uint32_t xp = xd[m][4 * d + j];   // elements 8d + 2j (low), 8d + 2j + 1
+              dot[m] = __builtin_fmaf(as_f(xp << 16), ql, dot[m]);
+              dot[m] = __builtin_fmaf(as_f(xp & 0xFFFF0000u), qh, dot[m]);
+            }
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < kM; ++m)
+          acc[m][r] = __builtin_fmaf(sc, __builtin_fmaf(-cz, xs[m], dot[m]), acc[m][r]);
+      }
+    }
+    if (it - b * chunks == chunks - 1) {   // last chunk of block b: finish its rows
+#pragma unroll
+      for (int m = 0; m < kM; ++m)
+#pragma unroll
+        for (int r = 0; r < kR; ++r) {
+          const float v = wave_sum(acc[m][r]);
+          acc[m][r] = 0.0f;
+          if (lane == 0 && n0 + r < N) {
+            if constexpr (kBf16Out)
+              reinterpret_cast<uint16_t*>(y)[(int64_t)m * N + n0 + r] = (uint16_t)bf16_rne_bits(v);
+            else
+              reinterpret_cast<float*>(y)[(int64_t)m * N + n0 + r] = v;
+          }
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s)
+#pragma unroll
+      for (int r = 0; r < kR; ++r) cur[s][r] = nxt[s][r];
+  }
+}
+
+template <int kM, int kR, int kSteps>
+void launch_m(const W4Args& a, int wgs, bool out_bf16, hipStream_t st) {
+  if (out_bf16)
+    hipLaunchKernelGGL((k_w4a16<kM, true, kR, kSteps>), dim3((unsigned)wgs), dim3(kWThreads), 0, st,
+                       a);
+  else
+    hipLaunchKernelGGL((k_w4a16<kM, false, kR, kSteps>), dim3((unsigned)wgs), dim3(kWThreads), 0,
+                       st, a);
+}
+
+template <int kM, int kR, int kSteps>
+hipError_t launch_shape(W4Args& a, bool out_bf16, hipStream_t st) {
+  constexpr int rows_per_wg = (kWThreads / 64) * kR;
+  int wg = 0;
+  for (int i = 0; i < a.njobs; ++i) {
+    a.wg_begin[i] = wg;
+    wg += (a.job[i].N + rows_per_wg - 1) / rows_per_wg;
+  }
+  a.wg_begin[a.njobs] = wg;
+  if (wg > 0) launch_m<kM, kR, kSteps>(a, wg, out_bf16, st);
+  return hipGetLastError();
+}
+
+// Shapes per M that keep every instantiation free of register spills: the
+// 8-row shape only for M <= 2, 1 row per wave from M = 6.
+hipError_t launch_args(W4Args& a, int M, bool big, bool out_bf16, hipStream_t st) {
+  switch (M) {
+    case 1: return big ? launch_shape<1, 8, 1>(a, out_bf16, st) : launch_shape<1, 2, 2>(a, out_bf16, st);
+    case 2: return big ? launch_shape<2, 8, 1>(a, out_bf16, st) : launch_shape<2, 2, 2>(a, out_bf16, st);
+    case 3: return launch_shape<3, 2, 2>(a, out_bf16, st);
+    case 4: return launch_shape<4, 2, 2>(a, out_bf16, st);
+    case 5: return launch_shape<5, 2, 2>(a, out_bf16, st);
+    case 6: return launch_shape<6, 1, 2>(a, out_bf16, st);
+    case 7: return launch_shape<7, 1, 2>(a, out_bf16, st);
+    case 8: return launch_shape<8, 1, 2>(a, out_bf16, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_w4a16(const W4Job* jobs, int njobs, int M, bool out_bf16, hipStream_t st) {
+  for (int base = 0; base < njobs; base += kW4MaxJobs) {
+    const int n = njobs - base < kW4MaxJobs ? njobs - base : kW4MaxJobs;
+    W4Args a{};
+    a.njobs = n;
+    int64_t rows = 0;
+    for (int i = 0; i < n; ++i) {
+      a.job[i] = jobs[base + i];
+      rows += a.job[i].N;
+    }
+    const hipError_t e = launch_args(a, M, rows >= kBigLaunchRows, out_bf16, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace pqb

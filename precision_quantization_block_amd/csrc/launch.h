@@ -121,6 +121,25 @@ hipError_t launch_gemm_fp8_bs(const uint8_t* a, const float* a_scales, const uin
                               const float* b_scales, int64_t M, int64_t N, int64_t K, int out,
                               void* c, float* c_scales, hipStream_t st);
 
+// W4A16 products y [M, N] = x [M, K] (bf16) x dequant(W)^T for INT4 group-128
+// asymmetric weights W [N, K] (codes, bf16 scales, zero-point nibbles); all
+// jobs of a call share M (1 <= M <= 8); K % 128 == 0; N * K / 128 < 2^31.
+struct W4Job {
+  const uint16_t* x;
+  const uint8_t* codes;
+  const uint16_t* scales;
+  const uint8_t* zeros;
+  void* y;
+  int32_t N, K;
+};
+constexpr int kW4MaxJobs = 32;
+struct W4Args {
+  int32_t njobs;
+  int32_t wg_begin[kW4MaxJobs + 1];
+  W4Job job[kW4MaxJobs];
+};
+hipError_t launch_w4a16(const W4Job* jobs, int njobs, int M, bool out_bf16, hipStream_t st);
+
 // ---- element codecs ---------------------------------------------------------
 hipError_t launch_encode_elem(const float* y, int64_t n, uint8_t* out, hipStream_t st, int elem);
 hipError_t launch_encode_e2m1(const float* y, int64_t n, uint8_t* out, hipStream_t st);

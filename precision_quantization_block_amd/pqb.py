@@ -45,6 +45,12 @@ class _Job(ctypes.Structure):
                 ("gran", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
+class _W4Job(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("zeros", ctypes.c_void_p), ("y", ctypes.c_void_p), ("n", ctypes.c_int64),
+                ("k", ctypes.c_int64)]
+
+
 class _Sizes(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_size_t), ("scales", ctypes.c_size_t),
                 ("aux", ctypes.c_size_t), ("workspace", ctypes.c_size_t)]
@@ -73,13 +79,16 @@ def lib():
         L.pqb_kv_read_kivi.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I, I, P, P, P]
         L.pqb_gemm_fp8_blockscaled.argtypes = [P, P, P, P, I64, I64, I64, I, P, P]
         L.pqb_gemm_fp8_blockscaled_quant.argtypes = [P, P, P, P, I64, I64, I64, P, P, P]
+        L.pqb_gemv_w4a16.argtypes = [P, I64, P, P, P, I64, I64, I, P, P]
+        L.pqb_gemv_w4a16_batch.argtypes = [ctypes.POINTER(_W4Job), I64, I64, I, P]
         L.pqb_encode_e4m3.argtypes = [P, I64, P, P]
         L.pqb_encode_e5m2.argtypes = [P, I64, P, P]
         L.pqb_encode_e2m1.argtypes = [P, I64, P, P]
         for f in ("pqb_query_sizes", "pqb_quantize", "pqb_quantize_batch", "pqb_dequantize",
                   "pqb_kv_write_fp8", "pqb_kv_write_fp8_ex", "pqb_kv_write_kivi",
                   "pqb_kv_read_kivi", "pqb_gemm_fp8_blockscaled",
-                  "pqb_gemm_fp8_blockscaled_quant",
+                  "pqb_gemm_fp8_blockscaled_quant", "pqb_gemv_w4a16",
+                  "pqb_gemv_w4a16_batch",
                   "pqb_encode_e4m3", "pqb_encode_e5m2", "pqb_encode_e2m1"):
             getattr(L, f).restype = I
         _lib = L
@@ -406,6 +415,53 @@ def gemm_fp8_blockscaled_quant(a_codes: torch.Tensor, a_scales: torch.Tensor,
                                                 _ptr(codes), _ptr(scales), _stream(a.device)),
            "gemm_fp8_blockscaled_quant")
     return codes, scales
+
+
+def gemv_w4a16(x: torch.Tensor, weight, out_dtype=torch.float32) -> torch.Tensor:
+    """y = x @ dequant(W)^T for bf16 activations x [M, K] (M <= 8) and an INT4
+    group-128 weight: a Quantized from quantize(w, "int4_asym") or a
+    (codes, scales, zeros) triple in that layout, W being [N, K]."""
+    x = _dev_tensor(x, "x", (torch.bfloat16,))
+    if isinstance(weight, Quantized):
+        codes, scales, zeros = weight.codes, weight.scales, weight.aux
+    else:
+        codes, scales, zeros = weight
+    codes = _dev_tensor(codes, "codes", (torch.uint8,))
+    scales = _dev_tensor(scales, "scales", (torch.bfloat16, torch.int16, torch.uint8))
+    zeros = _dev_tensor(zeros, "zeros", (torch.uint8,))
+    M, K = (1, x.shape[0]) if x.dim() == 1 else (x.shape[-2], x.shape[-1])
+    N = codes.numel() * 2 // K if K else 0
+    if K % 128 or codes.numel() != N * K // 2:
+        raise ValueError("codes must hold N x K / 2 bytes with K a multiple of 128")
+    y = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    _check(lib().pqb_gemv_w4a16(_ptr(x), M, _ptr(codes), _ptr(scales), _ptr(zeros), N, K,
+                                BF16 if out_dtype == torch.bfloat16 else F32, _ptr(y),
+                                _stream(x.device)), "gemv_w4a16")
+    return y
+
+
+def gemv_w4a16_batch(xs, weights, out_dtype=torch.float32):
+    """Several W4A16 products in as few launches as possible: xs[i] (bf16 [M, K_i],
+    one M for all) times weights[i] (Quantized INT4 g128, or (codes, scales,
+    zeros)).  Returns the list of outputs [M, N_i]."""
+    keep, ys = [], []
+    arr = (_W4Job * len(xs))()
+    for i, (x, wgt) in enumerate(zip(xs, weights)):
+        x = _dev_tensor(x, "x", (torch.bfloat16,))
+        c, s, z = (wgt.codes, wgt.scales, wgt.aux) if isinstance(wgt, Quantized) else wgt
+        K = x.shape[-1]
+        M = x.numel() // K
+        N = c.numel() * 2 // K
+        y = torch.empty((M, N), dtype=out_dtype, device=x.device)
+        keep += [x, c, s, z]
+        ys.append(y)
+        arr[i] = _W4Job(x.data_ptr(), c.data_ptr(), s.data_ptr(), z.data_ptr(), y.data_ptr(), N, K)
+    M = ys[0].shape[0] if ys else 0
+    if any(y.shape[0] != M for y in ys):
+        raise ValueError("all jobs must share M")
+    _check(lib().pqb_gemv_w4a16_batch(arr, len(xs), M, BF16 if out_dtype == torch.bfloat16 else F32,
+                                      _stream(ys[0].device) if ys else None), "gemv_w4a16_batch")
+    return ys
 
 
 def encode_e5m2(y: torch.Tensor) -> torch.Tensor:

@@ -1,0 +1,157 @@
+"""GPU parity of the W4A16 product (pqb_gemv_w4a16) against the oracle's
+float64 y = x @ dequant(W)^T, element by element, within a bound derived from
+the kernel's float32 evaluation.
+
+For each unit of 32 weights of one group, the kernel forms s * (sum x (q + 8) -
+(8 + z) sum x).  The products x (q + 8) are exact.  Each 32-term sum rounds at
+most 31 times, and the two fused multiply-adds once each.  The units of a row
+are accumulated per lane (at most K/2048 + 1 additions), then summed over 64
+lanes (6 levels).  First order, the error is at most
+  (40 + K/2048) * 2^-24 * sum_k |s| |x| (|q + 8| + |8 + z|),
+plus half a bf16 ulp of the value for bf16 output."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from precision_quantization_block_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+U = 2.0 ** -24
+
+
+@pytest.fixture(scope="module")
+def pqb():
+    import precision_quantization_block_amd as p
+    p.lib()
+    return p
+
+
+def rng(tag):
+    return np.random.default_rng(zlib.crc32(tag.encode()))
+
+
+def bound(xb, codes, scales, zeros):
+    """sum_k |s| |x| (|q + 8| + |8 + z|) for every (m, n)."""
+    N = codes.shape[-2]
+    K = codes.shape[-1] * 2
+    c = codes.reshape(N, K // 2).astype(np.int32)
+    q = np.empty((N, K), np.int32)
+    q[:, 0::2] = c & 0xF
+    q[:, 1::2] = c >> 4
+    q = np.where(q >= 8, q - 16, q)
+    G = K // 128
+    zn = np.stack([zeros & 0xF, zeros >> 4], 1).reshape(-1)[:N * G].astype(np.int32).reshape(N, G)
+    z = np.where(zn >= 8, zn - 16, zn)
+    s = np.abs(oracle.bf16_bits_to_f32(scales.reshape(N, G)).astype(np.float64))
+    A = np.repeat(s, 128, axis=1) * (np.abs(q + 8) + np.repeat(np.abs(8 + z), 128, axis=1))
+    return np.abs(oracle.bf16_bits_to_f32(xb).astype(np.float64)) @ A.T
+
+
+def bf16_bits(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16) \
+        .view(torch.int16).numpy().view(np.uint16)
+
+
+def check(pqb, xb, codes, scales, zeros, what):
+    M, K = xb.shape
+    N = codes.shape[-2]
+    want = oracle.w4a16_gemv(xb, codes, scales, zeros)
+    tol = (40 + K // 2048) * U * bound(xb, codes, scales, zeros) * 1.01 + 1e-30
+    xd = torch.from_numpy(xb.view(np.int16)).to(DEV).view(torch.bfloat16)
+    w = tuple(torch.from_numpy(np.ascontiguousarray(t)).to(DEV) for t in (codes, scales.view(np.int16), zeros))
+    for dt in (torch.float32, torch.bfloat16):
+        got = pqb.gemv_w4a16(xd, w, out_dtype=dt).float().cpu().numpy().astype(np.float64)
+        b = tol if dt == torch.float32 else tol + 2.0 ** -8 * (np.abs(want) + tol)
+        err = np.abs(got - want)
+        bad = np.argwhere(err > b)
+        assert bad.size == 0, (f"{what} {dt}: {len(bad)} outside the bound, first {bad[:3].tolist()}, "
+                               f"err {err[tuple(bad[0])]:.3e} bound {b[tuple(bad[0])]:.3e}")
+
+
+SHAPES = [(1, 128, 128), (1, 1000, 4096), (3, 333, 2176), (8, 64, 14336), (4, 257, 384),
+          (2, 4096, 1024), (5, 9, 128 * 50)]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_w4a16_matches_oracle(pqb, shape):
+    M, N, K = shape
+    r = rng(f"w4{shape}")
+    w = (0.02 * r.standard_normal((N, K)) * np.exp(r.uniform(-2, 2, (N, 1)))).astype(np.float32)
+    codes, scales, zeros = oracle.int4_quantize(w[None])
+    x = bf16_bits(r.standard_normal((M, K)) * np.exp(r.uniform(-3, 3, (1, K))))
+    check(pqb, x, codes[0], scales[0], zeros, f"w4a16 {shape}")
+
+
+def test_w4a16_exact_integer_case(pqb):
+    """Dequantized weights that are small integers and integer activations:
+    every term and every partial sum is an integer below 2^24, so the float32
+    result equals the integer matmul exactly."""
+    r = rng("int")
+    N, K = 96, 1024
+    w = r.integers(-7, 8, (N, K)).astype(np.float32)
+    w[:, ::128], w[:, 1::128] = 7.0, -8.0
+    codes, scales, zeros = oracle.int4_quantize(w[None])
+    x = r.integers(-20, 21, (2, K)).astype(np.float32)
+    xb = bf16_bits(x)
+    xd = torch.from_numpy(xb.view(np.int16)).to(DEV).view(torch.bfloat16)
+    wt = tuple(torch.from_numpy(np.ascontiguousarray(t)).to(DEV) for t in (codes[0], scales[0].view(np.int16), zeros))
+    got = pqb.gemv_w4a16(xd, wt, out_dtype=torch.float32).cpu().numpy()
+    assert np.array_equal(got.astype(np.int64), x.astype(np.int64) @ w.T.astype(np.int64))
+
+
+def test_w4a16_engine_quantized_llama_weights(pqb):
+    """The decode chain on the GPU: the engine quantizes Llama-3.1-8B-shaped
+    weights (gate [14336 x 4096] and down [4096 x 14336] of layer 0) to INT4
+    g128, byte-identical to the oracle's codes, and the product of one decode
+    token against them matches the oracle."""
+    r = rng("llama")
+    for proj in (4, 6):
+        w = synth.llama_weight(0, proj, device=DEV)
+        q = pqb.quantize(w, "int4_asym", "grp128")
+        N, K = w.shape
+        x = bf16_bits(r.standard_normal((1, K)))
+        c, s, z = q.codes.cpu().numpy().reshape(N, K // 2), q.scales.cpu().view(torch.int16).numpy() \
+            .view(np.uint16).reshape(N, K // 128), q.aux.cpu().numpy()
+        oc, os_, oz = oracle.int4_quantize(w.cpu()[None])
+        assert np.array_equal(c, oc[0]) and np.array_equal(s, os_[0]) and np.array_equal(z, oz)
+        check(pqb, x, c, s, z, f"llama proj {proj}")
+
+
+def test_w4a16_batch_equals_single_calls(pqb):
+    """A batch of 40 products of mixed shapes (two launches) gives, bit for bit,
+    the single-call results, which match the oracle above."""
+    r = rng("batch")
+    shapes = [(int(r.integers(1, 300)), 128 * int(r.integers(1, 40))) for _ in range(40)]
+    xs, ws = [], []
+    for N, K in shapes:
+        w = (0.02 * r.standard_normal((N, K))).astype(np.float32)
+        codes, scales, zeros = oracle.int4_quantize(w[None])
+        ws.append(tuple(torch.from_numpy(np.ascontiguousarray(t)).to(DEV)
+                        for t in (codes[0], scales[0].view(np.int16), zeros)))
+        xs.append(torch.from_numpy(bf16_bits(r.standard_normal((3, K))).view(np.int16)).to(DEV)
+                  .view(torch.bfloat16))
+    ys = pqb.gemv_w4a16_batch(xs, ws, out_dtype=torch.float32)
+    for i in (0, 7, 31, 32, 39):
+        one = pqb.gemv_w4a16(xs[i], ws[i], out_dtype=torch.float32)
+        assert torch.equal(ys[i], one), i
+    i = 33
+    c, s, z = (t.cpu().numpy() for t in ws[i])
+    check(pqb, xs[i].cpu().view(torch.int16).numpy().view(np.uint16), c, s.view(np.uint16), z,
+          "batch job 33")
+
+
+@pytest.mark.parametrize("M", [1, 2, 6])
+def test_w4a16_large_launch_shape(pqb, M):
+    """A launch of more than 65536 rows takes the 8-rows-per-wave shape (M <= 2);
+    M = 6 takes the 1-row shape.  Both against the oracle, with a ragged N."""
+    r = rng(f"big{M}")
+    N, K = 66001, 256
+    w = (0.02 * r.standard_normal((N, K))).astype(np.float32)
+    codes, scales, zeros = oracle.int4_quantize(w[None])
+    x = bf16_bits(r.standard_normal((M, K)))
+    check(pqb, x, codes[0], scales[0], zeros, f"large launch M={M}")
