@@ -98,38 +98,55 @@ __global__ __launch_bounds__(kWThreads) void k_w4a16(const W4Args a) {
   uint4 cur[kSteps][kR], nxt[kSteps][kR];
   load_item(0, cur);
   for (int it = 0; it < items; ++it) {
-    if (it + 1 < items) load_item(it + 1, nxt);
     const int b = it / chunks, u0 = (it - b * chunks) * 64 * kSteps;
     const int n0 = nw0 + b * kR;
+    // This item's activations, scales and zero-points are loaded before the
+    // next item's codes: loads complete in issue order, so waiting for them
+    // then does not wait for the prefetch.
+    uint32_t xd[kSteps][kM][16];
+    uint16_t sb[kSteps][kR];
+    uint8_t zb[kSteps][kR];
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
-      const int u = u0 + 64 * s + lane;
-      if (u >= U) break;
-      // activations of this unit: 16 bf16 pairs per row m
-      uint32_t xd[kM][16];
-      float xs[kM];
+      const int u = min(u0 + 64 * s + lane, U - 1);   // lanes past U compute nothing
 #pragma unroll
       for (int m = 0; m < kM; ++m) {
         const uint4* p = reinterpret_cast<const uint4*>(x + (int64_t)m * K + 32 * u);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const uint4 v = p[i];
-          xd[m][4 * i] = v.x;
-          xd[m][4 * i + 1] = v.y;
-          xd[m][4 * i + 2] = v.z;
-          xd[m][4 * i + 3] = v.w;
+          xd[s][m][4 * i] = v.x;
+          xd[s][m][4 * i + 1] = v.y;
+          xd[s][m][4 * i + 2] = v.z;
+          xd[s][m][4 * i + 3] = v.w;
         }
-        float t = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) t += as_f(xd[m][i] << 16) + as_f(xd[m][i] & 0xFFFF0000u);
-        xs[m] = t;
       }
-      const int g = u >> 2;
 #pragma unroll
       for (int r = 0; r < kR; ++r) {
-        const int gi = min(n0 + r, N - 1) * G + g;
-        const float sc = as_f((uint32_t)scales[gi] << 16);
-        const int zn = (zeros[gi >> 1] >> (4 * (gi & 1))) & 0xF;
+        const int gi = min(n0 + r, N - 1) * G + (u >> 2);
+        sb[s][r] = scales[gi];
+        zb[s][r] = zeros[gi >> 1];
+      }
+    }
+    if (it + 1 < items) load_item(it + 1, nxt);
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      const int u = u0 + 64 * s + lane;
+      if (u >= U) break;
+      float xs[kM];
+#pragma unroll
+      for (int m = 0; m < kM; ++m) {
+        float t = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          t += as_f(xd[s][m][i] << 16) + as_f(xd[s][m][i] & 0xFFFF0000u);
+        xs[m] = t;
+      }
+#pragma unroll
+      for (int r = 0; r < kR; ++r) {
+        const int gi = min(n0 + r, N - 1) * G + (u >> 2);
+        const float sc = as_f((uint32_t)sb[s][r] << 16);
+        const int zn = (zb[s][r] >> (4 * (gi & 1))) & 0xF;
         const float cz = (float)(8 + (zn >= 8 ? zn - 16 : zn));
         const uint32_t w4[4] = {cur[s][r].x, cur[s][r].y, cur[s][r].z, cur[s][r].w};
         float dot[kM];
@@ -144,7 +161,7 @@ __global__ __launch_bounds__(kWThreads) void k_w4a16(const W4Args a) {
             const float ql = byte_f(lo, j), qh = byte_f(hi, j);
 #pragma unroll
             for (int m = 0; m < kM; ++m) {
-              const uint32_t xp = xd[m][4 * d + j];   // elements 8d + 2j (low), 8d + 2j + 1
+              const uint32_t xp = xd[s][m][4 * d + j];   // elements 8d + 2j (low), 8d + 2j + 1
               dot[m] = __builtin_fmaf(as_f(xp << 16), ql, dot[m]);
               dot[m] = __builtin_fmaf(as_f(xp & 0xFFFF0000u), qh, dot[m]);
             }
@@ -200,18 +217,18 @@ hipError_t launch_shape(W4Args& a, bool out_bf16, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Shapes per M that keep every instantiation free of register spills: the
-// 8-row shape only for M <= 2, 1 row per wave from M = 6.
+// Shapes per M that keep every instantiation free of register spills and at
+// two or more waves per SIMD where possible: 2 units ahead only for M = 1.
 hipError_t launch_args(W4Args& a, int M, bool big, bool out_bf16, hipStream_t st) {
   switch (M) {
     case 1: return big ? launch_shape<1, 8, 1>(a, out_bf16, st) : launch_shape<1, 2, 2>(a, out_bf16, st);
-    case 2: return big ? launch_shape<2, 8, 1>(a, out_bf16, st) : launch_shape<2, 2, 2>(a, out_bf16, st);
-    case 3: return launch_shape<3, 2, 2>(a, out_bf16, st);
-    case 4: return launch_shape<4, 2, 2>(a, out_bf16, st);
-    case 5: return launch_shape<5, 2, 2>(a, out_bf16, st);
-    case 6: return launch_shape<6, 1, 2>(a, out_bf16, st);
-    case 7: return launch_shape<7, 1, 2>(a, out_bf16, st);
-    case 8: return launch_shape<8, 1, 2>(a, out_bf16, st);
+    case 2: return big ? launch_shape<2, 8, 1>(a, out_bf16, st) : launch_shape<2, 2, 1>(a, out_bf16, st);
+    case 3: return launch_shape<3, 2, 1>(a, out_bf16, st);
+    case 4: return launch_shape<4, 2, 1>(a, out_bf16, st);
+    case 5: return launch_shape<5, 2, 1>(a, out_bf16, st);
+    case 6: return launch_shape<6, 1, 1>(a, out_bf16, st);
+    case 7: return launch_shape<7, 1, 1>(a, out_bf16, st);
+    case 8: return launch_shape<8, 1, 1>(a, out_bf16, st);
     default: return hipErrorInvalidValue;
   }
 }
