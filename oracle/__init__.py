@@ -504,3 +504,31 @@ def w4a16_gemv(x, codes, scales, zeros, abs_sum=False):
     xf = bf16_bits_to_f32(xb).astype(np.float64)
     y = xf @ w.T
     return (y, np.abs(xf) @ np.abs(w).T) if abs_sum else y
+
+
+# --------------------------------------------------------------------------
+# MXFP4 x MXFP4 product (a consumer of the MXFP4 codes)
+# --------------------------------------------------------------------------
+
+def mxfp4_gemm(a_codes, a_scales, b_codes, b_scales, abs_sum=False):
+    """C = dequant(A) @ dequant(B)^T for two MXFP4 operands in the engine's
+    layout (E2M1 codes [rows, K/2], element 2i in the low nibble of byte i;
+    E8M0 scales [rows, K/32]): the product an MX-capable matrix core computes
+    from the codes and block scales directly (page "LLM 推理优化 · 量化学习笔记"
+    §4.5: MXFP4 is 32-element blocks with a shared E8M0 scale, and FP4 tensor
+    cores consume it natively).  The dequantized values are the oracle's own
+    mxfp4_dequantize results (+-V * 2^X, exact); the product is the float64
+    matmul.  Returns C [M, N] as float64; with abs_sum, also sum_k |a| |b|."""
+    a_codes = np.ascontiguousarray(a_codes, np.uint8)
+    b_codes = np.ascontiguousarray(b_codes, np.uint8)
+    M, Kh = a_codes.shape
+    N = b_codes.shape[0]
+    K = 2 * Kh
+    if b_codes.shape[1] != Kh or K % 32:
+        raise ValueError("need a [M, K/2], b [N, K/2] codes with K a multiple of 32")
+    a = mxfp4_dequantize(a_codes.reshape(1, M, Kh), np.asarray(a_scales, np.uint8).reshape(1, M, K // 32))[0]
+    b = mxfp4_dequantize(b_codes.reshape(1, N, Kh), np.asarray(b_scales, np.uint8).reshape(1, N, K // 32))[0]
+    a = a.astype(np.float64)
+    b = b.astype(np.float64)
+    C = a @ b.T
+    return (C, np.abs(a) @ np.abs(b).T) if abs_sum else C
