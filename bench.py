@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 FP8_MFMA_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 matrix peak (no sparsity)
+FP4_MFMA_PEAK_TFLOPS = 10100.0      # MI355X dense FP4 / FP6 matrix peak
 METRIC = "quantize-pack GB/s (bytes in+out) and % of HBM peak, per format"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "k_multi_fp8_w8a8_7168x2048_8192x7168_counters.json")
 KERNEL_SOURCES = ["precision_quantization_block_amd/csrc/k_multi.hip",
@@ -458,7 +459,26 @@ def bench_gemm(torch, eng, synth, reps):
             "op": "the same GEMM with its float32 result quantized to FP8 E4M3 1x128 in the "
                   "epilogue; unfused = bf16 GEMM output, then the 1x128 quantizer on it"}
         log(f"{key} fused fp8 1x128: {fm[0] * 1e3:.1f} us vs unfused {um[0] * 1e3:.1f} us")
-        del x, w, qa, qw, a, b, c, cc, cs, qbuf
+        # the same shapes with both operands in MXFP4, on the block-scaled matrix cores
+        ma, mw = eng.pqb.quantize(x, "mxfp4"), eng.pqb.quantize(w, "mxfp4")
+
+        def run_mx(i):
+            rc = eng.L.pqb_gemm_mxfp4(P(ma.codes), P(ma.scales), P(mw.codes), P(mw.scales), M, N, K,
+                                      1, P(c), eng.stream)
+            if rc != 0:
+                raise RuntimeError(f"pqb_gemm_mxfp4: status {rc}")
+
+        mean, med, mn = time_reps(torch, run_mx, max(10, reps), 3)
+        tf = flops / (mean * 1e-3) / 1e12
+        mkey = f"gemm_mxfp4_{M}x{N}x{K}_bf16"
+        out[mkey] = {"flops": flops, "ms": round(mean, 5), "ms_median": round(med, 5),
+                     "ms_min": round(mn, 5), "tflops": round(tf, 1),
+                     "frac_fp4_mfma_peak": round(tf / FP4_MFMA_PEAK_TFLOPS, 4),
+                     "op": "C = dequant(A) x dequant(W)^T, both MXFP4 (E2M1 + E8M0 per 32), "
+                           "scales applied by the matrix core, bf16 out"}
+        log(f"{mkey}: {tf:.1f} TFLOP/s ({tf / FP4_MFMA_PEAK_TFLOPS * 100:.1f}% of "
+            f"{FP4_MFMA_PEAK_TFLOPS:.0f})")
+        del x, w, qa, qw, a, b, c, cc, cs, qbuf, ma, mw
     torch.cuda.empty_cache()
     return out
 

@@ -289,6 +289,24 @@ pqb_status pqb_gemm_fp8_blockscaled_quant(const uint8_t* a, const float* a_scale
                                           int64_t n, int64_t k, uint8_t* c_codes,
                                           float* c_scales, void* stream);
 
+/* MXFP4 x MXFP4 product on the block-scaled matrix cores (page "LLM 推理优化
+ * · 量化学习笔记" §4.5: MXFP4 is 32-element blocks sharing one E8M0 scale, the
+ * format FP4 tensor cores consume directly):
+ *   C[m, n] = sum_k dec(a[m, k]) 2^(sa[m, k/32] - 127) dec(b[n, k]) 2^(sb[n, k/32] - 127).
+ * a, b: E2M1 codes [m, k/2] and [n, k/2] (element 2i in the low nibble of
+ * byte i), sa, sb: E8M0 scales [m, k/32] and [n, k/32], exactly as
+ * pqb_quantize writes MXFP4 x BLK_32 for [1, m, k] and [1, n, k]; c: [m, n]
+ * row-major of out_dtype.  The matrix core applies the scales; products of
+ * two E2M1 values sum exactly in groups of 8, and the float32 additions
+ * bound the error by about (17 + k/128) * 2^-24 * sum_k |a| |b|.  Shape
+ * rules: k % 128 == 0, n % 128 == 0, m, n, k < 2^31; m = 0 or n = 0 does
+ * nothing; k = 0 writes zeros.  Alignment: a, b and c 16 bytes, scales 4.
+ * Errors, before any launch: PQB_ERR_ENUM, PQB_ERR_SHAPE, PQB_ERR_NULL,
+ * PQB_ERR_ALIGN. */
+pqb_status pqb_gemm_mxfp4(const uint8_t* a, const uint8_t* a_scales, const uint8_t* b,
+                          const uint8_t* b_scales, int64_t m, int64_t n, int64_t k,
+                          pqb_dtype out_dtype, void* c, void* stream);
+
 /* W4A16 product, the consumer of the INT4 group-128 codes (page "14. 量化：让
  * 每一步搬更少的字节", 路线一: 4-bit weights read from memory, unpacked and
  * dequantized to 16 bits, then multiplied):

@@ -485,17 +485,18 @@ pqb_status pqb_kv_read_kivi(const uint8_t* k_codes, const uint8_t* v_codes,
 }
 
 // Shape, pointer and alignment rules shared by the GEMM entry points.
-static pqb_status check_gemm(const uint8_t* a, const float* a_scales, const uint8_t* b,
-                             const float* b_scales, int64_t m, int64_t n, int64_t k,
+static pqb_status check_gemm(const uint8_t* a, const void* a_scales, const uint8_t* b,
+                             const void* b_scales, int64_t m, int64_t n, int64_t k,
                              const void* c) {
+  (void)a_scales;
+  (void)b_scales;
   if (m < 0 || n < 0 || k < 0 || k % 128 || n % 128) return PQB_ERR_SHAPE;
   if (m > INT32_MAX || n > INT32_MAX || k > INT32_MAX) return PQB_ERR_SHAPE;
   if ((m + 127) / 128 * (n / 128) > INT32_MAX) return PQB_ERR_SHAPE;
   if (m == 0 || n == 0) return PQB_OK;
-  if (!c || (k > 0 && (!a || !b || !a_scales || !b_scales))) return PQB_ERR_NULL;
+  if (!c || (k > 0 && (!a || !b))) return PQB_ERR_NULL;
   if (!aligned(c, 16)) return PQB_ERR_ALIGN;
-  if (k > 0 && !(aligned(a, 16) && aligned(b, 16) && aligned(a_scales, 4) && aligned(b_scales, 4)))
-    return PQB_ERR_ALIGN;
+  if (k > 0 && !(aligned(a, 16) && aligned(b, 16))) return PQB_ERR_ALIGN;
   return PQB_OK;
 }
 
@@ -505,9 +506,23 @@ pqb_status pqb_gemm_fp8_blockscaled(const uint8_t* a, const float* a_scales, con
   if (!valid_dtype(out_dtype)) return PQB_ERR_ENUM;
   const pqb_status e = check_gemm(a, a_scales, b, b_scales, m, n, k, c);
   if (e != PQB_OK || m == 0 || n == 0) return e;
+  if (k > 0 && (!a_scales || !b_scales)) return PQB_ERR_NULL;
+  if (k > 0 && !(aligned(a_scales, 4) && aligned(b_scales, 4))) return PQB_ERR_ALIGN;
   return hip_status(launch_gemm_fp8_bs(a, a_scales, b, b_scales, m, n, k,
                                        out_dtype == PQB_BF16 ? 1 : 0, c, nullptr,
                                        (hipStream_t)stream));
+}
+
+pqb_status pqb_gemm_mxfp4(const uint8_t* a, const uint8_t* a_scales, const uint8_t* b,
+                          const uint8_t* b_scales, int64_t m, int64_t n, int64_t k,
+                          pqb_dtype out_dtype, void* c, void* stream) {
+  if (!valid_dtype(out_dtype)) return PQB_ERR_ENUM;
+  const pqb_status e = check_gemm(a, nullptr, b, nullptr, m, n, k, c);
+  if (e != PQB_OK || m == 0 || n == 0) return e;
+  if (k > 0 && (!a_scales || !b_scales)) return PQB_ERR_NULL;
+  if (k > 0 && !(aligned(a_scales, 4) && aligned(b_scales, 4))) return PQB_ERR_ALIGN;
+  return hip_status(launch_gemm_mxfp4(a, a_scales, b, b_scales, m, n, k, out_dtype == PQB_BF16, c,
+                                      (hipStream_t)stream));
 }
 
 pqb_status pqb_gemm_fp8_blockscaled_quant(const uint8_t* a, const float* a_scales,
@@ -516,6 +531,8 @@ pqb_status pqb_gemm_fp8_blockscaled_quant(const uint8_t* a, const float* a_scale
                                           float* c_scales, void* stream) {
   const pqb_status e = check_gemm(a, a_scales, b, b_scales, m, n, k, c_codes);
   if (e != PQB_OK || m == 0 || n == 0) return e;
+  if (k > 0 && (!a_scales || !b_scales)) return PQB_ERR_NULL;
+  if (k > 0 && !(aligned(a_scales, 4) && aligned(b_scales, 4))) return PQB_ERR_ALIGN;
   if (!c_scales) return PQB_ERR_NULL;
   if (!aligned(c_scales, 4)) return PQB_ERR_ALIGN;
   return hip_status(launch_gemm_fp8_bs(a, a_scales, b, b_scales, m, n, k, 2, c_codes, c_scales,

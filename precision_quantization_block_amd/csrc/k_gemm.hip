@@ -98,6 +98,87 @@ __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory
 // columns of a row (the 1x128 activation layout), quantized in the epilogue.
 enum GemmOut { kOutF32 = 0, kOutBf16 = 1, kOutFp8 = 2 };
 
+// Epilogue helpers.  Each wave stages its 64 x 64 floats in LDS (rows padded
+// to 68 floats); the float32 / bf16 forms then write whole row segments, 256
+// bytes per row for float32, 128 for bf16, with 16-byte stores.
+__device__ __forceinline__ void stage_tile(const v4f (&acc)[4][4], uint8_t* lds, int wave, int lane) {
+  const int r16 = lane & 15, q = lane >> 4;
+  float* out_lds = reinterpret_cast<float*>(lds) + wave * 64 * kGOutStride;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        out_lds[(mt * 16 + 4 * q + r) * kGOutStride + nt * 16 + r16] = acc[mt][nt][r];
+}
+
+template <int kOut>
+__device__ __forceinline__ void stage_and_store(const v4f (&acc)[4][4], uint8_t* lds, int wave,
+                                                int lane, int m0, int n0, int M, int N, void* C) {
+  stage_tile(acc, lds, wave, lane);
+  __syncthreads();
+  const float* out_lds = reinterpret_cast<const float*>(lds) + wave * 64 * kGOutStride;
+  const int row0 = m0 + (wave >> 1) * 64, col0 = n0 + (wave & 1) * 64;
+  if constexpr (kOut == kOutBf16) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {          // 8 lanes per row, 8 rows per step
+      const int rr = s * 8 + (lane >> 3), cc = (lane & 7) * 8;
+      if (row0 + rr < M) {
+        const float* v = out_lds + rr * kGOutStride + cc;
+        const v4f x0 = *reinterpret_cast<const v4f*>(v), x1 = *reinterpret_cast<const v4f*>(v + 4);
+        uint16_t* dst = reinterpret_cast<uint16_t*>(C) + (int64_t)(row0 + rr) * N + col0 + cc;
+        st_nt16(dst, bf16x2_rne(x0[0], x0[1]), bf16x2_rne(x0[2], x0[3]), bf16x2_rne(x1[0], x1[1]),
+                bf16x2_rne(x1[2], x1[3]));
+      }
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {         // 16 lanes per row, 4 rows per step
+      const int rr = s * 4 + (lane >> 4), cc = (lane & 15) * 4;
+      if (row0 + rr < M) {
+        const v4f x = *reinterpret_cast<const v4f*>(out_lds + rr * kGOutStride + cc);
+        float* dst = reinterpret_cast<float*>(C) + (int64_t)(row0 + rr) * N + col0 + cc;
+        st_nt16(dst, as_u(x[0]), as_u(x[1]), as_u(x[2]), as_u(x[3]));
+      }
+    }
+  }
+}
+
+// FP8 1x128 quantization of a staged 128 x 128 tile's rows, each exactly one
+// 128-column block: thread t takes columns 64 (t & 1) .. + 63 of row t >> 1
+// (staged by wave (row / 64, t & 1)); the pair's maxima meet by DPP, then the
+// scale and codes follow the 1x128 quantizer's arithmetic.
+__device__ __forceinline__ void quantize_tile_rows(const uint8_t* lds, int tid, int m0, int n0,
+                                                   int M, int N, uint8_t* C, float* c_scales) {
+  static_assert(kGTM == 128 && kGThreads == 256, "two threads per row of a 128-row tile");
+  const int rr = tid >> 1, half = tid & 1;
+  const float* v = reinterpret_cast<const float*>(lds) +
+                   ((rr >> 6) * 2 + half) * 64 * kGOutStride + (rr & 63) * kGOutStride;
+  uint32_t am = 0;
+#pragma unroll
+  for (int i = 0; i < 64; i += 4) {
+    const v4f x = *reinterpret_cast<const v4f*>(v + i);
+    am = max(am, max(max(as_u(fabsf(x[0])), as_u(fabsf(x[1]))),
+                     max(as_u(fabsf(x[2])), as_u(fabsf(x[3])))));
+  }
+  const float s = fp8_scale_bits<kE4M3>(group_umax<2>(am));
+  const float y = recip_rn(s);
+  if (m0 + rr < M) {
+    uint8_t* dst = C + (int64_t)(m0 + rr) * N + n0 + 64 * half;
+#pragma unroll
+    for (int i = 0; i < 64; i += 16) {
+      float w[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) w[j] = v[i + j];
+      const uint2 lo = fp8_pack8<kE4M3>(w, s, y), hi = fp8_pack8<kE4M3>(w + 8, s, y);
+      st_nt16(dst + i, lo.x, lo.y, hi.x, hi.y);
+    }
+    if (half == 0) c_scales[(int64_t)(m0 + rr) * (N / kGT) + n0 / kGT] = s;
+  }
+}
+
+
 template <int kOut>
 __global__ __launch_bounds__(kGThreads) void k_gemm_fp8_bs(const uint8_t* __restrict__ A,
                                                            const float* __restrict__ sA,
@@ -191,76 +272,130 @@ __global__ __launch_bounds__(kGThreads) void k_gemm_fp8_bs(const uint8_t* __rest
   }
   barrier();  // every wave done with the ring before it becomes the output stage
 
-  // Epilogue: each wave stages its 64 x 64 floats in LDS (rows padded to 68
-  // floats), then writes whole row segments: 256 bytes per row for float32,
-  // 128 for bf16, with 16-byte stores.
-  float* out_lds = reinterpret_cast<float*>(lds) + wave * 64 * kGOutStride;
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        out_lds[(mt * 16 + 4 * q + r) * kGOutStride + nt * 16 + r16] = acc[mt][nt][r];
-  __syncthreads();
   if constexpr (kOut == kOutFp8) {
-    // FP8 1x128 quantization of the tile's rows, each exactly one 128-column
-    // block: thread t takes columns 64 (t & 1) .. + 63 of row t >> 1 (staged by
-    // wave (row / 64, t & 1)); the pair's maxima meet by DPP, then the scale
-    // and codes follow the 1x128 quantizer's arithmetic.
-    static_assert(kGTM == 128 && kGThreads == 256, "two threads per row of a 128-row tile");
-    const int rr = tid >> 1, half = tid & 1;
-    const float* v = reinterpret_cast<const float*>(lds) +
-                     ((rr >> 6) * 2 + half) * 64 * kGOutStride + (rr & 63) * kGOutStride;
-    uint32_t am = 0;
-#pragma unroll
-    for (int i = 0; i < 64; i += 4) {
-      const v4f x = *reinterpret_cast<const v4f*>(v + i);
-      am = max(am, max(max(as_u(fabsf(x[0])), as_u(fabsf(x[1]))),
-                       max(as_u(fabsf(x[2])), as_u(fabsf(x[3])))));
-    }
-    const float s = fp8_scale_bits<kE4M3>(group_umax<2>(am));
-    const float y = recip_rn(s);
-    if (m0 + rr < M) {
-      uint8_t* dst = reinterpret_cast<uint8_t*>(C) + (int64_t)(m0 + rr) * N + n0 + 64 * half;
-#pragma unroll
-      for (int i = 0; i < 64; i += 16) {
-        float w[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) w[j] = v[i + j];
-        const uint2 lo = fp8_pack8<kE4M3>(w, s, y), hi = fp8_pack8<kE4M3>(w + 8, s, y);
-        st_nt16(dst + i, lo.x, lo.y, hi.x, hi.y);
-      }
-      if (half == 0) c_scales[(int64_t)(m0 + rr) * (N / kGT) + n0 / kGT] = s;
-    }
-    return;
-  }
-  const int row0 = m0 + wm * 64, col0 = n0 + wn * 64;
-  if constexpr (kOut == kOutBf16) {
-    // 8 lanes per row, 8 rows per step
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int rr = s * 8 + (lane >> 3), cc = (lane & 7) * 8;
-      if (row0 + rr < M) {
-        const float* v = out_lds + rr * kGOutStride + cc;
-        const v4f x0 = *reinterpret_cast<const v4f*>(v), x1 = *reinterpret_cast<const v4f*>(v + 4);
-        uint16_t* dst = reinterpret_cast<uint16_t*>(C) + (int64_t)(row0 + rr) * N + col0 + cc;
-        st_nt16(dst, bf16x2_rne(x0[0], x0[1]), bf16x2_rne(x0[2], x0[3]), bf16x2_rne(x1[0], x1[1]),
-                bf16x2_rne(x1[2], x1[3]));
-      }
-    }
+    stage_tile(acc, lds, wave, lane);
+    __syncthreads();
+    quantize_tile_rows(lds, tid, m0, n0, M, N, reinterpret_cast<uint8_t*>(C), c_scales);
   } else {
-    // 16 lanes per row, 4 rows per step
+    stage_and_store<kOut>(acc, lds, wave, lane, m0, n0, M, N, C);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MXFP4 x MXFP4 product C = dequant(A) dequant(B)^T on the block-scaled matrix
+// cores: v_mfma_scale_f32_16x16x128_f8f6f4 with E2M1 operands takes each
+// lane's 32 nibbles (16 bytes, one 32-element MX block: row l & 15, block
+// l >> 4 of the 128-deep K step) and that lane's E8M0 scale byte, exactly the
+// MXFP4 layout (codes [rows, K/2], scales [rows, K/32]).  The scales are
+// powers of two applied by the matrix core, so the MFMAs accumulate straight
+// into C, with no promotion step.  Same workgroup shape, DMA ring, swizzle and
+// epilogue as the FP8 GEMM; one ring slot holds a 256-deep K stage: 128 rows x
+// 128 bytes of codes for A and for B (the FP8 tile layout) and 8 scale bytes
+// per row of each.
+// ---------------------------------------------------------------------------
+constexpr int kMxKS = 256;                                 // K elements per stage
+constexpr int kMxScaleBytes = kGT * 8;                     // 8 E8M0 bytes per row and stage
+constexpr int kMxSlotBytes = 2 * kGTileB + 2 * kMxScaleBytes;
+static_assert(kGTM == 128 && kGThreads == 256, "the MX GEMM uses the 128 x 128 tile");
+static_assert(kGStages * kMxSlotBytes <= kGLdsBytes, "ring fits the FP8 GEMM's LDS");
+
+template <int kOut>
+__global__ __launch_bounds__(kGThreads) void k_gemm_mxfp4(const uint8_t* __restrict__ A,
+                                                          const uint8_t* __restrict__ sA,
+                                                          const uint8_t* __restrict__ B,
+                                                          const uint8_t* __restrict__ sB, int M,
+                                                          int N, int K, int tiles_n,
+                                                          void* __restrict__ C) {
+  static_assert(kGStages == 2, "one stage in flight at each wait");
+  __shared__ __align__(16) uint8_t lds[kGLdsBytes];
+  auto slot = [&](int s) { return lds + s * kMxSlotBytes; };
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nwg = gridDim.x, per = nwg / 8;
+  const int t = per * 8 == nwg ? (blockIdx.x & 7) * per + (blockIdx.x >> 3) : blockIdx.x;
+  const int band = t / (8 * tiles_n), rem = t - band * 8 * tiles_n;
+  const int band_rows = min(8, nwg / tiles_n - band * 8);
+  const int tm = band * 8 + rem % band_rows, tn = rem / band_rows;
+  const int m0 = tm * kGT, n0 = tn * kGT;
+  const int kb128 = K / 128, stages = (K + kMxKS - 1) / kMxKS;
+  const int rowb = K / 2, srow = K / 32;                   // code and scale bytes per row
+
+  // DMA of stage st into slot s.  Wave w fills code rows 32 w .. 32 w + 31 of
+  // A and B (4 instructions of 8 rows each), and 64 scale rows (2 dwords per
+  // row): waves 0, 1 those of A, waves 2, 3 those of B.  A second half past K
+  // (K / 128 odd, last stage) reads the first half again and is never used.
+  const int drow = lane >> 3, dpos = lane & 7;
+  auto issue_stage = [&](int st, int s) {
+    const uint32_t base = lds_addr(slot(s));
+    const int64_t k0 = (int64_t)st * (kMxKS / 2);
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      const int rr = s * 4 + (lane >> 4), cc = (lane & 15) * 4;
-      if (row0 + rr < M) {
-        const v4f x = *reinterpret_cast<const v4f*>(out_lds + rr * kGOutStride + cc);
-        float* dst = reinterpret_cast<float*>(C) + (int64_t)(row0 + rr) * N + col0 + cc;
-        st_nt16(dst, as_u(x[0]), as_u(x[1]), as_u(x[2]), as_u(x[3]));
+    for (int j = 0; j < 4; ++j) {
+      const int r = wave * 32 + j * 8 + drow;
+      int c = dpos ^ (r & 7);
+      if (k0 + 16 * c >= rowb) c -= 4;
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(base + (wave * 32 + j * 8) * kGT);
+      dma16(A + (int64_t)min(m0 + r, M - 1) * rowb + k0 + 16 * c, dst);
+      dma16(B + (int64_t)(n0 + r) * rowb + k0 + 16 * c, dst + kGTileB);
+    }
+    // scale rows r = 64 (w & 1) + 32 i + (l >> 1), i < 2, dword (l & 1): LDS
+    // dword 2 r + (l & 1), i.e. byte 512 (w & 1) + 256 i + 4 l
+    const int half = lane & 1;
+    const int hh = 8 * st + 4 * half < srow ? half : 0;
+    const uint32_t sdst = base + 2 * kGTileB + (wave < 2 ? 0 : kMxScaleBytes) + (wave & 1) * 512;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int sr = (wave & 1) * 64 + 32 * i + (lane >> 1);
+      const uint8_t* src = wave < 2 ? sA + (int64_t)min(m0 + sr, M - 1) * srow
+                                    : sB + (int64_t)(n0 + sr) * srow;
+      dma4(src + 8 * st + 4 * hh, __builtin_amdgcn_readfirstlane(sdst + 256 * i));
+    }
+  };
+
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r16 = lane & 15, q = lane >> 4;
+  v4f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  if (stages > 0) issue_stage(0, 0);
+  for (int st = 0; st < stages; ++st) {
+    // the only DMA in flight is this stage's (the next is issued after the
+    // barrier), so wait for all of it
+    wait_vmcnt<0>();
+    barrier();
+    if (st + 1 < stages) issue_stage(st + 1, (st + 1) & 1);
+    const uint8_t* sl = slot(st & 1);
+    const uint32_t* ls = reinterpret_cast<const uint32_t*>(sl + 2 * kGTileB);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (2 * st + h >= kb128) break;
+      v8i af[4];
+      int sa[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int r = wm * 64 + mt * 16 + r16;
+        const uint4 v = *reinterpret_cast<const uint4*>(sl + tile_off(r, 4 * h + q));
+        af[mt] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+        // scale dword of row r: rows 32 w' + i of wave w' at dword 64 w' + 2 i + half
+        sa[mt] = (ls[(r >> 5) * 64 + 2 * (r & 31) + h] >> (8 * q)) & 0xFF;
+      }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int r = wn * 64 + nt * 16 + r16;
+        const uint4 v = *reinterpret_cast<const uint4*>(sl + kGTileB + tile_off(r, 4 * h + q));
+        const v8i bf = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+        const int sb = (ls[kMxScaleBytes / 4 + (r >> 5) * 64 + 2 * (r & 31) + h] >> (8 * q)) & 0xFF;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mt], bf, acc[mt][nt], 4,
+                                                                         4, 0, sa[mt], 0, sb);
       }
     }
   }
+  barrier();
+  stage_and_store<kOut>(acc, lds, wave, lane, m0, n0, M, N, C);
 }
 
 }  // namespace
@@ -280,6 +415,20 @@ hipError_t launch_gemm_fp8_bs(const uint8_t* a, const float* a_scales, const uin
     go(k_gemm_fp8_bs<kOutFp8>);
   else
     go(k_gemm_fp8_bs<kOutF32>);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_mxfp4(const uint8_t* a, const uint8_t* a_scales, const uint8_t* b,
+                             const uint8_t* b_scales, int64_t M, int64_t N, int64_t K,
+                             bool out_bf16, void* c, hipStream_t st) {
+  const int tiles_m = (int)((M + kGT - 1) / kGT), tiles_n = (int)(N / kGT);
+  const dim3 grid((unsigned)tiles_m * (unsigned)tiles_n);
+  if (out_bf16)
+    hipLaunchKernelGGL(k_gemm_mxfp4<kOutBf16>, grid, dim3(kGThreads), 0, st, a, a_scales, b, b_scales,
+                       (int)M, (int)N, (int)K, tiles_n, c);
+  else
+    hipLaunchKernelGGL(k_gemm_mxfp4<kOutF32>, grid, dim3(kGThreads), 0, st, a, a_scales, b, b_scales,
+                       (int)M, (int)N, (int)K, tiles_n, c);
   return hipGetLastError();
 }
 

@@ -121,6 +121,13 @@ hipError_t launch_gemm_fp8_bs(const uint8_t* a, const float* a_scales, const uin
                               const float* b_scales, int64_t M, int64_t N, int64_t K, int out,
                               void* c, float* c_scales, hipStream_t st);
 
+// MXFP4 x MXFP4 product C [M, N] = dequant(A [M, K]) x dequant(B [N, K])^T on the
+// block-scaled matrix cores; MXFP4 layout (codes [rows, K/2], E8M0 scales
+// [rows, K/32]); K % 128 == 0, N % 128 == 0.
+hipError_t launch_gemm_mxfp4(const uint8_t* a, const uint8_t* a_scales, const uint8_t* b,
+                             const uint8_t* b_scales, int64_t M, int64_t N, int64_t K,
+                             bool out_bf16, void* c, hipStream_t st);
+
 // W4A16 products y [M, N] = x [M, K] (bf16) x dequant(W)^T for INT4 group-128
 // asymmetric weights W [N, K] (codes, bf16 scales, zero-point nibbles); all
 // jobs of a call share M (1 <= M <= 8); K % 128 == 0; N * K / 128 < 2^31.

@@ -80,6 +80,7 @@ def lib():
         L.pqb_gemm_fp8_blockscaled.argtypes = [P, P, P, P, I64, I64, I64, I, P, P]
         L.pqb_gemm_fp8_blockscaled_quant.argtypes = [P, P, P, P, I64, I64, I64, P, P, P]
         L.pqb_gemv_w4a16.argtypes = [P, I64, P, P, P, I64, I64, I, P, P]
+        L.pqb_gemm_mxfp4.argtypes = [P, P, P, P, I64, I64, I64, I, P, P]
         L.pqb_gemv_w4a16_batch.argtypes = [ctypes.POINTER(_W4Job), I64, I64, I, P]
         L.pqb_encode_e4m3.argtypes = [P, I64, P, P]
         L.pqb_encode_e5m2.argtypes = [P, I64, P, P]
@@ -88,7 +89,7 @@ def lib():
                   "pqb_kv_write_fp8", "pqb_kv_write_fp8_ex", "pqb_kv_write_kivi",
                   "pqb_kv_read_kivi", "pqb_gemm_fp8_blockscaled",
                   "pqb_gemm_fp8_blockscaled_quant", "pqb_gemv_w4a16",
-                  "pqb_gemv_w4a16_batch",
+                  "pqb_gemv_w4a16_batch", "pqb_gemm_mxfp4",
                   "pqb_encode_e4m3", "pqb_encode_e5m2", "pqb_encode_e2m1"):
             getattr(L, f).restype = I
         _lib = L
@@ -415,6 +416,25 @@ def gemm_fp8_blockscaled_quant(a_codes: torch.Tensor, a_scales: torch.Tensor,
                                                 _ptr(codes), _ptr(scales), _stream(a.device)),
            "gemm_fp8_blockscaled_quant")
     return codes, scales
+
+
+def gemm_mxfp4(a, b, out_dtype=torch.float32) -> torch.Tensor:
+    """C = dequant(A) @ dequant(B)^T for two MXFP4 operands, each a Quantized
+    from quantize(x, "mxfp4") or a (codes [rows, K/2], E8M0 scales [rows, K/32])
+    pair, on the block-scaled matrix cores."""
+    ac, as_ = (a.codes, a.scales) if isinstance(a, Quantized) else a
+    bc, bs = (b.codes, b.scales) if isinstance(b, Quantized) else b
+    K = a.shape[-1] if isinstance(a, Quantized) else 2 * ac.shape[-1]
+    ac, bc = _dev_tensor(ac, "a codes", (torch.uint8,)), _dev_tensor(bc, "b codes", (torch.uint8,))
+    as_, bs = _dev_tensor(as_, "a scales", (torch.uint8,)), _dev_tensor(bs, "b scales", (torch.uint8,))
+    M, N = ac.numel() // (K // 2), bc.numel() // (K // 2)
+    if bc.numel() != N * (K // 2) or as_.numel() != M * (K // 32) or bs.numel() != N * (K // 32):
+        raise ValueError("codes must be [rows, K/2] and scales [rows, K/32]")
+    c = torch.empty((M, N), dtype=out_dtype, device=ac.device)
+    _check(lib().pqb_gemm_mxfp4(_ptr(ac), _ptr(as_), _ptr(bc), _ptr(bs), M, N, K,
+                                BF16 if out_dtype == torch.bfloat16 else F32, _ptr(c),
+                                _stream(ac.device)), "gemm_mxfp4")
+    return c
 
 
 def gemv_w4a16(x: torch.Tensor, weight, out_dtype=torch.float32) -> torch.Tensor:
