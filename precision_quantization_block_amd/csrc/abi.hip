@@ -484,12 +484,10 @@ pqb_status pqb_kv_read_kivi(const uint8_t* k_codes, const uint8_t* v_codes,
   return PQB_OK;
 }
 
-// Shape, pointer and alignment rules shared by the GEMM entry points.
-static pqb_status check_gemm(const uint8_t* a, const void* a_scales, const uint8_t* b,
-                             const void* b_scales, int64_t m, int64_t n, int64_t k,
+// Shape, code-pointer and output rules shared by the GEMM entry points (each
+// checks its own scale pointers).
+static pqb_status check_gemm(const uint8_t* a, const uint8_t* b, int64_t m, int64_t n, int64_t k,
                              const void* c) {
-  (void)a_scales;
-  (void)b_scales;
   if (m < 0 || n < 0 || k < 0 || k % 128 || n % 128) return PQB_ERR_SHAPE;
   if (m > INT32_MAX || n > INT32_MAX || k > INT32_MAX) return PQB_ERR_SHAPE;
   if ((m + 127) / 128 * (n / 128) > INT32_MAX) return PQB_ERR_SHAPE;
@@ -504,7 +502,7 @@ pqb_status pqb_gemm_fp8_blockscaled(const uint8_t* a, const float* a_scales, con
                                     const float* b_scales, int64_t m, int64_t n, int64_t k,
                                     pqb_dtype out_dtype, void* c, void* stream) {
   if (!valid_dtype(out_dtype)) return PQB_ERR_ENUM;
-  const pqb_status e = check_gemm(a, a_scales, b, b_scales, m, n, k, c);
+  const pqb_status e = check_gemm(a, b, m, n, k, c);
   if (e != PQB_OK || m == 0 || n == 0) return e;
   if (k > 0 && (!a_scales || !b_scales)) return PQB_ERR_NULL;
   if (k > 0 && !(aligned(a_scales, 4) && aligned(b_scales, 4))) return PQB_ERR_ALIGN;
@@ -517,7 +515,7 @@ pqb_status pqb_gemm_mxfp4(const uint8_t* a, const uint8_t* a_scales, const uint8
                           const uint8_t* b_scales, int64_t m, int64_t n, int64_t k,
                           pqb_dtype out_dtype, void* c, void* stream) {
   if (!valid_dtype(out_dtype)) return PQB_ERR_ENUM;
-  const pqb_status e = check_gemm(a, nullptr, b, nullptr, m, n, k, c);
+  const pqb_status e = check_gemm(a, b, m, n, k, c);
   if (e != PQB_OK || m == 0 || n == 0) return e;
   if (k > 0 && (!a_scales || !b_scales)) return PQB_ERR_NULL;
   if (k > 0 && !(aligned(a_scales, 4) && aligned(b_scales, 4))) return PQB_ERR_ALIGN;
@@ -529,7 +527,7 @@ pqb_status pqb_gemm_fp8_blockscaled_quant(const uint8_t* a, const float* a_scale
                                           const uint8_t* b, const float* b_scales, int64_t m,
                                           int64_t n, int64_t k, uint8_t* c_codes,
                                           float* c_scales, void* stream) {
-  const pqb_status e = check_gemm(a, a_scales, b, b_scales, m, n, k, c_codes);
+  const pqb_status e = check_gemm(a, b, m, n, k, c_codes);
   if (e != PQB_OK || m == 0 || n == 0) return e;
   if (k > 0 && (!a_scales || !b_scales)) return PQB_ERR_NULL;
   if (k > 0 && !(aligned(a_scales, 4) && aligned(b_scales, 4))) return PQB_ERR_ALIGN;
