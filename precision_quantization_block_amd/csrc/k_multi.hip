@@ -174,10 +174,19 @@ hipError_t launch_family(const std::vector<const MultiJob*>& jobs, hipStream_t s
                                                                     : (size_t)kMaxBatchJobs);
     MultiArgs a{};
     a.njobs = n;
+    // whole-tile jobs (the heaviest workgroups) first, so that they are not
+    // the last to be dispatched
+    Job tmp[kMaxBatchJobs];
+    int64_t cnt[kMaxBatchJobs];
+    for (int i = 0; i < n; ++i) cnt[i] = describe(*jobs[base + i], tmp[i]);
+    int order[kMaxBatchJobs], k = 0;
+    for (int i = 0; i < n; ++i) if (tmp[i].kind == kJobFp8Tile) order[k++] = i;
+    for (int i = 0; i < n; ++i) if (tmp[i].kind != kJobFp8Tile) order[k++] = i;
     int64_t wg = 0;
     for (int i = 0; i < n; ++i) {
       a.wg_begin[i] = wg;
-      wg += describe(*jobs[base + i], a.job[i]);
+      a.job[i] = tmp[order[i]];
+      wg += cnt[order[i]];
     }
     a.wg_begin[n] = wg;
     if (wg > 0)
