@@ -10,17 +10,22 @@
 // the low nibble of byte i, two's complement), bf16 scales [N, K / 128],
 // zero-point nibbles over the flat group index n * K / 128 + g.
 //
-// With q + 8 = (nibble ^ 8) in 0 .. 15 and c = 8 + z, a unit of 32 weights
-// inside one group contributes s * (sum x (q + 8) - c * sum x): the products x
-// (q + 8) are exact in float32, each nibble costs one byte-to-float conversion
-// (v_cvt_f32_ubyte) and one FMA per activation row, and the 4-bit unpacking is
-// two AND / shift / XOR steps per four weights.
+// With q + 8 = (nibble ^ 8) in 0 .. 15, the weight w = 128 + q + 8 is an exact
+// bf16 whose high byte is 0x43 and whose low byte is q + 8.  A unit of 32
+// weights inside one group then contributes s * (sum x w - (136 + z) sum x),
+// and both sums are packed bf16 dot products (v_dot2c_f32_bf16: two exact
+// products per instruction added into a float32 accumulator; sum x is the dot
+// with (1, 1)).  Unpacking costs, per 8 weights, one mask and one shift-mask
+// (both with the sign flip) that split the nibbles into bytes, then one byte
+// permute per pair that places two of them under the 0x43 byte.  The same
+// permute pairs up the activations, once per unit for all rows.
 //
 // Lane l of a wave handles code units u = l, l + 64, ... (16 bytes = 32
 // weights each) of kR consecutive rows; every wave load instruction reads 1
 // KiB of one row.  The units are walked as items of kSteps units per lane, and
-// the codes of the next item are loaded before the current one is computed.  The activations are read once per unit and
-// reused for the kR rows.  A wave-wide sum ends each row.
+// the codes of the next item are loaded before the current one is computed.
+// The activations are read once per unit and reused for the kR rows.  A
+// wave-wide sum ends each row.
 // One launch serves up to kW4MaxJobs independent products (the projections
 // that share an input, or any batch of weights): workgroup b belongs to the
 // job whose range of workgroups holds b.
@@ -31,12 +36,13 @@ namespace pqb {
 namespace {
 
 constexpr int kWThreads = 256;  // 4 waves
-// Two launch shapes, chosen by the rows one launch covers (measured on the
-// Llama-3.1-8B-shaped weights): 2 rows per wave with 2 units per lane in
-// flight when a launch holds a few projections (more waves), 8 rows with 1
-// unit when it holds hundreds of thousands of rows (the activations then
-// serve 8 rows per load).
+// Launch shapes chosen by the rows one launch covers (measured on the
+// Llama-3.1-8B-shaped weights): 2 rows per wave when a launch holds a few
+// projections (more waves: with 2 units per lane in flight at M = 1), more
+// rows per wave when it holds many (the activations then serve more rows per
+// load): 8 at M <= 2 from 2^16 rows, 4 at M = 3 .. 5 from 2^13 rows.
 constexpr int kBigLaunchRows = 1 << 16;
+constexpr int kMidLaunchRows = 1 << 13;
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -44,15 +50,10 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Low and high nibbles of the 4 bytes of w as bytes, each plus 8 (sign flip).
-__device__ __forceinline__ void nibbles_plus8(uint32_t w, uint32_t& lo, uint32_t& hi) {
-  lo = (w & 0x0F0F0F0Fu) ^ 0x08080808u;
-  hi = ((w >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;
-}
-
-__device__ __forceinline__ float byte_f(uint32_t v, int j) {
-  return (float)((v >> (8 * j)) & 0xFFu);  // v_cvt_f32_ubyte<j>
-}
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16x2v as_bf2(uint32_t v) { return __builtin_bit_cast(bf16x2v, v); }
+constexpr uint32_t kBf16Ones = 0x3F803F80u;    // (1.0, 1.0)
+constexpr uint32_t kBf16Hi128 = 0x43434343u;   // high byte of bf16 128 .. 255
 
 template <int kM, bool kBf16Out, int kR, int kSteps>
 __global__ __launch_bounds__(kWThreads) void k_w4a16(const W4Args a) {
@@ -133,13 +134,25 @@ __global__ __launch_bounds__(kWThreads) void k_w4a16(const W4Args a) {
     for (int s = 0; s < kSteps; ++s) {
       const int u = u0 + 64 * s + lane;
       if (u >= U) break;
+      // Activation pairs matching the weight pairs below: for code dword d,
+      // xp[4d + 2h + e] = (x[8d + 4h + e], x[8d + 4h + e + 2]) (e: nibble,
+      // h: byte half); xs = sum of the unit's 32 x.
+      bf16x2v xp[kM][16];
       float xs[kM];
 #pragma unroll
       for (int m = 0; m < kM; ++m) {
         float t = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          t += as_f(xd[s][m][i] << 16) + as_f(xd[s][m][i] & 0xFFFF0000u);
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const uint32_t lo = xd[s][m][4 * d + 2 * h], hi = xd[s][m][4 * d + 2 * h + 1];
+              const bf16x2v v = as_bf2(__builtin_amdgcn_perm(hi, lo, e ? 0x07060302u : 0x05040100u));
+              xp[m][4 * d + 2 * h + e] = v;
+              t = __builtin_amdgcn_fdot2_f32_bf16(v, as_bf2(kBf16Ones), t, false);
+            }
         xs[m] = t;
       }
 #pragma unroll
@@ -147,25 +160,27 @@ __global__ __launch_bounds__(kWThreads) void k_w4a16(const W4Args a) {
         const int gi = min(n0 + r, N - 1) * G + (u >> 2);
         const float sc = as_f((uint32_t)sb[s][r] << 16);
         const int zn = (zb[s][r] >> (4 * (gi & 1))) & 0xF;
-        const float cz = (float)(8 + (zn >= 8 ? zn - 16 : zn));
+        const float cz = (float)(136 + (zn >= 8 ? zn - 16 : zn));    // 128 + 8 + z
         const uint32_t w4[4] = {cur[s][r].x, cur[s][r].y, cur[s][r].z, cur[s][r].w};
         float dot[kM];
 #pragma unroll
         for (int m = 0; m < kM; ++m) dot[m] = 0.0f;
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-          uint32_t lo, hi;
-          nibbles_plus8(w4[d], lo, hi);
+          // q + 8 of the low (e = 0) and high (e = 1) nibble of each byte
+          const uint32_t nb[2] = {(w4[d] & 0x0F0F0F0Fu) ^ 0x08080808u,
+                                  ((w4[d] >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u};
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float ql = byte_f(lo, j), qh = byte_f(hi, j);
+          for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int m = 0; m < kM; ++m) {
-              const uint32_t xp = xd[s][m][4 * d + j];   // elements 8d + 2j (low), 8d + 2j + 1
-              dot[m] = __builtin_fmaf(as_f(xp << 16), ql, dot[m]);
-              dot[m] = __builtin_fmaf(as_f(xp & 0xFFFF0000u), qh, dot[m]);
+            for (int e = 0; e < 2; ++e) {
+              // bytes 2h, 2h + 1 of nb[e] under the bf16 exponent byte 0x43:
+              // the pair (128 + q + 8) of weights 8d + 4h + e, 8d + 4h + e + 2
+              const bf16x2v wp = as_bf2(__builtin_amdgcn_perm(nb[e], kBf16Hi128, h ? 0x00070006u : 0x00050004u));
+#pragma unroll
+              for (int m = 0; m < kM; ++m)
+                dot[m] = __builtin_amdgcn_fdot2_f32_bf16(xp[m][4 * d + 2 * h + e], wp, dot[m], false);
             }
-          }
         }
 #pragma unroll
         for (int m = 0; m < kM; ++m)
@@ -218,17 +233,18 @@ hipError_t launch_shape(W4Args& a, bool out_bf16, hipStream_t st) {
 }
 
 // Shapes per M that keep every instantiation free of register spills and at
-// two or more waves per SIMD where possible: 2 units ahead only for M = 1.
-hipError_t launch_args(W4Args& a, int M, bool big, bool out_bf16, hipStream_t st) {
+// two or more waves per SIMD.
+hipError_t launch_args(W4Args& a, int M, int64_t rows, bool out_bf16, hipStream_t st) {
+  const bool big = rows >= kBigLaunchRows, mid = rows >= kMidLaunchRows;
   switch (M) {
     case 1: return big ? launch_shape<1, 8, 1>(a, out_bf16, st) : launch_shape<1, 2, 2>(a, out_bf16, st);
     case 2: return big ? launch_shape<2, 8, 1>(a, out_bf16, st) : launch_shape<2, 2, 1>(a, out_bf16, st);
-    case 3: return launch_shape<3, 2, 1>(a, out_bf16, st);
-    case 4: return launch_shape<4, 2, 1>(a, out_bf16, st);
-    case 5: return launch_shape<5, 2, 1>(a, out_bf16, st);
-    case 6: return launch_shape<6, 1, 1>(a, out_bf16, st);
-    case 7: return launch_shape<7, 1, 1>(a, out_bf16, st);
-    case 8: return launch_shape<8, 1, 1>(a, out_bf16, st);
+    case 3: return mid ? launch_shape<3, 4, 1>(a, out_bf16, st) : launch_shape<3, 2, 1>(a, out_bf16, st);
+    case 4: return mid ? launch_shape<4, 4, 1>(a, out_bf16, st) : launch_shape<4, 2, 1>(a, out_bf16, st);
+    case 5: return mid ? launch_shape<5, 4, 1>(a, out_bf16, st) : launch_shape<5, 2, 1>(a, out_bf16, st);
+    case 6: return launch_shape<6, 2, 1>(a, out_bf16, st);
+    case 7: return launch_shape<7, 2, 1>(a, out_bf16, st);
+    case 8: return launch_shape<8, 2, 1>(a, out_bf16, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -245,7 +261,7 @@ hipError_t launch_w4a16(const W4Job* jobs, int njobs, int M, bool out_bf16, hipS
       a.job[i] = jobs[base + i];
       rows += a.job[i].N;
     }
-    const hipError_t e = launch_args(a, M, rows >= kBigLaunchRows, out_bf16, st);
+    const hipError_t e = launch_args(a, M, rows, out_bf16, st);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

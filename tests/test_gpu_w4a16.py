@@ -2,12 +2,14 @@
 float64 y = x @ dequant(W)^T, element by element, within a bound derived from
 the kernel's float32 evaluation.
 
-For each unit of 32 weights of one group, the kernel forms s * (sum x (q + 8) -
-(8 + z) sum x).  The products x (q + 8) are exact.  Each 32-term sum rounds at
-most 31 times, and the two fused multiply-adds once each.  The units of a row
-are accumulated per lane (at most K/2048 + 1 additions), then summed over 64
-lanes (6 levels).  First order, the error is at most
-  (40 + K/2048) * 2^-24 * sum_k |s| |x| (|q + 8| + |8 + z|),
+For each unit of 32 weights of one group, the kernel forms s * (sum x w -
+(136 + z) sum x), where w = 136 + q (in 128 .. 143) is the code as an exact
+bf16.  The products x w are exact.  The two 32-term sums (pairs of products
+added into a float32 accumulator) round at most 32 times each, and the two
+fused multiply-adds once each.  The units of a row are accumulated per lane
+(at most K/2048 + 1 additions), then summed over 64 lanes (6 levels).  First
+order, the error is at most
+  (40 + K/2048) * 2^-24 * sum_k |s| |x| (|136 + q| + |136 + z|),
 plus half a bf16 ulp of the value for bf16 output."""
 import zlib
 
@@ -36,7 +38,7 @@ def rng(tag):
 
 
 def bound(xb, codes, scales, zeros):
-    """sum_k |s| |x| (|q + 8| + |8 + z|) for every (m, n)."""
+    """sum_k |s| |x| (|136 + q| + |136 + z|) for every (m, n)."""
     N = codes.shape[-2]
     K = codes.shape[-1] * 2
     c = codes.reshape(N, K // 2).astype(np.int32)
@@ -48,7 +50,7 @@ def bound(xb, codes, scales, zeros):
     zn = np.stack([zeros & 0xF, zeros >> 4], 1).reshape(-1)[:N * G].astype(np.int32).reshape(N, G)
     z = np.where(zn >= 8, zn - 16, zn)
     s = np.abs(oracle.bf16_bits_to_f32(scales.reshape(N, G)).astype(np.float64))
-    A = np.repeat(s, 128, axis=1) * (np.abs(q + 8) + np.repeat(np.abs(8 + z), 128, axis=1))
+    A = np.repeat(s, 128, axis=1) * (np.abs(136 + q) + np.repeat(np.abs(136 + z), 128, axis=1))
     return np.abs(oracle.bf16_bits_to_f32(xb).astype(np.float64)) @ A.T
 
 
@@ -74,7 +76,7 @@ def check(pqb, xb, codes, scales, zeros, what):
 
 
 SHAPES = [(1, 128, 128), (1, 1000, 4096), (3, 333, 2176), (8, 64, 14336), (4, 257, 384),
-          (2, 4096, 1024), (5, 9, 128 * 50)]
+          (2, 4096, 1024), (5, 9, 128 * 50), (6, 130, 512), (7, 77, 1152)]
 
 
 @pytest.mark.parametrize("shape", SHAPES)
@@ -145,10 +147,24 @@ def test_w4a16_batch_equals_single_calls(pqb):
           "batch job 33")
 
 
-@pytest.mark.parametrize("M", [1, 2, 6])
+def test_w4a16_subnormal_activations(pqb):
+    """Activations below 2^-126 (bf16 subnormals) keep their value: one row of
+    x is all subnormal, one mixes subnormal and normal values."""
+    r = rng("subn")
+    N, K = 200, 1024
+    w = (0.02 * r.standard_normal((N, K))).astype(np.float32)
+    codes, scales, zeros = oracle.int4_quantize(w[None])
+    x = np.empty((2, K), np.uint16)
+    x[0] = r.integers(1, 0x80, K) | (r.integers(0, 2, K) << 15)          # +-subnormal
+    x[1] = np.where(r.random(K) < 0.5, x[0], bf16_bits(r.standard_normal(K)))
+    check(pqb, x, codes[0], scales[0], zeros, "subnormal x")
+
+
+@pytest.mark.parametrize("M", range(1, 9))
 def test_w4a16_large_launch_shape(pqb, M):
-    """A launch of more than 65536 rows takes the 8-rows-per-wave shape (M <= 2);
-    M = 6 takes the 1-row shape.  Both against the oracle, with a ragged N."""
+    """A launch of more than 65536 rows takes the 8-rows-per-wave shape at M <=
+    2, the 4-row shape at M = 3 .. 5 and the 2-row shape above.  All against the
+    oracle, with a ragged N."""
     r = rng(f"big{M}")
     N, K = 66001, 256
     w = (0.02 * r.standard_normal((N, K))).astype(np.float32)
