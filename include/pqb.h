@@ -315,11 +315,13 @@ pqb_status pqb_gemm_mxfp4(const uint8_t* a, const uint8_t* a_scales, const uint8
  * zeros: the INT4_ASYM x GRP_128 layout pqb_quantize writes for a [1, n, k]
  * weight (codes u8 [n, k/2], bf16 scales [n, k/128], zero-point nibbles over
  * the flat group index); y: [m, n] row-major of out_dtype.  Evaluated in
- * float32 with FMAs: per 32 weights of one group, s * (sum x (q + 8) - (8 + z)
- * * sum x), then a sum over the units; the error against exact arithmetic is
- * at most about (40 + k/2048) * 2^-24 * sum_k |s| |x| (|q + 8| + |8 + z|).
+ * float32: per 32 weights of one group, s * (sum x w - (136 + z) * sum x)
+ * with w = 136 + q as exact bf16 products summed in float32, then a sum over
+ * the units; the error against exact arithmetic is at most about
+ * (40 + k/2048) * 2^-24 * sum_k |s| |x| (|136 + q| + |136 + z|).
  * Shape rules: k % 128 == 0, m <= 8, n * (k/128) < 2^31, k < 2^31; m = 0 or
- * n = 0 does nothing.  Alignment: x and codes 16 bytes, scales 2, y 4.
+ * n = 0 does nothing; k = 0 writes zeros.  Alignment: x and codes 16 bytes,
+ * scales 2, y 4.
  * Errors, before any launch: PQB_ERR_ENUM (out_dtype), PQB_ERR_SHAPE,
  * PQB_ERR_NULL, PQB_ERR_ALIGN. */
 pqb_status pqb_gemv_w4a16(const void* x, int64_t m, const uint8_t* codes, const void* scales,

@@ -73,6 +73,18 @@ __global__ __launch_bounds__(kWThreads) void k_w4a16(const W4Args a) {
   // is computed.
   const int nw0 = (((int)blockIdx.x - a.wg_begin[jb]) * (kWThreads / 64) + wave) * kR * kBlocks;
   if (nw0 >= N) return;
+  if (K == 0) {   // the empty sum: this wave's rows of y are zero
+    for (int i = lane; i < kM * kR * kBlocks; i += 64) {
+      const int m = i / (kR * kBlocks), n = nw0 + i % (kR * kBlocks);
+      if (n < N) {
+        if constexpr (kBf16Out)
+          reinterpret_cast<uint16_t*>(y)[(int64_t)m * N + n] = 0;
+        else
+          reinterpret_cast<float*>(y)[(int64_t)m * N + n] = 0.0f;
+      }
+    }
+    return;
+  }
   const int U = K / 32, G = K / 128;
   const int chunks = (U + 64 * kSteps - 1) / (64 * kSteps);
   const int blocks = min(kBlocks, (N - nw0 + kR - 1) / kR);

@@ -437,6 +437,14 @@ def gemm_mxfp4(a, b, out_dtype=torch.float32) -> torch.Tensor:
     return c
 
 
+def _w4_rows(codes: torch.Tensor, K: int) -> int:
+    """N of an INT4 weight [N, K] from its codes (2-D [N, K / 2], or flat when K > 0)."""
+    N = codes.shape[0] if codes.dim() == 2 else (codes.numel() * 2 // K if K else 0)
+    if K % 128 or codes.numel() != N * K // 2:
+        raise ValueError("codes must hold N x K / 2 bytes with K a multiple of 128")
+    return N
+
+
 def gemv_w4a16(x: torch.Tensor, weight, out_dtype=torch.float32) -> torch.Tensor:
     """y = x @ dequant(W)^T for bf16 activations x [M, K] (M <= 8) and an INT4
     group-128 weight: a Quantized from quantize(w, "int4_asym") or a
@@ -450,9 +458,7 @@ def gemv_w4a16(x: torch.Tensor, weight, out_dtype=torch.float32) -> torch.Tensor
     scales = _dev_tensor(scales, "scales", (torch.bfloat16, torch.int16, torch.uint8))
     zeros = _dev_tensor(zeros, "zeros", (torch.uint8,))
     M, K = (1, x.shape[0]) if x.dim() == 1 else (x.shape[-2], x.shape[-1])
-    N = codes.numel() * 2 // K if K else 0
-    if K % 128 or codes.numel() != N * K // 2:
-        raise ValueError("codes must hold N x K / 2 bytes with K a multiple of 128")
+    N = _w4_rows(codes, K)
     y = torch.empty((M, N), dtype=out_dtype, device=x.device)
     _check(lib().pqb_gemv_w4a16(_ptr(x), M, _ptr(codes), _ptr(scales), _ptr(zeros), N, K,
                                 BF16 if out_dtype == torch.bfloat16 else F32, _ptr(y),
@@ -469,9 +475,8 @@ def gemv_w4a16_batch(xs, weights, out_dtype=torch.float32):
     for i, (x, wgt) in enumerate(zip(xs, weights)):
         x = _dev_tensor(x, "x", (torch.bfloat16,))
         c, s, z = (wgt.codes, wgt.scales, wgt.aux) if isinstance(wgt, Quantized) else wgt
-        K = x.shape[-1]
-        M = x.numel() // K
-        N = c.numel() * 2 // K
+        M, K = (1, x.shape[0]) if x.dim() == 1 else (x.shape[-2], x.shape[-1])
+        N = _w4_rows(c, K)
         y = torch.empty((M, N), dtype=out_dtype, device=x.device)
         keep += [x, c, s, z]
         ys.append(y)

@@ -147,6 +147,33 @@ def test_w4a16_batch_equals_single_calls(pqb):
           "batch job 33")
 
 
+def test_w4a16_degenerate_sizes(pqb):
+    """k = 0 is the empty sum (y = 0, also inside a batch beside a real job);
+    m = 0 and n = 0 launch nothing."""
+    for dt in (torch.float32, torch.bfloat16):
+        for M, N in ((1, 5), (3, 300), (8, 70000)):
+            x = torch.empty((M, 0), dtype=torch.bfloat16, device=DEV)
+            codes = torch.empty((N, 0), dtype=torch.uint8, device=DEV)
+            empty = (codes, torch.empty((N, 0), dtype=torch.int16, device=DEV),
+                     torch.empty((0,), dtype=torch.uint8, device=DEV))
+            y = pqb.gemv_w4a16(x, empty, out_dtype=dt)
+            assert y.shape == (M, N) and bool((y == 0).all()), (dt, M, N)
+    x = torch.randn((2, 256), device=DEV).to(torch.bfloat16)
+    r = rng("deg")
+    w = (0.02 * r.standard_normal((130, 256))).astype(np.float32)
+    codes, scales, zeros = oracle.int4_quantize(w[None])
+    wt = tuple(torch.from_numpy(np.ascontiguousarray(t)).to(DEV) for t in (codes[0], scales[0].view(np.int16), zeros))
+    empty = (torch.empty((130, 0), dtype=torch.uint8, device=DEV), torch.empty((130, 0), dtype=torch.int16, device=DEV),
+             torch.empty((0,), dtype=torch.uint8, device=DEV))
+    ys = pqb.gemv_w4a16_batch([x, x[:, :0]], [wt, empty], out_dtype=torch.float32)
+    assert torch.equal(ys[0], pqb.gemv_w4a16(x, wt, out_dtype=torch.float32))
+    assert ys[1].shape == (2, 130) and bool((ys[1] == 0).all())
+    assert pqb.gemv_w4a16(x[:0], wt).shape == (0, 130)
+    none = (torch.empty((0, 128), dtype=torch.uint8, device=DEV), torch.empty((0, 2), dtype=torch.int16, device=DEV),
+            torch.empty((0,), dtype=torch.uint8, device=DEV))
+    assert pqb.gemv_w4a16(x, none).shape == (2, 0)
+
+
 def test_w4a16_subnormal_activations(pqb):
     """Activations below 2^-126 (bf16 subnormals) keep their value: one row of
     x is all subnormal, one mixes subnormal and normal values."""
