@@ -427,8 +427,14 @@ def gemm_mxfp4(a, b, out_dtype=torch.float32) -> torch.Tensor:
     K = a.shape[-1] if isinstance(a, Quantized) else 2 * ac.shape[-1]
     ac, bc = _dev_tensor(ac, "a codes", (torch.uint8,)), _dev_tensor(bc, "b codes", (torch.uint8,))
     as_, bs = _dev_tensor(as_, "a scales", (torch.uint8,)), _dev_tensor(bs, "b scales", (torch.uint8,))
-    M, N = ac.numel() // (K // 2), bc.numel() // (K // 2)
-    if bc.numel() != N * (K // 2) or as_.numel() != M * (K // 32) or bs.numel() != N * (K // 32):
+    def rows(q, codes):   # leading rows of a Quantized, else of 2-D codes (or flat, K > 0)
+        if isinstance(q, Quantized):
+            return math.prod(q.shape[:-1])
+        return codes.shape[0] if codes.dim() == 2 else (codes.numel() // (K // 2) if K else 0)
+
+    M, N = rows(a, ac), rows(b, bc)
+    if K % 128 or ac.numel() != M * (K // 2) or bc.numel() != N * (K // 2) \
+            or as_.numel() != M * (K // 32) or bs.numel() != N * (K // 32):
         raise ValueError("codes must be [rows, K/2] and scales [rows, K/32]")
     c = torch.empty((M, N), dtype=out_dtype, device=ac.device)
     _check(lib().pqb_gemm_mxfp4(_ptr(ac), _ptr(as_), _ptr(bc), _ptr(bs), M, N, K,

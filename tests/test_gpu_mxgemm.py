@@ -56,7 +56,7 @@ def check(pqb, a, sa, b, sb, what, rows=None):
 
 
 SHAPES = [(128, 128, 128), (256, 384, 512), (100, 256, 384), (1, 128, 1152), (300, 640, 2048),
-          (129, 128, 640)]
+          (129, 128, 640), (64, 256, 0)]
 
 
 @pytest.mark.parametrize("shape", SHAPES)
@@ -67,6 +67,11 @@ def test_mxgemm_random_codes_match_oracle(pqb, shape):
     b = r.integers(0, 256, (N, K // 2)).astype(np.uint8)
     sa = r.integers(107, 147, (M, K // 32)).astype(np.uint8)
     sb = r.integers(107, 147, (N, K // 32)).astype(np.uint8)
+    if K == 0:   # the empty sum
+        for dt in (torch.float32, torch.bfloat16):
+            got = pqb.gemm_mxfp4((dev(a), dev(sa)), (dev(b), dev(sb)), out_dtype=dt)
+            assert got.shape == (M, N) and torch.count_nonzero(got).item() == 0
+        return
     check(pqb, a, sa, b, sb, f"random {shape}")
 
 
