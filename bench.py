@@ -293,7 +293,7 @@ def bench_extras(torch, eng, synth, reps, only=None):
     # 1 GiB bf16 tensor, every format
     sweep = (("fp8_e4m3", "1x128", torch.bfloat16), ("fp8_e4m3", "128x128", None),
              ("fp8_e4m3", "row", None), ("fp8_e4m3", "tensor", None),
-             ("mxfp4", "blk32", torch.bfloat16), ("nvfp4", "blk16", None),
+             ("mxfp4", "blk32", torch.bfloat16), ("nvfp4", "blk16", torch.bfloat16),
              ("int4_asym", "grp128", torch.bfloat16), ("fp8_e5m2", "1x128", torch.bfloat16),
              ("int8_sym", "row", torch.bfloat16), ("mxfp8", "blk32", torch.bfloat16))
     names = [f"sweep1GiB_bf16_{f}_{g}" for f, g, _ in sweep]

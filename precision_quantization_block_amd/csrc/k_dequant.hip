@@ -138,7 +138,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_dq_mxfp8(const uint8_t* __res
 }
 
 // NVFP4, slice b = blockIdx.y: unit u is half of block u / 2; element scale
-// max(dec(block scale), 1e-12) * gs.
+// max(dec(block scale), 1e-12) * gs.  The nibbles are expanded by the scaled
+// FP4 conversion at scale 1, which returns +-V exactly (signed zeros
+// included), and each value is then multiplied by the element scale: one
+// rounding, as V * s.
 template <bool kBf16Out>
 __global__ __launch_bounds__(kBlockThreads) void k_dq_nvfp4(const uint8_t* __restrict__ codes,
                                                             const uint8_t* __restrict__ scales,
@@ -163,8 +166,12 @@ __global__ __launch_bounds__(kBlockThreads) void k_dq_nvfp4(const uint8_t* __res
     if (u < nunits) {
       const float s = fmaxf(e4m3_decode(bs[k]), 1e-12f) * g;
       float o[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) o[i] = e2m1_value(c[k] >> (4 * i)) * s;
+      const f32x2v v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[k], 1.0f, 0);
+      const f32x2v v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[k], 1.0f, 1);
+      const f32x2v v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[k], 1.0f, 2);
+      const f32x2v v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[k], 1.0f, 3);
+      o[0] = v0[0] * s; o[1] = v0[1] * s; o[2] = v1[0] * s; o[3] = v1[1] * s;
+      o[4] = v2[0] * s; o[5] = v2[1] * s; o[6] = v3[0] * s; o[7] = v3[1] * s;
       store_out8<kBf16Out>(out, base + u, o);
     }
   }

@@ -362,13 +362,6 @@ __device__ __forceinline__ void fp8_decode8(uint2 w, float s, float o[8]) {
   o[4] = c.x * s; o[5] = c.y * s; o[6] = d.x * s; o[7] = d.y * s;
 }
 
-// Signed E2M1 values, nibble -> float.
-__device__ __forceinline__ float e2m1_value(uint32_t nib) {
-  const uint32_t m = nib & 7u;
-  // m >= 2: 2^(m/2 - 1) * (1 + (m & 1) / 2); m == 1: 0.5; m == 0: 0
-  uint32_t b = m >= 2u ? ((((m >> 1) + 126u) << 23) | ((m & 1u) << 22)) : (m ? 0x3F000000u : 0u);
-  return as_f(b | ((nib & 8u) << 28));
-}
 
 // ---------------------------------------------------------------------------
 // MXFP8 (32-element blocks, E8M0 scale, E4M3 elements; pages "LLM 推理优化 ·

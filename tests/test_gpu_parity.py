@@ -172,6 +172,24 @@ def test_nvfp4_parity(pqb, dtype):
              f"nv {(b, r, c)} dequant bf16")
 
 
+def test_nvfp4_dequant_every_code(pqb):
+    """NVFP4 dequantization of hand-made codes: every code byte at every byte
+    position of a 4-byte unit, every block-scale code the quantizer can write
+    (0 .. 0x7E, one per row) and three tensor scales (the smallest gs the
+    quantizer forms, 1, and an arbitrary one), in float32 and bf16."""
+    b, r, c = 3, 127, 2048
+    byte = (np.arange(c // 2) // 4).astype(np.uint8)     # byte i = i // 4: all 256 at each position
+    codes = np.broadcast_to(byte, (b, r, c // 2)).copy()
+    scales = np.broadcast_to(np.arange(r, dtype=np.uint8)[:, None], (b, r, c // 16)).copy()
+    gs = np.array([np.float32(1e-12) / np.float32(2688), 1.0, 3.7e-5], np.float32)
+    q = pqb.Quantized(torch.from_numpy(codes).reshape(-1).to(DEV),
+                      torch.from_numpy(scales).reshape(-1).to(DEV),
+                      torch.from_numpy(gs).to(DEV), "nvfp4", "blk16", (b, r, c))
+    same(pqb.dequantize(q), oracle.nvfp4_dequantize(codes, scales, gs), "nv dequant every code")
+    same(pqb.dequantize(q, torch.bfloat16), oracle.nvfp4_dequantize(codes, scales, gs, True),
+         "nv dequant bf16 every code")
+
+
 # -------------------------------------------------------------- INT4 -------
 
 INT4_SHAPES = [(1, 64, 4096), (2, 9, 384), (1, 1, 128), (1, 3, 14336)]
