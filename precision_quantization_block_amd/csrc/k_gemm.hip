@@ -258,6 +258,9 @@ __global__ __launch_bounds__(kGThreads) void k_gemm_fp8_bs(const uint8_t* __rest
       const v4f s4 = *reinterpret_cast<const v4f*>(&ls[(r >> 5) * 64 + (r & 31) + 4 * q]);
       sab[mt] = s4 * sb;
     }
+    // The wave that has reached its matrix products is served first: the
+    // other waves of the CU are then mostly waiting on LDS reads or DMA.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       const v8i bf = frag(sl + kGTileA, wn * 64 + nt * 16 + r16, q);
@@ -268,7 +271,7 @@ __global__ __launch_bounds__(kGThreads) void k_gemm_fp8_bs(const uint8_t* __rest
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[mt][nt][r] = __builtin_fmaf(p[r], sab[mt][r], acc[mt][nt][r]);
       }
-    }
+    }    __builtin_amdgcn_s_setprio(0);
   }
   barrier();  // every wave done with the ring before it becomes the output stage
 
