@@ -307,7 +307,8 @@ def bench_extras(torch, eng, synth, reps, only=None):
         out.update(bench_kv(torch, eng, synth, reps))
     if want("gemm_fp8_bs_8192x7168x2048_bf16", "gemm_fp8_bs_8192x2048x7168_bf16"):
         out.update(bench_gemm(torch, eng, synth, reps))
-    if want("llama8b_224w_int4_g128_w4a16_decode_m1_one_batch"):
+    if want("llama8b_224w_int4_g128_w4a16_decode_m1_one_batch",
+            "llama8b_224w_int4_g128_w4a16_mfma_m16_one_batch"):
         out.update(bench_w4a16(torch, eng, synth, reps))
     if want("llama8b_224w_bf16_int4_g128"):
         out.update(bench_llama_int4(torch, eng, synth))
@@ -484,8 +485,9 @@ def bench_gemm(torch, eng, synth, reps):
 
 
 def bench_w4a16(torch, eng, synth, reps):
-    """W4A16 decode over the 224 Llama-3.1-8B-shaped weights in INT4 g128: one
-    token (M = 1) and a batch of 4, every weight read once per step."""
+    """W4A16 over the 224 Llama-3.1-8B-shaped weights in INT4 g128, every weight
+    read once per step (once per 32 rows on the matrix cores): the decode
+    kernel at M = 1 and 4, and the matrix-core kernel at M = 1, 4, 16 and 64."""
     dev = torch.device("cuda:0")
     from precision_quantization_block_amd.synth import LLAMA_LAYERS, LLAMA_PROJ
     ws, wbytes = [], 0
@@ -503,7 +505,7 @@ def bench_w4a16(torch, eng, synth, reps):
     J = eng.pqb.pqb._W4Job
     out = {}
     per_layer = len(LLAMA_PROJ)
-    for M in (1, 4):
+    for M in (1, 4, 16, 64):
         g = torch.Generator(device=dev).manual_seed(77)
         xs = {K: torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
               for K in sorted({c for _, c, _ in ws})}
@@ -511,34 +513,43 @@ def bench_w4a16(torch, eng, synth, reps):
         jobs = [J(xs[c].data_ptr(), b["codes"].data_ptr(), b["scales"].data_ptr(),
                   b["aux"].data_ptr(), y.data_ptr(), r, c) for (r, c, b), y in zip(ws, ys)]
 
-        def batch(js):
+        def batch(js, fn):
             arr = (J * len(js))(*js)
-            return lambda: eng.L.pqb_gemv_w4a16_batch(arr, len(js), M, 1, eng.stream)
+            return lambda: fn(arr, len(js), M, 1, eng.stream)
 
-        # one decode step three ways: every weight its own launch; per layer the
-        # projections that share an input together (q k v | o | gate up | down);
-        # all 224 weights in one batch call (7 launches of up to 32)
-        single = [batch([j]) for j in jobs]
-        grouped = []
-        for L0 in range(0, len(jobs), per_layer):
-            lj = jobs[L0:L0 + per_layer]
-            grouped += [batch(lj[0:3]), batch(lj[3:4]), batch(lj[4:6]), batch(lj[6:7])]
-        whole = [batch(jobs)]
         nb = wbytes + sum(2 * M * c + 2 * M * r for r, c, _ in ws)
-        for name, calls in (("per_weight", single), ("per_layer_groups", grouped),
-                            ("one_batch", whole)):
-            def step(i, calls=calls):
-                for f in calls:
-                    rc = f()
-                    if rc != 0:
-                        raise RuntimeError(f"pqb_gemv_w4a16_batch: status {rc}")
+        flops = 2 * M * sum(r * c for r, c, _ in ws)
+        kinds = [("mfma", eng.L.pqb_gemm_w4a16_batch)]
+        if M <= 8:
+            kinds.insert(0, ("decode", eng.L.pqb_gemv_w4a16_batch))
+        for kind, fn in kinds:
+            # one step three ways: every weight its own launch; per layer the
+            # projections that share an input together (q k v | o | gate up |
+            # down); all 224 weights in one batch call (7 launches of up to 32)
+            single = [batch([j], fn) for j in jobs]
+            grouped = []
+            for L0 in range(0, len(jobs), per_layer):
+                lj = jobs[L0:L0 + per_layer]
+                grouped += [batch(lj[0:3], fn), batch(lj[3:4], fn), batch(lj[4:6], fn),
+                            batch(lj[6:7], fn)]
+            whole = [batch(jobs, fn)]
+            ways = (("per_weight", single), ("per_layer_groups", grouped), ("one_batch", whole))
+            if kind == "mfma" and M > 8:
+                ways = ways[1:]
+            for name, calls in ways:
+                def step(i, calls=calls):
+                    for f in calls:
+                        rc = f()
+                        if rc != 0:
+                            raise RuntimeError(f"W4A16 batch call: status {rc}")
 
-            t = time_reps(torch, step, max(5, reps // 4), 2)
-            key = f"llama8b_224w_int4_g128_w4a16_decode_m{M}_{name}"
-            out[key] = rec(nb, t, op=f"W4A16 product, M = {M}, all 224 weights, {name}",
-                           calls=len(calls))
-            out[key]["ms_per_step"] = round(t[0], 4)
-            log(f"w4a16 decode M={M} {name}: {t[0]:.3f} ms per step, {out[key]['gbs']} GB/s")
+                t = time_reps(torch, step, max(5, reps // 4), 2)
+                key = f"llama8b_224w_int4_g128_w4a16_{kind}_m{M}_{name}"
+                out[key] = rec(nb, t, op=f"W4A16 product ({'matrix cores' if kind == 'mfma' else 'decode kernel'}), "
+                                         f"M = {M}, all 224 weights, {name}", calls=len(calls))
+                out[key]["ms_per_step"] = round(t[0], 4)
+                out[key]["tflops"] = round(flops / (t[0] * 1e-3) / 1e12, 1)
+                log(f"w4a16 {kind} M={M} {name}: {t[0]:.3f} ms per step, {out[key]['gbs']} GB/s")
     del ws
     torch.cuda.empty_cache()
     return out

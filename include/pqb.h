@@ -344,6 +344,30 @@ typedef struct pqb_w4a16_job {
 pqb_status pqb_gemv_w4a16_batch(const pqb_w4a16_job* jobs, int64_t njobs, int64_t m,
                                 pqb_dtype out_dtype, void* stream);
 
+/* The W4A16 product of pqb_gemv_w4a16 on the matrix cores, for any number of
+ * activation rows (decode batches and prefill chunks alike; the activations
+ * are taken 32 rows per launch and the weight is read once per 32 rows):
+ *   y[m, n] = sum_k x[m, k] * (q[n, k] - z[n, k/128]) * s[n, k/128],
+ * same layouts, ownership and alignment as pqb_gemv_w4a16, and m >= 0 with
+ * m < 2^31.  Evaluated in float32: for each group of 128, s * (P - (136 + z)
+ * * S), where P = sum x w with w = 136 + q and S = sum x are matrix-core
+ * float32 accumulations of exact bf16 products (32 per instruction), then a
+ * sum over the groups of each of four partial sums and a sum of the four;
+ * the error against exact arithmetic is at most about
+ * (256 + k/64) * 2^-24 * sum_k |s| |x| (|136 + q| + |136 + z|).
+ * Shape rules as pqb_gemv_w4a16 without the bound on m; m = 0 or n = 0 does
+ * nothing; k = 0 writes zeros.
+ * Errors, before any launch: PQB_ERR_ENUM (out_dtype), PQB_ERR_SHAPE,
+ * PQB_ERR_NULL, PQB_ERR_ALIGN. */
+pqb_status pqb_gemm_w4a16(const void* x, int64_t m, const uint8_t* codes, const void* scales,
+                          const uint8_t* zeros, int64_t n, int64_t k, pqb_dtype out_dtype,
+                          void* y, void* stream);
+/* Several such products in as few launches as possible (up to 32 jobs per
+ * launch and 32 activation rows): the job list of pqb_gemv_w4a16_batch, with
+ * any m >= 0. */
+pqb_status pqb_gemm_w4a16_batch(const pqb_w4a16_job* jobs, int64_t njobs, int64_t m,
+                                pqb_dtype out_dtype, void* stream);
+
 /* Element codecs exposed for testing the rounding rules on arrays of float32:
  * E4M3 of y (round-to-nearest-even; |y| must not exceed 464) into one byte
  * per element; E2M1 of y (ties to the smaller magnitude, saturating at 6)

@@ -583,6 +583,37 @@ pqb_status pqb_gemv_w4a16_batch(const pqb_w4a16_job* jobs, int64_t njobs, int64_
       launch_w4a16(w.data(), (int)w.size(), (int)m, out_dtype == PQB_BF16, (hipStream_t)stream));
 }
 
+pqb_status pqb_gemm_w4a16(const void* x, int64_t m, const uint8_t* codes, const void* scales,
+                          const uint8_t* zeros, int64_t n, int64_t k, pqb_dtype out_dtype,
+                          void* y, void* stream) {
+  if (!valid_dtype(out_dtype)) return PQB_ERR_ENUM;
+  if (m < 0 || m > INT32_MAX) return PQB_ERR_SHAPE;
+  W4Job job;
+  const pqb_status e = check_w4a16(x, m, codes, scales, zeros, n, k, y, &job);
+  if (e != PQB_OK || job.N == 0) return e;
+  return hip_status(launch_w4a16_mfma(&job, 1, m, out_dtype == PQB_BF16, (hipStream_t)stream));
+}
+
+pqb_status pqb_gemm_w4a16_batch(const pqb_w4a16_job* jobs, int64_t njobs, int64_t m,
+                                pqb_dtype out_dtype, void* stream) {
+  if (!valid_dtype(out_dtype)) return PQB_ERR_ENUM;
+  if (m < 0 || m > INT32_MAX || njobs < 0 || njobs > INT32_MAX) return PQB_ERR_SHAPE;
+  if (njobs == 0 || m == 0) return PQB_OK;
+  if (!jobs) return PQB_ERR_NULL;
+  std::vector<W4Job> w;
+  w.reserve((size_t)njobs);
+  for (int64_t i = 0; i < njobs; ++i) {
+    const pqb_w4a16_job& j = jobs[i];
+    W4Job job;
+    const pqb_status e = check_w4a16(j.x, m, j.codes, j.scales, j.zeros, j.n, j.k, j.y, &job);
+    if (e != PQB_OK) return e;
+    if (job.N > 0) w.push_back(job);
+  }
+  if (w.empty()) return PQB_OK;
+  return hip_status(
+      launch_w4a16_mfma(w.data(), (int)w.size(), m, out_dtype == PQB_BF16, (hipStream_t)stream));
+}
+
 pqb_status pqb_encode_e4m3(const float* y, int64_t n, uint8_t* out, void* stream) {
   if (n < 0) return PQB_ERR_SHAPE;
   if (n == 0) return PQB_OK;

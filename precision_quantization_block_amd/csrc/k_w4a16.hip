@@ -261,6 +261,183 @@ hipError_t launch_args(W4Args& a, int M, int64_t rows, bool out_bf16, hipStream_
   }
 }
 
+// ---------------------------------------------------------------------------
+// The same product on the matrix cores, for any M (v_mfma_f32_16x16x32_bf16).
+// A workgroup owns 64 weight rows, four tiles of 16 (the MFMA's N), and its 4
+// waves split K into four contiguous ranges of groups, so that one wave reads
+// both halves of a 128-byte code line and a row's scales in consecutive
+// steps.  For one group, lane l supplies row l & 15 of the activation block
+// and of each weight tile, and K positions 32 (l >> 4) .. + 31 of the group,
+// 8 per MFMA: its 16 code bytes of a tile are one load, and the activations
+// of each MFMA one 16-byte load in the same K order, shared by the four
+// tiles.  The codes become exact
+// bf16 w = 136 + q (high byte 0x43, low byte q + 8), so a group contributes
+// s * (P - (136 + z) * S) with P = sum x w from four MFMAs per tile and
+// S = sum x from four more against a B of ones; both are float32
+// accumulations of exact products.  The four waves' results meet in LDS and
+// are added in wave order.  Activation rows come in blocks of 16 (kMB of
+// them, up to 32 rows per launch); rows past M and weight rows past N are
+// read clamped and never stored.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+constexpr int kTiles = 4;                    // 16-row weight tiles per workgroup
+constexpr int kMfmaRows = 16 * kTiles;       // weight rows per workgroup
+constexpr int kMaxMB = 2;                    // 16-row activation blocks per launch
+constexpr int kMfmaWaves = kWThreads / 64;
+
+template <int kMB, bool kBf16Out>
+__global__ __launch_bounds__(kWThreads) void k_w4a16_mfma(const W4Args a, int M) {
+  int jb = 0;
+  while (jb + 1 < a.njobs && a.wg_begin[jb + 1] <= (int)blockIdx.x) ++jb;
+  const uint16_t* __restrict__ x = a.job[jb].x;
+  const uint8_t* __restrict__ codes = a.job[jb].codes;
+  const uint16_t* __restrict__ scales = a.job[jb].scales;
+  const uint8_t* __restrict__ zeros = a.job[jb].zeros;
+  void* __restrict__ y = a.job[jb].y;
+  const int N = a.job[jb].N, K = a.job[jb].K;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int n0 = ((int)blockIdx.x - a.wg_begin[jb]) * kMfmaRows;
+  const int col = lane & 15, kq = lane >> 4;
+  const int G = K / 128;
+  int nrow[kTiles];
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t) nrow[t] = min(n0 + 16 * t + col, N - 1);
+
+  f32x4v acc[kMB][kTiles];
+#pragma unroll
+  for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) acc[mb][t] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+  const int gb = wave * G / kMfmaWaves, ge = (wave + 1) * G / kMfmaWaves;   // this wave's groups
+  if (gb < ge) {
+    const uint16_t* xrow[kMB];
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb) xrow[mb] = x + (int64_t)min(16 * mb + col, M - 1) * K + 32 * kq;
+    // One group's weight data for this lane: the 16 code bytes of each tile
+    // row, with its scale and zero-point byte; loaded one group ahead.
+    struct Grp {
+      uint4 c[kTiles];
+      uint16_t s[kTiles];
+      uint8_t z[kTiles];
+    };
+    auto load_grp = [&](int g, Grp& v) {
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t) {
+        v.c[t] = *reinterpret_cast<const uint4*>(codes + (int64_t)nrow[t] * (K / 2) + 64 * g + 16 * kq);
+        const int gi = nrow[t] * G + g;
+        v.s[t] = scales[gi];
+        v.z[t] = zeros[gi >> 1];
+      }
+    };
+    const uint4 ones4 = {kBf16Ones, kBf16Ones, kBf16Ones, kBf16Ones};
+    const bf16x8v ones = __builtin_bit_cast(bf16x8v, ones4);
+    // Group g is computed from one buffer while group g + 1 loads into the
+    // other; the loop body takes two groups so that the buffers swap roles
+    // without a register copy (a copy would wait for the prefetch).
+    auto step = [&](int g, const Grp& cur, Grp& nxt) {
+      uint4 xv[4][kMB];
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb)
+          xv[st][mb] = *reinterpret_cast<const uint4*>(xrow[mb] + 128 * g + 8 * st);
+      // The prefetch is unconditional (the last group reloads itself): under
+      // a branch, the compiler's load counters would assume it absent and
+      // wait for it before this group's last product.  The scheduling fences
+      // keep the issue order activations, prefetch, products, so that the
+      // products wait only for the activations.
+      __builtin_amdgcn_sched_barrier(0);
+      load_grp(min(g + 1, ge - 1), nxt);
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4v p[kMB][kTiles], sx[kMB];
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb) {
+        sx[mb] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) p[mb][t] = sx[mb];
+      }
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb)
+          sx[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, xv[st][mb]),
+                                                           ones, sx[mb], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) {
+          // K positions 8 st + i: byte i / 2 of code dword st, low nibble for even i
+          const uint32_t w = st == 0 ? cur.c[t].x : st == 1 ? cur.c[t].y : st == 2 ? cur.c[t].z : cur.c[t].w;
+          const uint32_t lo = (w & 0x0F0F0F0Fu) ^ 0x08080808u;
+          const uint32_t hi = ((w >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;
+          uint4 wb;
+          wb.x = __builtin_amdgcn_perm(hi, lo, 0x0C040C00u) | 0x43004300u;
+          wb.y = __builtin_amdgcn_perm(hi, lo, 0x0C050C01u) | 0x43004300u;
+          wb.z = __builtin_amdgcn_perm(hi, lo, 0x0C060C02u) | 0x43004300u;
+          wb.w = __builtin_amdgcn_perm(hi, lo, 0x0C070C03u) | 0x43004300u;
+          const bf16x8v bv = __builtin_bit_cast(bf16x8v, wb);
+#pragma unroll
+          for (int mb = 0; mb < kMB; ++mb)
+            p[mb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, xv[st][mb]),
+                                                               bv, p[mb][t], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t) {
+        const int gi = nrow[t] * G + g;
+        const float sc = as_f((uint32_t)cur.s[t] << 16);
+        const int zn = (cur.z[t] >> (4 * (gi & 1))) & 0xF;
+        const float cz = (float)(136 + (zn >= 8 ? zn - 16 : zn));      // 128 + 8 + z
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[mb][t][r] = __builtin_fmaf(sc, __builtin_fmaf(-cz, sx[mb][r], p[mb][t][r]), acc[mb][t][r]);
+      }
+    };
+    Grp b0, b1;
+    load_grp(gb, b0);
+    for (int g = gb; g < ge; g += 2) {
+      step(g, b0, b1);
+      if (g + 1 < ge) step(g + 1, b1, b0);
+    }
+  }
+  // lane l holds rows 16 mb + 4 (l >> 4) + r of column n0 + 16 t + col
+  __shared__ f32x4v part[kMfmaWaves][kMB][kTiles][64];
+#pragma unroll
+  for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) part[wave][mb][t][lane] = acc[mb][t];
+  __syncthreads();
+  // wave w finishes tile w
+  const int t = wave, n = n0 + 16 * t + col;
+  if (t >= kTiles || n >= N) return;
+#pragma unroll
+  for (int mb = 0; mb < kMB; ++mb) {
+    f32x4v v = part[0][mb][t][lane];
+#pragma unroll
+    for (int w = 1; w < kMfmaWaves; ++w) v += part[w][mb][t][lane];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 16 * mb + 4 * kq + r;
+      if (m < M) {
+        if constexpr (kBf16Out)
+          reinterpret_cast<uint16_t*>(y)[(int64_t)m * N + n] = (uint16_t)bf16_rne_bits(v[r]);
+        else
+          reinterpret_cast<float*>(y)[(int64_t)m * N + n] = v[r];
+      }
+    }
+  }
+}
+
+template <int kMB>
+void launch_mfma_mb(const W4Args& a, int wgs, int M, bool out_bf16, hipStream_t st) {
+  if (out_bf16)
+    hipLaunchKernelGGL((k_w4a16_mfma<kMB, true>), dim3((unsigned)wgs), dim3(kWThreads), 0, st, a, M);
+  else
+    hipLaunchKernelGGL((k_w4a16_mfma<kMB, false>), dim3((unsigned)wgs), dim3(kWThreads), 0, st, a, M);
+}
+
 }  // namespace
 
 hipError_t launch_w4a16(const W4Job* jobs, int njobs, int M, bool out_bf16, hipStream_t st) {
@@ -275,6 +452,37 @@ hipError_t launch_w4a16(const W4Job* jobs, int njobs, int M, bool out_bf16, hipS
     }
     const hipError_t e = launch_args(a, M, rows, out_bf16, st);
     if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_w4a16_mfma(const W4Job* jobs, int njobs, int64_t M, bool out_bf16,
+                             hipStream_t st) {
+  constexpr int kSlice = 16 * kMaxMB;
+  for (int64_t m0 = 0; m0 < M; m0 += kSlice) {
+    const int mr = (int)(M - m0 < kSlice ? M - m0 : kSlice);
+    for (int base = 0; base < njobs; base += kW4MaxJobs) {
+      const int n = njobs - base < kW4MaxJobs ? njobs - base : kW4MaxJobs;
+      W4Args a{};
+      a.njobs = n;
+      int wg = 0;
+      for (int i = 0; i < n; ++i) {
+        W4Job j = jobs[base + i];
+        j.x += m0 * j.K;
+        j.y = static_cast<char*>(j.y) + m0 * j.N * (out_bf16 ? 2 : 4);
+        a.job[i] = j;
+        a.wg_begin[i] = wg;
+        wg += (j.N + kMfmaRows - 1) / kMfmaRows;
+      }
+      a.wg_begin[n] = wg;
+      if (wg == 0) continue;
+      if (mr > 16)
+        launch_mfma_mb<2>(a, wg, mr, out_bf16, st);
+      else
+        launch_mfma_mb<1>(a, wg, mr, out_bf16, st);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   return hipSuccess;
 }

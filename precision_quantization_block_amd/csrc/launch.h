@@ -146,6 +146,10 @@ struct W4Args {
   W4Job job[kW4MaxJobs];
 };
 hipError_t launch_w4a16(const W4Job* jobs, int njobs, int M, bool out_bf16, hipStream_t st);
+// The same products on the matrix cores for any M >= 1 (launched in slices of
+// 32 activation rows).
+hipError_t launch_w4a16_mfma(const W4Job* jobs, int njobs, int64_t M, bool out_bf16,
+                             hipStream_t st);
 
 // ---- element codecs ---------------------------------------------------------
 hipError_t launch_encode_elem(const float* y, int64_t n, uint8_t* out, hipStream_t st, int elem);

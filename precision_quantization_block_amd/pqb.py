@@ -82,6 +82,8 @@ def lib():
         L.pqb_gemv_w4a16.argtypes = [P, I64, P, P, P, I64, I64, I, P, P]
         L.pqb_gemm_mxfp4.argtypes = [P, P, P, P, I64, I64, I64, I, P, P]
         L.pqb_gemv_w4a16_batch.argtypes = [ctypes.POINTER(_W4Job), I64, I64, I, P]
+        L.pqb_gemm_w4a16.argtypes = [P, I64, P, P, P, I64, I64, I, P, P]
+        L.pqb_gemm_w4a16_batch.argtypes = [ctypes.POINTER(_W4Job), I64, I64, I, P]
         L.pqb_encode_e4m3.argtypes = [P, I64, P, P]
         L.pqb_encode_e5m2.argtypes = [P, I64, P, P]
         L.pqb_encode_e2m1.argtypes = [P, I64, P, P]
@@ -89,7 +91,8 @@ def lib():
                   "pqb_kv_write_fp8", "pqb_kv_write_fp8_ex", "pqb_kv_write_kivi",
                   "pqb_kv_read_kivi", "pqb_gemm_fp8_blockscaled",
                   "pqb_gemm_fp8_blockscaled_quant", "pqb_gemv_w4a16",
-                  "pqb_gemv_w4a16_batch", "pqb_gemm_mxfp4",
+                  "pqb_gemv_w4a16_batch", "pqb_gemm_mxfp4", "pqb_gemm_w4a16",
+                  "pqb_gemm_w4a16_batch",
                   "pqb_encode_e4m3", "pqb_encode_e5m2", "pqb_encode_e2m1"):
             getattr(L, f).restype = I
         _lib = L
@@ -451,10 +454,7 @@ def _w4_rows(codes: torch.Tensor, K: int) -> int:
     return N
 
 
-def gemv_w4a16(x: torch.Tensor, weight, out_dtype=torch.float32) -> torch.Tensor:
-    """y = x @ dequant(W)^T for bf16 activations x [M, K] (M <= 8) and an INT4
-    group-128 weight: a Quantized from quantize(w, "int4_asym") or a
-    (codes, scales, zeros) triple in that layout, W being [N, K]."""
+def _w4_one(fn, x, weight, out_dtype):
     x = _dev_tensor(x, "x", (torch.bfloat16,))
     if isinstance(weight, Quantized):
         codes, scales, zeros = weight.codes, weight.scales, weight.aux
@@ -466,16 +466,13 @@ def gemv_w4a16(x: torch.Tensor, weight, out_dtype=torch.float32) -> torch.Tensor
     M, K = (1, x.shape[0]) if x.dim() == 1 else (x.shape[-2], x.shape[-1])
     N = _w4_rows(codes, K)
     y = torch.empty((M, N), dtype=out_dtype, device=x.device)
-    _check(lib().pqb_gemv_w4a16(_ptr(x), M, _ptr(codes), _ptr(scales), _ptr(zeros), N, K,
-                                BF16 if out_dtype == torch.bfloat16 else F32, _ptr(y),
-                                _stream(x.device)), "gemv_w4a16")
+    _check(getattr(lib(), fn)(_ptr(x), M, _ptr(codes), _ptr(scales), _ptr(zeros), N, K,
+                              BF16 if out_dtype == torch.bfloat16 else F32, _ptr(y),
+                              _stream(x.device)), fn[4:])
     return y
 
 
-def gemv_w4a16_batch(xs, weights, out_dtype=torch.float32):
-    """Several W4A16 products in as few launches as possible: xs[i] (bf16 [M, K_i],
-    one M for all) times weights[i] (Quantized INT4 g128, or (codes, scales,
-    zeros)).  Returns the list of outputs [M, N_i]."""
+def _w4_batch(fn, xs, weights, out_dtype):
     keep, ys = [], []
     arr = (_W4Job * len(xs))()
     for i, (x, wgt) in enumerate(zip(xs, weights)):
@@ -490,9 +487,33 @@ def gemv_w4a16_batch(xs, weights, out_dtype=torch.float32):
     M = ys[0].shape[0] if ys else 0
     if any(y.shape[0] != M for y in ys):
         raise ValueError("all jobs must share M")
-    _check(lib().pqb_gemv_w4a16_batch(arr, len(xs), M, BF16 if out_dtype == torch.bfloat16 else F32,
-                                      _stream(ys[0].device) if ys else None), "gemv_w4a16_batch")
+    _check(getattr(lib(), fn)(arr, len(xs), M, BF16 if out_dtype == torch.bfloat16 else F32,
+                              _stream(ys[0].device) if ys else None), fn[4:])
     return ys
+
+
+def gemv_w4a16(x: torch.Tensor, weight, out_dtype=torch.float32) -> torch.Tensor:
+    """y = x @ dequant(W)^T for bf16 activations x [M, K] (M <= 8) and an INT4
+    group-128 weight: a Quantized from quantize(w, "int4_asym") or a
+    (codes, scales, zeros) triple in that layout, W being [N, K]."""
+    return _w4_one("pqb_gemv_w4a16", x, weight, out_dtype)
+
+
+def gemv_w4a16_batch(xs, weights, out_dtype=torch.float32):
+    """Several W4A16 products in as few launches as possible: xs[i] (bf16 [M, K_i],
+    one M for all) times weights[i] (Quantized INT4 g128, or (codes, scales,
+    zeros)).  Returns the list of outputs [M, N_i]."""
+    return _w4_batch("pqb_gemv_w4a16_batch", xs, weights, out_dtype)
+
+
+def gemm_w4a16(x: torch.Tensor, weight, out_dtype=torch.float32) -> torch.Tensor:
+    """gemv_w4a16 on the matrix cores, for any M."""
+    return _w4_one("pqb_gemm_w4a16", x, weight, out_dtype)
+
+
+def gemm_w4a16_batch(xs, weights, out_dtype=torch.float32):
+    """gemv_w4a16_batch on the matrix cores, for any M."""
+    return _w4_batch("pqb_gemm_w4a16_batch", xs, weights, out_dtype)
 
 
 def encode_e5m2(y: torch.Tensor) -> torch.Tensor:

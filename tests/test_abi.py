@@ -311,6 +311,33 @@ def test_w4a16_errors_before_launch(L):
     assert fb(arr(J(n=0, y=None)), 1, 1, 0, None) == 0
 
 
+def test_w4a16_matrix_core_errors_before_launch(L):
+    P = ctypes.c_void_p
+    fake, odd = P(0x10000), P(0x10008)
+    f = L.pqb_gemm_w4a16
+
+    def gm(x=fake, m=1, c=fake, s=fake, z=fake, n=256, k=512, dt=0, y=fake):
+        return f(x, m, c, s, z, n, k, dt, y, None)
+
+    assert gm(dt=4) == -2
+    assert gm(m=-1) == -4 and gm(m=1 << 31) == -4 and gm(k=500) == -4 and gm(n=-1) == -4
+    assert gm(n=1 << 30, k=1 << 20) == -4
+    assert gm(x=None) == -1 and gm(z=None) == -1 and gm(y=None) == -1
+    assert gm(m=9, x=odd) == -5 and gm(c=odd) == -5 and gm(s=P(0x10001)) == -5 and gm(y=P(0x10002)) == -5
+    assert gm(m=0) == 0 and gm(m=100, n=0, y=None) == 0
+    from precision_quantization_block_amd.pqb import _W4Job
+    fb = L.pqb_gemm_w4a16_batch
+    J = lambda **kw: _W4Job(**{**dict(x=0x10000, codes=0x10000, scales=0x10000, zeros=0x10000,  # noqa: E731
+                                      y=0x10000, n=256, k=512), **kw})
+    arr = lambda *js: (_W4Job * len(js))(*js)  # noqa: E731
+    assert fb(arr(J(), J(k=500)), 2, 40, 0, None) == -4       # second job bad: nothing launched
+    assert fb(arr(J(), J(y=None)), 2, 40, 0, None) == -1
+    assert fb(arr(J(x=0x10008)), 1, 40, 0, None) == -5
+    assert fb(arr(J()), 1, -1, 0, None) == -4 and fb(arr(J()), 1, 1, 3, None) == -2
+    assert fb(None, 1, 1, 0, None) == -1 and fb(None, 0, 1, 0, None) == 0
+    assert fb(arr(J(n=0, y=None)), 1, 40, 0, None) == 0
+
+
 def test_head_index_by_multiply_high_is_exact():
     """Per-head kernels find the head of a column c < heads * hu (hu = head_dim
     / 8 units) as the high 32 bits of c * ceil(2^32 / hu).  The ABI admits

@@ -198,3 +198,146 @@ def test_w4a16_large_launch_shape(pqb, M):
     codes, scales, zeros = oracle.int4_quantize(w[None])
     x = bf16_bits(r.standard_normal((M, K)))
     check(pqb, x, codes[0], scales[0], zeros, f"large launch M={M}")
+
+
+# ------------------------------------------------- matrix-core form, any M --
+# pqb_gemm_w4a16 evaluates each group of 128 as s * (P - (136 + z) S), where
+# P = sum x w and S = sum x are float32 matrix-core accumulations of exact
+# products, 32 per instruction, four instructions per group; then the groups
+# of each of four partial sums are added, and the four partial sums.  Counting
+# every one of the 128 additions of a group as one rounding, and twice that
+# for a matrix core that rounds each partial sum, the error is at most
+#   (256 + K/64) * 2^-24 * sum_k |s| |x| (|136 + q| + |136 + z|).
+
+def check_mfma(pqb, xb, codes, scales, zeros, what):
+    M, K = xb.shape
+    want = oracle.w4a16_gemv(xb, codes, scales, zeros)
+    tol = (256 + K // 64) * U * bound(xb, codes, scales, zeros) * 1.01 + 1e-30
+    xd = torch.from_numpy(xb.view(np.int16)).to(DEV).view(torch.bfloat16)
+    w = tuple(torch.from_numpy(np.ascontiguousarray(t)).to(DEV) for t in (codes, scales.view(np.int16), zeros))
+    for dt in (torch.float32, torch.bfloat16):
+        got = pqb.gemm_w4a16(xd, w, out_dtype=dt).float().cpu().numpy().astype(np.float64)
+        b = tol if dt == torch.float32 else tol + 2.0 ** -8 * (np.abs(want) + tol)
+        err = np.abs(got - want)
+        bad = np.argwhere(err > b)
+        assert bad.size == 0, (f"{what} {dt}: {len(bad)} outside the bound, first {bad[:3].tolist()}, "
+                               f"err {err[tuple(bad[0])]:.3e} bound {b[tuple(bad[0])]:.3e}")
+
+
+MFMA_SHAPES = [(1, 128, 128), (4, 1000, 4096), (9, 333, 2176), (16, 64, 14336), (17, 257, 384),
+               (32, 4096, 1024), (33, 9, 128 * 50), (100, 130, 512), (70, 77, 1152), (5, 16, 256),
+               (2, 1, 128 * 3)]
+
+
+@pytest.mark.parametrize("shape", MFMA_SHAPES)
+def test_w4a16_matrix_cores_match_oracle(pqb, shape):
+    """Several 16-row activation blocks and 32-row launch slices, ragged N (not
+    a multiple of 16), odd group counts (a half-empty last chunk) and K from
+    one group to 112."""
+    M, N, K = shape
+    r = rng(f"w4m{shape}")
+    w = (0.02 * r.standard_normal((N, K)) * np.exp(r.uniform(-2, 2, (N, 1)))).astype(np.float32)
+    codes, scales, zeros = oracle.int4_quantize(w[None])
+    x = bf16_bits(r.standard_normal((M, K)) * np.exp(r.uniform(-3, 3, (1, K))))
+    check_mfma(pqb, x, codes[0], scales[0], zeros, f"w4a16 mfma {shape}")
+
+
+def test_w4a16_matrix_cores_exact_integer_case(pqb):
+    """Small-integer weights and activations: every product, partial sum and
+    correction is an integer below 2^24, so the result is the integer matmul."""
+    r = rng("intm")
+    N, K = 96, 1024
+    w = r.integers(-7, 8, (N, K)).astype(np.float32)
+    w[:, ::128], w[:, 1::128] = 7.0, -8.0
+    codes, scales, zeros = oracle.int4_quantize(w[None])
+    x = r.integers(-20, 21, (40, K)).astype(np.float32)
+    xd = torch.from_numpy(bf16_bits(x).view(np.int16)).to(DEV).view(torch.bfloat16)
+    wt = tuple(torch.from_numpy(np.ascontiguousarray(t)).to(DEV) for t in (codes[0], scales[0].view(np.int16), zeros))
+    got = pqb.gemm_w4a16(xd, wt, out_dtype=torch.float32).cpu().numpy()
+    assert np.array_equal(got.astype(np.int64), x.astype(np.int64) @ w.T.astype(np.int64))
+
+
+def test_w4a16_matrix_cores_batch_equals_single_calls(pqb):
+    """40 products of mixed shapes at M = 20 (two launches of jobs, one slice
+    of rows) give, bit for bit, the single-call results."""
+    r = rng("batchm")
+    shapes = [(int(r.integers(1, 300)), 128 * int(r.integers(1, 40))) for _ in range(40)]
+    xs, ws = [], []
+    for N, K in shapes:
+        w = (0.02 * r.standard_normal((N, K))).astype(np.float32)
+        codes, scales, zeros = oracle.int4_quantize(w[None])
+        ws.append(tuple(torch.from_numpy(np.ascontiguousarray(t)).to(DEV)
+                        for t in (codes[0], scales[0].view(np.int16), zeros)))
+        xs.append(torch.from_numpy(bf16_bits(r.standard_normal((20, K))).view(np.int16)).to(DEV)
+                  .view(torch.bfloat16))
+    ys = pqb.gemm_w4a16_batch(xs, ws, out_dtype=torch.float32)
+    for i in (0, 7, 31, 32, 39):
+        assert torch.equal(ys[i], pqb.gemm_w4a16(xs[i], ws[i], out_dtype=torch.float32)), i
+    i = 33
+    c, s, z = (t.cpu().numpy() for t in ws[i])
+    check_mfma(pqb, xs[i].cpu().view(torch.int16).numpy().view(np.uint16), c, s.view(np.uint16), z,
+               "batch job 33")
+
+
+def test_w4a16_matrix_cores_rows_are_independent(pqb):
+    """Row m of the output depends only on row m of x: a 70-row product equals,
+    bit for bit, the products of its rows taken one at a time and in slices
+    that cross the 16- and 32-row boundaries differently."""
+    r = rng("rowsm")
+    N, K = 200, 768
+    w = (0.02 * r.standard_normal((N, K))).astype(np.float32)
+    codes, scales, zeros = oracle.int4_quantize(w[None])
+    wt = tuple(torch.from_numpy(np.ascontiguousarray(t)).to(DEV) for t in (codes[0], scales[0].view(np.int16), zeros))
+    x = torch.from_numpy(bf16_bits(r.standard_normal((70, K))).view(np.int16)).to(DEV).view(torch.bfloat16)
+    full = pqb.gemm_w4a16(x, wt, out_dtype=torch.float32)
+    for m in (0, 15, 16, 31, 32, 47, 69):
+        assert torch.equal(pqb.gemm_w4a16(x[m:m + 1].contiguous(), wt, out_dtype=torch.float32)[0], full[m]), m
+    assert torch.equal(pqb.gemm_w4a16(x[5:42].contiguous(), wt, out_dtype=torch.float32), full[5:42])
+
+
+def test_w4a16_matrix_cores_degenerate_sizes(pqb):
+    """k = 0 writes zeros (also inside a batch), m = 0 and n = 0 launch nothing."""
+    for dt in (torch.float32, torch.bfloat16):
+        for M, N in ((1, 5), (33, 300), (8, 70000)):
+            x = torch.empty((M, 0), dtype=torch.bfloat16, device=DEV)
+            empty = (torch.empty((N, 0), dtype=torch.uint8, device=DEV),
+                     torch.empty((N, 0), dtype=torch.int16, device=DEV),
+                     torch.empty((0,), dtype=torch.uint8, device=DEV))
+            y = pqb.gemm_w4a16(x, empty, out_dtype=dt)
+            assert y.shape == (M, N) and bool((y == 0).all()), (dt, M, N)
+    r = rng("degm")
+    w = (0.02 * r.standard_normal((130, 256))).astype(np.float32)
+    codes, scales, zeros = oracle.int4_quantize(w[None])
+    wt = tuple(torch.from_numpy(np.ascontiguousarray(t)).to(DEV) for t in (codes[0], scales[0].view(np.int16), zeros))
+    x = torch.from_numpy(bf16_bits(r.standard_normal((3, 256))).view(np.int16)).to(DEV).view(torch.bfloat16)
+    empty = (torch.empty((130, 0), dtype=torch.uint8, device=DEV), torch.empty((130, 0), dtype=torch.int16, device=DEV),
+             torch.empty((0,), dtype=torch.uint8, device=DEV))
+    ys = pqb.gemm_w4a16_batch([x, x[:, :0]], [wt, empty], out_dtype=torch.float32)
+    assert torch.equal(ys[0], pqb.gemm_w4a16(x, wt, out_dtype=torch.float32))
+    assert ys[1].shape == (3, 130) and bool((ys[1] == 0).all())
+    assert pqb.gemm_w4a16(x[:0], wt).shape == (0, 130)
+
+
+def test_w4a16_matrix_cores_subnormal_activations(pqb):
+    """bf16 subnormal activations keep their value on the matrix cores too."""
+    r = rng("subnm")
+    N, K = 200, 1024
+    w = (0.02 * r.standard_normal((N, K))).astype(np.float32)
+    codes, scales, zeros = oracle.int4_quantize(w[None])
+    x = np.empty((2, K), np.uint16)
+    x[0] = r.integers(1, 0x80, K) | (r.integers(0, 2, K) << 15)
+    x[1] = np.where(r.random(K) < 0.5, x[0], bf16_bits(r.standard_normal(K)))
+    check_mfma(pqb, x, codes[0], scales[0], zeros, "subnormal x (matrix cores)")
+
+
+def test_w4a16_matrix_cores_engine_quantized_llama_weights(pqb):
+    """A 16-token chunk against the engine's INT4 codes of Llama-3.1-8B-shaped
+    gate [14336 x 4096] and down [4096 x 14336] weights of layer 0."""
+    r = rng("llamam")
+    for proj in (4, 6):
+        w = synth.llama_weight(0, proj, device=DEV)
+        q = pqb.quantize(w, "int4_asym", "grp128")
+        N, K = w.shape
+        c, s, z = q.codes.cpu().numpy().reshape(N, K // 2), q.scales.cpu().view(torch.int16).numpy() \
+            .view(np.uint16).reshape(N, K // 128), q.aux.cpu().numpy()
+        check_mfma(pqb, bf16_bits(r.standard_normal((16, K))), c, s, z, f"llama proj {proj} M=16")
