@@ -201,3 +201,58 @@ def test_sweep_1gib_all_formats(pqb):
     oc, os_, oz = oracle.int4_quantize(gs_)
     eq(u8(q.codes.view(R, C // 2)[rows]), oc, "sweep int4 codes")
     eq(bits(q.scales.view(R, C // 128)[rows]), os_, "sweep int4 scales")
+
+
+def test_past_2_31_elements(pqb):
+    """A bf16 tensor [262272, 8192] holds 2^31 + 2^20 elements: its last
+    128-row band lies wholly past element 2^31, where 32-bit element indexing
+    would wrap.  Every one-pass and two-pass format, quantize and dequantize,
+    is compared with the oracle on three 128-row bands (first, middle, last);
+    the tensor maximum is planted in the last band, so the per-tensor scales
+    of the sample are the global ones."""
+    R, C = 262272, 8192
+    assert R * C > 2 ** 31 and (R - 128) * C >= 2 ** 31
+    g = torch.Generator(device=DEV).manual_seed(31)
+    x = torch.randn((R, C), generator=g, device=DEV).to(torch.bfloat16)
+    x[R - 1, C - 1] = 40.0
+    bands = list(range(0, 128)) + list(range(131072, 131200)) + list(range(R - 128, R))
+    xs = x[bands].cpu()
+    say("past 2^31: fp8 scopes")
+    for gran in ("1x128", "128x128", "row", "tensor"):
+        q = pqb.quantize(x, "fp8_e4m3", gran)
+        oc, os_ = oracle.fp8_quantize(xs, gran)
+        eq(u8(q.codes.view(R, C)[bands]), oc, f"fp8 {gran} codes")
+        if gran == "1x128":
+            eq(bits(q.scales.view(R, C // 128)[bands]), os_, "fp8 1x128 scales")
+        elif gran == "row":
+            eq(bits(q.scales[bands]), os_, "fp8 row scales")
+        elif gran == "tensor":
+            eq(bits(q.scales), os_, "fp8 tensor scale")
+        else:
+            tiles = [0, 1024, R // 128 - 1]
+            eq(bits(q.scales.view(R // 128, C // 128)[tiles]), os_, "fp8 128x128 scales")
+        dq = pqb.dequantize(q, torch.bfloat16)
+        eq(bits(dq[0][bands]), oracle.fp8_dequantize(oc, os_, gran, True), f"fp8 {gran} dequant")
+        del q, dq
+    say("past 2^31: mxfp4, nvfp4, int4")
+    q = pqb.quantize(x, "mxfp4")
+    oc, os_ = oracle.mxfp4_quantize(xs)
+    eq(u8(q.codes.view(R, C // 2)[bands]), oc, "mx codes")
+    eq(u8(q.scales.view(R, C // 32)[bands]), os_, "mx scales")
+    eq(bits(pqb.dequantize(q, torch.bfloat16)[0][bands]), oracle.mxfp4_dequantize(oc, os_, True), "mx dequant")
+    del q
+    q = pqb.quantize(x, "nvfp4")
+    oc, os_, og = oracle.nvfp4_quantize(xs)
+    eq(bits(q.aux), og, "nv tensor scale")
+    eq(u8(q.codes.view(R, C // 2)[bands]), oc, "nv codes")
+    eq(u8(q.scales.view(R, C // 16)[bands]), os_, "nv scales")
+    eq(bits(pqb.dequantize(q, torch.bfloat16)[0][bands]), oracle.nvfp4_dequantize(oc, os_, og, True), "nv dequant")
+    del q
+    q = pqb.quantize(x, "int4_asym")
+    oc, os_, oz = oracle.int4_quantize(xs)
+    eq(u8(q.codes.view(R, C // 2)[bands]), oc, "int4 codes")
+    eq(bits(q.scales.view(R, C // 128)[bands]), os_, "int4 scales")
+    zb = u8(q.aux).reshape(R, C // 256)          # 64 groups per row: 32 whole bytes
+    eq(zb[bands], oz, "int4 zero-points")
+    eq(bits(pqb.dequantize(q, torch.bfloat16)[0][bands]), oracle.int4_dequantize(oc, os_, oz, True),
+       "int4 dequant")
