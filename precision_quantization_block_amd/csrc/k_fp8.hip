@@ -32,14 +32,21 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_1x128(const T* __restrict
 
 constexpr int kTileWaves = 8;  // 512 threads per 128x128 tile: 4 rows of it per lane
 
-template <typename T, int kElem>
+// Large launches take two adjacent tiles per workgroup: twice the loads in
+// flight per lane and half the barriers per byte (1 GiB bf16: 272 -> 255 us).
+// With few tiles the halved workgroup count costs more than that gains
+// (896 tiles: 9.8 -> 10.6 us), hence the threshold.
+constexpr int64_t kPairTilesFrom = 4096;
+
+template <typename T, int kElem, int kTiles>
 __global__ __launch_bounds__(kTileWaves * kWave) void k_fp8_128x128(const T* __restrict__ x,
                                                                      int64_t rows, int64_t cols,
                                                                      int br,
                                                                      uint8_t* __restrict__ codes,
                                                                      float* __restrict__ scales) {
-  __shared__ uint32_t red[kTileWaves];
-  fp8_tile_128x128<T, kTileWaves, kElem>(x, rows, cols, br, blockIdx.x, codes, scales, red);
+  __shared__ uint32_t red[kTiles * kTileWaves];
+  fp8_tile_128x128<T, kTileWaves, kElem, kTiles>(x, rows, cols, br, (int64_t)blockIdx.x * kTiles,
+                                                 codes, scales, red);
 }
 
 template <typename T, int kMaxU, int kElem>
@@ -223,16 +230,24 @@ hipError_t launch_fp8_128x128(const void* x, bool bf16, int64_t batch, int64_t r
                               int elem) {
   const int br = (int)(rows < 128 ? rows : 128);
   const int64_t tiles = batch * (rows / br) * (cols / 128);
+  const bool pair = (cols / 128) % 2 == 0 && tiles >= kPairTilesFrom;
   return with_elem(elem, [&](auto e) {
     constexpr int E = decltype(e)::value;
-    if (bf16)
-      hipLaunchKernelGGL((k_fp8_128x128<uint16_t, E>), dim3((unsigned)tiles),
-                         dim3(kTileWaves * kWave), 0, st, (const uint16_t*)x, rows, cols, br, codes,
-                         scales);
-    else
-      hipLaunchKernelGGL((k_fp8_128x128<float, E>), dim3((unsigned)tiles),
-                         dim3(kTileWaves * kWave), 0, st, (const float*)x, rows, cols, br, codes,
-                         scales);
+    auto go = [&](auto kernel, const auto* xp, int64_t wgs) {
+      hipLaunchKernelGGL(kernel, dim3((unsigned)wgs), dim3(kTileWaves * kWave), 0, st, xp, rows,
+                         cols, br, codes, scales);
+    };
+    if (bf16) {
+      if (pair)
+        go(k_fp8_128x128<uint16_t, E, 2>, (const uint16_t*)x, tiles / 2);
+      else
+        go(k_fp8_128x128<uint16_t, E, 1>, (const uint16_t*)x, tiles);
+    } else {
+      if (pair)
+        go(k_fp8_128x128<float, E, 2>, (const float*)x, tiles / 2);
+      else
+        go(k_fp8_128x128<float, E, 1>, (const float*)x, tiles);
+    }
   });
 }
 

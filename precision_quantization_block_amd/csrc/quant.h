@@ -159,11 +159,15 @@ __device__ __forceinline__ void fp8_1x128_chunk(const T* __restrict__ x, int64_t
   }
 }
 
-// One br x 128 tile (br = min(128, rows)) per workgroup of kWaves waves (4 or
-// 8).  Lane l of wave w covers unit (l % 16) of tile rows w*4 + l/16 + 4*kWaves*k,
-// k < 32 / kWaves; the tile's amax is reduced through DPP, a cross-row shuffle
-// and LDS (`red`, kWaves words).  All threads of the workgroup must call it.
-template <typename T, int kWaves, int kElem = kE4M3>
+// kTiles horizontally adjacent br x 128 tiles (br = min(128, rows)), the
+// first being tile t, per workgroup of kWaves waves (4 or 8).  Lane l of wave
+// w covers unit (l % 16) of tile rows w*4 + l/16 + 4*kWaves*k, k < 32 /
+// kWaves, of every tile; all loads are issued before the first reduction.
+// Each tile's amax is reduced through DPP, a cross-row shuffle and LDS
+// (`red`, kTiles * kWaves words), with one barrier for all.  All threads of
+// the workgroup must call it; with kTiles = 2, t is even and the tile row
+// holds an even number of tiles.
+template <typename T, int kWaves, int kElem = kE4M3, int kTiles = 1>
 __device__ __forceinline__ void fp8_tile_128x128(const T* __restrict__ x, int64_t rows,
                                                  int64_t cols, int br, int64_t t,
                                                  uint8_t* __restrict__ codes,
@@ -175,35 +179,44 @@ __device__ __forceinline__ void fp8_tile_128x128(const T* __restrict__ x, int64_
   const int r0 = wave * 4 + (lane >> 4);
   // rows of consecutive batch slices are contiguous, so tile row trb starts at row trb*br
   const int64_t base = trb * br * cols + tc * 128 + (lane & 15) * 8;
-  Raw8 raw[kRowsPerLane];
+  Raw8 raw[kTiles][kRowsPerLane];
 #pragma unroll
-  for (int k = 0; k < kRowsPerLane; ++k) {
-    const int r = r0 + kRowStep * k;
-    raw[k] = r < br ? load_raw8(x + base + (int64_t)r * cols) : Raw8{};
-  }
-  uint32_t m = 0;
+  for (int h = 0; h < kTiles; ++h)
 #pragma unroll
-  for (int k = 0; k < kRowsPerLane; ++k) {
-    float v[8];
-    widen8(raw[k], x, v);
-    m = max(m, as_u(absmax8(v)));
+    for (int k = 0; k < kRowsPerLane; ++k) {
+      const int r = r0 + kRowStep * k;
+      raw[h][k] = r < br ? load_raw8(x + base + 128 * h + (int64_t)r * cols) : Raw8{};
+    }
+  uint32_t m[kTiles];
+#pragma unroll
+  for (int h = 0; h < kTiles; ++h) {
+    m[h] = 0;
+#pragma unroll
+    for (int k = 0; k < kRowsPerLane; ++k) {
+      float v[8];
+      widen8(raw[h][k], x, v);
+      m[h] = max(m[h], as_u(absmax8(v)));
+    }
+    m[h] = wave_umax(m[h]);
+    if (lane == 0) red[h * kWaves + wave] = m[h];
   }
-  m = wave_umax(m);
-  if (lane == 0) red[wave] = m;
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) m = max(m, red[i]);
-  const float s = fp8_scale_bits<kElem>(m);
-  const float y = recip_rn(s);
+  for (int h = 0; h < kTiles; ++h) {
 #pragma unroll
-  for (int k = 0; k < kRowsPerLane; ++k) {
-    const int r = r0 + kRowStep * k;
-    float v[8];
-    widen8(raw[k], x, v);
-    const uint2 w = fp8_pack8<kElem>(v, s, y);
-    if (r < br) store_codes8(codes + base + (int64_t)r * cols, w);
+    for (int i = 0; i < kWaves; ++i) m[h] = max(m[h], red[h * kWaves + i]);
+    const float s = fp8_scale_bits<kElem>(m[h]);
+    const float y = recip_rn(s);
+#pragma unroll
+    for (int k = 0; k < kRowsPerLane; ++k) {
+      const int r = r0 + kRowStep * k;
+      float v[8];
+      widen8(raw[h][k], x, v);
+      const uint2 w = fp8_pack8<kElem>(v, s, y);
+      if (r < br) store_codes8(codes + base + 128 * h + (int64_t)r * cols, w);
+    }
+    if (threadIdx.x == 0) scales[t + h] = s;
   }
-  if (threadIdx.x == 0) scales[t] = s;
 }
 
 // One row per wave, held in registers (cols % 8 == 0, cols <= 512 * kMaxU).

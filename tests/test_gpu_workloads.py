@@ -256,3 +256,27 @@ def test_past_2_31_elements(pqb):
     eq(zb[bands], oz, "int4 zero-points")
     eq(bits(pqb.dequantize(q, torch.bfloat16)[0][bands]), oracle.int4_dequantize(oc, os_, oz, True),
        "int4 dequant")
+
+
+def test_fp8_128x128_paired_tiles(pqb):
+    """Launches of 4096 or more 128x128 tiles (with an even number per tile row)
+    take two adjacent tiles per workgroup.  Checked on sampled tile rows: a
+    batch of 64 slices of 100 rows (short tiles, br = 100) in bf16 with E4M3,
+    and a float32 [16384, 4096] tensor with E5M2."""
+    g = torch.Generator(device=DEV).manual_seed(128)
+    x = (torch.randn((64, 100, 8192), generator=g, device=DEV) *
+         torch.exp(torch.randn((64, 100, 1), generator=g, device=DEV))).to(torch.bfloat16)
+    q = pqb.quantize(x, "fp8_e4m3", "128x128")
+    dq = pqb.dequantize(q, torch.bfloat16)
+    for b in (0, 31, 63):
+        oc, os_ = oracle.fp8_quantize(x[b:b + 1].cpu(), "128x128")
+        eq(u8(q.codes.view(64, 100, 8192)[b]), oc, f"paired e4m3 codes slice {b}")
+        eq(bits(q.scales.view(64, 64)[b]), os_, f"paired e4m3 scales slice {b}")
+        eq(bits(dq[b]), oracle.fp8_dequantize(oc, os_, "128x128", True), f"paired e4m3 dequant {b}")
+    y = torch.randn((16384, 4096), generator=g, device=DEV) * 3.0
+    q = pqb.quantize(y, "fp8_e5m2", "128x128")
+    for tr in (0, 77, 127):
+        rows = slice(128 * tr, 128 * tr + 128)
+        oc, os_ = oracle.fp8_quantize(y[rows].cpu(), "128x128", elem="e5m2")
+        eq(u8(q.codes.view(16384, 4096)[rows]), oc, f"paired e5m2 codes tile row {tr}")
+        eq(bits(q.scales.view(128, 32)[tr]), os_, f"paired e5m2 scales tile row {tr}")
