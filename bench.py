@@ -291,8 +291,8 @@ def bench_extras(torch, eng, synth, reps, only=None):
         one("w7168x2048_bf16_fp8_128x128", w, "fp8_e4m3", "128x128", (1, 7168, 2048))
         del w
     # 1 GiB bf16 tensor, every format
-    sweep = (("fp8_e4m3", "1x128", torch.bfloat16), ("fp8_e4m3", "128x128", None),
-             ("fp8_e4m3", "row", None), ("fp8_e4m3", "tensor", None),
+    sweep = (("fp8_e4m3", "1x128", torch.bfloat16), ("fp8_e4m3", "128x128", torch.bfloat16),
+             ("fp8_e4m3", "row", torch.bfloat16), ("fp8_e4m3", "tensor", torch.bfloat16),
              ("mxfp4", "blk32", torch.bfloat16), ("nvfp4", "blk16", torch.bfloat16),
              ("int4_asym", "grp128", torch.bfloat16), ("fp8_e5m2", "1x128", torch.bfloat16),
              ("int8_sym", "row", torch.bfloat16), ("mxfp8", "blk32", torch.bfloat16))

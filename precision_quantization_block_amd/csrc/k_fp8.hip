@@ -134,15 +134,69 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_tensor_quant(TensorArgs a
 
 // ---------------------------------------------------------------------------
 // Dequantization of the per-tensor, per-row and 128x128 scopes: out =
-// dec(code) * s, float32 or RNE bf16, one wave per row (rows of all slices in
-// sequence): the row's scale index is formed once per row; only the
-// 128-column block varies.
+// dec(code) * s, float32 or RNE bf16.  When cols % 8 == 0 a wave expands one
+// segment of a row, kDqSegUnits units of 8 elements (4 per lane, all loaded
+// before the first store), and the segment's scale index is formed once; the
+// segments of all rows of all slices are numbered in sequence.  Otherwise a
+// wave expands one row element by element.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint2 ld_codes8(const uint8_t* p) {
   return *reinterpret_cast<const uint2*>(p);
 }
 
-template <bool kBf16Out, bool kVec, int kElem>
+constexpr int kDqSegLane = 4;                       // units per lane of a segment
+constexpr int kDqSegUnits = kDqSegLane * kWave;     // units per segment
+
+// Scale index of column c of global row gr: si0 + (c / 128) * tile_stride.
+__device__ __forceinline__ void row_scale_index(int gran, int64_t gr, int64_t rows, int64_t cols,
+                                                int br, int64_t& si0, int64_t& tile_stride) {
+  const int64_t b = gr / rows, r = gr - b * rows;
+  tile_stride = 0;
+  switch (gran) {
+    case 0: si0 = b; break;
+    case 1: si0 = gr; break;
+    default: si0 = (b * (rows / br) + r / br) * (cols / 128); tile_stride = 1; break;
+  }
+}
+
+template <bool kBf16Out, int kElem>
+__global__ __launch_bounds__(kBlockThreads) void k_fp8_dequant_segs(const uint8_t* __restrict__ codes,
+                                                                     const float* __restrict__ scales,
+                                                                     int gran, int64_t nsegs,
+                                                                     int64_t rows, int64_t cols,
+                                                                     int br,
+                                                                     void* __restrict__ out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  const int64_t upr = cols / 8, spr = (upr + kDqSegUnits - 1) / kDqSegUnits;
+  const int64_t nw = (int64_t)gridDim.x * (kBlockThreads / kWave);
+  for (int64_t w = (int64_t)blockIdx.x * (kBlockThreads / kWave) + wave; w < nsegs; w += nw) {
+    const int64_t gr = w / spr, u0 = (w - gr * spr) * kDqSegUnits;
+    int64_t si0, tile_stride;
+    row_scale_index(gran, gr, rows, cols, br, si0, tile_stride);
+    uint2 c[kDqSegLane];
+    float sc[kDqSegLane];
+#pragma unroll
+    for (int k = 0; k < kDqSegLane; ++k) {
+      const int64_t u = u0 + k * kWave + lane;
+      if (u < upr) {
+        c[k] = ld_codes8(codes + gr * cols + u * 8);
+        sc[k] = scales[si0 + (u >> 4) * tile_stride];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kDqSegLane; ++k) {
+      const int64_t u = u0 + k * kWave + lane;
+      if (u < upr) {
+        float o[8];
+        fp8_decode8<kElem>(c[k], sc[k], o);
+        store_out8<kBf16Out>(out, gr * upr + u, o);
+      }
+    }
+  }
+}
+
+template <bool kBf16Out, int kElem>
 __global__ __launch_bounds__(kBlockThreads) void k_fp8_dequant_rows(const uint8_t* __restrict__ codes,
                                                                      const float* __restrict__ scales,
                                                                      int gran, int64_t nrows_total,
@@ -152,29 +206,15 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_dequant_rows(const uint8_
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t nw = (int64_t)gridDim.x * (kBlockThreads / kWave);
   for (int64_t gr = wave_index(); gr < nrows_total; gr += nw) {
-    const int64_t b = gr / rows, r = gr - b * rows;
-    int64_t si0 = 0, tile_stride = 0;  // scale index of column c: si0 + (c / 128) * tile_stride
-    switch (gran) {
-      case 0: si0 = b; break;
-      case 1: si0 = gr; break;
-      default: si0 = (b * (rows / br) + r / br) * (cols / 128); tile_stride = 1; break;
-    }
-    if constexpr (kVec) {
-      for (int64_t u = lane; u < cols / 8; u += kWave) {
-        float o[8];
-        fp8_decode8<kElem>(ld_codes8(codes + gr * cols + u * 8),
-                           scales[si0 + (u >> 4) * tile_stride], o);
-        store_out8<kBf16Out>(out, gr * (cols / 8) + u, o);
-      }
-    } else {
-      for (int64_t c = lane; c < cols; c += kWave) {
-        const float v = elem_decode2<kElem, false>(codes[gr * cols + c]).x *
-                        scales[si0 + (c >> 7) * tile_stride];
-        if constexpr (kBf16Out)
-          reinterpret_cast<uint16_t*>(out)[gr * cols + c] = (uint16_t)bf16x2_rne(v, 0.0f);
-        else
-          reinterpret_cast<float*>(out)[gr * cols + c] = v;
-      }
+    int64_t si0, tile_stride;
+    row_scale_index(gran, gr, rows, cols, br, si0, tile_stride);
+    for (int64_t c = lane; c < cols; c += kWave) {
+      const float v = elem_decode2<kElem, false>(codes[gr * cols + c]).x *
+                      scales[si0 + (c >> 7) * tile_stride];
+      if constexpr (kBf16Out)
+        reinterpret_cast<uint16_t*>(out)[gr * cols + c] = (uint16_t)bf16x2_rne(v, 0.0f);
+      else
+        reinterpret_cast<float*>(out)[gr * cols + c] = v;
     }
   }
 }
@@ -321,19 +361,26 @@ hipError_t launch_fp8_dequant(const uint8_t* codes, const float* scales, int gra
     return launch_fp8_1x128_dequant(codes, scales, n, out_bf16, out, st, elem);
   const int br = (int)(rows < 128 ? rows : 128);
   const int64_t nrows = batch * rows;
-  const int grid = blocks_for(nrows, kBlockThreads / kWave, 1 << 16);
-  const bool vec = cols % 8 == 0;
   return with_elem(elem, [&](auto e) {
     constexpr int E = decltype(e)::value;
-#define PQB_DQ(B, V)                                                                          \
-  hipLaunchKernelGGL((k_fp8_dequant_rows<B, V, E>), dim3(grid), dim3(kBlockThreads), 0, st,    \
-                     codes, scales, gran, nrows, rows, cols, br, out)
-    if (out_bf16) {
-      if (vec) PQB_DQ(true, true); else PQB_DQ(true, false);
+    if (cols % 8 == 0) {
+      const int64_t nsegs = nrows * ((cols / 8 + kDqSegUnits - 1) / kDqSegUnits);
+      const int grid = blocks_for(nsegs, kBlockThreads / kWave, 1 << 20);
+      if (out_bf16)
+        hipLaunchKernelGGL((k_fp8_dequant_segs<true, E>), dim3(grid), dim3(kBlockThreads), 0, st,
+                           codes, scales, gran, nsegs, rows, cols, br, out);
+      else
+        hipLaunchKernelGGL((k_fp8_dequant_segs<false, E>), dim3(grid), dim3(kBlockThreads), 0, st,
+                           codes, scales, gran, nsegs, rows, cols, br, out);
     } else {
-      if (vec) PQB_DQ(false, true); else PQB_DQ(false, false);
+      const int grid = blocks_for(nrows, kBlockThreads / kWave, 1 << 16);
+      if (out_bf16)
+        hipLaunchKernelGGL((k_fp8_dequant_rows<true, E>), dim3(grid), dim3(kBlockThreads), 0, st,
+                           codes, scales, gran, nrows, rows, cols, br, out);
+      else
+        hipLaunchKernelGGL((k_fp8_dequant_rows<false, E>), dim3(grid), dim3(kBlockThreads), 0, st,
+                           codes, scales, gran, nrows, rows, cols, br, out);
     }
-#undef PQB_DQ
   });
 }
 
