@@ -263,31 +263,31 @@ hipError_t launch_args(W4Args& a, int M, int64_t rows, bool out_bf16, hipStream_
 
 // ---------------------------------------------------------------------------
 // The same product on the matrix cores, for any M (v_mfma_f32_16x16x32_bf16).
-// A workgroup owns 64 weight rows, four tiles of 16 (the MFMA's N), and its 4
-// waves split K into four contiguous ranges of groups, so that one wave reads
-// both halves of a 128-byte code line and a row's scales in consecutive
-// steps.  For one group, lane l supplies row l & 15 of the activation block
-// and of each weight tile, and K positions 32 (l >> 4) .. + 31 of the group,
-// 8 per MFMA: its 16 code bytes of a tile are one load, and the activations
-// of each MFMA one 16-byte load in the same K order, shared by the four
-// tiles.  The codes become exact
-// bf16 w = 136 + q (high byte 0x43, low byte q + 8), so a group contributes
-// s * (P - (136 + z) * S) with P = sum x w from four MFMAs per tile and
-// S = sum x from four more against a B of ones; both are float32
-// accumulations of exact products.  The four waves' results meet in LDS and
-// are added in wave order.  Activation rows come in blocks of 16 (kMB of
-// them, up to 32 rows per launch); rows past M and weight rows past N are
-// read clamped and never stored.
+// A workgroup owns kTiles tiles of 16 weight rows (the MFMA's N): four in
+// launches of 2^16 rows or more, where sharing each activation load among the
+// tiles pays, and one in smaller launches (a layer's projections), which need
+// the workgroups.  Its 4 waves split K into four contiguous ranges of groups,
+// so that one wave reads both halves of a 128-byte code line and a row's
+// scales in consecutive steps.  For one group, lane l supplies row l & 15 of
+// the activation block and of each weight tile, and K positions 32 (l >> 4)
+// .. + 31 of the group, 8 per MFMA: its 16 code bytes of a tile are one load,
+// and the activations of each MFMA one 16-byte load in the same K order,
+// shared by the tiles.  The codes become exact bf16 w = 136 + q (high byte
+// 0x43, low byte q + 8), so a group contributes s * (P - (136 + z) * S) with
+// P = sum x w from four MFMAs per tile and S = sum x from four more against a
+// B of ones; both are float32 accumulations of exact products.  The four
+// waves' results meet in LDS and are added in wave order.  Activation rows
+// come in blocks of 16 (kMB of them, up to 32 rows per launch); rows past M
+// and weight rows past N are read clamped and never stored.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
-constexpr int kTiles = 4;                    // 16-row weight tiles per workgroup
-constexpr int kMfmaRows = 16 * kTiles;       // weight rows per workgroup
 constexpr int kMaxMB = 2;                    // 16-row activation blocks per launch
 constexpr int kMfmaWaves = kWThreads / 64;
 
-template <int kMB, bool kBf16Out>
+template <int kMB, int kTiles, bool kBf16Out>
 __global__ __launch_bounds__(kWThreads) void k_w4a16_mfma(const W4Args a, int M) {
+  constexpr int kMfmaRows = 16 * kTiles;
   int jb = 0;
   while (jb + 1 < a.njobs && a.wg_begin[jb + 1] <= (int)blockIdx.x) ++jb;
   const uint16_t* __restrict__ x = a.job[jb].x;
@@ -430,12 +430,17 @@ __global__ __launch_bounds__(kWThreads) void k_w4a16_mfma(const W4Args a, int M)
   }
 }
 
-template <int kMB>
+// Launches of this many weight rows or more take four tiles per workgroup.
+constexpr int64_t kMfmaBigLaunchRows = 1 << 16;
+
+template <int kMB, int kTiles>
 void launch_mfma_mb(const W4Args& a, int wgs, int M, bool out_bf16, hipStream_t st) {
   if (out_bf16)
-    hipLaunchKernelGGL((k_w4a16_mfma<kMB, true>), dim3((unsigned)wgs), dim3(kWThreads), 0, st, a, M);
+    hipLaunchKernelGGL((k_w4a16_mfma<kMB, kTiles, true>), dim3((unsigned)wgs), dim3(kWThreads), 0,
+                       st, a, M);
   else
-    hipLaunchKernelGGL((k_w4a16_mfma<kMB, false>), dim3((unsigned)wgs), dim3(kWThreads), 0, st, a, M);
+    hipLaunchKernelGGL((k_w4a16_mfma<kMB, kTiles, false>), dim3((unsigned)wgs), dim3(kWThreads), 0,
+                       st, a, M);
 }
 
 }  // namespace
@@ -465,6 +470,9 @@ hipError_t launch_w4a16_mfma(const W4Job* jobs, int njobs, int64_t M, bool out_b
       const int n = njobs - base < kW4MaxJobs ? njobs - base : kW4MaxJobs;
       W4Args a{};
       a.njobs = n;
+      int64_t rows = 0;
+      for (int i = 0; i < n; ++i) rows += jobs[base + i].N;
+      const int tiles = rows >= kMfmaBigLaunchRows ? 4 : 1, per_wg = 16 * tiles;
       int wg = 0;
       for (int i = 0; i < n; ++i) {
         W4Job j = jobs[base + i];
@@ -472,14 +480,16 @@ hipError_t launch_w4a16_mfma(const W4Job* jobs, int njobs, int64_t M, bool out_b
         j.y = static_cast<char*>(j.y) + m0 * j.N * (out_bf16 ? 2 : 4);
         a.job[i] = j;
         a.wg_begin[i] = wg;
-        wg += (j.N + kMfmaRows - 1) / kMfmaRows;
+        wg += (j.N + per_wg - 1) / per_wg;
       }
       a.wg_begin[n] = wg;
       if (wg == 0) continue;
       if (mr > 16)
-        launch_mfma_mb<2>(a, wg, mr, out_bf16, st);
+        tiles == 4 ? launch_mfma_mb<2, 4>(a, wg, mr, out_bf16, st)
+                   : launch_mfma_mb<2, 1>(a, wg, mr, out_bf16, st);
       else
-        launch_mfma_mb<1>(a, wg, mr, out_bf16, st);
+        tiles == 4 ? launch_mfma_mb<1, 4>(a, wg, mr, out_bf16, st)
+                   : launch_mfma_mb<1, 1>(a, wg, mr, out_bf16, st);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }

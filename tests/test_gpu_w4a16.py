@@ -341,3 +341,16 @@ def test_w4a16_matrix_cores_engine_quantized_llama_weights(pqb):
         c, s, z = q.codes.cpu().numpy().reshape(N, K // 2), q.scales.cpu().view(torch.int16).numpy() \
             .view(np.uint16).reshape(N, K // 128), q.aux.cpu().numpy()
         check_mfma(pqb, bf16_bits(r.standard_normal((16, K))), c, s, z, f"llama proj {proj} M=16")
+
+
+@pytest.mark.parametrize("M", [1, 17, 40])
+def test_w4a16_matrix_cores_large_launch(pqb, M):
+    """A launch of 2^16 weight rows or more takes four 16-row tiles per
+    workgroup (smaller launches one): a ragged N = 66001 with M in one block,
+    two blocks, and two launch slices."""
+    r = rng(f"bigm{M}")
+    N, K = 66001, 256
+    w = (0.02 * r.standard_normal((N, K))).astype(np.float32)
+    codes, scales, zeros = oracle.int4_quantize(w[None])
+    check_mfma(pqb, bf16_bits(r.standard_normal((M, K))), codes[0], scales[0], zeros,
+               f"large launch M={M}")
