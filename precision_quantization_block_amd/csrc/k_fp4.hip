@@ -17,15 +17,33 @@ __global__ __launch_bounds__(kBlockThreads) void k_mxfp4(const T* __restrict__ x
                                                           uint8_t* __restrict__ codes,
                                                           uint8_t* __restrict__ scales) {
   __shared__ __align__(16) uint8_t lut[kE2M1LutSize];
+  const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
+  int64_t t0 = (int64_t)wave_index() * kUnr;
+  // The first chunk's loads go out before the table fill and its barrier
+  // (a small tensor is one chunk per wave: 5.7 -> 5.2 us for 12.6 MB).
+  const int64_t u0 = t0 * kWave;
+  const bool have = u0 < nunits, full = u0 + kUnr * kWave <= nunits;
+  Raw8 raw[kUnr];
+  if (have) {
+    if (full)
+      load_chunk<T, kUnr, false>(x, u0, nunits, raw);
+    else
+      load_chunk<T, kUnr, true>(x, u0, nunits, raw);
+  }
   e2m1_lut_fill(lut, 0);
   __syncthreads();
-  const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
-  for (int64_t t0 = (int64_t)wave_index() * kUnr; t0 * kWave < nunits; t0 += nwaves * kUnr) {
-    const int64_t u0 = t0 * kWave;
-    if (u0 + kUnr * kWave <= nunits)
-      mx_chunk<T, kUnr, false>(x, u0, nunits, codes, scales, lut);
+  if (have) {
+    if (full)
+      mx_pack<T, kUnr, false>(x, raw, u0, nunits, codes, scales, lut);
     else
-      mx_chunk<T, kUnr, true>(x, u0, nunits, codes, scales, lut);
+      mx_pack<T, kUnr, true>(x, raw, u0, nunits, codes, scales, lut);
+  }
+  for (t0 += nwaves * kUnr; t0 * kWave < nunits; t0 += nwaves * kUnr) {
+    const int64_t u1 = t0 * kWave;
+    if (u1 + kUnr * kWave <= nunits)
+      mx_chunk<T, kUnr, false>(x, u1, nunits, codes, scales, lut);
+    else
+      mx_chunk<T, kUnr, true>(x, u1, nunits, codes, scales, lut);
   }
 }
 

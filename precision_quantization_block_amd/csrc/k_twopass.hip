@@ -302,10 +302,14 @@ __global__ __launch_bounds__(kBlockThreads) void k_tp_nv(TpArgs a, TpGeo g,
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
   const int64_t u0 = ((int64_t)blockIdx.x * kWgWaves + wave) * U * kWave;
   if (u0 >= nunits) return;
-  if (u0 + U * kWave <= nunits)
-    nv_chunk<T, U, false>(xs, u0, nunits, cs, bs, gs, ygs, tb);
-  else
-    nv_chunk<T, U, true>(xs, u0, nunits, cs, bs, gs, ygs, tb);
+  Raw8 raw[U];
+  if (u0 + U * kWave <= nunits) {
+    load_chunk<T, U, false>(xs, u0, nunits, raw);
+    nv_pack<T, U, false>(xs, raw, u0, nunits, cs, bs, gs, ygs, tb);
+  } else {
+    load_chunk<T, U, true>(xs, u0, nunits, raw);
+    nv_pack<T, U, true>(xs, raw, u0, nunits, cs, bs, gs, ygs, tb);
+  }
 }
 
 int64_t wgs_per_slice(int64_t per_slice, bool bf16) {

@@ -277,12 +277,10 @@ __device__ __forceinline__ void fp8_row_any(const T* __restrict__ x, int64_t row
 // the page's quotient, signed zeros included.
 // ---------------------------------------------------------------------------
 template <typename T, int kUnr, bool kGuard>
-__device__ __forceinline__ void mx_chunk(const T* __restrict__ x, int64_t u0, int64_t nunits,
-                                         uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                         const uint8_t* lut) {
+__device__ __forceinline__ void mx_pack(const T* __restrict__ x, const Raw8 (&raw)[kUnr], int64_t u0,
+                                        int64_t nunits, uint8_t* __restrict__ codes,
+                                        uint8_t* __restrict__ scales, const uint8_t* lut) {
   const int lane = threadIdx.x & (kWave - 1);
-  Raw8 raw[kUnr];
-  load_chunk<T, kUnr, kGuard>(x, u0, nunits, raw);
 #pragma unroll
   for (int k = 0; k < kUnr; ++k) {
     float v[8];
@@ -301,6 +299,17 @@ __device__ __forceinline__ void mx_chunk(const T* __restrict__ x, int64_t u0, in
   }
 }
 
+// Load and pack one chunk (the loads may instead be issued earlier, then
+// mx_pack called on the raw tiles).
+template <typename T, int kUnr, bool kGuard>
+__device__ __forceinline__ void mx_chunk(const T* __restrict__ x, int64_t u0, int64_t nunits,
+                                         uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                         const uint8_t* lut) {
+  Raw8 raw[kUnr];
+  load_chunk<T, kUnr, kGuard>(x, u0, nunits, raw);
+  mx_pack<T, kUnr, kGuard>(x, raw, u0, nunits, codes, scales, lut);
+}
+
 // ---------------------------------------------------------------------------
 // NVFP4 (page "量化部署实战", section 伪量化实现), pass 2: 2 lanes x 8 elements
 // per 16-element block.  The block scale code is E4M3((amax_b / 6) / gs); the
@@ -313,16 +322,11 @@ struct __align__(16) NvTables {
 };
 
 template <typename T, int kUnr, bool kGuard>
-__device__ __forceinline__ void nv_chunk(const T* __restrict__ xs, int64_t u0, int64_t nunits,
-                                         uint8_t* __restrict__ cs, uint8_t* __restrict__ ss,
-                                         float gs, float ygs, const NvTables& tb) {
+__device__ __forceinline__ void nv_pack(const T* __restrict__ xs, const Raw8 (&raw)[kUnr], int64_t u0,
+                                        int64_t nunits, uint8_t* __restrict__ cs,
+                                        uint8_t* __restrict__ ss, float gs, float ygs,
+                                        const NvTables& tb) {
   const int lane = threadIdx.x & (kWave - 1);
-  const T* xb = xs + u0 * 8;
-  Raw8 raw[kUnr];
-#pragma unroll
-  for (int k = 0; k < kUnr; ++k)
-    raw[k] = (!kGuard || u0 + k * kWave + lane < nunits) ? load_raw8(xb + (k * kWave + lane) * 8)
-                                                           : Raw8{};
 #pragma unroll
   for (int k = 0; k < kUnr; ++k) {
     float v[8];
