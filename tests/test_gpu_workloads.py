@@ -280,3 +280,19 @@ def test_fp8_128x128_paired_tiles(pqb):
         oc, os_ = oracle.fp8_quantize(y[rows].cpu(), "128x128", elem="e5m2")
         eq(u8(q.codes.view(16384, 4096)[rows]), oc, f"paired e5m2 codes tile row {tr}")
         eq(bits(q.scales.view(128, 32)[tr]), os_, f"paired e5m2 scales tile row {tr}")
+
+
+def test_fp8_1x128_large_ragged_chunk(pqb):
+    """From 2^28 elements the 1x128 quantizer takes chunks of 2 tiles per wave.
+    A bf16 [32300, 8320] tensor (>= 2^28 elements, an odd number of 64-unit
+    tiles) ends in a half chunk; the first rows and the last rows, which hold
+    it, are compared with the oracle."""
+    R, C = 32300, 8320
+    assert R * C >= 2 ** 28 and (R * C // 8 // 64) % 2 == 1
+    g = torch.Generator(device=DEV).manual_seed(283)
+    x = torch.randn((R, C), generator=g, device=DEV).to(torch.bfloat16)
+    q = pqb.quantize(x, "fp8_e4m3", "1x128")
+    rows = list(range(0, 4)) + list(range(R - 40, R))
+    oc, os_ = oracle.fp8_quantize(x[rows].cpu(), "1x128")
+    eq(u8(q.codes.view(R, C)[rows]), oc, "1x128 codes")
+    eq(bits(q.scales.view(R, C // 128)[rows]), os_, "1x128 scales")
