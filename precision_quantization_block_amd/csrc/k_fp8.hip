@@ -149,18 +149,25 @@ constexpr int kDqSegLane = 2;                       // units per lane of a segme
 constexpr int kDqSegUnits = kDqSegLane * kWave;     // units per segment
 
 // Scale index of column c of global row gr: si0 + (c / 128) * tile_stride.
-__device__ __forceinline__ void row_scale_index(int gran, int64_t gr, int64_t rows, int64_t cols,
-                                                int br, int64_t& si0, int64_t& tile_stride) {
-  const int64_t b = gr / rows, r = gr - b * rows;
+// I is the index type of the divisions: uint32_t when every count fits, which
+// spares a 64-bit division routine per segment.
+template <typename I>
+__device__ __forceinline__ void row_scale_index(int gran, I gr, I rows, I cols, int br,
+                                                int64_t& si0, int64_t& tile_stride) {
   tile_stride = 0;
   switch (gran) {
-    case 0: si0 = b; break;
-    case 1: si0 = gr; break;
-    default: si0 = (b * (rows / br) + r / br) * (cols / 128); tile_stride = 1; break;
+    case 0: si0 = (int64_t)(gr / rows); break;
+    case 1: si0 = (int64_t)gr; break;
+    default: {
+      const I b = gr / rows, r = gr - b * rows;
+      si0 = ((int64_t)b * (int64_t)(rows / (I)br) + (int64_t)(r / (I)br)) * (int64_t)(cols / 128);
+      tile_stride = 1;
+      break;
+    }
   }
 }
 
-template <bool kBf16Out, int kElem>
+template <bool kBf16Out, int kElem, typename I>
 __global__ __launch_bounds__(kBlockThreads) void k_fp8_dequant_segs(const uint8_t* __restrict__ codes,
                                                                      const float* __restrict__ scales,
                                                                      int gran, int64_t nsegs,
@@ -169,12 +176,14 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_dequant_segs(const uint8_
                                                                      void* __restrict__ out) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
-  const int64_t upr = cols / 8, spr = (upr + kDqSegUnits - 1) / kDqSegUnits;
+  const int64_t upr = cols / 8;
+  const I spr = (I)((upr + kDqSegUnits - 1) / kDqSegUnits);
   const int64_t nw = (int64_t)gridDim.x * (kBlockThreads / kWave);
   for (int64_t w = (int64_t)blockIdx.x * (kBlockThreads / kWave) + wave; w < nsegs; w += nw) {
-    const int64_t gr = w / spr, u0 = (w - gr * spr) * kDqSegUnits;
+    const I gri = (I)w / spr;
+    const int64_t gr = (int64_t)gri, u0 = (int64_t)((I)w - gri * spr) * kDqSegUnits;
     int64_t si0, tile_stride;
-    row_scale_index(gran, gr, rows, cols, br, si0, tile_stride);
+    row_scale_index<I>(gran, gri, (I)rows, (I)cols, br, si0, tile_stride);
     uint2 c[kDqSegLane];
     float sc[kDqSegLane];
 #pragma unroll
@@ -208,7 +217,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_dequant_rows(const uint8_
   const int64_t nw = (int64_t)gridDim.x * (kBlockThreads / kWave);
   for (int64_t gr = wave_index(); gr < nrows_total; gr += nw) {
     int64_t si0, tile_stride;
-    row_scale_index(gran, gr, rows, cols, br, si0, tile_stride);
+    row_scale_index<int64_t>(gran, gr, rows, cols, br, si0, tile_stride);
     for (int64_t c = lane; c < cols; c += kWave) {
       const float v = elem_decode2<kElem, false>(codes[gr * cols + c]).x *
                       scales[si0 + (c >> 7) * tile_stride];
@@ -377,12 +386,16 @@ hipError_t launch_fp8_dequant(const uint8_t* codes, const float* scales, int gra
     if (cols % 8 == 0) {
       const int64_t nsegs = nrows * ((cols / 8 + kDqSegUnits - 1) / kDqSegUnits);
       const int grid = blocks_for(nsegs, kBlockThreads / kWave, 1 << 20);
+      // 32-bit divisions while segment, row and column counts fit
+      const bool narrow = nsegs <= UINT32_MAX && cols <= UINT32_MAX;
+      auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3(grid), dim3(kBlockThreads), 0, st, codes, scales, gran,
+                           nsegs, rows, cols, br, out);
+      };
       if (out_bf16)
-        hipLaunchKernelGGL((k_fp8_dequant_segs<true, E>), dim3(grid), dim3(kBlockThreads), 0, st,
-                           codes, scales, gran, nsegs, rows, cols, br, out);
+        narrow ? go(k_fp8_dequant_segs<true, E, uint32_t>) : go(k_fp8_dequant_segs<true, E, int64_t>);
       else
-        hipLaunchKernelGGL((k_fp8_dequant_segs<false, E>), dim3(grid), dim3(kBlockThreads), 0, st,
-                           codes, scales, gran, nsegs, rows, cols, br, out);
+        narrow ? go(k_fp8_dequant_segs<false, E, uint32_t>) : go(k_fp8_dequant_segs<false, E, int64_t>);
     } else {
       const int grid = blocks_for(nrows, kBlockThreads / kWave, 1 << 16);
       if (out_bf16)
