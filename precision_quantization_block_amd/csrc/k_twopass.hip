@@ -54,8 +54,12 @@ __device__ __forceinline__ int groups_of(const TpArgs& a, const TpGeo& g, int tz
 // and the per-tile step, for the per-head scope.
 struct ColWalk {
   uint32_t c, step, R, magic;
+  // 32-bit remainder while a slice's unit indices fit (a 64-bit one costs a
+  // division routine per lane and chunk)
   __device__ __forceinline__ ColWalk(int64_t u0, const TpGeo& g)
-      : c((uint32_t)((u0 + (threadIdx.x & (kWave - 1))) % g.row_units)),
+      : c(g.per_slice / 8 + kWave <= (int64_t)UINT32_MAX
+              ? ((uint32_t)u0 + (uint32_t)(threadIdx.x & (kWave - 1))) % (uint32_t)g.row_units
+              : (uint32_t)((u0 + (threadIdx.x & (kWave - 1))) % g.row_units)),
         step((uint32_t)(kWave % g.row_units)),
         R((uint32_t)g.row_units),
         magic(g.head_magic) {}
