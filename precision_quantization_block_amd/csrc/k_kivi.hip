@@ -112,6 +112,20 @@ __device__ __forceinline__ void widen4(const Raw4<T>& r, float v[4]) {
 
 // K: thread t owns channels [4c, 4c + 4) of token group `slab` (= layer * (T /
 // 32) + token group), with c = t % R4, R4 = heads * head_dim / 4.
+// slab = t / R4 and c = t % R4, in 32 bits while the thread count fits (a
+// 64-bit division is a routine of its own in every thread).
+__device__ __forceinline__ void slab_of(int64_t t, int64_t nthreads, int64_t R4, int64_t& slab,
+                                        int64_t& c) {
+  if (nthreads <= (int64_t)UINT32_MAX) {
+    const uint32_t s32 = (uint32_t)t / (uint32_t)R4;
+    slab = s32;
+    c = (int64_t)((uint32_t)t - s32 * (uint32_t)R4);
+  } else {
+    slab = t / R4;
+    c = t - slab * R4;
+  }
+}
+
 template <typename T, int kBits>
 __global__ __launch_bounds__(kBlockThreads) void k_kivi_k(const T* __restrict__ x, int64_t nslabs,
                                                           int64_t R4, uint8_t* __restrict__ codes,
@@ -119,7 +133,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_kivi_k(const T* __restrict__ 
                                                           float* __restrict__ mins) {
   const int64_t t = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
   if (t >= nslabs * R4) return;
-  const int64_t slab = t / R4, c = t - slab * R4, row = 4 * R4;  // row length in elements
+  int64_t slab, c;
+  slab_of(t, nslabs * R4, R4, slab, c);
+  const int64_t row = 4 * R4;  // row length in elements
   const T* base = x + slab * 32 * row + 4 * c;
   Raw4<T> r[32];
 #pragma unroll
@@ -232,7 +248,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_kivi_k_dequant(const uint8_t*
                                                                   void* __restrict__ out) {
   const int64_t t = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
   if (t >= nslabs * R4) return;
-  const int64_t slab = t / R4, c = t - slab * R4, row = 4 * R4;
+  int64_t slab, c;
+  slab_of(t, nslabs * R4, R4, slab, c);
+  const int64_t row = 4 * R4;
   const int64_t g0 = slab * row + 4 * c;
   const uint4 sv = *reinterpret_cast<const uint4*>(scales + g0);
   const uint4 mv = *reinterpret_cast<const uint4*>(mins + g0);
