@@ -203,10 +203,30 @@ __global__ __launch_bounds__(kBlockThreads) void k_dq_int4(const uint8_t* __rest
       const float s = as_f(sb[k] << 16);
       const int z = ((int)(zb[k] >> (4 * ((u >> 4) & 1))) << 28) >> 28;  // sign-extend
       float o[8];
+      if constexpr (kBf16Out) {
+        // q - z as (q + 8) - (z + 8), a difference of small integers in
+        // float32 (exact), times s: one rounding, as the oracle, a zero
+        // difference giving +0.  q + 8 of a nibble is the nibble with its top
+        // bit flipped, converted from a byte.  (Forming (q + 8) s - (z + 8) s
+        // in one fused multiply-add instead would overflow at (z + 8) s for
+        // groups whose range is near the float32 maximum.)  On a 1 GiB
+        // tensor this form is 1.5% faster than the one below with bf16
+        // output and no faster with float32 output, where the stores set
+        // the pace, so float32 output keeps the sign-extending form.
+        const float zf = (float)(z + 8);
+        const uint32_t lo = (c[k] & 0x0F0F0F0Fu) ^ 0x08080808u;          // elements 0, 2, 4, 6
+        const uint32_t hi = ((c[k] >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;   // elements 1, 3, 5, 7
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int q = ((int)(c[k] >> (4 * i)) << 28) >> 28;
-        o[i] = (float)(q - z) * s;
+        for (int j = 0; j < 4; ++j) {
+          o[2 * j] = ((float)((lo >> (8 * j)) & 0xFFu) - zf) * s;
+          o[2 * j + 1] = ((float)((hi >> (8 * j)) & 0xFFu) - zf) * s;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int q = ((int)(c[k] >> (4 * i)) << 28) >> 28;
+          o[i] = (float)(q - z) * s;
+        }
       }
       store_out8<kBf16Out>(out, u, o);
     }

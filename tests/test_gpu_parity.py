@@ -294,6 +294,35 @@ def test_mx_exponent_boundaries(pqb):
     same(q.scales, os_, "mx boundary scales")
 
 
+def test_int4_dequant_extreme_ranges(pqb):
+    """Groups whose range is the input type's largest finite value, with the
+    zero-point at both ends of its range (7 when the group is all negative,
+    -8 when all positive).  In float32, (z + 8) s alone would overflow while
+    (q - z) s is finite for every code but the one at -max, whose value
+    overflows in the oracle too."""
+    for dtype in (torch.float32, torch.bfloat16):
+        fmax = torch.finfo(dtype).max   # FLT_MAX itself rounds to inf in bf16
+        ramp = torch.linspace(0, 1, 128).repeat(2)
+        g = torch.zeros((6, 256))
+        g[0] = -ramp * fmax                                   # lo = -max, hi = 0: z = 7
+        g[1] = ramp * fmax                                    # lo = 0, hi = max: z = -8
+        g[2, :128] = -fmax * 0.97
+        g[2, 128:] = fmax * 0.45                              # one extreme group, one constant
+        g[3] = torch.linspace(-1, 1, 256) * fmax * 0.49       # range just under the maximum
+        g[4] = -torch.linspace(0, 1, 256) * 1e30
+        g[5] = torch.linspace(-3, 5, 256)
+        x = g.to(dtype)
+        assert torch.isfinite(x).all()
+        q = pqb.quantize(x.to(DEV), "int4_asym")
+        oc, os_, oz = oracle.int4_quantize(x)
+        same(q.codes, oc, f"extreme int4 codes {dtype}")
+        same(q.scales, os_, f"extreme int4 scales {dtype}")
+        same(q.aux, oz, f"extreme int4 zeros {dtype}")
+        same(pqb.dequantize(q), oracle.int4_dequantize(oc, os_, oz), f"extreme int4 deq {dtype}")
+        same(pqb.dequantize(q, torch.bfloat16), oracle.int4_dequantize(oc, os_, oz, True),
+             f"extreme int4 deq bf16 {dtype}")
+
+
 def test_int4_exact_ties(pqb):
     """Groups whose elements sit exactly on half-steps of the stored scale."""
     g = torch.zeros((4, 128))
