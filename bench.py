@@ -1,20 +1,24 @@
 """Throughput of the quantize-pack path on one MI355X.
 
-Headline workload: the FP8 E4M3 W8A8 set, one step =
-  quantize a bf16 weight [7168, 2048] with 128x128 block scales
-  + quantize bf16 activations [8192, 7168] with 1x128 block scales,
-issued as one pqb_quantize_batch call (a single fused launch).
-value = (bytes read + bytes written) per step / time, in GB/s; inputs sit in HBM
-before timing starts, and several buffer sets rotate so the 256 MB Infinity
-Cache cannot serve repeated reads.
+Headline workload: INT4 group-128 asymmetric conversion of a whole
+Llama-3.1-8B-shaped decoder, 32 layers x {q [4096x4096], k and v [1024x4096],
+o [4096x4096], gate and up [14336x4096], down [4096x14336]} bf16 weights
+(6,979,321,856 weights, 13.96 GB in, 3.63 GB of codes, bf16 scales and
+zero-point nibbles out).  One step = one pqb_quantize_batch call over all 224
+weights.  value = (bytes read + bytes written) per step / time, in GB/s; the
+inputs sit in HBM before timing starts, and one step touches 17.6 GB, far more
+than the 256 MB Infinity Cache, so nothing is served from it.
 
-Also reported (under "formats"): MXFP4 / NVFP4 on the float32 [3072, 1024] MLP
-weight and on the bf16 [28672, 8192] heavy-tailed weight, INT4 group-128 over
-all 224 Llama-3.1-8B-shaped decoder weights, the FP8 KV write of
-[28 x 32768 x 8 x 128] K and V, and every format on a 1 GiB bf16 tensor.
+The last stdout line is the headline record (one compact JSON object).  Every
+other workload gets one `record <name> <json>` line on stderr (and, with
+--records FILE, a JSON file holding all of them): the FP8 W8A8 step, MXFP4 /
+NVFP4 on the float32 [3072, 1024] MLP weight and on the bf16 [28672, 8192]
+heavy-tailed weight, the FP8 KV write of [28 x 32768 x 8 x 128] K and V,
+every format on a 1 GiB bf16 tensor, the GEMMs and W4A16.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras]
-       [--no-cpu] [--copy-probe] [--reps R] [--only NAME]
+       [--no-cpu] [--copy-probe] [--reps R] [--only NAME] [--records FILE]
+       [--headline-only]
 """
 import argparse
 import ctypes
@@ -32,10 +36,19 @@ HBM_PEAK_GBS = 8000.0
 FP8_MFMA_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 matrix peak (no sparsity)
 FP4_MFMA_PEAK_TFLOPS = 10100.0      # MI355X dense FP4 / FP6 matrix peak
 METRIC = "quantize-pack GB/s (bytes in+out) and % of HBM peak, per format"
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "k_multi_fp8_w8a8_7168x2048_8192x7168_counters.json")
+HEADLINE_KERNEL = "k_multi<INT4> (fused INT4 g128 batch kernel)"
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "k_multi_int4_llama8b_224w_counters.json")
 KERNEL_SOURCES = ["precision_quantization_block_amd/csrc/k_multi.hip",
                   "precision_quantization_block_amd/csrc/quant.h",
                   "precision_quantization_block_amd/csrc/device.h"]
+_RECORDS = {}
+
+
+def record(name, rec_):
+    """One non-headline result: a stderr line now, the --records file at the end."""
+    _RECORDS[name] = rec_
+    print(f"record {name} {json.dumps(rec_, separators=(',', ':'))}", file=sys.stderr,
+          flush=True)
 
 
 def log(*a):
@@ -170,10 +183,99 @@ def rec(bytes_moved, times, two_pass_read=0, **kw):
 
 
 # ----------------------------------------------------------------------------
-# headline: FP8 W8A8 set
+# headline: INT4 g128 over the 224 Llama-3.1-8B-shaped decoder weights
 # ----------------------------------------------------------------------------
 
-def bench_main(torch, eng, synth, steps, warmup, nsets):
+def llama_int4_set(torch, eng, synth, dev):
+    """The 224 bf16 weights (seed 3000 + 7 layer + proj) and their INT4 outputs."""
+    from precision_quantization_block_amd.synth import LLAMA_LAYERS, LLAMA_PROJ
+    xs, bufs, shapes = [], [], []
+    nb = 0
+    for layer in range(LLAMA_LAYERS):
+        for p, (_, r, c) in enumerate(LLAMA_PROJ):
+            x = synth.llama_weight(layer, p, device=dev)
+            b = eng.alloc("int4_asym", "grp128", (1, r, c), dev)
+            xs.append(x)
+            bufs.append(b)
+            shapes.append((1, r, c))
+            nb += x.numel() * 2 + out_bytes(b["sizes"])
+    return xs, bufs, shapes, nb
+
+
+def bench_headline(torch, eng, synth, steps, warmup):
+    dev = torch.device("cuda:0")
+    xs, bufs, shapes, step_bytes = llama_int4_set(torch, eng, synth, dev)
+    jobs = eng.jobs([(x, "int4_asym", "grp128", shp, b) for x, shp, b in zip(xs, shapes, bufs)])
+    launches = eng.L.pqb_quantize_batch_launches(jobs[0], jobs[1])
+
+    def step(i):
+        eng.batch(jobs)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # timed region: K steps back to back on the stream the kernels are launched
+    # on (the current stream, which eng.stream is), events only at the ends.
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    wall0 = time.perf_counter()
+    ev[0].record()
+    for k in range(steps):
+        step(k)
+    ev[1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = ev[0].elapsed_time(ev[1])
+    log(f"headline: {steps} steps of INT4 g128 over 224 weights, {ms_total / steps:.4f} ms per "
+        f"step, {launches} launches per step (wall {wall * 1e3:.1f} ms)")
+    return {"ms_per_step": ms_total / steps, "step_bytes": step_bytes, "launches": launches,
+            "wall_s": wall, "xs": xs, "bufs": bufs, "shapes": shapes}
+
+
+def int4_records_extra(torch, eng, h, reps=5):
+    """The same 224 weights quantized with one pqb_quantize call each, and
+    dequantized back to bf16, one call each and as one batch call."""
+    dev = torch.device("cuda:0")
+    xs, bufs, shapes = h["xs"], h["bufs"], h["shapes"]
+
+    def one_by_one(i):
+        for x, shp, b in zip(xs, shapes, bufs):
+            eng.quantize(x, "int4_asym", "grp128", shp, b)
+
+    t = time_reps(torch, one_by_one, reps, 1)
+    record("llama8b_224w_bf16_int4_g128_per_tensor",
+           rec(h["step_bytes"], t, op="INT4 g128 asym, 224 weights, one pqb_quantize call each",
+               launches=224))
+    # leave the batch call's outputs in place for the parity check
+    eng.batch(eng.jobs([(x, "int4_asym", "grp128", shp, b)
+                        for x, shp, b in zip(xs, shapes, bufs)]))
+    outs = [torch.empty(shp, dtype=torch.bfloat16, device=dev) for shp in shapes]
+    nbd = sum(out_bytes(b["sizes"]) + o.numel() * 2 for b, o in zip(bufs, outs))
+
+    def dq_all(i):
+        for shp, b, o in zip(shapes, bufs, outs):
+            eng.dequantize(b, "int4_asym", "grp128", shp, o)
+
+    t = time_reps(torch, dq_all, reps, 1)
+    record("llama8b_224w_bf16_int4_g128_dequant",
+           rec(nbd, t, op="dequantize INT4 -> bf16, 224 weights, one call each", launches=224))
+    if hasattr(eng.L, "pqb_dequantize_batch"):
+        djobs = eng.dq_jobs([(b, "int4_asym", "grp128", shp, o)
+                             for shp, b, o in zip(shapes, bufs, outs)])
+        t = time_reps(torch, lambda i: eng.dequantize_batch(djobs), reps, 1)
+        record("llama8b_224w_bf16_int4_g128_dequant_batch",
+               rec(nbd, t, op="dequantize INT4 -> bf16, 224 weights, one batch call"))
+    del outs
+    torch.cuda.synchronize()
+
+
+# ----------------------------------------------------------------------------
+# secondary: the FP8 E4M3 W8A8 step (weight 128x128 + activations 1x128)
+# ----------------------------------------------------------------------------
+
+def bench_w8a8(torch, eng, synth, steps, warmup, nsets):
+    """bf16 weight [7168, 2048] with 128x128 block scales plus bf16 activations
+    [8192, 7168] with 1x128 block scales, one pqb_quantize_batch call (one fused
+    launch) per step, rotated over `nsets` buffer sets (> 1 GiB in all)."""
     dev = torch.device("cuda:0")
     wshape, ashape = (1, 7168, 2048), (1, 8192, 7168)
     sets = []
@@ -196,37 +298,16 @@ def bench_main(torch, eng, synth, steps, warmup, nsets):
         eng.quantize(a, "fp8_e4m3", "1x128", ashape, ab)
         eng.quantize(w, "fp8_e4m3", "128x128", wshape, wb)
 
-    def act_only(i):
-        _, a, _, ab = sets[i % nsets]
-        eng.quantize(a, "fp8_e4m3", "1x128", ashape, ab)
-
-    for i in range(warmup):
-        step(i)
-        two_launches(i)
-    torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    # timed region: K steps back to back, events only at the ends.  A step is
-    # one launch, so this is also the fused kernel's average launch duration.
-    wall0 = time.perf_counter()
-    ev[0].record()
-    for k in range(steps):
-        step(k)
-    ev[1].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_total = ev[0].elapsed_time(ev[1])
-    # for comparison: the same step as two single-tensor launches, and the
-    # activation kernel alone
-    ms_two = time_loop(torch, two_launches, steps, 0)
-    a_avg = time_loop(torch, act_only, steps, 0)
-    log(f"main: {steps} fused steps {ms_total:.3f} ms (wall {wall * 1e3:.3f} ms); "
-        f"two launches {ms_two * 1e3:.1f} us/step; activation kernel {a_avg * 1e3:.1f} us")
-    # leave set 0's outputs from the fused kernel in place for the parity check
-    step(0)
-    torch.cuda.synchronize()
-    return {"ms_per_step": ms_total / steps, "step_bytes": step_bytes, "act_bytes": a_bytes,
-            "w_bytes": w_bytes, "ms_two_launches": ms_two, "act_kernel_ms_avg": a_avg,
-            "wall_s": wall, "set0": sets[0]}
+    t = time_reps(torch, step, steps, warmup)
+    ms_two = time_loop(torch, two_launches, steps, warmup)
+    r = rec(step_bytes, t, op="FP8 E4M3 W8A8 step: weight [7168x2048] 128x128 + "
+            "activations [8192x7168] 1x128, one fused launch", rotated_sets=nsets)
+    r["two_launch_ms"] = round(ms_two, 5)
+    r["two_launch_gbs"] = round(step_bytes / (ms_two * 1e-3) / 1e9, 1)
+    record("w8a8_fp8_7168x2048_128x128_8192x7168_1x128", r)
+    del sets, jobs
+    torch.cuda.empty_cache()
+    return r
 
 
 # ----------------------------------------------------------------------------
@@ -310,8 +391,6 @@ def bench_extras(torch, eng, synth, reps, only=None):
     if want("llama8b_224w_int4_g128_w4a16_decode_m1_one_batch",
             "llama8b_224w_int4_g128_w4a16_mfma_m16_one_batch"):
         out.update(bench_w4a16(torch, eng, synth, reps))
-    if want("llama8b_224w_bf16_int4_g128"):
-        out.update(bench_llama_int4(torch, eng, synth))
     return out
 
 
@@ -555,118 +634,73 @@ def bench_w4a16(torch, eng, synth, reps):
     return out
 
 
-def bench_llama_int4(torch, eng, synth):
-    """INT4 g128 over the 224 Llama-3.1-8B-shaped decoder weights."""
-    dev = torch.device("cuda:0")
-    out = {}
-    ws_ = []
-    bufs = []
-    from precision_quantization_block_amd.synth import LLAMA_LAYERS, LLAMA_PROJ
-    nb = 0
-    for layer in range(LLAMA_LAYERS):
-        for p, (_, r, c) in enumerate(LLAMA_PROJ):
-            x = synth.llama_weight(layer, p, device=dev)
-            b = eng.alloc("int4_asym", "grp128", (1, r, c), dev)
-            ws_.append((x, (1, r, c)))
-            bufs.append(b)
-            nb += x.numel() * 2 + out_bytes(b["sizes"])
-
-    jobs = eng.jobs([(x, "int4_asym", "grp128", shp, b) for (x, shp), b in zip(ws_, bufs)])
-
-    def all_int4(i):
-        eng.batch(jobs)
-
-    def one_by_one(i):
-        for (x, shp), b in zip(ws_, bufs):
-            eng.quantize(x, "int4_asym", "grp128", shp, b)
-
-    t = time_reps(torch, all_int4, 5, 1)
-    out["llama8b_224w_bf16_int4_g128"] = rec(nb, t, op="INT4 g128 asym, 224 tensors, one "
-                                             "pqb_quantize_batch call", launches=-(-224 // 24))
-    t = time_reps(torch, one_by_one, 5, 1)
-    out["llama8b_224w_bf16_int4_g128_per_tensor"] = rec(nb, t, op="same, one pqb_quantize "
-                                                        "call per tensor", launches=224)
-    log(f"int4 llama: {out['llama8b_224w_bf16_int4_g128']['gbs']} GB/s batched, "
-        f"{out['llama8b_224w_bf16_int4_g128_per_tensor']['gbs']} GB/s per tensor")
-    # dequantize all 224 back to bf16 (one call per tensor)
-    outs = [torch.empty(shp, dtype=torch.bfloat16, device=dev) for _, shp in ws_]
-    nbd = sum(out_bytes(b["sizes"]) + o.numel() * 2 for b, o in zip(bufs, outs))
-
-    def dq_all(i):
-        for (_, shp), b, o in zip(ws_, bufs, outs):
-            eng.dequantize(b, "int4_asym", "grp128", shp, o)
-
-    t = time_reps(torch, dq_all, 5, 1)
-    out["llama8b_224w_bf16_int4_g128_dequant"] = rec(nbd, t, op="dequantize INT4 -> bf16, "
-                                                     "224 tensors", launches=224)
-    log(f"int4 llama dequant: {out['llama8b_224w_bf16_int4_g128_dequant']['gbs']} GB/s")
-    del ws_, bufs, outs
-    torch.cuda.empty_cache()
-    return out
-
-
 # ----------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample of the headline workload
 # ----------------------------------------------------------------------------
 
-def cpu_baseline(torch, a_host, w_host, act_rows=2304, w_rows=256, threads=None):
-    """The oracle on the host cores, on the same inputs as the GPU's set 0:
-    single-threaded on the first rows of the step's tensors, then one thread per
-    core over row chunks of the whole step (ctypes releases the GIL inside the
-    C oracle).  Returns the record and the oracle's outputs for the whole step."""
+def cpu_baseline_int4(torch, h, st_layers=1, mt_layers=8, threads=None, chunk_rows=512):
+    """The INT4 oracle on the host cores, on host copies of the headline's own
+    inputs: single-threaded over the first `st_layers` layers' weights, then
+    one thread per core over row chunks of the first `mt_layers` layers
+    (ctypes releases the GIL inside the C oracle).  Returns the record and the
+    oracle's outputs (codes, scales, zero-points per weight) of the threaded leg."""
     import numpy as np
     import oracle
     from concurrent.futures import ThreadPoolExecutor
+    from precision_quantization_block_amd.synth import LLAMA_PROJ
     threads = threads or min(16, os.cpu_count() or 1)
     oracle.lib()
+    P = len(LLAMA_PROJ)
+    xs = [x.cpu() for x in h["xs"][: P * mt_layers]]
 
-    def step_bytes(a_rows, w_rows_):
-        return a_rows * 7168 * 3 + a_rows * 56 * 4 + w_rows_ * 2048 * 3 + (w_rows_ // 128) * 16 * 4
+    def nbytes(x):
+        n = x.numel()
+        return 2 * n + n // 2 + 2 * (n // 128) + n // 256
 
     t0 = time.perf_counter()
-    oracle.fp8_quantize(a_host[:act_rows].contiguous(), "1x128")
-    oracle.fp8_quantize(w_host[:w_rows].contiguous(), "128x128")
+    for x in xs[: P * st_layers]:
+        oracle.int4_quantize(x)
     dt1 = time.perf_counter() - t0
-    nb1 = step_bytes(act_rows, w_rows)
-    # whole step, row chunks (multiples of 128 rows for the 128x128 weight)
-    jobs = [(w_host[i:i + 256], "128x128") for i in range(0, 7168, 256)] + \
-           [(a_host[i:i + 256], "1x128") for i in range(0, 8192, 256)]
+    nb1 = sum(nbytes(x) for x in xs[: P * st_layers])
+    # row chunks; every chunk holds an even number of groups (32 or 112 per row),
+    # so its zero-point nibbles start on a byte and the pieces concatenate
+    jobs = [(i, x[r:r + chunk_rows]) for i, x in enumerate(xs)
+            for r in range(0, x.shape[0], chunk_rows)]
     with ThreadPoolExecutor(threads) as ex:
         t0 = time.perf_counter()
-        res = list(ex.map(lambda j: oracle.fp8_quantize(j[0].contiguous(), j[1]), jobs))
+        res = list(ex.map(lambda j: oracle.int4_quantize(j[1].contiguous()), jobs))
         dtn = time.perf_counter() - t0
-    nw = 7168 // 256
-    outs = {"w_codes": np.concatenate([r[0].reshape(-1) for r in res[:nw]]),
-            "w_scales": np.concatenate([r[1].reshape(-1) for r in res[:nw]]),
-            "a_codes": np.concatenate([r[0].reshape(-1) for r in res[nw:]]),
-            "a_scales": np.concatenate([r[1].reshape(-1) for r in res[nw:]])}
-    nbn = step_bytes(8192, 7168)
-    return {"value": round(nbn / dtn / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"the whole W8A8 step (activations [8192x7168] 1x128 + weight [7168x2048] "
-                      f"128x128), {threads} threads over 256-row chunks: {dtn:.2f} s wall for "
-                      f"{nbn / 1e6:.1f} MB",
-            "single_thread": {"value": round(nb1 / dt1 / 1e9, 4), "cores": 1,
-                              "sample": f"first {act_rows} activation rows and first {w_rows} "
-                                        f"weight rows: {dt1:.1f} s for {nb1 / 1e6:.1f} MB"},
-            "host_cpu": _cpu_model(), "host_cores_available": os.cpu_count()}, outs
+    outs = [([], [], []) for _ in xs]
+    for (i, _), (c, s, z) in zip(jobs, res):
+        outs[i][0].append(c.reshape(-1))
+        outs[i][1].append(s.reshape(-1))
+        outs[i][2].append(z.reshape(-1))
+    outs = [tuple(np.concatenate(p) for p in o) for o in outs]
+    nbn = sum(nbytes(x) for x in xs)
+    r = {"value": round(nbn / dtn / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+         "sample": f"INT4 g128 of the first {mt_layers} of 32 layers (56 of 224 weights, "
+                   f"{nbn / 1e9:.2f} GB in+out), {threads} threads over {chunk_rows}-row "
+                   f"chunks: {dtn:.2f} s",
+         "single_thread": {"value": round(nb1 / dt1 / 1e9, 4), "cores": 1,
+                           "sample": f"layer 0's 7 weights: {dt1:.2f} s for {nb1 / 1e6:.0f} MB"},
+         "host_cpu": _cpu_model(), "host_cores_available": os.cpu_count()}
+    return r, outs
 
 
-def parity_of_step(torch, set0, outs):
-    """Byte-compare the GPU's codes and scales for one W8A8 step with the oracle's."""
+def parity_int4(torch, h, outs):
+    """Byte-compare the GPU's INT4 codes, bf16 scales and zero-point nibbles with
+    the oracle's for the weights the threaded CPU leg quantized."""
     import numpy as np
-    _, _, wb, ab = set0
     mism, total = 0, 0
-    for key, buf, name in (("w_codes", wb, "codes"), ("w_scales", wb, "scales"),
-                           ("a_codes", ab, "codes"), ("a_scales", ab, "scales")):
-        ref = outs[key].view(np.uint8)
-        got = buf[name][: buf["sizes"][name]].cpu().numpy()
-        if got.shape != ref.shape:
-            mism += max(got.size, ref.size)
-        else:
-            mism += int(np.count_nonzero(got != ref))
-        total += ref.size
-    return {"checked": "every code and scale byte of one fused W8A8 step (buffer set 0) "
-                       "against the oracle on the same inputs",
+    for b, (c, s, z) in zip(h["bufs"], outs):
+        for name, ref in (("codes", c), ("scales", s), ("aux", z)):
+            ref = ref.view(np.uint8).reshape(-1)
+            got = b[name][: b["sizes"][name]].cpu().numpy()
+            mism += int(np.count_nonzero(got != ref)) if got.shape == ref.shape \
+                else max(got.size, ref.size)
+            total += ref.size
+    return {"checked": f"every code, scale and zero-point byte of the first {len(outs)} weights "
+                       f"of the last batch call against the oracle on the same inputs",
             "bytes_compared": total, "mismatches": mism}
 
 
@@ -719,13 +753,17 @@ def copy_probe(torch, reps=3):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--sets", type=int, default=6, help="rotated buffer sets (> 1 GiB total)")
+    ap.add_argument("--sets", type=int, default=6,
+                    help="rotated buffer sets of the W8A8 step (> 1 GiB in all)")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time the headline only (no CPU baseline, no other workloads)")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--reps", type=int, default=20)
+    ap.add_argument("--records", default=None, help="write every record to this JSON file")
     ap.add_argument("--only", default=None,
                     help="run only the format workloads whose name contains this string "
                          "(no headline line; prints the records as JSON)")
@@ -751,9 +789,13 @@ def main():
         print(json.dumps(bench_extras(torch, eng, synth, args.reps, args.only)), flush=True)
         return
 
-    m = bench_main(torch, eng, synth, args.steps, args.warmup, args.sets)
-    value = m["step_bytes"] / (m["ms_per_step"] * 1e-3) / 1e9
-    achieved = value   # one fused launch per step
+    h = bench_headline(torch, eng, synth, args.steps, args.warmup)
+    value = h["step_bytes"] / (h["ms_per_step"] * 1e-3) / 1e9
+    # k_multi<INT4> is the only kernel of a step: its average launch duration
+    # is the step time over the launches, and its bytes per launch the step's
+    # bytes over the launches, so achieved = step bytes / step time
+    avg_launch_ms = h["ms_per_step"] / h["launches"]
+    achieved = (h["step_bytes"] / h["launches"]) / (avg_launch_ms * 1e-3) / 1e9
     traffic = None
     try:
         with open(COUNTERS_FILE) as f:
@@ -764,36 +806,44 @@ def main():
         pass
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(m["ms_per_step"], 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16->e4m3",
-        "data": "synthetic (seeded; see precision_quantization_block_amd/synth.py)",
-        "config": {"workload": "FP8 E4M3 W8A8 set: bf16 weight [7168x2048] 128x128 blocks + "
-                               "bf16 activations [8192x7168] 1x128 blocks",
-                   "step_bytes": m["step_bytes"], "rotated_buffer_sets": args.sets,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(h["ms_per_step"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16->int4 g128 (fp32 arithmetic)",
+        "data": "synthetic (seeded; precision_quantization_block_amd/synth.py)",
+        "config": {"workload": "INT4 g128 asymmetric, 224 Llama-3.1-8B-shaped bf16 weights "
+                               "(32 layers x q,k,v,o,gate,up,down), one pqb_quantize_batch call",
+                   "weights": sum(x.numel() for x in h["xs"]), "step_bytes": h["step_bytes"],
+                   "launches_per_step": h["launches"],
                    "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
-        "roofline": {"bound": "hbm", "kernel": "k_multi (fused W 128x128 + A 1x128 launch)",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "roofline": {"bound": "hbm", "kernel": HEADLINE_KERNEL, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": m["step_bytes"],
-                     "avg_launch_ms": round(m["ms_per_step"], 5)},
-        "unfused": {"two_launch_step_ms": round(m["ms_two_launches"], 5),
-                    "two_launch_gbs": round(m["step_bytes"] / (m["ms_two_launches"] * 1e-3) / 1e9,
-                                            1),
-                    "act_kernel_k_fp8_1x128_ms": round(m["act_kernel_ms_avg"], 5),
-                    "act_kernel_gbs": round(m["act_bytes"] / (m["act_kernel_ms_avg"] * 1e-3) / 1e9,
-                                            1)},
+                     "algorithmic_bytes_per_launch": h["step_bytes"] // h["launches"],
+                     "avg_launch_ms": round(avg_launch_ms, 5)},
+        "cpu_baseline": None, "parity": None,
     }
-    if not args.no_extras:
-        line["formats"] = bench_extras(torch, eng, synth, args.reps)
-        line["hbm_reference"] = hbm_reference(torch)
-    line["parity"] = None
-    if not args.no_cpu:
-        w0, a0 = m["set0"][0], m["set0"][1]
-        line["cpu_baseline"], outs = cpu_baseline(torch, a0.cpu(), w0.cpu())
-        line["parity"] = parity_of_step(torch, m["set0"], outs)
-    else:
-        line["cpu_baseline"] = None
-    print(json.dumps(line), flush=True)
+    if not args.headline_only:
+        int4_records_extra(torch, eng, h)
+        if not args.no_cpu:
+            line["cpu_baseline"], outs = cpu_baseline_int4(torch, h)
+            line["parity"] = parity_int4(torch, h, outs)
+            del outs
+        del h
+        torch.cuda.empty_cache()
+        w8 = bench_w8a8(torch, eng, synth, args.steps, args.warmup, args.sets)
+        sec = {"w8a8_fp8_step_gbs": w8["gbs"], "w8a8_fp8_step_frac": w8["frac_hbm_peak"]}
+        if "llama8b_224w_bf16_int4_g128_dequant_batch" in _RECORDS:
+            sec["int4_224w_dequant_batch_gbs"] = \
+                _RECORDS["llama8b_224w_bf16_int4_g128_dequant_batch"]["gbs"]
+        if not args.no_extras:
+            for k, v in bench_extras(torch, eng, synth, args.reps).items():
+                record(k, v)
+            record("hbm_reference", hbm_reference(torch))
+        line["secondary"] = sec
+    if args.records:
+        with open(args.records, "w") as f:
+            json.dump({"headline": line, "records": _RECORDS}, f, indent=1)
+    print(json.dumps(line, separators=(",", ":")), flush=True)
     if line["parity"] is not None and line["parity"]["mismatches"]:
         log(f"PARITY FAILURE: {line['parity']['mismatches']} bytes differ from the oracle")
         sys.exit(3)

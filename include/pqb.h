@@ -62,7 +62,8 @@
  *
  * Shape rules: 1x128 and GRP_128 need c % 128 == 0; 128x128 needs c % 128 == 0
  * and r <= 128 or r % 128 == 0; BLK_32 needs c % 32 == 0; BLK_16 needs
- * c % 16 == 0.  An empty tensor (b*r*c == 0) is accepted and launches nothing.
+ * c % 16 == 0; ROW needs b * r <= 4 * (2^32 - 1) / 256 (one wave per row).
+ * An empty tensor (b*r*c == 0) is accepted and launches nothing.
  *
  * Alignment: x, codes and out must be 16-byte aligned; scales and aux 4-byte
  * aligned (2-byte for INT4 scales, 1 for byte scales and zero-points);
@@ -149,15 +150,21 @@ typedef struct pqb_job {
 } pqb_job;
 
 /* Quantize several tensors with as few launches as possible: jobs of one
- * family share fused launches of up to 24 jobs (FP8 E4M3/E5M2 1x128 and
- * 128x128 together; MXFP4 with MXFP8; INT4), per-row jobs (FP8, INT8) get a
- * launch each.  Each job's outputs are exactly those of pqb_quantize on the
- * same arguments.  Only the one-pass pairs qualify; a per-tensor job (FP8,
- * INT8) or an NVFP4 job returns PQB_ERR_COMBO.  Every job is validated (same rules and codes as
- * pqb_quantize) before anything is enqueued.  Outputs of different jobs must
- * not overlap each other or any input.  `jobs` is a host array and may be
- * reused once the call returns. */
+ * family share fused launches of up to 72 jobs each (FP8 E4M3/E5M2 1x128 and
+ * 128x128 together; MXFP4 with MXFP8; INT4), a family's jobs split as evenly
+ * as possible over its launches; per-row jobs (FP8, INT8) get a launch each.
+ * Each job's outputs are exactly those of pqb_quantize on the same arguments.
+ * Only the one-pass pairs qualify; a per-tensor job (FP8, INT8) or an NVFP4
+ * job returns PQB_ERR_COMBO.  Every job is validated (same rules and codes as
+ * pqb_quantize) and every launch is planned before anything is enqueued; a
+ * launch that would exceed the grid limit of 2^32 - 1 threads returns
+ * PQB_ERR_SHAPE.  Outputs of different jobs must not overlap each other or any
+ * input.  `jobs` is a host array and may be reused once the call returns. */
 pqb_status pqb_quantize_batch(const pqb_job* jobs, int64_t njobs, void* stream);
+
+/* The number of kernel launches pqb_quantize_batch makes for these jobs
+ * (after the same validation; no GPU work), or a negative pqb_status. */
+int64_t pqb_quantize_batch_launches(const pqb_job* jobs, int64_t njobs);
 
 /* Inverse of pqb_quantize: out[b, r, c] = decoded code times its scale(s),
  * as float32 or rounded to bf16 (round-to-nearest-even) by `out_dtype`.

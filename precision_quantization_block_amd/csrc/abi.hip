@@ -57,6 +57,9 @@ pqb_status check_shape(int fmt, int gran, int64_t b, int64_t r, int64_t c) {
       if (b > kMaxGridY) return PQB_ERR_SHAPE;
       break;
     case PQB_ROW:
+      // one wave per row, 4 rows per 256-thread workgroup: the grid must stay
+      // within 2^32 - 1 threads
+      if (c > 0 && (b * r + 3) / 4 > (int64_t)(0xFFFFFFFFu / 256u)) return PQB_ERR_SHAPE;
       break;
     case PQB_BLK_1x128:
     case PQB_GRP_128:
@@ -237,7 +240,13 @@ pqb_status pqb_quantize(const void* x, pqb_dtype dtype, int64_t batch, int64_t r
   return PQB_ERR_ENUM;
 }
 
-pqb_status pqb_quantize_batch(const pqb_job* jobs, int64_t njobs, void* stream) {
+// Validates a batch and sorts its jobs: one-pass jobs for the fused launches
+// into `fused`, per-row one-byte jobs into `rows`; `launches` receives the
+// number of kernel launches the batch takes.  Every check happens here, before
+// anything is enqueued.
+static pqb_status prepare_batch(const pqb_job* jobs, int64_t njobs, std::vector<MultiJob>& fused,
+                                std::vector<int64_t>& rows, int64_t* launches) {
+  *launches = 0;
   if (njobs < 0) return PQB_ERR_SHAPE;
   if (njobs == 0) return PQB_OK;
   if (!jobs) return PQB_ERR_NULL;
@@ -251,15 +260,16 @@ pqb_status pqb_quantize_batch(const pqb_job* jobs, int64_t njobs, void* stream) 
     if (st != PQB_OK) return st;
     if (need.workspace) return PQB_ERR_COMBO;
   }
-  hipStream_t s = (hipStream_t)stream;
-  std::vector<MultiJob> fused;
   fused.reserve((size_t)njobs);
   for (int64_t i = 0; i < njobs; ++i) {
     const pqb_job& j = jobs[i];
     if (j.batch * j.rows * j.cols == 0) continue;
+    if (one_byte(j.fmt) && j.gran == PQB_ROW) {  // a launch of its own
+      rows.push_back(i);
+      continue;
+    }
     MultiJob m{j.x, (uint8_t*)j.codes, j.scales, (uint8_t*)j.aux, j.batch, j.rows, j.cols, 0,
                j.dtype == PQB_BF16, elem_of(j.fmt)};
-    if (one_byte(j.fmt) && j.gran == PQB_ROW) continue;  // launched below
     if (one_byte(j.fmt))  // E4M3 or E5M2 (INT8 has only ROW here)
       m.kind = j.gran == PQB_BLK_1x128 ? kMultiFp8Blk : kMultiFp8Tile;
     else if (j.fmt == PQB_MXFP4)
@@ -270,13 +280,33 @@ pqb_status pqb_quantize_batch(const pqb_job* jobs, int64_t njobs, void* stream) 
       m.kind = kMultiInt4;
     fused.push_back(m);
   }
+  const int64_t nl = fused.empty() ? 0 : multi_launches(fused.data(), (int)fused.size());
+  if (nl < 0) return PQB_ERR_SHAPE;
+  *launches = nl + (int64_t)rows.size();
+  return PQB_OK;
+}
+
+int64_t pqb_quantize_batch_launches(const pqb_job* jobs, int64_t njobs) {
+  std::vector<MultiJob> fused;
+  std::vector<int64_t> rows;
+  int64_t launches;
+  const pqb_status st = prepare_batch(jobs, njobs, fused, rows, &launches);
+  return st == PQB_OK ? launches : (int64_t)st;
+}
+
+pqb_status pqb_quantize_batch(const pqb_job* jobs, int64_t njobs, void* stream) {
+  std::vector<MultiJob> fused;
+  std::vector<int64_t> rows;
+  int64_t launches;
+  const pqb_status st = prepare_batch(jobs, njobs, fused, rows, &launches);
+  if (st != PQB_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
   if (!fused.empty()) {
     const hipError_t e = launch_multi(fused.data(), (int)fused.size(), s);
     if (e != hipSuccess) return PQB_ERR_HIP;
   }
-  for (int64_t i = 0; i < njobs; ++i) {
+  for (const int64_t i : rows) {
     const pqb_job& j = jobs[i];
-    if (!one_byte(j.fmt) || j.gran != PQB_ROW || j.batch * j.rows * j.cols == 0) continue;
     const hipError_t e = launch_fp8_row(j.x, j.dtype == PQB_BF16, j.batch * j.rows, j.cols,
                                         (uint8_t*)j.codes, (float*)j.scales, s, elem_of(j.fmt));
     if (e != hipSuccess) return PQB_ERR_HIP;

@@ -33,19 +33,21 @@ constexpr int kFp4Unr = sizeof(T) == 2 ? 8 : 4;
 template <int kFam>
 constexpr int kThreads = (kFam == kFamFp8 ? kFp8Waves : kFp4Waves) * kWave;
 
+// Kernel-side job, 48 bytes: a launch's argument block (njobs, the workgroup
+// prefix table and the jobs) stays within 4 KiB for kMaxBatchJobs jobs.
 struct Job {
   const void* x;
   uint8_t* codes;
   void* scales;
   uint8_t* aux;
-  int64_t rows;    // tiles: rows of one slice
-  int64_t cols;
-  int64_t nunits;  // flat kinds
-  int32_t kind;
-  int32_t bf16;
-  int32_t br;      // tiles: min(128, rows)
-  int32_t elem;    // FP8 kinds: kE4M3 or kE5M2
+  int64_t n;      // flat kinds: units (8 elements each); tiles: columns
+  uint32_t meta;  // kind | bf16 << 4 | elem << 5 | br << 8 (tiles: min(128, rows))
+  uint32_t pad;
 };
+__host__ __device__ constexpr uint32_t job_kind(uint32_t m) { return m & 15u; }
+__host__ __device__ constexpr bool job_bf16(uint32_t m) { return (m >> 4) & 1u; }
+__host__ __device__ constexpr int job_elem(uint32_t m) { return (int)((m >> 5) & 7u); }
+__host__ __device__ constexpr int job_br(uint32_t m) { return (int)(m >> 8); }
 
 struct MultiArgs {
   int32_t njobs;
@@ -53,6 +55,8 @@ struct MultiArgs {
   int64_t wg_begin[kMaxBatchJobs + 1];
   Job job[kMaxBatchJobs];
 };
+static_assert(sizeof(Job) == 48, "kernel-side job layout");
+static_assert(sizeof(MultiArgs) <= 4096, "kernel arguments must stay within 4 KiB");
 
 // One chunk of kUnr tiles per wave: chunk = local * kWaves + wave.
 template <int kWaves, int kUnr, typename Body>
@@ -68,13 +72,13 @@ __device__ __forceinline__ void flat_job(int64_t local, int64_t nunits, Body bod
 
 template <typename T, int kElem>
 __device__ __forceinline__ void fp8_job(const Job& jb, const T* x, int64_t local, uint32_t* red) {
-  if (jb.kind == kJobFp8Blk) {
-    flat_job<kFp8Waves, kFp8Unr>(local, jb.nunits, [&](int64_t u0, auto g) {
-      fp8_1x128_chunk<T, kFp8Unr, decltype(g)::value, kElem>(x, u0, jb.nunits, jb.codes,
+  if (job_kind(jb.meta) == kJobFp8Blk) {
+    flat_job<kFp8Waves, kFp8Unr>(local, jb.n, [&](int64_t u0, auto g) {
+      fp8_1x128_chunk<T, kFp8Unr, decltype(g)::value, kElem>(x, u0, jb.n, jb.codes,
                                                               reinterpret_cast<float*>(jb.scales));
     });
   } else {
-    fp8_tile_128x128<T, kFp8Waves, kElem>(x, jb.rows, jb.cols, jb.br, local, jb.codes,
+    fp8_tile_128x128<T, kFp8Waves, kElem>(x, 0, jb.n, job_br(jb.meta), local, jb.codes,
                                           reinterpret_cast<float*>(jb.scales), red);
   }
 }
@@ -83,25 +87,25 @@ template <int kFam, typename T>
 __device__ __forceinline__ void run_job(const Job& jb, int64_t local, uint8_t* lut, uint32_t* red) {
   const T* x = reinterpret_cast<const T*>(jb.x);
   if constexpr (kFam == kFamFp8) {
-    if (jb.elem == kE5M2)
+    if (job_elem(jb.meta) == kE5M2)
       fp8_job<T, kE5M2>(jb, x, local, red);
     else
       fp8_job<T, kE4M3>(jb, x, local, red);
   } else if constexpr (kFam == kFamMx) {
-    if (jb.kind == kJobMx8) {
-      flat_job<kFp4Waves, kFp4Unr<T>>(local, jb.nunits, [&](int64_t u0, auto g) {
-        mx8_chunk<T, kFp4Unr<T>, decltype(g)::value>(x, u0, jb.nunits, jb.codes,
+    if (job_kind(jb.meta) == kJobMx8) {
+      flat_job<kFp4Waves, kFp4Unr<T>>(local, jb.n, [&](int64_t u0, auto g) {
+        mx8_chunk<T, kFp4Unr<T>, decltype(g)::value>(x, u0, jb.n, jb.codes,
                                                       reinterpret_cast<uint8_t*>(jb.scales));
       });
     } else {
-      flat_job<kFp4Waves, kFp4Unr<T>>(local, jb.nunits, [&](int64_t u0, auto g) {
-        mx_chunk<T, kFp4Unr<T>, decltype(g)::value>(x, u0, jb.nunits, jb.codes,
+      flat_job<kFp4Waves, kFp4Unr<T>>(local, jb.n, [&](int64_t u0, auto g) {
+        mx_chunk<T, kFp4Unr<T>, decltype(g)::value>(x, u0, jb.n, jb.codes,
                                                      reinterpret_cast<uint8_t*>(jb.scales), lut);
       });
     }
   } else {
-    flat_job<kFp4Waves, kFp4Unr<T>>(local, jb.nunits, [&](int64_t u0, auto g) {
-      int4_chunk<T, kFp4Unr<T>, decltype(g)::value>(x, u0, jb.nunits, jb.codes,
+    flat_job<kFp4Waves, kFp4Unr<T>>(local, jb.n, [&](int64_t u0, auto g) {
+      int4_chunk<T, kFp4Unr<T>, decltype(g)::value>(x, u0, jb.n, jb.codes,
                                                      reinterpret_cast<uint16_t*>(jb.scales),
                                                      jb.aux);
     });
@@ -116,12 +120,20 @@ __global__ __launch_bounds__(kThreads<kFam>) void k_multi(MultiArgs a) {
     e2m1_lut_fill(lut, 0);
     __syncthreads();
   }
+  // this workgroup's job: the last j with wg_begin[j] <= wg (binary search,
+  // uniform over the workgroup)
   const int64_t wg = blockIdx.x;
-  int j = 0;
-  while (j + 1 < a.njobs && wg >= a.wg_begin[j + 1]) ++j;
-  const Job& jb = a.job[j];
-  const int64_t local = wg - a.wg_begin[j];
-  if (jb.bf16)
+  int lo = 0, hi = a.njobs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.wg_begin[mid] <= wg)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  const Job& jb = a.job[lo];
+  const int64_t local = wg - a.wg_begin[lo];
+  if (job_bf16(jb.meta))
     run_job<kFam, uint16_t>(jb, local, lut, red);
   else
     run_job<kFam, float>(jb, local, lut, red);
@@ -138,76 +150,121 @@ int64_t describe(const MultiJob& m, Job& jb) {
   jb.codes = m.codes;
   jb.scales = m.scales;
   jb.aux = m.aux;
-  jb.bf16 = m.bf16;
-  jb.elem = m.elem;
-  jb.cols = m.cols;
-  jb.nunits = m.batch * m.rows * m.cols / 8;
+  const int64_t nunits = m.batch * m.rows * m.cols / 8;
+  jb.n = nunits;
+  uint32_t kind;
   auto flat_wgs = [&](int waves, int unr) {
-    const int64_t nchunks = (jb.nunits + (int64_t)unr * kWave - 1) / ((int64_t)unr * kWave);
+    const int64_t nchunks = (nunits + (int64_t)unr * kWave - 1) / ((int64_t)unr * kWave);
     return (nchunks + waves - 1) / waves;
   };
   const int fp4_unr = m.bf16 ? kFp4Unr<uint16_t> : kFp4Unr<float>;
+  int64_t wgs;
+  uint32_t br = 0;
   switch (m.kind) {
     case kMultiFp8Blk:
-      jb.kind = kJobFp8Blk;
-      return flat_wgs(kFp8Waves, kFp8Unr);
+      kind = kJobFp8Blk;
+      wgs = flat_wgs(kFp8Waves, kFp8Unr);
+      break;
     case kMultiFp8Tile:
-      jb.kind = kJobFp8Tile;
-      jb.rows = m.rows;
-      jb.br = (int32_t)(m.rows < 128 ? m.rows : 128);
-      return m.batch * (m.rows / jb.br) * (m.cols / 128);
+      kind = kJobFp8Tile;
+      br = (uint32_t)(m.rows < 128 ? m.rows : 128);
+      jb.n = m.cols;
+      wgs = m.batch * (m.rows / br) * (m.cols / 128);
+      break;
     case kMultiMx:
-      jb.kind = kJobMx;
-      return flat_wgs(kFp4Waves, fp4_unr);
+      kind = kJobMx;
+      wgs = flat_wgs(kFp4Waves, fp4_unr);
+      break;
     case kMultiMx8:
-      jb.kind = kJobMx8;
-      return flat_wgs(kFp4Waves, fp4_unr);
+      kind = kJobMx8;
+      wgs = flat_wgs(kFp4Waves, fp4_unr);
+      break;
     default:
-      jb.kind = kJobInt4;
-      return flat_wgs(kFp4Waves, fp4_unr);
+      kind = kJobInt4;
+      wgs = flat_wgs(kFp4Waves, fp4_unr);
   }
+  jb.meta = kind | (m.bf16 ? 1u : 0u) << 4 | (uint32_t)m.elem << 5 | br << 8;
+  return wgs;
 }
 
+struct Launch {
+  int fam;
+  int64_t wgs;
+  MultiArgs args;
+};
+
+// Splits one family's jobs into launches of at most kMaxBatchJobs jobs, as
+// even in job count as possible; false if a launch would exceed the grid
+// limit (2^32 - 1 threads), in which case nothing is planned to be launched.
 template <int kFam>
-hipError_t launch_family(const std::vector<const MultiJob*>& jobs, hipStream_t st) {
-  for (size_t base = 0; base < jobs.size(); base += kMaxBatchJobs) {
-    const int n = (int)(jobs.size() - base < (size_t)kMaxBatchJobs ? jobs.size() - base
-                                                                    : (size_t)kMaxBatchJobs);
-    MultiArgs a{};
-    a.njobs = n;
+bool plan_family(const std::vector<const MultiJob*>& jobs, std::vector<Launch>& out) {
+  const size_t n = jobs.size();
+  if (n == 0) return true;
+  const size_t nl = (n + kMaxBatchJobs - 1) / kMaxBatchJobs, per = (n + nl - 1) / nl;
+  for (size_t base = 0; base < n; base += per) {
+    const int cnt_jobs = (int)(n - base < per ? n - base : per);
+    Launch L;
+    L.fam = kFam;
+    L.args = MultiArgs{};
+    L.args.njobs = cnt_jobs;
     // whole-tile jobs (the heaviest workgroups) first, so that they are not
     // the last to be dispatched
     Job tmp[kMaxBatchJobs];
     int64_t cnt[kMaxBatchJobs];
-    for (int i = 0; i < n; ++i) cnt[i] = describe(*jobs[base + i], tmp[i]);
+    for (int i = 0; i < cnt_jobs; ++i) cnt[i] = describe(*jobs[base + i], tmp[i]);
     int order[kMaxBatchJobs], k = 0;
-    for (int i = 0; i < n; ++i) if (tmp[i].kind == kJobFp8Tile) order[k++] = i;
-    for (int i = 0; i < n; ++i) if (tmp[i].kind != kJobFp8Tile) order[k++] = i;
+    for (int i = 0; i < cnt_jobs; ++i)
+      if (job_kind(tmp[i].meta) == kJobFp8Tile) order[k++] = i;
+    for (int i = 0; i < cnt_jobs; ++i)
+      if (job_kind(tmp[i].meta) != kJobFp8Tile) order[k++] = i;
     int64_t wg = 0;
-    for (int i = 0; i < n; ++i) {
-      a.wg_begin[i] = wg;
-      a.job[i] = tmp[order[i]];
+    for (int i = 0; i < cnt_jobs; ++i) {
+      L.args.wg_begin[i] = wg;
+      L.args.job[i] = tmp[order[i]];
       wg += cnt[order[i]];
     }
-    a.wg_begin[n] = wg;
-    if (wg > 0)
-      hipLaunchKernelGGL(k_multi<kFam>, dim3((unsigned)wg), dim3(kThreads<kFam>), 0, st, a);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    L.args.wg_begin[cnt_jobs] = wg;
+    L.wgs = wg;
+    if (wg > (int64_t)(0xFFFFFFFFu / (uint32_t)kThreads<kFam>)) return false;
+    if (wg > 0) out.push_back(L);
   }
-  return hipSuccess;
+  return true;
+}
+
+bool plan_multi(const MultiJob* jobs, int njobs, std::vector<Launch>& out) {
+  std::vector<const MultiJob*> fam[3];
+  for (int i = 0; i < njobs; ++i) fam[family_of(jobs[i].kind)].push_back(&jobs[i]);
+  return plan_family<kFamFp8>(fam[kFamFp8], out) && plan_family<kFamMx>(fam[kFamMx], out) &&
+         plan_family<kFamInt4>(fam[kFamInt4], out);
 }
 
 }  // namespace
 
+int64_t multi_launches(const MultiJob* jobs, int njobs) {
+  std::vector<Launch> plan;
+  if (!plan_multi(jobs, njobs, plan)) return -1;
+  return (int64_t)plan.size();
+}
+
 hipError_t launch_multi(const MultiJob* jobs, int njobs, hipStream_t st) {
-  std::vector<const MultiJob*> fam[3];
-  for (int i = 0; i < njobs; ++i) fam[family_of(jobs[i].kind)].push_back(&jobs[i]);
-  hipError_t e = hipSuccess;
-  if (!fam[kFamFp8].empty()) e = launch_family<kFamFp8>(fam[kFamFp8], st);
-  if (e == hipSuccess && !fam[kFamMx].empty()) e = launch_family<kFamMx>(fam[kFamMx], st);
-  if (e == hipSuccess && !fam[kFamInt4].empty()) e = launch_family<kFamInt4>(fam[kFamInt4], st);
-  return e;
+  std::vector<Launch> plan;
+  if (!plan_multi(jobs, njobs, plan)) return hipErrorInvalidConfiguration;
+  for (const Launch& L : plan) {
+    const dim3 grid((unsigned)L.wgs);
+    switch (L.fam) {
+      case kFamFp8:
+        hipLaunchKernelGGL(k_multi<kFamFp8>, grid, dim3(kThreads<kFamFp8>), 0, st, L.args);
+        break;
+      case kFamMx:
+        hipLaunchKernelGGL(k_multi<kFamMx>, grid, dim3(kThreads<kFamMx>), 0, st, L.args);
+        break;
+      default:
+        hipLaunchKernelGGL(k_multi<kFamInt4>, grid, dim3(kThreads<kFamInt4>), 0, st, L.args);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace pqb

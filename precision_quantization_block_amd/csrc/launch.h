@@ -58,8 +58,9 @@ hipError_t launch_int4_dequant(const uint8_t* codes, const uint16_t* scales, con
                                int64_t n, bool out_bf16, void* out, hipStream_t st);
 
 // ---- fused multi-tensor launch ----------------------------------------------
-// Jobs of the one-pass formats, fused into launches of up to kMaxBatchJobs.
-constexpr int kMaxBatchJobs = 24;
+// Jobs of the one-pass formats, fused into launches of up to kMaxBatchJobs
+// (one family per launch; a family's jobs are split as evenly as possible).
+constexpr int kMaxBatchJobs = 72;
 enum MultiKind { kMultiFp8Blk = 0, kMultiFp8Tile = 1, kMultiMx = 2, kMultiInt4 = 3, kMultiMx8 = 4 };
 struct MultiJob {
   const void* x;
@@ -71,6 +72,10 @@ struct MultiJob {
   bool bf16;
   int elem;  // FP8 kinds: kE4M3 or kE5M2
 };
+// Launches the fused jobs take, or -1 if one of them would exceed the grid
+// limit of 2^32 - 1 threads (launch_multi then enqueues nothing and returns
+// hipErrorInvalidConfiguration).
+int64_t multi_launches(const MultiJob* jobs, int njobs);
 hipError_t launch_multi(const MultiJob* jobs, int njobs, hipStream_t st);
 
 // ---- two-pass formats (k_twopass.hip) -------------------------------------

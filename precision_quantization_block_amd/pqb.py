@@ -70,6 +70,8 @@ def lib():
         L.pqb_quantize.argtypes = [P, I, I64, I64, I64, I, I, P, P, P, P, SZ, P]
         L.pqb_dequantize.argtypes = [P, P, P, I, I, I64, I64, I64, I, P, P]
         L.pqb_quantize_batch.argtypes = [ctypes.POINTER(_Job), I64, P]
+        L.pqb_quantize_batch_launches.argtypes = [ctypes.POINTER(_Job), I64]
+        L.pqb_quantize_batch_launches.restype = I64
         L.pqb_kv_workspace_bytes.argtypes, L.pqb_kv_workspace_bytes.restype = [I64, I64], SZ
         L.pqb_kv_write_fp8.argtypes = [P, P, I, I64, I64, P, P, P, P, P, SZ, P]
         L.pqb_kv_workspace_bytes_ex.argtypes = [I64, I64, I64, I64]

@@ -179,6 +179,39 @@ def test_quantize_batch_errors_before_launch(L):
     assert run(job(rows=0), job(batch=0, fmt=3, gran=6, aux=fake)) == 0
 
 
+def test_quantize_batch_launch_plan(L):
+    """How many launches a batch takes (no device work), and the grid limit:
+    a launch of more than 2^32 - 1 threads is refused before anything runs."""
+    J = pqb.pqb._Job
+    fake = 0x10000
+
+    def job(**kw):
+        d = dict(x=fake, codes=fake, scales=fake, aux=None, batch=1, rows=128, cols=256,
+                 dtype=1, fmt=0, gran=2, reserved=0)
+        d.update(kw)
+        return J(**d)
+
+    def launches(*jobs):
+        return L.pqb_quantize_batch_launches((J * len(jobs))(*jobs), len(jobs))
+
+    int4 = dict(fmt=3, gran=6, aux=fake)
+    assert launches(job(), job(gran=3)) == 1                       # 1x128 and 128x128 share one
+    assert launches(job(), job(gran=3), job(gran=1)) == 2          # a per-row job is its own
+    assert launches(*[job(**int4)] * 72) == 1                      # up to 72 jobs per launch
+    assert launches(*[job(**int4)] * 73) == 2
+    assert launches(*[job(**int4)] * 224) == 4                     # the Llama-3.1-8B decoder
+    assert launches(job(), job(fmt=1, gran=4), job(**int4)) == 3   # one launch per family
+    assert launches(job(rows=0)) == 0
+    assert launches(job(gran=0)) == -3
+    # 2^36 elements of 1x128 FP8 need 2^23 workgroups of 512 threads: one too many
+    assert launches(job(rows=1 << 20, cols=1 << 16)) == -4
+    assert launches(job(rows=(1 << 20) - 1, cols=1 << 16)) == 1
+    assert L.pqb_quantize_batch((J * 1)(job(rows=1 << 20, cols=1 << 16)), 1, None) == -4
+    # one wave per row, 4 rows per 256-thread workgroup
+    assert launches(job(gran=1, rows=4 * (0xFFFFFFFF // 256) + 1, cols=8)) == -4
+    assert launches(job(gran=1, rows=4 * (0xFFFFFFFF // 256), cols=8)) == 1
+
+
 def test_kv_write_ex_errors_before_launch(L):
     P = ctypes.c_void_p
     fake, odd = P(0x10000), P(0x10002)

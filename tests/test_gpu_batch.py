@@ -85,7 +85,7 @@ def _inputs(specs, seed0):
 
 @pytest.mark.parametrize("repeat", [1, 3])
 def test_batch_matches_oracle(pqb, repeat):
-    """`repeat` copies of the mixed list: 14 jobs in one launch, 42 in two."""
+    """`repeat` copies of the mixed list (14 or 42 jobs)."""
     specs = MIXED * repeat
     xs = _inputs(specs, 100)
     outs = pqb.quantize_batch([(x.to(DEV), f, g) for x, (f, g, _) in zip(xs, specs)])
@@ -130,6 +130,30 @@ def test_batch_decoder_int4_weights(pqb):
             # zero-points of one row: g nibbles starting at flat group row*g (g even)
             zb = host_bits(q.aux[row * g // 2:(row * g + g) // 2])
             assert np.array_equal(zb, ref_bits(oz)), f"proj {i} row {row} zeros"
+
+
+def test_batch_many_jobs_several_launches(pqb):
+    """300 small ragged jobs: 150 FP8 (1x128 and 128x128), 75 MXFP4 and 75
+    INT4, so each family is split over several launches (FP8 3, MXFP4 2,
+    INT4 2) and the workgroup-to-job search crosses every job boundary."""
+    rng = np.random.default_rng(11)
+    specs = []
+    for i in range(300):
+        k = i % 4
+        if k in (0, 1):
+            gran = "1x128" if k == 0 else "128x128"
+            rows = int(rng.integers(1, 6)) if k == 0 else int(rng.choice([1, 3, 64, 128, 256]))
+            specs.append(("fp8_e4m3", gran, (1, rows, 128 * int(rng.integers(1, 4)))))
+        elif k == 2:
+            specs.append(("mxfp4", None, (1, int(rng.integers(1, 9)), 32 * int(rng.integers(1, 6)))))
+        else:
+            specs.append(("int4_asym", None, (1, int(rng.integers(1, 5)), 128 * int(rng.integers(1, 4)))))
+    xs = _inputs(specs, 700)
+    items = [(x.to(DEV), f, g) for x, (f, g, _) in zip(xs, specs)]
+    outs = pqb.quantize_batch(items)
+    for i, (x, (fmt, gran, shp), q) in enumerate(zip(xs, specs, outs)):
+        check(q, oracle_of(x, fmt, gran or pqb.pqb.DEFAULT_GRAN[fmt]),
+              f"job {i} {fmt} {gran} {shp} {x.dtype}")
 
 
 def test_batch_empty_list(pqb):
