@@ -209,6 +209,66 @@ def test_int4_parity(pqb, dtype):
              f"int4 {(b, r, c)} dequant bf16")
 
 
+def _int4_edge_groups(rows=64, cols=4096):
+    """bf16 rows of 32 groups each, many of them hand-made: exact .5 ties at
+    scales 1 and 3 (lo = -8 s, hi = 7 s), ties next to the range ends, constant
+    groups (zero, -0, negative, positive), one-signed groups (zero-point 7 and
+    -8), rint(lo / s) = -15, tiny and huge ranges, single outliers; the rest is
+    the weight recipe.  Full rows are whole 512-unit chunks, the shape on which
+    bf16 quantization stages its loads through LDS."""
+    g = torch.Generator().manual_seed(91)
+    x = torch.randn((rows, cols), generator=g) * 0.02
+    grp = x.view(rows, cols // 128, 128)
+    ties1 = torch.cat([torch.tensor([-8.0, 7.0]), torch.arange(-7.5, 7.0, 1.0)])    # s = 1
+    ties3 = torch.cat([torch.tensor([-24.0, 21.0]), 3 * torch.arange(-7.5, 7.0, 1.0)])  # s = 3
+    for r in range(rows):
+        for k in range(cols // 128):
+            kind = (r * 32 + k) % 16
+            if kind == 0:
+                grp[r, k] = ties1.repeat(128 // ties1.numel() + 1)[:128]
+            elif kind == 1:
+                grp[r, k] = ties3.repeat(128 // ties3.numel() + 1)[:128]
+            elif kind == 2:
+                grp[r, k] = 0.0
+            elif kind == 3:
+                grp[r, k] = -0.0
+            elif kind == 4:
+                grp[r, k] = -1.25
+            elif kind == 5:
+                grp[r, k] = 3.0
+            elif kind == 6:
+                grp[r, k] = -grp[r, k].abs() - 1e-3          # all negative: z = 7
+            elif kind == 7:
+                grp[r, k] = grp[r, k].abs() + 1e-3           # all positive: z = -8
+            elif kind == 8:
+                grp[r, k] = grp[r, k].abs()
+                grp[r, k, 17] = -1.0                         # lo far below: rint(lo/s) = -15
+                grp[r, k, 18] = 0.0
+            elif kind == 9:
+                grp[r, k] = grp[r, k] * 1e-35                # subnormal-scale range
+            elif kind == 10:
+                grp[r, k] = grp[r, k] * 1e36                 # range near 1e35
+            elif kind == 11:
+                grp[r, k, (r + k) % 128] = 50.0              # one outlier
+            elif kind == 12:
+                grp[r, k] = torch.arange(128) % 16 - 8.0     # every code at s = 1
+    return x.to(torch.bfloat16)
+
+
+def test_int4_full_chunks_edge_groups(pqb):
+    x = _int4_edge_groups()
+    oc, os_, oz = oracle.int4_quantize(x)
+    q = pqb.quantize(x.to(DEV), "int4_asym")
+    same(q.codes, oc, "int4 edge groups codes")
+    same(q.scales, os_, "int4 edge groups scales")
+    same(q.aux, oz, "int4 edge groups zeros")
+    (qb,) = pqb.quantize_batch([(x.to(DEV), "int4_asym", None)])
+    same(qb.codes, oc, "int4 edge groups codes (batch)")
+    same(qb.scales, os_, "int4 edge groups scales (batch)")
+    same(qb.aux, oz, "int4 edge groups zeros (batch)")
+    same(pqb.dequantize(q), oracle.int4_dequantize(oc, os_, oz), "int4 edge groups dequant")
+
+
 # ---------------------------------------------------------------- KV -------
 
 def test_kv_write_parity(pqb):
