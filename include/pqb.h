@@ -386,6 +386,22 @@ pqb_status pqb_encode_e4m3(const float* y, int64_t n, uint8_t* out, void* stream
 pqb_status pqb_encode_e5m2(const float* y, int64_t n, uint8_t* out, void* stream);
 pqb_status pqb_encode_e2m1(const float* y, int64_t n, uint8_t* out, void* stream);
 
+/* The engine's division routines on generated arguments, exposed for testing
+ * them against IEEE division over whole ranges of floats (every quantizer
+ * code above rests on x / s being the correctly rounded quotient; page
+ * "量化部署实战", section 伪量化实现, divides by the scale before rounding).
+ * pqb_check_recip: out[i] = the engine's RN(1 / s) for s = the float whose
+ *   bit pattern is first_bits + i, i < n; needs first_bits + n <= 2^32.
+ * pqb_check_div: out[j * nx + i] = the engine's RN(x / s[j]) for x = the
+ *   float whose bit pattern is x_first_bits + i, i < nx, j < ns, formed as the
+ *   quantizers form it (from y = RN(1 / s[j]) and one correction); needs
+ *   x_first_bits + nx <= 2^32.
+ * s and out are device arrays (4-byte aligned) of ns and n (ns * nx) floats.
+ * Errors, before any launch: PQB_ERR_SHAPE, PQB_ERR_NULL, PQB_ERR_ALIGN. */
+pqb_status pqb_check_recip(uint32_t first_bits, int64_t n, float* out, void* stream);
+pqb_status pqb_check_div(const float* s, int64_t ns, uint32_t x_first_bits, int64_t nx,
+                         float* out, void* stream);
+
 const char* pqb_status_string(pqb_status s);
 int pqb_abi_version(void);
 

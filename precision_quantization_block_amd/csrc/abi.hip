@@ -668,4 +668,23 @@ pqb_status pqb_encode_e2m1(const float* y, int64_t n, uint8_t* out, void* stream
   return hip_status(launch_encode_e2m1(y, n, out, (hipStream_t)stream));
 }
 
+pqb_status pqb_check_recip(uint32_t first_bits, int64_t n, float* out, void* stream) {
+  if (n < 0 || (uint64_t)first_bits + (uint64_t)n > ((uint64_t)1 << 32)) return PQB_ERR_SHAPE;
+  if (n == 0) return PQB_OK;
+  if (!out) return PQB_ERR_NULL;
+  if (!aligned(out, 4)) return PQB_ERR_ALIGN;
+  return hip_status(launch_check_recip(first_bits, n, out, (hipStream_t)stream));
+}
+
+pqb_status pqb_check_div(const float* s, int64_t ns, uint32_t x_first_bits, int64_t nx,
+                         float* out, void* stream) {
+  if (ns < 0 || nx < 0 || (uint64_t)x_first_bits + (uint64_t)nx > ((uint64_t)1 << 32))
+    return PQB_ERR_SHAPE;
+  if (nx > 0 && ns > INT64_MAX / nx) return PQB_ERR_SHAPE;
+  if (ns == 0 || nx == 0) return PQB_OK;
+  if (!s || !out) return PQB_ERR_NULL;
+  if (!aligned(s, 4) || !aligned(out, 4)) return PQB_ERR_ALIGN;
+  return hip_status(launch_check_div(s, ns, x_first_bits, nx, out, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -156,6 +156,11 @@ hipError_t launch_w4a16(const W4Job* jobs, int njobs, int M, bool out_bf16, hipS
 hipError_t launch_w4a16_mfma(const W4Job* jobs, int njobs, int64_t M, bool out_bf16,
                              hipStream_t st);
 
+// ---- division checks (k_check.hip) -----------------------------------------
+hipError_t launch_check_recip(uint32_t first, int64_t n, float* out, hipStream_t st);
+hipError_t launch_check_div(const float* s, int64_t ns, uint32_t x_first, int64_t nx, float* out,
+                            hipStream_t st);
+
 // ---- element codecs ---------------------------------------------------------
 hipError_t launch_encode_elem(const float* y, int64_t n, uint8_t* out, hipStream_t st, int elem);
 hipError_t launch_encode_e2m1(const float* y, int64_t n, uint8_t* out, hipStream_t st);

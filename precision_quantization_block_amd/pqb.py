@@ -89,13 +89,16 @@ def lib():
         L.pqb_encode_e4m3.argtypes = [P, I64, P, P]
         L.pqb_encode_e5m2.argtypes = [P, I64, P, P]
         L.pqb_encode_e2m1.argtypes = [P, I64, P, P]
+        L.pqb_check_recip.argtypes = [ctypes.c_uint32, I64, P, P]
+        L.pqb_check_div.argtypes = [P, I64, ctypes.c_uint32, I64, P, P]
         for f in ("pqb_query_sizes", "pqb_quantize", "pqb_quantize_batch", "pqb_dequantize",
                   "pqb_kv_write_fp8", "pqb_kv_write_fp8_ex", "pqb_kv_write_kivi",
                   "pqb_kv_read_kivi", "pqb_gemm_fp8_blockscaled",
                   "pqb_gemm_fp8_blockscaled_quant", "pqb_gemv_w4a16",
                   "pqb_gemv_w4a16_batch", "pqb_gemm_mxfp4", "pqb_gemm_w4a16",
                   "pqb_gemm_w4a16_batch",
-                  "pqb_encode_e4m3", "pqb_encode_e5m2", "pqb_encode_e2m1"):
+                  "pqb_encode_e4m3", "pqb_encode_e5m2", "pqb_encode_e2m1",
+                  "pqb_check_recip", "pqb_check_div"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -536,6 +539,23 @@ def encode_e2m1(y: torch.Tensor) -> torch.Tensor:
     y = _dev_tensor(y, "y", (torch.float32,))
     out = torch.empty(y.shape, dtype=torch.uint8, device=y.device)
     _check(lib().pqb_encode_e2m1(_ptr(y), y.numel(), _ptr(out), _stream(y.device)), "encode_e2m1")
+    return out
+
+
+def check_recip(first_bits: int, n: int, device="cuda") -> torch.Tensor:
+    """The engine's RN(1/s) for the n floats whose bit patterns start at first_bits."""
+    out = torch.empty((n,), dtype=torch.float32, device=device)
+    _check(lib().pqb_check_recip(first_bits, n, _ptr(out), _stream(out.device)), "check_recip")
+    return out
+
+
+def check_div(s: torch.Tensor, x_first_bits: int, nx: int) -> torch.Tensor:
+    """The engine's RN(x / s[j]) for the nx floats x whose bit patterns start at
+    x_first_bits; returns [len(s), nx]."""
+    s = _dev_tensor(s, "s", (torch.float32,)).contiguous()
+    out = torch.empty((s.numel(), nx), dtype=torch.float32, device=s.device)
+    _check(lib().pqb_check_div(_ptr(s), s.numel(), x_first_bits, nx, _ptr(out), _stream(s.device)),
+           "check_div")
     return out
 
 

@@ -212,6 +212,21 @@ def test_quantize_batch_launch_plan(L):
     assert launches(job(gran=1, rows=4 * (0xFFFFFFFF // 256), cols=8)) == 1
 
 
+def test_division_check_errors_before_launch(L):
+    fake = 0x10000
+    assert L.pqb_check_recip(0, -1, fake, None) == -4
+    assert L.pqb_check_recip(0xFFFFFFFF, 2, fake, None) == -4     # past the last pattern
+    assert L.pqb_check_recip(5, 0, None, None) == 0
+    assert L.pqb_check_recip(5, 3, None, None) == -1
+    assert L.pqb_check_recip(5, 3, fake + 2, None) == -5
+    assert L.pqb_check_div(fake, -1, 0, 4, fake, None) == -4
+    assert L.pqb_check_div(fake, 1, 0xFFFFFFF0, 17, fake, None) == -4
+    assert L.pqb_check_div(fake, 1 << 40, 0, 1 << 30, fake, None) == -4
+    assert L.pqb_check_div(None, 2, 0, 4, fake, None) == -1
+    assert L.pqb_check_div(fake, 2, 0, 4, fake + 1, None) == -5
+    assert L.pqb_check_div(fake, 0, 0, 4, fake, None) == 0
+
+
 def test_kv_write_ex_errors_before_launch(L):
     P = ctypes.c_void_p
     fake, odd = P(0x10000), P(0x10002)
