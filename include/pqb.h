@@ -5,8 +5,8 @@
  * device pointer owned by the caller; the library never allocates, frees or
  * synchronizes.  Every call enqueues its kernels on `stream` (a hipStream_t,
  * NULL for the default stream) and returns at once; results are ready when
- * the stream reaches that point.  Calls are thread-safe: the library keeps no
- * mutable global state.
+ * the stream reaches that point.  Calls are thread-safe: apart from the fixed
+ * scratch of pqb_quantize_noalloc, the library keeps no mutable global state.
  *
  * Formats and the passages that define them (page title, section):
  *   "量化部署实战" (quantization deployment in practice), section 伪量化实现
@@ -93,7 +93,8 @@ typedef enum pqb_status {
   PQB_ERR_SHAPE = -4,     /* negative size, or a shape the block rules reject */
   PQB_ERR_ALIGN = -5,     /* a pointer breaks the alignment rules */
   PQB_ERR_WORKSPACE = -6, /* workspace smaller than pqb_query_sizes asks */
-  PQB_ERR_HIP = -7        /* the HIP runtime refused a launch */
+  PQB_ERR_HIP = -7,       /* the HIP runtime refused a launch */
+  PQB_ERR_SCRATCH = -8    /* pqb_quantize_noalloc: needs more than its fixed scratch */
 } pqb_status;
 
 typedef enum pqb_dtype { PQB_F32 = 0, PQB_BF16 = 1 } pqb_dtype;
@@ -135,6 +136,26 @@ pqb_status pqb_query_sizes(pqb_format fmt, pqb_gran gran, int64_t batch, int64_t
 pqb_status pqb_quantize(const void* x, pqb_dtype dtype, int64_t batch, int64_t rows, int64_t cols,
                         pqb_format fmt, pqb_gran gran, void* codes, void* scales, void* aux,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* pqb_quantize for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments and results without `workspace`.  The two-pass formats
+ * (FP8 / E5M2 / INT8 TENSOR, NVFP4) use instead a scratch array of
+ * PQB_NOALLOC_SCRATCH_BYTES (1 MiB) that the library holds on each GPU it runs
+ * on until the process ends; its address is looked up once per device, on the
+ * first call with that device current.  The call allocates and frees nothing
+ * (no hipMalloc, no allocating library routine).  A shape whose workspace
+ * (pqb_query_sizes) exceeds the scratch returns PQB_ERR_SCRATCH before
+ * anything is enqueued: e.g. one per-tensor slice of up to 2^31 - 8192 elements
+ * fits.
+ * `stream` must belong to the current device.  Every call on one GPU shares
+ * that GPU's scratch, and each call overwrites what it uses before reading it:
+ * calls that overlap on one GPU (other streams, other host threads) race, so
+ * order them.  Every other rule and error is pqb_quantize's. */
+#define PQB_NOALLOC_SCRATCH_BYTES (1u << 20)
+pqb_status pqb_quantize_noalloc(const void* x, pqb_dtype dtype, int64_t batch, int64_t rows,
+                                int64_t cols, pqb_format fmt, pqb_gran gran, void* codes,
+                                void* scales, void* aux, void* stream);
 
 /* One tensor of a fused batch: the arguments of one pqb_quantize call. */
 typedef struct pqb_job {

@@ -2,6 +2,8 @@
 // dispatch to the kernel launchers.  Nothing here allocates or synchronizes.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <mutex>
 #include <vector>
 
 #include "../../include/pqb.h"
@@ -140,6 +142,37 @@ pqb_status hip_status(hipError_t e) { return e == hipSuccess ? PQB_OK : PQB_ERR_
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Fixed scratch for pqb_quantize_noalloc: one array per GPU, resolved once per
+// device with hipGetSymbolAddress (host code never passes the symbol itself,
+// which is only a host-side stand-in) and kept until the process ends.
+// ---------------------------------------------------------------------------
+static_assert(PQB_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) uint8_t scratch[PQB_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch array.
+pqb_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PQB_ERR_HIP;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PQB_ERR_HIP;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return PQB_OK;
+}
+}  // namespace
+
 extern "C" {
 
 int pqb_abi_version(void) { return PQB_ABI_VERSION; }
@@ -154,6 +187,7 @@ const char* pqb_status_string(pqb_status s) {
     case PQB_ERR_ALIGN: return "pointer alignment rule broken";
     case PQB_ERR_WORKSPACE: return "workspace too small";
     case PQB_ERR_HIP: return "HIP launch failed";
+    case PQB_ERR_SCRATCH: return "needs more scratch than the fixed buffer of pqb_quantize_noalloc";
   }
   return "unknown status";
 }
@@ -173,7 +207,8 @@ pqb_status pqb_query_sizes(pqb_format fmt, pqb_gran gran, int64_t batch, int64_t
 static pqb_status check_quantize(const void* x, int dtype, int64_t batch, int64_t rows,
                                  int64_t cols, int fmt, int gran, const void* codes,
                                  const void* scales, const void* aux, const void* workspace,
-                                 size_t workspace_bytes, pqb_sizes* need) {
+                                 size_t workspace_bytes, pqb_sizes* need,
+                                 bool check_workspace = true) {
   if (!valid_dtype(dtype) || !known_format(fmt) || !known_gran(gran)) return PQB_ERR_ENUM;
   if (!valid_pair(fmt, gran)) return PQB_ERR_COMBO;
   pqb_status st = check_shape(fmt, gran, batch, rows, cols);
@@ -182,10 +217,12 @@ static pqb_status check_quantize(const void* x, int dtype, int64_t batch, int64_
   if (batch * rows * cols == 0) return PQB_OK;
   if (!x || !codes || !scales) return PQB_ERR_NULL;
   if (need->aux && !aux) return PQB_ERR_NULL;
-  if (need->workspace && !workspace) return PQB_ERR_NULL;
-  if (workspace_bytes < need->workspace) return PQB_ERR_WORKSPACE;
-  if (!aligned(x, 16) || !aligned(codes, 16) || (need->workspace && !aligned(workspace, 16)))
-    return PQB_ERR_ALIGN;
+  if (check_workspace) {
+    if (need->workspace && !workspace) return PQB_ERR_NULL;
+    if (workspace_bytes < need->workspace) return PQB_ERR_WORKSPACE;
+    if (need->workspace && !aligned(workspace, 16)) return PQB_ERR_ALIGN;
+  }
+  if (!aligned(x, 16) || !aligned(codes, 16)) return PQB_ERR_ALIGN;
   if (one_byte(fmt) && !aligned(scales, 4)) return PQB_ERR_ALIGN;
   if (fmt == PQB_INT4_ASYM && !aligned(scales, 2)) return PQB_ERR_ALIGN;
   if (fmt == PQB_NVFP4 && !aligned(aux, 4)) return PQB_ERR_ALIGN;
@@ -238,6 +275,26 @@ pqb_status pqb_quantize(const void* x, pqb_dtype dtype, int64_t batch, int64_t r
           launch_int4(x, bf16, n, c8, (uint16_t*)scales, (uint8_t*)aux, s));
   }
   return PQB_ERR_ENUM;
+}
+
+pqb_status pqb_quantize_noalloc(const void* x, pqb_dtype dtype, int64_t batch, int64_t rows,
+                                int64_t cols, pqb_format fmt, pqb_gran gran, void* codes,
+                                void* scales, void* aux, void* stream) {
+  pqb_sizes need;
+  // every rule of pqb_quantize except the workspace's, which the fixed
+  // scratch replaces
+  pqb_status st = check_quantize(x, dtype, batch, rows, cols, fmt, gran, codes, scales, aux,
+                                 nullptr, 0, &need, false);
+  if (st != PQB_OK) return st;
+  if (need.workspace > PQB_NOALLOC_SCRATCH_BYTES) return PQB_ERR_SCRATCH;
+  if (batch * rows * cols == 0) return PQB_OK;
+  void* ws = nullptr;
+  if (need.workspace) {
+    st = scratch_of_current_device(&ws);
+    if (st != PQB_OK) return st;
+  }
+  return pqb_quantize(x, dtype, batch, rows, cols, fmt, gran, codes, scales, aux, ws,
+                      need.workspace ? (size_t)PQB_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 // Validates a batch and sorts its jobs: one-pass jobs for the fused launches

@@ -68,6 +68,7 @@ def lib():
         L.pqb_status_string.argtypes, L.pqb_status_string.restype = [I], ctypes.c_char_p
         L.pqb_query_sizes.argtypes = [I, I, I64, I64, I64, ctypes.POINTER(_Sizes)]
         L.pqb_quantize.argtypes = [P, I, I64, I64, I64, I, I, P, P, P, P, SZ, P]
+        L.pqb_quantize_noalloc.argtypes = [P, I, I64, I64, I64, I, I, P, P, P, P]
         L.pqb_dequantize.argtypes = [P, P, P, I, I, I64, I64, I64, I, P, P]
         L.pqb_quantize_batch.argtypes = [ctypes.POINTER(_Job), I64, P]
         L.pqb_quantize_batch_launches.argtypes = [ctypes.POINTER(_Job), I64]
@@ -91,7 +92,8 @@ def lib():
         L.pqb_encode_e2m1.argtypes = [P, I64, P, P]
         L.pqb_check_recip.argtypes = [ctypes.c_uint32, I64, P, P]
         L.pqb_check_div.argtypes = [P, I64, ctypes.c_uint32, I64, P, P]
-        for f in ("pqb_query_sizes", "pqb_quantize", "pqb_quantize_batch", "pqb_dequantize",
+        for f in ("pqb_query_sizes", "pqb_quantize", "pqb_quantize_noalloc", "pqb_quantize_batch",
+                  "pqb_dequantize",
                   "pqb_kv_write_fp8", "pqb_kv_write_fp8_ex", "pqb_kv_write_kivi",
                   "pqb_kv_read_kivi", "pqb_gemm_fp8_blockscaled",
                   "pqb_gemm_fp8_blockscaled_quant", "pqb_gemv_w4a16",

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for code in range(0, -8, -1):
+    for code in range(0, -9, -1):
         assert pqb.status_string(code) not in ("", "unknown status")
     assert pqb.status_string(5) == "unknown status"
 
@@ -225,6 +225,24 @@ def test_division_check_errors_before_launch(L):
     assert L.pqb_check_div(None, 2, 0, 4, fake, None) == -1
     assert L.pqb_check_div(fake, 2, 0, 4, fake + 1, None) == -5
     assert L.pqb_check_div(fake, 0, 0, 4, fake, None) == 0
+
+
+def test_quantize_noalloc_errors_before_launch(L):
+    """The no-allocation entry point validates like pqb_quantize and refuses a
+    shape whose workspace exceeds its fixed scratch, before any GPU call."""
+    fake = 0x10000
+    P = pqb.lib().pqb_quantize_noalloc
+    # a per-tensor FP8 slice of 2^33 float32 elements needs > 1 MiB of partials
+    assert pqb.query_sizes("fp8_e4m3", "tensor", 1, 1 << 17, 1 << 16)["workspace"] > 1 << 20
+    assert P(fake, 0, 1, 1 << 17, 1 << 16, 0, 0, fake, fake, None, None) == -8
+    assert P(fake, 1, 1, 1 << 17, 1 << 16, 2, 5, fake, fake, fake, None) == -8   # NVFP4
+    assert P(fake, 1, 1, 8, 100, 0, 2, fake, fake, None, None) == -4            # 1x128 shape
+    assert P(None, 1, 1, 8, 128, 0, 0, fake, fake, None, None) == -1
+    assert P(fake, 1, 1, 8, 128, 2, 5, fake, fake, None, None) == -1            # NVFP4 needs aux
+    assert P(fake + 2, 1, 1, 8, 128, 0, 0, fake, fake, None, None) == -5
+    assert P(fake, 1, 1, 8, 128, 9, 0, fake, fake, None, None) == -2
+    assert P(fake, 1, 1, 0, 128, 0, 0, None, None, None, None) == 0               # empty
+    assert pqb.status_string(-8) != "unknown status"
 
 
 def test_kv_write_ex_errors_before_launch(L):
