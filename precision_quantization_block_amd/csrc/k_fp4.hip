@@ -85,15 +85,28 @@ hipError_t launch_mxfp4(const void* x, bool bf16, int64_t n, uint8_t* codes, uin
                         hipStream_t st) {
   // one chunk of 4 tiles per wave (4 KiB of bf16 or 8 KiB of float32 input;
   // with the first chunk's loads ahead of the table fill, 4 bf16 tiles beat 8
-  // by 4-5% from 117 MB to 1 GiB in a same-process A/B)
+  // by 4-5% from 117 MB to 1 GiB in a same-process A/B); one tile per wave
+  // when 4-tile chunks would give fewer than 4096 waves, so that a small
+  // tensor spreads over more waves (float32 [3072, 1024]: 5.5 -> 5.0 us;
+  // 16M elements and up: equal)
   const int64_t nunits = n / 8, ntiles = (nunits + kWave - 1) / kWave;
   const int64_t waves = kBlockThreads / kWave;
-  if (bf16)
-    hipLaunchKernelGGL((k_mxfp4<uint16_t, 4>), dim3(grid_cap(ntiles, 4 * waves, 1 << 30)),
-                       dim3(kBlockThreads), 0, st, (const uint16_t*)x, nunits, codes, scales);
-  else
-    hipLaunchKernelGGL((k_mxfp4<float, 4>), dim3(grid_cap(ntiles, 4 * waves, 1 << 30)),
-                       dim3(kBlockThreads), 0, st, (const float*)x, nunits, codes, scales);
+  const bool small = (ntiles + 3) / 4 < 4096;
+  if (bf16) {
+    if (small)
+      hipLaunchKernelGGL((k_mxfp4<uint16_t, 1>), dim3(grid_cap(ntiles, waves, 1 << 30)),
+                         dim3(kBlockThreads), 0, st, (const uint16_t*)x, nunits, codes, scales);
+    else
+      hipLaunchKernelGGL((k_mxfp4<uint16_t, 4>), dim3(grid_cap(ntiles, 4 * waves, 1 << 30)),
+                         dim3(kBlockThreads), 0, st, (const uint16_t*)x, nunits, codes, scales);
+  } else {
+    if (small)
+      hipLaunchKernelGGL((k_mxfp4<float, 1>), dim3(grid_cap(ntiles, waves, 1 << 30)),
+                         dim3(kBlockThreads), 0, st, (const float*)x, nunits, codes, scales);
+    else
+      hipLaunchKernelGGL((k_mxfp4<float, 4>), dim3(grid_cap(ntiles, 4 * waves, 1 << 30)),
+                         dim3(kBlockThreads), 0, st, (const float*)x, nunits, codes, scales);
+  }
   return hipGetLastError();
 }
 

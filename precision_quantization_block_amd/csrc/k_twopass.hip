@@ -10,6 +10,10 @@
 //             and a small table for pass 2 (s per group; for NVFP4 gs, RN(1/gs)
 //             and s, RN(1/s) of all 127 block-scale codes);
 //   pass 2    quantizes with the finished table.
+// When every slice has few partials (at most kFoldMaxPartials, no per-head
+// groups) the finalize launch is left out: each pass-2 workgroup reduces its
+// slice's partials itself (from L2) and forms the same scale or table with the
+// same arithmetic, so a small tensor takes two launches instead of three.
 // A slice is one batch slice (per-tensor FP8, NVFP4) or one layer of K or V.
 // Per head, a lane follows its unit's column through the chunk: one 64-bit
 // remainder per chunk, then +64 units per tile with one wrap, and the head is
@@ -21,9 +25,18 @@
 namespace pqb {
 namespace {
 
-template <typename T>
-constexpr int kChunkUnr = sizeof(T) == 2 ? 8 : 4;
 constexpr int kWgWaves = kBlockThreads / kWave;
+
+// Tiles per wave chunk (U): 8 bf16 or 4 float32 tiles (8 KiB of input), or
+// half that when a slice would give fewer than 2048 waves at the full size, so
+// that a small tensor spreads over more waves (NVFP4 on bf16 [4096, 1024]:
+// 10.9 -> 9.3 us; on float32 [3072, 1024]: 11.9 -> 11.0 us; a 16M-element
+// slice is 4% faster at the full size).  Every kernel of a call uses the same U.
+int chunk_tiles(int64_t per_slice, bool bf16) {
+  const int full = bf16 ? 8 : 4;
+  const int64_t waves = (per_slice / 8 + (int64_t)full * kWave - 1) / ((int64_t)full * kWave);
+  return waves < 2048 ? full / 2 : full;
+}
 
 struct TpArgs {
   const void* x[2];
@@ -74,10 +87,9 @@ struct ColWalk {
 // ---------------------------------------------------------------------------
 // pass 1
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, int U>
 __global__ __launch_bounds__(kBlockThreads) void k_tp_amax(TpArgs a, TpGeo g,
                                                            float* __restrict__ partials) {
-  constexpr int U = kChunkUnr<T>;
   __shared__ uint32_t red[kMaxKvHeads > kWgWaves ? kMaxKvHeads : kWgWaves];
   const int tz = blockIdx.z;
   if (a.mode[tz] == kKvStatic) return;  // uniform over the workgroup
@@ -159,6 +171,21 @@ __device__ __forceinline__ uint32_t reduce_row(const float* __restrict__ p, int 
   return m;
 }
 
+// Max of a slice's W partials over one 256-thread workgroup (every thread
+// gets it); `red` holds kWgWaves words.  All threads must call it.
+constexpr int kFoldMaxPartials = 1024;
+__device__ __forceinline__ uint32_t fold_partials(const float* __restrict__ p, int W, uint32_t* red) {
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < W; i += kBlockThreads) m = max(m, as_u(p[i]));
+  m = wave_umax(m);
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = m;
+  __syncthreads();
+  m = red[0];
+#pragma unroll
+  for (int w = 1; w < kWgWaves; ++w) m = max(m, red[w]);
+  return m;
+}
+
 template <int kElem>
 __global__ __launch_bounds__(kFinThreads) void k_tp_finalize_fp8(TpArgs a, TpGeo g,
                                                                  const float* __restrict__ partials,
@@ -215,11 +242,10 @@ __device__ __forceinline__ uint2 fp8_pack8_clamped(const float v[8], float s, fl
   return make_uint2(e4m3_bytes4(q[0], q[1], q[2], q[3]), e4m3_bytes4(q[4], q[5], q[6], q[7]));
 }
 
-template <typename T, int kMode, bool kGuard, int kElem>
+template <typename T, int U, int kMode, bool kGuard, int kElem>
 __device__ __forceinline__ void fp8_tp_chunk(const T* __restrict__ xs, int64_t u0, int64_t nunits,
                                              uint8_t* __restrict__ cs, float s, float y,
                                              const float* ss, const float* ys, const TpGeo& g) {
-  constexpr int U = kChunkUnr<T>;
   const int lane = threadIdx.x & (kWave - 1);
   Raw8 raw[U];
   load_chunk<T, U, kGuard>(xs, u0, nunits, raw);
@@ -244,15 +270,25 @@ __device__ __forceinline__ void fp8_tp_chunk(const T* __restrict__ xs, int64_t u
   }
 }
 
-template <typename T, int kElem>
+// kFold: `fin` holds the partials (no per-head groups); each workgroup
+// reduces its slice's own, and workgroup 0 of the slice writes the scale.
+template <typename T, int kElem, bool kFold, int U>
 __global__ __launch_bounds__(kBlockThreads) void k_tp_fp8(TpArgs a, TpGeo g,
                                                           const float* __restrict__ fin) {
-  constexpr int U = kChunkUnr<T>;
   __shared__ float ss[kMaxKvHeads], ys[kMaxKvHeads];
+  __shared__ uint32_t red[kWgWaves];
   const int tz = blockIdx.z, mode = a.mode[tz];
   const int64_t b = blockIdx.y, slot = (int64_t)tz * g.slices + b;
   float s = 0.0f, y = 0.0f;
-  if (mode == kKvHead) {
+  if constexpr (kFold) {
+    if (mode == kKvStatic) {
+      s = reinterpret_cast<const float*>(a.scales[tz])[b];
+    } else {
+      s = fp8_scale_bits<kElem>(fold_partials(fin + slot * g.W, g.W, red));
+      if (blockIdx.x == 0 && threadIdx.x == 0) reinterpret_cast<float*>(a.scales[tz])[b] = s;
+    }
+    y = recip_rn(s);
+  } else if (mode == kKvHead) {
     for (int i = threadIdx.x; i < g.G; i += kBlockThreads) {
       const float si = fin[slot * g.G + i];
       ss[i] = si;
@@ -272,32 +308,49 @@ __global__ __launch_bounds__(kBlockThreads) void k_tp_fp8(TpArgs a, TpGeo g,
   const bool full = u0 + U * kWave <= nunits;
   switch (mode) {
     case kKvHead:
-      if (full) fp8_tp_chunk<T, kKvHead, false, kElem>(xs, u0, nunits, cs, s, y, ss, ys, g);
-      else fp8_tp_chunk<T, kKvHead, true, kElem>(xs, u0, nunits, cs, s, y, ss, ys, g);
+      if (full) fp8_tp_chunk<T, U, kKvHead, false, kElem>(xs, u0, nunits, cs, s, y, ss, ys, g);
+      else fp8_tp_chunk<T, U, kKvHead, true, kElem>(xs, u0, nunits, cs, s, y, ss, ys, g);
       break;
     case kKvStatic:
-      if (full) fp8_tp_chunk<T, kKvStatic, false, kElem>(xs, u0, nunits, cs, s, y, ss, ys, g);
-      else fp8_tp_chunk<T, kKvStatic, true, kElem>(xs, u0, nunits, cs, s, y, ss, ys, g);
+      if (full) fp8_tp_chunk<T, U, kKvStatic, false, kElem>(xs, u0, nunits, cs, s, y, ss, ys, g);
+      else fp8_tp_chunk<T, U, kKvStatic, true, kElem>(xs, u0, nunits, cs, s, y, ss, ys, g);
       break;
     default:
-      if (full) fp8_tp_chunk<T, kKvLayer, false, kElem>(xs, u0, nunits, cs, s, y, ss, ys, g);
-      else fp8_tp_chunk<T, kKvLayer, true, kElem>(xs, u0, nunits, cs, s, y, ss, ys, g);
+      if (full) fp8_tp_chunk<T, U, kKvLayer, false, kElem>(xs, u0, nunits, cs, s, y, ss, ys, g);
+      else fp8_tp_chunk<T, U, kKvLayer, true, kElem>(xs, u0, nunits, cs, s, y, ss, ys, g);
   }
 }
 
-template <typename T>
+// kFold: `fin` holds the partials; each workgroup reduces its slice's own and
+// forms gs and the block-scale table as k_tp_finalize_nv does, and workgroup 0
+// of the slice writes gs.
+template <typename T, bool kFold, int U>
 __global__ __launch_bounds__(kBlockThreads) void k_tp_nv(TpArgs a, TpGeo g,
                                                          const float* __restrict__ fin) {
-  constexpr int U = kChunkUnr<T>;
   __shared__ NvTables tb;
+  __shared__ uint32_t red[kWgWaves];
   const int64_t b = blockIdx.y;
-  const float* f = fin + b * kNvFinal;
+  float gs, ygs;
   e2m1_lut_fill(tb.lut, 8);
-  for (int c = threadIdx.x; c < 127; c += kBlockThreads) {
-    tb.se[c] = f[kNvSe + c];
-    tb.ye[c] = f[kNvYe + c];
+  if constexpr (kFold) {
+    const uint32_t m = fold_partials(fin + b * g.W, g.W, red);
+    gs = as_f(max(m, kAmaxFloorBits)) / 2688.0f;  // 448 * 6, IEEE division
+    ygs = recip_rn(gs);
+    if (blockIdx.x == 0 && threadIdx.x == 0) a.gs[0][b] = gs;
+    for (int c = threadIdx.x; c < 127; c += kBlockThreads) {
+      const float sc = fmaxf(e4m3_decode((uint32_t)c), 1e-12f) * gs;
+      tb.se[c] = sc;
+      tb.ye[c] = 1.0f / sc;  // IEEE division
+    }
+  } else {
+    const float* f = fin + b * kNvFinal;
+    for (int c = threadIdx.x; c < 127; c += kBlockThreads) {
+      tb.se[c] = f[kNvSe + c];
+      tb.ye[c] = f[kNvYe + c];
+    }
+    gs = f[0];
+    ygs = f[1];
   }
-  const float gs = f[0], ygs = f[1];
   __syncthreads();
   const T* xs = reinterpret_cast<const T*>(a.x[0]) + b * g.per_slice;
   uint8_t* cs = a.codes[0] + b * (g.per_slice / 2);
@@ -317,7 +370,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_tp_nv(TpArgs a, TpGeo g,
 }
 
 int64_t wgs_per_slice(int64_t per_slice, bool bf16) {
-  const int64_t units_per_wg = (int64_t)(bf16 ? 8 : 4) * kWave * kWgWaves;
+  const int64_t units_per_wg = (int64_t)chunk_tiles(per_slice, bf16) * kWave * kWgWaves;
   const int64_t w = (per_slice / 8 + units_per_wg - 1) / units_per_wg;
   return w < 1 ? 1 : w;
 }
@@ -327,18 +380,34 @@ uint32_t head_magic(int64_t head_units) {
   return head_units == 1 ? 0u : (uint32_t)((0xFFFFFFFFull / (uint64_t)head_units) + 1);
 }
 
-hipError_t launch_tp(const TpArgs& a, int nt, bool bf16, const TpGeo& g, bool nv, float* ws,
-                     hipStream_t st, int elem = kE4M3) {
+template <typename T, int U>
+hipError_t launch_tp_t(const TpArgs& a, int nt, const TpGeo& g, bool nv, float* ws,
+                       hipStream_t st, int elem) {
   float* partials = ws;
   float* fin = ws + (int64_t)nt * g.slices * g.G * g.W;
   bool dynamic = false;
   for (int i = 0; i < nt; ++i) dynamic |= a.mode[i] != kKvStatic;
   const dim3 grid((unsigned)g.W, (unsigned)g.slices, (unsigned)nt);
+  // two launches (no finalize) when pass 2 can reduce the partials itself: no
+  // per-head scope (even with one head, pass 2 then reads per-head tables)
+  bool per_head = false;
+  for (int i = 0; i < nt; ++i) per_head |= a.mode[i] == kKvHead;
+  const bool fold = dynamic && !per_head && g.G == 1 && g.W <= kFoldMaxPartials;
+  if (fold) {
+    hipLaunchKernelGGL((k_tp_amax<T, U>), grid, dim3(kBlockThreads), 0, st, a, g, partials);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (nv) {
+      hipLaunchKernelGGL((k_tp_nv<T, true, U>), grid, dim3(kBlockThreads), 0, st, a, g, partials);
+      return hipGetLastError();
+    }
+    return with_elem(elem, [&](auto el) {
+      constexpr int E = decltype(el)::value;
+      hipLaunchKernelGGL((k_tp_fp8<T, E, true, U>), grid, dim3(kBlockThreads), 0, st, a, g, partials);
+    });
+  }
   if (dynamic) {
-    if (bf16)
-      hipLaunchKernelGGL(k_tp_amax<uint16_t>, grid, dim3(kBlockThreads), 0, st, a, g, partials);
-    else
-      hipLaunchKernelGGL(k_tp_amax<float>, grid, dim3(kBlockThreads), 0, st, a, g, partials);
+    hipLaunchKernelGGL((k_tp_amax<T, U>), grid, dim3(kBlockThreads), 0, st, a, g, partials);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (nv)
@@ -354,20 +423,24 @@ hipError_t launch_tp(const TpArgs& a, int nt, bool bf16, const TpGeo& g, bool nv
     if (e != hipSuccess) return e;
   }
   if (nv) {
-    if (bf16)
-      hipLaunchKernelGGL(k_tp_nv<uint16_t>, grid, dim3(kBlockThreads), 0, st, a, g, fin);
-    else
-      hipLaunchKernelGGL(k_tp_nv<float>, grid, dim3(kBlockThreads), 0, st, a, g, fin);
+    hipLaunchKernelGGL((k_tp_nv<T, false, U>), grid, dim3(kBlockThreads), 0, st, a, g, fin);
   } else {
     return with_elem(elem, [&](auto el) {
       constexpr int E = decltype(el)::value;
-      if (bf16)
-        hipLaunchKernelGGL((k_tp_fp8<uint16_t, E>), grid, dim3(kBlockThreads), 0, st, a, g, fin);
-      else
-        hipLaunchKernelGGL((k_tp_fp8<float, E>), grid, dim3(kBlockThreads), 0, st, a, g, fin);
+      hipLaunchKernelGGL((k_tp_fp8<T, E, false, U>), grid, dim3(kBlockThreads), 0, st, a, g, fin);
     });
   }
   return hipGetLastError();
+}
+
+hipError_t launch_tp(const TpArgs& a, int nt, bool bf16, const TpGeo& g, bool nv, float* ws,
+                     hipStream_t st, int elem = kE4M3) {
+  const bool half = chunk_tiles(g.per_slice, bf16) < (bf16 ? 8 : 4);
+  if (bf16)
+    return half ? launch_tp_t<uint16_t, 4>(a, nt, g, nv, ws, st, elem)
+                : launch_tp_t<uint16_t, 8>(a, nt, g, nv, ws, st, elem);
+  return half ? launch_tp_t<float, 2>(a, nt, g, nv, ws, st, elem)
+              : launch_tp_t<float, 4>(a, nt, g, nv, ws, st, elem);
 }
 
 }  // namespace
@@ -375,7 +448,8 @@ hipError_t launch_tp(const TpArgs& a, int nt, bool bf16, const TpGeo& g, bool nv
 size_t twopass_workspace_bytes(int ntensors, int64_t slices, int64_t per_slice, int64_t groups,
                                bool nv) {
   if (slices <= 0 || per_slice <= 0) return 0;
-  const int64_t W = wgs_per_slice(per_slice, false);  // float32 needs the most workgroups
+  const int64_t wf = wgs_per_slice(per_slice, false), wb = wgs_per_slice(per_slice, true);
+  const int64_t W = wf > wb ? wf : wb;  // the larger of the two input types' counts
   const int64_t fin = nv ? kNvFinal : groups;
   return 4 * (size_t)ntensors * (size_t)slices * ((size_t)groups * (size_t)W + (size_t)fin);
 }

@@ -269,6 +269,38 @@ def test_int4_full_chunks_edge_groups(pqb):
     same(pqb.dequantize(q), oracle.int4_dequantize(oc, os_, oz), "int4 edge groups dequant")
 
 
+@pytest.mark.parametrize("rows", [16384, 16385])
+def test_two_pass_fold_threshold(pqb, rows):
+    """Per-tensor FP8 and NVFP4 on bf16 [2, rows, 1024]: 16384 rows give 1024
+    pass-1 partials per slice, which pass 2 reduces itself (two launches);
+    16385 rows give 1025, which take the finalize launch.  Each slice has one
+    planted maximum, so the oracle on sampled rows plus the maximum's row sees
+    the slice's own tensor scale."""
+    cols = 1024
+    g = torch.Generator().manual_seed(rows)
+    x = torch.randn((2, rows, cols), generator=g)
+    maxpos = [(int(torch.randint(rows, (1,), generator=g)), int(torch.randint(cols, (1,), generator=g)))
+              for _ in range(2)]
+    for b, (r, c) in enumerate(maxpos):
+        x[b, r, c] = -40.0 if b else 40.0
+    x = x.to(torch.bfloat16)
+    xd = x.to(DEV)
+    qf = pqb.quantize(xd, "fp8_e4m3", "tensor")
+    qn = pqb.quantize(xd, "nvfp4")
+    fc, fs = qf.codes.reshape(2, rows, cols), qf.scales
+    nc, nb = qn.codes.reshape(2, rows, cols // 2), qn.scales.reshape(2, rows, cols // 16)
+    for b in range(2):
+        pick = sorted({int(i) for i in torch.randint(rows, (8,), generator=g)} | {maxpos[b][0]})
+        xs = x[b, pick].unsqueeze(0)
+        oc, os_ = oracle.fp8_quantize(xs, "tensor")
+        same(fs[b:b + 1], os_, f"fold {rows} fp8 scale {b}")
+        same(fc[b, pick], oc, f"fold {rows} fp8 codes {b}")
+        oc, ob, og = oracle.nvfp4_quantize(xs)
+        same(qn.aux[b:b + 1], og, f"fold {rows} nvfp4 gs {b}")
+        same(nc[b, pick], oc, f"fold {rows} nvfp4 codes {b}")
+        same(nb[b, pick], ob, f"fold {rows} nvfp4 block scales {b}")
+
+
 # ---------------------------------------------------------------- KV -------
 
 def test_kv_write_parity(pqb):
