@@ -115,6 +115,24 @@ class Engine:
         if rc != 0:
             raise RuntimeError(f"pqb_dequantize {fmt}/{gran}: status {rc}")
 
+    def dq_jobs(self, items):
+        """A prebuilt pqb_dq_job array for `items` = [(buf, fmt, gran, shape, out)]."""
+        J = self.pqb.pqb._DqJob
+        arr = (J * len(items))()
+        for j, (buf, fmt, gran, shape, out) in zip(arr, items):
+            j.codes, j.scales = buf["codes"].data_ptr(), buf["scales"].data_ptr()
+            j.aux = buf["aux"].data_ptr() if buf["aux"] is not None else None
+            j.out = out.data_ptr()
+            j.batch, j.rows, j.cols = shape
+            j.fmt, j.gran = self.pqb.FORMATS[fmt], self.pqb.GRANS[gran]
+            j.out_dtype = 1 if out.dtype == self.torch.bfloat16 else 0
+        return arr, len(items)
+
+    def dequantize_batch(self, jobs):
+        rc = self.L.pqb_dequantize_batch(jobs[0], jobs[1], self.stream)
+        if rc != 0:
+            raise RuntimeError(f"pqb_dequantize_batch: status {rc}")
+
     def kv(self, k, v, kc, vc, ks, vs, ws):
         P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
         layers = k.shape[0]

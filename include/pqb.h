@@ -58,7 +58,11 @@
  *                                                 byte over the flat group
  *                                                 index (ceil(b*r*c/256) bytes)
  * 4-bit codes: element 2i in the low nibble of byte i.  INT4 codes and
- * zero-points are two's-complement nibbles; dequant is (q - z) * s.
+ * zero-points are two's-complement nibbles; dequant is (q - z) * s.  INT4
+ * also needs each group's range max(0, max x) - min(0, min x) to be finite in
+ * float32 (values of both signs beyond about +-1.7e38 in one group overflow
+ * it); such a group's codes, scale and zero-point are unspecified, and no
+ * other group is affected.
  *
  * Shape rules: 1x128 and GRP_128 need c % 128 == 0; 128x128 needs c % 128 == 0
  * and r <= 128 or r % 128 == 0; BLK_32 needs c % 32 == 0; BLK_16 needs
@@ -195,6 +199,32 @@ int64_t pqb_quantize_batch_launches(const pqb_job* jobs, int64_t njobs);
 pqb_status pqb_dequantize(const void* codes, const void* scales, const void* aux, pqb_format fmt,
                           pqb_gran gran, int64_t batch, int64_t rows, int64_t cols,
                           pqb_dtype out_dtype, void* out, void* stream);
+
+/* One tensor of a fused dequantization batch: the arguments of one
+ * pqb_dequantize call. */
+typedef struct pqb_dq_job {
+  const void* codes;  /* codes, scales and aux as pqb_quantize wrote them */
+  const void* scales;
+  const void* aux;    /* INT4 zero-points or NVFP4 tensor scales; NULL otherwise */
+  void* out;          /* [batch, rows, cols] of out_dtype */
+  int64_t batch, rows, cols;
+  int32_t fmt;        /* pqb_format */
+  int32_t gran;       /* pqb_gran */
+  int32_t out_dtype;  /* pqb_dtype */
+  int32_t reserved;   /* must be 0 (else PQB_ERR_ENUM) */
+} pqb_dq_job;
+
+/* Dequantize several tensors with as few launches as possible: FP8 E4M3 / E5M2
+ * 1x128, MXFP4, MXFP8, NVFP4 (each batch slice counts as one job) and INT4
+ * jobs share fused launches of up to 72 jobs, one kernel per output dtype;
+ * the other scopes (FP8 / E5M2 / INT8 per tensor and per row, FP8 128x128)
+ * get a pqb_dequantize launch each.  Each job's output is exactly that of
+ * pqb_dequantize on the same arguments.  Every job is validated (same rules
+ * and codes as pqb_dequantize) and the fused launches are planned before
+ * anything is enqueued; a launch that would exceed 2^32 - 1 threads returns
+ * PQB_ERR_SHAPE.  Outputs must not overlap each other or any input.  `jobs`
+ * is a host array and may be reused once the call returns. */
+pqb_status pqb_dequantize_batch(const pqb_dq_job* jobs, int64_t njobs, void* stream);
 
 /* FP8 KV-cache write: K and V are [layers, elems_per_layer] of `dtype`.  Each
  * (layer, K) and (layer, V) slice gets its own per-tensor FP8 scale (written
@@ -425,6 +455,10 @@ pqb_status pqb_check_div(const float* s, int64_t ns, uint32_t x_first_bits, int6
 
 const char* pqb_status_string(pqb_status s);
 int pqb_abi_version(void);
+/* A digest of the sources the library was built from (16 hex digits; the
+ * build computes it over csrc/ and this header), so that a loader can refuse
+ * a library that no longer matches its sources. */
+const char* pqb_source_hash(void);
 
 #ifdef __cplusplus
 }

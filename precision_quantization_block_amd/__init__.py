@@ -11,7 +11,7 @@ the C ABI in include/pqb.h.  The binding is loaded on first use so that the inpu
 generators in `synth` import without the engine.
 """
 _EXPORTS = {
-    "quantize", "quantize_batch", "dequantize", "query_sizes", "kv_write_fp8", "kv_write_fp8_ex",
+    "quantize", "quantize_batch", "dequantize", "dequantize_batch", "query_sizes", "kv_write_fp8", "kv_write_fp8_ex",
     "KV_MODES", "kv_write_kivi", "kv_read_kivi", "kivi_layouts", "gemm_fp8_blockscaled", "gemm_fp8_blockscaled_quant",
     "gemv_w4a16", "gemv_w4a16_batch", "gemm_w4a16", "gemm_w4a16_batch", "gemm_mxfp4", "encode_e4m3", "encode_e5m2", "encode_e2m1",
     "check_recip", "check_div",

@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import concurrent.futures
 import glob
+import hashlib
 import os
 import shutil
 import subprocess
@@ -36,14 +37,30 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+def source_hash() -> str:
+    """First 16 hex digits of the SHA-256 over every file of csrc/ and the ABI
+    header (names and contents), compiled into libpqb.so so that a library can
+    be checked against the sources beside it."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(CSRC, "*"))) + [os.path.join(ROOT, "include", "pqb.h")]
+    for p in files:
+        if os.path.isfile(p):
+            h.update(os.path.basename(p).encode())
+            with open(p, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def build(verbose: bool = False, jobs: int = 8) -> str:
     """Compile every source and link libpqb.so; returns the library path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = sources()
 
+    digest = source_hash()
+
     def compile_one(src):
         obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-        cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+        cmd = [HIPCC, *FLAGS, f'-DPQB_SOURCE_HASH="{digest}"', "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)

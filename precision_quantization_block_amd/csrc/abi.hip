@@ -177,6 +177,11 @@ extern "C" {
 
 int pqb_abi_version(void) { return PQB_ABI_VERSION; }
 
+#ifndef PQB_SOURCE_HASH
+#define PQB_SOURCE_HASH "unknown"
+#endif
+const char* pqb_source_hash(void) { return PQB_SOURCE_HASH; }
+
 const char* pqb_status_string(pqb_status s) {
   switch (s) {
     case PQB_OK: return "ok";
@@ -371,15 +376,15 @@ pqb_status pqb_quantize_batch(const pqb_job* jobs, int64_t njobs, void* stream) 
   return PQB_OK;
 }
 
-pqb_status pqb_dequantize(const void* codes, const void* scales, const void* aux, pqb_format fmt,
-                          pqb_gran gran, int64_t batch, int64_t rows, int64_t cols,
-                          pqb_dtype out_dtype, void* out, void* stream) {
+// Validation shared by pqb_dequantize and pqb_dequantize_batch.
+static pqb_status check_dequantize(const void* codes, const void* scales, const void* aux, int fmt,
+                                   int gran, int64_t batch, int64_t rows, int64_t cols,
+                                   int out_dtype, const void* out) {
   if (!valid_dtype(out_dtype) || !known_format(fmt) || !known_gran(gran)) return PQB_ERR_ENUM;
   if (!valid_pair(fmt, gran)) return PQB_ERR_COMBO;
-  pqb_status st = check_shape(fmt, gran, batch, rows, cols);
+  const pqb_status st = check_shape(fmt, gran, batch, rows, cols);
   if (st != PQB_OK) return st;
-  const int64_t n = batch * rows * cols;
-  if (n == 0) return PQB_OK;
+  if (batch * rows * cols == 0) return PQB_OK;
   const pqb_sizes need = sizes_of(fmt, gran, batch, rows, cols);
   if (!codes || !scales || !out || (need.aux && !aux)) return PQB_ERR_NULL;
   if (!aligned(codes, 16) || !aligned(out, 16)) return PQB_ERR_ALIGN;
@@ -387,6 +392,17 @@ pqb_status pqb_dequantize(const void* codes, const void* scales, const void* aux
   if (fmt == PQB_INT4_ASYM && !aligned(scales, 2)) return PQB_ERR_ALIGN;
   if (fmt == PQB_NVFP4 && !aligned(aux, 4)) return PQB_ERR_ALIGN;
   if (one_byte(fmt) && batch * rows > 0 && (cols > 0x7FFFFFFF)) return PQB_ERR_SHAPE;
+  return PQB_OK;
+}
+
+pqb_status pqb_dequantize(const void* codes, const void* scales, const void* aux, pqb_format fmt,
+                          pqb_gran gran, int64_t batch, int64_t rows, int64_t cols,
+                          pqb_dtype out_dtype, void* out, void* stream) {
+  const pqb_status st =
+      check_dequantize(codes, scales, aux, fmt, gran, batch, rows, cols, out_dtype, out);
+  if (st != PQB_OK) return st;
+  const int64_t n = batch * rows * cols;
+  if (n == 0) return PQB_OK;
   const bool bf16 = out_dtype == PQB_BF16;
   hipStream_t s = (hipStream_t)stream;
   switch (fmt) {
@@ -410,6 +426,71 @@ pqb_status pqb_dequantize(const void* codes, const void* scales, const void* aux
                                             (const uint8_t*)aux, n, bf16, out, s));
   }
   return PQB_ERR_ENUM;
+}
+
+// The fused kind of a dequantization job, or -1 for the scopes that keep a
+// launch of their own (FP8 / E5M2 / INT8 per tensor, per row, 128x128).
+static int dq_kind_of(int fmt, int gran) {
+  switch (fmt) {
+    case PQB_FP8_E4M3: return gran == PQB_BLK_1x128 ? kDqFp8 : -1;
+    case PQB_FP8_E5M2: return gran == PQB_BLK_1x128 ? kDqE5m2 : -1;
+    case PQB_MXFP4: return kDqMx4;
+    case PQB_MXFP8: return kDqMx8;
+    case PQB_NVFP4: return kDqNv;
+    case PQB_INT4_ASYM: return kDqInt4;
+  }
+  return -1;
+}
+
+pqb_status pqb_dequantize_batch(const pqb_dq_job* jobs, int64_t njobs, void* stream) {
+  if (njobs < 0) return PQB_ERR_SHAPE;
+  if (njobs == 0) return PQB_OK;
+  if (!jobs) return PQB_ERR_NULL;
+  std::vector<DqMultiJob> fused;
+  std::vector<int64_t> own;
+  for (int64_t i = 0; i < njobs; ++i) {
+    const pqb_dq_job& j = jobs[i];
+    if (j.reserved != 0) return PQB_ERR_ENUM;
+    const pqb_status st = check_dequantize(j.codes, j.scales, j.aux, j.fmt, j.gran, j.batch,
+                                           j.rows, j.cols, j.out_dtype, j.out);
+    if (st != PQB_OK) return st;
+  }
+  for (int64_t i = 0; i < njobs; ++i) {
+    const pqb_dq_job& j = jobs[i];
+    const int64_t n = j.batch * j.rows * j.cols;
+    if (n == 0) continue;
+    const int kind = dq_kind_of(j.fmt, j.gran);
+    if (kind < 0) {
+      own.push_back(i);
+      continue;
+    }
+    const bool bf16 = j.out_dtype == PQB_BF16;
+    if (kind == kDqNv) {  // one job per slice, each with its own tensor scale
+      const int64_t per = j.rows * j.cols;
+      const size_t ob = bf16 ? 2 : 4;
+      for (int64_t b = 0; b < j.batch; ++b)
+        fused.push_back(DqMultiJob{(const uint8_t*)j.codes + b * (per / 2),
+                                   (const uint8_t*)j.scales + b * (per / 16),
+                                   (const float*)j.aux + b, (uint8_t*)j.out + (size_t)(b * per) * ob,
+                                   per / 8, kind, bf16});
+    } else {
+      fused.push_back(DqMultiJob{(const uint8_t*)j.codes, j.scales, j.aux, j.out, n / 8, kind,
+                                 bf16});
+    }
+  }
+  if (!fused.empty() && dq_multi_launches(fused.data(), (int)fused.size()) < 0)
+    return PQB_ERR_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  if (!fused.empty() && launch_dq_multi(fused.data(), (int)fused.size(), s) != hipSuccess)
+    return PQB_ERR_HIP;
+  for (const int64_t i : own) {
+    const pqb_dq_job& j = jobs[i];
+    const pqb_status st = pqb_dequantize(j.codes, j.scales, j.aux, (pqb_format)j.fmt,
+                                         (pqb_gran)j.gran, j.batch, j.rows, j.cols,
+                                         (pqb_dtype)j.out_dtype, j.out, stream);
+    if (st != PQB_OK) return st;
+  }
+  return PQB_OK;
 }
 
 size_t pqb_kv_workspace_bytes(int64_t layers, int64_t elems_per_layer) {

@@ -7,6 +7,8 @@
 // for float32) each cover one contiguous range, so every store instruction
 // writes whole 1 KiB (2 KiB) spans.  All loads of the chunk are issued before
 // the first store.  Outputs are float32 or RNE bf16.
+#include <vector>
+
 #include "launch.h"
 #include "quant.h"
 
@@ -16,10 +18,12 @@ namespace {
 constexpr int kDqTiles = 4;
 constexpr int kDqWaves = kBlockThreads / kWave;
 
-// Unit of this lane in tile 0 of its wave's chunk.
-__device__ __forceinline__ int64_t dq_unit0() {
+// Unit of this lane in tile 0 of its wave's chunk, for workgroup `blk` of a
+// job (blockIdx.x in the single-tensor kernels, the job-local index in the
+// batch kernel).
+__device__ __forceinline__ int64_t dq_unit0(int64_t blk) {
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
-  return ((int64_t)blockIdx.x * kDqWaves + wave) * kDqTiles * kWave + (threadIdx.x & (kWave - 1));
+  return (blk * kDqWaves + wave) * kDqTiles * kWave + (threadIdx.x & (kWave - 1));
 }
 
 int dq_grid(int64_t nunits) {
@@ -30,11 +34,10 @@ int dq_grid(int64_t nunits) {
 
 // FP8 1x128: unit u's scale is u / 16.
 template <bool kBf16Out, int kElem>
-__global__ __launch_bounds__(kBlockThreads) void k_dq_fp8_1x128(const uint8_t* __restrict__ codes,
-                                                                const float* __restrict__ scales,
-                                                                int64_t nunits,
-                                                                void* __restrict__ out) {
-  const int64_t u0 = dq_unit0();
+__device__ __forceinline__ void dq_fp8_1x128_body(int64_t blk, const uint8_t* __restrict__ codes,
+                                                  const float* __restrict__ scales, int64_t nunits,
+                                                  void* __restrict__ out) {
+  const int64_t u0 = dq_unit0(blk);
   uint2 c[kDqTiles];
   float s[kDqTiles];
 #pragma unroll
@@ -86,11 +89,10 @@ __device__ __forceinline__ void mx_expand8(uint32_t w, float s, void* out, int64
 
 // MXFP4: unit u is a quarter of block u / 4; +-V * 2^(e - 127) is exact.
 template <bool kBf16Out>
-__global__ __launch_bounds__(kBlockThreads) void k_dq_mxfp4(const uint8_t* __restrict__ codes,
-                                                            const uint8_t* __restrict__ scales,
-                                                            int64_t nunits,
-                                                            void* __restrict__ out) {
-  const int64_t u0 = dq_unit0();
+__device__ __forceinline__ void dq_mxfp4_body(int64_t blk, const uint8_t* __restrict__ codes,
+                                              const uint8_t* __restrict__ scales, int64_t nunits,
+                                              void* __restrict__ out) {
+  const int64_t u0 = dq_unit0(blk);
   uint32_t c[kDqTiles], e[kDqTiles];
 #pragma unroll
   for (int k = 0; k < kDqTiles; ++k) {
@@ -111,11 +113,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_dq_mxfp4(const uint8_t* __res
 
 // MXFP8: unit u is a quarter of block u / 4; dec(code) * 2^(e - 127) is exact.
 template <bool kBf16Out>
-__global__ __launch_bounds__(kBlockThreads) void k_dq_mxfp8(const uint8_t* __restrict__ codes,
-                                                            const uint8_t* __restrict__ scales,
-                                                            int64_t nunits,
-                                                            void* __restrict__ out) {
-  const int64_t u0 = dq_unit0();
+__device__ __forceinline__ void dq_mxfp8_body(int64_t blk, const uint8_t* __restrict__ codes,
+                                              const uint8_t* __restrict__ scales, int64_t nunits,
+                                              void* __restrict__ out) {
+  const int64_t u0 = dq_unit0(blk);
   uint2 c[kDqTiles];
   uint32_t e[kDqTiles];
 #pragma unroll
@@ -142,15 +143,13 @@ __global__ __launch_bounds__(kBlockThreads) void k_dq_mxfp8(const uint8_t* __res
 // FP4 conversion at scale 1, which returns +-V exactly (signed zeros
 // included), and each value is then multiplied by the element scale: one
 // rounding, as V * s.
+// (base: the slice's first unit; g its tensor scale)
 template <bool kBf16Out>
-__global__ __launch_bounds__(kBlockThreads) void k_dq_nvfp4(const uint8_t* __restrict__ codes,
-                                                            const uint8_t* __restrict__ scales,
-                                                            const float* __restrict__ gs,
-                                                            int64_t per_slice,
-                                                            void* __restrict__ out) {
-  const int64_t b = blockIdx.y, nunits = per_slice / 8, base = b * nunits;
-  const float g = gs[b];
-  const int64_t u0 = dq_unit0();
+__device__ __forceinline__ void dq_nvfp4_body(int64_t blk, const uint8_t* __restrict__ codes,
+                                              const uint8_t* __restrict__ scales, float g,
+                                              int64_t nunits, int64_t base,
+                                              void* __restrict__ out) {
+  const int64_t u0 = dq_unit0(blk);
   uint32_t c[kDqTiles], bs[kDqTiles];
 #pragma unroll
   for (int k = 0; k < kDqTiles; ++k) {
@@ -234,17 +233,16 @@ __device__ __forceinline__ void dq_int4_chunk(const uint8_t* __restrict__ codes,
 // A full chunk has no per-lane bound, so no branch lets the compiler sink a
 // load next to its use; only the chunk holding the end takes the guarded form.
 template <bool kBf16Out>
-__global__ __launch_bounds__(kBlockThreads) void k_dq_int4(const uint8_t* __restrict__ codes,
-                                                           const uint16_t* __restrict__ scales,
-                                                           const uint8_t* __restrict__ zeros,
-                                                           int64_t nunits,
-                                                           void* __restrict__ out) {
+__device__ __forceinline__ void dq_int4_body(int64_t blk, const uint8_t* __restrict__ codes,
+                                             const uint16_t* __restrict__ scales,
+                                             const uint8_t* __restrict__ zeros, int64_t nunits,
+                                             void* __restrict__ out) {
   if (nunits <= 0) return;
   if constexpr (!kBf16Out) {
     // float32 output: each unit's scale and zero-point gathered per tile.  The
     // chunked form above gave the same bytes but took this output on 1 GiB
     // from 610 to 901 us, so it serves bf16 output only.
-    const int64_t v0 = dq_unit0();
+    const int64_t v0 = dq_unit0(blk);
     uint32_t c[kDqTiles], sb[kDqTiles], zb[kDqTiles];
 #pragma unroll
     for (int k = 0; k < kDqTiles; ++k) {
@@ -273,12 +271,164 @@ __global__ __launch_bounds__(kBlockThreads) void k_dq_int4(const uint8_t* __rest
     return;
   }
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
-  const int64_t wave_u0 = ((int64_t)blockIdx.x * kDqWaves + wave) * kDqTiles * kWave;  // uniform
+  const int64_t wave_u0 = (blk * kDqWaves + wave) * kDqTiles * kWave;  // uniform
   const int64_t u0 = wave_u0 + (threadIdx.x & (kWave - 1));
   if (wave_u0 + kDqTiles * kWave <= nunits)
     dq_int4_chunk<false>(codes, scales, zeros, nunits, u0, out);
   else
     dq_int4_chunk<true>(codes, scales, zeros, nunits, u0, out);
+}
+
+// Single-tensor kernels: one body call per workgroup.
+template <bool kBf16Out, int kElem>
+__global__ __launch_bounds__(kBlockThreads) void k_dq_fp8_1x128(const uint8_t* __restrict__ codes,
+                                                                const float* __restrict__ scales,
+                                                                int64_t nunits,
+                                                                void* __restrict__ out) {
+  dq_fp8_1x128_body<kBf16Out, kElem>(blockIdx.x, codes, scales, nunits, out);
+}
+
+template <bool kBf16Out>
+__global__ __launch_bounds__(kBlockThreads) void k_dq_mxfp4(const uint8_t* __restrict__ codes,
+                                                            const uint8_t* __restrict__ scales,
+                                                            int64_t nunits,
+                                                            void* __restrict__ out) {
+  dq_mxfp4_body<kBf16Out>(blockIdx.x, codes, scales, nunits, out);
+}
+
+template <bool kBf16Out>
+__global__ __launch_bounds__(kBlockThreads) void k_dq_mxfp8(const uint8_t* __restrict__ codes,
+                                                            const uint8_t* __restrict__ scales,
+                                                            int64_t nunits,
+                                                            void* __restrict__ out) {
+  dq_mxfp8_body<kBf16Out>(blockIdx.x, codes, scales, nunits, out);
+}
+
+// NVFP4, slice b = blockIdx.y.
+template <bool kBf16Out>
+__global__ __launch_bounds__(kBlockThreads) void k_dq_nvfp4(const uint8_t* __restrict__ codes,
+                                                            const uint8_t* __restrict__ scales,
+                                                            const float* __restrict__ gs,
+                                                            int64_t per_slice,
+                                                            void* __restrict__ out) {
+  const int64_t b = blockIdx.y, nunits = per_slice / 8;
+  dq_nvfp4_body<kBf16Out>(blockIdx.x, codes, scales, gs[b], nunits, b * nunits, out);
+}
+
+template <bool kBf16Out>
+__global__ __launch_bounds__(kBlockThreads) void k_dq_int4(const uint8_t* __restrict__ codes,
+                                                           const uint16_t* __restrict__ scales,
+                                                           const uint8_t* __restrict__ zeros,
+                                                           int64_t nunits,
+                                                           void* __restrict__ out) {
+  dq_int4_body<kBf16Out>(blockIdx.x, codes, scales, zeros, nunits, out);
+}
+
+// Fused dequantization of several tensors (pqb_dequantize_batch), one launch
+// per output type and up to kMaxBatchJobs jobs: every job gets a contiguous
+// range of workgroups, a workgroup finds its job by binary search over the
+// prefix table (uniform) and runs that job's body with its local index.  An
+// NVFP4 job is one slice (the host splits a batch of slices), its tensor scale
+// read through `aux`.
+struct DqJob {
+  const uint8_t* codes;
+  const void* scales;
+  const void* aux;   // INT4 zero-points; NVFP4: the slice's tensor scale
+  void* out;
+  int64_t nunits;
+  uint32_t kind;
+  uint32_t pad;
+};
+struct DqArgs {
+  int32_t njobs;
+  int32_t pad;
+  int64_t wg_begin[kMaxBatchJobs + 1];
+  DqJob job[kMaxBatchJobs];
+};
+static_assert(sizeof(DqArgs) <= 4096, "kernel arguments must stay within 4 KiB");
+
+template <bool kBf16Out>
+__global__ __launch_bounds__(kBlockThreads) void k_dq_multi(DqArgs a) {
+  const int64_t wg = blockIdx.x;
+  int lo = 0, hi = a.njobs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.wg_begin[mid] <= wg)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  const DqJob& jb = a.job[lo];
+  const int64_t local = wg - a.wg_begin[lo];
+  switch (jb.kind) {
+    case kDqFp8:
+      dq_fp8_1x128_body<kBf16Out, kE4M3>(local, jb.codes, (const float*)jb.scales, jb.nunits,
+                                          jb.out);
+      break;
+    case kDqE5m2:
+      dq_fp8_1x128_body<kBf16Out, kE5M2>(local, jb.codes, (const float*)jb.scales, jb.nunits,
+                                          jb.out);
+      break;
+    case kDqMx4:
+      dq_mxfp4_body<kBf16Out>(local, jb.codes, (const uint8_t*)jb.scales, jb.nunits, jb.out);
+      break;
+    case kDqMx8:
+      dq_mxfp8_body<kBf16Out>(local, jb.codes, (const uint8_t*)jb.scales, jb.nunits, jb.out);
+      break;
+    case kDqNv:
+      dq_nvfp4_body<kBf16Out>(local, jb.codes, (const uint8_t*)jb.scales,
+                              *(const float*)jb.aux, jb.nunits, 0, jb.out);
+      break;
+    default:
+      dq_int4_body<kBf16Out>(local, jb.codes, (const uint16_t*)jb.scales,
+                             (const uint8_t*)jb.aux, jb.nunits, jb.out);
+  }
+}
+
+struct DqLaunch {
+  bool bf16;
+  int64_t wgs;
+  DqArgs args;
+};
+
+// Jobs of one output type into launches of at most kMaxBatchJobs, as even in
+// job count as possible; false if a launch would exceed 2^32 - 1 threads.
+bool plan_dq(const std::vector<const DqMultiJob*>& jobs, bool bf16, std::vector<DqLaunch>& out) {
+  const size_t n = jobs.size();
+  if (n == 0) return true;
+  const size_t nl = (n + kMaxBatchJobs - 1) / kMaxBatchJobs, per = (n + nl - 1) / nl;
+  const int64_t per_wg = (int64_t)kDqTiles * kWave * kDqWaves;
+  for (size_t base = 0; base < n; base += per) {
+    const int cnt = (int)(n - base < per ? n - base : per);
+    DqLaunch L;
+    L.bf16 = bf16;
+    L.args = DqArgs{};
+    L.args.njobs = cnt;
+    int64_t wg = 0;
+    for (int i = 0; i < cnt; ++i) {
+      const DqMultiJob& m = *jobs[base + i];
+      DqJob& j = L.args.job[i];
+      j.codes = m.codes;
+      j.scales = m.scales;
+      j.aux = m.aux;
+      j.out = m.out;
+      j.nunits = m.nunits;
+      j.kind = (uint32_t)m.kind;
+      L.args.wg_begin[i] = wg;
+      wg += (m.nunits + per_wg - 1) / per_wg;
+    }
+    L.args.wg_begin[cnt] = wg;
+    L.wgs = wg;
+    if (wg > (int64_t)(0xFFFFFFFFu / (uint32_t)kBlockThreads)) return false;
+    if (wg > 0) out.push_back(L);
+  }
+  return true;
+}
+
+bool plan_dq_all(const DqMultiJob* jobs, int njobs, std::vector<DqLaunch>& out) {
+  std::vector<const DqMultiJob*> by[2];
+  for (int i = 0; i < njobs; ++i) by[jobs[i].bf16_out ? 1 : 0].push_back(&jobs[i]);
+  return plan_dq(by[0], false, out) && plan_dq(by[1], true, out);
 }
 
 }  // namespace
@@ -344,6 +494,32 @@ hipError_t launch_int4_dequant(const uint8_t* codes, const uint16_t* scales, con
     hipLaunchKernelGGL(k_dq_int4<false>, dim3(dq_grid(nl)), dim3(kBlockThreads), 0, st, codes,
                        scales, zeros, nl, out);
   return hipGetLastError();
+}
+
+}  // namespace pqb
+
+namespace pqb {
+
+int64_t dq_multi_launches(const DqMultiJob* jobs, int njobs) {
+  std::vector<DqLaunch> plan;
+  if (!plan_dq_all(jobs, njobs, plan)) return -1;
+  return (int64_t)plan.size();
+}
+
+hipError_t launch_dq_multi(const DqMultiJob* jobs, int njobs, hipStream_t st) {
+  std::vector<DqLaunch> plan;
+  if (!plan_dq_all(jobs, njobs, plan)) return hipErrorInvalidConfiguration;
+  for (const DqLaunch& L : plan) {
+    if (L.bf16)
+      hipLaunchKernelGGL(k_dq_multi<true>, dim3((unsigned)L.wgs), dim3(kBlockThreads), 0, st,
+                         L.args);
+    else
+      hipLaunchKernelGGL(k_dq_multi<false>, dim3((unsigned)L.wgs), dim3(kBlockThreads), 0, st,
+                         L.args);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace pqb

@@ -78,6 +78,24 @@ struct MultiJob {
 int64_t multi_launches(const MultiJob* jobs, int njobs);
 hipError_t launch_multi(const MultiJob* jobs, int njobs, hipStream_t st);
 
+// ---- fused multi-tensor dequantization (k_dequant.hip) ---------------------
+// Flat formats only: FP8 E4M3 / E5M2 1x128, MXFP4, MXFP8, one NVFP4 slice
+// (aux = its tensor scale), INT4 (aux = zero-points); n = elements / 8.
+enum DqKind { kDqFp8 = 0, kDqE5m2 = 1, kDqMx4 = 2, kDqMx8 = 3, kDqNv = 4, kDqInt4 = 5 };
+struct DqMultiJob {
+  const uint8_t* codes;
+  const void* scales;
+  const void* aux;
+  void* out;
+  int64_t nunits;
+  int kind;
+  bool bf16_out;
+};
+// Launches the jobs take, or -1 if one would exceed 2^32 - 1 threads
+// (launch_dq_multi then enqueues nothing and returns hipErrorInvalidConfiguration).
+int64_t dq_multi_launches(const DqMultiJob* jobs, int njobs);
+hipError_t launch_dq_multi(const DqMultiJob* jobs, int njobs, hipStream_t st);
+
 // ---- two-pass formats (k_twopass.hip) -------------------------------------
 // Chunked pass 1 -> finalize -> pass 2 for slices whose length is a multiple
 // of 8.  Workspace: twopass_workspace_bytes(); contents on entry do not matter.

@@ -45,6 +45,13 @@ class _Job(ctypes.Structure):
                 ("gran", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
+class _DqJob(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("aux", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("batch", ctypes.c_int64), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64), ("fmt", ctypes.c_int32), ("gran", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
 class _W4Job(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("zeros", ctypes.c_void_p), ("y", ctypes.c_void_p), ("n", ctypes.c_int64),
@@ -64,12 +71,15 @@ def lib():
             raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
         L = ctypes.CDLL(LIB_PATH)
         P, I64, I, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+        L.pqb_source_hash.restype = ctypes.c_char_p
+        check_source_hash(L)
         L.pqb_abi_version.restype = I
         L.pqb_status_string.argtypes, L.pqb_status_string.restype = [I], ctypes.c_char_p
         L.pqb_query_sizes.argtypes = [I, I, I64, I64, I64, ctypes.POINTER(_Sizes)]
         L.pqb_quantize.argtypes = [P, I, I64, I64, I64, I, I, P, P, P, P, SZ, P]
         L.pqb_quantize_noalloc.argtypes = [P, I, I64, I64, I64, I, I, P, P, P, P]
         L.pqb_dequantize.argtypes = [P, P, P, I, I, I64, I64, I64, I, P, P]
+        L.pqb_dequantize_batch.argtypes = [ctypes.POINTER(_DqJob), I64, P]
         L.pqb_quantize_batch.argtypes = [ctypes.POINTER(_Job), I64, P]
         L.pqb_quantize_batch_launches.argtypes = [ctypes.POINTER(_Job), I64]
         L.pqb_quantize_batch_launches.restype = I64
@@ -93,7 +103,7 @@ def lib():
         L.pqb_check_recip.argtypes = [ctypes.c_uint32, I64, P, P]
         L.pqb_check_div.argtypes = [P, I64, ctypes.c_uint32, I64, P, P]
         for f in ("pqb_query_sizes", "pqb_quantize", "pqb_quantize_noalloc", "pqb_quantize_batch",
-                  "pqb_dequantize",
+                  "pqb_dequantize", "pqb_dequantize_batch",
                   "pqb_kv_write_fp8", "pqb_kv_write_fp8_ex", "pqb_kv_write_kivi",
                   "pqb_kv_read_kivi", "pqb_gemm_fp8_blockscaled",
                   "pqb_gemm_fp8_blockscaled_quant", "pqb_gemv_w4a16",
@@ -104,6 +114,18 @@ def lib():
             getattr(L, f).restype = I
         _lib = L
     return _lib
+
+
+def check_source_hash(L) -> None:
+    """Refuse a libpqb.so built from other sources than the csrc/ beside it
+    (a stale build would run old kernels without any sign of it)."""
+    from . import _build
+    if not os.path.isdir(_build.CSRC):
+        return
+    built, here = L.pqb_source_hash().decode(), _build.source_hash()
+    if built != here:
+        raise RuntimeError(f"{LIB_PATH} was built from other sources (hash {built}, sources now "
+                           f"{here}); rebuild it with __graft_entry__.build()")
 
 
 def status_string(status: int) -> str:
@@ -237,6 +259,27 @@ def dequantize(q: Quantized, out_dtype=torch.float32) -> torch.Tensor:
                                 BF16 if out_dtype == torch.bfloat16 else F32, _ptr(out),
                                 _stream(out.device)), "dequantize")
     return out
+
+
+def dequantize_batch(items) -> list:
+    """Dequantize several Quantized results with fused launches.  `items`:
+    sequence of Quantized or (Quantized, out_dtype) pairs (float32 by default).
+    Returns one tensor per item, identical to dequantize() on each."""
+    outs, jobs, dev = [], [], None
+    for it in items:
+        q, out_dtype = (it, torch.float32) if isinstance(it, Quantized) else (it[0], it[1])
+        b, r, c = q.shape
+        out = torch.empty((b, r, c), dtype=out_dtype, device=q.codes.device)
+        dev = out.device
+        outs.append(out)
+        jobs.append(_DqJob(_ptr(q.codes), _ptr(q.scales), _ptr(q.aux), _ptr(out), b, r, c,
+                           _fmt(q.fmt), _gran(q.gran), BF16 if out_dtype == torch.bfloat16 else F32,
+                           0))
+    if not jobs:
+        return []
+    arr = (_DqJob * len(jobs))(*jobs)
+    _check(lib().pqb_dequantize_batch(arr, len(jobs), _stream(dev)), "dequantize_batch")
+    return outs
 
 
 def kv_write_fp8(k: torch.Tensor, v: torch.Tensor, workspace: torch.Tensor | None = None):

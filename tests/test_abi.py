@@ -33,6 +33,17 @@ def test_library_exports_every_declared_symbol(L):
     assert pqb.abi_version() == 1
 
 
+def test_source_hash_is_checked(L, monkeypatch):
+    """The library carries the digest of the sources it was built from, and the
+    binding refuses one that no longer matches them."""
+    from precision_quantization_block_amd import _build
+    assert L.pqb_source_hash().decode() == _build.source_hash()
+    pqb.pqb.check_source_hash(L)
+    monkeypatch.setattr(_build, "source_hash", lambda: "0000000000000000")
+    with pytest.raises(RuntimeError, match="other sources"):
+        pqb.pqb.check_source_hash(L)
+
+
 def test_status_strings(L):
     for code in range(0, -9, -1):
         assert pqb.status_string(code) not in ("", "unknown status")
@@ -243,6 +254,31 @@ def test_quantize_noalloc_errors_before_launch(L):
     assert P(fake, 1, 1, 8, 128, 9, 0, fake, fake, None, None) == -2
     assert P(fake, 1, 1, 0, 128, 0, 0, None, None, None, None) == 0               # empty
     assert pqb.status_string(-8) != "unknown status"
+
+
+def test_dequantize_batch_errors_before_launch(L):
+    J = pqb.pqb._DqJob
+    fake = 0x10000
+
+    def job(**kw):
+        d = dict(codes=fake, scales=fake, aux=None, out=fake, batch=1, rows=128, cols=256, fmt=0,
+                 gran=2, out_dtype=1, reserved=0)
+        d.update(kw)
+        return J(**d)
+
+    def run(*jobs):
+        return L.pqb_dequantize_batch((J * len(jobs))(*jobs), len(jobs), None)
+
+    assert run(job(), job(reserved=1)) == -2
+    assert run(job(), job(out_dtype=5)) == -2
+    assert run(job(), job(fmt=1, gran=5)) == -3
+    assert run(job(), job(fmt=3, gran=6)) == -1          # INT4 needs its zero-points
+    assert run(job(), job(fmt=2, gran=5)) == -1          # NVFP4 needs its tensor scales
+    assert run(job(), job(cols=100)) == -4
+    assert run(job(), job(out=fake + 8)) == -5
+    assert L.pqb_dequantize_batch(None, -1, None) == -4
+    assert L.pqb_dequantize_batch(None, 0, None) == 0
+    assert run(job(rows=0), job(batch=0, fmt=3, gran=6)) == 0   # empty: nothing launched
 
 
 def test_kv_write_ex_errors_before_launch(L):

@@ -156,5 +156,32 @@ def test_batch_many_jobs_several_launches(pqb):
               f"job {i} {fmt} {gran} {shp} {x.dtype}")
 
 
+DQ_SPECS = [("fp8_e4m3", "1x128", (1, 33, 384)), ("fp8_e5m2", "1x128", (2, 5, 128)),
+            ("mxfp4", "blk32", (1, 17, 96)), ("mxfp8", "blk32", (3, 4, 64)),
+            ("nvfp4", "blk16", (3, 7, 48)), ("int4_asym", "grp128", (2, 9, 384)),
+            ("fp8_e4m3", "tensor", (2, 10, 40)), ("fp8_e4m3", "row", (1, 6, 200)),
+            ("fp8_e4m3", "128x128", (1, 256, 256)), ("int8_sym", "row", (1, 3, 24)),
+            ("int4_asym", "grp128", (1, 0, 128))]
+
+
+@pytest.mark.parametrize("repeat", [1, 9])
+def test_dequantize_batch_equals_single_calls(pqb, repeat):
+    """Mixed formats and scopes, both output dtypes, NVFP4 with several slices
+    and an empty job; 9 copies make 90 fused jobs (NVFP4 slices counted one by
+    one: 108), so the float32 and bf16 launches each split in two."""
+    qs = []
+    for i, (fmt, gran, shp) in enumerate(DQ_SPECS * repeat):
+        b, r, c = shp
+        x = synth.fp8_activation(rows=max(b * r, 1), cols=c, seed=900 + i)[: b * r].reshape(b, r, c)
+        qs.append((pqb.quantize(x.to(DEV), fmt, gran), torch.bfloat16 if i % 2 else torch.float32))
+    outs = pqb.dequantize_batch(qs)
+    for i, ((q, dt), o) in enumerate(zip(qs, outs)):
+        ref = pqb.dequantize(q, dt)
+        assert o.dtype == ref.dtype and o.shape == ref.shape
+        assert torch.equal(o.view(torch.int16 if dt == torch.bfloat16 else torch.int32),
+                           ref.view(torch.int16 if dt == torch.bfloat16 else torch.int32)), \
+            f"job {i} {q.fmt} {q.gran} {q.shape} {dt}"
+
+
 def test_batch_empty_list(pqb):
     assert pqb.quantize_batch([]) == []

@@ -301,6 +301,31 @@ def test_two_pass_fold_threshold(pqb, rows):
         same(nb[b, pick], ob, f"fold {rows} nvfp4 block scales {b}")
 
 
+def test_int4_infinite_range_group_stays_local(pqb):
+    """A group whose range overflows float32 (values of both signs near
+    +-3e38) is outside INT4's documented input range; its own bytes are
+    unspecified, but every other group must match the oracle."""
+    x = synth.fp8_weight(rows=16, cols=512, seed=5).float()
+    x[3, 128:256:2] = 3.0e38
+    x[3, 129:256:2] = -3.0e38
+    for dtype in (torch.float32, torch.bfloat16):
+        xt = x.to(dtype)
+        q = pqb.quantize(xt.to(DEV), "int4_asym")
+        oc, os_, oz = oracle.int4_quantize(xt)
+        bad_group = 3 * 4 + 1
+        keep_g = np.ones(16 * 4, bool)
+        keep_g[bad_group] = False
+        keep_c = np.repeat(keep_g, 64)
+        g_codes = host_bits(q.codes).reshape(-1)
+        assert np.array_equal(g_codes[keep_c], oc.reshape(-1)[keep_c]), f"int4 codes {dtype}"
+        g_s = host_bits(q.scales).reshape(-1)
+        assert np.array_equal(g_s[keep_g], os_.reshape(-1)[keep_g]), f"int4 scales {dtype}"
+        zn = host_bits(q.aux).reshape(-1)
+        zg = np.stack([zn & 15, zn >> 4], -1).reshape(-1)
+        zo = np.stack([oz & 15, oz >> 4], -1).reshape(-1)
+        assert np.array_equal(zg[keep_g], zo[keep_g]), f"int4 zero-points {dtype}"
+
+
 # ---------------------------------------------------------------- KV -------
 
 def test_kv_write_parity(pqb):

@@ -206,8 +206,9 @@ def test_sweep_1gib_all_formats(pqb):
 def test_past_2_31_elements(pqb):
     """A bf16 tensor [262272, 8192] holds 2^31 + 2^20 elements: its last
     128-row band lies wholly past element 2^31, where 32-bit element indexing
-    would wrap.  Every one-pass and two-pass format, quantize and dequantize,
-    is compared with the oracle on three 128-row bands (first, middle, last);
+    would wrap.  Every one-pass and two-pass format, quantize and dequantize to
+    bf16 and to float32, is compared with the oracle on three 128-row bands
+    (first, middle, last);
     the tensor maximum is planted in the last band, so the per-tensor scales
     of the sample are the global ones."""
     R, C = 262272, 8192
@@ -233,6 +234,9 @@ def test_past_2_31_elements(pqb):
             eq(bits(q.scales.view(R // 128, C // 128)[tiles]), os_, "fp8 128x128 scales")
         dq = pqb.dequantize(q, torch.bfloat16)
         eq(bits(dq[0][bands]), oracle.fp8_dequantize(oc, os_, gran, True), f"fp8 {gran} dequant")
+        del dq
+        dq = pqb.dequantize(q, torch.float32)
+        eq(bits(dq[0][bands]), oracle.fp8_dequantize(oc, os_, gran), f"fp8 {gran} dequant f32")
         del q, dq
     say("past 2^31: mxfp4, nvfp4, int4")
     q = pqb.quantize(x, "mxfp4")
@@ -240,6 +244,7 @@ def test_past_2_31_elements(pqb):
     eq(u8(q.codes.view(R, C // 2)[bands]), oc, "mx codes")
     eq(u8(q.scales.view(R, C // 32)[bands]), os_, "mx scales")
     eq(bits(pqb.dequantize(q, torch.bfloat16)[0][bands]), oracle.mxfp4_dequantize(oc, os_, True), "mx dequant")
+    eq(bits(pqb.dequantize(q, torch.float32)[0][bands]), oracle.mxfp4_dequantize(oc, os_), "mx dequant f32")
     del q
     q = pqb.quantize(x, "nvfp4")
     oc, os_, og = oracle.nvfp4_quantize(xs)
@@ -247,6 +252,7 @@ def test_past_2_31_elements(pqb):
     eq(u8(q.codes.view(R, C // 2)[bands]), oc, "nv codes")
     eq(u8(q.scales.view(R, C // 16)[bands]), os_, "nv scales")
     eq(bits(pqb.dequantize(q, torch.bfloat16)[0][bands]), oracle.nvfp4_dequantize(oc, os_, og, True), "nv dequant")
+    eq(bits(pqb.dequantize(q, torch.float32)[0][bands]), oracle.nvfp4_dequantize(oc, os_, og), "nv dequant f32")
     del q
     q = pqb.quantize(x, "int4_asym")
     oc, os_, oz = oracle.int4_quantize(xs)
@@ -256,6 +262,29 @@ def test_past_2_31_elements(pqb):
     eq(zb[bands], oz, "int4 zero-points")
     eq(bits(pqb.dequantize(q, torch.bfloat16)[0][bands]), oracle.int4_dequantize(oc, os_, oz, True),
        "int4 dequant")
+    eq(bits(pqb.dequantize(q, torch.float32)[0][bands]), oracle.int4_dequantize(oc, os_, oz),
+       "int4 dequant f32")
+    del q
+    say("past 2^31: e5m2, int8, mxfp8")
+    q = pqb.quantize(x, "fp8_e5m2", "1x128")
+    oc, os_ = oracle.fp8_quantize(xs, "1x128", elem="e5m2")
+    eq(u8(q.codes.view(R, C)[bands]), oc, "e5m2 codes")
+    eq(bits(q.scales.view(R, C // 128)[bands]), os_, "e5m2 scales")
+    eq(bits(pqb.dequantize(q, torch.float32)[0][bands]), oracle.fp8_dequantize(oc, os_, "1x128", elem="e5m2"),
+       "e5m2 dequant f32")
+    del q
+    q = pqb.quantize(x, "int8_sym", "row")
+    oc, os_ = oracle.int8_quantize(xs, "row")
+    eq(u8(q.codes.view(R, C)[bands]), oc.view(np.uint8), "int8 codes")
+    eq(bits(q.scales[bands]), os_, "int8 scales")
+    eq(bits(pqb.dequantize(q, torch.float32)[0][bands]), oracle.int8_dequantize(oc, os_, "row"),
+       "int8 dequant f32")
+    del q
+    q = pqb.quantize(x, "mxfp8")
+    oc, os_ = oracle.mxfp8_quantize(xs)
+    eq(u8(q.codes.view(R, C)[bands]), oc, "mxfp8 codes")
+    eq(u8(q.scales.view(R, C // 32)[bands]), os_, "mxfp8 scales")
+    eq(bits(pqb.dequantize(q, torch.float32)[0][bands]), oracle.mxfp8_dequantize(oc, os_), "mxfp8 dequant f32")
 
 
 def test_fp8_128x128_paired_tiles(pqb):

@@ -393,6 +393,25 @@ def test_int4_special_groups(orc):
     assert codes[0, 2, 0] & 15 == 8
 
 
+def test_int4_infinite_range_group(orc):
+    """A group holding values of both signs near the float32 maximum has a
+    range hi - lo that overflows to inf.  The definition then gives s = inf
+    (bf16 0x7F80), x / s = 0 for every finite x, so every code and the
+    zero-point are -8; the engine leaves such groups unspecified (a documented
+    precondition), and the neighbouring group is untouched."""
+    x = np.zeros((1, 2, 128), np.float32)
+    x[0, 0, ::2] = 3.0e38
+    x[0, 0, 1::2] = -3.0e38
+    x[0, 1] = np.linspace(-1.0, 2.0, 128, dtype=np.float32)
+    codes, scales, zeros = orc.int4_quantize(x)
+    assert scales[0, 0, 0] == 0x7F80
+    assert all(nib(codes, i) == 8 for i in range(128))
+    assert zeros[0] & 15 == 8
+    c2, s2, z2 = orc.int4_quantize(x[:, 1:])
+    assert scales[0, 1, 0] == s2[0, 0, 0]
+    assert np.array_equal(codes[0, 1], c2[0, 0]) and zeros[0] >> 4 == z2[0] & 15
+
+
 def test_int4_range_always_contains_zero(orc):
     """A group that lies entirely above (or below) zero still spans [0, hi]
     (or [lo, 0]): 0 must stay exactly representable."""
