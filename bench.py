@@ -783,8 +783,10 @@ def main():
     ap.add_argument("--reps", type=int, default=20)
     ap.add_argument("--records", default=None, help="write every record to this JSON file")
     ap.add_argument("--only", default=None,
-                    help="run only the format workloads whose name contains this string "
-                         "(no headline line; prints the records as JSON)")
+                    help="run only the format workloads whose name contains this string, or "
+                         "'w8a8' (the FP8 W8A8 step), or 'llama8b_224w_int4' (the headline set "
+                         "with its per-tensor and dequantization records); no headline line, "
+                         "prints the records as JSON")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -803,6 +805,15 @@ def main():
 
     if args.copy_probe:
         copy_probe(torch)
+    if args.only == "w8a8":
+        print(json.dumps(bench_w8a8(torch, eng, synth, args.steps, args.warmup, args.sets)),
+              flush=True)
+        return
+    if args.only == "llama8b_224w_int4":
+        h = bench_headline(torch, eng, synth, args.steps, args.warmup)
+        int4_records_extra(torch, eng, h, args.reps)
+        print(json.dumps(_RECORDS), flush=True)
+        return
     if args.only is not None:
         print(json.dumps(bench_extras(torch, eng, synth, args.reps, args.only)), flush=True)
         return
