@@ -88,6 +88,36 @@ class Engine:
         if rc != 0:
             raise RuntimeError(f"pqb_quantize {fmt}/{gran}: status {rc}")
 
+    def quantize_call(self, x, fmt, gran, shape, buf):
+        """pqb_quantize on `x` into `buf` with its arguments marshalled once: the
+        returned call costs one ctypes call, so that a loop of small tensors times
+        the library rather than Python."""
+        ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+        args = (ptr(x), 1 if x.dtype == self.torch.bfloat16 else 0, *shape,
+                self.pqb.FORMATS[fmt], self.pqb.GRANS[gran], ptr(buf["codes"]), ptr(buf["scales"]),
+                ptr(buf["aux"]), ptr(buf["workspace"]), buf["sizes"]["workspace"], self.stream)
+        f = self.L.pqb_quantize
+
+        def call():
+            rc = f(*args)
+            if rc != 0:
+                raise RuntimeError(f"pqb_quantize {fmt}/{gran}: status {rc}")
+        return call
+
+    def dequantize_call(self, buf, fmt, gran, shape, out):
+        """pqb_dequantize of `buf` into `out`, arguments marshalled once."""
+        ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+        args = (ptr(buf["codes"]), ptr(buf["scales"]), ptr(buf["aux"]), self.pqb.FORMATS[fmt],
+                self.pqb.GRANS[gran], *shape, 1 if out.dtype == self.torch.bfloat16 else 0,
+                ptr(out), self.stream)
+        f = self.L.pqb_dequantize
+
+        def call():
+            rc = f(*args)
+            if rc != 0:
+                raise RuntimeError(f"pqb_dequantize {fmt}/{gran}: status {rc}")
+        return call
+
     def jobs(self, items):
         """A prebuilt pqb_job array for `items` = [(x, fmt, gran, shape, buf)]."""
         J = self.pqb.pqb._Job
@@ -255,9 +285,12 @@ def int4_records_extra(torch, eng, h, reps=5):
     dev = torch.device("cuda:0")
     xs, bufs, shapes = h["xs"], h["bufs"], h["shapes"]
 
+    qcalls = [eng.quantize_call(x, "int4_asym", "grp128", shp, b)
+              for x, shp, b in zip(xs, shapes, bufs)]
+
     def one_by_one(i):
-        for x, shp, b in zip(xs, shapes, bufs):
-            eng.quantize(x, "int4_asym", "grp128", shp, b)
+        for c in qcalls:
+            c()
 
     t = time_reps(torch, one_by_one, reps, 1)
     record("llama8b_224w_bf16_int4_g128_per_tensor",
@@ -269,9 +302,12 @@ def int4_records_extra(torch, eng, h, reps=5):
     outs = [torch.empty(shp, dtype=torch.bfloat16, device=dev) for shp in shapes]
     nbd = sum(out_bytes(b["sizes"]) + o.numel() * 2 for b, o in zip(bufs, outs))
 
+    dcalls = [eng.dequantize_call(b, "int4_asym", "grp128", shp, o)
+              for shp, b, o in zip(shapes, bufs, outs)]
+
     def dq_all(i):
-        for shp, b, o in zip(shapes, bufs, outs):
-            eng.dequantize(b, "int4_asym", "grp128", shp, o)
+        for c in dcalls:
+            c()
 
     t = time_reps(torch, dq_all, reps, 1)
     record("llama8b_224w_bf16_int4_g128_dequant",
@@ -311,10 +347,13 @@ def bench_w8a8(torch, eng, synth, steps, warmup, nsets):
     def step(i):
         eng.batch(jobs[i % nsets])
 
+    pairs = [(eng.quantize_call(a, "fp8_e4m3", "1x128", ashape, ab),
+              eng.quantize_call(w, "fp8_e4m3", "128x128", wshape, wb)) for w, a, wb, ab in sets]
+
     def two_launches(i):
-        w, a, wb, ab = sets[i % nsets]
-        eng.quantize(a, "fp8_e4m3", "1x128", ashape, ab)
-        eng.quantize(w, "fp8_e4m3", "128x128", wshape, wb)
+        qa, qw = pairs[i % nsets]
+        qa()
+        qw()
 
     t = time_reps(torch, step, steps, warmup)
     ms_two = time_loop(torch, two_launches, steps, warmup)
@@ -355,16 +394,16 @@ def bench_extras(torch, eng, synth, reps, only=None):
         bufs = [eng.alloc(fmt, gran, shape, dev) for _ in range(nsets)]
         nb = in_bytes + out_bytes(bufs[0]["sizes"])
         two_pass = fmt == "nvfp4" or gran == "tensor"
-        t = time_reps(torch, lambda i: eng.quantize(xs[i % nsets], fmt, gran, shape,
-                                                    bufs[i % nsets]), reps, 3)
+        qcalls = [eng.quantize_call(xs[i], fmt, gran, shape, bufs[i]) for i in range(nsets)]
+        t = time_reps(torch, lambda i: qcalls[i % nsets](), reps, 3)
         out[name] = rec(nb, t, in_bytes if two_pass else 0, op=f"quantize {fmt}/{gran}",
                         shape=list(shape), dtype=str(x.dtype).replace("torch.", ""),
                         rotated_sets=nsets)
         if dq_dtype is not None:
             o = [torch.empty(shape, dtype=dq_dtype, device=dev) for _ in range(nsets)]
             nbd = out_bytes(bufs[0]["sizes"]) + o[0].numel() * o[0].element_size()
-            t = time_reps(torch, lambda i: eng.dequantize(bufs[i % nsets], fmt, gran, shape,
-                                                          o[i % nsets]), reps, 3)
+            dcalls = [eng.dequantize_call(bufs[i], fmt, gran, shape, o[i]) for i in range(nsets)]
+            t = time_reps(torch, lambda i: dcalls[i % nsets](), reps, 3)
             out[name + "_dequant"] = rec(nbd, t, op=f"dequantize {fmt} -> "
                                          f"{str(dq_dtype).replace('torch.', '')}",
                                          shape=list(shape), rotated_sets=nsets)
