@@ -5,8 +5,8 @@
 // 8 waves), MXFP4 with MXFP8 (256-thread workgroups), and INT4 (512-thread
 // workgroups).  Within a
 // launch every job gets a contiguous range of workgroups; a workgroup finds its
-// job by scanning the prefix table in the kernel arguments (uniform, scalar)
-// and runs that job's body from quant.h with its local workgroup index.  One
+// job by a binary search of the prefix table in the kernel arguments (uniform,
+// scalar) and runs that job's body from quant.h with its local workgroup index.  One
 // dispatch then covers, e.g., a weight's 128x128 tiles and an activation's
 // 1x128 blocks, or a whole decoder's INT4 weights.  Each family kernel only
 // holds the registers of its own bodies.  (Per-row FP8 jobs keep a whole row in
