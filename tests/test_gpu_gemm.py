@@ -96,8 +96,10 @@ def check(pqb, a, sa, b, sb, what, rows=None):
                                f"{bound[tuple(bad[0])]:.3e}")
 
 
+# (600, 768, 1152): several tiles in both directions and a ragged last row of
+# tiles; (1024, 512, 384): a grid of 32 workgroups (the XCD-grouped order).
 SHAPES = [(128, 128, 128), (256, 384, 512), (100, 256, 256), (1, 128, 384), (300, 640, 1152),
-          (129, 128, 2048), (64, 256, 0)]
+          (129, 128, 2048), (64, 256, 0), (600, 768, 1152), (1024, 512, 384)]
 
 
 @pytest.mark.parametrize("shape", SHAPES)
