@@ -152,7 +152,8 @@ pqb_status pqb_quantize(const void* x, pqb_dtype dtype, int64_t batch, int64_t r
  * (pqb_query_sizes) exceeds the scratch returns PQB_ERR_SCRATCH before
  * anything is enqueued: e.g. one per-tensor slice of up to 2^31 - 8192 elements
  * fits.
- * `stream` must belong to the current device.  Every call on one GPU shares
+ * `stream` must belong to the current device (else PQB_ERR_HIP, before
+ * anything is enqueued).  Every call on one GPU shares
  * that GPU's scratch, and each call overwrites what it uses before reading it:
  * calls that overlap on one GPU (other streams, other host threads) race, so
  * order them.  Every other rule and error is pqb_quantize's. */

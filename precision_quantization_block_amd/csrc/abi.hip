@@ -155,10 +155,15 @@ constexpr int kMaxDevices = 64;
 std::atomic<void*> g_scratch[kMaxDevices];
 std::mutex g_scratch_mu;
 
-// Device address of the current device's scratch array.
-pqb_status scratch_of_current_device(void** out) {
+// Device address of the current device's scratch array; PQB_ERR_HIP when
+// `stream` runs on another device, where that address would not be valid.
+pqb_status scratch_of_current_device(hipStream_t stream, void** out) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PQB_ERR_HIP;
+  if (stream) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess || sdev != dev) return PQB_ERR_HIP;
+  }
   void* p = g_scratch[dev].load(std::memory_order_acquire);
   if (!p) {
     std::lock_guard<std::mutex> lock(g_scratch_mu);
@@ -295,7 +300,7 @@ pqb_status pqb_quantize_noalloc(const void* x, pqb_dtype dtype, int64_t batch, i
   if (batch * rows * cols == 0) return PQB_OK;
   void* ws = nullptr;
   if (need.workspace) {
-    st = scratch_of_current_device(&ws);
+    st = scratch_of_current_device((hipStream_t)stream, &ws);
     if (st != PQB_OK) return st;
   }
   return pqb_quantize(x, dtype, batch, rows, cols, fmt, gran, codes, scales, aux, ws,
