@@ -153,38 +153,48 @@ __device__ __forceinline__ void stage_and_store(const v4f (&acc)[4][4], uint8_t*
 }
 
 // FP8 1x128 quantization of a staged 128 x 128 tile's rows, each exactly one
-// 128-column block: thread t takes columns 64 (t & 1) .. + 63 of row t >> 1
-// (staged by wave (row / 64, t & 1)); the pair's maxima meet by DPP, then the
-// scale and codes follow the 1x128 quantizer's arithmetic.
+// 128-column block, two threads per row (t >> 1): thread t takes columns
+// 32 i + 16 (t & 1) + j (i < 4, j < 16), so that each 16-byte code store of the
+// pair covers 32 contiguous bytes of the row (with 64-column halves per
+// thread, every store covered half of a 32-byte sector, and the fused form
+// wrote 1.77x its output bytes).  The pair's maxima meet by DPP, then the scale
+// and codes follow the 1x128 quantizer's arithmetic.  Column c of row r is
+// staged by wave (r / 64, c / 64).
 __device__ __forceinline__ void quantize_tile_rows(const uint8_t* lds, int tid, int m0, int n0,
                                                    int M, int N, uint8_t* C, float* c_scales) {
   static_assert(kGTM == 128 && kGThreads == 256, "two threads per row of a 128-row tile");
   const int rr = tid >> 1, half = tid & 1;
-  const float* v = reinterpret_cast<const float*>(lds) +
-                   ((rr >> 6) * 2 + half) * 64 * kGOutStride + (rr & 63) * kGOutStride;
+  const float* stage = reinterpret_cast<const float*>(lds) + (rr & 63) * kGOutStride;
+  auto piece = [&](int i) {   // the 16 staged floats of columns 32 i + 16 half ..
+    return stage + ((rr >> 6) * 2 + (i >> 1)) * 64 * kGOutStride + 32 * (i & 1) + 16 * half;
+  };
   uint32_t am = 0;
 #pragma unroll
-  for (int i = 0; i < 64; i += 4) {
-    const v4f x = *reinterpret_cast<const v4f*>(v + i);
-    am = max(am, max(max(as_u(fabsf(x[0])), as_u(fabsf(x[1]))),
-                     max(as_u(fabsf(x[2])), as_u(fabsf(x[3])))));
+  for (int i = 0; i < 4; ++i) {
+    const float* v = piece(i);
+#pragma unroll
+    for (int j = 0; j < 16; j += 4) {
+      const v4f x = *reinterpret_cast<const v4f*>(v + j);
+      am = max(am, max(max(as_u(fabsf(x[0])), as_u(fabsf(x[1]))),
+                       max(as_u(fabsf(x[2])), as_u(fabsf(x[3])))));
+    }
   }
   const float s = fp8_scale_bits<kE4M3>(group_umax<2>(am));
   const float y = recip_rn(s);
   if (m0 + rr < M) {
-    uint8_t* dst = C + (int64_t)(m0 + rr) * N + n0 + 64 * half;
+    uint8_t* dst = C + (int64_t)(m0 + rr) * N + n0 + 16 * half;
 #pragma unroll
-    for (int i = 0; i < 64; i += 16) {
+    for (int i = 0; i < 4; ++i) {
+      const float* v = piece(i);
       float w[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) w[j] = v[i + j];
+      for (int j = 0; j < 16; ++j) w[j] = v[j];
       const uint2 lo = fp8_pack8<kE4M3>(w, s, y), hi = fp8_pack8<kE4M3>(w + 8, s, y);
-      st_nt16(dst + i, lo.x, lo.y, hi.x, hi.y);
+      st_nt16(dst + 32 * i, lo.x, lo.y, hi.x, hi.y);
     }
     if (half == 0) c_scales[(int64_t)(m0 + rr) * (N / kGT) + n0 / kGT] = s;
   }
 }
-
 
 template <int kOut>
 __global__ __launch_bounds__(kGThreads) void k_gemm_fp8_bs(const uint8_t* __restrict__ A,
