@@ -829,7 +829,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              f"(the quantizers shard without communication; see the design notes).",
+              f"(the quantizers shard by rows or blocks without communication; a per-tensor scale would need one MAX all-reduce of the pass-1 maxima).",
               file=sys.stderr)
         sys.exit(2)
 
