@@ -532,3 +532,55 @@ def mxfp4_gemm(a_codes, a_scales, b_codes, b_scales, abs_sum=False):
     b = b.astype(np.float64)
     C = a @ b.T
     return (C, np.abs(a) @ np.abs(b).T) if abs_sum else C
+
+
+# --------------------------------------------------------------------------
+# NVFP4 x NVFP4 product (a consumer of the NVFP4 codes)
+# --------------------------------------------------------------------------
+
+_E2M1_MAG = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def _nvfp4_scaled_elements(codes, scales, rows, K):
+    """V(code) * dec(block scale) for every element, float64 [rows, K]: the
+    nibble's E2M1 value (element 2i in the low nibble of byte i) times the
+    E4M3 value of its 16-element block's scale byte."""
+    codes = np.ascontiguousarray(codes, np.uint8).reshape(rows, K // 2)
+    nib = np.empty((rows, K), np.uint8)
+    nib[:, 0::2] = codes & 0xF
+    nib[:, 1::2] = codes >> 4
+    val = np.where(nib & 8, -1.0, 1.0) * np.array(_E2M1_MAG)[nib & 7]
+    dec = _e4m3_table()[np.asarray(scales, np.uint8).reshape(rows, K // 16)]
+    return val * np.repeat(dec, 16, axis=1)
+
+
+def nvfp4_gemm(a_codes, a_scales, a_gs, b_codes, b_scales, b_gs, abs_sum=False):
+    """C = g * sum_k A'[m, k] B'[n, k] for two NVFP4 operands in the engine's
+    layout (E2M1 codes [rows, K/2], E4M3 block scales [rows, K/16], one float32
+    tensor scale each), the product a matrix core forms from the format (page
+    "14. 量化：让每一步搬更少的字节", section 新一代低位格式：FP8、FP4 与微缩放:
+    FP4 matrix units take NVFP4 operands directly; page "量化部署实战", 格式速查,
+    NVFP4 row: 16-element blocks, an E4M3 scale per block and a float32 scale
+    per tensor):
+
+        A'[m, k] = V(a[m, k]) * dec(sa[m, k // 16]),  B' likewise,
+        g = float32(gsA * gsB).
+
+    Each block scale enters as its E4M3 value, so a block whose scale code is
+    0 contributes 0 (pqb_dequantize's 1e-12 floor only keeps the quantizer's
+    division finite); the two tensor scales enter once, as their float32
+    product.  Every A' and B' value has at most 6 significant bits between
+    2^-10 and 2688, so every product is exact in float64 and the matmul rounds
+    only at 2^-53.  Returns C as float64 [M, N]; with abs_sum, also
+    g * sum_k |A'| |B'|, which sets the scale of a float32 evaluation's error."""
+    a_codes = np.asarray(a_codes, np.uint8)
+    b_codes = np.asarray(b_codes, np.uint8)
+    M, N = a_codes.shape[0], b_codes.shape[0]
+    K = 2 * a_codes.shape[1]
+    if b_codes.shape[1] != K // 2 or K % 16:
+        raise ValueError("need a [M, K/2], b [N, K/2] codes with K a multiple of 16")
+    A = _nvfp4_scaled_elements(a_codes, a_scales, M, K)
+    B = _nvfp4_scaled_elements(b_codes, b_scales, N, K)
+    g = float(np.float32(np.float32(a_gs).reshape(-1)[0]) * np.float32(np.float32(b_gs).reshape(-1)[0]))
+    C = g * (A @ B.T)
+    return (C, g * (np.abs(A) @ np.abs(B).T)) if abs_sum else C
