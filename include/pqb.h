@@ -366,6 +366,31 @@ pqb_status pqb_gemm_mxfp4(const uint8_t* a, const uint8_t* a_scales, const uint8
                           const uint8_t* b_scales, int64_t m, int64_t n, int64_t k,
                           pqb_dtype out_dtype, void* c, void* stream);
 
+/* NVFP4 x NVFP4 product on the matrix cores (page "14. 量化：让每一步搬更少的
+ * 字节", section 新一代低位格式：FP8、FP4 与微缩放: FP4 matrix units take
+ * NVFP4 operands; page "量化部署实战", 格式速查, NVFP4 row: 16-element blocks,
+ * one E4M3 scale each, and a float32 scale per tensor):
+ *   C[m, n] = g * sum_k (V(a[m, k]) dec(sa[m, k/16])) (V(b[n, k]) dec(sb[n, k/16])),
+ *   g = float32(a_gs[0] * b_gs[0]),
+ * with V the E2M1 value of a nibble and dec the E4M3 value of a scale byte,
+ * so a block whose scale code is 0 contributes 0.  a, b: E2M1 codes [m, k/2]
+ * and [n, k/2] (element 2i in the low nibble of byte i); sa, sb: E4M3 scales
+ * [m, k/16] and [n, k/16]; a_gs, b_gs: one float32 each in device memory;
+ * exactly what pqb_quantize writes for NVFP4 x BLK_16 of [1, m, k] and
+ * [1, n, k].  Scale bytes are read without their sign bit and must not be
+ * 0x7F (NaN), as the quantizer never writes either.  c: [m, n] row-major of
+ * out_dtype.  Each scaled element V dec(s) is exact in f16, the products are
+ * exact, and the float32 sums bound the error against exact arithmetic by
+ * about (34 + k/32) * 2^-24 * g * sum_k |V dec(sa)| |V dec(sb)|, plus half an
+ * ulp of the result (float32, or bf16 for bf16 output).  Shape rules: k % 128 == 0,
+ * n % 128 == 0, m, n, k < 2^31; m = 0 or n = 0 does nothing; k = 0 writes
+ * zeros (and reads neither scale).  Alignment: a, b and c 16 bytes, scales and
+ * tensor scales 4.  Errors, before any launch: PQB_ERR_ENUM, PQB_ERR_SHAPE,
+ * PQB_ERR_NULL, PQB_ERR_ALIGN. */
+pqb_status pqb_gemm_nvfp4(const uint8_t* a, const uint8_t* a_scales, const float* a_gs,
+                          const uint8_t* b, const uint8_t* b_scales, const float* b_gs, int64_t m,
+                          int64_t n, int64_t k, pqb_dtype out_dtype, void* c, void* stream);
+
 /* W4A16 product, the consumer of the INT4 group-128 codes (page "14. 量化：让
  * 每一步搬更少的字节", 路线一: 4-bit weights read from memory, unpacked and
  * dequantized to 16 bits, then multiplied):

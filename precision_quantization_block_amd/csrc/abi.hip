@@ -696,6 +696,20 @@ pqb_status pqb_gemm_mxfp4(const uint8_t* a, const uint8_t* a_scales, const uint8
                                       (hipStream_t)stream));
 }
 
+pqb_status pqb_gemm_nvfp4(const uint8_t* a, const uint8_t* a_scales, const float* a_gs,
+                          const uint8_t* b, const uint8_t* b_scales, const float* b_gs, int64_t m,
+                          int64_t n, int64_t k, pqb_dtype out_dtype, void* c, void* stream) {
+  if (!valid_dtype(out_dtype)) return PQB_ERR_ENUM;
+  const pqb_status e = check_gemm(a, b, m, n, k, c);
+  if (e != PQB_OK || m == 0 || n == 0) return e;
+  if (k > 0 && (!a_scales || !b_scales || !a_gs || !b_gs)) return PQB_ERR_NULL;
+  if (k > 0 && !(aligned(a_scales, 4) && aligned(b_scales, 4) && aligned(a_gs, 4) &&
+                 aligned(b_gs, 4)))
+    return PQB_ERR_ALIGN;
+  return hip_status(launch_gemm_nvfp4(a, a_scales, a_gs, b, b_scales, b_gs, m, n, k,
+                                      out_dtype == PQB_BF16, c, (hipStream_t)stream));
+}
+
 pqb_status pqb_gemm_fp8_blockscaled_quant(const uint8_t* a, const float* a_scales,
                                           const uint8_t* b, const float* b_scales, int64_t m,
                                           int64_t n, int64_t k, uint8_t* c_codes,

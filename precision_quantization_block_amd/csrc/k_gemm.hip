@@ -418,6 +418,154 @@ __global__ __launch_bounds__(kGThreads) void k_gemm_mxfp4(const uint8_t* __restr
   stage_and_store<kOut>(acc, lds, wave, lane, m0, n0, M, N, C);
 }
 
+// ---------------------------------------------------------------------------
+// NVFP4 x NVFP4 product C = g * sum_k A'[m, k] B'[n, k] with A' = V(a) dec(sa)
+// over 16-element blocks and g = float32(gsA gsB).  The matrix core's own
+// scales are E8M0 per 32 elements, so they cannot carry NVFP4's E4M3 scales per
+// 16; instead each wave widens its fragments to f16 between LDS and the matrix
+// core.  v_cvt_scalef32_pk_f16_fp4 turns two nibbles into two halves times 2^8
+// (the instruction takes only the exponent of its scale operand), and one
+// packed f16 multiply by the half whose bits are the scale byte shifted left by
+// 7 (the E4M3 value times 2^-8; E4M3's subnormals land on f16 subnormals) gives
+// V dec(s) exactly: at most 6 significant bits, between 2^-10 and 2688.
+// v_mfma_f32_16x16x32_f16 then forms exact products and accumulates them in
+// float32, and g multiplies each result once.  Workgroup shape, DMA ring and
+// swizzle are the MXFP4 product's: a stage is 256 deep in K (128 code bytes per
+// row); its scales are 16 bytes per row.  Lane l of a fragment holds row l & 15
+// and the 32 elements of 16-byte chunk q = l >> 4 of the 128-deep half (blocks
+// 2q and 2q + 1); its dword t holds the 8 elements of K step t, and A and B
+// take the same elements, so the products pair up.
+// ---------------------------------------------------------------------------
+constexpr int kNvScaleBytes = kGT * 16;                    // 16 E4M3 bytes per row and stage
+constexpr int kNvSlotBytes = 2 * kGTileB + 2 * kNvScaleBytes;
+constexpr int kNvLdsBytes = 2 * kNvSlotBytes > kGOutBytes ? 2 * kNvSlotBytes : kGOutBytes;
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+
+// dec(s) * 2^-8 in both halves, for a scale byte s (sign bit cleared).
+__device__ __forceinline__ h2 nv_scale(uint32_t s) {
+  return __builtin_bit_cast(h2, s * 0x00800080u);
+}
+
+// The 8 nibbles of w (low nibble first) as V * dec(s) in halves.
+__device__ __forceinline__ h8 nv_widen8(uint32_t w, h2 s) {
+  const h2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 0) * s;
+  const h2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 1) * s;
+  const h2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 2) * s;
+  const h2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 3) * s;
+  return h8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// Fragment of row r in half h of a staged stage: the lane's 16 code bytes
+// (chunk 4 h + q) and its two block scales (bytes 8 h + 2 q, + 1 of the row).
+__device__ __forceinline__ void nv_frag(const uint8_t* tile, const uint32_t* scales, int r, int h,
+                                        int q, h8 (&f)[4]) {
+  const uint4 v = *reinterpret_cast<const uint4*>(tile + tile_off(r, 4 * h + q));
+  const uint32_t sw = scales[4 * r + 2 * h + (q >> 1)] >> (16 * (q & 1));
+  const h2 s0 = nv_scale(sw & 0x7Fu), s1 = nv_scale((sw >> 8) & 0x7Fu);
+  f[0] = nv_widen8(v.x, s0);
+  f[1] = nv_widen8(v.y, s0);
+  f[2] = nv_widen8(v.z, s1);
+  f[3] = nv_widen8(v.w, s1);
+}
+
+template <int kOut>
+__global__ __launch_bounds__(kGThreads) void k_gemm_nvfp4(const uint8_t* __restrict__ A,
+                                                          const uint8_t* __restrict__ sA,
+                                                          const float* __restrict__ gA,
+                                                          const uint8_t* __restrict__ B,
+                                                          const uint8_t* __restrict__ sB,
+                                                          const float* __restrict__ gB, int M,
+                                                          int N, int K, int tiles_n,
+                                                          void* __restrict__ C) {
+  static_assert(kGTM == 128 && kGThreads == 256, "the NVFP4 GEMM uses the 128 x 128 tile");
+  __shared__ __align__(16) uint8_t lds[kNvLdsBytes];
+  auto slot = [&](int s) { return lds + s * kNvSlotBytes; };
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nwg = gridDim.x, per = nwg / 8;
+  const int t = per * 8 == nwg ? (blockIdx.x & 7) * per + (blockIdx.x >> 3) : blockIdx.x;
+  const int band = t / (8 * tiles_n), rem = t - band * 8 * tiles_n;
+  const int band_rows = min(8, nwg / tiles_n - band * 8);
+  const int tm = band * 8 + rem % band_rows, tn = rem / band_rows;
+  const int m0 = tm * kGT, n0 = tn * kGT;
+  const int kb128 = K / 128, stages = (K + kMxKS - 1) / kMxKS;
+  const int rowb = K / 2, srow = K / 16;                   // code and scale bytes per row
+
+  // DMA of stage st into slot s: code rows as in the MXFP4 product; scale
+  // rows r = 64 (w & 1) + 16 i + (l >> 2), dword l & 3 (LDS byte 16 r + 4 (l & 3)),
+  // waves 0, 1 those of A, waves 2, 3 those of B.  A second half past K
+  // (K / 128 odd, last stage) reads the first half again and is never used.
+  const int drow = lane >> 3, dpos = lane & 7;
+  auto issue_stage = [&](int st, int s) {
+    const uint32_t base = lds_addr(slot(s));
+    const int64_t k0 = (int64_t)st * (kMxKS / 2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = wave * 32 + j * 8 + drow;
+      int c = dpos ^ (r & 7);
+      if (k0 + 16 * c >= rowb) c -= 4;
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(base + (wave * 32 + j * 8) * kGT);
+      dma16(A + (int64_t)min(m0 + r, M - 1) * rowb + k0 + 16 * c, dst);
+      dma16(B + (int64_t)(n0 + r) * rowb + k0 + 16 * c, dst + kGTileB);
+    }
+    const int dw = 16 * st + 4 * (lane & 3) < srow ? (lane & 3) : (lane & 1);
+    const uint32_t sdst = base + 2 * kGTileB + (wave < 2 ? 0 : kNvScaleBytes) + (wave & 1) * 64 * 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int sr = (wave & 1) * 64 + 16 * i + (lane >> 2);
+      const uint8_t* src = wave < 2 ? sA + (int64_t)min(m0 + sr, M - 1) * srow
+                                    : sB + (int64_t)(n0 + sr) * srow;
+      dma4(src + 16 * st + 4 * dw, __builtin_amdgcn_readfirstlane(sdst + 256 * i));
+    }
+  };
+
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r16 = lane & 15, q = lane >> 4;
+  v4f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  if (stages > 0) issue_stage(0, 0);
+  for (int st = 0; st < stages; ++st) {
+    // the only DMA in flight is this stage's (the next is issued after the
+    // barrier), so wait for all of it
+    wait_vmcnt<0>();
+    barrier();
+    if (st + 1 < stages) issue_stage(st + 1, (st + 1) & 1);
+    const uint8_t* sl = slot(st & 1);
+    const uint32_t* lsa = reinterpret_cast<const uint32_t*>(sl + 2 * kGTileB);
+    const uint32_t* lsb = lsa + kNvScaleBytes / 4;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (2 * st + h >= kb128) break;
+      h8 af[4][4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) nv_frag(sl, lsa, wm * 64 + mt * 16 + r16, h, q, af[mt]);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        h8 bf[4];
+        nv_frag(sl + kGTileB, lsb, wn * 64 + nt * 16 + r16, h, q, bf);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mt][ks], bf[ks], acc[mt][nt], 0, 0, 0);
+      }
+    }
+  }
+  barrier();
+  const float g = K > 0 ? gA[0] * gB[0] : 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = acc[i][j] * g;
+  stage_and_store<kOut>(acc, lds, wave, lane, m0, n0, M, N, C);
+}
+
 }  // namespace
 
 hipError_t launch_gemm_fp8_bs(const uint8_t* a, const float* a_scales, const uint8_t* b,
@@ -449,6 +597,20 @@ hipError_t launch_gemm_mxfp4(const uint8_t* a, const uint8_t* a_scales, const ui
   else
     hipLaunchKernelGGL(k_gemm_mxfp4<kOutF32>, grid, dim3(kGThreads), 0, st, a, a_scales, b, b_scales,
                        (int)M, (int)N, (int)K, tiles_n, c);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_nvfp4(const uint8_t* a, const uint8_t* a_scales, const float* a_gs,
+                             const uint8_t* b, const uint8_t* b_scales, const float* b_gs, int64_t M,
+                             int64_t N, int64_t K, bool out_bf16, void* c, hipStream_t st) {
+  const int tiles_m = (int)((M + kGT - 1) / kGT), tiles_n = (int)(N / kGT);
+  const dim3 grid((unsigned)tiles_m * (unsigned)tiles_n);
+  if (out_bf16)
+    hipLaunchKernelGGL(k_gemm_nvfp4<kOutBf16>, grid, dim3(kGThreads), 0, st, a, a_scales, a_gs, b,
+                       b_scales, b_gs, (int)M, (int)N, (int)K, tiles_n, c);
+  else
+    hipLaunchKernelGGL(k_gemm_nvfp4<kOutF32>, grid, dim3(kGThreads), 0, st, a, a_scales, a_gs, b,
+                       b_scales, b_gs, (int)M, (int)N, (int)K, tiles_n, c);
   return hipGetLastError();
 }
 

@@ -94,6 +94,7 @@ def lib():
         L.pqb_gemm_fp8_blockscaled_quant.argtypes = [P, P, P, P, I64, I64, I64, P, P, P]
         L.pqb_gemv_w4a16.argtypes = [P, I64, P, P, P, I64, I64, I, P, P]
         L.pqb_gemm_mxfp4.argtypes = [P, P, P, P, I64, I64, I64, I, P, P]
+        L.pqb_gemm_nvfp4.argtypes = [P, P, P, P, P, P, I64, I64, I64, I, P, P]
         L.pqb_gemv_w4a16_batch.argtypes = [ctypes.POINTER(_W4Job), I64, I64, I, P]
         L.pqb_gemm_w4a16.argtypes = [P, I64, P, P, P, I64, I64, I, P, P]
         L.pqb_gemm_w4a16_batch.argtypes = [ctypes.POINTER(_W4Job), I64, I64, I, P]
@@ -107,7 +108,7 @@ def lib():
                   "pqb_kv_write_fp8", "pqb_kv_write_fp8_ex", "pqb_kv_write_kivi",
                   "pqb_kv_read_kivi", "pqb_gemm_fp8_blockscaled",
                   "pqb_gemm_fp8_blockscaled_quant", "pqb_gemv_w4a16",
-                  "pqb_gemv_w4a16_batch", "pqb_gemm_mxfp4", "pqb_gemm_w4a16",
+                  "pqb_gemv_w4a16_batch", "pqb_gemm_mxfp4", "pqb_gemm_nvfp4", "pqb_gemm_w4a16",
                   "pqb_gemm_w4a16_batch",
                   "pqb_encode_e4m3", "pqb_encode_e5m2", "pqb_encode_e2m1",
                   "pqb_check_recip", "pqb_check_div"):
@@ -493,6 +494,36 @@ def gemm_mxfp4(a, b, out_dtype=torch.float32) -> torch.Tensor:
     _check(lib().pqb_gemm_mxfp4(_ptr(ac), _ptr(as_), _ptr(bc), _ptr(bs), M, N, K,
                                 BF16 if out_dtype == torch.bfloat16 else F32, _ptr(c),
                                 _stream(ac.device)), "gemm_mxfp4")
+    return c
+
+
+def gemm_nvfp4(a, b, out_dtype=torch.float32) -> torch.Tensor:
+    """C = float32(gsA gsB) * sum_k A'[m, k] B'[n, k] for two NVFP4 operands
+    (A' = E2M1 value times the E4M3 block scale), each a Quantized from
+    quantize(x, "nvfp4") of one [rows, K] tensor or a (codes [rows, K/2],
+    E4M3 scales [rows, K/16], float32 tensor scale [1]) triple, on the f16
+    matrix cores."""
+    ac, as_, ag = (a.codes, a.scales, a.aux) if isinstance(a, Quantized) else a
+    bc, bs, bg = (b.codes, b.scales, b.aux) if isinstance(b, Quantized) else b
+    K = a.shape[-1] if isinstance(a, Quantized) else 2 * ac.shape[-1]
+    ac, bc = _dev_tensor(ac, "a codes", (torch.uint8,)), _dev_tensor(bc, "b codes", (torch.uint8,))
+    as_, bs = _dev_tensor(as_, "a scales", (torch.uint8,)), _dev_tensor(bs, "b scales", (torch.uint8,))
+    ag, bg = _dev_tensor(ag, "a tensor scale", (torch.float32,)), _dev_tensor(bg, "b tensor scale", (torch.float32,))
+    def rows(q, codes):
+        if isinstance(q, Quantized):
+            return math.prod(q.shape[:-1])
+        return codes.shape[0] if codes.dim() == 2 else (codes.numel() // (K // 2) if K else 0)
+
+    M, N = rows(a, ac), rows(b, bc)
+    if K % 128 or ac.numel() != M * (K // 2) or bc.numel() != N * (K // 2) \
+            or as_.numel() != M * (K // 16) or bs.numel() != N * (K // 16):
+        raise ValueError("codes must be [rows, K/2] and scales [rows, K/16]")
+    if ag.numel() != 1 or bg.numel() != 1:
+        raise ValueError("each operand needs exactly one tensor scale (quantize one [rows, K] tensor)")
+    c = torch.empty((M, N), dtype=out_dtype, device=ac.device)
+    _check(lib().pqb_gemm_nvfp4(_ptr(ac), _ptr(as_), _ptr(ag), _ptr(bc), _ptr(bs), _ptr(bg), M, N, K,
+                                BF16 if out_dtype == torch.bfloat16 else F32, _ptr(c),
+                                _stream(ac.device)), "gemm_nvfp4")
     return c
 
 

@@ -386,6 +386,23 @@ def test_gemm_mxfp4_errors_before_launch(L):
     assert gm(m=0) == 0
 
 
+def test_gemm_nvfp4_errors_before_launch(L):
+    P = ctypes.c_void_p
+    fake = P(0x10000)
+    g = L.pqb_gemm_nvfp4
+
+    def gm(a=fake, sa=fake, ga=fake, b=fake, sb=fake, gb=fake, m=256, n=256, k=512, dt=0, c=fake):
+        return g(a, sa, ga, b, sb, gb, m, n, k, dt, c, None)
+
+    assert gm(dt=2) == -2
+    assert gm(k=500) == -4 and gm(n=200) == -4 and gm(m=-1) == -4 and gm(k=1 << 31) == -4
+    assert gm(sa=None) == -1 and gm(ga=None) == -1 and gm(gb=None) == -1 and gm(b=None) == -1
+    assert gm(c=None) == -1
+    assert gm(a=P(0x10008)) == -5 and gm(sb=P(0x10002)) == -5 and gm(gb=P(0x10002)) == -5
+    assert gm(c=P(0x10004)) == -5
+    assert gm(m=0) == 0 and gm(n=0, c=None) == 0
+
+
 def test_w4a16_errors_before_launch(L):
     P = ctypes.c_void_p
     fake, odd = P(0x10000), P(0x10008)
