@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 FP8_MFMA_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 matrix peak (no sparsity)
 FP4_MFMA_PEAK_TFLOPS = 10100.0      # MI355X dense FP4 / FP6 matrix peak
+BF16_MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 / f16 matrix peak
 METRIC = "quantize-pack GB/s (bytes in+out) and % of HBM peak, per format"
 HEADLINE_KERNEL = "k_multi<INT4> (fused INT4 g128 batch kernel)"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "k_multi_int4_llama8b_224w_counters.json")
@@ -615,7 +616,27 @@ def bench_gemm(torch, eng, synth, reps):
                            "scales applied by the matrix core, bf16 out"}
         log(f"{mkey}: {tf:.1f} TFLOP/s ({tf / FP4_MFMA_PEAK_TFLOPS * 100:.1f}% of "
             f"{FP4_MFMA_PEAK_TFLOPS:.0f})")
-        del x, w, qa, qw, a, b, c, cc, cs, qbuf, ma, mw
+        # both operands in NVFP4: E2M1 times E4M3 block scales widened to f16
+        # per wave, f16 matrix cores, tensor scales applied once
+        na, nw = eng.pqb.quantize(x, "nvfp4"), eng.pqb.quantize(w, "nvfp4")
+
+        def run_nv(i):
+            rc = eng.L.pqb_gemm_nvfp4(P(na.codes), P(na.scales), P(na.aux), P(nw.codes),
+                                      P(nw.scales), P(nw.aux), M, N, K, 1, P(c), eng.stream)
+            if rc != 0:
+                raise RuntimeError(f"pqb_gemm_nvfp4: status {rc}")
+
+        mean, med, mn = time_reps(torch, run_nv, max(10, reps), 3)
+        tf = flops / (mean * 1e-3) / 1e12
+        nkey = f"gemm_nvfp4_{M}x{N}x{K}_bf16"
+        out[nkey] = {"flops": flops, "ms": round(mean, 5), "ms_median": round(med, 5),
+                     "ms_min": round(mn, 5), "tflops": round(tf, 1),
+                     "frac_f16_mfma_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                     "op": "C = g sum_k (V dec(sA)) (V dec(sB)), both NVFP4 (E2M1 + E4M3 per 16, "
+                           "float32 per tensor), widened exactly to f16, bf16 out"}
+        log(f"{nkey}: {tf:.1f} TFLOP/s ({tf / BF16_MFMA_PEAK_TFLOPS * 100:.1f}% of the f16 peak "
+            f"{BF16_MFMA_PEAK_TFLOPS:.0f})")
+        del x, w, qa, qw, a, b, c, cc, cs, qbuf, ma, mw, na, nw
     torch.cuda.empty_cache()
     return out
 
