@@ -154,15 +154,19 @@ def test_gemm_of_engine_quantized_tensors(pqb):
     assert np.abs(got - ref).max() < 0.05 * np.abs(ref).max()
 
 
-def test_gemm_full_size_sampled(pqb):
-    """The benchmark's GEMM, activations [8192 x 2048] (1x128) times the weight
-    [7168 x 2048] (128x128), bf16 output: sampled rows of every column against
-    the oracle."""
-    x = synth.fp8_activation(rows=8192, cols=2048, device=DEV)
-    w = synth.fp8_weight(device=DEV)
+BENCH_SHAPES = [(8192, 7168, 2048), (8192, 2048, 7168)]
+
+
+@pytest.mark.parametrize("shape", BENCH_SHAPES)
+def test_gemm_full_size_sampled(pqb, shape):
+    """The benchmark's GEMMs, activations [M x K] (1x128) times the weight
+    [N x K] (128x128), bf16 output: sampled rows of every column against the
+    oracle."""
+    M, N, K = shape
+    x = synth.fp8_activation(rows=M, cols=K, device=DEV)
+    w = synth.fp8_weight(rows=N, cols=K, device=DEV)
     qa = pqb.quantize(x, "fp8_e4m3", "1x128")
     qw = pqb.quantize(w, "fp8_e4m3", "128x128")
-    M, N, K = 8192, 7168, 2048
     a, sa = qa.codes.reshape(M, K), qa.scales.reshape(M, K // 128)
     b, sb = qw.codes.reshape(N, K), qw.scales.reshape(N // 128, K // 128)
     c = pqb.gemm_fp8_blockscaled(a, sa, b, sb, out_dtype=torch.bfloat16)
@@ -198,14 +202,15 @@ def test_gemm_fused_fp8_quant_matches_oracle_quantizer(pqb, shape):
         check(pqb, a, sa, b, sb, f"fused {shape} (float32 result)")
 
 
-def test_gemm_fused_quant_full_size_sampled(pqb):
-    """Fused GEMM + 1x128 quantization at the benchmark's shape: sampled rows of
+@pytest.mark.parametrize("shape", BENCH_SHAPES)
+def test_gemm_fused_quant_full_size_sampled(pqb, shape):
+    """Fused GEMM + 1x128 quantization at the benchmark's shapes: sampled rows of
     the codes and scales against the oracle quantizer on the GEMM's float32 rows."""
-    x = synth.fp8_activation(rows=8192, cols=2048, device=DEV)
-    w = synth.fp8_weight(device=DEV)
+    M, N, K = shape
+    x = synth.fp8_activation(rows=M, cols=K, device=DEV)
+    w = synth.fp8_weight(rows=N, cols=K, device=DEV)
     qa = pqb.quantize(x, "fp8_e4m3", "1x128")
     qw = pqb.quantize(w, "fp8_e4m3", "128x128")
-    M, N, K = 8192, 7168, 2048
     args = (qa.codes.reshape(M, K), qa.scales.reshape(M, K // 128), qw.codes.reshape(N, K),
             qw.scales.reshape(N // 128, K // 128))
     codes, scales = pqb.gemm_fp8_blockscaled_quant(*args)

@@ -103,19 +103,21 @@ def test_mxgemm_of_engine_quantized_tensors(pqb):
     assert np.median(np.abs(got - ref) / (np.abs(x.double().numpy()) @ np.abs(w.double().numpy()).T)) < 0.15
 
 
-def test_mxgemm_full_size_sampled(pqb):
-    """Activations [8192 x 2048] times the weight [7168 x 2048], both MXFP4,
-    bf16 output: sampled rows of every column against the oracle."""
-    x = synth.fp8_activation(rows=8192, cols=2048, device=DEV)
-    w = synth.fp8_weight(device=DEV)
+@pytest.mark.parametrize("shape", [(8192, 7168, 2048), (8192, 2048, 7168)])
+def test_mxgemm_full_size_sampled(pqb, shape):
+    """The benchmark's shapes, activations [M x K] times a weight [N x K], both
+    MXFP4, bf16 output: sampled rows of every column against the oracle."""
+    M, N, K = shape
+    x = synth.fp8_activation(rows=M, cols=K, device=DEV)
+    w = synth.fp8_weight(rows=N, cols=K, device=DEV)
     qa, qw = pqb.quantize(x, "mxfp4"), pqb.quantize(w, "mxfp4")
     c = pqb.gemm_mxfp4(qa, qw, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
-    rows = np.sort(rng("full").choice(8192, 24, replace=False))
-    rows[-1] = 8191
-    a, sa = qa.codes.cpu().numpy().reshape(8192, 1024), qa.scales.cpu().numpy().reshape(8192, 64)
-    b, sb = qw.codes.cpu().numpy().reshape(7168, 1024), qw.scales.cpu().numpy().reshape(7168, 64)
+    rows = np.sort(rng("full").choice(M, 24, replace=False))
+    rows[-1] = M - 1
+    a, sa = qa.codes.cpu().numpy().reshape(M, K // 2), qa.scales.cpu().numpy().reshape(M, K // 32)
+    b, sb = qw.codes.cpu().numpy().reshape(N, K // 2), qw.scales.cpu().numpy().reshape(N, K // 32)
     want, S = oracle.mxfp4_gemm(a[rows], sa[rows], b, sb, abs_sum=True)
-    tol = (17 + 2048 // 128) * U * S * 1.01
+    tol = (17 + K // 128) * U * S * 1.01
     got = c[torch.from_numpy(rows).to(DEV)].float().cpu().numpy().astype(np.float64)
     assert np.all(np.abs(got - want) <= tol + 2.0 ** -8 * (np.abs(want) + tol))
