@@ -479,6 +479,21 @@ pqb_status pqb_check_recip(uint32_t first_bits, int64_t n, float* out, void* str
 pqb_status pqb_check_div(const float* s, int64_t ns, uint32_t x_first_bits, int64_t nx,
                          float* out, void* stream);
 
+/* Measurement reference, not a quantizer: the memory pattern of the
+ * quantizers with nothing computed, so that their bandwidth can be set beside
+ * what the same loads and stores reach at the same read:write mix.  Reads
+ * read_bytes from src and writes read_bytes / reads_per_write to dst, in
+ * chunks of 8192 source bytes: chunk c's 8 KiB are 8 tiles of 1 KiB, and
+ * output tile j of the chunk (at dst + c * 8192 / reads_per_write + 1024 j)
+ * is the bytewise XOR of its source tiles reads_per_write * j ..
+ * reads_per_write * (j + 1) - 1, loaded and stored 16 bytes per lane with
+ * non-temporal hints as the quantizers' bf16 loads and code stores are.
+ * reads_per_write is 1, 2 or 4; read_bytes a multiple of 8192, at most 2^38;
+ * src and dst 16-byte aligned device buffers that do not overlap.  Errors,
+ * before any launch: PQB_ERR_ENUM, PQB_ERR_SHAPE, PQB_ERR_NULL, PQB_ERR_ALIGN. */
+pqb_status pqb_stream_reference(const void* src, int64_t read_bytes, int reads_per_write,
+                                void* dst, void* stream);
+
 const char* pqb_status_string(pqb_status s);
 int pqb_abi_version(void);
 /* A digest of the sources the library was built from (16 hex digits; the

@@ -13,7 +13,7 @@ generators in `synth` import without the engine.
 _EXPORTS = {
     "quantize", "quantize_batch", "dequantize", "dequantize_batch", "query_sizes", "kv_write_fp8", "kv_write_fp8_ex",
     "KV_MODES", "kv_write_kivi", "kv_read_kivi", "kivi_layouts", "gemm_fp8_blockscaled", "gemm_fp8_blockscaled_quant",
-    "gemv_w4a16", "gemv_w4a16_batch", "gemm_w4a16", "gemm_w4a16_batch", "gemm_mxfp4", "gemm_nvfp4", "encode_e4m3", "encode_e5m2", "encode_e2m1",
+    "gemv_w4a16", "gemv_w4a16_batch", "gemm_w4a16", "gemm_w4a16_batch", "gemm_mxfp4", "gemm_nvfp4", "stream_reference", "encode_e4m3", "encode_e5m2", "encode_e2m1",
     "check_recip", "check_div",
     "fp8_per_tensor", "fp8_per_row", "fp8_blockwise", "mxfp4", "nvfp4", "fp8_kv_write",
     "Quantized", "PqbError", "abi_version", "status_string", "lib", "FORMATS", "GRANS",

@@ -95,6 +95,7 @@ def lib():
         L.pqb_gemv_w4a16.argtypes = [P, I64, P, P, P, I64, I64, I, P, P]
         L.pqb_gemm_mxfp4.argtypes = [P, P, P, P, I64, I64, I64, I, P, P]
         L.pqb_gemm_nvfp4.argtypes = [P, P, P, P, P, P, I64, I64, I64, I, P, P]
+        L.pqb_stream_reference.argtypes = [P, I64, I, P, P]
         L.pqb_gemv_w4a16_batch.argtypes = [ctypes.POINTER(_W4Job), I64, I64, I, P]
         L.pqb_gemm_w4a16.argtypes = [P, I64, P, P, P, I64, I64, I, P, P]
         L.pqb_gemm_w4a16_batch.argtypes = [ctypes.POINTER(_W4Job), I64, I64, I, P]
@@ -108,7 +109,7 @@ def lib():
                   "pqb_kv_write_fp8", "pqb_kv_write_fp8_ex", "pqb_kv_write_kivi",
                   "pqb_kv_read_kivi", "pqb_gemm_fp8_blockscaled",
                   "pqb_gemm_fp8_blockscaled_quant", "pqb_gemv_w4a16",
-                  "pqb_gemv_w4a16_batch", "pqb_gemm_mxfp4", "pqb_gemm_nvfp4", "pqb_gemm_w4a16",
+                  "pqb_gemv_w4a16_batch", "pqb_gemm_mxfp4", "pqb_gemm_nvfp4", "pqb_stream_reference", "pqb_gemm_w4a16",
                   "pqb_gemm_w4a16_batch",
                   "pqb_encode_e4m3", "pqb_encode_e5m2", "pqb_encode_e2m1",
                   "pqb_check_recip", "pqb_check_div"):
@@ -525,6 +526,21 @@ def gemm_nvfp4(a, b, out_dtype=torch.float32) -> torch.Tensor:
                                 BF16 if out_dtype == torch.bfloat16 else F32, _ptr(c),
                                 _stream(ac.device)), "gemm_nvfp4")
     return c
+
+
+def stream_reference(src: torch.Tensor, reads_per_write: int, dst: torch.Tensor | None = None) -> torch.Tensor:
+    """The quantizers' memory pattern with nothing computed (a bandwidth
+    reference): reads all of src (a multiple of 8192 bytes) and writes
+    src.nbytes / reads_per_write bytes, each 1 KiB output tile the XOR of
+    reads_per_write consecutive 1 KiB source tiles of its 8 KiB chunk."""
+    if not isinstance(src, torch.Tensor) or src.device.type != "cuda" or not src.is_contiguous():
+        raise ValueError("src must be a contiguous GPU tensor")
+    nb = src.numel() * src.element_size()
+    if dst is None:
+        dst = torch.empty((nb // reads_per_write,), dtype=torch.uint8, device=src.device)
+    _check(lib().pqb_stream_reference(_ptr(src), nb, reads_per_write, _ptr(dst), _stream(src.device)),
+           "stream_reference")
+    return dst
 
 
 def _w4_rows(codes: torch.Tensor, K: int) -> int:

@@ -403,6 +403,18 @@ def test_gemm_nvfp4_errors_before_launch(L):
     assert gm(m=0) == 0 and gm(n=0, c=None) == 0
 
 
+def test_stream_reference_errors_before_launch(L):
+    P = ctypes.c_void_p
+    fake = P(0x10000)
+    f = L.pqb_stream_reference
+    assert f(fake, 8192, 3, fake, None) == -2 and f(fake, 8192, 0, fake, None) == -2
+    assert f(fake, 8000, 1, fake, None) == -4 and f(fake, -8192, 1, fake, None) == -4
+    assert f(fake, (1 << 38) + 8192, 1, fake, None) == -4
+    assert f(None, 8192, 1, fake, None) == -1 and f(fake, 8192, 2, None, None) == -1
+    assert f(P(0x10008), 8192, 1, fake, None) == -5 and f(fake, 8192, 4, P(0x10004), None) == -5
+    assert f(None, 0, 1, None, None) == 0
+
+
 def test_w4a16_errors_before_launch(L):
     P = ctypes.c_void_p
     fake, odd = P(0x10000), P(0x10008)
