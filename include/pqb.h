@@ -483,16 +483,17 @@ pqb_status pqb_check_div(const float* s, int64_t ns, uint32_t x_first_bits, int6
  * quantizers with nothing computed, so that their bandwidth can be set beside
  * what the same loads and stores reach at the same read:write mix.  Reads
  * read_bytes from src and writes read_bytes / reads_per_write to dst, in
- * chunks of 8192 source bytes: chunk c's 8 KiB are 8 tiles of 1 KiB, and
- * output tile j of the chunk (at dst + c * 8192 / reads_per_write + 1024 j)
- * is the bytewise XOR of its source tiles reads_per_write * j ..
- * reads_per_write * (j + 1) - 1, loaded and stored 16 bytes per lane with
- * non-temporal hints as the quantizers' bf16 loads and code stores are.
- * reads_per_write is 1, 2 or 4; read_bytes a multiple of 8192, at most 2^38;
- * src and dst 16-byte aligned device buffers that do not overlap.  Errors,
- * before any launch: PQB_ERR_ENUM, PQB_ERR_SHAPE, PQB_ERR_NULL, PQB_ERR_ALIGN. */
+ * chunks of T = tiles_per_wave tiles of 1 KiB per wave: output tile j of chunk
+ * c (at dst + c * 1024 * T / reads_per_write + 1024 j) is the bytewise XOR of
+ * the chunk's source tiles reads_per_write * j .. reads_per_write * (j + 1) -
+ * 1, loaded and stored 16 bytes per lane with non-temporal hints as the
+ * quantizers' bf16 loads and code stores are.  reads_per_write is 1, 2 or 4;
+ * tiles_per_wave 4 or 8 (the quantizers take 8); read_bytes a multiple of
+ * 8192, at most 2^38; src and dst 16-byte aligned device buffers that do not
+ * overlap.  Errors, before any launch: PQB_ERR_ENUM, PQB_ERR_SHAPE,
+ * PQB_ERR_NULL, PQB_ERR_ALIGN. */
 pqb_status pqb_stream_reference(const void* src, int64_t read_bytes, int reads_per_write,
-                                void* dst, void* stream);
+                                int tiles_per_wave, void* dst, void* stream);
 
 const char* pqb_status_string(pqb_status s);
 int pqb_abi_version(void);

@@ -697,13 +697,15 @@ pqb_status pqb_gemm_mxfp4(const uint8_t* a, const uint8_t* a_scales, const uint8
 }
 
 pqb_status pqb_stream_reference(const void* src, int64_t read_bytes, int reads_per_write,
-                                void* dst, void* stream) {
+                                int tiles_per_wave, void* dst, void* stream) {
   if (reads_per_write != 1 && reads_per_write != 2 && reads_per_write != 4) return PQB_ERR_ENUM;
+  if (tiles_per_wave != 4 && tiles_per_wave != 8) return PQB_ERR_ENUM;
   if (read_bytes < 0 || read_bytes % 8192 || read_bytes > ((int64_t)1 << 38)) return PQB_ERR_SHAPE;
   if (read_bytes == 0) return PQB_OK;
   if (!src || !dst) return PQB_ERR_NULL;
   if (!aligned(src, 16) || !aligned(dst, 16)) return PQB_ERR_ALIGN;
-  return hip_status(launch_stream_ref(src, read_bytes, reads_per_write, dst, (hipStream_t)stream));
+  return hip_status(launch_stream_ref(src, read_bytes, reads_per_write, tiles_per_wave, dst,
+                                     (hipStream_t)stream));
 }
 
 pqb_status pqb_gemm_nvfp4(const uint8_t* a, const uint8_t* a_scales, const float* a_gs,

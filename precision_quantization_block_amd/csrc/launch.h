@@ -151,8 +151,8 @@ hipError_t launch_gemm_mxfp4(const uint8_t* a, const uint8_t* a_scales, const ui
                              const uint8_t* b_scales, int64_t M, int64_t N, int64_t K,
                              bool out_bf16, void* c, hipStream_t st);
 // Streaming reference: reads read_bytes, writes read_bytes / reads_per_write.
-hipError_t launch_stream_ref(const void* src, int64_t read_bytes, int reads_per_write, void* dst,
-                             hipStream_t st);
+hipError_t launch_stream_ref(const void* src, int64_t read_bytes, int reads_per_write,
+                             int tiles_per_wave, void* dst, hipStream_t st);
 hipError_t launch_gemm_nvfp4(const uint8_t* a, const uint8_t* a_scales, const float* a_gs,
                              const uint8_t* b, const uint8_t* b_scales, const float* b_gs, int64_t M,
                              int64_t N, int64_t K, bool out_bf16, void* c, hipStream_t st);

@@ -95,7 +95,7 @@ def lib():
         L.pqb_gemv_w4a16.argtypes = [P, I64, P, P, P, I64, I64, I, P, P]
         L.pqb_gemm_mxfp4.argtypes = [P, P, P, P, I64, I64, I64, I, P, P]
         L.pqb_gemm_nvfp4.argtypes = [P, P, P, P, P, P, I64, I64, I64, I, P, P]
-        L.pqb_stream_reference.argtypes = [P, I64, I, P, P]
+        L.pqb_stream_reference.argtypes = [P, I64, I, I, P, P]
         L.pqb_gemv_w4a16_batch.argtypes = [ctypes.POINTER(_W4Job), I64, I64, I, P]
         L.pqb_gemm_w4a16.argtypes = [P, I64, P, P, P, I64, I64, I, P, P]
         L.pqb_gemm_w4a16_batch.argtypes = [ctypes.POINTER(_W4Job), I64, I64, I, P]
@@ -528,17 +528,20 @@ def gemm_nvfp4(a, b, out_dtype=torch.float32) -> torch.Tensor:
     return c
 
 
-def stream_reference(src: torch.Tensor, reads_per_write: int, dst: torch.Tensor | None = None) -> torch.Tensor:
+def stream_reference(src: torch.Tensor, reads_per_write: int, dst: torch.Tensor | None = None,
+                     tiles_per_wave: int = 8) -> torch.Tensor:
     """The quantizers' memory pattern with nothing computed (a bandwidth
     reference): reads all of src (a multiple of 8192 bytes) and writes
     src.nbytes / reads_per_write bytes, each 1 KiB output tile the XOR of
-    reads_per_write consecutive 1 KiB source tiles of its 8 KiB chunk."""
+    reads_per_write consecutive 1 KiB source tiles of its chunk of
+    tiles_per_wave tiles."""
     if not isinstance(src, torch.Tensor) or src.device.type != "cuda" or not src.is_contiguous():
         raise ValueError("src must be a contiguous GPU tensor")
     nb = src.numel() * src.element_size()
     if dst is None:
         dst = torch.empty((nb // reads_per_write,), dtype=torch.uint8, device=src.device)
-    _check(lib().pqb_stream_reference(_ptr(src), nb, reads_per_write, _ptr(dst), _stream(src.device)),
+    _check(lib().pqb_stream_reference(_ptr(src), nb, reads_per_write, tiles_per_wave, _ptr(dst),
+                                      _stream(src.device)),
            "stream_reference")
     return dst
 

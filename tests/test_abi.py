@@ -407,12 +407,13 @@ def test_stream_reference_errors_before_launch(L):
     P = ctypes.c_void_p
     fake = P(0x10000)
     f = L.pqb_stream_reference
-    assert f(fake, 8192, 3, fake, None) == -2 and f(fake, 8192, 0, fake, None) == -2
-    assert f(fake, 8000, 1, fake, None) == -4 and f(fake, -8192, 1, fake, None) == -4
-    assert f(fake, (1 << 38) + 8192, 1, fake, None) == -4
-    assert f(None, 8192, 1, fake, None) == -1 and f(fake, 8192, 2, None, None) == -1
-    assert f(P(0x10008), 8192, 1, fake, None) == -5 and f(fake, 8192, 4, P(0x10004), None) == -5
-    assert f(None, 0, 1, None, None) == 0
+    assert f(fake, 8192, 3, 8, fake, None) == -2 and f(fake, 8192, 0, 8, fake, None) == -2
+    assert f(fake, 8192, 1, 2, fake, None) == -2 and f(fake, 8192, 4, 16, fake, None) == -2
+    assert f(fake, 8000, 1, 8, fake, None) == -4 and f(fake, -8192, 1, 4, fake, None) == -4
+    assert f(fake, (1 << 38) + 8192, 1, 8, fake, None) == -4
+    assert f(None, 8192, 1, 8, fake, None) == -1 and f(fake, 8192, 2, 4, None, None) == -1
+    assert f(P(0x10008), 8192, 1, 8, fake, None) == -5 and f(fake, 8192, 4, 4, P(0x10004), None) == -5
+    assert f(None, 0, 1, 8, None, None) == 0
 
 
 def test_w4a16_errors_before_launch(L):
