@@ -144,3 +144,16 @@ def test_nvgemm_full_size_sampled(pqb, shape):
     tol = (34 + K // 32) * U * S * 1.01
     got = c[torch.from_numpy(rows).to(DEV)].float().cpu().numpy().astype(np.float64)
     assert np.all(np.abs(got - want) <= tol + 2.0 ** -8 * (np.abs(want) + tol))
+
+
+def test_nvgemm_scale_sign_bit_is_ignored(pqb):
+    """The header reads block-scale bytes without their sign bit: setting bit 7
+    of every scale byte leaves the product bit for bit unchanged."""
+    r = rng("sign")
+    M, N, K = 130, 256, 384
+    a, sa = operand(r, M, K, 1, 127)
+    b, sb = operand(r, N, K, 1, 127)
+    g = dev(np.float32([0.75]))
+    base = pqb.gemm_nvfp4((dev(a), dev(sa), g), (dev(b), dev(sb), g), out_dtype=torch.float32)
+    signed = pqb.gemm_nvfp4((dev(a), dev(sa | 0x80), g), (dev(b), dev(sb | 0x80), g), out_dtype=torch.float32)
+    assert torch.equal(base.view(torch.int32), signed.view(torch.int32))
