@@ -89,14 +89,16 @@ class Engine:
         if rc != 0:
             raise RuntimeError(f"pqb_quantize {fmt}/{gran}: status {rc}")
 
-    def quantize_call(self, x, fmt, gran, shape, buf):
+    def quantize_call(self, x, fmt, gran, shape, buf, stream=None):
         """pqb_quantize on `x` into `buf` with its arguments marshalled once: the
         returned call costs one ctypes call, so that a loop of small tensors times
-        the library rather than Python."""
+        the library rather than Python.  `stream` (a raw handle) defaults to the
+        engine's stream."""
         ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+        st = self.stream if stream is None else ctypes.c_void_p(stream)
         args = (ptr(x), 1 if x.dtype == self.torch.bfloat16 else 0, *shape,
                 self.pqb.FORMATS[fmt], self.pqb.GRANS[gran], ptr(buf["codes"]), ptr(buf["scales"]),
-                ptr(buf["aux"]), ptr(buf["workspace"]), buf["sizes"]["workspace"], self.stream)
+                ptr(buf["aux"]), ptr(buf["workspace"]), buf["sizes"]["workspace"], st)
         f = self.L.pqb_quantize
 
         def call():
@@ -105,12 +107,13 @@ class Engine:
                 raise RuntimeError(f"pqb_quantize {fmt}/{gran}: status {rc}")
         return call
 
-    def dequantize_call(self, buf, fmt, gran, shape, out):
+    def dequantize_call(self, buf, fmt, gran, shape, out, stream=None):
         """pqb_dequantize of `buf` into `out`, arguments marshalled once."""
         ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+        st = self.stream if stream is None else ctypes.c_void_p(stream)
         args = (ptr(buf["codes"]), ptr(buf["scales"]), ptr(buf["aux"]), self.pqb.FORMATS[fmt],
                 self.pqb.GRANS[gran], *shape, 1 if out.dtype == self.torch.bfloat16 else 0,
-                ptr(out), self.stream)
+                ptr(out), st)
         f = self.L.pqb_dequantize
 
         def call():
@@ -380,6 +383,23 @@ def bench_extras(torch, eng, synth, reps, only=None):
     def want(*names):
         return only is None or any(only in n for n in names)
 
+    def graph_time(r, nb, nsets, make_calls):
+        """The same calls (one per buffer set) captured once in a HIP graph and
+        replayed: GPU time per call without the host's launch cost, added to
+        record `r`.  The library issues kernel launches only, so a replay
+        rewrites exactly what the eager calls wrote."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        calls = make_calls(side.cuda_stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for c in calls:
+                c()
+        t = time_loop(torch, lambda i: g.replay(), max(4, reps // 2), 2) / nsets
+        r["graph_ms_per_call"] = round(t, 5)
+        r["graph_gbs"] = round(nb / (t * 1e-3) / 1e9, 1)
+        del g
+
     def one(name, x, fmt, gran, shape, dq_dtype=None):
         """Quantize (and dequantize) `x`, rotating over enough buffer sets that
         the Infinity Cache cannot serve repeated reads: at least 4 sets and
@@ -400,6 +420,10 @@ def bench_extras(torch, eng, synth, reps, only=None):
         out[name] = rec(nb, t, in_bytes if two_pass else 0, op=f"quantize {fmt}/{gran}",
                         shape=list(shape), dtype=str(x.dtype).replace("torch.", ""),
                         rotated_sets=nsets)
+        if in_bytes < (64 << 20):
+            graph_time(out[name], nb, nsets,
+                       lambda st: [eng.quantize_call(xs[i], fmt, gran, shape, bufs[i], st)
+                                   for i in range(nsets)])
         if dq_dtype is not None:
             o = [torch.empty(shape, dtype=dq_dtype, device=dev) for _ in range(nsets)]
             nbd = out_bytes(bufs[0]["sizes"]) + o[0].numel() * o[0].element_size()
@@ -408,7 +432,12 @@ def bench_extras(torch, eng, synth, reps, only=None):
             out[name + "_dequant"] = rec(nbd, t, op=f"dequantize {fmt} -> "
                                          f"{str(dq_dtype).replace('torch.', '')}",
                                          shape=list(shape), rotated_sets=nsets)
-        log(f"{name}: {out[name]['gbs']} GB/s over {nsets} buffer sets")
+            if in_bytes < (64 << 20):
+                graph_time(out[name + "_dequant"], nbd, nsets,
+                           lambda st: [eng.dequantize_call(bufs[i], fmt, gran, shape, o[i], st)
+                                       for i in range(nsets)])
+        log(f"{name}: {out[name]['gbs']} GB/s over {nsets} buffer sets"
+            + (f", {out[name]['graph_gbs']} GB/s replayed from a graph" if "graph_gbs" in out[name] else ""))
         del xs, bufs
         torch.cuda.empty_cache()
 
