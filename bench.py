@@ -907,8 +907,8 @@ def main():
     ap.add_argument("--only", default=None,
                     help="run only the format workloads whose name contains this string, or "
                          "'w8a8' (the FP8 W8A8 step), or 'llama8b_224w_int4' (the headline set "
-                         "with its per-tensor and dequantization records); no headline line, "
-                         "prints the records as JSON")
+                         "with its per-tensor and dequantization records), or 'stream_reference' "
+                         "(the copy ceiling); no headline line, prints the records as JSON")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -935,6 +935,10 @@ def main():
         h = bench_headline(torch, eng, synth, args.steps, args.warmup)
         int4_records_extra(torch, eng, h, args.reps)
         print(json.dumps(_RECORDS), flush=True)
+        return
+    if args.only == "stream_reference":
+        print(json.dumps({"stream_reference": stream_ceiling(torch, eng),
+                          "hbm_reference": hbm_reference(torch)}), flush=True)
         return
     if args.only is not None:
         print(json.dumps(bench_extras(torch, eng, synth, args.reps, args.only)), flush=True)
