@@ -997,10 +997,8 @@ def main():
         record("hbm_reference", ref)
         sc = stream_ceiling(torch, eng)
         record("stream_reference", sc)
-        line["copy_ceiling"] = {"kernel": "pqb_stream_reference: the quantizers' 16-byte non-temporal loads and "
-                                          "stores, nothing computed, 1 GiB read and outputs rotated over 1 GiB, the "
-                                          "faster of 8 and 4 KiB per wave; GB/s at 1, 2, 4 bytes read per byte "
-                                          "written",
+        line["copy_ceiling"] = {"kernel": "pqb_stream_reference (16-byte nt loads/stores, no arithmetic; 1 GiB "
+                                          "read, outputs rotated); rN = GB/s at N bytes read per byte written",
                                 "r1_gbs": sc["r1_gbs"], "r2_gbs": sc["r2_gbs"], "r4_gbs": sc["r4_gbs"],
                                 "headline_frac_of_r4": round(value / sc["r4_gbs"], 4),
                                 "torch_best_gbs": max(ref.values())}
