@@ -14,6 +14,13 @@
 // 64 x 64 quarter at (64 wm, 64 wn), as 4 x 4 tiles of 16 x 16.  One
 // v_mfma_f32_16x16x128_f8f6f4 covers a whole 128-deep K block of one 16 x 16
 // tile, so every MFMA result is promoted at once: acc = fma(P, sA sB, acc).
+// The products are taken transposed, weight rows as the matrix core's first
+// operand, so that each lane's results share one activation row per tile and
+// one scale product sA sB (4 multiplies per block instead of 16).  The four
+// products of a column of tiles are issued before any of them is promoted,
+// into distinct registers: with one result register set the compiler routed
+// every product through the same accumulation registers and waited out each
+// one's latency before the next could issue.
 // The 128 x 128-byte tiles of A and B for one K block, and its 128 activation
 // scales, go straight from global memory into LDS (global_load_lds_dwordx4:
 // each wave instruction fills 1 KiB of LDS, lane l the 16 bytes at 16 l) in a
@@ -36,7 +43,8 @@
 // the MXFP4 product also reads (5-6% faster).  Each 16-byte chunk is 16
 // consecutive K elements either way, so the matrix core still sums aligned
 // groups of 8 consecutive K elements.  Result layout: lane l, register r is
-// C[4 (l >> 4) + r][l & 15].
+// D[4 (l >> 4) + r][l & 15] of D = (first operand) x (second operand)^T, i.e.
+// C[l & 15][4 (l >> 4) + r] for the transposed FP8 products.
 #include "launch.h"
 #include "quant.h"
 
@@ -120,10 +128,26 @@ __device__ __forceinline__ void stage_tile(const v4f (&acc)[4][4], uint8_t* lds,
         out_lds[(mt * 16 + 4 * q + r) * kGOutStride + nt * 16 + r16] = acc[mt][nt][r];
 }
 
-template <int kOut>
+// The same for a wave whose products were taken transposed (weight rows as
+// the matrix core's first operand): acc[mt][nt][r] is row 16 mt + (lane & 15),
+// column 16 nt + 4 (lane >> 4) + r, so each lane writes 4 consecutive floats.
+__device__ __forceinline__ void stage_tile_t(const v4f (&acc)[4][4], uint8_t* lds, int wave, int lane) {
+  const int r16 = lane & 15, q = lane >> 4;
+  float* out_lds = reinterpret_cast<float*>(lds) + wave * 64 * kGOutStride;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+      *reinterpret_cast<v4f*>(&out_lds[(mt * 16 + r16) * kGOutStride + nt * 16 + 4 * q]) = acc[mt][nt];
+}
+
+template <int kOut, bool kTransposed = false>
 __device__ __forceinline__ void stage_and_store(const v4f (&acc)[4][4], uint8_t* lds, int wave,
                                                 int lane, int m0, int n0, int M, int N, void* C) {
-  stage_tile(acc, lds, wave, lane);
+  if constexpr (kTransposed)
+    stage_tile_t(acc, lds, wave, lane);
+  else
+    stage_tile(acc, lds, wave, lane);
   __syncthreads();
   const float* out_lds = reinterpret_cast<const float*>(lds) + wave * 64 * kGOutStride;
   const int row0 = m0 + (wave >> 1) * 64, col0 = n0 + (wave & 1) * 64;
@@ -267,13 +291,12 @@ __global__ __launch_bounds__(kGThreads) void k_gemm_fp8_bs(const uint8_t* __rest
     const float* ls = reinterpret_cast<const float*>(sl + kGTileA + kGTileB);
     const float sb = sB_col[kb];
     v8i af[4];
-    v4f sab[4];
+    float sab[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const int r = wm * 64 + mt * 16;               // 16 rows from one wave's scale run
-      af[mt] = frag(sl, r + r16, q);
-      const v4f s4 = *reinterpret_cast<const v4f*>(&ls[(r >> 5) * 64 + (r & 31) + 4 * q]);
-      sab[mt] = s4 * sb;
+      const int r = wm * 64 + mt * 16 + r16;         // this lane's activation row
+      af[mt] = frag(sl, r, q);
+      sab[mt] = ls[(r >> 5) * 64 + (r & 31)] * sb;
     }
     // The wave that has reached its matrix products is served first: the
     // other waves of the CU are then mostly waiting on LDS reads or DMA.
@@ -281,23 +304,26 @@ __global__ __launch_bounds__(kGThreads) void k_gemm_fp8_bs(const uint8_t* __rest
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       const v8i bf = frag(sl + kGTileA, wn * 64 + nt * 16 + r16, q);
+      v4f p[4];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            af[mt], bf, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
+      for (int mt = 0; mt < 4; ++mt)
+        p[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            bf, af[mt], v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[mt][nt][r] = __builtin_fmaf(p[r], sab[mt][r], acc[mt][nt][r]);
-      }
-    }    __builtin_amdgcn_s_setprio(0);
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[mt][nt][r] = __builtin_fmaf(p[mt][r], sab[mt], acc[mt][nt][r]);
+    }
+    __builtin_amdgcn_s_setprio(0);
   }
   barrier();  // every wave done with the ring before it becomes the output stage
 
   if constexpr (kOut == kOutFp8) {
-    stage_tile(acc, lds, wave, lane);
+    stage_tile_t(acc, lds, wave, lane);
     __syncthreads();
     quantize_tile_rows(lds, tid, m0, n0, M, N, reinterpret_cast<uint8_t*>(C), c_scales);
   } else {
-    stage_and_store<kOut>(acc, lds, wave, lane, m0, n0, M, N, C);
+    stage_and_store<kOut, true>(acc, lds, wave, lane, m0, n0, M, N, C);
   }
 }
 
