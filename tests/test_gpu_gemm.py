@@ -154,6 +154,34 @@ def test_gemm_of_engine_quantized_tensors(pqb):
     assert np.abs(got - ref).max() < 0.05 * np.abs(ref).max()
 
 
+@pytest.mark.parametrize("K", [0, 128, 256, 384])
+def test_gemm_three_per_cu_ragged(pqb, K):
+    """528 tiles of 128 x 128, three or more per CU, so the kernel that runs
+    three workgroups per CU computes them: a ragged last row of tiles
+    (M = 4174) and 0 to 3 K blocks.  Sampled rows, the ragged tile's among
+    them, against the oracle in float32 and bf16; the fused FP8 form's codes
+    and scales on the same rows against the oracle quantizer of the float32
+    result."""
+    M, N = 4174, 2048
+    r = rng(f"three{K}")
+    a, b = random_codes(r, (M, K)), random_codes(r, (N, K))
+    sa = (r.uniform(0.5, 2, (M, K // 128)) * 2.0 ** r.integers(-6, 6, (M, 1))).astype(np.float32)
+    sb = (r.uniform(0.5, 2, (N // 128, K // 128)) * 2.0 ** -8).astype(np.float32)
+    ad, sad, bd, sbd = to_dev(a), to_dev(sa), to_dev(b), to_dev(sb)
+    c32 = pqb.gemm_fp8_blockscaled(ad, sad, bd, sbd, out_dtype=torch.float32)
+    codes, scales = pqb.gemm_fp8_blockscaled_quant(ad, sad, bd, sbd)
+    if K == 0:
+        assert torch.count_nonzero(c32).item() == 0 and torch.count_nonzero(codes).item() == 0
+        return
+    rows = np.unique(np.concatenate([r.choice(4096, 32, replace=False),
+                                     [4096, 4100, 4150, M - 2, M - 1]]))
+    check(pqb, a, sa, b, sb, f"three per CU, K = {K}", rows=rows)
+    sel = torch.from_numpy(rows).to(DEV)
+    oc, os_ = oracle.fp8_quantize(c32[sel].cpu().numpy()[None], "1x128")
+    assert np.array_equal(codes[sel].cpu().numpy().reshape(-1), oc.reshape(-1))
+    assert np.array_equal(scales[sel].cpu().numpy().reshape(-1).view(np.int32), os_.reshape(-1).view(np.int32))
+
+
 BENCH_SHAPES = [(8192, 7168, 2048), (8192, 2048, 7168)]
 
 
