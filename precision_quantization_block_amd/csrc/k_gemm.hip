@@ -45,6 +45,8 @@
 // groups of 8 consecutive K elements.  Result layout: lane l, register r is
 // D[4 (l >> 4) + r][l & 15] of D = (first operand) x (second operand)^T, i.e.
 // C[l & 15][4 (l >> 4) + r] for the transposed FP8 products.
+#include <atomic>
+
 #include "launch.h"
 #include "quant.h"
 
@@ -121,6 +123,19 @@ __device__ __forceinline__ void wait_blocks(int blocks) {
 }
 
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// The tile (row tm, column tn) that this workgroup computes.  Workgroups i,
+// i + 8, ... run on one XCD: each XCD takes a contiguous run of tiles, walked
+// down bands of up to 8 tile rows, so neighbouring workgroups on an XCD share
+// A rows and B columns in its L2.  The grid is tiles_m x tiles_n workgroups.
+__device__ __forceinline__ void gemm_tile(int tiles_n, int& tm, int& tn) {
+  const int nwg = gridDim.x, per = nwg / 8;
+  const int t = per * 8 == nwg ? (blockIdx.x & 7) * per + (blockIdx.x >> 3) : blockIdx.x;
+  const int band = t / (8 * tiles_n), rem = t - band * 8 * tiles_n;
+  const int band_rows = min(8, nwg / tiles_n - band * 8);
+  tm = band * 8 + rem % band_rows;
+  tn = rem / band_rows;
+}
 
 // Output forms: float32, bf16, or FP8 E4M3 codes with one scale per 128
 // columns of a row (the 1x128 activation layout), quantized in the epilogue.
@@ -255,14 +270,8 @@ __global__ __launch_bounds__(kGThreads) void k_gemm_fp8_bs(const uint8_t* __rest
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // Workgroups i, i + 8, ... run on one XCD: each XCD takes a contiguous run of
-  // tiles, walked down bands of up to 8 tile rows, so neighbouring workgroups
-  // on an XCD share A rows and B columns in its L2.
-  const int nwg = gridDim.x, per = nwg / 8;
-  const int t = per * 8 == nwg ? (blockIdx.x & 7) * per + (blockIdx.x >> 3) : blockIdx.x;
-  const int band = t / (8 * tiles_n), rem = t - band * 8 * tiles_n;
-  const int band_rows = min(8, nwg / tiles_n - band * 8);
-  const int tm = band * 8 + rem % band_rows, tn = rem / band_rows;
+  int tm, tn;
+  gemm_tile(tiles_n, tm, tn);
   const int m0 = tm * kGTM, n0 = tn * kGT;
   const int nkb = K / kGT;
 
@@ -374,12 +383,8 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gemm_fp8_bs3(const uint8_t* __
   __shared__ __align__(16) uint8_t lds[kG3LdsBytes];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // XCD-aware tile order, as in k_gemm_fp8_bs
-  const int nwg = gridDim.x, per = nwg / 8;
-  const int t = per * 8 == nwg ? (blockIdx.x & 7) * per + (blockIdx.x >> 3) : blockIdx.x;
-  const int band = t / (8 * tiles_n), rem = t - band * 8 * tiles_n;
-  const int band_rows = min(8, nwg / tiles_n - band * 8);
-  const int tm = band * 8 + rem % band_rows, tn = rem / band_rows;
+  int tm, tn;
+  gemm_tile(tiles_n, tm, tn);
   const int m0 = tm * kGTM, n0 = tn * kGT;
   const int nkb = K / kGT;
 
@@ -505,11 +510,8 @@ __global__ __launch_bounds__(kGThreads) void k_gemm_mxfp4(const uint8_t* __restr
   auto slot = [&](int s) { return lds + s * kMxSlotBytes; };
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nwg = gridDim.x, per = nwg / 8;
-  const int t = per * 8 == nwg ? (blockIdx.x & 7) * per + (blockIdx.x >> 3) : blockIdx.x;
-  const int band = t / (8 * tiles_n), rem = t - band * 8 * tiles_n;
-  const int band_rows = min(8, nwg / tiles_n - band * 8);
-  const int tm = band * 8 + rem % band_rows, tn = rem / band_rows;
+  int tm, tn;
+  gemm_tile(tiles_n, tm, tn);
   const int m0 = tm * kGT, n0 = tn * kGT;
   const int kb128 = K / 128, stages = (K + kMxKS - 1) / kMxKS;
   const int rowb = K / 2, srow = K / 32;                   // code and scale bytes per row
@@ -658,11 +660,8 @@ __global__ __launch_bounds__(kGThreads) void k_gemm_nvfp4(const uint8_t* __restr
   auto slot = [&](int s) { return lds + s * kNvSlotBytes; };
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nwg = gridDim.x, per = nwg / 8;
-  const int t = per * 8 == nwg ? (blockIdx.x & 7) * per + (blockIdx.x >> 3) : blockIdx.x;
-  const int band = t / (8 * tiles_n), rem = t - band * 8 * tiles_n;
-  const int band_rows = min(8, nwg / tiles_n - band * 8);
-  const int tm = band * 8 + rem % band_rows, tn = rem / band_rows;
+  int tm, tn;
+  gemm_tile(tiles_n, tm, tn);
   const int m0 = tm * kGT, n0 = tn * kGT;
   const int kb128 = K / 128, stages = (K + kMxKS - 1) / kMxKS;
   const int rowb = K / 2, srow = K / 16;                   // code and scale bytes per row
@@ -742,19 +741,21 @@ __global__ __launch_bounds__(kGThreads) void k_gemm_nvfp4(const uint8_t* __restr
 
 }  // namespace
 
-// Compute units of the current device, read once per device.
+// Compute units of the current device, read once per device (concurrent
+// first calls store the same value).
 static int gemm_cus() {
-  static int cus[64] = {};
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     int v = 0;
-    cus[dev] = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-                       v > 0
-                   ? v
-                   : 256;
+    n = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0
+            ? v
+            : 256;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
 hipError_t launch_gemm_fp8_bs(const uint8_t* a, const float* a_scales, const uint8_t* b,
