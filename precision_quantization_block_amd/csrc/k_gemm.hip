@@ -255,6 +255,44 @@ __device__ __forceinline__ void quantize_tile_rows(const uint8_t* lds, int tid, 
   }
 }
 
+// The same for 64 staged rows, with all 256 threads: four per row (t >> 2).
+// Thread t takes columns 64 i + 16 (t & 3) + j (i < 2, j < 16), so each
+// 16-byte code store of the four covers 64 contiguous bytes of the row; the
+// row's columns 0 .. 63 and 64 .. 127 are staged at positions 0 and 1.
+__device__ __forceinline__ void quantize_half_tile_rows(const uint8_t* lds, int tid, int row0,
+                                                        int n0, int M, int N, uint8_t* C,
+                                                        float* c_scales) {
+  static_assert(kGThreads == 256, "four threads per row of 64 rows");
+  const int rr = tid >> 2, part = tid & 3;
+  const float* stage = reinterpret_cast<const float*>(lds) + rr * kGOutStride + 16 * part;
+  uint32_t am = 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float* v = stage + i * 64 * kGOutStride;
+#pragma unroll
+    for (int j = 0; j < 16; j += 4) {
+      const v4f x = *reinterpret_cast<const v4f*>(v + j);
+      am = max(am, max(max(as_u(fabsf(x[0])), as_u(fabsf(x[1]))),
+                       max(as_u(fabsf(x[2])), as_u(fabsf(x[3])))));
+    }
+  }
+  const float s = fp8_scale_bits<kE4M3>(group_umax<4>(am));
+  const float y = recip_rn(s);
+  if (row0 + rr < M) {
+    uint8_t* dst = C + (int64_t)(row0 + rr) * N + n0 + 16 * part;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float* v = stage + i * 64 * kGOutStride;
+      float w[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) w[j] = v[j];
+      const uint2 lo = fp8_pack8<kE4M3>(w, s, y), hi = fp8_pack8<kE4M3>(w + 8, s, y);
+      st_nt16(dst + 64 * i, lo.x, lo.y, hi.x, hi.y);
+    }
+    if (part == 0) c_scales[(int64_t)(row0 + rr) * (N / kGT) + n0 / kGT] = s;
+  }
+}
+
 template <int kOut>
 __global__ __launch_bounds__(kGThreads) void k_gemm_fp8_bs(const uint8_t* __restrict__ A,
                                                            const float* __restrict__ sA,
@@ -465,15 +503,14 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gemm_fp8_bs3(const uint8_t* __
 
   // Rows 64 pass .. 64 pass + 63 of the tile: waves (pass, 0) and (pass, 1)
   // stage their blocks at positions 0 and 1, then they are stored (or
-  // quantized, two threads per row).
+  // quantized, four threads per row).
   for (int pass = 0; pass < 2; ++pass) {
     if (pass) __syncthreads();
     if (wm == pass) stage_tile_t(acc, lds, wn, lane);
     __syncthreads();
     if constexpr (kOut == kOutFp8) {
-      if (tid < 128)
-        quantize_tile_rows(lds, tid, m0 + 64 * pass, n0, M, N, reinterpret_cast<uint8_t*>(C),
-                           c_scales);
+      quantize_half_tile_rows(lds, tid, m0 + 64 * pass, n0, M, N, reinterpret_cast<uint8_t*>(C),
+                              c_scales);
     } else if (wm == pass) {
       store_staged<kOut>(lds, wn, lane, m0 + 64 * pass, n0 + 64 * wn, M, N, C);
     }
