@@ -169,15 +169,17 @@ __device__ __forceinline__ void stage_tile_t(const v4f (&acc)[4][4], uint8_t* ld
       *reinterpret_cast<v4f*>(&out_lds[(mt * 16 + r16) * kGOutStride + nt * 16 + 4 * q]) = acc[mt][nt];
 }
 
-// Writes the 64 x 64 floats staged at position pos to C at (row0, col0),
-// rows at or past M skipped.
-template <int kOut>
+// Writes kRows rows, from row r0 on, of the 64 x 64 floats staged at position
+// pos to C at (row0 + r0, col0), rows at or past M skipped.
+template <int kOut, int kRows = 64>
 __device__ __forceinline__ void store_staged(const uint8_t* lds, int pos, int lane, int row0,
-                                             int col0, int M, int N, void* C) {
-  const float* out_lds = reinterpret_cast<const float*>(lds) + pos * 64 * kGOutStride;
+                                             int col0, int M, int N, void* C, int r0 = 0) {
+  static_assert(kRows % 8 == 0, "whole steps of 8 rows");
+  const float* out_lds = reinterpret_cast<const float*>(lds) + (pos * 64 + r0) * kGOutStride;
+  row0 += r0;
   if constexpr (kOut == kOutBf16) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {          // 8 lanes per row, 8 rows per step
+    for (int s = 0; s < kRows / 8; ++s) {  // 8 lanes per row, 8 rows per step
       const int rr = s * 8 + (lane >> 3), cc = (lane & 7) * 8;
       if (row0 + rr < M) {
         const float* v = out_lds + rr * kGOutStride + cc;
@@ -189,7 +191,7 @@ __device__ __forceinline__ void store_staged(const uint8_t* lds, int pos, int la
     }
   } else {
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {         // 16 lanes per row, 4 rows per step
+    for (int s = 0; s < kRows / 4; ++s) {  // 16 lanes per row, 4 rows per step
       const int rr = s * 4 + (lane >> 4), cc = (lane & 15) * 4;
       if (row0 + rr < M) {
         const v4f x = *reinterpret_cast<const v4f*>(out_lds + rr * kGOutStride + cc);
@@ -502,8 +504,8 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gemm_fp8_bs3(const uint8_t* __
   barrier();  // every wave done with the slot before it becomes the output stage
 
   // Rows 64 pass .. 64 pass + 63 of the tile: waves (pass, 0) and (pass, 1)
-  // stage their blocks at positions 0 and 1, then they are stored (or
-  // quantized, four threads per row).
+  // stage their blocks at positions 0 and 1, then all four waves store them
+  // (32 rows of one position each) or quantize them (four threads per row).
   for (int pass = 0; pass < 2; ++pass) {
     if (pass) __syncthreads();
     if (wm == pass) stage_tile_t(acc, lds, wn, lane);
@@ -511,8 +513,9 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gemm_fp8_bs3(const uint8_t* __
     if constexpr (kOut == kOutFp8) {
       quantize_half_tile_rows(lds, tid, m0 + 64 * pass, n0, M, N, reinterpret_cast<uint8_t*>(C),
                               c_scales);
-    } else if (wm == pass) {
-      store_staged<kOut>(lds, wn, lane, m0 + 64 * pass, n0 + 64 * wn, M, N, C);
+    } else {                               // wave w: rows 32 (w >> 1) .. of position w & 1
+      store_staged<kOut, 32>(lds, wave & 1, lane, m0 + 64 * pass, n0 + 64 * (wave & 1), M, N, C,
+                             32 * (wave >> 1));
     }
   }
 }
