@@ -432,6 +432,11 @@ __global__ __launch_bounds__(kWThreads) void k_w4a16_mfma(const W4Args a, int M)
 
 // Launches of this many weight rows or more take four tiles per workgroup.
 constexpr int64_t kMfmaBigLaunchRows = 1 << 16;
+// With more than 16 activation rows, each activation load serves 4 tiles
+// instead of 1 once a launch has enough rows to keep 256 workgroups of 64
+// rows busy (at 32 or 64 activation rows: a gate-up projection of 28672 rows
+// 70.8 -> 39.4 and 140.0 -> 76.6 us; one of 4096 rows, 64 workgroups, slower).
+constexpr int64_t kMfmaWideLaunchRows = 1 << 14;
 
 template <int kMB, int kTiles>
 void launch_mfma_mb(const W4Args& a, int wgs, int M, bool out_bf16, hipStream_t st) {
@@ -472,7 +477,8 @@ hipError_t launch_w4a16_mfma(const W4Job* jobs, int njobs, int64_t M, bool out_b
       a.njobs = n;
       int64_t rows = 0;
       for (int i = 0; i < n; ++i) rows += jobs[base + i].N;
-      const int tiles = rows >= kMfmaBigLaunchRows ? 4 : 1, per_wg = 16 * tiles;
+      const bool four = rows >= kMfmaBigLaunchRows || (mr > 16 && rows >= kMfmaWideLaunchRows);
+      const int tiles = four ? 4 : 1, per_wg = 16 * tiles;
       int wg = 0;
       for (int i = 0; i < n; ++i) {
         W4Job j = jobs[base + i];

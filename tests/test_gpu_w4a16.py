@@ -354,3 +354,18 @@ def test_w4a16_matrix_cores_large_launch(pqb, M):
     codes, scales, zeros = oracle.int4_quantize(w[None])
     check_mfma(pqb, bf16_bits(r.standard_normal((M, K))), codes[0], scales[0], zeros,
                f"large launch M={M}")
+
+
+@pytest.mark.parametrize("N", [16383, 16400])
+@pytest.mark.parametrize("M", [17, 40])
+def test_w4a16_matrix_cores_wide_launch(pqb, M, N):
+    """With more than 16 activation rows in a launch slice, a launch of 2^14
+    weight rows or more also takes four tiles per workgroup: N on both sides
+    of that threshold (ragged above it), M in one slice (17) and in two
+    (32 + 8, the second slice with one tile)."""
+    r = rng(f"widem{M}n{N}")
+    K = 256
+    w = (0.02 * r.standard_normal((N, K))).astype(np.float32)
+    codes, scales, zeros = oracle.int4_quantize(w[None])
+    check_mfma(pqb, bf16_bits(r.standard_normal((M, K))), codes[0], scales[0], zeros,
+               f"wide launch M={M} N={N}")
