@@ -264,9 +264,9 @@ hipError_t launch_args(W4Args& a, int M, int64_t rows, bool out_bf16, hipStream_
 // ---------------------------------------------------------------------------
 // The same product on the matrix cores, for any M (v_mfma_f32_16x16x32_bf16).
 // A workgroup owns kTiles tiles of 16 weight rows (the MFMA's N): four in
-// launches of 2^16 rows or more, where sharing each activation load among the
-// tiles pays, and one in smaller launches (a layer's projections), which need
-// the workgroups.  Its 4 waves split K into four contiguous ranges of groups,
+// launches of 2^14 rows or more, where sharing each activation load among the
+// tiles pays, and one in smaller launches (most of a layer's projections),
+// which need the workgroups.  Its 4 waves split K into four contiguous ranges of groups,
 // so that one wave reads both halves of a 128-byte code line and a row's
 // scales in consecutive steps.  For one group, lane l supplies row l & 15 of
 // the activation block and of each weight tile, and K positions 32 (l >> 4)
@@ -430,13 +430,12 @@ __global__ __launch_bounds__(kWThreads) void k_w4a16_mfma(const W4Args a, int M)
   }
 }
 
-// Launches of this many weight rows or more take four tiles per workgroup.
-constexpr int64_t kMfmaBigLaunchRows = 1 << 16;
-// With more than 16 activation rows, each activation load serves 4 tiles
-// instead of 1 once a launch has enough rows to keep 256 workgroups of 64
-// rows busy (at 32 or 64 activation rows: a gate-up projection of 28672 rows
-// 70.8 -> 39.4 and 140.0 -> 76.6 us; one of 4096 rows, 64 workgroups, slower).
-constexpr int64_t kMfmaWideLaunchRows = 1 << 14;
+// Launches of this many weight rows or more take four tiles per workgroup:
+// enough rows for 256 workgroups of 64, and each activation load then serves
+// 4 tiles instead of 1 (a gate-up projection of 28672 rows: 27.7 -> 25.8 us
+// per launch at M = 1, 32.0 -> 27.2 at M = 4, 45.7 -> 31.2 at M = 16, 140.0
+// -> 76.3 at M = 64; one of 4096 rows, 64 workgroups of 4 tiles, is slower).
+constexpr int64_t kMfmaBigLaunchRows = 1 << 14;
 
 template <int kMB, int kTiles>
 void launch_mfma_mb(const W4Args& a, int wgs, int M, bool out_bf16, hipStream_t st) {
@@ -477,8 +476,7 @@ hipError_t launch_w4a16_mfma(const W4Job* jobs, int njobs, int64_t M, bool out_b
       a.njobs = n;
       int64_t rows = 0;
       for (int i = 0; i < n; ++i) rows += jobs[base + i].N;
-      const bool four = rows >= kMfmaBigLaunchRows || (mr > 16 && rows >= kMfmaWideLaunchRows);
-      const int tiles = four ? 4 : 1, per_wg = 16 * tiles;
+      const int tiles = rows >= kMfmaBigLaunchRows ? 4 : 1, per_wg = 16 * tiles;
       int wg = 0;
       for (int i = 0; i < n; ++i) {
         W4Job j = jobs[base + i];

@@ -345,7 +345,7 @@ def test_w4a16_matrix_cores_engine_quantized_llama_weights(pqb):
 
 @pytest.mark.parametrize("M", [1, 17, 40])
 def test_w4a16_matrix_cores_large_launch(pqb, M):
-    """A launch of 2^16 weight rows or more takes four 16-row tiles per
+    """A launch of 2^14 weight rows or more takes four 16-row tiles per
     workgroup (smaller launches one): a ragged N = 66001 with M in one block,
     two blocks, and two launch slices."""
     r = rng(f"bigm{M}")
@@ -357,12 +357,11 @@ def test_w4a16_matrix_cores_large_launch(pqb, M):
 
 
 @pytest.mark.parametrize("N", [16383, 16400])
-@pytest.mark.parametrize("M", [17, 40])
-def test_w4a16_matrix_cores_wide_launch(pqb, M, N):
-    """With more than 16 activation rows in a launch slice, a launch of 2^14
-    weight rows or more also takes four tiles per workgroup: N on both sides
-    of that threshold (ragged above it), M in one slice (17) and in two
-    (32 + 8, the second slice with one tile)."""
+@pytest.mark.parametrize("M", [3, 17, 40])
+def test_w4a16_matrix_cores_launch_threshold(pqb, M, N):
+    """Four tiles per workgroup from 2^14 weight rows on: N on both sides of
+    that threshold (ragged above it), M in one 16-row block (3), in two (17)
+    and in two launch slices (40 = 32 + 8)."""
     r = rng(f"widem{M}n{N}")
     K = 256
     w = (0.02 * r.standard_normal((N, K))).astype(np.float32)
