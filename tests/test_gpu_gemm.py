@@ -182,6 +182,31 @@ def test_gemm_three_per_cu_ragged(pqb, K):
     assert np.array_equal(scales[sel].cpu().numpy().reshape(-1).view(np.int32), os_.reshape(-1).view(np.int32))
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_gemm_random_shapes(pqb, seed):
+    """Seeded random shapes spanning 1 to 5 tiles per CU, so that either of
+    the two kernels the launcher chooses between (two or three workgroups
+    per CU) computes them: sampled rows, the last row among them, against
+    the oracle in float32 and bf16, and the fused form's codes and scales on
+    the same rows against the oracle quantizer of the float32 result."""
+    r = rng(f"gshape{seed}")
+    M = int(r.integers(1, 6001))
+    N = 128 * int(r.integers(1, 33))
+    K = 128 * int(r.choice([1, 2, 3, 5]))
+    a, b = random_codes(r, (M, K)), random_codes(r, (N, K))
+    sa = (r.uniform(0.5, 2, (M, K // 128)) * 2.0 ** r.integers(-6, 6, (M, 1))).astype(np.float32)
+    sb = (r.uniform(0.5, 2, (N // 128, K // 128)) * 2.0 ** -8).astype(np.float32)
+    rows = np.unique(np.concatenate([r.choice(M, min(M, 12), replace=False), [M - 1]]))
+    check(pqb, a, sa, b, sb, f"random shape {(M, N, K)}", rows=rows)
+    ad, sad, bd, sbd = to_dev(a), to_dev(sa), to_dev(b), to_dev(sb)
+    c32 = pqb.gemm_fp8_blockscaled(ad, sad, bd, sbd, out_dtype=torch.float32)
+    codes, scales = pqb.gemm_fp8_blockscaled_quant(ad, sad, bd, sbd)
+    sel = torch.from_numpy(rows).to(DEV)
+    oc, os_ = oracle.fp8_quantize(c32[sel].cpu().numpy()[None], "1x128")
+    assert np.array_equal(codes[sel].cpu().numpy().reshape(-1), oc.reshape(-1))
+    assert np.array_equal(scales[sel].cpu().numpy().reshape(-1).view(np.int32), os_.reshape(-1).view(np.int32))
+
+
 BENCH_SHAPES = [(8192, 7168, 2048), (8192, 2048, 7168)]
 
 
